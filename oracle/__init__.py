@@ -1,0 +1,221 @@
+"""fp64 CPU oracle for attention over a paged KV cache -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, links or calls it, and it imports nothing
+from the product package.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, two-pass softmax over an
+explicit visible-key list); this module only builds it with gcc and marshals
+numpy / torch CPU arrays into it.  Every function returns float64 numpy
+arrays.  See ``oracle.c`` for the definition it follows and the passages it
+cites.
+
+Parity pins (what holds this oracle to something other than itself) live in
+``tests/test_oracle_pins.py``; no function here is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F32, BF16 = 0, 1
+
+
+def compile_source(src: str, out: str) -> str:
+    """gcc -O2, no fast-math, no FMA contraction: fp64 as written."""
+    tmp = out + f".tmp{os.getpid()}"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                           "-ffp-contract=off", "-fno-fast-math", src, "-o", tmp, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = False) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` when it is missing or stale."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        compile_source(_SRC, _LIB)
+    return _LIB
+
+
+def use_library(path: Optional[str]):
+    """Point this module at another build of ``oracle.c`` (``None``: the
+    default one).  Used by the tests that plant mistakes in a copy of the
+    oracle to show the pins catch them."""
+    global _lib, _override
+    _override = path
+    _lib = None
+
+
+_override: Optional[str] = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        path = _override
+        if path is None:
+            path = build()
+        lib = ctypes.CDLL(path)
+        P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+        lib.oracle_paged_decode.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, D, I, I, I,
+                                            I, P, I, I]
+        lib.oracle_varlen_prefill.argtypes = [P, P, P, P, P, P, P, P, I, I, P, P, I, I, I, I, D,
+                                              I, P, I, P, I, I]
+        lib.oracle_merge.argtypes = [P, P, P, P, P, P, I, I, I, I]
+        lib.oracle_reshape_and_cache.argtypes = [P, P, P, P, P, I, I, I, I, I, I]
+        lib.oracle_token_request.argtypes = [P, I, I, P]
+        lib.oracle_slot_of.argtypes = [P, I, I]
+        lib.oracle_slot_of.restype = ctypes.c_longlong
+        _lib = lib
+    return _lib
+
+
+def _np(t) -> Optional[np.ndarray]:
+    """Contiguous numpy view of a CPU tensor/array (bf16 as its uint16 bits)."""
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        t = t.detach().cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+    return np.ascontiguousarray(t)
+
+
+def _dtype_code(t) -> int:
+    if isinstance(t, torch.Tensor):
+        if t.dtype == torch.bfloat16:
+            return BF16
+        if t.dtype == torch.float32:
+            return F32
+    elif isinstance(t, np.ndarray) and t.dtype == np.float32:
+        return F32
+    raise TypeError(f"oracle inputs must be float32 or bfloat16, got {getattr(t, 'dtype', t)}")
+
+
+def _ptr(a) -> Optional[int]:
+    return None if a is None else a.ctypes.data
+
+
+def _threads(n: Optional[int]) -> int:
+    return n if n else (os.cpu_count() or 1)
+
+
+def token_request(cu: Sequence[int], T: Optional[int] = None) -> np.ndarray:
+    """Request index of every packed token (varlen cumulative-length map)."""
+    cu = np.asarray(cu, dtype=np.int32)
+    B = len(cu) - 1
+    T = int(cu[-1] - cu[0]) if T is None else T
+    out = np.empty(max(T, 1), dtype=np.int32)
+    _load().oracle_token_request(_ptr(cu), B, T, _ptr(out))
+    return out[:T]
+
+
+def slot_of(block_table_row: Sequence[int], pos: int, block_size: int) -> int:
+    row = np.asarray(block_table_row, dtype=np.int32)
+    return int(_load().oracle_slot_of(_ptr(row), pos, block_size))
+
+
+def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sink, sm_scale: float,
+                 window_left: int = -1, partition_size: int = 0,
+                 units: Optional[Sequence[int]] = None, nthreads: Optional[int] = None):
+    """Decode over a paged cache.
+
+    Returns ``(out [B,Hq,D], lse [B,Hq])`` for ``partition_size == 0``, else
+    the per-partition results ``(out [B,Hq,P,D], lse [B,Hq,P])`` with the
+    sink left out.  ``units`` restricts the work to flat ids
+    ``(b*Hq + h) * P + p``; other entries are left NaN."""
+    dt = _dtype_code(q)
+    qn, kn, vn = _np(q), _np(k_cache), _np(v_cache)
+    bt = _np(block_table).astype(np.int32, copy=False)
+    sl = _np(cache_seqlens).astype(np.int32, copy=False)
+    sk = None if sink is None else _np(sink).astype(np.float32, copy=False)
+    B, Hq, D = qn.shape
+    NB, bs, Hkv, D2 = kn.shape
+    assert D2 == D and tuple(vn.shape) == tuple(kn.shape)
+    if partition_size > 0:
+        P = max(1, (int(sl.max(initial=0)) + partition_size - 1) // partition_size)
+        out = np.full((B, Hq, P, D), np.nan)
+        lse = np.full((B, Hq, P), np.nan)
+    else:
+        P = 1
+        out = np.full((B, Hq, D), np.nan)
+        lse = np.full((B, Hq), np.nan)
+    un = None if units is None else np.ascontiguousarray(units, dtype=np.int32)
+    rc = _load().oracle_paged_decode(
+        _ptr(out), _ptr(lse), _ptr(qn), _ptr(kn), _ptr(vn), _ptr(bt), _ptr(sl), _ptr(sk),
+        B, Hq, Hkv, D, bs, bt.shape[1], float(sm_scale), int(window_left), int(partition_size),
+        P, dt, _ptr(un), 0 if un is None else len(un), _threads(nthreads))
+    assert rc == 0
+    return out, lse
+
+
+def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, sink, sm_scale: float, num_kv_heads: int,
+                   k=None, v=None, k_cache=None, v_cache=None, block_table=None,
+                   block_size: int = 0, window_left: int = -1,
+                   units: Optional[Sequence[int]] = None, nthreads: Optional[int] = None):
+    """Causal varlen prefill; returns ``(out [sum Lq,Hq,D], lse [sum Lq,Hq])``.
+    ``units`` restricts the work to flat ids ``t*Hq + h``."""
+    dt = _dtype_code(q)
+    qn = _np(q)
+    T, Hq, D = qn.shape
+    cq = _np(cu_seqlens_q).astype(np.int32, copy=False)
+    ck = _np(cu_seqlens_k).astype(np.int32, copy=False)
+    B = len(cq) - 1
+    kn, vn = _np(k), _np(v)
+    kc, vc = _np(k_cache), _np(v_cache)
+    bt = None if block_table is None else _np(block_table).astype(np.int32, copy=False)
+    assert (kn is None) != (kc is None), "exactly one of contiguous or paged K/V"
+    sk = None if sink is None else _np(sink).astype(np.float32, copy=False)
+    out = np.full((T, Hq, D), np.nan)
+    lse = np.full((T, Hq), np.nan)
+    un = None if units is None else np.ascontiguousarray(units, dtype=np.int32)
+    rc = _load().oracle_varlen_prefill(
+        _ptr(out), _ptr(lse), _ptr(qn), _ptr(kn), _ptr(vn), _ptr(kc), _ptr(vc), _ptr(bt),
+        int(block_size), 0 if bt is None else bt.shape[1], _ptr(cq), _ptr(ck), B, Hq,
+        int(num_kv_heads), D, float(sm_scale), int(window_left), _ptr(sk), dt, _ptr(un),
+        0 if un is None else len(un), _threads(nthreads))
+    assert rc == 0
+    return out, lse
+
+
+def merge(part_out, part_lse, nparts_per_seq, sink):
+    """Split-KV merge of partition results ``[B,Hq,P,D]`` / ``[B,Hq,P]``."""
+    po = np.ascontiguousarray(np.asarray(part_out, dtype=np.float64))
+    pl = np.ascontiguousarray(np.asarray(part_lse, dtype=np.float64))
+    npb = np.ascontiguousarray(nparts_per_seq, dtype=np.int32)
+    sk = None if sink is None else _np(sink).astype(np.float32, copy=False)
+    B, Hq, P, D = po.shape
+    out = np.zeros((B, Hq, D))
+    lse = np.zeros((B, Hq))
+    _load().oracle_merge(_ptr(out), _ptr(lse), _ptr(po), _ptr(pl), _ptr(npb), _ptr(sk), B, Hq,
+                         D, P)
+    return out, lse
+
+
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping):
+    """Returns new (k_cache, v_cache) CPU tensors with the rows scattered."""
+    kc = k_cache.detach().cpu().clone().contiguous()
+    vc = v_cache.detach().cpu().clone().contiguous()
+    key = key.detach().cpu().contiguous()
+    value = value.detach().cpu().contiguous()
+    sm = _np(slot_mapping).astype(np.int32, copy=False)
+    T, Hkv, D = key.shape
+    NB, bs = kc.shape[0], kc.shape[1]
+    rc = _load().oracle_reshape_and_cache(
+        key.data_ptr(), value.data_ptr(), kc.data_ptr(), vc.data_ptr(), _ptr(sm), T, Hkv, D, bs,
+        NB, key.element_size())
+    assert rc == 0, "slot out of range"
+    return kc, vc
