@@ -1,0 +1,366 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV attention library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--skip-long]
+
+One "step" of the headline workload is one bf16 paged decode over 64
+sequences with cache_seqlens ~ U[512, 4096], 32 query / 8 kv heads, head_dim
+128, block size 16 and a shuffled block pool: the decode kernel (per-partition
+results) followed by the log-sum-exp merge, both on torch's current stream.
+Inputs are resident in HBM before the timed region; K steps are timed
+between a synchronize on each side, each kernel with its own pair of HIP
+events.  Consecutive steps alternate between two copies of the KV pool so
+that no step finds its keys in the 256 MB last-level cache.
+
+The other workloads (varlen prefill with reshape_and_cache, chunked paged
+prefill with a window, long-context split decode) are timed the same way and
+reported in the same JSON line under "workloads".  The fp64 CPU oracle is
+timed on the host cores for the headline workload ("cpu_baseline").
+
+Peaks: HBM3E 8.0 TB/s, dense bf16 MFMA 2.5 PFLOP/s (MI355X public figures).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--only", default="all",
+                   choices=["all", "decode", "prefill", "chunked", "longctx", "none"])
+    p.add_argument("--skip-long", action="store_true", help="skip the 131072-token workload")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--partition-size", type=int, default=0, help="decode partition (0 = auto)")
+    p.add_argument("--copy-calibration-mb", type=int, default=0,
+                   help="also run a plain device copy of this size (counter calibration)")
+    return p.parse_args()
+
+
+ARGS = parse()
+if ARGS.gpus != 1:
+    print(f"bench.py runs on one GPU only (asked for --gpus {ARGS.gpus}); the library has no "
+          f"multi-GPU path.", file=sys.stderr)
+    sys.exit(2)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import synth  # noqa: E402
+from paged_kv_cache_02_amd import pkv  # noqa: E402
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class KernelTimer:
+    """Pairs of HIP events on torch's current stream around named launches."""
+
+    def __init__(self):
+        self.pairs = {}
+
+    def time(self, name, fn):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        r = fn()
+        e.record()
+        self.pairs.setdefault(name, []).append((s, e))
+        return r
+
+    def mean_ms(self, name):
+        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs[name]]))
+
+
+def timed_steps(step, steps, warmup):
+    """Run warmup + timed steps; returns (ms per step, KernelTimer of the timed steps)."""
+    for i in range(warmup):
+        step(i, KernelTimer())
+    torch.cuda.synchronize()
+    kt = KernelTimer()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, kt)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    return ms, kt
+
+
+def roofline(bound, achieved, peak, unit, traffic=None):
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+# ----------------------------------------------------------------------------
+# decode workloads
+# ----------------------------------------------------------------------------
+
+def decode_bytes(c):
+    """Algorithmic bytes of one decode: K and V of every attended token, q,
+    the output, the used block-table entries and the sequence lengths."""
+    L = c.cache_seqlens.numpy().astype(np.int64)
+    kv = int(L.sum()) * c.Hkv * c.D * 2 * 2
+    q = c.B * c.Hq * c.D * 2
+    table = int(np.sum((L + c.block_size - 1) // c.block_size)) * 4 + c.B * 4
+    return kv, q, table
+
+
+def replicate_pool(c, reps):
+    """reps copies of the block pool in one allocation; copy r is reached
+    through block_table + r * num_blocks (same values, disjoint memory)."""
+    kc = c.k_cache.cuda().repeat(reps, 1, 1, 1)
+    vc = c.v_cache.cuda().repeat(reps, 1, 1, 1)
+    bt = c.block_table.cuda()
+    tables = [torch.where(bt >= 0, bt + r * c.num_blocks, bt).contiguous() for r in range(reps)]
+    return kc, vc, tables
+
+
+def bench_decode(c, name, steps, warmup, partition_size, reps):
+    B, Hq, D = c.B, c.Hq, c.D
+    kc, vc, tables = replicate_pool(c, reps)
+    q = c.q.cuda()
+    sl = c.cache_seqlens.cuda()
+    sink = None if c.sink is None else c.sink.cuda()
+    out = torch.empty_like(q)
+    msk = c.max_seqlen_k
+    P = partition_size or pkv.decode_auto_partition(B, Hq, c.Hkv, D, c.block_size, msk)
+    split = P > 0 and P < msk
+    nparts = (msk + P - 1) // P if split else 1
+    part_out = torch.empty((B, Hq, nparts, D), dtype=torch.float32, device="cuda")
+    part_lse = torch.empty((B, Hq, nparts), dtype=torch.float32, device="cuda")
+
+    def step(i, kt):
+        bt = tables[i % reps]
+        if split:
+            kt.time("decode", lambda: pkv.paged_decode_partitions(
+                q, kc, vc, bt, sl, c.sm_scale, P, msk, c.window_left, part_out, part_lse))
+            kt.time("merge", lambda: pkv.merge_partitions(part_out, part_lse, sl, P, sink=sink,
+                                                          out=out))
+        else:
+            kt.time("decode", lambda: pkv.paged_decode(q, kc, vc, bt, sl, c.sm_scale, sink=sink,
+                                                       window_left=c.window_left,
+                                                       max_seqlen_k=msk, out=out))
+
+    ms, kt = timed_steps(step, steps, warmup)
+    kv, qb, table = decode_bytes(c)
+    step_bytes = kv + 2 * qb + table
+    dec_ms = kt.mean_ms("decode")
+    dec_bytes = kv + qb + table + (0 if split else qb)
+    res = {
+        "name": name, "value": round(step_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "ms_per_step": round(ms, 4), "algorithmic_bytes": step_bytes,
+        "partition_size": P if split else 0, "nparts": nparts,
+        "kernels_ms": {"decode": round(dec_ms, 4)},
+        "roofline": roofline("hbm", dec_bytes / (dec_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+    }
+    if split:
+        res["kernels_ms"]["merge"] = round(kt.mean_ms("merge"), 4)
+    res["frac_of_hbm_peak_step"] = round(res["value"] / HBM_PEAK_GBS, 4)
+    del kc, vc, tables
+    torch.cuda.empty_cache()
+    return res, out
+
+
+# ----------------------------------------------------------------------------
+# prefill workloads
+# ----------------------------------------------------------------------------
+
+def visible_pairs(q_lens, k_lens, window):
+    n = 0
+    for Lq, Lk in zip(q_lens, k_lens):
+        p = np.arange(Lk - Lq, Lk, dtype=np.int64)
+        hi = np.minimum(p, Lk - 1)
+        lo = np.zeros_like(p) if window < 0 else np.maximum(0, p - window)
+        n += int(np.maximum(0, hi - lo + 1).sum())
+    return n
+
+
+def bench_prefill(c, name, steps, warmup, reps, with_cache_write=False):
+    T = c.q.shape[0]
+    qs = [c.q.cuda() for _ in range(reps)]
+    cq, ck = c.cu_seqlens_q.cuda(), c.cu_seqlens_k.cuda()
+    sink = None if c.sink is None else c.sink.cuda()
+    out = torch.empty_like(qs[0])
+    if c.paged:
+        kc, vc, tables = replicate_pool(
+            synth.DecodeCase(c.q[:1], c.k_cache, c.v_cache, c.block_table,
+                             torch.zeros(1, dtype=torch.int32), None, c.block_size, 1.0),
+            reps)
+        ks = vs = None
+    else:
+        ks = [c.k.cuda() for _ in range(reps)]
+        vs = [c.v.cuda() for _ in range(reps)]
+    if with_cache_write:
+        # the new K/V go into a shuffled paged pool of block size 16
+        rng = np.random.default_rng(7)
+        bt, nb = synth.pool_from_lengths(rng, c.k_lens, 16)
+        slots = torch.cat([synth.slots_for_tokens(bt[r:r + 1].expand(L, -1).contiguous(),
+                                                  list(range(L)), 16)
+                           for r, L in enumerate(c.k_lens)]).cuda()
+        kcache = torch.zeros((nb, 16, c.Hkv, c.D), dtype=c.q.dtype, device="cuda")
+        vcache = torch.zeros_like(kcache)
+
+    def step(i, kt):
+        r = i % reps
+        if with_cache_write:
+            kt.time("reshape_and_cache",
+                    lambda: pkv.reshape_and_cache(ks[r], vs[r], kcache, vcache, slots))
+        if c.paged:
+            kt.time("prefill", lambda: pkv.varlen_prefill(
+                qs[r], cq, ck, c.max_seqlen_q, c.max_seqlen_k, c.sm_scale, c.Hkv,
+                k_cache=kc, v_cache=vc, block_table=tables[r], sink=sink,
+                window_left=c.window_left, out=out))
+        else:
+            kt.time("prefill", lambda: pkv.varlen_prefill(
+                qs[r], cq, ck, c.max_seqlen_q, c.max_seqlen_k, c.sm_scale, c.Hkv, k=ks[r],
+                v=vs[r], sink=sink, window_left=c.window_left, out=out))
+
+    ms, kt = timed_steps(step, steps, warmup)
+    pairs = visible_pairs(c.q_lens, c.k_lens, c.window_left)
+    flops = 4 * c.D * c.Hq * pairs
+    pre_ms = kt.mean_ms("prefill")
+    res = {"name": name, "value": round(flops / (pre_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+           "ms_per_step": round(ms, 4), "algorithmic_flops": flops,
+           "kernels_ms": {"prefill": round(pre_ms, 4)},
+           "roofline": roofline("mfma", flops / (pre_ms * 1e-3) / 1e12, MFMA_BF16_PEAK_TFS,
+                                "TFLOP/s")}
+    # bytes the method must move: q and out, plus K/V of the visible key range
+    kv_tokens = 0
+    for Lq, Lk in zip(c.q_lens, c.k_lens):
+        lo = 0 if c.window_left < 0 else max(0, Lk - Lq - c.window_left)
+        kv_tokens += Lk - lo
+    byts = 2 * T * c.Hq * c.D * 2 + kv_tokens * c.Hkv * c.D * 2 * 2
+    res["algorithmic_bytes"] = byts
+    res["hbm_gbs"] = round(byts / (pre_ms * 1e-3) / 1e9, 2)
+    if c.window_left >= 0:
+        ridge = min(MFMA_BF16_PEAK_TFS * 1e12, flops / byts * HBM_PEAK_GBS * 1e9)
+        res["min_roofline_tflops"] = round(ridge / 1e12, 2)
+        res["frac_of_min_roofline"] = round(flops / (pre_ms * 1e-3) / ridge, 4)
+    if with_cache_write:
+        rc_ms = kt.mean_ms("reshape_and_cache")
+        rbytes = 2 * sum(c.k_lens) * c.Hkv * c.D * 2 * 2
+        res["reshape_and_cache"] = {
+            "value": round(rbytes / (rc_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "kernel_ms": round(rc_ms, 4), "algorithmic_bytes": rbytes,
+            "roofline": roofline("hbm", rbytes / (rc_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
+    torch.cuda.empty_cache()
+    return res, out
+
+
+# ----------------------------------------------------------------------------
+# oracle parity spot check and CPU baseline
+# ----------------------------------------------------------------------------
+
+def host_threads():
+    for k in ("OMP_NUM_THREADS",):
+        if os.environ.get(k, "").isdigit():
+            return int(os.environ[k])
+    return min(16, os.cpu_count() or 1)
+
+
+def cpu_baseline_decode(c, algo_bytes):
+    import oracle  # the CPU-baseline leg is the only bench code that runs the oracle
+    n = host_threads()
+    t0 = time.perf_counter()
+    o, _ = oracle.paged_decode(c.q, c.k_cache, c.v_cache, c.block_table, c.cache_seqlens,
+                               c.sink, c.sm_scale, c.window_left, nthreads=n)
+    dt = time.perf_counter() - t0
+    return {"value": round(algo_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": n,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "the full headline workload (64 sequences x 32 heads), fp64 two-pass"}, o
+
+
+def spot_check(out, want, units, Hq, what):
+    b, h = units // Hq, units % Hq
+    got = out.float().cpu().numpy()[b, h]
+    ref = want[b, h]
+    err = np.abs(got - ref)
+    ok = bool(np.all(err <= 2e-2 + 1e-2 * np.abs(ref)))
+    return {"what": what, "rows": int(len(units)), "max_abs_err": float(err.max()), "pass": ok}
+
+
+# ----------------------------------------------------------------------------
+
+def main():
+    torch.cuda.init()
+    dev = torch.cuda.get_device_properties(0)
+    log(f"device {dev.name} CUs={dev.multi_processor_count}")
+    steps, warmup = ARGS.steps, ARGS.warmup
+    workloads = {}
+
+    log("generating decode workload (64 seqs, U[512,4096], 32/8 heads, D 128, bs 16)")
+    c2 = synth.config2_decode()
+    head = None
+    if ARGS.only in ("all", "decode"):
+        head, out2 = bench_decode(c2, "decode_64x_U512-4096", steps, warmup,
+                                  ARGS.partition_size, reps=2)
+        log(f"decode: {head['value']} GB/s step, kernel {head['roofline']['achieved']} GB/s")
+
+    if ARGS.only in ("all", "prefill"):
+        log("prefill workload (8 reqs U[256,4096], 32/8 heads, D 128, sink)")
+        c3 = synth.config3_prefill()
+        r3, _ = bench_prefill(c3, "varlen_prefill_8x_U256-4096", steps, warmup, reps=2,
+                              with_cache_write=True)
+        workloads["varlen_prefill"] = r3
+        log(f"prefill: {r3['value']} TFLOP/s")
+    if ARGS.only in ("all", "chunked"):
+        log("chunked prefill workload (4 x 512 q on 8704 paged keys, window 128, 64/8, D 64)")
+        c4 = synth.config4_chunked(poison=False, spare_blocks=0)
+        r4, _ = bench_prefill(c4, "chunked_prefill_4x512_on_8704_w128", steps, warmup, reps=8)
+        workloads["chunked_prefill"] = r4
+        log(f"chunked: {r4['value']} TFLOP/s, {r4['hbm_gbs']} GB/s")
+    if ARGS.only in ("all", "longctx") and not ARGS.skip_long:
+        log("long-context decode workload (16 x 131072, bs 64, partitions of 512, sink)")
+        c5 = synth.config5_split_decode()
+        r5, out5 = bench_decode(c5, "split_decode_16x131072", max(3, steps // 4), 2, 512, reps=1)
+        workloads["split_decode_long"] = r5
+        log(f"long decode: {r5['value']} GB/s")
+        del c5
+    if ARGS.copy_calibration_mb:
+        n = ARGS.copy_calibration_mb * (1 << 20) // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        workloads["copy_calibration"] = {"bytes_read": n * 4, "bytes_written": n * 4}
+
+    line = {"metric": "decode KV GB/s (% HBM peak); prefill TFLOP/s (% bf16 MFMA peak)",
+            "n_gpus": 1, "steps": steps, "warmup": warmup, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded numpy PCG64, N(0,1) rounded to bf16)"}
+    if head is not None:
+        line.update({"value": head["value"], "unit": "GB/s", "ms_per_step": head["ms_per_step"],
+                     "config": {"workload": "bf16 paged decode: 64 sequences, cache_seqlens "
+                                            "U[512,4096], 32 q / 8 kv heads, head_dim 128, "
+                                            "block_size 16, shuffled pool, no sink, no window",
+                                "global_batch": 64, "seq_len": "U[512,4096]",
+                                "parallelism": "single GPU",
+                                "partition_size": head["partition_size"]},
+                     "roofline": head["roofline"], "kernels_ms": head["kernels_ms"],
+                     "frac_of_hbm_peak_step": head["frac_of_hbm_peak_step"]})
+        if not ARGS.no_cpu_baseline:
+            log("timing the fp64 oracle on the host cores")
+            cb, o2 = cpu_baseline_decode(c2, head["algorithmic_bytes"])
+            line["cpu_baseline"] = cb
+            rng = np.random.default_rng(0)
+            units = rng.choice(c2.B * c2.Hq, 64, replace=False)
+            line["parity_spot_check"] = spot_check(out2, o2, units, c2.Hq, "decode vs oracle")
+    line["workloads"] = workloads
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

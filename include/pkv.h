@@ -1,0 +1,254 @@
+/*
+ * pkv.h -- C ABI of libpkv.so: attention over a paged KV cache on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Four operations, named after the pages that state the problem:
+ *
+ *   pkv_reshape_and_cache   store new K/V rows into cache slots
+ *                           (vLLM "attention.py" page, PagedAttention.forward:
+ *                           the cache_ops.reshape_and_cache call and its
+ *                           slot_mapping argument)
+ *   pkv_paged_decode        one query token per sequence over a paged cache
+ *                           (Transformers "Paged attention" doc, decode path:
+ *                           block_table and cache_seqlens; vLLM page,
+ *                           single_query_cached_kv_attention)
+ *   pkv_merge_partitions    log-sum-exp merge of split-KV partition results
+ *                           (vLLM page, single_query_cached_kv_attention: the
+ *                           partitioned "v2" path with exp_sums / max_logits /
+ *                           tmp_output)
+ *   pkv_varlen_prefill      causal attention for packed variable-length
+ *                           requests (Transformers doc, varlen path:
+ *                           cu_seq_lens_q/k and max_length_q/k), over
+ *                           contiguous K/V or over the paged cache
+ *
+ * What every attention call computes (FlashInfer "sink_attention_reference.py"
+ * page, sink_softmax and sink_attention_unified): for request r with Lq
+ * queries and Lk keys, query row i sits at absolute position p = Lk - Lq + i
+ * and sees key j iff 0 <= j <= p and (window_left < 0 or j >= p - window_left).
+ * Query head h reads kv head h / (Hq / Hkv).  Logits are sm_scale * q.k;
+ * the optional per-query-head sink is one more logit, NOT multiplied by
+ * sm_scale, that joins the softmax denominator and has no value row.  A row
+ * with no visible key gets output 0 (its lse is the sink, or -inf without one).
+ * lse, when requested, is the natural-log log-sum-exp of the row's logits
+ * including the sink.
+ *
+ * Conventions for every entry point:
+ *   - Array arguments are DEVICE pointers owned by the caller; the library
+ *     allocates nothing, keeps no state between calls and never prints.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the legacy
+ *     default stream) and the call returns without waiting; results are
+ *     valid in stream order.
+ *   - q, k, v, the caches and out share one dtype (pkv_dtype); sink, lse and
+ *     split-KV partials are always float32; index arrays are int32.
+ *   - Output dtype is the input dtype; bf16 results are rounded to nearest
+ *     even from float32 accumulators.
+ *   - Arguments are checked on the host before anything is launched; a bad
+ *     argument returns an error status and launches nothing.  Device-resident
+ *     index data (block_table entries, cache_seqlens, cu_seqlens, slots) is
+ *     NOT checked, since that would need a device-to-host copy: it is a
+ *     caller contract (see each function), and violating it is undefined.
+ *   - out/lse/workspace must not alias any input.
+ *
+ * Cache layout (both caches): [num_blocks, block_size, num_kv_heads,
+ * head_dim], contiguous, token-major like the packed [tokens, heads, dim]
+ * activations.  Logical token j of sequence b lives in physical block
+ * block_table[b * max_blocks_per_seq + j / block_size] at offset
+ * j % block_size.  Entries of block_table past the ones a sequence needs are
+ * never read (they may hold -1).
+ *
+ * Supported: head_dim in {64, 128}; block_size a power of two in [16, 512];
+ * num_q_heads a multiple of num_kv_heads; dtype PKV_F32 or PKV_BF16.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+    PKV_OK = 0,
+    PKV_ERR_NULL = 1,        /* a required pointer is NULL                    */
+    PKV_ERR_SHAPE = 2,       /* sizes inconsistent or out of range            */
+    PKV_ERR_UNSUPPORTED = 3, /* valid request this library does not implement */
+    PKV_ERR_WORKSPACE = 4,   /* workspace missing or too small                */
+    PKV_ERR_HIP = 5          /* a HIP launch failed (hipGetLastError)         */
+} pkv_status;
+
+typedef enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *pkv_status_string(pkv_status s);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int pkv_version(void);
+
+/*
+ * pkv_reshape_and_cache -- store T new tokens' K and V rows into the paged
+ * caches (vLLM page, PagedAttention.forward, cache_ops.reshape_and_cache).
+ *
+ *   key, value      [T, num_kv_heads, head_dim]; token t starts at element
+ *                   t * key_stride (value_stride); a stride of 0 means dense
+ *                   (num_kv_heads * head_dim), which allows K and V sliced out
+ *                   of a fused QKV buffer.  Strides must be multiples of 8
+ *                   elements and the pointers 16-byte aligned.
+ *   k_cache,v_cache [num_blocks, block_size, num_kv_heads, head_dim], written
+ *                   in place.
+ *   slot_mapping    [T] int32: slot s = block * block_size + offset receives
+ *                   token t; s < 0 marks a padding token, which is skipped.
+ *                   Contract: 0 <= s < num_blocks * block_size and no two
+ *                   tokens share a slot.
+ * Bytes are copied exactly; no slot other than the listed ones is touched.
+ * T == 0 is a no-op.
+ */
+pkv_status pkv_reshape_and_cache(const void *key, const void *value, void *k_cache,
+                                 void *v_cache, const int32_t *slot_mapping, int32_t T,
+                                 int64_t key_stride, int64_t value_stride, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 pkv_dtype dtype, void *stream);
+
+/*
+ * Bytes of workspace pkv_paged_decode needs for these sizes and this
+ * partition_size (after the automatic choice when partition_size is 0):
+ * float32 part_out [B, Hq, P, head_dim] and part_lse [B, Hq, P], with
+ * P = ceil(max_seqlen_k / partition), each 256-byte aligned.  Returns 0 when
+ * the call would not split.  Returns (size_t)-1 for invalid sizes.
+ */
+size_t pkv_paged_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size,
+                                        int32_t max_seqlen_k, int32_t partition_size);
+
+/* The partition size pkv_paged_decode uses for partition_size == 0 (a
+ * multiple of block_size), or 0 when it does not split these sizes. */
+int32_t pkv_paged_decode_auto_partition(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size,
+                                        int32_t max_seqlen_k);
+
+/*
+ * pkv_paged_decode -- one query token per sequence attending to its
+ * cache_seqlens[b] cached keys (Transformers doc, decode path; vLLM page,
+ * single_query_cached_kv_attention).  The query sits at position
+ * cache_seqlens[b] - 1: a token that is being generated must already have
+ * been stored with pkv_reshape_and_cache (write the cache, then attend, the
+ * order of PagedAttention.forward).
+ *
+ *   out             [B, num_q_heads, head_dim]
+ *   lse             [B, num_q_heads] float32, or NULL
+ *   q               [B, num_q_heads, head_dim]
+ *   block_table     [B, max_blocks_per_seq] int32
+ *   cache_seqlens   [B] int32.  Contract: 0 <= cache_seqlens[b] <=
+ *                   max_seqlen_k <= max_blocks_per_seq * block_size, and the
+ *                   first ceil(cache_seqlens[b] / block_size) entries of row b
+ *                   are valid block ids < num_blocks.
+ *   sink            [num_q_heads] float32, or NULL for none
+ *   max_seqlen_k    host upper bound on cache_seqlens (sizes the launch)
+ *   window_left     -1 for none, else >= 0
+ *   partition_size  0: automatic (may or may not split); > 0: split the keys
+ *                   into [p*P, (p+1)*P) partitions (a multiple of block_size),
+ *                   each reduced on its own, then merged by log-sum-exp.
+ *                   For a fixed partition size results are bitwise
+ *                   reproducible.
+ *   workspace       device buffer of at least
+ *                   pkv_paged_decode_workspace_bytes(...) bytes (may be NULL
+ *                   when that is 0).
+ */
+pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_cache,
+                            const void *v_cache, const int32_t *block_table,
+                            const int32_t *cache_seqlens, const float *sink, int32_t B,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                            int32_t max_seqlen_k, float sm_scale, int32_t window_left,
+                            int32_t partition_size, void *workspace, size_t workspace_bytes,
+                            pkv_dtype dtype, void *stream);
+
+/*
+ * pkv_paged_decode_partitions -- the first stage of split-KV decode (vLLM
+ * page, the paged_attention_v2 path that fills tmp_output / exp_sums /
+ * max_logits): for every sequence b, query head h and partition
+ * p < max_partitions, attention restricted to the visible keys in
+ * [p * partition_size, (p + 1) * partition_size), WITHOUT the sink:
+ *     part_out[b,h,p,:] = that partition's normalised output (0 if no key)
+ *     part_lse[b,h,p]   = ln of its softmax denominator (-inf if no key)
+ * pkv_merge_partitions then adds the sink once and combines them.
+ * pkv_paged_decode with partition_size > 0 is exactly these two calls.
+ *
+ *   part_out        [B, num_q_heads, max_partitions, head_dim] float32
+ *   part_lse        [B, num_q_heads, max_partitions] float32
+ *   max_partitions  >= ceil(max_seqlen_k / partition_size)
+ *   other arguments as for pkv_paged_decode (partition_size > 0, a multiple
+ *   of block_size).
+ */
+pkv_status pkv_paged_decode_partitions(float *part_out, float *part_lse, const void *q,
+                                       const void *k_cache, const void *v_cache,
+                                       const int32_t *block_table, const int32_t *cache_seqlens,
+                                       int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                       int32_t max_blocks_per_seq, int32_t max_seqlen_k,
+                                       float sm_scale, int32_t window_left,
+                                       int32_t partition_size, int32_t max_partitions,
+                                       pkv_dtype dtype, void *stream);
+
+/*
+ * pkv_merge_partitions -- combine split-KV partition results (vLLM page, the
+ * paged_attention_v2 path): for (b, h), with n_b = ceil(cache_seqlens[b] /
+ * partition_size) partitions and sink s (or -inf),
+ *     LSE = log(sum_{p < n_b} exp(part_lse[b,h,p]) + exp(s))
+ *     out = sum_{p < n_b} exp(part_lse[b,h,p] - LSE) * part_out[b,h,p,:]
+ * A partition with part_lse = -inf (no visible key) contributes nothing;
+ * entries p >= n_b are never read.  If every term is -inf, out = 0 and
+ * lse = -inf.
+ *
+ *   part_out        [B, num_q_heads, max_partitions, head_dim] float32, each
+ *                   row normalised over its own partition
+ *   part_lse        [B, num_q_heads, max_partitions] float32, natural log,
+ *                   sink excluded
+ *   cache_seqlens   [B] int32.  Contract: ceil(cache_seqlens[b] /
+ *                   partition_size) <= max_partitions.
+ *   out             [B, num_q_heads, head_dim] in dtype; lse [B, Hq] or NULL
+ */
+pkv_status pkv_merge_partitions(void *out, float *lse, const float *part_out,
+                                const float *part_lse, const int32_t *cache_seqlens,
+                                int32_t partition_size, const float *sink, int32_t B,
+                                int32_t num_q_heads, int32_t head_dim, int32_t max_partitions,
+                                pkv_dtype dtype, void *stream);
+
+/*
+ * pkv_varlen_prefill -- causal attention over packed variable-length requests
+ * (Transformers doc, varlen path; FlashInfer page, varlen branch).
+ *
+ *   out             [sum Lq, num_q_heads, head_dim]
+ *   lse             [sum Lq, num_q_heads] float32, or NULL
+ *   q               [sum Lq, num_q_heads, head_dim]
+ *   K/V, one of:
+ *     contiguous    k, v [sum Lk, num_kv_heads, head_dim]; request r's key j
+ *                   is row cu_seqlens_k[r] + j.  k_cache/v_cache/block_table
+ *                   must be NULL.
+ *     paged         k = v = NULL; k_cache, v_cache and block_table
+ *                   [B, max_blocks_per_seq] as for pkv_paged_decode; request
+ *                   r's key j is at block_table[r][j / block_size], offset
+ *                   j % block_size; cu_seqlens_k still gives Lk per request.
+ *   cu_seqlens_q/k  [B + 1] int32 exclusive prefix sums starting at 0.
+ *                   Contract: nondecreasing; every Lq <= max_seqlen_q and
+ *                   Lk <= max_seqlen_k (host upper bounds that size the
+ *                   launch); paged: Lk <= max_blocks_per_seq * block_size.
+ *   causal          must be 1 (bottom-right aligned: queries are the last Lq
+ *                   positions of the request's keys)
+ */
+pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *k, const void *v,
+                              const void *k_cache, const void *v_cache,
+                              const int32_t *block_table, int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, const int32_t *cu_seqlens_q,
+                              const int32_t *cu_seqlens_k, int32_t B, int32_t max_seqlen_q,
+                              int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, float sm_scale, int32_t causal,
+                              int32_t window_left, const float *sink, pkv_dtype dtype,
+                              void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,327 @@
+// extern "C" entry points of libpkv.so: argument checks on the host, workspace
+// sizing, the split-KV choice, and launches on the caller's stream.  The
+// operations and their arguments are documented in include/pkv.h.
+
+#include "common.h"
+#include "decode.h"
+
+using namespace pkv;
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int x) { int l = 0; while ((1 << l) < x) ++l; return l; }
+bool dtype_ok(pkv_dtype d) { return d == PKV_F32 || d == PKV_BF16; }
+int elem_bytes(pkv_dtype d) { return d == PKV_BF16 ? 2 : 4; }
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+pkv_status check_heads(int32_t Hq, int32_t Hkv, int32_t D) {
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return PKV_ERR_SHAPE;
+    if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
+    return PKV_OK;
+}
+
+pkv_status check_block_size(int32_t bs) {
+    if (bs <= 0) return PKV_ERR_SHAPE;
+    if (!is_pow2(bs) || bs < 16 || bs > 512) return PKV_ERR_UNSUPPORTED;
+    return PKV_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Partition used when the caller passes 0: split only when one unit per
+// (sequence, head group) would leave the 256 compute units short of work.
+int32_t auto_partition(int32_t B, int32_t Hq, int32_t Hkv, int32_t bs, int32_t max_seqlen_k) {
+    const int HU = decode_heads_per_unit(Hq / Hkv);
+    const long long units = (long long)B * (Hq / HU);
+    if (max_seqlen_k <= 512 || units >= 4096) return 0;
+    int32_t P = 512;
+    if (P % bs) P = bs;
+    return P;
+}
+
+struct SplitPlan {
+    int32_t part_size;   // tokens per partition (>= max_seqlen_k when not split)
+    int32_t nparts;
+    bool split;
+};
+
+SplitPlan plan_split(int32_t max_seqlen_k, int32_t partition_size) {
+    SplitPlan p{};
+    const int32_t msk = max_seqlen_k > 0 ? max_seqlen_k : 1;
+    if (partition_size <= 0 || partition_size >= msk) {
+        p.part_size = msk;
+        p.nparts = 1;
+        p.split = false;
+    } else {
+        p.part_size = partition_size;
+        p.nparts = (msk + partition_size - 1) / partition_size;
+        p.split = p.nparts > 1;
+    }
+    return p;
+}
+
+// Launch the decode kernel for one plan: the final output (no split) or
+// the per-partition results (split).
+pkv_status launch_decode_stage(void *out, float *lse, float *part_out, float *part_lse,
+                               const void *q, const void *k_cache, const void *v_cache,
+                               const int32_t *block_table, const int32_t *cache_seqlens,
+                               const float *sink, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                               int32_t block_size, int32_t mbps, float sm_scale,
+                               int32_t window_left, const SplitPlan &plan, pkv_dtype dtype,
+                               hipStream_t s)
+{
+    if (dtype == PKV_BF16) {
+        DecodeArgs a{};
+        a.out = out; a.lse = lse; a.part_out = part_out; a.part_lse = part_lse;
+        a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
+        a.block_table = block_table; a.seqlens = cache_seqlens; a.sink = sink;
+        a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D;
+        a.bs_log2 = ilog2(block_size); a.mbps = mbps; a.window_left = window_left;
+        a.part_size = plan.part_size; a.nparts = plan.nparts; a.split = plan.split ? 1 : 0;
+        a.scale_log2 = sm_scale * kLog2e;
+        return launch_decode_bf16(a, s);
+    }
+    RowArgs a{};
+    a.mode = 0; a.out = out; a.lse = lse; a.part_out = part_out; a.part_lse = part_lse;
+    a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.block_table = block_table;
+    a.seqlens = cache_seqlens; a.sink = sink; a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+    a.D = D; a.bs_log2 = ilog2(block_size); a.mbps = mbps; a.window_left = window_left;
+    a.part_size = plan.part_size; a.nparts = plan.nparts; a.split = plan.split ? 1 : 0;
+    a.scale_log2 = sm_scale * kLog2e;
+    return launch_rows(a, false, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pkv_status_string(pkv_status s) {
+    switch (s) {
+        case PKV_OK: return "ok";
+        case PKV_ERR_NULL: return "required pointer is NULL";
+        case PKV_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+        case PKV_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, dtype or mode";
+        case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+        case PKV_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+int pkv_version(void) { return kVersion; }
+
+pkv_status pkv_reshape_and_cache(const void *key, const void *value, void *k_cache,
+                                 void *v_cache, const int32_t *slot_mapping, int32_t T,
+                                 int64_t key_stride, int64_t value_stride, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 pkv_dtype dtype, void *stream)
+{
+    if (T < 0 || num_kv_heads <= 0 || num_blocks < 0) return PKV_ERR_SHAPE;
+    if (!dtype_ok(dtype)) return PKV_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    pkv_status st = check_block_size(block_size);
+    if (st != PKV_OK) return st;
+    if (T == 0) return PKV_OK;
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_NULL;
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    if (key_stride == 0) key_stride = row;
+    if (value_stride == 0) value_stride = row;
+    if (key_stride < row || value_stride < row) return PKV_ERR_SHAPE;
+    if (key_stride % 8 || value_stride % 8) return PKV_ERR_UNSUPPORTED;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PKV_ERR_UNSUPPORTED;
+    return launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, T, key_stride,
+                                    value_stride, num_kv_heads, head_dim, elem_bytes(dtype),
+                                    (hipStream_t)stream);
+}
+
+int32_t pkv_paged_decode_auto_partition(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size,
+                                        int32_t max_seqlen_k)
+{
+    if (B < 0 || max_seqlen_k < 0 || check_heads(num_q_heads, num_kv_heads, head_dim) != PKV_OK ||
+        check_block_size(block_size) != PKV_OK)
+        return 0;
+    return auto_partition(B, num_q_heads, num_kv_heads, block_size, max_seqlen_k);
+}
+
+size_t pkv_paged_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size,
+                                        int32_t max_seqlen_k, int32_t partition_size)
+{
+    if (B < 0 || max_seqlen_k < 0 || partition_size < 0) return (size_t)-1;
+    if (check_heads(num_q_heads, num_kv_heads, head_dim) != PKV_OK) return (size_t)-1;
+    if (check_block_size(block_size) != PKV_OK) return (size_t)-1;
+    if (partition_size == 0)
+        partition_size = auto_partition(B, num_q_heads, num_kv_heads, block_size, max_seqlen_k);
+    else if (partition_size % block_size)
+        return (size_t)-1;
+    const SplitPlan p = plan_split(max_seqlen_k, partition_size);
+    if (!p.split || B == 0) return 0;
+    const size_t rows = (size_t)B * num_q_heads * p.nparts;
+    return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_cache,
+                            const void *v_cache, const int32_t *block_table,
+                            const int32_t *cache_seqlens, const float *sink, int32_t B,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                            int32_t max_seqlen_k, float sm_scale, int32_t window_left,
+                            int32_t partition_size, void *workspace, size_t workspace_bytes,
+                            pkv_dtype dtype, void *stream)
+{
+    if (B < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_seqlen_k < 0)
+        return PKV_ERR_SHAPE;
+    pkv_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
+    if (st != PKV_OK) return st;
+    if ((st = check_block_size(block_size)) != PKV_OK) return st;
+    if (!dtype_ok(dtype)) return PKV_ERR_UNSUPPORTED;
+    if (window_left < -1 || partition_size < 0) return PKV_ERR_SHAPE;
+    if (partition_size > 0 && partition_size % block_size) return PKV_ERR_SHAPE;
+    if ((long long)max_seqlen_k > (long long)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
+    if (B == 0) return PKV_OK;
+    if (!out || !q || !block_table || !cache_seqlens) return PKV_ERR_NULL;
+    if (max_seqlen_k > 0 && (!k_cache || !v_cache)) return PKV_ERR_NULL;
+    if (max_seqlen_k > 0 && num_blocks == 0) return PKV_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
+
+    if (partition_size == 0)
+        partition_size =
+            auto_partition(B, num_q_heads, num_kv_heads, block_size, max_seqlen_k);
+    const SplitPlan plan = plan_split(max_seqlen_k, partition_size);
+    const size_t need = pkv_paged_decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_dim,
+                                                         block_size, max_seqlen_k,
+                                                         plan.split ? plan.part_size : 0);
+    if (plan.split && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+    if (plan.split && ((uintptr_t)workspace & 255u)) return PKV_ERR_WORKSPACE;
+
+    const size_t rows = (size_t)B * num_q_heads * plan.nparts;
+    float *part_out = plan.split ? (float *)workspace : nullptr;
+    float *part_lse =
+        plan.split ? (float *)((char *)workspace + align256(rows * head_dim * sizeof(float)))
+                   : nullptr;
+    hipStream_t s = (hipStream_t)stream;
+    st = launch_decode_stage(out, lse, part_out, part_lse, q, k_cache, v_cache, block_table,
+                             cache_seqlens, sink, B, num_q_heads, num_kv_heads, head_dim,
+                             block_size, max_blocks_per_seq, sm_scale, window_left, plan, dtype,
+                             s);
+    if (st != PKV_OK || !plan.split) return st;
+    MergeArgs m{};
+    m.out = out; m.lse = lse; m.part_out = part_out; m.part_lse = part_lse;
+    m.seqlens = cache_seqlens; m.sink = sink; m.B = B; m.Hq = num_q_heads; m.D = head_dim;
+    m.part_size = plan.part_size; m.nparts = plan.nparts; m.dtype = dtype;
+    return launch_merge(m, s);
+}
+
+pkv_status pkv_paged_decode_partitions(float *part_out, float *part_lse, const void *q,
+                                       const void *k_cache, const void *v_cache,
+                                       const int32_t *block_table, const int32_t *cache_seqlens,
+                                       int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                       int32_t max_blocks_per_seq, int32_t max_seqlen_k,
+                                       float sm_scale, int32_t window_left,
+                                       int32_t partition_size, int32_t max_partitions,
+                                       pkv_dtype dtype, void *stream)
+{
+    if (B < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_seqlen_k < 0)
+        return PKV_ERR_SHAPE;
+    pkv_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
+    if (st != PKV_OK) return st;
+    if ((st = check_block_size(block_size)) != PKV_OK) return st;
+    if (!dtype_ok(dtype)) return PKV_ERR_UNSUPPORTED;
+    if (window_left < -1 || partition_size <= 0 || partition_size % block_size)
+        return PKV_ERR_SHAPE;
+    if ((long long)max_seqlen_k > (long long)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
+    const long long need_parts = ((long long)max_seqlen_k + partition_size - 1) / partition_size;
+    if (max_partitions <= 0 || max_partitions < need_parts) return PKV_ERR_SHAPE;
+    if (B == 0) return PKV_OK;
+    if (!part_out || !part_lse || !q || !block_table || !cache_seqlens) return PKV_ERR_NULL;
+    if (max_seqlen_k > 0 && (!k_cache || !v_cache)) return PKV_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
+    SplitPlan plan{partition_size, max_partitions, true};
+    return launch_decode_stage(nullptr, nullptr, part_out, part_lse, q, k_cache, v_cache,
+                               block_table, cache_seqlens, nullptr, B, num_q_heads, num_kv_heads,
+                               head_dim, block_size, max_blocks_per_seq, sm_scale, window_left,
+                               plan, dtype, (hipStream_t)stream);
+}
+
+pkv_status pkv_merge_partitions(void *out, float *lse, const float *part_out,
+                                const float *part_lse, const int32_t *cache_seqlens,
+                                int32_t partition_size, const float *sink, int32_t B,
+                                int32_t num_q_heads, int32_t head_dim, int32_t max_partitions,
+                                pkv_dtype dtype, void *stream)
+{
+    if (B < 0 || num_q_heads <= 0 || max_partitions <= 0 || partition_size <= 0)
+        return PKV_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (!dtype_ok(dtype)) return PKV_ERR_UNSUPPORTED;
+    if (B == 0) return PKV_OK;
+    if (!out || !part_out || !part_lse || !cache_seqlens) return PKV_ERR_NULL;
+    MergeArgs m{};
+    m.out = out; m.lse = lse; m.part_out = part_out; m.part_lse = part_lse;
+    m.seqlens = cache_seqlens; m.sink = sink; m.B = B; m.Hq = num_q_heads; m.D = head_dim;
+    m.part_size = partition_size; m.nparts = max_partitions; m.dtype = dtype;
+    return launch_merge(m, (hipStream_t)stream);
+}
+
+pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *k, const void *v,
+                              const void *k_cache, const void *v_cache,
+                              const int32_t *block_table, int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, const int32_t *cu_seqlens_q,
+                              const int32_t *cu_seqlens_k, int32_t B, int32_t max_seqlen_q,
+                              int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, float sm_scale, int32_t causal,
+                              int32_t window_left, const float *sink, pkv_dtype dtype,
+                              void *stream)
+{
+    if (B < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return PKV_ERR_SHAPE;
+    pkv_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
+    if (st != PKV_OK) return st;
+    if (!dtype_ok(dtype) || causal != 1) return PKV_ERR_UNSUPPORTED;
+    if (window_left < -1) return PKV_ERR_SHAPE;
+    const bool contiguous = k != nullptr || v != nullptr;
+    const bool paged = k_cache != nullptr || v_cache != nullptr || block_table != nullptr;
+    if (contiguous && paged) return PKV_ERR_SHAPE;
+    if (paged) {
+        if ((st = check_block_size(block_size)) != PKV_OK) return st;
+        if (num_blocks < 0 || max_blocks_per_seq < 0) return PKV_ERR_SHAPE;
+        if ((long long)max_seqlen_k > (long long)max_blocks_per_seq * block_size)
+            return PKV_ERR_SHAPE;
+    }
+    if (B == 0 || max_seqlen_q == 0) return PKV_OK;
+    if (!out || !q || !cu_seqlens_q || !cu_seqlens_k) return PKV_ERR_NULL;
+    if (!contiguous && !paged) return PKV_ERR_NULL;
+    if (contiguous && (!k || !v)) return PKV_ERR_NULL;
+    if (paged && (!k_cache || !v_cache || !block_table)) return PKV_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(k) || !aligned16(v) ||
+        !aligned16(k_cache) || !aligned16(v_cache))
+        return PKV_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    const int bs_log2 = paged ? ilog2(block_size) : 0;
+
+    if (dtype == PKV_BF16) {
+        PrefillArgs a{};
+        a.out = out; a.lse = lse; a.q = q; a.k = k; a.v = v; a.k_cache = k_cache;
+        a.v_cache = v_cache; a.block_table = block_table; a.cu_q = cu_seqlens_q;
+        a.cu_k = cu_seqlens_k; a.sink = sink; a.B = B; a.Hq = num_q_heads; a.Hkv = num_kv_heads;
+        a.G = num_q_heads / num_kv_heads; a.D = head_dim; a.bs_log2 = bs_log2;
+        a.mbps = max_blocks_per_seq; a.window_left = window_left;
+        a.max_q_tiles = (max_seqlen_q + prefill_block_m() - 1) / prefill_block_m();
+        a.scale_log2 = sm_scale * kLog2e;
+        return launch_prefill_bf16(a, s);
+    }
+    // fp32: one wave per (request, row < max_seqlen_q, head)
+    RowArgs a{};
+    a.mode = 1; a.out = out; a.lse = lse; a.q = q; a.k = k; a.v = v; a.k_cache = k_cache;
+    a.v_cache = v_cache; a.block_table = block_table; a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+    a.sink = sink; a.B = B; a.Hq = num_q_heads; a.Hkv = num_kv_heads;
+    a.G = num_q_heads / num_kv_heads; a.D = head_dim; a.bs_log2 = bs_log2;
+    a.mbps = max_blocks_per_seq; a.window_left = window_left; a.scale_log2 = sm_scale * kLog2e;
+    a.T = max_seqlen_q;
+    return launch_rows(a, false, s);
+}
+
+}  // extern "C"

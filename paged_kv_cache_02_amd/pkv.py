@@ -1,0 +1,221 @@
+"""Thin ctypes binding of libpkv.so (see include/pkv.h for the operations).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's kernels.  The
+library must have been built (``python -m paged_kv_cache_02_amd.build``);
+importing this module without it raises ``ImportError`` -- there is no other
+implementation to fall back to.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = range(6)
+PKV_F32, PKV_BF16 = 0, 1
+
+# name -> (restype, argtypes), in the order of include/pkv.h
+_P, _I32, _I64, _SZ, _F = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                           ctypes.c_float)
+SIGNATURES = {
+    "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pkv_version": (ctypes.c_int, []),
+    "pkv_reshape_and_cache": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I32, _I32,
+                                             _I32, _I32, ctypes.c_int, _P]),
+    "pkv_paged_decode_workspace_bytes": (ctypes.c_size_t, [_I32] * 7),
+    "pkv_paged_decode_auto_partition": (ctypes.c_int32, [_I32] * 6),
+    "pkv_paged_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                        _I32, _I32, _I32, _I32, _F, _I32, _I32, _P, _SZ,
+                                        ctypes.c_int, _P]),
+    "pkv_paged_decode_partitions": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                                   _I32, _I32, _I32, _I32, _I32, _F, _I32, _I32,
+                                                   _I32, ctypes.c_int, _P]),
+    "pkv_merge_partitions": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32,
+                                            _I32, ctypes.c_int, _P]),
+    "pkv_varlen_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P,
+                                          _P, _I32, _I32, _I32, _I32, _I32, _I32, _F, _I32,
+                                          _I32, _P, ctypes.c_int, _P]),
+}
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m paged_kv_cache_02_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = load_library()
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib.pkv_status_string(status).decode()} (status {status})")
+
+
+def _check(status: int, what: str):
+    if status != PKV_OK:
+        raise PkvError(status, what)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    if t.dtype == torch.float32:
+        return PKV_F32
+    raise ValueError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.int32:
+        raise ValueError(f"{name} must be int32")
+    return t
+
+
+def _f32(t: Optional[torch.Tensor], name: str) -> Optional[torch.Tensor]:
+    if t is not None and t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32")
+    return t
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def version() -> int:
+    return lib.pkv_version()
+
+
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping):
+    """Store rows key/value [T, Hkv, D] into the caches at slot_mapping [T]."""
+    T, Hkv, D = key.shape
+    NB, bs = k_cache.shape[0], k_cache.shape[1]
+    if not (key.is_cuda and value.is_cuda):
+        raise ValueError("tensors must be on the GPU")
+    ks = key.stride(0) if key.dim() == 3 and key[0].is_contiguous() else None
+    vs = value.stride(0) if value.dim() == 3 and value[0].is_contiguous() else None
+    if ks is None or vs is None:
+        raise ValueError("key/value rows must be contiguous [Hkv, D] blocks")
+    _check(lib.pkv_reshape_and_cache(
+        key.data_ptr(), value.data_ptr(), _ptr(k_cache), _ptr(v_cache),
+        _ptr(_i32(slot_mapping, "slot_mapping")), T, ks, vs, Hkv, D, bs, NB, _dt(key), _stream()),
+        "reshape_and_cache")
+
+
+def decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_dim, block_size, max_seqlen_k,
+                           partition_size=0) -> int:
+    n = lib.pkv_paged_decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_dim, block_size,
+                                             max_seqlen_k, partition_size)
+    if n == ctypes.c_size_t(-1).value:
+        raise PkvError(PKV_ERR_SHAPE, "paged_decode_workspace_bytes")
+    return n
+
+
+def decode_auto_partition(B, num_q_heads, num_kv_heads, head_dim, block_size, max_seqlen_k) -> int:
+    return lib.pkv_paged_decode_auto_partition(B, num_q_heads, num_kv_heads, head_dim,
+                                               block_size, max_seqlen_k)
+
+
+def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: float, sink=None,
+                 window_left: int = -1, partition_size: int = 0,
+                 max_seqlen_k: Optional[int] = None, out=None, lse=None, workspace=None):
+    """out [B,Hq,D] for q [B,Hq,D] over k/v_cache [NB,bs,Hkv,D]."""
+    B, Hq, D = q.shape
+    NB, bs, Hkv, _ = k_cache.shape
+    if max_seqlen_k is None:
+        max_seqlen_k = int(cache_seqlens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_workspace_bytes(B, Hq, Hkv, D, bs, max_seqlen_k, partition_size)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib.pkv_paged_decode(
+        _ptr(out), _ptr(_f32(lse, "lse")), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        _ptr(_i32(block_table, "block_table")), _ptr(_i32(cache_seqlens, "cache_seqlens")),
+        _ptr(_f32(sink, "sink")), B, Hq, Hkv, D, bs, NB, block_table.shape[1], max_seqlen_k,
+        float(sm_scale), window_left, partition_size, _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _dt(q),
+        _stream()), "paged_decode")
+    return out
+
+
+def paged_decode_partitions(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: float,
+                            partition_size: int, max_seqlen_k: int, window_left: int = -1,
+                            part_out=None, part_lse=None):
+    """Per-partition results (sink excluded): part_out [B,Hq,P,D], part_lse [B,Hq,P]."""
+    B, Hq, D = q.shape
+    NB, bs, Hkv, _ = k_cache.shape
+    P = max(1, (max_seqlen_k + partition_size - 1) // partition_size)
+    if part_out is None:
+        part_out = torch.empty((B, Hq, P, D), dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty((B, Hq, P), dtype=torch.float32, device=q.device)
+    _check(lib.pkv_paged_decode_partitions(
+        _ptr(_f32(part_out, "part_out")), _ptr(_f32(part_lse, "part_lse")), _ptr(q),
+        _ptr(k_cache), _ptr(v_cache), _ptr(_i32(block_table, "block_table")),
+        _ptr(_i32(cache_seqlens, "cache_seqlens")), B, Hq, Hkv, D, bs, NB, block_table.shape[1],
+        max_seqlen_k, float(sm_scale), window_left, partition_size, part_out.shape[2], _dt(q),
+        _stream()), "paged_decode_partitions")
+    return part_out, part_lse
+
+
+def merge_partitions(part_out, part_lse, cache_seqlens, partition_size: int, sink=None,
+                     out_dtype=torch.bfloat16, out=None, lse=None):
+    """out [B,Hq,D] from part_out [B,Hq,P,D] / part_lse [B,Hq,P] (float32)."""
+    B, Hq, P, D = part_out.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=part_out.device)
+    _check(lib.pkv_merge_partitions(
+        _ptr(out), _ptr(_f32(lse, "lse")), _ptr(_f32(part_out, "part_out")),
+        _ptr(_f32(part_lse, "part_lse")), _ptr(_i32(cache_seqlens, "cache_seqlens")),
+        partition_size, _ptr(_f32(sink, "sink")), B, Hq, D, P, _dt(out), _stream()),
+        "merge_partitions")
+    return out
+
+
+def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                   sm_scale: float, num_kv_heads: Optional[int] = None, k=None, v=None,
+                   k_cache=None, v_cache=None, block_table=None, sink=None,
+                   window_left: int = -1, out=None, lse=None):
+    """Causal varlen prefill: out [sum Lq, Hq, D]."""
+    T, Hq, D = q.shape
+    B = cu_seqlens_q.shape[0] - 1
+    if k is not None:
+        Hkv = k.shape[1]
+        bs = NB = MB = 0
+    else:
+        NB, bs, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+        MB = block_table.shape[1]
+    if num_kv_heads is not None and num_kv_heads != Hkv:
+        raise ValueError("num_kv_heads does not match the K/V tensors")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.pkv_varlen_prefill(
+        _ptr(out), _ptr(_f32(lse, "lse")), _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache),
+        _ptr(v_cache), _ptr(None if block_table is None else _i32(block_table, "block_table")),
+        bs, NB, MB, _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")),
+        _ptr(_i32(cu_seqlens_k, "cu_seqlens_k")), B, int(max_seqlen_q), int(max_seqlen_k), Hq,
+        Hkv, D, float(sm_scale), 1, window_left, _ptr(_f32(sink, "sink")), _dt(q), _stream()),
+        "varlen_prefill")
+    return out

@@ -1,0 +1,137 @@
+"""Varlen causal prefill (contiguous and paged K/V) on the GPU against the fp64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import assert_close, banner, dev, oracle_prefill, run_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+def test_config1_prefill_fp32():
+    banner("config1 prefill")
+    c = synth.config1_prefill()
+    out, lse = run_prefill(c)
+    o, l = oracle_prefill(c)
+    assert_close(out, o, torch.float32, "config1 prefill")
+    assert_close(lse, l, torch.float32, "config1 lse", lse=True)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_page_example_lengths(dtype):
+    """The doc's varlen example lengths: q [10,3,1] over k [0,1,7]; rows
+    that see no key give 0 (lse = sink)."""
+    banner(f"page varlen example {dtype}")
+    c = synth.prefill_case(3, [10, 3, 1], [0, 1, 7], 4, 2, 64, dtype, True)
+    out, lse = run_prefill(c)
+    o, l = oracle_prefill(c)
+    assert (out.float().cpu()[:12] == 0).all()
+    assert_close(out, o, dtype, "page example")
+    assert_close(lse, l, dtype, "page example lse", lse=True)
+
+
+def test_request_tag_probe():
+    """q = 0 gives uniform weights over the visible keys; V = 2^r for every
+    key of request r, so each output is 2^r and names the request whose keys
+    were read (cu_seqlens_k indexing); no sink."""
+    banner("request tag probe")
+    lens = [37, 1, 130, 64, 200]
+    c = synth.prefill_case(4, lens, lens, 8, 2, 128, torch.bfloat16, False)
+    c.q.zero_()
+    cu = c.cu_seqlens_k.tolist()
+    for r in range(len(lens)):
+        c.v[cu[r]:cu[r + 1]] = float(2 ** r)
+    out, _ = run_prefill(c, with_lse=False)
+    out = out.float().cpu()
+    for r in range(len(lens)):
+        assert (out[cu[r]:cu[r + 1]] == float(2 ** r)).all(), r
+
+
+CASES = [
+    # q_lens, k_lens, Hq, Hkv, D, sink, window
+    ([1, 5, 128, 129, 300], None, 8, 2, 128, True, -1),
+    ([64, 255, 256, 257], None, 32, 8, 128, False, -1),
+    ([100, 513], None, 16, 16, 64, True, -1),
+    ([200, 77, 400], None, 8, 1, 64, True, 31),
+    ([130, 20], [500, 20], 8, 4, 128, True, -1),           # chunk: queries at the end
+    ([0, 33, 1], [10, 40, 1000], 4, 2, 128, True, 64),
+    ([300], None, 4, 4, 128, True, 0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_prefill_contiguous_vs_oracle(case, dtype):
+    q_lens, k_lens, Hq, Hkv, D, sink, window = case
+    banner(f"prefill contiguous {dtype} {case}")
+    c = synth.prefill_case(40 + len(q_lens), q_lens, k_lens or q_lens, Hq, Hkv, D, dtype, sink,
+                           window_left=window)
+    out, lse = run_prefill(c)
+    o, l = oracle_prefill(c)
+    assert_close(out, o, dtype, "out")
+    assert_close(lse, l, dtype, "lse", lse=True)
+
+
+PAGED = [
+    ([64, 100], [64 + 300, 100], 16, 8, 64, 16, True, 128),
+    ([512, 3], [1000, 700], 8, 2, 128, 32, True, -1),
+    ([129, 1], [129, 2000], 8, 8, 128, 64, False, 17),
+]
+
+
+@pytest.mark.parametrize("case", PAGED, ids=[str(i) for i in range(len(PAGED))])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_prefill_paged_vs_oracle(case, dtype):
+    q_lens, k_lens, Hq, Hkv, D, bs, sink, window = case
+    banner(f"prefill paged {dtype} {case}")
+    c = synth.paged_prefill_case(60 + len(q_lens), q_lens, k_lens, Hq, Hkv, D, bs, dtype, sink,
+                                 window_left=window, poison=True)
+    out, lse = run_prefill(c)
+    o, l = oracle_prefill(c)
+    assert_close(out, o, dtype, "out")
+    assert_close(lse, l, dtype, "lse", lse=True)
+
+
+def test_prefill_deterministic():
+    banner("prefill determinism")
+    c = synth.prefill_case(70, [300, 1000], [300, 1000], 32, 8, 128, torch.bfloat16, True)
+    o1, l1 = run_prefill(c)
+    o2, l2 = run_prefill(c)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_config3_full_size_sampled():
+    """bf16 varlen causal prefill at full size: 8 requests of 256..4096
+    tokens, 32/8 heads, D 128, sink; 256 sampled (token, head) rows."""
+    banner("config3 full size")
+    c = synth.config3_prefill()
+    out, lse = run_prefill(c)
+    rng = np.random.default_rng(2)
+    T = c.q.shape[0]
+    units = np.sort(rng.choice(T * c.Hq, 256, replace=False))
+    # always include each request's first and last row
+    cu = c.cu_seqlens_q.tolist()
+    extra = [cu[r] * c.Hq for r in range(c.B)] + [(cu[r + 1] - 1) * c.Hq + c.Hq - 1
+                                                  for r in range(c.B)]
+    units = np.unique(np.concatenate([units, extra]))
+    o, l = oracle_prefill(c, units=units)
+    t, h = units // c.Hq, units % c.Hq
+    assert_close(out.float().cpu()[t, h], o[t, h], torch.bfloat16, "config3 sampled")
+    assert_close(lse.cpu()[t, h], l[t, h], torch.bfloat16, "config3 lse", lse=True)
+
+
+def test_config4_full_size_sampled():
+    """bf16 chunked prefill at full size: 4 x (512 queries after 8192 cached
+    keys), paged bs 16, window 128, 64/8 heads, D 64, sink; sampled rows."""
+    banner("config4 full size")
+    c = synth.config4_chunked()
+    out, lse = run_prefill(c)
+    rng = np.random.default_rng(3)
+    T = c.q.shape[0]
+    units = np.sort(rng.choice(T * c.Hq, 512, replace=False))
+    o, l = oracle_prefill(c, units=units)
+    t, h = units // c.Hq, units % c.Hq
+    assert_close(out.float().cpu()[t, h], o[t, h], torch.bfloat16, "config4 sampled")
+    assert_close(lse.cpu()[t, h], l[t, h], torch.bfloat16, "config4 lse", lse=True)
