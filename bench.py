@@ -42,7 +42,8 @@ def parse():
                    choices=["all", "decode", "prefill", "chunked", "longctx", "none"])
     p.add_argument("--skip-long", action="store_true", help="skip the 131072-token workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--partition-size", type=int, default=0, help="decode partition (0 = auto)")
+    p.add_argument("--partition-size", type=int, default=0,
+                   help="headline decode partition size (0 = automatic balanced schedule)")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="also run a plain device copy of this size (counter calibration)")
     return p.parse_args()
@@ -67,29 +68,48 @@ def log(msg):
 
 
 class KernelTimer:
-    """Pairs of HIP events on torch's current stream around named launches."""
+    """HIP events on torch's current stream at launch boundaries.
 
-    def __init__(self):
-        self.pairs = {}
+    Events are preallocated and shared between neighbouring launches (the
+    event that ends one launch starts the next), so a two-kernel step costs
+    two event records, not four."""
+
+    def __init__(self, n=0):
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        self.marks = []      # (name, start index, end index)
+        self.k = 0
+
+    def _next(self):
+        if self.k == len(self.events):
+            self.events.append(torch.cuda.Event(enable_timing=True))
+        e = self.events[self.k]
+        self.k += 1
+        e.record()
+        return self.k - 1
 
     def time(self, name, fn):
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
+        if self.k == 0 or not self.marks or self.marks[-1][2] != self.k - 1:
+            self._next()
+        start = self.k - 1
         r = fn()
-        e.record()
-        self.pairs.setdefault(name, []).append((s, e))
+        end = self._next()
+        self.marks.append((name, start, end))
         return r
 
     def mean_ms(self, name):
-        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs[name]]))
+        return float(np.mean([self.events[a].elapsed_time(self.events[b])
+                              for n, a, b in self.marks if n == name]))
+
+    def names(self):
+        return {n for n, _, _ in self.marks}
 
 
-def timed_steps(step, steps, warmup):
+def timed_steps(step, steps, warmup, launches_per_step=2):
     """Run warmup + timed steps; returns (ms per step, KernelTimer of the timed steps)."""
     for i in range(warmup):
-        step(i, KernelTimer())
+        step(i, KernelTimer(4))
+    kt = KernelTimer(steps * launches_per_step + 1)
     torch.cuda.synchronize()
-    kt = KernelTimer()
     t0 = time.perf_counter()
     for i in range(steps):
         step(i, kt)
@@ -128,6 +148,8 @@ def replicate_pool(c, reps):
 
 
 def bench_decode(c, name, steps, warmup, partition_size, reps):
+    """partition_size 0: the automatic (balanced) schedule, timed as its two
+    launches -- decode stage and merge; > 0: fixed partitions + merge."""
     B, Hq, D = c.B, c.Hq, c.D
     kc, vc, tables = replicate_pool(c, reps)
     q = c.q.cuda()
@@ -135,15 +157,22 @@ def bench_decode(c, name, steps, warmup, partition_size, reps):
     sink = None if c.sink is None else c.sink.cuda()
     out = torch.empty_like(q)
     msk = c.max_seqlen_k
-    P = partition_size or pkv.decode_auto_partition(B, Hq, c.Hkv, D, c.block_size, msk)
+    P = partition_size
+    ws_bytes = pkv.decode_workspace_bytes(B, Hq, c.Hkv, D, c.block_size, msk, P, q.dtype)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     split = P > 0 and P < msk
     nparts = (msk + P - 1) // P if split else 1
-    part_out = torch.empty((B, Hq, nparts, D), dtype=torch.float32, device="cuda")
-    part_lse = torch.empty((B, Hq, nparts), dtype=torch.float32, device="cuda")
+    if split:
+        part_out = torch.empty((B, Hq, nparts, D), dtype=torch.float32, device="cuda")
+        part_lse = torch.empty((B, Hq, nparts), dtype=torch.float32, device="cuda")
 
     def step(i, kt):
         bt = tables[i % reps]
-        if split:
+        if P == 0:
+            kt.time("decode", lambda: pkv.paged_decode_stage(q, kc, vc, bt, sl, c.sm_scale, msk,
+                                                             ws, c.window_left))
+            kt.time("merge", lambda: pkv.paged_decode_finish(out, ws, c.Hkv, sink=sink))
+        elif split:
             kt.time("decode", lambda: pkv.paged_decode_partitions(
                 q, kc, vc, bt, sl, c.sm_scale, P, msk, c.window_left, part_out, part_lse))
             kt.time("merge", lambda: pkv.merge_partitions(part_out, part_lse, sl, P, sink=sink,
@@ -151,21 +180,23 @@ def bench_decode(c, name, steps, warmup, partition_size, reps):
         else:
             kt.time("decode", lambda: pkv.paged_decode(q, kc, vc, bt, sl, c.sm_scale, sink=sink,
                                                        window_left=c.window_left,
-                                                       max_seqlen_k=msk, out=out))
+                                                       partition_size=P, max_seqlen_k=msk,
+                                                       out=out))
 
     ms, kt = timed_steps(step, steps, warmup)
     kv, qb, table = decode_bytes(c)
     step_bytes = kv + 2 * qb + table
     dec_ms = kt.mean_ms("decode")
-    dec_bytes = kv + qb + table + (0 if split else qb)
+    two = "merge" in kt.names()
+    dec_bytes = kv + qb + table + (0 if two else qb)
     res = {
         "name": name, "value": round(step_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
         "ms_per_step": round(ms, 4), "algorithmic_bytes": step_bytes,
-        "partition_size": P if split else 0, "nparts": nparts,
+        "schedule": "balanced" if P == 0 else (f"partitions of {P}" if split else "unsplit"),
         "kernels_ms": {"decode": round(dec_ms, 4)},
         "roofline": roofline("hbm", dec_bytes / (dec_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
     }
-    if split:
+    if two:
         res["kernels_ms"]["merge"] = round(kt.mean_ms("merge"), 4)
     res["frac_of_hbm_peak_step"] = round(res["value"] / HBM_PEAK_GBS, 4)
     del kc, vc, tables
@@ -324,9 +355,14 @@ def main():
     if ARGS.only in ("all", "longctx") and not ARGS.skip_long:
         log("long-context decode workload (16 x 131072, bs 64, partitions of 512, sink)")
         c5 = synth.config5_split_decode()
-        r5, out5 = bench_decode(c5, "split_decode_16x131072", max(3, steps // 4), 2, 512, reps=1)
+        # the workload asks for 512-token partitions merged by log-sum-exp
+        r5, out5 = bench_decode(c5, "split_decode_16x131072_P512", max(3, steps // 4), 2, 512,
+                                reps=1)
         workloads["split_decode_long"] = r5
-        log(f"long decode: {r5['value']} GB/s")
+        r5b, _ = bench_decode(c5, "split_decode_16x131072_auto", max(3, steps // 4), 2, 0,
+                              reps=1)
+        workloads["split_decode_long_auto"] = r5b
+        log(f"long decode: {r5['value']} GB/s (P=512), {r5b['value']} GB/s (auto)")
         del c5
     if ARGS.copy_calibration_mb:
         n = ARGS.copy_calibration_mb * (1 << 20) // 4
@@ -348,7 +384,7 @@ def main():
                                             "block_size 16, shuffled pool, no sink, no window",
                                 "global_batch": 64, "seq_len": "U[512,4096]",
                                 "parallelism": "single GPU",
-                                "partition_size": head["partition_size"]},
+                                "schedule": head["schedule"]},
                      "roofline": head["roofline"], "kernels_ms": head["kernels_ms"],
                      "frac_of_hbm_peak_step": head["frac_of_hbm_peak_step"]})
         if not ARGS.no_cpu_baseline:

@@ -111,21 +111,22 @@ pkv_status pkv_reshape_and_cache(const void *key, const void *value, void *k_cac
                                  pkv_dtype dtype, void *stream);
 
 /*
- * Bytes of workspace pkv_paged_decode needs for these sizes and this
- * partition_size (after the automatic choice when partition_size is 0):
- * float32 part_out [B, Hq, P, head_dim] and part_lse [B, Hq, P], with
- * P = ceil(max_seqlen_k / partition), each 256-byte aligned.  Returns 0 when
- * the call would not split.  Returns (size_t)-1 for invalid sizes.
+ * Bytes of workspace pkv_paged_decode needs for these sizes, this
+ * partition_size and dtype; 0 when the call needs none.  Returns (size_t)-1
+ * for invalid sizes.  The result does not depend on the sequence lengths
+ * (device data), only on the arguments here and on the current device:
+ *   - partition_size > 0 and max_seqlen_k > partition_size: float32 part_out
+ *     [B, Hq, P, head_dim] and part_lse [B, Hq, P], P = ceil(max_seqlen_k /
+ *     partition_size), each 256-byte aligned;
+ *   - partition_size == 0, bf16: the balanced schedule's partial results,
+ *     (4 * W + B) * Hq * (head_dim + 1) floats plus B + 2 ints (W grows with
+ *     the device's compute-unit count), for any B up to 4096;
+ *   - otherwise 0.
  */
 size_t pkv_paged_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t block_size,
-                                        int32_t max_seqlen_k, int32_t partition_size);
-
-/* The partition size pkv_paged_decode uses for partition_size == 0 (a
- * multiple of block_size), or 0 when it does not split these sizes. */
-int32_t pkv_paged_decode_auto_partition(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
-                                        int32_t head_dim, int32_t block_size,
-                                        int32_t max_seqlen_k);
+                                        int32_t max_seqlen_k, int32_t partition_size,
+                                        pkv_dtype dtype);
 
 /*
  * pkv_paged_decode -- one query token per sequence attending to its
@@ -146,11 +147,14 @@ int32_t pkv_paged_decode_auto_partition(int32_t B, int32_t num_q_heads, int32_t 
  *   sink            [num_q_heads] float32, or NULL for none
  *   max_seqlen_k    host upper bound on cache_seqlens (sizes the launch)
  *   window_left     -1 for none, else >= 0
- *   partition_size  0: automatic (may or may not split); > 0: split the keys
- *                   into [p*P, (p+1)*P) partitions (a multiple of block_size),
- *                   each reduced on its own, then merged by log-sum-exp.
- *                   For a fixed partition size results are bitwise
- *                   reproducible.
+ *   partition_size  > 0: split the keys into [p*P, (p+1)*P) partitions (a
+ *                   multiple of block_size), each reduced on its own, then
+ *                   merged by log-sum-exp.  0: automatic -- bf16 uses a balanced
+ *                   schedule that gives every wave of the device an equal share
+ *                   of all sequences' key tiles and merges the pieces the same
+ *                   way (B <= 4096); fp32 (and larger B) does not split.
+ *                   Results are bitwise reproducible for fixed arguments on a
+ *                   given device.
  *   workspace       device buffer of at least
  *                   pkv_paged_decode_workspace_bytes(...) bytes (may be NULL
  *                   when that is 0).
@@ -163,6 +167,34 @@ pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_
                             int32_t max_seqlen_k, float sm_scale, int32_t window_left,
                             int32_t partition_size, void *workspace, size_t workspace_bytes,
                             pkv_dtype dtype, void *stream);
+
+/*
+ * The two stages of pkv_paged_decode with partition_size == 0 in bf16 (the
+ * balanced schedule), for callers that want to time or overlap them:
+ *   pkv_paged_decode_stage   every wave of the device takes an equal share of
+ *                            all sequences' key tiles and writes one partial
+ *                            result (normalised output + lse, sink left out)
+ *                            per sequence it touches into `workspace`;
+ *   pkv_paged_decode_finish  log-sum-exp merge of those pieces with the sink
+ *                            into out / lse (same formula as
+ *                            pkv_merge_partitions).
+ * Arguments mean what they mean for pkv_paged_decode; `workspace` must hold
+ * pkv_paged_decode_workspace_bytes(..., partition_size = 0, PKV_BF16) bytes,
+ * and finish must run after stage (stream order) with the same B,
+ * num_q_heads, num_kv_heads, head_dim and workspace.  The workspace layout is
+ * private to the library.  dtype must be PKV_BF16 and B <= 4096.
+ */
+pkv_status pkv_paged_decode_stage(const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *block_table, const int32_t *cache_seqlens,
+                                  int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_seqlen_k,
+                                  float sm_scale, int32_t window_left, void *workspace,
+                                  size_t workspace_bytes, pkv_dtype dtype, void *stream);
+pkv_status pkv_paged_decode_finish(void *out, float *lse, const float *sink, int32_t B,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   const void *workspace, size_t workspace_bytes,
+                                   pkv_dtype dtype, void *stream);
 
 /*
  * pkv_paged_decode_partitions -- the first stage of split-KV decode (vLLM

@@ -5,6 +5,8 @@
 #include "common.h"
 #include "decode.h"
 
+#include <algorithm>
+
 using namespace pkv;
 
 namespace {
@@ -31,15 +33,42 @@ pkv_status check_block_size(int32_t bs) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Partition used when the caller passes 0: split only when one unit per
-// (sequence, head group) would leave the 256 compute units short of work.
-int32_t auto_partition(int32_t B, int32_t Hq, int32_t Hkv, int32_t bs, int32_t max_seqlen_k) {
-    const int HU = decode_heads_per_unit(Hq / Hkv);
-    const long long units = (long long)B * (Hq / HU);
-    if (max_seqlen_k <= 512 || units >= 4096) return 0;
-    int32_t P = 512;
-    if (P % bs) P = bs;
-    return P;
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Balanced schedule: two resident 4-wave workgroups per compute unit, spread
+// over the head groups.
+int stream_wgs_per_head_group(int Hq, int Hkv) {
+    const int NHG = Hq / decode_heads_per_unit(Hq / Hkv);
+    return std::max(1, (2 * device_cus() + NHG - 1) / NHG);
+}
+
+struct StreamLayout {
+    size_t part_out, part_lse, cum, total;
+};
+StreamLayout stream_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t D) {
+    const size_t slots = (size_t)stream_wgs_per_head_group(Hq, Hkv) * 4 + B;
+    StreamLayout l;
+    l.part_out = 0;
+    l.part_lse = align256(slots * Hq * D * sizeof(float));
+    l.cum = l.part_lse + align256(slots * Hq * sizeof(float));
+    l.total = l.cum + align256((size_t)(B + 2) * sizeof(int32_t));
+    return l;
+}
+bool use_stream(pkv_dtype dtype, int32_t B, int32_t partition_size, int32_t max_seqlen_k) {
+    return dtype == PKV_BF16 && partition_size == 0 && B <= kStreamMaxB && max_seqlen_k > 0;
 }
 
 struct SplitPlan {
@@ -137,29 +166,21 @@ pkv_status pkv_reshape_and_cache(const void *key, const void *value, void *k_cac
                                     (hipStream_t)stream);
 }
 
-int32_t pkv_paged_decode_auto_partition(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
-                                        int32_t head_dim, int32_t block_size,
-                                        int32_t max_seqlen_k)
-{
-    if (B < 0 || max_seqlen_k < 0 || check_heads(num_q_heads, num_kv_heads, head_dim) != PKV_OK ||
-        check_block_size(block_size) != PKV_OK)
-        return 0;
-    return auto_partition(B, num_q_heads, num_kv_heads, block_size, max_seqlen_k);
-}
-
 size_t pkv_paged_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t block_size,
-                                        int32_t max_seqlen_k, int32_t partition_size)
+                                        int32_t max_seqlen_k, int32_t partition_size,
+                                        pkv_dtype dtype)
 {
     if (B < 0 || max_seqlen_k < 0 || partition_size < 0) return (size_t)-1;
     if (check_heads(num_q_heads, num_kv_heads, head_dim) != PKV_OK) return (size_t)-1;
     if (check_block_size(block_size) != PKV_OK) return (size_t)-1;
-    if (partition_size == 0)
-        partition_size = auto_partition(B, num_q_heads, num_kv_heads, block_size, max_seqlen_k);
-    else if (partition_size % block_size)
-        return (size_t)-1;
+    if (!dtype_ok(dtype)) return (size_t)-1;
+    if (partition_size > 0 && partition_size % block_size) return (size_t)-1;
+    if (B == 0) return 0;
+    if (use_stream(dtype, B, partition_size, max_seqlen_k))
+        return stream_layout(B, num_q_heads, num_kv_heads, head_dim).total;
     const SplitPlan p = plan_split(max_seqlen_k, partition_size);
-    if (!p.split || B == 0) return 0;
+    if (!p.split) return 0;
     const size_t rows = (size_t)B * num_q_heads * p.nparts;
     return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
 }
@@ -188,22 +209,29 @@ pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_
     if (max_seqlen_k > 0 && num_blocks == 0) return PKV_ERR_SHAPE;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
 
-    if (partition_size == 0)
-        partition_size =
-            auto_partition(B, num_q_heads, num_kv_heads, block_size, max_seqlen_k);
-    const SplitPlan plan = plan_split(max_seqlen_k, partition_size);
+    hipStream_t s = (hipStream_t)stream;
     const size_t need = pkv_paged_decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_dim,
                                                          block_size, max_seqlen_k,
-                                                         plan.split ? plan.part_size : 0);
-    if (plan.split && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
-    if (plan.split && ((uintptr_t)workspace & 255u)) return PKV_ERR_WORKSPACE;
+                                                         partition_size, dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+    if (need > 0 && ((uintptr_t)workspace & 255u)) return PKV_ERR_WORKSPACE;
 
+    if (use_stream(dtype, B, partition_size, max_seqlen_k)) {
+        st = pkv_paged_decode_stage(q, k_cache, v_cache, block_table, cache_seqlens, B,
+                                    num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                    max_blocks_per_seq, max_seqlen_k, sm_scale, window_left,
+                                    workspace, workspace_bytes, dtype, stream);
+        if (st != PKV_OK) return st;
+        return pkv_paged_decode_finish(out, lse, sink, B, num_q_heads, num_kv_heads, head_dim,
+                                       workspace, workspace_bytes, dtype, stream);
+    }
+
+    const SplitPlan plan = plan_split(max_seqlen_k, partition_size);
     const size_t rows = (size_t)B * num_q_heads * plan.nparts;
     float *part_out = plan.split ? (float *)workspace : nullptr;
     float *part_lse =
         plan.split ? (float *)((char *)workspace + align256(rows * head_dim * sizeof(float)))
                    : nullptr;
-    hipStream_t s = (hipStream_t)stream;
     st = launch_decode_stage(out, lse, part_out, part_lse, q, k_cache, v_cache, block_table,
                              cache_seqlens, sink, B, num_q_heads, num_kv_heads, head_dim,
                              block_size, max_blocks_per_seq, sm_scale, window_left, plan, dtype,
@@ -214,6 +242,65 @@ pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_
     m.seqlens = cache_seqlens; m.sink = sink; m.B = B; m.Hq = num_q_heads; m.D = head_dim;
     m.part_size = plan.part_size; m.nparts = plan.nparts; m.dtype = dtype;
     return launch_merge(m, s);
+}
+
+pkv_status pkv_paged_decode_stage(const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *block_table, const int32_t *cache_seqlens,
+                                  int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_seqlen_k,
+                                  float sm_scale, int32_t window_left, void *workspace,
+                                  size_t workspace_bytes, pkv_dtype dtype, void *stream)
+{
+    if (B < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_seqlen_k < 0)
+        return PKV_ERR_SHAPE;
+    pkv_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
+    if (st != PKV_OK) return st;
+    if ((st = check_block_size(block_size)) != PKV_OK) return st;
+    if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+    if (window_left < -1 || B > kStreamMaxB) return PKV_ERR_SHAPE;
+    if ((long long)max_seqlen_k > (long long)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
+    if (B == 0) return PKV_OK;
+    if (!q || !block_table || !cache_seqlens || !k_cache || !v_cache) return PKV_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
+    const StreamLayout lay = stream_layout(B, num_q_heads, num_kv_heads, head_dim);
+    if (!workspace || workspace_bytes < lay.total || ((uintptr_t)workspace & 255u))
+        return PKV_ERR_WORKSPACE;
+    StreamArgs a{};
+    a.part_out = (float *)((char *)workspace + lay.part_out);
+    a.part_lse = (float *)((char *)workspace + lay.part_lse);
+    a.cum_out = (int32_t *)((char *)workspace + lay.cum);
+    a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.block_table = block_table;
+    a.seqlens = cache_seqlens; a.B = B; a.Hq = num_q_heads; a.Hkv = num_kv_heads;
+    a.G = num_q_heads / num_kv_heads; a.D = head_dim; a.bs_log2 = ilog2(block_size);
+    a.mbps = max_blocks_per_seq; a.window_left = window_left;
+    a.W = stream_wgs_per_head_group(num_q_heads, num_kv_heads);
+    a.scale_log2 = sm_scale * kLog2e;
+    return launch_decode_stream_bf16(a, (hipStream_t)stream);
+}
+
+pkv_status pkv_paged_decode_finish(void *out, float *lse, const float *sink, int32_t B,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   const void *workspace, size_t workspace_bytes,
+                                   pkv_dtype dtype, void *stream)
+{
+    if (B < 0) return PKV_ERR_SHAPE;
+    pkv_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
+    if (st != PKV_OK) return st;
+    if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+    if (B > kStreamMaxB) return PKV_ERR_SHAPE;
+    if (B == 0) return PKV_OK;
+    if (!out) return PKV_ERR_NULL;
+    const StreamLayout lay = stream_layout(B, num_q_heads, num_kv_heads, head_dim);
+    if (!workspace || workspace_bytes < lay.total || ((uintptr_t)workspace & 255u))
+        return PKV_ERR_WORKSPACE;
+    MergeArgs m{};
+    m.out = out; m.lse = lse;
+    m.part_out = (const float *)((const char *)workspace + lay.part_out);
+    m.part_lse = (const float *)((const char *)workspace + lay.part_lse);
+    m.cum = (const int32_t *)((const char *)workspace + lay.cum);
+    m.sink = sink; m.B = B; m.Hq = num_q_heads; m.D = head_dim; m.stream = 1; m.dtype = dtype;
+    return launch_merge(m, (hipStream_t)stream);
 }
 
 pkv_status pkv_paged_decode_partitions(float *part_out, float *part_lse, const void *q,

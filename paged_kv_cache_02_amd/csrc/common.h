@@ -16,6 +16,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Word 3 of a raw buffer descriptor on gfx9-family GPUs (32-bit data, no
+// swizzle, offsets checked against num_records).
+constexpr int kBufferWord3 = 0x00020000;
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Reference maximum of a row that has seen no visible key yet: finite, so

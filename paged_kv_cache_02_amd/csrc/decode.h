@@ -22,14 +22,87 @@ struct DecodeArgs {
     float scale_log2;            // sm_scale * log2(e)
 };
 
+// Balanced decode schedule (decode_stream_kernel): the 16-token tiles of all
+// sequences of a head group laid end to end and cut into equal contiguous
+// ranges, one per wave.  Wave gw's partial result for sequence b goes to slot
+// gw + b (unique: a wave's range moves forward through the sequences).
+constexpr int kStreamMaxB = 4096;
+
+struct StreamArgs {
+    float *part_out;             // [slots, Hq, D], slots = W*4 + B
+    float *part_lse;             // [slots, Hq]
+    int32_t *cum_out;            // [B + 2]: tile prefix sums, then the per-wave chunk
+    const void *q;
+    const void *k_cache;
+    const void *v_cache;
+    const int32_t *block_table;
+    const int32_t *seqlens;
+    int32_t B, Hq, Hkv, G, D;
+    int32_t bs_log2, mbps, window_left;
+    int32_t W;                   // workgroups (of 4 waves) per head group
+    float scale_log2;
+};
+
+// First visible key of a decode query over L keys (the window's left edge).
+__device__ __forceinline__ int stream_lo(int L, int window_left) {
+    return window_left >= 0 ? max(0, L - 1 - window_left) : 0;
+}
+// 16-token tiles covering [stream_lo & ~15, L).
+__device__ __forceinline__ int stream_tiles(int L, int window_left) {
+    if (L <= 0) return 0;
+    return (L - (stream_lo(L, window_left) & ~15) + 15) >> 4;
+}
+__device__ __forceinline__ int stream_chunk(int T, int nwaves) {
+    return max(1, (T + nwaves - 1) / nwaves);
+}
+// Block-wide (256 threads): s_cum[b] = tiles of sequences 0..b-1, b <= B.
+__device__ __forceinline__ void stream_prefix_tiles(const int32_t *seqlens, int B,
+                                                    int window_left, int *s_cum, int *s_part) {
+    const int tid = threadIdx.x;
+    const int per = (B + 255) / 256;
+    const int b0 = tid * per;
+    int sum = 0;
+    for (int b = b0; b < min(b0 + per, B); ++b) sum += stream_tiles(seqlens[b], window_left);
+    s_part[tid] = sum;
+    __syncthreads();
+    if (tid < 64) {   // exclusive scan of the 256 strip sums by one wave
+        int x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = s_part[4 * tid + u];
+        const int mine = x[0] + x[1] + x[2] + x[3];
+        int incl = mine;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off, 64);
+            if (tid >= off) incl += y;
+        }
+        int run = incl - mine;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            s_part[4 * tid + u] = run;
+            run += x[u];
+        }
+    }
+    __syncthreads();
+    int run = s_part[tid];
+    for (int b = b0; b < min(b0 + per, B); ++b) {
+        s_cum[b] = run;
+        run += stream_tiles(seqlens[b], window_left);
+    }
+    if (tid == 255) s_cum[B] = run;   // strip 255 ends at B (B <= 256 * per)
+    __syncthreads();
+}
+
 struct MergeArgs {
     void *out;
     float *lse;
     const float *part_out;
     const float *part_lse;
-    const int32_t *seqlens;
+    const int32_t *seqlens;      // partition mode
+    const int32_t *cum;          // stream mode: [B + 2] from decode_stream_kernel
     const float *sink;
     int32_t B, Hq, D, part_size, nparts;
+    int32_t stream;              // 1: slots of the balanced schedule
     int32_t dtype;
 };
 
@@ -77,6 +150,7 @@ struct PrefillArgs {
 
 int decode_heads_per_unit(int G);
 pkv_status launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);
+pkv_status launch_decode_stream_bf16(const StreamArgs &a, hipStream_t stream);
 pkv_status launch_merge(const MergeArgs &a, hipStream_t stream);
 pkv_status launch_rows(const RowArgs &a, bool bf16, hipStream_t stream);
 pkv_status launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream);

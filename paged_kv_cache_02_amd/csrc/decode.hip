@@ -5,32 +5,43 @@
 // sequence's block_table row.  FlashInfer "sink_attention_reference.py"
 // page, incremental branch: the query sits at position Lk-1; GQA head h reads
 // kv head h / (Hq/Hkv); the sink logit joins the softmax denominator.  vLLM
-// "attention.py" page, single_query_cached_kv_attention: a long context can
-// be split into fixed-size token partitions whose partial results are merged
-// afterwards (the merge is in merge.hip).
+// "attention.py" page, single_query_cached_kv_attention: the keys can be split
+// into parts whose partial results are combined by log-sum-exp afterwards
+// (merge.hip).
 //
-// gfx950 design (bf16, head_dim 64/128):
-//   * one workgroup (4 waves) per (sequence, group of HU <= 4 query heads that
-//     share a kv head, partition); the HU heads are packed into one MFMA so
-//     every K/V tile is read from HBM once for all of them;
-//   * a wave handles 16-token tiles (tile i of the partition goes to wave
-//     i % 4), double-buffered in registers: the next tile's K/V 16-byte loads
-//     are in flight while the current one is computed;
+// gfx950 design (bf16, head_dim 64/128).  The work is a stream of 16-token
+// tiles; a tile is 16 consecutive token rows of one block, read for one kv
+// head.  Each wave runs the same tile engine (DecodeWave below):
+//   * HU <= 4 query heads that share a kv head are packed into one MFMA, so
+//     each K/V tile is read from HBM once for all of them;
 //   * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: K rows are the A operand
-//     straight from the 16-byte loads (lane r%16 = token, 8 consecutive dims
-//     per lane), the HU query heads (replicated to 16 columns) are the B
-//     operand held in registers; lane (j, r) receives the logits of tokens
-//     4j..4j+3 for head r % HU;
+//     straight from 16-byte loads (lane r%16 = token, 8 dims per lane), the
+//     HU heads (replicated to 16 columns) are the B operand in registers;
+//     lane (j, r) receives the logits of tokens 4j..4j+3 for head r % HU;
 //   * P.V on the VALU: lane (j, r) loads V rows of the same 4 tokens (16
-//     lanes cover a whole row, so each row is one contiguous 256-byte read)
-//     and takes the other heads' probabilities from its quad with DPP
-//     broadcasts;
-//   * online softmax with a wave-uniform reference maximum per head that is
-//     only raised when a logit exceeds it by more than 2^8 (checked with one
-//     ballot per tile), so the accumulator is almost never rescaled;
-//   * the 4 waves' partial (max, sum, acc) are merged through LDS.
-// The fp32 path (small correctness workloads) is a plain one-wave-per-row
-// kernel in rowattn.hip.
+//     lanes cover a 256-byte row) and takes the other heads' probabilities
+//     from its quad with DPP broadcasts;
+//   * online softmax with a reference maximum per head that is raised only
+//     when a logit exceeds it by more than 2^8 (one ballot per tile);
+//   * a ring of 4 register buffers keeps 3 tiles in flight per wave; loads go
+//     through buffer descriptors (an empty range for padding tiles, which then
+//     cost no memory traffic) so every trip issues the same loads and the
+//     in-order vmcnt waits stay exact; block ids come through the scalar cache
+//     one tile ahead of use.
+//
+// Two schedules use the engine:
+//   * decode_part_kernel: fixed token partitions [p*P, (p+1)*P) (the API's
+//     explicit partition_size, or no split): one workgroup per (sequence,
+//     head group, partition), its 4 waves interleave the partition's tiles and
+//     merge through LDS;
+//   * decode_stream_kernel: balanced persistent schedule.  The tiles of all
+//     sequences of a head group are laid end to end; each wave of a grid sized
+//     to the machine takes an equal contiguous range of that list (computed on
+//     the device from cache_seqlens), streams it without stopping at sequence
+//     boundaries and writes one partial result per sequence it touches.  A
+//     wave's pipeline is filled and drained once, not once per partition, and
+//     no wave is left with a short last partition.
+// The fp32 path (small correctness workloads) is rowattn.hip.
 
 #include "common.h"
 #include "decode.h"
@@ -41,10 +52,15 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr float kTau = 8.0f;  // log2 headroom before the reference max is raised
+constexpr int kDepth = 3;     // K/V tiles in flight per wave
+constexpr int kRing = kDepth + 1;
+// s_waitcnt immediate for vmcnt(0) with expcnt/lgkmcnt left at their maxima
+// (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);
 
 template <int HU>
 __device__ __forceinline__ float bcast_head(float x, int hh) {
-    // quad lane hh holds head hh (lanes r, r%4 == hh; HU divides 4)
+    // quad lane hh holds head hh (lanes r with r % 4 == hh; HU divides 4)
     switch (hh) {
         case 0: return quad_bcast<0>(x);
         case 1: return quad_bcast<1>(x);
@@ -54,103 +70,88 @@ __device__ __forceinline__ float bcast_head(float x, int hh) {
 }
 
 template <int D, int HU>
-__global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a)
-{
-    constexpr int KSTEPS = D / 32;            // MFMA k-steps over head_dim
-    constexpr int VLD = D == 128 ? 4 : 2;     // V rows loaded per lane per tile
+struct DecodeWave {
+    static constexpr int KSTEPS = D / 32;          // MFMA k-steps over head_dim
+    static constexpr int VLD = D == 128 ? 4 : 2;   // V rows loaded per lane per tile
     static_assert(HU == 1 || HU == 2 || HU == 4, "heads per unit");
 
-    __shared__ float sm_m[kWaves][HU];
-    __shared__ float sm_l[kWaves][HU];
-    __shared__ float sm_acc[kWaves][HU][D];
+    int lane, j, r;
+    int tok_bytes;          // one token row, all kv heads
+    uint32_t koff, voff[VLD];
+    bf16x8 qf[KSTEPS];
+    float acc[HU][8];
+    float m_lane, l_lane;
+    float scale_log2;
 
-    const int lane = threadIdx.x & 63;
-    const int wave = readfirstlane(threadIdx.x >> 6);
-    const int j = lane >> 4, r = lane & 15;
-
-    const int NHG = a.Hq / HU;
-    int unit = blockIdx.x;
-    const int pidx = unit % a.nparts;
-    unit /= a.nparts;
-    const int hg = unit % NHG;
-    const int b = unit / NHG;
-    const int h0 = hg * HU;
-    const int g = h0 / a.G;
-    const int L = a.seqlens[b];
-    int start = pidx * a.part_size;
-    const int end = min(start + a.part_size, L);
-    if (a.window_left >= 0) start = max(start, L - 1 - a.window_left);
-
-    const int tok_bytes = a.Hkv * D * 2;               // one token row, all kv heads
-    const int bs_mask = (1 << a.bs_log2) - 1;
+    __device__ void setup(int g, int Hkv, float sl2) {
+        lane = threadIdx.x & 63;
+        j = lane >> 4;
+        r = lane & 15;
+        tok_bytes = Hkv * D * 2;
+        scale_log2 = sl2;
+        koff = (uint32_t)(r * tok_bytes + (g * D + 8 * j) * 2);
+#pragma unroll
+        for (int i = 0; i < VLD; ++i) {
+            const int tv = D == 128 ? 4 * j + i : 4 * j + 2 * (r >> 3) + i;
+            const int dv = D == 128 ? 8 * r : 8 * (r & 7);
+            voff[i] = (uint32_t)(tv * tok_bytes + (g * D + dv) * 2);
+        }
+    }
 
     // Q as the MFMA B operand: lane (j, r) holds dims 32c+8j..+8 of head h0 + r%HU.
-    bf16x8 qf[KSTEPS];
-    {
-        const char *qp = (const char *)a.q +
-                         (((size_t)b * a.Hq + h0 + (r % HU)) * D + 8 * j) * 2;
+    __device__ void load_q(const void *q, size_t first_head_row) {
+        const char *qp = (const char *)q + ((first_head_row + (r % HU)) * D + 8 * j) * 2;
 #pragma unroll
         for (int c = 0; c < KSTEPS; ++c) qf[c] = __builtin_bit_cast(bf16x8, ld16(qp, 64 * c));
     }
 
-    // Per-lane byte offsets inside a tile (relative to the tile's first token row).
-    const uint32_t koff = (uint32_t)(r * tok_bytes + (g * D + 8 * j) * 2);
-    uint32_t voff[VLD];
+    __device__ void reset() {
 #pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-        const int tv = D == 128 ? 4 * j + i : 4 * j + 2 * (r >> 3) + i;
-        const int dv = D == 128 ? 8 * r : 8 * (r & 7);
-        voff[i] = (uint32_t)(tv * tok_bytes + (g * D + dv) * 2);
+        for (int hh = 0; hh < HU; ++hh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+        m_lane = kNoMax;
+        l_lane = 0.f;
     }
 
-    float acc[HU][8];
+    // Issue the 16-byte loads of one tile whose first token row starts
+    // `row_off` bytes into the caches; a dead tile gets an empty range.
+    __device__ void load(const void *kc, const void *vc, size_t row_off, bool live,
+                         u32x4 (&kb)[KSTEPS], u32x4 (&vb)[VLD]) const {
+        const int span = live ? 16 * tok_bytes : 0;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)((const char *)kc + row_off), (short)0, span, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)((const char *)vc + row_off), (short)0, span, kBufferWord3);
 #pragma unroll
-    for (int hh = 0; hh < HU; ++hh)
+        for (int c = 0; c < KSTEPS; ++c)
+            kb[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(koff + 64 * c), 0, 0);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
-    float m_lane = kNoMax;   // reference max (log2 units) of head r%HU; equal across those lanes
-    float l_lane = 0.f;      // sum of p over this lane's 4 tokens, head r%HU
+        for (int i = 0; i < VLD; ++i)
+            vb[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)voff[i], 0, 0);
+    }
 
-    const int tile0 = start & ~15;
-    const int ntiles = start < end ? (end - tile0 + 15) >> 4 : 0;
-    const int my_n = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
-
-    const int32_t *bt = a.block_table + (size_t)b * a.mbps;
-
-    auto tile_base = [&](int t, const void *cache) -> const char * {
-        const int blk = bt[t >> a.bs_log2];
-        const size_t row0 = ((size_t)blk << a.bs_log2) + (t & bs_mask);
-        return (const char *)cache + row0 * (size_t)tok_bytes;
-    };
-
-    auto load = [&](int t, u32x4 (&kb)[KSTEPS], u32x4 (&vb)[VLD]) {
-        const char *kbase = tile_base(t, a.k_cache);
-        const char *vbase = (const char *)a.v_cache + (kbase - (const char *)a.k_cache);
-#pragma unroll
-        for (int c = 0; c < KSTEPS; ++c) kb[c] = ld16(kbase, koff + 64 * c);
-#pragma unroll
-        for (int i = 0; i < VLD; ++i) vb[i] = ld16(vbase, voff[i]);
-    };
-
-    auto process = [&](int t, const u32x4 (&kb)[KSTEPS], u32x4 (&vb)[VLD]) {
+    // Fold tile [t, t+16) into the running state; positions outside [lo, hi)
+    // (or every position, for a dead tile) are masked.
+    __device__ void process(int t, int lo, int hi, bool live, const u32x4 (&kb)[KSTEPS],
+                            u32x4 (&vb)[VLD]) {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < KSTEPS; ++c)
             s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[c]), qf[c],
                                                         s, 0, 0, 0);
-        // s[i]: token t + 4j + i, head h0 + r%HU
-        const bool partial = t < start || t + 16 > end;
+        const bool partial = !live || t < lo || t + 16 > hi;
         bool valid[4];
         float sv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int pos = t + 4 * j + i;
-            valid[i] = !partial || (pos >= start && pos < end);
-            sv[i] = valid[i] ? s[i] * a.scale_log2 : -INFINITY;
+            valid[i] = !partial || (live && pos >= lo && pos < hi);
+            sv[i] = valid[i] ? s[i] * scale_log2 : -INFINITY;
         }
         const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
         if (__any(mx > m_lane + kTau)) {
-            // raise the reference max of every head to its running maximum
+            // raise every head's reference max to its running maximum
             float tm = mx;
 #pragma unroll
             for (int msk = HU; msk < 64; msk <<= 1) tm = fmaxf(tm, shfl_xor(tm, msk));
@@ -193,64 +194,127 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a)
                 for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(ph, v[e], acc[hh][e]);
             }
         }
-    };
-
-    if (my_n > 0) {
-        u32x4 ka[KSTEPS], va[VLD], kb2[KSTEPS], vb2[VLD];
-        int t = tile0 + 16 * wave;
-        load(t, ka, va);
-        for (int it = 0; it < my_n; it += 2) {
-            const int t1 = t + 16 * kWaves;
-            if (it + 1 < my_n) load(t1, kb2, vb2);
-            process(t, ka, va);
-            const int t2 = t1 + 16 * kWaves;
-            if (it + 2 < my_n) load(t2, ka, va);
-            if (it + 1 < my_n) process(t1, kb2, vb2);
-            t = t2;
-        }
     }
 
-    // ---- reduce within the wave ----
-    // l: lanes (j, r) with r < HU hold head r; sum over the 4 lane groups.
-    float lsum = l_lane + shfl_xor(l_lane, 16);
-    lsum += shfl_xor(lsum, 32);
-    // acc: sum over lane groups j (and, for D=64, the two token halves r>>3).
-#pragma unroll
-    for (int hh = 0; hh < HU; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = acc[hh][e];
-            if (D == 64) x += shfl_xor(x, 8);
-            x += shfl_xor(x, 16);
-            x += shfl_xor(x, 32);
-            acc[hh][e] = x;
-        }
-    if (j == 0 && r < HU) {
-        sm_m[wave][r] = m_lane;
-        sm_l[wave][r] = lsum;
-    }
-    if (j == 0 && (D == 128 || r < 8)) {
-        const int d0 = 8 * (D == 128 ? r : (r & 7));
+    // Sum the state over the lanes that hold the same (head, dims): afterwards
+    // lanes with j == 0 (and r < 8 for D = 64) hold acc for dims d0()..d0()+7,
+    // and the returned sum of p is complete in lanes r < HU (for head r).
+    __device__ float reduce() {
+        float lsum = l_lane + shfl_xor(l_lane, 16);
+        lsum += shfl_xor(lsum, 32);
 #pragma unroll
         for (int hh = 0; hh < HU; ++hh)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sm_acc[wave][hh][d0 + e] = acc[hh][e];
+            for (int e = 0; e < 8; ++e) {
+                float x = acc[hh][e];
+                if (D == 64) x += shfl_xor(x, 8);
+                x += shfl_xor(x, 16);
+                x += shfl_xor(x, 32);
+                acc[hh][e] = x;
+            }
+        return lsum;
+    }
+    __device__ bool holds_acc() const { return j == 0 && (D == 128 || r < 8); }
+    __device__ int d0() const { return 8 * (D == 128 ? r : (r & 7)); }
+};
+
+// ---------------------------------------------------------------------------
+// Fixed partitions: one workgroup per (sequence, head group, partition).
+// ---------------------------------------------------------------------------
+template <int D, int HU>
+__global__ __launch_bounds__(256) void decode_part_kernel(DecodeArgs a)
+{
+    __shared__ float sm_m[kWaves][HU];
+    __shared__ float sm_l[kWaves][HU];
+    __shared__ float sm_acc[kWaves][HU][D];
+
+    const int wave = readfirstlane(threadIdx.x >> 6);
+    const int NHG = a.Hq / HU;
+    // Head groups of one (sequence, partition) are adjacent in dispatch order,
+    // so the workgroups that share a block's token rows run together.
+    int unit = blockIdx.x;
+    const int hg = unit % NHG;
+    unit /= NHG;
+    const int pidx = unit % a.nparts;
+    const int b = unit / a.nparts;
+    const int h0 = hg * HU;
+    const int g = h0 / a.G;
+    const int L = a.seqlens[b];
+    int start = pidx * a.part_size;
+    const int end = min(start + a.part_size, L);
+    if (a.window_left >= 0) start = max(start, L - 1 - a.window_left);
+
+    DecodeWave<D, HU> w;
+    w.setup(g, a.Hkv, a.scale_log2);
+    w.load_q(a.q, (size_t)b * a.Hq + h0);
+    w.reset();
+
+    const int bs_mask = (1 << a.bs_log2) - 1;
+    const int tile0 = start & ~15;
+    const int ntiles = start < end ? (end - tile0 + 15) >> 4 : 0;
+    const int my_n = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+
+    // block ids through the scalar cache (constant address space)
+    const __attribute__((address_space(4))) int32_t *bt =
+        (const __attribute__((address_space(4))) int32_t *)(a.block_table + (size_t)b * a.mbps);
+    auto tile_tok = [&](int i) { return tile0 + 16 * (wave + kWaves * i); };
+    auto block_of = [&](int i) { return bt[tile_tok(i) >> a.bs_log2]; };
+    auto row_off = [&](int i, int blk) {
+        return (((size_t)blk << a.bs_log2) + (tile_tok(i) & bs_mask)) * (size_t)w.tok_bytes;
+    };
+
+    if (my_n > 0) {
+        u32x4 kbuf[kRing][DecodeWave<D, HU>::KSTEPS], vbuf[kRing][DecodeWave<D, HU>::VLD];
+        const int last = my_n - 1;
+        const int n_pad = (my_n + kRing - 1) / kRing * kRing;
+#pragma unroll
+        for (int k = 0; k < kDepth; ++k) {
+            const int i = min(k, last);
+            w.load(a.k_cache, a.v_cache, row_off(i, block_of(i)), k < my_n, kbuf[k], vbuf[k]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        int blk_next = block_of(min(kDepth, last));
+        for (int it = 0; it < n_pad; it += kRing) {
+#pragma unroll
+            for (int k = 0; k < kRing; ++k) {
+                const int cur = it + k;
+                const int nxt = cur + kDepth;
+                const int ni = min(nxt, last);
+                w.load(a.k_cache, a.v_cache, row_off(ni, blk_next), nxt < my_n,
+                       kbuf[(k + kDepth) % kRing], vbuf[(k + kDepth) % kRing]);
+                blk_next = block_of(min(nxt + 1, last));
+                __builtin_amdgcn_sched_barrier(0);
+                w.process(tile_tok(cur), start, end, cur < my_n, kbuf[k], vbuf[k]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+
+    const float lsum = w.reduce();
+    if (w.j == 0 && w.r < HU) {
+        sm_m[wave][w.r] = w.m_lane;
+        sm_l[wave][w.r] = lsum;
+    }
+    if (w.holds_acc()) {
+#pragma unroll
+        for (int hh = 0; hh < HU; ++hh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sm_acc[wave][hh][w.d0() + e] = w.acc[hh][e];
     }
     __syncthreads();
 
-    // ---- merge the waves and write ----
     for (int idx = threadIdx.x; idx < HU * D; idx += 256) {
         const int hh = idx / D, d = idx % D;
         const int h = h0 + hh;
         float M = sm_m[0][hh];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][hh]);
+        for (int v = 1; v < kWaves; ++v) M = fmaxf(M, sm_m[v][hh]);
         float Ls = 0.f, o = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float sc = fast_exp2(sm_m[w][hh] - M);
-            Ls = fmaf(sm_l[w][hh], sc, Ls);
-            o = fmaf(sm_acc[w][hh][d], sc, o);
+        for (int v = 0; v < kWaves; ++v) {
+            const float sc = fast_exp2(sm_m[v][hh] - M);
+            Ls = fmaf(sm_l[v][hh], sc, Ls);
+            o = fmaf(sm_acc[v][hh][d], sc, o);
         }
         if (a.split) {
             const size_t pi = ((size_t)b * a.Hq + h) * a.nparts + pidx;
@@ -262,17 +326,162 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a)
             const float sc = fast_exp2(M - Mt);
             const float Lt = Ls * sc + fast_exp2(sig - Mt);
             const float res = Lt > 0.f ? o * sc / Lt : 0.f;
-            const size_t oi = ((size_t)b * a.Hq + h) * D + d;
-            ((uint16_t *)a.out)[oi] = f32_to_bf16(res);
+            ((uint16_t *)a.out)[((size_t)b * a.Hq + h) * D + d] = f32_to_bf16(res);
             if (a.lse && d == 0)
                 a.lse[(size_t)b * a.Hq + h] = Lt > 0.f ? Mt * kLn2 + logf(Lt) : -INFINITY;
         }
     }
 }
 
+// ---------------------------------------------------------------------------
+// Balanced stream: equal contiguous tile ranges per wave.
+// ---------------------------------------------------------------------------
+
 template <int D, int HU>
-void launch_one(const DecodeArgs &a, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_bf16_kernel<D, HU>), dim3(grid), dim3(256), 0, stream, a);
+__global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
+{
+    __shared__ int s_cum[kStreamMaxB + 1];   // tiles of the sequences before b
+    __shared__ int s_part[256];
+
+    const int tid = threadIdx.x;
+    const int wave = readfirstlane(tid >> 6);
+    const int NHG = a.Hq / HU;
+    const int hg = blockIdx.x % NHG;
+    const int wg = blockIdx.x / NHG;
+    const int W = gridDim.x / NHG;                 // workgroups per head group
+    const int h0 = hg * HU;
+    const int g = h0 / a.G;
+
+    stream_prefix_tiles(a.seqlens, a.B, a.window_left, s_cum, s_part);
+    const int T = s_cum[a.B];
+    const int nw = W * kWaves;
+    const int chunk = stream_chunk(T, nw);
+    if (blockIdx.x == 0) {
+        for (int b = tid; b <= a.B; b += 256) a.cum_out[b] = s_cum[b];
+        if (tid == 0) a.cum_out[a.B + 1] = chunk;
+    }
+
+    const int gw = wg * kWaves + wave;            // wave index within the head group
+    const int x0 = min(T, gw * chunk);
+    const int n = min(T, x0 + chunk) - x0;        // tiles of this wave
+    if (n <= 0) return;
+
+    DecodeWave<D, HU> w;
+    w.setup(g, a.Hkv, a.scale_log2);
+    const int bs_mask = (1 << a.bs_log2) - 1;
+
+    // the sequence that holds flattened tile x0: s_cum[b] <= x0 < s_cum[b+1]
+    int b_ld;
+    {
+        int lo = 0, hi = a.B;                     // s_cum[lo] <= x0 < s_cum[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_cum[mid] <= x0) lo = mid; else hi = mid;
+        }
+        b_ld = readfirstlane(lo);
+    }
+    int L_ld = readfirstlane(a.seqlens[b_ld]);
+    int t_ld = readfirstlane((stream_lo(L_ld, a.window_left) & ~15) + 16 * (x0 - s_cum[b_ld]));
+    // advance the load cursor by one tile, skipping sequences with no tiles
+    auto advance = [&]() {
+        t_ld += 16;
+        if (t_ld >= L_ld) {
+            do { ++b_ld; } while (b_ld < a.B && s_cum[b_ld + 1] == s_cum[b_ld]);
+            b_ld = readfirstlane(b_ld);
+            if (b_ld < a.B) {
+                L_ld = readfirstlane(a.seqlens[b_ld]);
+                t_ld = stream_lo(L_ld, a.window_left) & ~15;
+            }
+        }
+    };
+    const __attribute__((address_space(4))) int32_t *bt0 =
+        (const __attribute__((address_space(4))) int32_t *)a.block_table;
+    auto block_at = [&](int b, int t) { return bt0[(size_t)b * a.mbps + (t >> a.bs_log2)]; };
+    auto row_off = [&](int blk, int t) {
+        return (((size_t)blk << a.bs_log2) + (t & bs_mask)) * (size_t)w.tok_bytes;
+    };
+
+    int seg_b = -1, seg_lo = 0, seg_hi = 0;
+    auto flush = [&]() {
+        const float lsum = w.reduce();
+        const size_t slot = (size_t)gw + seg_b;   // unique per (wave, sequence)
+        float *po = a.part_out + (slot * a.Hq + h0) * D;
+#pragma unroll
+        for (int hh = 0; hh < HU; ++hh) {
+            const float lh = __shfl(lsum, hh, 64);
+            const float inv = lh > 0.f ? 1.f / lh : 0.f;
+            if (w.holds_acc()) {
+                const f32x4 v0 = {w.acc[hh][0] * inv, w.acc[hh][1] * inv, w.acc[hh][2] * inv,
+                                  w.acc[hh][3] * inv};
+                const f32x4 v1 = {w.acc[hh][4] * inv, w.acc[hh][5] * inv, w.acc[hh][6] * inv,
+                                  w.acc[hh][7] * inv};
+                *reinterpret_cast<f32x4 *>(po + hh * D + w.d0()) = v0;
+                *reinterpret_cast<f32x4 *>(po + hh * D + w.d0() + 4) = v1;
+            }
+        }
+        if (w.j == 0 && w.r < HU)
+            a.part_lse[slot * a.Hq + h0 + w.r] =
+                lsum > 0.f ? w.m_lane * kLn2 + logf(lsum) : -INFINITY;
+    };
+
+    u32x4 kbuf[kRing][DecodeWave<D, HU>::KSTEPS], vbuf[kRing][DecodeWave<D, HU>::VLD];
+    int rb[kRing], rt[kRing];                     // (sequence, first token) of each ring slot
+    const int n_pad = (n + kRing - 1) / kRing * kRing;
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+        const bool live = k < n;
+        rb[k] = b_ld;
+        rt[k] = t_ld;
+        w.load(a.k_cache, a.v_cache, live ? row_off(block_at(b_ld, t_ld), t_ld) : 0, live,
+               kbuf[k], vbuf[k]);
+        if (k + 1 < n) advance();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    int blk_next = kDepth < n ? block_at(b_ld, t_ld) : 0;
+    for (int it = 0; it < n_pad; it += kRing) {
+#pragma unroll
+        for (int k = 0; k < kRing; ++k) {
+            const int cur = it + k;
+            const int nxt = cur + kDepth;
+            const int slot = (k + kDepth) % kRing;
+            const bool live_n = nxt < n;
+            rb[slot] = b_ld;
+            rt[slot] = t_ld;
+            w.load(a.k_cache, a.v_cache, live_n ? row_off(blk_next, t_ld) : 0, live_n,
+                   kbuf[slot], vbuf[slot]);
+            if (nxt + 1 < n) {
+                advance();
+                blk_next = block_at(b_ld, t_ld);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (cur < n) {
+                if (rb[k] != seg_b) {                 // entering a new sequence
+                    if (seg_b >= 0) flush();
+                    seg_b = rb[k];
+                    const int L = a.seqlens[seg_b];
+                    seg_lo = stream_lo(L, a.window_left);
+                    seg_hi = L;
+                    w.load_q(a.q, (size_t)seg_b * a.Hq + h0);
+                    // Wait for Q here, inside the rare branch: otherwise the
+                    // wait lands after the join and drains the ring every trip.
+                    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                    w.reset();
+                }
+                w.process(rt[k], seg_lo, seg_hi, true, kbuf[k], vbuf[k]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    if (seg_b >= 0) flush();
+}
+
+template <int D, int HU>
+void launch_part(const DecodeArgs &a, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_part_kernel<D, HU>), dim3(grid), dim3(256), 0, stream, a);
+}
+template <int D, int HU>
+void launch_stream(const StreamArgs &a, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_stream_kernel<D, HU>), dim3(grid), dim3(256), 0, stream, a);
 }
 
 }  // namespace
@@ -286,13 +495,31 @@ pkv_status launch_decode_bf16(const DecodeArgs &a, hipStream_t stream)
     if (grid <= 0) return PKV_OK;
     if (grid > 0x7fffffffLL) return PKV_ERR_SHAPE;
     if (a.D == 128) {
-        if (HU == 4) launch_one<128, 4>(a, (int)grid, stream);
-        else if (HU == 2) launch_one<128, 2>(a, (int)grid, stream);
-        else launch_one<128, 1>(a, (int)grid, stream);
+        if (HU == 4) launch_part<128, 4>(a, (int)grid, stream);
+        else if (HU == 2) launch_part<128, 2>(a, (int)grid, stream);
+        else launch_part<128, 1>(a, (int)grid, stream);
     } else {
-        if (HU == 4) launch_one<64, 4>(a, (int)grid, stream);
-        else if (HU == 2) launch_one<64, 2>(a, (int)grid, stream);
-        else launch_one<64, 1>(a, (int)grid, stream);
+        if (HU == 4) launch_part<64, 4>(a, (int)grid, stream);
+        else if (HU == 2) launch_part<64, 2>(a, (int)grid, stream);
+        else launch_part<64, 1>(a, (int)grid, stream);
+    }
+    return launch_status();
+}
+
+pkv_status launch_decode_stream_bf16(const StreamArgs &a, hipStream_t stream)
+{
+    const int HU = decode_heads_per_unit(a.G);
+    const long long grid = (long long)a.W * (a.Hq / HU);
+    if (a.B == 0 || grid <= 0) return PKV_OK;
+    if (a.B > kStreamMaxB || grid > 0x7fffffffLL) return PKV_ERR_SHAPE;
+    if (a.D == 128) {
+        if (HU == 4) launch_stream<128, 4>(a, (int)grid, stream);
+        else if (HU == 2) launch_stream<128, 2>(a, (int)grid, stream);
+        else launch_stream<128, 1>(a, (int)grid, stream);
+    } else {
+        if (HU == 4) launch_stream<64, 4>(a, (int)grid, stream);
+        else if (HU == 2) launch_stream<64, 2>(a, (int)grid, stream);
+        else launch_stream<64, 1>(a, (int)grid, stream);
     }
     return launch_status();
 }

@@ -8,9 +8,10 @@
 // the denominator, no value row) added exactly once:
 //     LSE = ln(sum_p exp(lse_p) + exp(s_h)),   out = sum_p exp(lse_p - LSE) o_p.
 //
-// One wave per (sequence, head): the lanes first reduce the partition
-// maxima and the denominator over the (cheap) lse vector, then stream the
-// partial rows, D/64 dims per lane, four partitions per loop trip.
+// One 256-thread workgroup per (sequence, head): the threads first reduce the
+// partition maxima and the denominator over the lse vector, then stream the
+// partial rows as float4 chunks, 256 / (D/4) partitions side by side, and
+// sum those lanes of partitions through LDS.
 
 #include "common.h"
 #include "decode.h"
@@ -20,75 +21,110 @@ namespace pkv {
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a)
 {
-    constexpr int E = D / 64;
-    const int lane = threadIdx.x & 63;
-    const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (bh >= a.B * a.Hq) return;
+    constexpr int CH = D / 4;            // float4 chunks per partial row
+    constexpr int ROWS = 256 / CH;       // partitions streamed in parallel
+    __shared__ float red[8];
+    __shared__ f32x4 part[ROWS][CH];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int bh = blockIdx.x;
     const int b = bh / a.Hq, h = bh % a.Hq;
-    const int L = a.seqlens[b];
-    const int n = (L + a.part_size - 1) / a.part_size;
-    const float *pl = a.part_lse + (size_t)bh * a.nparts;
-    const float *po = a.part_out + (size_t)bh * a.nparts * D;
+    // partial results of (b, h): n entries, entry p at element p * stride
+    int n;
+    size_t pl0, pls, po0, pos;
+    if (a.stream) {
+        // slots gw + b for the waves gw whose tile range meets sequence b
+        const int c0 = a.cum[b], c1 = a.cum[b + 1], chunk = a.cum[a.B + 1];
+        const int g0 = c0 / chunk;
+        n = c1 > c0 ? (c1 - 1) / chunk - g0 + 1 : 0;
+        pl0 = ((size_t)(g0 + b)) * a.Hq + h;
+        pls = a.Hq;
+    } else {
+        const int L = a.seqlens[b];
+        n = (L + a.part_size - 1) / a.part_size;
+        pl0 = (size_t)bh * a.nparts;
+        pls = 1;
+    }
+    po0 = pl0 * D;
+    pos = pls * D;
+    const float *pl = a.part_lse + pl0;
+    const float *po_base = a.part_out + po0;
     const float sig = a.sink ? a.sink[h] * kLog2e : -INFINITY;
 
     // lse in log2 units, rounded once (no FMA contraction) so that the same
     // value enters the maximum and the weights: the dominant partition then
     // gets a weight of exactly 1.
-    auto lse2 = [&](int p) { return __fmul_rn(pl[p], kLog2e); };
-    float M = sig;
-    for (int p = lane; p < n; p += 64) M = fmaxf(M, lse2(p));
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, shfl_xor(M, m));
+    auto lse2 = [&](int p) { return __fmul_rn(pl[(size_t)p * pls], kLog2e); };
+    auto prow = [&](int p, int c) {
+        return *reinterpret_cast<const f32x4 *>(po_base + (size_t)p * pos + 4 * c);
+    };
 
-    float o[E];
+    auto block_max = [&](float x) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = 0.f;
+        for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, shfl_xor(x, m));
+        if (lane == 0) red[wave] = x;
+        __syncthreads();
+        x = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        __syncthreads();
+        return x;
+    };
+    auto block_sum = [&](float x) {
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) x += shfl_xor(x, m);
+        if (lane == 0) red[4 + wave] = x;
+        __syncthreads();
+        return (red[4] + red[5]) + (red[6] + red[7]);
+    };
+
+    float M = tid == 0 ? sig : -INFINITY;
+    for (int p = tid; p < n; p += 256) M = fmaxf(M, lse2(p));
+    M = block_max(M);
+
+    const int c = tid % CH, row = tid / CH;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
     float lse_out = -INFINITY;
     if (M != -INFINITY) {
-        float Z = lane == 0 ? fast_exp2(sig - M) : 0.f;
-        for (int p = lane; p < n; p += 64) Z += fast_exp2(lse2(p) - M);
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) Z += shfl_xor(Z, m);
+        float Z = tid == 0 ? fast_exp2(sig - M) : 0.f;
+        for (int p = tid; p < n; p += 256) Z += fast_exp2(lse2(p) - M);
+        Z = block_sum(Z);
         const float LSE = M + fast_log2(Z);   // log2 units
         lse_out = LSE * kLn2;
-        int p = 0;
-        for (; p + 4 <= n; p += 4) {
-            float w[4], x[4][E];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float lp = lse2(p + u);
-                w[u] = lp == -INFINITY ? 0.f : fast_exp2(lp - LSE);
-#pragma unroll
-                for (int e = 0; e < E; ++e) x[u][e] = po[(size_t)(p + u) * D + lane + 64 * e];
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (w[u] > 0.f)
-#pragma unroll
-                    for (int e = 0; e < E; ++e) o[e] = fmaf(w[u], x[u][e], o[e]);
+        int p = row;
+        for (; p + ROWS < n; p += 2 * ROWS) {
+            const float l0 = lse2(p), l1 = lse2(p + ROWS);
+            const f32x4 x0 = prow(p, c);
+            const f32x4 x1 = prow(p + ROWS, c);
+            if (l0 != -INFINITY) o += fast_exp2(l0 - LSE) * x0;
+            if (l1 != -INFINITY) o += fast_exp2(l1 - LSE) * x1;
         }
-        for (; p < n; ++p) {
-            const float lp = lse2(p);
-            if (lp == -INFINITY) continue;
-            const float w = fast_exp2(lp - LSE);
-#pragma unroll
-            for (int e = 0; e < E; ++e) o[e] = fmaf(w, po[(size_t)p * D + lane + 64 * e], o[e]);
+        if (p < n) {
+            const float l0 = lse2(p);
+            if (l0 != -INFINITY) o += fast_exp2(l0 - LSE) * prow(p, c);
         }
     }
+    part[row][c] = o;
+    __syncthreads();
+    if (tid < CH) {
+        f32x4 t = part[0][tid];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const size_t oi = (size_t)bh * D + lane + 64 * e;
-        if (BF16) ((uint16_t *)a.out)[oi] = f32_to_bf16(o[e]);
-        else ((float *)a.out)[oi] = o[e];
+        for (int r2 = 1; r2 < ROWS; ++r2) t += part[r2][tid];
+        const size_t oi = (size_t)bh * D + 4 * tid;
+        if (BF16) {
+            u32x2 w = {pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
+            *reinterpret_cast<u32x2 *>((uint16_t *)a.out + oi) = w;
+        } else {
+            *reinterpret_cast<f32x4 *>((float *)a.out + oi) = t;
+        }
     }
-    if (a.lse && lane == 0) a.lse[bh] = lse_out;
+    if (a.lse && tid == 0) a.lse[bh] = lse_out;
 }
 
 pkv_status launch_merge(const MergeArgs &a, hipStream_t stream)
 {
-    const long long waves = (long long)a.B * a.Hq;
-    if (waves == 0) return PKV_OK;
-    const int grid = (int)((waves + 3) / 4);
+    const long long rows = (long long)a.B * a.Hq;
+    if (rows == 0) return PKV_OK;
+    if (rows > 0x7fffffffLL) return PKV_ERR_SHAPE;
+    const int grid = (int)rows;
     const bool bf = a.dtype == PKV_BF16;
     if (a.D == 128) {
         if (bf) hipLaunchKernelGGL((merge_kernel<128, true>), dim3(grid), dim3(256), 0, stream, a);

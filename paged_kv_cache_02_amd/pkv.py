@@ -28,11 +28,15 @@ SIGNATURES = {
     "pkv_version": (ctypes.c_int, []),
     "pkv_reshape_and_cache": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I32, _I32,
                                              _I32, _I32, ctypes.c_int, _P]),
-    "pkv_paged_decode_workspace_bytes": (ctypes.c_size_t, [_I32] * 7),
-    "pkv_paged_decode_auto_partition": (ctypes.c_int32, [_I32] * 6),
+    "pkv_paged_decode_workspace_bytes": (ctypes.c_size_t, [_I32] * 7 + [ctypes.c_int]),
     "pkv_paged_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                         _I32, _I32, _I32, _I32, _F, _I32, _I32, _P, _SZ,
                                         ctypes.c_int, _P]),
+    "pkv_paged_decode_stage": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                              _I32, _I32, _I32, _F, _I32, _P, _SZ, ctypes.c_int,
+                                              _P]),
+    "pkv_paged_decode_finish": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _SZ,
+                                               ctypes.c_int, _P]),
     "pkv_paged_decode_partitions": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
                                                    _I32, _I32, _I32, _I32, _I32, _F, _I32, _I32,
                                                    _I32, ctypes.c_int, _P]),
@@ -124,17 +128,13 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping):
 
 
 def decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_dim, block_size, max_seqlen_k,
-                           partition_size=0) -> int:
+                           partition_size=0, dtype=torch.bfloat16) -> int:
+    dt = PKV_BF16 if dtype == torch.bfloat16 else PKV_F32
     n = lib.pkv_paged_decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_dim, block_size,
-                                             max_seqlen_k, partition_size)
+                                             max_seqlen_k, partition_size, dt)
     if n == ctypes.c_size_t(-1).value:
         raise PkvError(PKV_ERR_SHAPE, "paged_decode_workspace_bytes")
     return n
-
-
-def decode_auto_partition(B, num_q_heads, num_kv_heads, head_dim, block_size, max_seqlen_k) -> int:
-    return lib.pkv_paged_decode_auto_partition(B, num_q_heads, num_kv_heads, head_dim,
-                                               block_size, max_seqlen_k)
 
 
 def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: float, sink=None,
@@ -147,7 +147,7 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: floa
         max_seqlen_k = int(cache_seqlens.max().item()) if B else 0
     if out is None:
         out = torch.empty_like(q)
-    need = decode_workspace_bytes(B, Hq, Hkv, D, bs, max_seqlen_k, partition_size)
+    need = decode_workspace_bytes(B, Hq, Hkv, D, bs, max_seqlen_k, partition_size, q.dtype)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     _check(lib.pkv_paged_decode(
@@ -157,6 +157,28 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: floa
         float(sm_scale), window_left, partition_size, _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _dt(q),
         _stream()), "paged_decode")
+    return out
+
+
+def paged_decode_stage(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: float,
+                       max_seqlen_k: int, workspace, window_left: int = -1):
+    """First stage of automatic bf16 decode: balanced partial results into workspace."""
+    B, Hq, D = q.shape
+    NB, bs, Hkv, _ = k_cache.shape
+    _check(lib.pkv_paged_decode_stage(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(_i32(block_table, "block_table")),
+        _ptr(_i32(cache_seqlens, "cache_seqlens")), B, Hq, Hkv, D, bs, NB, block_table.shape[1],
+        max_seqlen_k, float(sm_scale), window_left, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _dt(q), _stream()), "paged_decode_stage")
+
+
+def paged_decode_finish(out, workspace, num_kv_heads: int, sink=None, lse=None):
+    """Second stage: merge the workspace pieces (with the sink) into out [B,Hq,D]."""
+    B, Hq, D = out.shape
+    _check(lib.pkv_paged_decode_finish(
+        _ptr(out), _ptr(_f32(lse, "lse")), _ptr(_f32(sink, "sink")), B, Hq, num_kv_heads, D,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _dt(out), _stream()),
+        "paged_decode_finish")
     return out
 
 

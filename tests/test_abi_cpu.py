@@ -39,17 +39,23 @@ def test_status_strings_and_version():
 
 
 def test_workspace_sizes():
+    import torch
+    f32, bf = torch.float32, torch.bfloat16
     # long-context split: B=16, Hq=32, D=128, 131072 keys, partitions of 512
-    n = pkv.decode_workspace_bytes(16, 32, 8, 128, 64, 131072, 512)
+    n = pkv.decode_workspace_bytes(16, 32, 8, 128, 64, 131072, 512, bf)
     rows = 16 * 32 * 256
     assert n == rows * 128 * 4 + rows * 4
-    assert pkv.decode_workspace_bytes(4, 8, 8, 64, 16, 100, 0) == 0      # short: no split
-    assert pkv.decode_workspace_bytes(4, 8, 8, 64, 16, 512, 512) == 0    # one partition
+    assert pkv.decode_workspace_bytes(4, 8, 8, 64, 16, 100, 0, f32) == 0    # fp32 auto: no split
+    assert pkv.decode_workspace_bytes(4, 8, 8, 64, 16, 512, 512, bf) == 0   # one partition
+    # bf16 auto: balanced schedule, size independent of the sequence lengths
+    a = pkv.decode_workspace_bytes(64, 32, 8, 128, 16, 4096, 0, bf)
+    b = pkv.decode_workspace_bytes(64, 32, 8, 128, 16, 100, 0, bf)
+    assert a == b and a > 0 and a % 256 == 0
+    assert pkv.decode_workspace_bytes(0, 32, 8, 128, 16, 100, 0, bf) == 0
     with pytest.raises(pkv.PkvError):
-        pkv.decode_workspace_bytes(4, 8, 3, 64, 16, 100, 0)              # Hq % Hkv
+        pkv.decode_workspace_bytes(4, 8, 3, 64, 16, 100, 0, bf)              # Hq % Hkv
     with pytest.raises(pkv.PkvError):
-        pkv.decode_workspace_bytes(4, 8, 8, 64, 16, 1000, 24)            # P % bs
-    assert pkv.decode_auto_partition(16, 32, 8, 128, 64, 131072) % 64 == 0
+        pkv.decode_workspace_bytes(4, 8, 8, 64, 16, 1000, 24, bf)            # P % bs
 
 
 def decode_call(**over):
@@ -76,6 +82,7 @@ def decode_call(**over):
     (dict(max_seqlen_k=65, MB=4), pkv.PKV_ERR_SHAPE),
     (dict(B=-1), pkv.PKV_ERR_SHAPE),
     (dict(part=16), pkv.PKV_ERR_WORKSPACE),          # split without workspace
+    (dict(part=0), pkv.PKV_ERR_WORKSPACE),           # bf16 balanced schedule needs one
     (dict(part=16, ws=FAKE, ws_bytes=10), pkv.PKV_ERR_WORKSPACE),
     (dict(q=FAKE + 4), pkv.PKV_ERR_UNSUPPORTED),     # misaligned
     (dict(B=0), pkv.PKV_OK),                         # no-op, nothing launched
