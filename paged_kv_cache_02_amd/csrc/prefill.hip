@@ -13,21 +13,24 @@
 // gfx950 design:
 //   * workgroup = (request, 128-row query tile, query head), 4 waves of 32
 //     rows; tiles are issued longest-first (highest tile index first);
-//   * K/V tiles of 64 keys are staged in LDS, double-buffered: global loads of
-//     tile t+1 are in flight while tile t is computed; K is stored row-major
-//     (padded), V transposed (V^T[d][key]) as it is written, so both MFMA
-//     operands are read with plain ds_read_b128 / ds_read_b64;
+//   * K and V tiles of 64 keys go straight from global memory into LDS with
+//     global_load_lds_dwordx4 (no register staging, no VALU work), double
+//     buffered: the next tile's loads are issued before the current tile is
+//     computed; each 16-byte piece is placed with an XOR swizzle chosen so
+//     that the operand reads below hit distinct LDS banks;
 //   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 with Q held in registers, so
 //     each lane owns one query row: the row max/sum need one cross-lane step;
-//   * O^T = V^T . P^T on the same MFMA; P goes from the S^T accumulators to
-//     bf16 in place (the key order inside a k-step is the accumulator order,
-//     matched by the V^T reads);
+//     K operands are read with ds_read_b128;
+//   * O^T = V^T . P^T on the same MFMA: P goes from the S^T accumulators to
+//     bf16 in place, and the V^T operand comes from the row-major V tile via
+//     the LDS transpose read ds_read_b64_tr_b16 (within each 16-lane group,
+//     lane 4a+b receives element b of the rows addressed by lanes a, a+4,
+//     a+8, a+12), so no transpose pass is needed;
 //   * online softmax with a reference max raised only when a logit exceeds it
-//     by more than 2^8 (one ballot per tile), exp2 with the log2(e) scale folded
-//     into the logit scale;
-//   * masks are applied only on tiles that straddle the causal diagonal, the
-//     window edge or the end of the keys; tiles outside a wave's visible range
-//     are skipped.
+//     by more than 2^8 (one ballot per tile); the logit scale and log2(e) are
+//     folded into one FMA per exp2;
+//   * masks only on tiles that straddle the causal diagonal, the window edge
+//     or the end of the keys; tiles outside a wave's visible range are skipped.
 
 #include "common.h"
 #include "decode.h"
@@ -39,33 +42,29 @@ namespace {
 constexpr int BM = 128;   // query rows per workgroup
 constexpr int BN = 64;    // keys per tile
 constexpr float kTau = 8.0f;
+constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);   // s_waitcnt vmcnt(0)
 
 template <int D>
-struct Lds {
-    static constexpr int KSTRIDE = D * 2 + 16;     // bytes per K row
-    static constexpr int VSTRIDE = BN * 2 + 16;    // bytes per V^T row
-    static constexpr int KBYTES = BN * KSTRIDE;
-    static constexpr int VBYTES = D * VSTRIDE;
-    static constexpr int BUF = KBYTES + VBYTES;
+struct Tile {
+    static constexpr int U = D / 8;             // 16-byte units per key row
+    static constexpr int BYTES = BN * D * 2;    // one K (or V) tile
+    static constexpr int BUF = 2 * BYTES;       // K + V
+    static constexpr int LOADS = U / 4;         // direct loads per wave per K (or V) tile
+    // swizzled unit position inside a row
+    __device__ static int swz_k(int row) { return row & (U - 1); }
+    __device__ static int swz_v(int row) { return (2 * row) & (U - 1); }
 };
 
-__device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) {
-    // low halves: result = (a.lo) | (b.lo << 16)
-    return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) {
-    // high halves: result = (a.hi) | (b.hi << 16)
-    return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
 {
-    using L = Lds<D>;
+    using TL = Tile<D>;
+    constexpr int U = TL::U;
     constexpr int QK_STEPS = D / 16;      // k-steps of 16 dims
     constexpr int DT = D / 32;            // 32-dim output tiles
-    constexpr int NPAIR = (BN / 4) * (D / 8);   // (4-key group, 8-dim chunk) pairs per tile
-    constexpr int PER_THREAD = (2 * NPAIR) / 256;  // K+V pairs per thread (2 or 1)
     extern __shared__ __attribute__((aligned(16))) char lds[];
 
     const int tid = threadIdx.x;
@@ -125,113 +124,115 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
         for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
     float m = kNoMax, l = 0.f;
 
-    // ---- tile loading: each thread owns PER_THREAD (4-key, 8-dim) pairs ----
+    // ---- direct loads: wave w issues instructions i = w + 4n (n < LOADS) per
+    // tile; lane L of instruction i fills unit 64i + L of the tile, i.e. row
+    // (64i + L) / U at swizzled position (64i + L) % U.
     const int32_t *bt = a.block_table ? a.block_table + (size_t)r * a.mbps : nullptr;
     const int bs_mask = (1 << a.bs_log2) - 1;
-    u32x4 stage[PER_THREAD][4];
-
-    auto key_row = [&](int key) -> size_t {   // element offset of (key, kv head g, dim 0)
-        size_t row;
-        if (bt) row = ((size_t)bt[key >> a.bs_log2] << a.bs_log2) + (key & bs_mask);
-        else row = (size_t)ck0 + key;
-        return row * kvstride + (size_t)g * D;
+    const uint16_t *kg = (const uint16_t *)(bt ? a.k_cache : a.k);
+    const uint16_t *vg = (const uint16_t *)(bt ? a.v_cache : a.v);
+    int ld_row[TL::LOADS], ld_ck[TL::LOADS], ld_cv[TL::LOADS];
+#pragma unroll
+    for (int n = 0; n < TL::LOADS; ++n) {
+        const int u = 64 * (wave + 4 * n) + lane;
+        const int row = u / U, q = u % U;
+        ld_row[n] = row;
+        ld_ck[n] = q ^ TL::swz_k(row);
+        ld_cv[n] = q ^ TL::swz_v(row);
+    }
+    auto key_elem = [&](int key) -> size_t {   // element offset of (key, kv head g, dim 0)
+        size_t rowp;
+        if (bt) rowp = ((size_t)bt[key >> a.bs_log2] << a.bs_log2) + (key & bs_mask);
+        else rowp = (size_t)ck0 + key;
+        return rowp * kvstride + (size_t)g * D;
     };
-
-    auto issue_loads = [&](int t0) {
+    auto issue = [&](int t0, int buf) {
+        char *kl = lds + buf * TL::BUF;
+        char *vl = kl + TL::BYTES;
 #pragma unroll
-        for (int u = 0; u < PER_THREAD; ++u) {
-            const int pidx = tid + 256 * u;
-            const bool isv = pidx >= NPAIR;
-            const int pp = isv ? pidx - NPAIR : pidx;
-            // K: 8-dim chunk fastest (coalesced rows); V: 4-key group fastest
-            const int kq = isv ? (pp % (BN / 4)) : (pp / (D / 8));
-            const int dc = isv ? (pp / (BN / 4)) : (pp % (D / 8));
-            const int key0 = t0 + 4 * kq;
-            const uint16_t *base = (const uint16_t *)(isv ? (bt ? a.v_cache : a.v)
-                                                          : (bt ? a.k_cache : a.k));
-            if (key0 + 3 < Lk) {
-                const size_t off = key_row(key0) + 8 * dc;   // 4 keys share a block (bs >= 16)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    stage[u][c] = *reinterpret_cast<const u32x4 *>(base + off + c * kvstride);
-            } else {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    stage[u][c] = u32x4{0u, 0u, 0u, 0u};
-                    if (key0 + c < Lk)
-                        stage[u][c] = *reinterpret_cast<const u32x4 *>(base + key_row(key0 + c) +
-                                                                        8 * dc);
-                }
-            }
+        for (int n = 0; n < TL::LOADS; ++n) {
+            // keys past the end read the last key instead (finite values whose
+            // logits are masked), so no load leaves the request's rows
+            const int key = min(t0 + ld_row[n], Lk - 1);
+            const size_t e = key_elem(key);
+            const int i = wave + 4 * n;
+            __builtin_amdgcn_global_load_lds((const void *)(kg + e + 8 * ld_ck[n]),
+                                             (lds_void *)(kl + 1024 * i), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(vg + e + 8 * ld_cv[n]),
+                                             (lds_void *)(vl + 1024 * i), 16, 0, 0);
         }
     };
 
-    auto store_lds = [&](int buf) {
-        char *kl = lds + buf * L::BUF;
-        char *vl = kl + L::KBYTES;
+    // ---- LDS operand addresses (lane constants) ----
+    // K: row 32kc + lr, unit 2c + lh  ->  (row * U + ((2c + lh) ^ swz_k(lr))) * 16
+    const int k_lane = lr * U * 16;
+    int k_unit[QK_STEPS];
 #pragma unroll
-        for (int u = 0; u < PER_THREAD; ++u) {
-            const int pidx = tid + 256 * u;
-            const bool isv = pidx >= NPAIR;
-            const int pp = isv ? pidx - NPAIR : pidx;
-            const int kq = isv ? (pp % (BN / 4)) : (pp / (D / 8));
-            const int dc = isv ? (pp / (BN / 4)) : (pp % (D / 8));
-            if (!isv) {
+    for (int c = 0; c < QK_STEPS; ++c) k_unit[c] = ((2 * c + lh) ^ TL::swz_k(lr)) * 16;
+    // V (transpose read): lane k = lane%16 of group G = lane/16 addresses row
+    // 16ks + 4lh + k/4 (+8), dims 32dt + 16(G%2) + 4(k%4) .. +3
+    const int vk = lane & 15, vG = (lane >> 4) & 1;
+    const int v_row = 4 * lh + (vk >> 2);
+    const int v_swz = TL::swz_v(v_row);                 // same for rows +16ks and +8
+    const int v_lane = v_row * U * 16 + ((vk & 3) & 1) * 8;
+    int v_unit[DT];
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    *reinterpret_cast<u32x4 *>(kl + (4 * kq + c) * L::KSTRIDE + 16 * dc) =
-                        stage[u][c];
-            } else {
-                // transpose 4 keys x 8 dims into 8 rows of V^T, 4 keys (8 bytes) each
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const u32x2 lo = {perm_lo(stage[u][0][w], stage[u][1][w]),
-                                      perm_lo(stage[u][2][w], stage[u][3][w])};
-                    const u32x2 hi = {perm_hi(stage[u][0][w], stage[u][1][w]),
-                                      perm_hi(stage[u][2][w], stage[u][3][w])};
-                    *reinterpret_cast<u32x2 *>(vl + (8 * dc + 2 * w) * L::VSTRIDE + 8 * kq) = lo;
-                    *reinterpret_cast<u32x2 *>(vl + (8 * dc + 2 * w + 1) * L::VSTRIDE + 8 * kq) = hi;
-                }
-            }
-        }
-    };
+    for (int t = 0; t < DT; ++t) v_unit[t] = ((4 * t + 2 * vG + ((vk & 3) >> 1)) ^ v_swz) * 16;
 
     auto compute = [&](int buf, int t0) {
-        const char *kl = lds + buf * L::BUF;
-        const char *vl = kl + L::KBYTES;
-        // S^T for the two 32-key chunks
+        const char *kl = lds + buf * TL::BUF;
+        const char *vl = kl + TL::BYTES;
+        auto kread = [&](int c, int kc) {
+            return *reinterpret_cast<const bf16x8 *>(kl + k_lane + 32 * kc * U * 16 + k_unit[c]);
+        };
+        // S^T for the two 32-key chunks; K operands are read two k-steps ahead
+        // so the LDS latency overlaps the MFMAs.
         f32x16 s[2];
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
+        for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[kc][i] = 0.f;
-            const char *krow = kl + (32 * kc + lr) * L::KSTRIDE + 16 * lh;
+        bf16x8 kk[3][2];
 #pragma unroll
-            for (int c = 0; c < QK_STEPS; ++c) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(krow + 32 * c);
-                s[kc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kc], 0, 0, 0);
-            }
+        for (int c = 0; c < 2; ++c) {
+            kk[c][0] = kread(c, 0);
+            kk[c][1] = kread(c, 1);
         }
-        // scale + mask.  Key of accumulator (kc, i): t0 + 32kc + 8(i/4) + 4lh + i%4.
+#pragma unroll
+        for (int c = 0; c < QK_STEPS; ++c) {
+            if (c + 2 < QK_STEPS) {
+                kk[(c + 2) % 3][0] = kread(c + 2, 0);
+                kk[(c + 2) % 3][1] = kread(c + 2, 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[c % 3][0], qf[c], s[0], 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[c % 3][1], qf[c], s[1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Mask, then the row max of the raw logits (the scale is positive, so
+        // it is applied once to the max and folded into the exp argument).
+        // Key of accumulator (kc, i): t0 + 32kc + 8(i/4) + 4lh + i%4.
         const int pos = wpos0 + lr;
         const bool full = (t0 + BN - 1 <= wpos0) && (t0 + BN <= Lk) &&
                           (a.window_left < 0 || t0 >= wpos1 - a.window_left);
+        if (!full) {
+            const int hi = min(pos, Lk - 1) - t0;                         // keys <= hi visible
+            const int lo = a.window_left >= 0 ? pos - a.window_left - t0 : -1 << 30;
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int kx = 32 * kc + 8 * (i >> 2) + 4 * lh + (i & 3);
+                    s[kc][i] = (kx <= hi) & (kx >= lo) ? s[kc][i] : -INFINITY;
+                }
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float x = s[kc][i] * a.scale_log2;
-                if (!full) {
-                    const int key = t0 + 32 * kc + 8 * (i >> 2) + 4 * lh + (i & 3);
-                    const bool vis = key <= pos && key < Lk &&
-                                     (a.window_left < 0 || key >= pos - a.window_left);
-                    x = vis ? x : -INFINITY;
-                }
-                s[kc][i] = x;
-                mx = fmaxf(mx, x);
-            }
-        mx = fmaxf(mx, shfl_xor(mx, 32));
+            for (int i = 0; i < 16; i += 2)
+                mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[kc][i], s[kc][i + 1]));
+        mx = fmaxf(mx, shfl_xor(mx, 32)) * a.scale_log2;
         if (__any(mx > m + kTau)) {
             const float nm = fmaxf(m, mx);
             const float alpha = fast_exp2(m - nm);
@@ -242,47 +243,57 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
                 for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
             m = nm;
         }
-        // P = exp2(S - m) -> bf16, 4 k-steps of 16 keys
-        bf16x8 pf[4];
+        // O^T += V^T . P^T, one 16-key k-step at a time: P of k-step ks is
+        // made (exp2 of S * scale - m, rounded to bf16) just before its MFMAs,
+        // so the exp2 of the next k-step overlaps them.  Slot (lh, e) of
+        // k-step ks is key 16ks + 8(e/4) + 4lh + e%4.  V^T operands are read
+        // (transposed) three MFMAs ahead.
+        auto vread = [&](int ks, int t) {
+            const char *p0 = vl + v_lane + 16 * ks * U * 16 + v_unit[t];
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p0);
+            const bf16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p0 + 8 * U * 16));
+            return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        };
+        constexpr int NPV = 4 * DT;          // MFMAs of the P.V step, ks-major
+        constexpr int VA = 3;                // V operands in flight
+        bf16x8 vv[VA + 1];
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
+        for (int n = 0; n < VA; ++n) vv[n] = vread(n / DT, n % DT);
+        float lsum = 0.f;
+        bf16x8 pf;
 #pragma unroll
-            for (int sp = 0; sp < 2; ++sp) {
+        for (int n = 0; n < NPV; ++n) {
+            const int ks = n / DT, t = n % DT;
+            if (t == 0) {
+                const int kc = ks >> 1, sp = ks & 1;
                 u32x4 w;
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
-                    const float p0 = fast_exp2(s[kc][8 * sp + 2 * e2] - m);
-                    const float p1 = fast_exp2(s[kc][8 * sp + 2 * e2 + 1] - m);
-                    l += p0 + p1;
+                    const float p0 = fast_exp2(fmaf(s[kc][8 * sp + 2 * e2], a.scale_log2, -m));
+                    const float p1 = fast_exp2(fmaf(s[kc][8 * sp + 2 * e2 + 1], a.scale_log2, -m));
+                    lsum += p0 + p1;
                     w[e2] = pack_bf16x2(p0, p1);
                 }
-                pf[2 * kc + sp] = __builtin_bit_cast(bf16x8, w);
+                pf = __builtin_bit_cast(bf16x8, w);
             }
-        // O^T += V^T . P^T
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-            const char *vrow = vl + (32 * t + lr) * L::VSTRIDE;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int kb = 16 * ks + 4 * lh;   // key of element 0 (elements 4..7: kb + 8)
-                const u32x2 v0 = *reinterpret_cast<const u32x2 *>(vrow + 2 * kb);
-                const u32x2 v1 = *reinterpret_cast<const u32x2 *>(vrow + 2 * (kb + 8));
-                const u32x4 vv = {v0[0], v0[1], v1[0], v1[1]};
-                o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
-                                                               pf[ks], o[t], 0, 0, 0);
-            }
+            if (n + VA < NPV) vv[(n + VA) % (VA + 1)] = vread((n + VA) / DT, (n + VA) % DT);
+            __builtin_amdgcn_sched_barrier(0);
+            o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[n % (VA + 1)], pf, o[t], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        l += lsum;
     };
 
     if (ntiles > 0) {
-        issue_loads(t_begin);
-        store_lds(0);
+        issue(t_begin, 0);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         for (int it = 0; it < ntiles; ++it) {
             const int t0 = t_begin + it * BN;
-            if (it + 1 < ntiles) issue_loads(t0 + BN);
+            if (it + 1 < ntiles) issue(t0 + BN, (it + 1) & 1);
             if (wrows > 0 && t0 < w_hi && t0 + BN > w_lo) compute(it & 1, t0);
-            if (it + 1 < ntiles) store_lds((it + 1) & 1);
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             __syncthreads();
         }
     }
@@ -321,18 +332,18 @@ pkv_status launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream)
     // more than 64 KiB of dynamic LDS: raise the per-kernel limit once
     static const bool raised = [] {
         hipFuncSetAttribute((const void *)prefill_bf16_kernel<128>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Lds<128>::BUF);
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Tile<128>::BUF);
         hipFuncSetAttribute((const void *)prefill_bf16_kernel<64>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Lds<64>::BUF);
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Tile<64>::BUF);
         return true;
     }();
     (void)raised;
     if (a.D == 128) {
-        const int lds = 2 * Lds<128>::BUF;
-        hipLaunchKernelGGL((prefill_bf16_kernel<128>), dim3((int)grid), dim3(256), lds, stream, a);
+        hipLaunchKernelGGL((prefill_bf16_kernel<128>), dim3((int)grid), dim3(256),
+                           2 * Tile<128>::BUF, stream, a);
     } else {
-        const int lds = 2 * Lds<64>::BUF;
-        hipLaunchKernelGGL((prefill_bf16_kernel<64>), dim3((int)grid), dim3(256), lds, stream, a);
+        hipLaunchKernelGGL((prefill_bf16_kernel<64>), dim3((int)grid), dim3(256),
+                           2 * Tile<64>::BUF, stream, a);
     }
     return launch_status();
 }
