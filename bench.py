@@ -23,6 +23,7 @@ Peaks: HBM3E 8.0 TB/s, dense bf16 MFMA 2.5 PFLOP/s (MI355X public figures).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -118,6 +119,43 @@ def timed_steps(step, steps, warmup, launches_per_step=2):
     return ms, kt
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+# source files of each kernel whose PMC traffic is recorded in the summary
+KERNEL_SOURCES = {
+    "decode_c2": ("decode.hip", "decode.h", "common.h"),
+    "prefill_c3": ("prefill.hip", "decode.h", "common.h"),
+    "prefill_c4": ("prefill.hip", "decode.h", "common.h"),
+    "reshape_c3": ("cache.hip", "common.h"),
+}
+
+
+def sources_digest(key):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[key]:
+        with open(os.path.join(ROOT, "paged_kv_cache_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(key):
+    """HBM bytes per launch of one kernel on one workload, from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary (copy-calibrated); None when the
+    summary has no row for it or the kernel's sources changed since."""
+    try:
+        with open(TRAFFIC_SUMMARY) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 7 and cells[0] == key:
+            if cells[3] != sources_digest(key):
+                return None
+            return int(cells[6].replace(",", ""))
+    return None
+
+
 def roofline(bound, achieved, peak, unit, traffic=None):
     return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic}
@@ -147,7 +185,7 @@ def replicate_pool(c, reps):
     return kc, vc, tables
 
 
-def bench_decode(c, name, steps, warmup, partition_size, reps):
+def bench_decode(c, name, steps, warmup, partition_size, reps, traffic_key=None):
     """partition_size 0: the automatic (balanced) schedule, timed as its two
     launches -- decode stage and merge; > 0: fixed partitions + merge."""
     B, Hq, D = c.B, c.Hq, c.D
@@ -194,7 +232,8 @@ def bench_decode(c, name, steps, warmup, partition_size, reps):
         "ms_per_step": round(ms, 4), "algorithmic_bytes": step_bytes,
         "schedule": "balanced" if P == 0 else (f"partitions of {P}" if split else "unsplit"),
         "kernels_ms": {"decode": round(dec_ms, 4)},
-        "roofline": roofline("hbm", dec_bytes / (dec_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+        "roofline": roofline("hbm", dec_bytes / (dec_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                             pmc_traffic(traffic_key) if traffic_key else None),
     }
     if two:
         res["kernels_ms"]["merge"] = round(kt.mean_ms("merge"), 4)
@@ -218,7 +257,7 @@ def visible_pairs(q_lens, k_lens, window):
     return n
 
 
-def bench_prefill(c, name, steps, warmup, reps, with_cache_write=False):
+def bench_prefill(c, name, steps, warmup, reps, with_cache_write=False, traffic_key=None):
     T = c.q.shape[0]
     qs = [c.q.cuda() for _ in range(reps)]
     cq, ck = c.cu_seqlens_q.cuda(), c.cu_seqlens_k.cuda()
@@ -266,7 +305,7 @@ def bench_prefill(c, name, steps, warmup, reps, with_cache_write=False):
            "ms_per_step": round(ms, 4), "algorithmic_flops": flops,
            "kernels_ms": {"prefill": round(pre_ms, 4)},
            "roofline": roofline("mfma", flops / (pre_ms * 1e-3) / 1e12, MFMA_BF16_PEAK_TFS,
-                                "TFLOP/s")}
+                                "TFLOP/s", pmc_traffic(traffic_key) if traffic_key else None)}
     # bytes the method must move: q and out, plus K/V of the visible key range
     kv_tokens = 0
     for Lq, Lk in zip(c.q_lens, c.k_lens):
@@ -285,7 +324,8 @@ def bench_prefill(c, name, steps, warmup, reps, with_cache_write=False):
         res["reshape_and_cache"] = {
             "value": round(rbytes / (rc_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
             "kernel_ms": round(rc_ms, 4), "algorithmic_bytes": rbytes,
-            "roofline": roofline("hbm", rbytes / (rc_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
+            "roofline": roofline("hbm", rbytes / (rc_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                                 pmc_traffic("reshape_c3"))}
     torch.cuda.empty_cache()
     return res, out
 
@@ -336,20 +376,22 @@ def main():
     head = None
     if ARGS.only in ("all", "decode"):
         head, out2 = bench_decode(c2, "decode_64x_U512-4096", steps, warmup,
-                                  ARGS.partition_size, reps=2)
+                                  ARGS.partition_size, reps=2,
+                                  traffic_key="decode_c2" if ARGS.partition_size == 0 else None)
         log(f"decode: {head['value']} GB/s step, kernel {head['roofline']['achieved']} GB/s")
 
     if ARGS.only in ("all", "prefill"):
         log("prefill workload (8 reqs U[256,4096], 32/8 heads, D 128, sink)")
         c3 = synth.config3_prefill()
         r3, _ = bench_prefill(c3, "varlen_prefill_8x_U256-4096", steps, warmup, reps=2,
-                              with_cache_write=True)
+                              with_cache_write=True, traffic_key="prefill_c3")
         workloads["varlen_prefill"] = r3
         log(f"prefill: {r3['value']} TFLOP/s")
     if ARGS.only in ("all", "chunked"):
         log("chunked prefill workload (4 x 512 q on 8704 paged keys, window 128, 64/8, D 64)")
         c4 = synth.config4_chunked(poison=False, spare_blocks=0)
-        r4, _ = bench_prefill(c4, "chunked_prefill_4x512_on_8704_w128", steps, warmup, reps=8)
+        r4, _ = bench_prefill(c4, "chunked_prefill_4x512_on_8704_w128", steps, warmup, reps=8,
+                              traffic_key="prefill_c4")
         workloads["chunked_prefill"] = r4
         log(f"chunked: {r4['value']} TFLOP/s, {r4['hbm_gbs']} GB/s")
     if ARGS.only in ("all", "longctx") and not ARGS.skip_long:
