@@ -55,6 +55,16 @@ struct Tile {
     __device__ static int swz_v(int row) { return (2 * row) & (U - 1); }
 };
 
+// acc + lo(a) + hi(a) for a packed bf16 pair, in one v_dot2_f32_bf16 against
+// (1, 1).  Written as an instruction rather than the dot2 builtin: this
+// compiler's rewrite of that builtin into the accumulator-tied VOP2 form read
+// operand registers after they had been reused.
+__device__ __forceinline__ float add_bf16_pair(uint32_t a, float acc) {
+    float d;
+    asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(0x3f803f80u), "v"(acc));
+    return d;
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -124,42 +134,63 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
         for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
     float m = kNoMax, l = 0.f;
 
-    // ---- direct loads: wave w issues instructions i = w + 4n (n < LOADS) per
-    // tile; lane L of instruction i fills unit 64i + L of the tile, i.e. row
-    // (64i + L) / U at swizzled position (64i + L) % U.
-    const int32_t *bt = a.block_table ? a.block_table + (size_t)r * a.mbps : nullptr;
+    // ---- direct loads.  Instruction i = wave + 4n (n < LOADS) of a tile fills
+    // LDS bytes [1024i, 1024i + 1024): lane L writes unit 64i + L, i.e. row
+    // RPI*i + L/U at swizzled position (L % U) ^ swz(row).  The RPI <= 8 rows
+    // of one instruction form an aligned group inside one cache block (block
+    // size >= 16), so its global address is a wave-uniform row base (scalar
+    // registers, one block-table read) plus a lane-constant 32-bit offset.
+    constexpr int RPI = 64 / U;                     // key rows per load instruction
+    typedef __attribute__((address_space(4))) const int32_t cint32;
+    cint32 *bt = a.block_table ? (cint32 *)a.block_table + (size_t)r * a.mbps : nullptr;
     const int bs_mask = (1 << a.bs_log2) - 1;
-    const uint16_t *kg = (const uint16_t *)(bt ? a.k_cache : a.k);
-    const uint16_t *vg = (const uint16_t *)(bt ? a.v_cache : a.v);
-    int ld_row[TL::LOADS], ld_ck[TL::LOADS], ld_cv[TL::LOADS];
+    const uint32_t rowbytes = (uint32_t)kvstride * 2;
+    const char *kg = (const char *)(bt ? a.k_cache : a.k) + (size_t)g * D * 2;
+    const char *vg = (const char *)(bt ? a.v_cache : a.v) + (size_t)g * D * 2;
+    if (!bt) {
+        kg += (size_t)ck0 * rowbytes;
+        vg += (size_t)ck0 * rowbytes;
+    }
+    const int lrow = lane / U;                      // row of this lane within an instruction
+    uint32_t off_k[TL::LOADS], off_v[TL::LOADS];
 #pragma unroll
     for (int n = 0; n < TL::LOADS; ++n) {
-        const int u = 64 * (wave + 4 * n) + lane;
-        const int row = u / U, q = u % U;
-        ld_row[n] = row;
-        ld_ck[n] = q ^ TL::swz_k(row);
-        ld_cv[n] = q ^ TL::swz_v(row);
+        const int row = RPI * (wave + 4 * n) + lrow, q = lane % U;
+        off_k[n] = lrow * rowbytes + 16 * (q ^ TL::swz_k(row));
+        off_v[n] = lrow * rowbytes + 16 * (q ^ TL::swz_v(row));
     }
-    auto key_elem = [&](int key) -> size_t {   // element offset of (key, kv head g, dim 0)
-        size_t rowp;
-        if (bt) rowp = ((size_t)bt[key >> a.bs_log2] << a.bs_log2) + (key & bs_mask);
-        else rowp = (size_t)ck0 + key;
-        return rowp * kvstride + (size_t)g * D;
+    auto row_base = [&](int key) -> size_t {        // byte offset of key's row (uniform)
+        if (bt) return ((size_t)(((uint32_t)bt[key >> a.bs_log2] << a.bs_log2) | (key & bs_mask))) *
+                       rowbytes;
+        return (size_t)key * rowbytes;
     };
     auto issue = [&](int t0, int buf) {
         char *kl = lds + buf * TL::BUF;
         char *vl = kl + TL::BYTES;
+        if (t0 + BN <= Lk) {
 #pragma unroll
-        for (int n = 0; n < TL::LOADS; ++n) {
-            // keys past the end read the last key instead (finite values whose
-            // logits are masked), so no load leaves the request's rows
-            const int key = min(t0 + ld_row[n], Lk - 1);
-            const size_t e = key_elem(key);
-            const int i = wave + 4 * n;
-            __builtin_amdgcn_global_load_lds((const void *)(kg + e + 8 * ld_ck[n]),
-                                             (lds_void *)(kl + 1024 * i), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(vg + e + 8 * ld_cv[n]),
-                                             (lds_void *)(vl + 1024 * i), 16, 0, 0);
+            for (int n = 0; n < TL::LOADS; ++n) {
+                const int i = wave + 4 * n;
+                const size_t rb = row_base(t0 + RPI * i);
+                __builtin_amdgcn_global_load_lds((const void *)(kg + rb + off_k[n]),
+                                                 (lds_void *)(kl + 1024 * i), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void *)(vg + rb + off_v[n]),
+                                                 (lds_void *)(vl + 1024 * i), 16, 0, 0);
+            }
+        } else {
+            // last tile: rows past the end read the last key instead (finite
+            // values whose logits are masked), so no load leaves the request
+#pragma unroll
+            for (int n = 0; n < TL::LOADS; ++n) {
+                const int i = wave + 4 * n;
+                const int key0 = min(t0 + RPI * i, Lk - 1);
+                const size_t rb = row_base(key0);
+                const uint32_t back = (uint32_t)(lrow - min(lrow, Lk - 1 - key0)) * rowbytes;
+                __builtin_amdgcn_global_load_lds((const void *)(kg + rb + (off_k[n] - back)),
+                                                 (lds_void *)(kl + 1024 * i), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void *)(vg + rb + (off_v[n] - back)),
+                                                 (lds_void *)(vl + 1024 * i), 16, 0, 0);
+            }
         }
     };
 
@@ -226,12 +257,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
                     s[kc][i] = (kx <= hi) & (kx >= lo) ? s[kc][i] : -INFINITY;
                 }
         }
-        float mx = -INFINITY;
+        float ma = __builtin_fmaxf(s[0][0], s[0][1]), mb = __builtin_fmaxf(s[1][0], s[1][1]);
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-            for (int i = 0; i < 16; i += 2)
-                mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[kc][i], s[kc][i + 1]));
+        for (int i = 2; i < 16; i += 2) {
+            ma = __builtin_fmaxf(__builtin_fmaxf(ma, s[0][i]), s[0][i + 1]);
+            mb = __builtin_fmaxf(__builtin_fmaxf(mb, s[1][i]), s[1][i + 1]);
+        }
+        float mx = __builtin_fmaxf(ma, mb);
         mx = fmaxf(mx, shfl_xor(mx, 32)) * a.scale_log2;
         if (__any(mx > m + kTau)) {
             const float nm = fmaxf(m, mx);
@@ -260,7 +292,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
         bf16x8 vv[VA + 1];
 #pragma unroll
         for (int n = 0; n < VA; ++n) vv[n] = vread(n / DT, n % DT);
-        float lsum = 0.f;
+        // row sum of the bf16-rounded probabilities (the values P.V uses), two
+        // per instruction
+        float lsum0 = 0.f, lsum1 = 0.f;
         bf16x8 pf;
 #pragma unroll
         for (int n = 0; n < NPV; ++n) {
@@ -272,9 +306,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
                 for (int e2 = 0; e2 < 4; ++e2) {
                     const float p0 = fast_exp2(fmaf(s[kc][8 * sp + 2 * e2], a.scale_log2, -m));
                     const float p1 = fast_exp2(fmaf(s[kc][8 * sp + 2 * e2 + 1], a.scale_log2, -m));
-                    lsum += p0 + p1;
                     w[e2] = pack_bf16x2(p0, p1);
                 }
+                lsum0 = add_bf16_pair(w[0], lsum0);
+                lsum1 = add_bf16_pair(w[1], lsum1);
+                lsum0 = add_bf16_pair(w[2], lsum0);
+                lsum1 = add_bf16_pair(w[3], lsum1);
                 pf = __builtin_bit_cast(bf16x8, w);
             }
             if (n + VA < NPV) vv[(n + VA) % (VA + 1)] = vread((n + VA) / DT, (n + VA) % DT);
@@ -282,7 +319,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
             o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[n % (VA + 1)], pf, o[t], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        l += lsum;
+        l += lsum0 + lsum1;
     };
 
     if (ntiles > 0) {

@@ -25,7 +25,14 @@ def assert_close(got, want, dtype, what="", lse=False):
     got = got.detach().float().cpu().double().numpy() if isinstance(got, torch.Tensor) else got
     want = np.asarray(want, dtype=np.float64)
     assert got.shape == want.shape, (what, got.shape, want.shape)
-    atol, rtol = tol(dtype) if not lse else (1e-3, 1e-3)
+    if lse:
+        # bf16 calls round the probabilities to bf16 before P.V and sum those
+        # rounded values, so Z carries a relative error of at most 2^-9 and
+        # lse = M + ln Z one of at most 2^-9 ~ 1.95e-3 (plus fp32 rounding);
+        # fp32 calls keep the fp32 bar
+        atol, rtol = (2.5e-3, 1e-3) if dtype == torch.bfloat16 else (1e-4, 1e-4)
+    else:
+        atol, rtol = tol(dtype)
     both_inf = np.isinf(want) & (got == want)
     err = np.abs(got - want)
     ok = (err <= atol + rtol * np.abs(want)) | both_inf
