@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--only", default="all",
                    choices=["all", "decode", "prefill", "chunked", "longctx", "none"])
     p.add_argument("--skip-long", action="store_true", help="skip the 131072-token workload")
+    p.add_argument("--spinup", type=float, default=0.3,
+                   help="seconds of untimed steps before the warmup steps of each workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--partition-size", type=int, default=0,
                    help="headline decode partition size (0 = automatic balanced schedule)")
@@ -105,10 +107,33 @@ class KernelTimer:
         return {n for n, _, _ in self.marks}
 
 
+class NoTimer:
+    """Stands in for KernelTimer outside the timed region: launches only."""
+
+    def time(self, name, fn):
+        return fn()
+
+
+def spin_up(step, seconds):
+    """Repeat the step until `seconds` of wall time have passed, so the GPU
+    runs at its sustained clocks when timing starts (a cold GPU runs the
+    prefill kernel ~15 % slower for its first tens of milliseconds)."""
+    t_end = time.perf_counter() + seconds
+    i = 0
+    nt = NoTimer()
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            step(i, nt)
+            i += 1
+        torch.cuda.synchronize()
+
+
 def timed_steps(step, steps, warmup, launches_per_step=2):
-    """Run warmup + timed steps; returns (ms per step, KernelTimer of the timed steps)."""
+    """Spin-up, warmup steps, then timed steps; returns (ms per step,
+    KernelTimer of the timed steps)."""
+    spin_up(step, ARGS.spinup)
     for i in range(warmup):
-        step(i, KernelTimer(4))
+        step(i, NoTimer())
     kt = KernelTimer(steps * launches_per_step + 1)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -416,7 +441,8 @@ def main():
         workloads["copy_calibration"] = {"bytes_read": n * 4, "bytes_written": n * 4}
 
     line = {"metric": "decode KV GB/s (% HBM peak); prefill TFLOP/s (% bf16 MFMA peak)",
-            "n_gpus": 1, "steps": steps, "warmup": warmup, "higher_is_better": True,
+            "n_gpus": 1, "steps": steps, "warmup": warmup, "spinup_s": ARGS.spinup,
+            "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic (seeded numpy PCG64, N(0,1) rounded to bf16)"}
     if head is not None:

@@ -268,6 +268,10 @@ pkv_status pkv_merge_partitions(void *out, float *lse, const float *part_out,
  *                   launch); paged: Lk <= max_blocks_per_seq * block_size.
  *   causal          must be 1 (bottom-right aligned: queries are the last Lq
  *                   positions of the request's keys)
+ *
+ * Errors besides the common ones: PKV_ERR_UNSUPPORTED for bfloat16 with
+ * contiguous K/V when max_seqlen_k * num_kv_heads * head_dim * 2 bytes (one
+ * request's K rows) reaches 4 GiB; use the paged form for such requests.
  */
 pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *k, const void *v,
                               const void *k_cache, const void *v_cache,

@@ -390,6 +390,9 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
     const int bs_log2 = paged ? ilog2(block_size) : 0;
 
     if (dtype == PKV_BF16) {
+        // contiguous K/V are read through one 32-bit-ranged buffer per request
+        if (contiguous && (unsigned long long)max_seqlen_k * num_kv_heads * head_dim * 2 >= (1ull << 32))
+            return PKV_ERR_UNSUPPORTED;
         PrefillArgs a{};
         a.out = out; a.lse = lse; a.q = q; a.k = k; a.v = v; a.k_cache = k_cache;
         a.v_cache = v_cache; a.block_table = block_table; a.cu_q = cu_seqlens_q;

@@ -42,6 +42,11 @@ namespace {
 constexpr int BM = 128;   // query rows per workgroup
 constexpr int BN = 64;    // keys per tile
 constexpr float kTau = 8.0f;
+// LDS operand reads are issued this many MFMAs ahead of their use (K for S,
+// V^T for P.V), to cover LDS latency with eight waves per CU reading (2 and 3
+// ahead left 15 % of the C3 time on the table; 6 and 7 gain nothing more)
+constexpr int KA = 4;
+constexpr int VA = 5;
 constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);   // s_waitcnt vmcnt(0)
 
 template <int D>
@@ -68,7 +73,7 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t a, float acc) {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
 {
     using TL = Tile<D>;
@@ -136,59 +141,64 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
 
     // ---- direct loads.  Instruction i = wave + 4n (n < LOADS) of a tile fills
     // LDS bytes [1024i, 1024i + 1024): lane L writes unit 64i + L, i.e. row
-    // RPI*i + L/U at swizzled position (L % U) ^ swz(row).  The RPI <= 8 rows
-    // of one instruction form an aligned group inside one cache block (block
-    // size >= 16), so its global address is a wave-uniform row base (scalar
-    // registers, one block-table read) plus a lane-constant 32-bit offset.
+    // RPI*i + L/U at swizzled position (L % U) ^ swz(row).  Instruction i's
+    // first row RPI*i is a multiple of U (U <= 16), so a lane's swizzle is the
+    // same in every instruction: one K and one V lane offset.
     constexpr int RPI = 64 / U;                     // key rows per load instruction
-    typedef __attribute__((address_space(4))) const int32_t cint32;
-    cint32 *bt = a.block_table ? (cint32 *)a.block_table + (size_t)r * a.mbps : nullptr;
-    const int bs_mask = (1 << a.bs_log2) - 1;
     const uint32_t rowbytes = (uint32_t)kvstride * 2;
-    const char *kg = (const char *)(bt ? a.k_cache : a.k) + (size_t)g * D * 2;
-    const char *vg = (const char *)(bt ? a.v_cache : a.v) + (size_t)g * D * 2;
-    if (!bt) {
-        kg += (size_t)ck0 * rowbytes;
-        vg += (size_t)ck0 * rowbytes;
-    }
     const int lrow = lane / U;                      // row of this lane within an instruction
-    uint32_t off_k[TL::LOADS], off_v[TL::LOADS];
-#pragma unroll
-    for (int n = 0; n < TL::LOADS; ++n) {
-        const int row = RPI * (wave + 4 * n) + lrow, q = lane % U;
-        off_k[n] = lrow * rowbytes + 16 * (q ^ TL::swz_k(row));
-        off_v[n] = lrow * rowbytes + 16 * (q ^ TL::swz_v(row));
-    }
-    auto row_base = [&](int key) -> size_t {        // byte offset of key's row (uniform)
-        if (bt) return ((size_t)(((uint32_t)bt[key >> a.bs_log2] << a.bs_log2) | (key & bs_mask))) *
-                       rowbytes;
-        return (size_t)key * rowbytes;
-    };
+    const int lrow_w = RPI * wave + lrow;           // its row in the wave's first instruction
+    const uint32_t off_k = lrow * rowbytes + 16 * ((lane % U) ^ TL::swz_k(lrow_w));
+    const uint32_t off_v = lrow * rowbytes + 16 * ((lane % U) ^ TL::swz_v(lrow_w));
+    constexpr uint32_t kStepRows = 4 * RPI;         // rows between a wave's instructions
+
+    // Contiguous K/V: one buffer descriptor per tile whose range ends at the
+    // request's last key, so rows past it read as zeros (finite, and masked)
+    // and no load leaves the request; the row offset inside the tile goes in
+    // the range-checked vector offset.
+    const char *kreq = (const char *)a.k + ((size_t)ck0 * kvstride + (size_t)g * D) * 2;
+    const char *vreq = (const char *)a.v + ((size_t)ck0 * kvstride + (size_t)g * D) * 2;
+    // Paged K/V: the RPI <= 8 rows of one instruction form an aligned group
+    // inside one cache block (block size >= 16), so its global address is a
+    // wave-uniform row base (one block-table read) plus the lane offset.
+    typedef __attribute__((address_space(4))) const int32_t cint32;
+    cint32 *bt = PAGED ? (cint32 *)a.block_table + (size_t)r * a.mbps : nullptr;
+    const int bs_mask = (1 << a.bs_log2) - 1;
+    const char *kcache = (const char *)a.k_cache + (size_t)g * D * 2;
+    const char *vcache = (const char *)a.v_cache + (size_t)g * D * 2;
+
     auto issue = [&](int t0, int buf) {
         char *kl = lds + buf * TL::BUF;
         char *vl = kl + TL::BYTES;
-        if (t0 + BN <= Lk) {
+        if constexpr (!PAGED) {
+            const uint32_t left = (uint32_t)(Lk - t0) * rowbytes;      // bytes from row t0 to the end
+            const auto kr = __builtin_amdgcn_make_buffer_rsrc((void *)(kreq + (size_t)t0 * rowbytes), 0,
+                                                              left, kBufferWord3);
+            const auto vr = __builtin_amdgcn_make_buffer_rsrc((void *)(vreq + (size_t)t0 * rowbytes), 0,
+                                                              left, kBufferWord3);
 #pragma unroll
             for (int n = 0; n < TL::LOADS; ++n) {
                 const int i = wave + 4 * n;
-                const size_t rb = row_base(t0 + RPI * i);
-                __builtin_amdgcn_global_load_lds((const void *)(kg + rb + off_k[n]),
-                                                 (lds_void *)(kl + 1024 * i), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const void *)(vg + rb + off_v[n]),
-                                                 (lds_void *)(vl + 1024 * i), 16, 0, 0);
+                const uint32_t rows = (uint32_t)(RPI * wave) + n * kStepRows;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)(kl + 1024 * i), 16,
+                                                         off_k + rows * rowbytes, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(vl + 1024 * i), 16,
+                                                         off_v + rows * rowbytes, 0, 0, 0);
             }
         } else {
-            // last tile: rows past the end read the last key instead (finite
-            // values whose logits are masked), so no load leaves the request
+            const bool tail = t0 + BN > Lk;
 #pragma unroll
             for (int n = 0; n < TL::LOADS; ++n) {
                 const int i = wave + 4 * n;
-                const int key0 = min(t0 + RPI * i, Lk - 1);
-                const size_t rb = row_base(key0);
-                const uint32_t back = (uint32_t)(lrow - min(lrow, Lk - 1 - key0)) * rowbytes;
-                __builtin_amdgcn_global_load_lds((const void *)(kg + rb + (off_k[n] - back)),
+                // rows past the end read the last key instead (finite values
+                // whose logits are masked), so no load leaves the request
+                const int key0 = tail ? min(t0 + RPI * i, Lk - 1) : t0 + RPI * i;
+                const size_t rb = (size_t)(((uint32_t)bt[key0 >> a.bs_log2] << a.bs_log2) |
+                                           (key0 & bs_mask)) * rowbytes;
+                const uint32_t back = tail ? (uint32_t)(lrow - min(lrow, Lk - 1 - key0)) * rowbytes : 0u;
+                __builtin_amdgcn_global_load_lds((const void *)(kcache + rb + (off_k - back)),
                                                  (lds_void *)(kl + 1024 * i), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const void *)(vg + rb + (off_v[n] - back)),
+                __builtin_amdgcn_global_load_lds((const void *)(vcache + rb + (off_v - back)),
                                                  (lds_void *)(vl + 1024 * i), 16, 0, 0);
             }
         }
@@ -210,76 +220,94 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
 #pragma unroll
     for (int t = 0; t < DT; ++t) v_unit[t] = ((4 * t + 2 * vG + ((vk & 3) >> 1)) ^ v_swz) * 16;
 
-    auto compute = [&](int buf, int t0) {
-        const char *kl = lds + buf * TL::BUF;
-        const char *vl = kl + TL::BYTES;
-        auto kread = [&](int c, int kc) {
-            return *reinterpret_cast<const bf16x8 *>(kl + k_lane + 32 * kc * U * 16 + k_unit[c]);
-        };
-        // S^T for the two 32-key chunks; K operands are read two k-steps ahead
-        // so the LDS latency overlaps the MFMAs.
-        f32x16 s[2];
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[kc][i] = 0.f;
-        bf16x8 kk[3][2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            kk[c][0] = kread(c, 0);
-            kk[c][1] = kread(c, 1);
-        }
-#pragma unroll
-        for (int c = 0; c < QK_STEPS; ++c) {
-            if (c + 2 < QK_STEPS) {
-                kk[(c + 2) % 3][0] = kread(c + 2, 0);
-                kk[(c + 2) % 3][1] = kread(c + 2, 1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[c % 3][0], qf[c], s[0], 0, 0, 0);
-            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[c % 3][1], qf[c], s[1], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // Mask, then the row max of the raw logits (the scale is positive, so
-        // it is applied once to the max and folded into the exp argument).
-        // Key of accumulator (kc, i): t0 + 32kc + 8(i/4) + 4lh + i%4.
+    // Mask chunk sx (32 keys from c0) where needed, then raise the reference
+    // max when a logit exceeds it by more than 2^kTau, rescaling O and the
+    // running sums.  Accumulator i holds key c0 + 8(i/4) + 4lh + i%4.
+    float l1 = 0.f;                    // second running sum (two add chains)
+    auto finish = [&](f32x16 &sx, int c0) {
         const int pos = wpos0 + lr;
-        const bool full = (t0 + BN - 1 <= wpos0) && (t0 + BN <= Lk) &&
-                          (a.window_left < 0 || t0 >= wpos1 - a.window_left);
+        const bool full = (c0 + 31 <= wpos0) && (c0 + 32 <= Lk) &&
+                          (a.window_left < 0 || c0 >= wpos1 - a.window_left);
         if (!full) {
-            const int hi = min(pos, Lk - 1) - t0;                         // keys <= hi visible
-            const int lo = a.window_left >= 0 ? pos - a.window_left - t0 : -1 << 30;
+            const int hi = min(pos, Lk - 1) - c0;                         // keys <= hi visible
+            const int lo = a.window_left >= 0 ? pos - a.window_left - c0 : -1 << 30;
 #pragma unroll
-            for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int kx = 32 * kc + 8 * (i >> 2) + 4 * lh + (i & 3);
-                    s[kc][i] = (kx <= hi) & (kx >= lo) ? s[kc][i] : -INFINITY;
-                }
+            for (int i = 0; i < 16; ++i) {
+                const int kx = 8 * (i >> 2) + 4 * lh + (i & 3);
+                sx[i] = (kx <= hi) & (kx >= lo) ? sx[i] : -INFINITY;
+            }
         }
-        float ma = __builtin_fmaxf(s[0][0], s[0][1]), mb = __builtin_fmaxf(s[1][0], s[1][1]);
+        float ma = __builtin_fmaxf(sx[0], sx[1]), mb = __builtin_fmaxf(sx[2], sx[3]);
 #pragma unroll
-        for (int i = 2; i < 16; i += 2) {
-            ma = __builtin_fmaxf(__builtin_fmaxf(ma, s[0][i]), s[0][i + 1]);
-            mb = __builtin_fmaxf(__builtin_fmaxf(mb, s[1][i]), s[1][i + 1]);
+        for (int i = 4; i < 16; i += 4) {
+            ma = __builtin_fmaxf(__builtin_fmaxf(ma, sx[i]), sx[i + 1]);
+            mb = __builtin_fmaxf(__builtin_fmaxf(mb, sx[i + 2]), sx[i + 3]);
         }
-        float mx = __builtin_fmaxf(ma, mb);
-        mx = fmaxf(mx, shfl_xor(mx, 32)) * a.scale_log2;
+        const float mw = __builtin_fmaxf(ma, mb);
+        // the other lane half holds the row's other keys
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mw), __float_as_uint(mw),
+                                                         false, false);
+        const float mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) *
+                         a.scale_log2;
         if (__any(mx > m + kTau)) {
             const float nm = fmaxf(m, mx);
             const float alpha = fast_exp2(m - nm);
             l *= alpha;
+            l1 *= alpha;
 #pragma unroll
             for (int t = 0; t < DT; ++t)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
             m = nm;
         }
-        // O^T += V^T . P^T, one 16-key k-step at a time: P of k-step ks is
-        // made (exp2 of S * scale - m, rounded to bf16) just before its MFMAs,
-        // so the exp2 of the next k-step overlaps them.  Slot (lh, e) of
-        // k-step ks is key 16ks + 8(e/4) + 4lh + e%4.  V^T operands are read
-        // (transposed) three MFMAs ahead.
+    };
+    // P of 16-key step sp of chunk sx: exp2(S * scale - m) rounded to bf16;
+    // slot (lh, e) is key 16sp + 8(e/4) + 4lh + e%4 of the chunk.  The row
+    // sums take the rounded values.
+    auto make_p = [&](const f32x16 &sx, int sp) {
+        u32x4 w;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            const float p0 = fast_exp2(fmaf(sx[8 * sp + 2 * e2], a.scale_log2, -m));
+            const float p1 = fast_exp2(fmaf(sx[8 * sp + 2 * e2 + 1], a.scale_log2, -m));
+            w[e2] = pack_bf16x2(p0, p1);
+        }
+        l = add_bf16_pair(w[0], l);
+        l1 = add_bf16_pair(w[1], l1);
+        l = add_bf16_pair(w[2], l);
+        l1 = add_bf16_pair(w[3], l1);
+        return __builtin_bit_cast(bf16x8, w);
+    };
+
+    // One 64-key tile as two 32-key chunks.  MFMA issue order: S of chunk 0,
+    // S of chunk 1, then P.V by 16-key steps.  The softmax work of chunk 0
+    // runs while the S MFMAs of chunk 1 execute, and that of chunk 1 while the
+    // first P.V step executes, so the matrix pipe is rarely left idle.
+    auto compute = [&](int buf, int t0) {
+        const char *kl = lds + buf * TL::BUF;
+        const char *vl = kl + TL::BYTES;
+        auto kread = [&](int n) {      // K operand of S MFMA n: chunk n / QK, k-step n % QK
+            return *reinterpret_cast<const bf16x8 *>(kl + k_lane + 32 * (n / QK_STEPS) * U * 16 +
+                                                     k_unit[n % QK_STEPS]);
+        };
+        f32x16 s0, s1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
+        constexpr int NS = 2 * QK_STEPS;
+        bf16x8 kk[KA + 1];
+#pragma unroll
+        for (int n = 0; n < KA; ++n) kk[n] = kread(n);
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            if (n + KA < NS) kk[(n + KA) % (KA + 1)] = kread(n + KA);
+            __builtin_amdgcn_sched_barrier(0);
+            if (n < QK_STEPS) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[n % (KA + 1)], qf[n], s0, 0, 0, 0);
+            else s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[n % (KA + 1)], qf[n - QK_STEPS], s1, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (n == QK_STEPS + 1) finish(s0, t0);
+        }
+        // O^T += V^T . P^T, one 16-key step at a time (ks 0, 1 from chunk 0,
+        // ks 2, 3 from chunk 1); V^T operands (transpose reads) VA ahead
         auto vread = [&](int ks, int t) {
             const char *p0 = vl + v_lane + 16 * ks * U * 16 + v_unit[t];
             const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p0);
@@ -287,39 +315,24 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
                 __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p0 + 8 * U * 16));
             return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         };
-        constexpr int NPV = 4 * DT;          // MFMAs of the P.V step, ks-major
-        constexpr int VA = 3;                // V operands in flight
+        constexpr int NPV = 4 * DT;
         bf16x8 vv[VA + 1];
 #pragma unroll
         for (int n = 0; n < VA; ++n) vv[n] = vread(n / DT, n % DT);
-        // row sum of the bf16-rounded probabilities (the values P.V uses), two
-        // per instruction
-        float lsum0 = 0.f, lsum1 = 0.f;
-        bf16x8 pf;
+        bf16x8 pf = make_p(s0, 0);
 #pragma unroll
         for (int n = 0; n < NPV; ++n) {
             const int ks = n / DT, t = n % DT;
-            if (t == 0) {
-                const int kc = ks >> 1, sp = ks & 1;
-                u32x4 w;
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    const float p0 = fast_exp2(fmaf(s[kc][8 * sp + 2 * e2], a.scale_log2, -m));
-                    const float p1 = fast_exp2(fmaf(s[kc][8 * sp + 2 * e2 + 1], a.scale_log2, -m));
-                    w[e2] = pack_bf16x2(p0, p1);
-                }
-                lsum0 = add_bf16_pair(w[0], lsum0);
-                lsum1 = add_bf16_pair(w[1], lsum1);
-                lsum0 = add_bf16_pair(w[2], lsum0);
-                lsum1 = add_bf16_pair(w[3], lsum1);
-                pf = __builtin_bit_cast(bf16x8, w);
-            }
             if (n + VA < NPV) vv[(n + VA) % (VA + 1)] = vread((n + VA) / DT, (n + VA) % DT);
             __builtin_amdgcn_sched_barrier(0);
             o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[n % (VA + 1)], pf, o[t], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
+            if (t == DT - 1) {
+                // a rescale may only fall between whole k-steps of P.V
+                if (ks == 0) finish(s1, t0 + 32);
+                if (ks + 1 < 4) pf = make_p(ks + 1 < 2 ? s0 : s1, (ks + 1) & 1);
+            }
         }
-        l += lsum0 + lsum1;
     };
 
     if (ntiles > 0) {
@@ -336,6 +349,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
     }
 
     // ---- epilogue: normalise with the sink, write the wave's rows ----
+    l += l1;
     l += shfl_xor(l, 32);
     const float sig = a.sink ? a.sink[h] * kLog2e : -INFINITY;
     const float Mt = fmaxf(l > 0.f ? m : kNoMax, sig);
@@ -368,19 +382,25 @@ pkv_status launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream)
     if (grid > 0x7fffffffLL) return PKV_ERR_SHAPE;
     // more than 64 KiB of dynamic LDS: raise the per-kernel limit once
     static const bool raised = [] {
-        hipFuncSetAttribute((const void *)prefill_bf16_kernel<128>,
+        hipFuncSetAttribute((const void *)prefill_bf16_kernel<128, false>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Tile<128>::BUF);
-        hipFuncSetAttribute((const void *)prefill_bf16_kernel<64>,
+        hipFuncSetAttribute((const void *)prefill_bf16_kernel<128, true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Tile<128>::BUF);
+        hipFuncSetAttribute((const void *)prefill_bf16_kernel<64, false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Tile<64>::BUF);
+        hipFuncSetAttribute((const void *)prefill_bf16_kernel<64, true>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Tile<64>::BUF);
         return true;
     }();
     (void)raised;
+    const bool paged = a.block_table != nullptr;
+    const dim3 g((unsigned)grid), b(256);
     if (a.D == 128) {
-        hipLaunchKernelGGL((prefill_bf16_kernel<128>), dim3((int)grid), dim3(256),
-                           2 * Tile<128>::BUF, stream, a);
+        if (paged) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), g, b, 2 * Tile<128>::BUF, stream, a);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), g, b, 2 * Tile<128>::BUF, stream, a);
     } else {
-        hipLaunchKernelGGL((prefill_bf16_kernel<64>), dim3((int)grid), dim3(256),
-                           2 * Tile<64>::BUF, stream, a);
+        if (paged) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), g, b, 2 * Tile<64>::BUF, stream, a);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), g, b, 2 * Tile<64>::BUF, stream, a);
     }
     return launch_status();
 }

@@ -114,6 +114,7 @@ def prefill_call(**over):
     (dict(D=80), pkv.PKV_ERR_UNSUPPORTED),
     (dict(window=-5), pkv.PKV_ERR_SHAPE),
     (dict(dt=2), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(maxk=1 << 24, Hkv=8, Hq=8, D=128), pkv.PKV_ERR_UNSUPPORTED),   # 4 GiB of K per request
     (dict(B=0), pkv.PKV_OK),
     (dict(maxq=0), pkv.PKV_OK),
 ])
