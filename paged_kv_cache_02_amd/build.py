@@ -56,6 +56,15 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # a shared library links with unresolved symbols; one of ours (e.g. a
+    # kernel's host stub the front end did not emit) must fail the build here
+    # rather than at load time
+    nm = shutil.which("nm") or "/usr/bin/nm"
+    r = subprocess.run([nm, "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in r.stdout.splitlines() if "_ZN3pkv" in ln]
+    if r.returncode != 0 or missing:
+        os.remove(tmp)
+        raise RuntimeError(f"libpkv.so would leave its own symbols undefined: {missing or r.stderr}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
