@@ -382,9 +382,11 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
     }
     int L_ld = readfirstlane(a.seqlens[b_ld]);
     int t_ld = readfirstlane((stream_lo(L_ld, a.window_left) & ~15) + 16 * (x0 - s_cum[b_ld]));
+    int x_ld = x0;                                // flattened index of the cursor's tile
     // advance the load cursor by one tile, skipping sequences with no tiles
     auto advance = [&]() {
         t_ld += 16;
+        ++x_ld;
         if (t_ld >= L_ld) {
             do { ++b_ld; } while (b_ld < a.B && s_cum[b_ld + 1] == s_cum[b_ld]);
             b_ld = readfirstlane(b_ld);
@@ -396,7 +398,40 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
     };
     const __attribute__((address_space(4))) int32_t *bt0 =
         (const __attribute__((address_space(4))) int32_t *)a.block_table;
-    auto block_at = [&](int b, int t) { return bt0[(size_t)b * a.mbps + (t >> a.bs_log2)]; };
+    // Block ids of this wave's tiles, 64 at a time: lane i of a batch holds
+    // the block of tile xb + i.  A tile's block id is then a lane read, not a
+    // dependent memory load per tile queued behind the K/V stream (that
+    // dependency, not bandwidth, limited short-context decode).  The first
+    // batch is read before any tile load; later ones 64 tiles ahead.
+    (void)bt0;
+    const int lane = tid & 63;
+    const int x_end = x0 + n;
+    auto gather = [&](int xs) {
+        const int x = xs + lane;
+        int v = 0;
+        if (x < x_end) {
+            int lo = 0, hi = a.B;                 // s_cum[lo] <= x < s_cum[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (s_cum[mid] <= x) lo = mid; else hi = mid;
+            }
+            const int t = (stream_lo(a.seqlens[lo], a.window_left) & ~15) + 16 * (x - s_cum[lo]);
+            v = a.block_table[(size_t)lo * a.mbps + (t >> a.bs_log2)];
+        }
+        return v;
+    };
+    int xb = x0, blk_batch = gather(x0), blk_ahead = 0;
+    if (x0 + 64 < x_end) blk_ahead = gather(x0 + 64);
+    auto block_at = [&](int b, int t) {
+        (void)b;
+        (void)t;
+        if (x_ld - xb >= 64) {                    // next batch (read 64 tiles ago)
+            xb += 64;
+            blk_batch = blk_ahead;
+            if (xb + 64 < x_end) blk_ahead = gather(xb + 64);
+        }
+        return __builtin_amdgcn_readlane(blk_batch, x_ld - xb);
+    };
     auto row_off = [&](int blk, int t) {
         return (((size_t)blk << a.bs_log2) + (t & bs_mask)) * (size_t)w.tok_bytes;
     };
