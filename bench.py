@@ -5,8 +5,9 @@
 
 One "step" of the headline workload is one bf16 paged decode over 64
 sequences with cache_seqlens ~ U[512, 4096], 32 query / 8 kv heads, head_dim
-128, block size 16 and a shuffled block pool: the decode kernel (per-partition
-results) followed by the log-sum-exp merge, both on torch's current stream.
+128, block size 16 and a shuffled block pool: one launch of the balanced
+decode kernel, whose last wave per (sequence, head group) merges the pieces
+by log-sum-exp, on torch's current stream.
 Inputs are resident in HBM before the timed region; K steps are timed
 between a synchronize on each side, each kernel with its own pair of HIP
 events.  Consecutive steps alternate between two copies of the KV pool so
@@ -210,9 +211,11 @@ def replicate_pool(c, reps):
     return kc, vc, tables
 
 
-def bench_decode(c, name, steps, warmup, partition_size, reps, traffic_key=None):
-    """partition_size 0: the automatic (balanced) schedule, timed as its two
-    launches -- decode stage and merge; > 0: fixed partitions + merge."""
+def bench_decode(c, name, steps, warmup, partition_size, reps, traffic_key=None,
+                 two_stage=False):
+    """partition_size 0: the automatic (balanced) schedule, one launch with the
+    merge fused in (two_stage: its stage and merge launches, timed apart);
+    > 0: fixed partitions + merge."""
     B, Hq, D = c.B, c.Hq, c.D
     kc, vc, tables = replicate_pool(c, reps)
     q = c.q.cuda()
@@ -222,7 +225,7 @@ def bench_decode(c, name, steps, warmup, partition_size, reps, traffic_key=None)
     msk = c.max_seqlen_k
     P = partition_size
     ws_bytes = pkv.decode_workspace_bytes(B, Hq, c.Hkv, D, c.block_size, msk, P, q.dtype)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     split = P > 0 and P < msk
     nparts = (msk + P - 1) // P if split else 1
     if split:
@@ -231,7 +234,7 @@ def bench_decode(c, name, steps, warmup, partition_size, reps, traffic_key=None)
 
     def step(i, kt):
         bt = tables[i % reps]
-        if P == 0:
+        if P == 0 and two_stage:
             kt.time("decode", lambda: pkv.paged_decode_stage(q, kc, vc, bt, sl, c.sm_scale, msk,
                                                              ws, c.window_left))
             kt.time("merge", lambda: pkv.paged_decode_finish(out, ws, c.Hkv, sink=sink))
@@ -244,7 +247,7 @@ def bench_decode(c, name, steps, warmup, partition_size, reps, traffic_key=None)
             kt.time("decode", lambda: pkv.paged_decode(q, kc, vc, bt, sl, c.sm_scale, sink=sink,
                                                        window_left=c.window_left,
                                                        partition_size=P, max_seqlen_k=msk,
-                                                       out=out))
+                                                       out=out, workspace=ws))
 
     ms, kt = timed_steps(step, steps, warmup)
     kv, qb, table = decode_bytes(c)
@@ -255,7 +258,8 @@ def bench_decode(c, name, steps, warmup, partition_size, reps, traffic_key=None)
     res = {
         "name": name, "value": round(step_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
         "ms_per_step": round(ms, 4), "algorithmic_bytes": step_bytes,
-        "schedule": "balanced" if P == 0 else (f"partitions of {P}" if split else "unsplit"),
+        "schedule": ("balanced, two launches" if two_stage else "balanced, merge fused")
+        if P == 0 else (f"partitions of {P}" if split else "unsplit"),
         "kernels_ms": {"decode": round(dec_ms, 4)},
         "roofline": roofline("hbm", dec_bytes / (dec_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
                              pmc_traffic(traffic_key) if traffic_key else None),
@@ -404,6 +408,11 @@ def main():
                                   ARGS.partition_size, reps=2,
                                   traffic_key="decode_c2" if ARGS.partition_size == 0 else None)
         log(f"decode: {head['value']} GB/s step, kernel {head['roofline']['achieved']} GB/s")
+        if ARGS.partition_size == 0:
+            r2s, _ = bench_decode(c2, "decode_64x_U512-4096_two_launches", steps, warmup, 0,
+                                  reps=2, two_stage=True)
+            workloads["decode_two_launches"] = r2s
+            log(f"decode as stage + merge launches: {r2s['value']} GB/s step")
 
     if ARGS.only in ("all", "prefill"):
         log("prefill workload (8 reqs U[256,4096], 32/8 heads, D 128, sink)")

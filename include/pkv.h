@@ -118,9 +118,10 @@ pkv_status pkv_reshape_and_cache(const void *key, const void *value, void *k_cac
  *   - partition_size > 0 and max_seqlen_k > partition_size: float32 part_out
  *     [B, Hq, P, head_dim] and part_lse [B, Hq, P], P = ceil(max_seqlen_k /
  *     partition_size), each 256-byte aligned;
- *   - partition_size == 0, bf16: the balanced schedule's partial results,
- *     (4 * W + B) * Hq * (head_dim + 1) floats plus B + 2 ints (W grows with
- *     the device's compute-unit count), for any B up to 4096;
+ *   - partition_size == 0, bf16: 4096 * Hq int32 arrival counters, then
+ *     the balanced schedule's partial results, (4 * W + B) * Hq *
+ *     (head_dim + 1) floats, plus B + 2 ints (W grows with the device's
+ *     compute-unit count), for any B up to 4096;
  *   - otherwise 0.
  */
 size_t pkv_paged_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
@@ -152,12 +153,20 @@ size_t pkv_paged_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t 
  *                   merged by log-sum-exp.  0: automatic -- bf16 uses a balanced
  *                   schedule that gives every wave of the device an equal share
  *                   of all sequences' key tiles and merges the pieces the same
- *                   way (B <= 4096); fp32 (and larger B) does not split.
- *                   Results are bitwise reproducible for fixed arguments on a
- *                   given device.
+ *                   way (B <= 4096), in one launch: the last wave to finish
+ *                   a (sequence, head group) merges its pieces; fp32 (and
+ *                   larger B) does not split.  Results are bitwise
+ *                   reproducible for fixed arguments on a given device.
  *   workspace       device buffer of at least
  *                   pkv_paged_decode_workspace_bytes(...) bytes (may be NULL
- *                   when that is 0).
+ *                   when that is 0), 256-byte aligned.  For the balanced
+ *                   schedule its leading 4096 * num_q_heads int32 counters
+ *                   must be zero when the call starts; every call leaves
+ *                   them zero.  Zero-fill a workspace once after allocating
+ *                   it (and again after using it for anything else, such as
+ *                   the partition modes, which write it from byte 0), then
+ *                   reuse it for calls with the same num_q_heads and any B.
+ *                   Calls that share a workspace must not overlap in time.
  */
 pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_cache,
                             const void *v_cache, const int32_t *block_table,

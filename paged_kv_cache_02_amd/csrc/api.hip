@@ -55,17 +55,40 @@ int stream_wgs_per_head_group(int Hq, int Hkv) {
     return std::max(1, (2 * device_cus() + NHG - 1) / NHG);
 }
 
+// Balanced-schedule workspace: the fused merge's arrival counters (one per
+// sequence and head group; kStreamMaxB * Hq ints whatever B is, so that one
+// zeroed workspace serves calls with any batch size), then the partial
+// results and the tile prefix sums.
 struct StreamLayout {
-    size_t part_out, part_lse, cum, total;
+    size_t counters, part_out, part_lse, cum, total;
 };
 StreamLayout stream_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t D) {
     const size_t slots = (size_t)stream_wgs_per_head_group(Hq, Hkv) * 4 + B;
     StreamLayout l;
-    l.part_out = 0;
-    l.part_lse = align256(slots * Hq * D * sizeof(float));
+    l.counters = 0;
+    l.part_out = align256((size_t)kStreamMaxB * Hq * sizeof(int32_t));
+    l.part_lse = l.part_out + align256(slots * Hq * D * sizeof(float));
     l.cum = l.part_lse + align256(slots * Hq * sizeof(float));
     l.total = l.cum + align256((size_t)(B + 2) * sizeof(int32_t));
     return l;
+}
+// Arguments of the balanced stream kernel without the fused merge.
+StreamArgs stream_args(const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *block_table, const int32_t *cache_seqlens, int32_t B,
+                       int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size, int32_t mbps,
+                       float sm_scale, int32_t window_left, void *workspace) {
+    const StreamLayout lay = stream_layout(B, Hq, Hkv, D);
+    StreamArgs a{};
+    a.part_out = (float *)((char *)workspace + lay.part_out);
+    a.part_lse = (float *)((char *)workspace + lay.part_lse);
+    a.cum_out = (int32_t *)((char *)workspace + lay.cum);
+    a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.block_table = block_table;
+    a.seqlens = cache_seqlens; a.B = B; a.Hq = Hq; a.Hkv = Hkv;
+    a.G = Hq / Hkv; a.D = D; a.bs_log2 = ilog2(block_size);
+    a.mbps = mbps; a.window_left = window_left;
+    a.W = stream_wgs_per_head_group(Hq, Hkv);
+    a.scale_log2 = sm_scale * kLog2e;
+    return a;
 }
 bool use_stream(pkv_dtype dtype, int32_t B, int32_t partition_size, int32_t max_seqlen_k) {
     return dtype == PKV_BF16 && partition_size == 0 && B <= kStreamMaxB && max_seqlen_k > 0;
@@ -217,13 +240,14 @@ pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_
     if (need > 0 && ((uintptr_t)workspace & 255u)) return PKV_ERR_WORKSPACE;
 
     if (use_stream(dtype, B, partition_size, max_seqlen_k)) {
-        st = pkv_paged_decode_stage(q, k_cache, v_cache, block_table, cache_seqlens, B,
-                                    num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                                    max_blocks_per_seq, max_seqlen_k, sm_scale, window_left,
-                                    workspace, workspace_bytes, dtype, stream);
-        if (st != PKV_OK) return st;
-        return pkv_paged_decode_finish(out, lse, sink, B, num_q_heads, num_kv_heads, head_dim,
-                                       workspace, workspace_bytes, dtype, stream);
+        // one launch: the balanced stream with the merge fused into it
+        StreamArgs a = stream_args(q, k_cache, v_cache, block_table, cache_seqlens, B,
+                                   num_q_heads, num_kv_heads, head_dim, block_size,
+                                   max_blocks_per_seq, sm_scale, window_left, workspace);
+        const StreamLayout lay = stream_layout(B, num_q_heads, num_kv_heads, head_dim);
+        a.counters = (int32_t *)((char *)workspace + lay.counters);
+        a.out = out; a.lse = lse; a.sink = sink;
+        return launch_decode_stream_bf16(a, s);
     }
 
     const SplitPlan plan = plan_split(max_seqlen_k, partition_size);
@@ -266,16 +290,9 @@ pkv_status pkv_paged_decode_stage(const void *q, const void *k_cache, const void
     const StreamLayout lay = stream_layout(B, num_q_heads, num_kv_heads, head_dim);
     if (!workspace || workspace_bytes < lay.total || ((uintptr_t)workspace & 255u))
         return PKV_ERR_WORKSPACE;
-    StreamArgs a{};
-    a.part_out = (float *)((char *)workspace + lay.part_out);
-    a.part_lse = (float *)((char *)workspace + lay.part_lse);
-    a.cum_out = (int32_t *)((char *)workspace + lay.cum);
-    a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.block_table = block_table;
-    a.seqlens = cache_seqlens; a.B = B; a.Hq = num_q_heads; a.Hkv = num_kv_heads;
-    a.G = num_q_heads / num_kv_heads; a.D = head_dim; a.bs_log2 = ilog2(block_size);
-    a.mbps = max_blocks_per_seq; a.window_left = window_left;
-    a.W = stream_wgs_per_head_group(num_q_heads, num_kv_heads);
-    a.scale_log2 = sm_scale * kLog2e;
+    const StreamArgs a = stream_args(q, k_cache, v_cache, block_table, cache_seqlens, B,
+                                     num_q_heads, num_kv_heads, head_dim, block_size,
+                                     max_blocks_per_seq, sm_scale, window_left, workspace);
     return launch_decode_stream_bf16(a, (hipStream_t)stream);
 }
 

@@ -32,6 +32,13 @@ struct StreamArgs {
     float *part_out;             // [slots, Hq, D], slots = W*4 + B
     float *part_lse;             // [slots, Hq]
     int32_t *cum_out;            // [B + 2]: tile prefix sums, then the per-wave chunk
+    // Fused merge (counters != null): the last wave to finish a (sequence,
+    // head group) merges its pieces into out/lse.  counters [B, Hq / HU] must
+    // be zero at launch; the kernel leaves them zero.
+    int32_t *counters;
+    void *out;                   // [B, Hq, D] bf16
+    float *lse;                  // [B, Hq] or null
+    const float *sink;           // [Hq] or null
     const void *q;
     const void *k_cache;
     const void *v_cache;

@@ -26,8 +26,7 @@
 //   * a ring of 4 register buffers keeps 3 tiles in flight per wave; loads go
 //     through buffer descriptors (an empty range for padding tiles, which then
 //     cost no memory traffic) so every trip issues the same loads and the
-//     in-order vmcnt waits stay exact; block ids come through the scalar cache
-//     one tile ahead of use.
+//     in-order vmcnt waits stay exact.
 //
 // Two schedules use the engine:
 //   * decode_part_kernel: fixed token partitions [p*P, (p+1)*P) (the API's
@@ -40,7 +39,11 @@
 //     the device from cache_seqlens), streams it without stopping at sequence
 //     boundaries and writes one partial result per sequence it touches.  A
 //     wave's pipeline is filled and drained once, not once per partition, and
-//     no wave is left with a short last partition.
+//     no wave is left with a short last partition.  The pieces are merged
+//     either by the merge kernel (two launches) or inside the same launch:
+//     each wave counts its pieces in a per-(sequence, head group) counter
+//     after its stream, and the wave whose count completes a sequence merges
+//     it (a sequence held by one wave alone is written directly).
 // The fp32 path (small correctness workloads) is rowattn.hip.
 
 #include "common.h"
@@ -337,7 +340,117 @@ __global__ __launch_bounds__(256) void decode_part_kernel(DecodeArgs a)
 // Balanced stream: equal contiguous tile ranges per wave.
 // ---------------------------------------------------------------------------
 
+// Pieces of the fused merge travel between waves on different XCDs, whose
+// L2 caches are not coherent with each other.  They are written and read with
+// device-coherent accesses (the sc1 cache policy of the buffer loads and
+// stores, the form agent-scope atomic loads and stores take), so no L2
+// writeback or invalidation is needed; a wait for the stores to complete
+// orders them before the arrival count, and the last arriver reads them only
+// after its count returned.  `base` is wave-uniform.
+constexpr int kSc1 = 16;   // cache-policy operand bit of sc1 on gfx950
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const float *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, bytes,
+                                             kBufferWord3);
+}
+
+// bf16 image of a row of E floats.
+template <int E>
+__device__ __forceinline__ void store_row_bf16(uint16_t *p, const float (&x)[E]) {
+    if constexpr (E == 8) {
+        const u32x4 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                         pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+        *reinterpret_cast<u32x4 *>(p) = w;
+    } else if constexpr (E == 4) {
+        const u32x2 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+        *reinterpret_cast<u32x2 *>(p) = w;
+    } else if constexpr (E == 2) {
+        *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(x[0], x[1]);
+    } else {
+        p[0] = f32_to_bf16(x[0]);
+    }
+}
+
+// Log-sum-exp merge by one wave of the nb pieces of (sequence b, heads
+// h0..h0+HU-1) in slots s0..s0+nb-1, with the sink, into out / lse.  The
+// formula is the one of merge.hip (vLLM attention.py page, the reduction
+// step of single_query_cached_kv_attention; FlashInfer sink page for the
+// sink term), folded in slot order with a running maximum, so the result
+// does not depend on which wave runs it.
 template <int D, int HU>
+__device__ void stream_merge_wave(const StreamArgs &a, int b, int h0, int s0, int nb) {
+    constexpr int E = HU * D / 64;                // floats of the head rows per lane
+    const int lane = threadIdx.x & 63;
+    const int hh = lane * E / D, d = lane * E % D;
+    const int h = h0 + hh;
+    float M = -INFINITY, Z = 0.f, o[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = 0.f;
+    constexpr int U = 8;                          // pieces whose loads are issued together
+    for (int i0 = 0; i0 < nb; i0 += U) {
+        float l[U], x[U][E];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t row0 = (size_t)(s0 + min(i0 + u, nb - 1)) * a.Hq + h0;   // uniform
+            const __amdgpu_buffer_rsrc_t rl = coherent_rsrc(a.part_lse + row0, HU * 4);
+            const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(a.part_out + row0 * D, HU * D * 4);
+            l[u] = __builtin_bit_cast(float,
+                                      __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * hh, 0, kSc1));
+            const int off = 4 * (hh * D + d);
+            // (whole-vector bit casts: a bit cast of one vector element
+            // reads element 0 with this compiler)
+            if constexpr (E >= 4) {
+#pragma unroll
+                for (int c = 0; c < E / 4; ++c) {
+                    const f32x4 v = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off + 16 * c, 0, kSc1));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[u][4 * c + e] = v[e];
+                }
+            } else if constexpr (E == 2) {
+                const f32x2 v =
+                    __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(ro, off, 0, kSc1));
+                x[u][0] = v[0];
+                x[u][1] = v[1];
+            } else {
+                x[u][0] = __builtin_bit_cast(float,
+                                             __builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, kSc1));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float l2 = __fmul_rn(l[u], kLog2e);
+            if (i0 + u >= nb || l2 == -INFINITY) continue;
+            if (l2 > M) {
+                const float sc = fast_exp2(M - l2);
+                Z = fmaf(Z, sc, 1.f);
+#pragma unroll
+                for (int e = 0; e < E; ++e) o[e] = fmaf(o[e], sc, x[u][e]);
+                M = l2;
+            } else {
+                const float wt = fast_exp2(l2 - M);
+                Z += wt;
+#pragma unroll
+                for (int e = 0; e < E; ++e) o[e] = fmaf(wt, x[u][e], o[e]);
+            }
+        }
+    }
+    const float sig = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+    const float Mt = fmaxf(M, sig);
+    float lse_v = -INFINITY;
+    if (Mt != -INFINITY) {
+        const float sc = fast_exp2(M - Mt);
+        const float Zt = fmaf(Z, sc, fast_exp2(sig - Mt));
+        const float f = sc / Zt;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] *= f;
+        lse_v = (Mt + fast_log2(Zt)) * kLn2;
+    }
+    store_row_bf16<E>((uint16_t *)a.out + ((size_t)b * a.Hq + h) * D + d, o);
+    if (a.lse && d == 0) a.lse[(size_t)b * a.Hq + h] = lse_v;
+}
+
+template <int D, int HU, bool FUSED>
 __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
 {
     __shared__ int s_cum[kStreamMaxB + 1];   // tiles of the sequences before b
@@ -356,7 +469,19 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
     const int T = s_cum[a.B];
     const int nw = W * kWaves;
     const int chunk = stream_chunk(T, nw);
-    if (blockIdx.x == 0) {
+    if (FUSED) {
+        // sequences without tiles: zero output, lse = sink (or -inf)
+        if (wg == 0) {
+            for (int idx = tid; idx < a.B * HU; idx += 256) {
+                const int b = idx / HU, h = h0 + idx % HU;
+                if (s_cum[b + 1] != s_cum[b]) continue;
+                uint16_t *po = (uint16_t *)a.out + ((size_t)b * a.Hq + h) * D;
+                for (int d = 0; d < D; d += 8)
+                    *reinterpret_cast<u32x4 *>(po + d) = u32x4{0u, 0u, 0u, 0u};
+                if (a.lse) a.lse[(size_t)b * a.Hq + h] = a.sink ? a.sink[h] : -INFINITY;
+            }
+        }
+    } else if (blockIdx.x == 0) {
         for (int b = tid; b <= a.B; b += 256) a.cum_out[b] = s_cum[b];
         if (tid == 0) a.cum_out[a.B + 1] = chunk;
     }
@@ -396,14 +521,11 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
             }
         }
     };
-    const __attribute__((address_space(4))) int32_t *bt0 =
-        (const __attribute__((address_space(4))) int32_t *)a.block_table;
     // Block ids of this wave's tiles, 64 at a time: lane i of a batch holds
     // the block of tile xb + i.  A tile's block id is then a lane read, not a
     // dependent memory load per tile queued behind the K/V stream (that
     // dependency, not bandwidth, limited short-context decode).  The first
     // batch is read before any tile load; later ones 64 tiles ahead.
-    (void)bt0;
     const int lane = tid & 63;
     const int x_end = x0 + n;
     auto gather = [&](int xs) {
@@ -422,9 +544,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
     };
     int xb = x0, blk_batch = gather(x0), blk_ahead = 0;
     if (x0 + 64 < x_end) blk_ahead = gather(x0 + 64);
-    auto block_at = [&](int b, int t) {
-        (void)b;
-        (void)t;
+    auto block_at = [&]() {
         if (x_ld - xb >= 64) {                    // next batch (read 64 tiles ago)
             xb += 64;
             blk_batch = blk_ahead;
@@ -436,11 +556,45 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
         return (((size_t)blk << a.bs_log2) + (t & bs_mask)) * (size_t)w.tok_bytes;
     };
 
+    // Pieces of sequence b: the waves whose ranges meet its tiles; their
+    // slots are consecutive from first_slot(b).
+    auto pieces = [&](int b) { return (s_cum[b + 1] - 1) / chunk - s_cum[b] / chunk + 1; };
+    auto first_slot = [&](int b) { return s_cum[b] / chunk + b; };
+
     int seg_b = -1, seg_lo = 0, seg_hi = 0;
+    // sequences whose pieces this wave wrote but has not counted yet: only the
+    // first and the last sequence of a range can be shared with other waves
+    int shared_a = -1, shared_b = -1;
     auto flush = [&]() {
         const float lsum = w.reduce();
+        if (FUSED && pieces(seg_b) == 1) {
+            // the whole sequence was this wave's: final result with the sink
+#pragma unroll
+            for (int hh = 0; hh < HU; ++hh) {
+                const int h = h0 + hh;
+                const float lh = __shfl(lsum, hh, 64);
+                const float mh = __shfl(w.m_lane, hh, 64);
+                const float sig = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+                const float Mt = fmaxf(lh > 0.f ? mh : kNoMax, sig);
+                const float sc = fast_exp2(mh - Mt);
+                const float Lt = fmaf(lh, sc, fast_exp2(sig - Mt));
+                const float f = Lt > 0.f ? sc / Lt : 0.f;
+                if (w.holds_acc()) {
+                    float x[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = w.acc[hh][e] * f;
+                    store_row_bf16<8>((uint16_t *)a.out + ((size_t)seg_b * a.Hq + h) * D + w.d0(),
+                                      x);
+                }
+                if (a.lse && lane == hh)
+                    a.lse[(size_t)seg_b * a.Hq + h] =
+                        Lt > 0.f ? (Mt + fast_log2(Lt)) * kLn2 : -INFINITY;
+            }
+            return;
+        }
         const size_t slot = (size_t)gw + seg_b;   // unique per (wave, sequence)
         float *po = a.part_out + (slot * a.Hq + h0) * D;
+        const __amdgpu_buffer_rsrc_t rpo = coherent_rsrc(po, HU * D * 4);
 #pragma unroll
         for (int hh = 0; hh < HU; ++hh) {
             const float lh = __shfl(lsum, hh, 64);
@@ -450,13 +604,30 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
                                   w.acc[hh][3] * inv};
                 const f32x4 v1 = {w.acc[hh][4] * inv, w.acc[hh][5] * inv, w.acc[hh][6] * inv,
                                   w.acc[hh][7] * inv};
-                *reinterpret_cast<f32x4 *>(po + hh * D + w.d0()) = v0;
-                *reinterpret_cast<f32x4 *>(po + hh * D + w.d0() + 4) = v1;
+                if (FUSED) {
+                    const int off = 4 * (hh * D + w.d0());
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v0), rpo, off,
+                                                           0, kSc1);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v1), rpo,
+                                                           off + 16, 0, kSc1);
+                } else {
+                    *reinterpret_cast<f32x4 *>(po + hh * D + w.d0()) = v0;
+                    *reinterpret_cast<f32x4 *>(po + hh * D + w.d0() + 4) = v1;
+                }
             }
         }
-        if (w.j == 0 && w.r < HU)
-            a.part_lse[slot * a.Hq + h0 + w.r] =
-                lsum > 0.f ? w.m_lane * kLn2 + logf(lsum) : -INFINITY;
+        if (w.j == 0 && w.r < HU) {
+            const float lse_p = lsum > 0.f ? w.m_lane * kLn2 + logf(lsum) : -INFINITY;
+            if (FUSED)
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __builtin_bit_cast(uint32_t, lse_p),
+                    coherent_rsrc(a.part_lse + slot * a.Hq + h0, HU * 4), 4 * w.r, 0, kSc1);
+            else
+                a.part_lse[slot * a.Hq + h0 + w.r] = lse_p;
+        }
+        if (FUSED) {
+            if (shared_a < 0) shared_a = seg_b; else shared_b = seg_b;
+        }
     };
 
     u32x4 kbuf[kRing][DecodeWave<D, HU>::KSTEPS], vbuf[kRing][DecodeWave<D, HU>::VLD];
@@ -467,12 +638,12 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
         const bool live = k < n;
         rb[k] = b_ld;
         rt[k] = t_ld;
-        w.load(a.k_cache, a.v_cache, live ? row_off(block_at(b_ld, t_ld), t_ld) : 0, live,
-               kbuf[k], vbuf[k]);
+        w.load(a.k_cache, a.v_cache, live ? row_off(block_at(), t_ld) : 0, live, kbuf[k],
+               vbuf[k]);
         if (k + 1 < n) advance();
         __builtin_amdgcn_sched_barrier(0);
     }
-    int blk_next = kDepth < n ? block_at(b_ld, t_ld) : 0;
+    int blk_next = kDepth < n ? block_at() : 0;
     for (int it = 0; it < n_pad; it += kRing) {
 #pragma unroll
         for (int k = 0; k < kRing; ++k) {
@@ -486,7 +657,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
                    kbuf[slot], vbuf[slot]);
             if (nxt + 1 < n) {
                 advance();
-                blk_next = block_at(b_ld, t_ld);
+                blk_next = block_at();
             }
             __builtin_amdgcn_sched_barrier(0);
             if (cur < n) {
@@ -508,6 +679,34 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
         }
     }
     if (seg_b >= 0) flush();
+    if (FUSED && shared_a >= 0) {
+        // Count this wave's shared pieces once its stream is over (the
+        // pieces are complete first), so the stream itself never waits on a
+        // count.  The wave that brings a count to pieces(b) merges b and
+        // leaves its counter zero for the next call.
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        auto arrive = [&](int b) {
+            int old = 0;
+            if (lane == 0)
+                old = __hip_atomic_fetch_add(a.counters + (size_t)b * NHG + hg, 1,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return __builtin_amdgcn_readlane(old, 0) == pieces(b) - 1;
+        };
+        const bool last_a = arrive(shared_a);
+        const bool last_b = shared_b >= 0 && arrive(shared_b);
+        if (last_a) {
+            stream_merge_wave<D, HU>(a, shared_a, h0, first_slot(shared_a), pieces(shared_a));
+            if (lane == 0)
+                __hip_atomic_store(a.counters + (size_t)shared_a * NHG + hg, 0, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (last_b) {
+            stream_merge_wave<D, HU>(a, shared_b, h0, first_slot(shared_b), pieces(shared_b));
+            if (lane == 0)
+                __hip_atomic_store(a.counters + (size_t)shared_b * NHG + hg, 0, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 template <int D, int HU>
@@ -516,7 +715,12 @@ void launch_part(const DecodeArgs &a, int grid, hipStream_t stream) {
 }
 template <int D, int HU>
 void launch_stream(const StreamArgs &a, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_stream_kernel<D, HU>), dim3(grid), dim3(256), 0, stream, a);
+    if (a.counters)
+        hipLaunchKernelGGL((decode_stream_kernel<D, HU, true>), dim3(grid), dim3(256), 0, stream,
+                           a);
+    else
+        hipLaunchKernelGGL((decode_stream_kernel<D, HU, false>), dim3(grid), dim3(256), 0,
+                           stream, a);
 }
 
 }  // namespace

@@ -140,7 +140,11 @@ def decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_dim, block_size, m
 def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: float, sink=None,
                  window_left: int = -1, partition_size: int = 0,
                  max_seqlen_k: Optional[int] = None, out=None, lse=None, workspace=None):
-    """out [B,Hq,D] for q [B,Hq,D] over k/v_cache [NB,bs,Hkv,D]."""
+    """out [B,Hq,D] for q [B,Hq,D] over k/v_cache [NB,bs,Hkv,D].
+
+    A caller-provided `workspace` must have been zero-filled once (the library
+    leaves it zero after every call; see pkv_paged_decode); without one, a
+    zeroed buffer is allocated for this call."""
     B, Hq, D = q.shape
     NB, bs, Hkv, _ = k_cache.shape
     if max_seqlen_k is None:
@@ -149,7 +153,7 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: floa
         out = torch.empty_like(q)
     need = decode_workspace_bytes(B, Hq, Hkv, D, bs, max_seqlen_k, partition_size, q.dtype)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     _check(lib.pkv_paged_decode(
         _ptr(out), _ptr(_f32(lse, "lse")), _ptr(q), _ptr(k_cache), _ptr(v_cache),
         _ptr(_i32(block_table, "block_table")), _ptr(_i32(cache_seqlens, "cache_seqlens")),

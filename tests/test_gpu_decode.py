@@ -139,17 +139,19 @@ def test_config2_full_size_sampled():
 
 @pytest.mark.slow
 def test_config5_long_context_sampled():
-    """Long-context split decode at full size: 16 x 131072 keys, bs 64,
-    partitions of 512 merged by log-sum-exp, sink; 48 sampled rows."""
+    """Long-context split decode at full size: 16 x 131072 keys, bs 64, sink;
+    partitions of 512 merged by log-sum-exp, and the automatic one-launch
+    balanced schedule (16 pieces per sequence); 48 sampled rows each."""
     banner("config5 full size (generating 8.6 GB of K/V)")
     c = synth.config5_split_decode()
-    out, lse = run_decode(c, partition_size=512)
     rng = np.random.default_rng(1)
     units = np.sort(rng.choice(c.B * c.Hq, 48, replace=False))
     o, l = oracle_decode(c, units=units)
     b, h = units // c.Hq, units % c.Hq
-    assert_close(out.float().cpu()[b, h], o[b, h], torch.bfloat16, "config5 sampled")
-    assert_close(lse.cpu()[b, h], l[b, h], torch.bfloat16, "config5 lse", lse=True)
+    for P in (512, 0):
+        out, lse = run_decode(c, partition_size=P)
+        assert_close(out.float().cpu()[b, h], o[b, h], torch.bfloat16, f"config5 P={P} sampled")
+        assert_close(lse.cpu()[b, h], l[b, h], torch.bfloat16, f"config5 P={P} lse", lse=True)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
@@ -187,3 +189,59 @@ def test_decode_equals_paged_prefill_single_row():
     o, _ = oracle_decode(c)
     assert_close(pre, o, torch.bfloat16, "prefill Lq=1 vs oracle")
     assert_close(out, pre.float().cpu().numpy(), torch.bfloat16, "decode vs prefill")
+
+
+def test_fused_merge_workspace_reuse():
+    """The one-launch balanced decode counts the pieces of each (sequence,
+    head group) in the workspace and leaves the counters zero: one zeroed
+    workspace serves consecutive calls with different batches; each result
+    matches the oracle and a repeated call is bitwise identical."""
+    banner("fused merge: workspace reuse")
+    from paged_kv_cache_02_amd import pkv
+    cases = [
+        synth.decode_case(41, [0, 3, 700, 1500, 16, 2100], 32, 8, 128, 16, torch.bfloat16,
+                          with_sink=True, poison=True),
+        synth.decode_case(42, [90, 4000, 1], 32, 8, 128, 16, torch.bfloat16, with_sink=False,
+                          window_left=300, poison=True),
+    ]
+    need = max(pkv.decode_workspace_bytes(c.B, c.Hq, c.Hkv, c.D, c.block_size, c.max_seqlen_k,
+                                          0, torch.bfloat16) for c in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    first = None
+    for rep, c in enumerate(cases + cases[:1]):
+        lse = torch.empty(c.B, c.Hq, dtype=torch.float32, device="cuda")
+        out = pkv.paged_decode(dev(c.q), dev(c.k_cache), dev(c.v_cache), dev(c.block_table),
+                               dev(c.cache_seqlens), c.sm_scale, sink=dev(c.sink),
+                               window_left=c.window_left, max_seqlen_k=c.max_seqlen_k, lse=lse,
+                               workspace=ws)
+        torch.cuda.synchronize()
+        counters = ws[:4096 * c.Hq * 4].view(torch.int32)
+        assert int(counters.abs().sum()) == 0, f"call {rep}: counters left non-zero"
+        o, l = oracle_decode(c)
+        assert_close(out, o, torch.bfloat16, f"call {rep} out")
+        assert_close(lse, l, torch.bfloat16, f"call {rep} lse", lse=True)
+        if rep == 0:
+            first = (out.clone(), lse.clone())
+        elif rep == 2:
+            assert torch.equal(out, first[0]) and torch.equal(lse, first[1]), "repeat differs"
+
+
+@pytest.mark.parametrize("case", CASES[:4], ids=[str(i) for i in range(4)])
+def test_two_launch_decode_vs_oracle(case):
+    """The balanced schedule as two launches (pieces, then the merge kernel)."""
+    lengths, Hq, Hkv, D, bs, sink, window = case
+    banner(f"two-launch decode {case}")
+    from paged_kv_cache_02_amd import pkv
+    c = synth.decode_case(51 + len(lengths), lengths, Hq, Hkv, D, bs, torch.bfloat16,
+                          with_sink=sink, window_left=window, poison=True)
+    ws = torch.empty(pkv.decode_workspace_bytes(c.B, Hq, Hkv, D, bs, c.max_seqlen_k, 0,
+                                                torch.bfloat16), dtype=torch.uint8, device="cuda")
+    out = torch.empty(c.B, Hq, D, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(c.B, Hq, dtype=torch.float32, device="cuda")
+    pkv.paged_decode_stage(dev(c.q), dev(c.k_cache), dev(c.v_cache), dev(c.block_table),
+                           dev(c.cache_seqlens), c.sm_scale, c.max_seqlen_k, ws, c.window_left)
+    pkv.paged_decode_finish(out, ws, Hkv, sink=dev(c.sink), lse=lse)
+    torch.cuda.synchronize()
+    o, l = oracle_decode(c)
+    assert_close(out, o, torch.bfloat16, "two-launch out")
+    assert_close(lse, l, torch.bfloat16, "two-launch lse", lse=True)
