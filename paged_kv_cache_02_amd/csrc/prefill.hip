@@ -12,11 +12,14 @@
 //
 // gfx950 design:
 //   * workgroup = (request, 128-row query tile, query head), 4 waves of 32
-//     rows; tiles are issued longest-first (highest tile index first);
+//     rows; tiles are issued longest-first (highest tile index first), and
+//     the query heads of one kv head are placed on the same XCD so that its
+//     K/V tiles are fetched into that XCD's L2 once for all of them;
 //   * K and V tiles of 64 keys go straight from global memory into LDS with
-//     global_load_lds_dwordx4 (no register staging, no VALU work), double
-//     buffered: the next tile's loads are issued before the current tile is
-//     computed; each 16-byte piece is placed with an XOR swizzle chosen so
+//     the load-to-LDS forms of buffer_load_dwordx4 / global_load_dwordx4 (no
+//     register staging, no VALU work), double buffered: the next tile's loads
+//     are issued before the current tile is computed and waited for only at
+//     its end; each 16-byte piece is placed with an XOR swizzle chosen so
 //     that the operand reads below hit distinct LDS banks;
 //   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 with Q held in registers, so
 //     each lane owns one query row: the row max/sum need one cross-lane step;
@@ -73,6 +76,36 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t a, float acc) {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
+__device__ __forceinline__ uint32_t lds_addr(const char *p) {
+    return (uint32_t)(uintptr_t)(const lds_void *)p;
+}
+
+// Global -> LDS copies, 16 bytes per lane, lane L's bytes landing at LDS
+// address dst + 16 L.  They are written as instructions: the compiler tracks
+// an LDS read issued after a copy it knows of as possibly depending on it and
+// waits for every outstanding copy first, which here would stall each tile on
+// the copies just issued for the next one.  The kernel orders them itself:
+// each tile's copies are waited for (vmcnt 0) and published with a barrier
+// before any wave reads them, and each buffer is refilled only after the
+// barrier that follows the last read of its previous contents.
+//   buffer form: rsrc = raw buffer descriptor, voff = byte offset checked
+//   against its range (lanes past it read zeros and touch no memory);
+__device__ __forceinline__ void copy16_buffer(u32x4 rsrc, uint32_t voff, uint32_t dst) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(dst) : "memory", "m0");
+}
+//   global form: base (wave-uniform) + voff.
+__device__ __forceinline__ void copy16_global(const void *base, uint32_t voff, uint32_t dst) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "s"(dst) : "memory", "m0");
+}
+
+// Raw buffer descriptor of `bytes` bytes from base (stride 0).
+__device__ __forceinline__ u32x4 buffer_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kBufferWord3};
+}
+
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
 {
@@ -89,7 +122,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
     const int lh = lane >> 5;     // lane half
 
     // ---- which (request, q tile, head) ----
-    const int h = blockIdx.x % a.Hq;
+    // Consecutive workgroups go to the eight XCDs in turn, and each XCD has
+    // its own L2.  Position p among the Hq workgroups of one (request, tile)
+    // takes kv head p % Hkv and query head (p % Hkv) * G + p / Hkv, so the G
+    // query heads that read the same K/V land on the same XCD (whenever Hkv
+    // divides 8 or 8 divides Hkv, and Hq is a multiple of 8) and share its L2.
+    const int p = blockIdx.x % a.Hq;
+    const int h = (p % a.Hkv) * a.G + p / a.Hkv;
     const int slot = blockIdx.x / a.Hq;
     const int r = slot % a.B;
     const int qt = a.max_q_tiles - 1 - slot / a.B;
@@ -172,18 +211,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
         char *vl = kl + TL::BYTES;
         if constexpr (!PAGED) {
             const uint32_t left = (uint32_t)(Lk - t0) * rowbytes;      // bytes from row t0 to the end
-            const auto kr = __builtin_amdgcn_make_buffer_rsrc((void *)(kreq + (size_t)t0 * rowbytes), 0,
-                                                              left, kBufferWord3);
-            const auto vr = __builtin_amdgcn_make_buffer_rsrc((void *)(vreq + (size_t)t0 * rowbytes), 0,
-                                                              left, kBufferWord3);
+            const u32x4 kr = buffer_rsrc(kreq + (size_t)t0 * rowbytes, left);
+            const u32x4 vr = buffer_rsrc(vreq + (size_t)t0 * rowbytes, left);
 #pragma unroll
             for (int n = 0; n < TL::LOADS; ++n) {
                 const int i = wave + 4 * n;
                 const uint32_t rows = (uint32_t)(RPI * wave) + n * kStepRows;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)(kl + 1024 * i), 16,
-                                                         off_k + rows * rowbytes, 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(vl + 1024 * i), 16,
-                                                         off_v + rows * rowbytes, 0, 0, 0);
+                copy16_buffer(kr, off_k + rows * rowbytes, lds_addr(kl + 1024 * i));
+                copy16_buffer(vr, off_v + rows * rowbytes, lds_addr(vl + 1024 * i));
             }
         } else {
             const bool tail = t0 + BN > Lk;
@@ -196,10 +231,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
                 const size_t rb = (size_t)(((uint32_t)bt[key0 >> a.bs_log2] << a.bs_log2) |
                                            (key0 & bs_mask)) * rowbytes;
                 const uint32_t back = tail ? (uint32_t)(lrow - min(lrow, Lk - 1 - key0)) * rowbytes : 0u;
-                __builtin_amdgcn_global_load_lds((const void *)(kcache + rb + (off_k - back)),
-                                                 (lds_void *)(kl + 1024 * i), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const void *)(vcache + rb + (off_v - back)),
-                                                 (lds_void *)(vl + 1024 * i), 16, 0, 0);
+                copy16_global(kcache + rb, off_k - back, lds_addr(kl + 1024 * i));
+                copy16_global(vcache + rb, off_v - back, lds_addr(vl + 1024 * i));
             }
         }
     };
@@ -234,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int kx = 8 * (i >> 2) + 4 * lh + (i & 3);
-                sx[i] = (kx <= hi) & (kx >= lo) ? sx[i] : -INFINITY;
+                sx[i] = ((kx <= hi) & (kx >= lo)) ? sx[i] : -INFINITY;
             }
         }
         float ma = __builtin_fmaxf(sx[0], sx[1]), mb = __builtin_fmaxf(sx[2], sx[3]);
