@@ -58,9 +58,17 @@ struct Tile {
     static constexpr int BYTES = BN * D * 2;    // one K (or V) tile
     static constexpr int BUF = 2 * BYTES;       // K + V
     static constexpr int LOADS = U / 4;         // direct loads per wave per K (or V) tile
-    // swizzled unit position inside a row
-    __device__ static int swz_k(int row) { return row & (U - 1); }
-    __device__ static int swz_v(int row) { return (2 * row) & (U - 1); }
+    // Swizzled unit position inside a row: LDS unit u ^ swz(row) holds the
+    // row's 16-byte unit u.  LDS has 64 banks of 4 bytes, and a 256-byte row
+    // (D = 128) starts on bank 0, a 128-byte row (D = 64) on bank 0 or 32.
+    // K is read 16 bytes per lane, 16 rows at a time, each row at its own
+    // unit: swz_k gives the rows that start on the same bank distinct units.
+    // V is read 8 bytes per lane by the transpose read, 4 rows x 4 units per
+    // half wave: swz_v moves each row's 4 units to their own 64 bytes.  Both
+    // depend on row bits 0-4 only, so rows 32 apart share a swizzle.
+    __device__ static int swz_k(int row) { return U == 16 ? (row & 15) : ((row >> 1) & 7); }
+    __device__ static int swz_v(int row) { return U == 16 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+    static_assert(U == 16 || U == 8, "head_dim 128 or 64");
 };
 
 // acc + lo(a) + hi(a) for a packed bf16 pair, in one v_dot2_f32_bf16 against
@@ -180,9 +188,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
 
     // ---- direct loads.  Instruction i = wave + 4n (n < LOADS) of a tile fills
     // LDS bytes [1024i, 1024i + 1024): lane L writes unit 64i + L, i.e. row
-    // RPI*i + L/U at swizzled position (L % U) ^ swz(row).  Instruction i's
-    // first row RPI*i is a multiple of U (U <= 16), so a lane's swizzle is the
-    // same in every instruction: one K and one V lane offset.
+    // RPI*i + L/U at swizzled position (L % U) ^ swz(row).  A wave's
+    // instructions are 4 RPI rows apart and both swizzles repeat with a period
+    // that divides 4 RPI, so a lane's swizzle is the same in every one of its
+    // instructions: one K and one V lane offset.
     constexpr int RPI = 64 / U;                     // key rows per load instruction
     const uint32_t rowbytes = (uint32_t)kvstride * 2;
     const int lrow = lane / U;                      // row of this lane within an instruction
