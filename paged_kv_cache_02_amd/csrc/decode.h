@@ -63,13 +63,19 @@ __device__ __forceinline__ int stream_chunk(int T, int nwaves) {
     return max(1, (T + nwaves - 1) / nwaves);
 }
 // Block-wide (256 threads): s_cum[b] = tiles of sequences 0..b-1, b <= B.
+// The lengths themselves are kept in s_len[b] (read from global memory once).
 __device__ __forceinline__ void stream_prefix_tiles(const int32_t *seqlens, int B,
-                                                    int window_left, int *s_cum, int *s_part) {
+                                                    int window_left, int *s_cum, int *s_part,
+                                                    int *s_len) {
     const int tid = threadIdx.x;
     const int per = (B + 255) / 256;
     const int b0 = tid * per;
     int sum = 0;
-    for (int b = b0; b < min(b0 + per, B); ++b) sum += stream_tiles(seqlens[b], window_left);
+    for (int b = b0; b < min(b0 + per, B); ++b) {
+        const int L = seqlens[b];
+        s_len[b] = L;
+        sum += stream_tiles(L, window_left);
+    }
     s_part[tid] = sum;
     __syncthreads();
     if (tid < 64) {   // exclusive scan of the 256 strip sums by one wave
@@ -94,7 +100,7 @@ __device__ __forceinline__ void stream_prefix_tiles(const int32_t *seqlens, int 
     int run = s_part[tid];
     for (int b = b0; b < min(b0 + per, B); ++b) {
         s_cum[b] = run;
-        run += stream_tiles(seqlens[b], window_left);
+        run += stream_tiles(s_len[b], window_left);
     }
     if (tid == 255) s_cum[B] = run;   // strip 255 ends at B (B <= 256 * per)
     __syncthreads();

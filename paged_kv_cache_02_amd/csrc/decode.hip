@@ -60,6 +60,8 @@ constexpr int kRing = kDepth + 1;
 // s_waitcnt immediate for vmcnt(0) with expcnt/lgkmcnt left at their maxima
 // (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
 constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);
+// the same immediate for vmcnt(n), n < 64
+constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <int HU>
 __device__ __forceinline__ float bcast_head(float x, int hh) {
@@ -102,10 +104,11 @@ struct DecodeWave {
     }
 
     // Q as the MFMA B operand: lane (j, r) holds dims 32c+8j..+8 of head h0 + r%HU.
-    __device__ void load_q(const void *q, size_t first_head_row) {
+    __device__ void load_q(const void *q, size_t first_head_row) { load_q_to(qf, q, first_head_row); }
+    __device__ void load_q_to(bf16x8 (&dst)[KSTEPS], const void *q, size_t first_head_row) const {
         const char *qp = (const char *)q + ((first_head_row + (r % HU)) * D + 8 * j) * 2;
 #pragma unroll
-        for (int c = 0; c < KSTEPS; ++c) qf[c] = __builtin_bit_cast(bf16x8, ld16(qp, 64 * c));
+        for (int c = 0; c < KSTEPS; ++c) dst[c] = __builtin_bit_cast(bf16x8, ld16(qp, 64 * c));
     }
 
     __device__ void reset() {
@@ -454,6 +457,7 @@ template <int D, int HU, bool FUSED>
 __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
 {
     __shared__ int s_cum[kStreamMaxB + 1];   // tiles of the sequences before b
+    __shared__ int s_len[kStreamMaxB];       // cache_seqlens
     __shared__ int s_part[256];
 
     const int tid = threadIdx.x;
@@ -465,7 +469,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
     const int h0 = hg * HU;
     const int g = h0 / a.G;
 
-    stream_prefix_tiles(a.seqlens, a.B, a.window_left, s_cum, s_part);
+    stream_prefix_tiles(a.seqlens, a.B, a.window_left, s_cum, s_part, s_len);
     const int T = s_cum[a.B];
     const int nw = W * kWaves;
     const int chunk = stream_chunk(T, nw);
@@ -505,7 +509,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
         }
         b_ld = readfirstlane(lo);
     }
-    int L_ld = readfirstlane(a.seqlens[b_ld]);
+    int L_ld = readfirstlane(s_len[b_ld]);
     int t_ld = readfirstlane((stream_lo(L_ld, a.window_left) & ~15) + 16 * (x0 - s_cum[b_ld]));
     int x_ld = x0;                                // flattened index of the cursor's tile
     // advance the load cursor by one tile, skipping sequences with no tiles
@@ -516,7 +520,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
             do { ++b_ld; } while (b_ld < a.B && s_cum[b_ld + 1] == s_cum[b_ld]);
             b_ld = readfirstlane(b_ld);
             if (b_ld < a.B) {
-                L_ld = readfirstlane(a.seqlens[b_ld]);
+                L_ld = readfirstlane(s_len[b_ld]);
                 t_ld = stream_lo(L_ld, a.window_left) & ~15;
             }
         }
@@ -537,13 +541,34 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
                 const int mid = (lo + hi) >> 1;
                 if (s_cum[mid] <= x) lo = mid; else hi = mid;
             }
-            const int t = (stream_lo(a.seqlens[lo], a.window_left) & ~15) + 16 * (x - s_cum[lo]);
+            const int t = (stream_lo(s_len[lo], a.window_left) & ~15) + 16 * (x - s_cum[lo]);
             v = a.block_table[(size_t)lo * a.mbps + (t >> a.bs_log2)];
         }
         return v;
     };
     int xb = x0, blk_batch = gather(x0), blk_ahead = 0;
     if (x0 + 64 < x_end) blk_ahead = gather(x0 + 64);
+
+    // Q of the first two sequences of the range, loaded before the first
+    // tiles and waited for on their own after the tiles are issued, so that
+    // neither the first tile nor the change to the second sequence waits for
+    // the K/V loads in flight.  A later sequence (ranges over short
+    // sequences) loads its Q at the change and waits for it there.
+    using DW = DecodeWave<D, HU>;
+    bf16x8 q_next[DW::KSTEPS];
+    int q_held = b_ld, q_nb = -1;
+    if (s_cum[b_ld + 1] < x_end) {
+        int lo = b_ld + 1, hi = a.B;              // s_cum[lo] <= s_cum[b_ld+1] < s_cum[hi]
+        const int xs = s_cum[b_ld + 1];
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_cum[mid] <= xs) lo = mid; else hi = mid;
+        }
+        q_nb = readfirstlane(lo);
+    }
+    w.load_q(a.q, (size_t)q_held * a.Hq + h0);
+    if (q_nb >= 0) w.load_q_to(q_next, a.q, (size_t)q_nb * a.Hq + h0);
+    __builtin_amdgcn_sched_barrier(0);
     auto block_at = [&]() {
         if (x_ld - xb >= 64) {                    // next batch (read 64 tiles ago)
             xb += 64;
@@ -643,6 +668,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
         if (k + 1 < n) advance();
         __builtin_amdgcn_sched_barrier(0);
     }
+    // every tile issues KSTEPS + VLD loads: this waits for the Q loads only
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(kDepth * (DW::KSTEPS + DW::VLD)));
     int blk_next = kDepth < n ? block_at() : 0;
     for (int it = 0; it < n_pad; it += kRing) {
 #pragma unroll
@@ -664,13 +691,21 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
                 if (rb[k] != seg_b) {                 // entering a new sequence
                     if (seg_b >= 0) flush();
                     seg_b = rb[k];
-                    const int L = a.seqlens[seg_b];
+                    const int L = s_len[seg_b];
                     seg_lo = stream_lo(L, a.window_left);
                     seg_hi = L;
-                    w.load_q(a.q, (size_t)seg_b * a.Hq + h0);
-                    // Wait for Q here, inside the rare branch: otherwise the
-                    // wait lands after the join and drains the ring every trip.
-                    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                    if (seg_b != q_held) {
+                        if (seg_b == q_nb) {
+#pragma unroll
+                            for (int c = 0; c < DW::KSTEPS; ++c) w.qf[c] = q_next[c];
+                        } else {
+                            w.load_q(a.q, (size_t)seg_b * a.Hq + h0);
+                            // Wait for Q here, inside the rare branch: otherwise the
+                            // wait lands after the join and drains the ring every trip.
+                            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                        }
+                        q_held = seg_b;
+                    }
                     w.reset();
                 }
                 w.process(rt[k], seg_lo, seg_hi, true, kbuf[k], vbuf[k]);
