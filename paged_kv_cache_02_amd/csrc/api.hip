@@ -48,11 +48,16 @@ int device_cus() {
     return cached[dev];
 }
 
-// Balanced schedule: two resident 4-wave workgroups per compute unit, spread
-// over the head groups.
+// Balanced schedule: one 4-wave workgroup (one wave per SIMD) per compute
+// unit, spread over the head groups.  With two per unit the one dispatched
+// second gets its memory requests served only after the first has finished
+// (a timeline probe showed its first tile arriving ~50 us into a ~120 us
+// launch), so the two ran one after the other and the second one's spread
+// of end times set the launch time; one per unit measured 5 % faster on the
+// 64-sequence workload.
 int stream_wgs_per_head_group(int Hq, int Hkv) {
     const int NHG = Hq / decode_heads_per_unit(Hq / Hkv);
-    return std::max(1, (2 * device_cus() + NHG - 1) / NHG);
+    return std::max(1, (device_cus() + NHG - 1) / NHG);
 }
 
 // Balanced-schedule workspace: the fused merge's arrival counters (one per
