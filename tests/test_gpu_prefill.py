@@ -58,6 +58,7 @@ CASES = [
     ([130, 20], [500, 20], 8, 4, 128, True, -1),           # chunk: queries at the end
     ([0, 33, 1], [10, 40, 1000], 4, 2, 128, True, 64),
     ([300], None, 4, 4, 128, True, 0),
+    ([1, 63, 64, 65, 129, 192, 257], None, 8, 4, 64, True, -1),   # D 64: 1 to 5 key tiles
 ]
 
 
@@ -78,6 +79,7 @@ PAGED = [
     ([64, 100], [64 + 300, 100], 16, 8, 64, 16, True, 128),
     ([512, 3], [1000, 700], 8, 2, 128, 32, True, -1),
     ([129, 1], [129, 2000], 8, 8, 128, 64, False, 17),
+    ([40, 1, 200], [40 + 150, 70, 200 + 64], 8, 2, 64, 16, False, -1),   # D 64 ring, no window
 ]
 
 
