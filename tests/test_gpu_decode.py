@@ -245,3 +245,31 @@ def test_two_launch_decode_vs_oracle(case):
     o, l = oracle_decode(c)
     assert_close(out, o, torch.bfloat16, "two-launch out")
     assert_close(lse, l, torch.bfloat16, "two-launch lse", lse=True)
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,window,B", [(128, 32, 8, -1, 300), (64, 16, 2, 9, 1200)])
+def test_decode_many_short_sequences(D, Hq, Hkv, window, B):
+    """Hundreds of 1..40-key sequences: each wave's range of the balanced
+    schedule crosses several sequences, so the Q of the second sequence
+    (preloaded) and of later ones (loaded at the change) are both used;
+    one launch and two launches against the oracle."""
+    banner(f"many short sequences D={D} window={window}")
+    from paged_kv_cache_02_amd import pkv
+    rng = np.random.default_rng(61)
+    lengths = rng.integers(1, 40, size=B, endpoint=True).tolist()
+    c = synth.decode_case(62, lengths, Hq, Hkv, D, 16, torch.bfloat16, with_sink=True,
+                          window_left=window, poison=True)
+    o, l = oracle_decode(c)
+    out, lse = run_decode(c)
+    assert_close(out, o, torch.bfloat16, "one launch out")
+    assert_close(lse, l, torch.bfloat16, "one launch lse", lse=True)
+    ws = torch.empty(pkv.decode_workspace_bytes(c.B, Hq, Hkv, D, 16, c.max_seqlen_k, 0,
+                                                torch.bfloat16), dtype=torch.uint8, device="cuda")
+    out2 = torch.empty(c.B, Hq, D, dtype=torch.bfloat16, device="cuda")
+    lse2 = torch.empty(c.B, Hq, dtype=torch.float32, device="cuda")
+    pkv.paged_decode_stage(dev(c.q), dev(c.k_cache), dev(c.v_cache), dev(c.block_table),
+                           dev(c.cache_seqlens), c.sm_scale, c.max_seqlen_k, ws, c.window_left)
+    pkv.paged_decode_finish(out2, ws, Hkv, sink=dev(c.sink), lse=lse2)
+    torch.cuda.synchronize()
+    assert_close(out2, o, torch.bfloat16, "two launches out")
+    assert_close(lse2, l, torch.bfloat16, "two launches lse", lse=True)
