@@ -421,6 +421,7 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
         a.cu_k = cu_seqlens_k; a.sink = sink; a.B = B; a.Hq = num_q_heads; a.Hkv = num_kv_heads;
         a.G = num_q_heads / num_kv_heads; a.D = head_dim; a.bs_log2 = bs_log2;
         a.mbps = max_blocks_per_seq; a.window_left = window_left;
+        a.hpw = prefill_heads_per_wg(a.G);
         a.max_q_tiles = (max_seqlen_q + prefill_block_m() - 1) / prefill_block_m();
         a.scale_log2 = sm_scale * kLog2e;
         return launch_prefill_bf16(a, s);

@@ -157,7 +157,8 @@ struct PrefillArgs {
     const float *sink;
     int32_t B, Hq, Hkv, G, D;
     int32_t bs_log2, mbps, window_left;
-    int32_t max_q_tiles;         // ceil(max_seqlen_q / BLOCK_M)
+    int32_t hpw;                 // query heads per workgroup: prefill_heads_per_wg(G)
+    int32_t max_q_tiles;         // ceil(max_seqlen_q / prefill_block_m())
     float scale_log2;
 };
 
@@ -167,6 +168,7 @@ pkv_status launch_decode_stream_bf16(const StreamArgs &a, hipStream_t stream);
 pkv_status launch_merge(const MergeArgs &a, hipStream_t stream);
 pkv_status launch_rows(const RowArgs &a, bool bf16, hipStream_t stream);
 pkv_status launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream);
+int prefill_heads_per_wg(int G);
 int prefill_block_m();
 pkv_status launch_reshape_and_cache(const void *key, const void *value, void *k_cache,
                                     void *v_cache, const int32_t *slot_mapping, int32_t T,

@@ -11,10 +11,15 @@
 // query chunk can attend to keys already in the cache.
 //
 // gfx950 design:
-//   * workgroup = (request, 128-row query tile, query head), 4 waves of 32
-//     rows; tiles are issued longest-first (highest tile index first), and
-//     the query heads of one kv head are placed on the same XCD so that its
-//     K/V tiles are fetched into that XCD's L2 once for all of them;
+//   * workgroup = 4 waves of 32 query rows that share one kv head: the
+//     query heads of a GQA group at the same 32 positions when the group
+//     has 4 (or a multiple of 4) heads, else 2 heads x 64 positions or 1 head
+//     x 128 positions.  Waves that read the same K/V at the same positions
+//     see the same causal and window range, so no wave idles at the
+//     diagonal while the others finish it.  Tiles are issued longest-first
+//     (highest position tile first), and the workgroups of one kv head are
+//     placed on the same XCD so that its K/V tiles are fetched into that
+//     XCD's L2 once for all of them;
 //   * K and V tiles of 64 keys go straight from global memory into LDS with
 //     the load-to-LDS forms of buffer_load_dwordx4 / global_load_dwordx4 (no
 //     register staging, no VALU work), double buffered: the next tile's loads
@@ -42,7 +47,6 @@ namespace pkv {
 
 namespace {
 
-constexpr int BM = 128;   // query rows per workgroup
 constexpr int BN = 64;    // keys per tile
 constexpr float kTau = 8.0f;
 // LDS operand reads are issued this many MFMAs ahead of their use (K for S,
@@ -129,23 +133,39 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
     const int lr = lane & 31;     // row within the wave / column of the MFMA
     const int lh = lane >> 5;     // lane half
 
-    // ---- which (request, q tile, head) ----
-    // Consecutive workgroups go to the eight XCDs in turn, and each XCD has
-    // its own L2.  Position p among the Hq workgroups of one (request, tile)
-    // takes kv head p % Hkv and query head (p % Hkv) * G + p / Hkv, so the G
-    // query heads that read the same K/V land on the same XCD (whenever Hkv
-    // divides 8 or 8 divides Hkv, and Hq is a multiple of 8) and share its L2.
+    // ---- which (request, positions, kv head, query heads) ----
+    // A workgroup holds hpw query heads of one kv head (hpw = 4, 2 or 1,
+    // dividing G) at bm = 128 / hpw positions; wave w takes head w % hpw of
+    // them and the 32 rows from 32 (w / hpw).  The grid has Hq workgroups per
+    // (request, 128-position tile): G / hpw head subgroups x hpw position
+    // blocks for each kv head.  Consecutive workgroups go to the eight XCDs
+    // in turn (each with its own L2), and an XCD hands its workgroups to its
+    // shader engines in turn.  Position p among the Hq takes kv head p % Hkv,
+    // so the workgroups that read the same K/V land on the same XCD (whenever
+    // Hkv divides 8 or 8 divides Hkv, and Hq is a multiple of 8), and the
+    // position blocks of one tile are consecutive in that XCD's queue, so
+    // they spread over its shader engines.  The block order rotates from tile
+    // to tile: the partly empty last tiles of the requests would otherwise
+    // hand their work to the same engines, and an XCD stalls its queue on
+    // the first full engine while the others sit idle.
+    const int hpw = a.hpw;
+    const int bm = 128 / hpw;                       // positions per workgroup
+    const int ng = a.G / hpw;                       // head subgroups per kv head
     const int p = blockIdx.x % a.Hq;
-    const int h = (p % a.Hkv) * a.G + p / a.Hkv;
     const int slot = blockIdx.x / a.Hq;
+    const int g = p % a.Hkv;
+    const int hs = (p / a.Hkv) % ng;
+    const int blk = (hpw - 1 - (p / a.Hkv) / ng + slot) % hpw;   // position block
+    const int h = g * a.G + hs * hpw + wave % hpw;
     const int r = slot % a.B;
     const int qt = a.max_q_tiles - 1 - slot / a.B;
     const int cq0 = a.cu_q[r], Lq = a.cu_q[r + 1] - cq0;
-    if (qt * BM >= Lq) return;
+    if (qt * 128 + blk * bm >= Lq) return;
     const int ck0 = a.cu_k[r], Lk = a.cu_k[r + 1] - ck0;
-    const int g = h / a.G;
-    const int row0 = qt * BM;                       // first row of the tile (within request)
-    const int nrows = min(BM, Lq - row0);
+    // the sink logit is needed only at the end: fetch it now, off the tail
+    const float sig = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+    const int row0 = qt * 128 + blk * bm;           // first row of the workgroup (within request)
+    const int nrows = min(bm, Lq - row0);
     const int pos0 = Lk - Lq + row0;                // position of the tile's first row
     const int pos_last = pos0 + nrows - 1;
     int kv_lo = 0;
@@ -155,7 +175,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
     const int ntiles = kv_hi > kv_lo ? (kv_hi - t_begin + BN - 1) / BN : 0;
 
     // this wave's rows and visible key range
-    const int wrow0 = row0 + 32 * wave;
+    const int wrow0 = row0 + 32 * (wave / hpw);
     const int wrows = max(0, min(32, Lq - wrow0));
     const int wpos0 = Lk - Lq + wrow0;
     const int wpos1 = wpos0 + wrows - 1;
@@ -391,34 +411,49 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
     }
 
     // ---- epilogue: normalise with the sink, write the wave's rows ----
+    // The accumulators hold 4 dims of a row per lane, so a direct store would
+    // write 32 separate 16-byte pieces per instruction.  Instead each wave
+    // stages its 32 rows in LDS (the K/V buffers are free after the last
+    // barrier) and writes whole rows, 16 bytes per lane.  Staged rows are
+    // padded by 16 bytes so that both the 8-byte writes (rows 16 apart share
+    // banks) and the 16-byte reads (one row per 16 lanes) stay conflict-free.
     l += l1;
     l += shfl_xor(l, 32);
-    const float sig = a.sink ? a.sink[h] * kLog2e : -INFINITY;
     const float Mt = fmaxf(l > 0.f ? m : kNoMax, sig);
     const float sc = fast_exp2(m - Mt);
     const float Lt = l * sc + fast_exp2(sig - Mt);
     const float f = Lt > 0.f ? sc / Lt : 0.f;
-    if (lr < wrows) {
-        uint16_t *op = (uint16_t *)a.out + (size_t)(cq0 + wrow0 + lr) * qstride + (size_t)h * D;
+    constexpr int kRowPad = D * 2 + 16;
+    static_assert(4 * 32 * kRowPad <= 2 * TL::BUF, "staging fits in the K/V buffers");
+    char *stage = lds + wave * 32 * kRowPad;
 #pragma unroll
-        for (int t = 0; t < DT; ++t)
+    for (int t = 0; t < DT; ++t)
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = 32 * t + 8 * q4 + 4 * lh;
-                const u32x2 w = {pack_bf16x2(o[t][4 * q4] * f, o[t][4 * q4 + 1] * f),
-                                 pack_bf16x2(o[t][4 * q4 + 2] * f, o[t][4 * q4 + 3] * f)};
-                *reinterpret_cast<u32x2 *>(op + d) = w;
-            }
-        if (a.lse && lh == 0)
-            a.lse[(size_t)(cq0 + wrow0 + lr) * a.Hq + h] =
-                Lt > 0.f ? Mt * kLn2 + logf(Lt) : -INFINITY;
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int d = 32 * t + 8 * q4 + 4 * lh;
+            const u32x2 w = {pack_bf16x2(o[t][4 * q4] * f, o[t][4 * q4 + 1] * f),
+                             pack_bf16x2(o[t][4 * q4 + 2] * f, o[t][4 * q4 + 3] * f)};
+            *reinterpret_cast<u32x2 *>(stage + lr * kRowPad + d * 2) = w;
+        }
+    constexpr int LPR = D / 8;      // lanes per row, 16 bytes each
+    constexpr int RPS = 64 / LPR;   // rows per store instruction
+    const int srow = lane / LPR, sunit = lane % LPR;
+    uint16_t *ob = (uint16_t *)a.out + (size_t)(cq0 + wrow0) * qstride + (size_t)h * D;
+#pragma unroll
+    for (int k = 0; k < 32 / RPS; ++k) {
+        const int row = srow + RPS * k;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * kRowPad + sunit * 16);
+        if (row < wrows) *reinterpret_cast<u32x4 *>(ob + (size_t)row * qstride + sunit * 8) = v;
     }
+    if (a.lse && lh == 0 && lr < wrows)
+        a.lse[(size_t)(cq0 + wrow0 + lr) * a.Hq + h] = Lt > 0.f ? Mt * kLn2 + logf(Lt) : -INFINITY;
 }
 
 }  // namespace
 
 pkv_status launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream)
 {
+    if (a.hpw != prefill_heads_per_wg(a.G) || a.Hq % a.hpw) return PKV_ERR_SHAPE;
     const long long grid = (long long)a.B * a.max_q_tiles * a.Hq;
     if (grid == 0) return PKV_OK;
     if (grid > 0x7fffffffLL) return PKV_ERR_SHAPE;
@@ -447,6 +482,7 @@ pkv_status launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream)
     return launch_status();
 }
 
-int prefill_block_m() { return BM; }
+int prefill_heads_per_wg(int G) { return G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1; }
+int prefill_block_m() { return 128; }
 
 }  // namespace pkv
