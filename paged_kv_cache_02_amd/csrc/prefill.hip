@@ -415,8 +415,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
     // write 32 separate 16-byte pieces per instruction.  Instead each wave
     // stages its 32 rows in LDS (the K/V buffers are free after the last
     // barrier) and writes whole rows, 16 bytes per lane.  Staged rows are
-    // padded by 16 bytes so that both the 8-byte writes (rows 16 apart share
-    // banks) and the 16-byte reads (one row per 16 lanes) stay conflict-free.
+    // padded by 16 bytes so that consecutive rows start on different banks.
     l += l1;
     l += shfl_xor(l, 32);
     const float Mt = fmaxf(l > 0.f ? m : kNoMax, sig);
@@ -457,19 +456,22 @@ pkv_status launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream)
     const long long grid = (long long)a.B * a.max_q_tiles * a.Hq;
     if (grid == 0) return PKV_OK;
     if (grid > 0x7fffffffLL) return PKV_ERR_SHAPE;
-    // more than 64 KiB of dynamic LDS: raise the per-kernel limit once
-    static const bool raised = [] {
-        hipFuncSetAttribute((const void *)prefill_bf16_kernel<128, false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Tile<128>::BUF);
-        hipFuncSetAttribute((const void *)prefill_bf16_kernel<128, true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Tile<128>::BUF);
-        hipFuncSetAttribute((const void *)prefill_bf16_kernel<64, false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Tile<64>::BUF);
-        hipFuncSetAttribute((const void *)prefill_bf16_kernel<64, true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Tile<64>::BUF);
-        return true;
+    // 64 KiB of dynamic LDS at D 128: raise the per-kernel limit once; a
+    // failure there is reported by every call rather than by a faulting launch
+    static const hipError_t raised = [] {
+        hipError_t first = hipSuccess;
+        auto set = [&](const void *fn, int bytes) {
+            const hipError_t e =
+                hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+            if (first == hipSuccess) first = e;
+        };
+        set((const void *)prefill_bf16_kernel<128, false>, 2 * Tile<128>::BUF);
+        set((const void *)prefill_bf16_kernel<128, true>, 2 * Tile<128>::BUF);
+        set((const void *)prefill_bf16_kernel<64, false>, 2 * Tile<64>::BUF);
+        set((const void *)prefill_bf16_kernel<64, true>, 2 * Tile<64>::BUF);
+        return first;
     }();
-    (void)raised;
+    if (raised != hipSuccess) return PKV_ERR_HIP;
     const bool paged = a.block_table != nullptr;
     const dim3 g((unsigned)grid), b(256);
     if (a.D == 128) {

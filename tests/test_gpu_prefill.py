@@ -59,6 +59,10 @@ CASES = [
     ([0, 33, 1], [10, 40, 1000], 4, 2, 128, True, 64),
     ([300], None, 4, 4, 128, True, 0),
     ([1, 63, 64, 65, 129, 192, 257], None, 8, 4, 64, True, -1),   # D 64: 1 to 5 key tiles
+    # GQA groups that set the workgroup shape: heads per workgroup x positions
+    ([70, 333], None, 12, 4, 128, True, -1),       # G 3: 1 head x 128, three head subgroups
+    ([129, 40, 260], None, 12, 2, 64, True, 50),   # G 6: 2 heads x 64, three subgroups, window
+    ([300, 17], None, 16, 1, 128, False, -1),      # G 16: 4 heads x 32, four subgroups
 ]
 
 
@@ -80,6 +84,7 @@ PAGED = [
     ([512, 3], [1000, 700], 8, 2, 128, 32, True, -1),
     ([129, 1], [129, 2000], 8, 8, 128, 64, False, 17),
     ([40, 1, 200], [40 + 150, 70, 200 + 64], 8, 2, 64, 16, False, -1),   # D 64 ring, no window
+    ([90, 200], [300, 200], 16, 2, 128, 16, True, -1),                   # G 8: two head subgroups
 ]
 
 
@@ -94,6 +99,30 @@ def test_prefill_paged_vs_oracle(case, dtype):
     o, l = oracle_prefill(c)
     assert_close(out, o, dtype, "out")
     assert_close(lse, l, dtype, "lse", lse=True)
+
+
+@pytest.mark.parametrize("heads", [(4, 4), (8, 4), (12, 4), (8, 2), (12, 2), (16, 2), (16, 1)],
+                         ids=lambda x: f"{x[0]}q{x[1]}kv")
+def test_prefill_every_row_written(heads):
+    """Every (row, head) of out and lse is written exactly by the grid: both
+    start as NaN, and lengths straddle the 32-row blocks and 128-row tiles
+    that the GQA group size arranges into workgroups."""
+    from paged_kv_cache_02_amd import pkv
+    Hq, Hkv = heads
+    banner(f"prefill coverage {Hq}/{Hkv}")
+    lens = [1, 31, 32, 33, 95, 128, 161, 255]
+    c = synth.prefill_case(80, lens, lens, Hq, Hkv, 64, torch.bfloat16, True)
+    T = c.q.shape[0]
+    out = torch.full((T, Hq, 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((T, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    pkv.varlen_prefill(dev(c.q), dev(c.cu_seqlens_q), dev(c.cu_seqlens_k), c.max_seqlen_q,
+                       c.max_seqlen_k, c.sm_scale, c.Hkv, k=dev(c.k), v=dev(c.v), sink=dev(c.sink),
+                       window_left=c.window_left, lse=lse, out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any()
+    o, l = oracle_prefill(c)
+    assert_close(out, o, torch.bfloat16, "out")
+    assert_close(lse, l, torch.bfloat16, "lse", lse=True)
 
 
 def test_prefill_deterministic():
