@@ -272,6 +272,62 @@ def bench_decode(c, name, steps, warmup, partition_size, reps, traffic_key=None,
     return res, out
 
 
+def bench_decode_append(c, name, steps, warmup, reps):
+    """Decode with the new token appended: each sequence's last cached token of
+    the workload becomes the token being appended (L = cache_seqlens - 1
+    tokens already cached), so the attended keys are those of the plain
+    decode.  Timed as one pkv_paged_decode_append launch, and beside it the
+    unfused equivalent: reshape_and_cache of the B new rows, then decode."""
+    B, Hq, D, bs = c.B, c.Hq, c.D, c.block_size
+    kc, vc, tables = replicate_pool(c, reps)
+    q = c.q.cuda()
+    L = (c.cache_seqlens - 1).cuda()
+    L1 = c.cache_seqlens.cuda()
+    kn = synth.to_dtype(synth.normal(21, (B, c.Hkv, D), stream=1), q.dtype).cuda()
+    vn = synth.to_dtype(synth.normal(21, (B, c.Hkv, D), stream=2), q.dtype).cuda()
+    sink = None if c.sink is None else c.sink.cuda()
+    out = torch.empty_like(q)
+    msk = c.max_seqlen_k
+    ws = torch.zeros(max(pkv.decode_workspace_bytes(B, Hq, c.Hkv, D, bs, msk, 0, q.dtype), 256),
+                     dtype=torch.uint8, device="cuda")
+    ar = torch.arange(B, device="cuda")
+    slots = [(t[ar, (L // bs).long()] * bs + L % bs).to(torch.int32) for t in tables]
+
+    def fused(i, kt):
+        bt = tables[i % reps]
+        kt.time("append_decode", lambda: pkv.paged_decode_append(
+            q, kn, vn, kc, vc, bt, L, c.sm_scale, sink=sink, window_left=c.window_left,
+            max_seqlen_k=msk - 1, out=out, workspace=ws))
+
+    def unfused(i, kt):
+        bt = tables[i % reps]
+        kt.time("reshape_and_cache", lambda: pkv.reshape_and_cache(kn, vn, kc, vc,
+                                                                   slots[i % reps]))
+        kt.time("decode", lambda: pkv.paged_decode(q, kc, vc, bt, L1, c.sm_scale, sink=sink,
+                                                   window_left=c.window_left, max_seqlen_k=msk,
+                                                   out=out, workspace=ws))
+
+    ms, kt = timed_steps(fused, steps, warmup, launches_per_step=1)
+    ms_u, kt_u = timed_steps(unfused, steps, warmup)
+    kv, qb, table = decode_bytes(c)          # K/V of the L + 1 attended keys, q, table
+    new_rows = B * c.Hkv * D * 2 * 2         # the new K/V rows, written into the cache
+    step_bytes = kv + 2 * qb + table + new_rows
+    k_ms = kt.mean_ms("append_decode")
+    res = {
+        "name": name, "value": round(step_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "ms_per_step": round(ms, 4), "algorithmic_bytes": step_bytes,
+        "kernels_ms": {"append_decode": round(k_ms, 4)},
+        "roofline": roofline("hbm", step_bytes / (k_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+        "unfused_ms_per_step": round(ms_u, 4),
+        "unfused_kernels_ms": {"reshape_and_cache": round(kt_u.mean_ms("reshape_and_cache"), 4),
+                               "decode": round(kt_u.mean_ms("decode"), 4)},
+        "speedup_vs_unfused": round(ms_u / ms, 3),
+    }
+    del kc, vc, tables
+    torch.cuda.empty_cache()
+    return res
+
+
 # ----------------------------------------------------------------------------
 # prefill workloads
 # ----------------------------------------------------------------------------
@@ -413,6 +469,10 @@ def main():
                                   reps=2, two_stage=True)
             workloads["decode_two_launches"] = r2s
             log(f"decode as stage + merge launches: {r2s['value']} GB/s step")
+            ra = bench_decode_append(c2, "decode_append_64x_U512-4096", steps, warmup, reps=2)
+            workloads["decode_append"] = ra
+            log(f"decode with the new token appended: {ra['value']} GB/s step, "
+                f"{ra['speedup_vs_unfused']}x the unfused reshape_and_cache + decode")
 
     if ARGS.only in ("all", "prefill"):
         log("prefill workload (8 reqs U[256,4096], 32/8 heads, D 128, sink)")

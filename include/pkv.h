@@ -12,6 +12,10 @@
  *                           (Transformers "Paged attention" doc, decode path:
  *                           block_table and cache_seqlens; vLLM page,
  *                           single_query_cached_kv_attention)
+ *   pkv_paged_decode_append store each sequence's new K/V token into the cache
+ *                           and attend to it in the same call (Transformers
+ *                           doc, flash_attn_with_kvcache: the cache is
+ *                           "updated in place" at cache_seqlens)
  *   pkv_merge_partitions    log-sum-exp merge of split-KV partition results
  *                           (vLLM page, single_query_cached_kv_attention: the
  *                           partitioned "v2" path with exp_sums / max_logits /
@@ -176,6 +180,49 @@ pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_
                             int32_t max_seqlen_k, float sm_scale, int32_t window_left,
                             int32_t partition_size, void *workspace, size_t workspace_bytes,
                             pkv_dtype dtype, void *stream);
+
+/*
+ * pkv_paged_decode_append -- decode with the new token appended in the same
+ * call (Transformers doc, flash_attn_with_kvcache: k and v are written into
+ * the cache at index cache_seqlens[b], the cache is updated in place, and the
+ * query attends to the cache including the new token; the doc's example puts
+ * the new tokens of lengths 30 / 32 / 70 at slots 94 / 32 / 198 with
+ * block_size 32).  For each sequence b with L = cache_seqlens[b] tokens
+ * already cached: k_new[b] / v_new[b] are stored at position L (slot
+ * block_table[b][L / block_size] * block_size + L % block_size), and the
+ * query, at position L, attends to keys 0..L (window: L - window_left <= j)
+ * with the sink -- exactly pkv_reshape_and_cache of the new rows followed by
+ * pkv_paged_decode over cache_seqlens[b] + 1 keys, in one launch.
+ *
+ *   k_new, v_new    [B, num_kv_heads, head_dim], same dtype as the caches
+ *   k_cache,        written at the new tokens' slots and nowhere else
+ *   v_cache
+ *   cache_seqlens   [B] int32, NOT modified (the caller advances it).
+ *                   Contract: 0 <= cache_seqlens[b] <= max_seqlen_k, the
+ *                   first cache_seqlens[b] / block_size + 1 entries of row b
+ *                   are valid block ids < num_blocks, and no other sequence
+ *                   of the call reads the slot of position cache_seqlens[b].
+ *   max_seqlen_k    host upper bound on cache_seqlens; max_seqlen_k + 1 <=
+ *                   max_blocks_per_seq * block_size
+ *   workspace       bf16: at least pkv_paged_decode_workspace_bytes(B,
+ *                   num_q_heads, num_kv_heads, head_dim, block_size,
+ *                   max_seqlen_k + 1, 0, PKV_BF16) bytes, zeroed and reused
+ *                   under the same rules as pkv_paged_decode's balanced
+ *                   schedule (B <= 4096); fp32: none (may be NULL).
+ * Other arguments as for pkv_paged_decode.  bf16 runs the balanced schedule
+ * with the merge fused (the wave that reads a sequence's last tile stores its
+ * new row first); fp32 runs one wave per (sequence, head).  Returns
+ * PKV_ERR_SHAPE for B > 4096 in bf16 or when the new token does not fit.
+ */
+pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const void *k_new,
+                                   const void *v_new, void *k_cache, void *v_cache,
+                                   const int32_t *block_table, const int32_t *cache_seqlens,
+                                   const float *sink, int32_t B, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t num_blocks, int32_t max_blocks_per_seq,
+                                   int32_t max_seqlen_k, float sm_scale, int32_t window_left,
+                                   void *workspace, size_t workspace_bytes, pkv_dtype dtype,
+                                   void *stream);
 
 /*
  * The two stages of pkv_paged_decode with partition_size == 0 in bf16 (the

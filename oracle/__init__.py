@@ -219,3 +219,25 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping):
         NB, key.element_size())
     assert rc == 0, "slot out of range"
     return kc, vc
+
+
+def decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, sink,
+                  sm_scale: float, window_left: int = -1,
+                  units: Optional[Sequence[int]] = None, nthreads: Optional[int] = None):
+    """Decode with the new token appended in the same call (Transformers
+    "Paged attention" doc, decode path: the kvcache kernel writes k and v
+    into the cache at index cache_seqlens[b], updating it in place, and the
+    query attends to the cache including them).  Written as its two steps:
+    row b of k_new / v_new goes to the slot of position cache_seqlens[b]
+    (reshape_and_cache), then decode over cache_seqlens[b] + 1 keys with the
+    query at that position (paged_decode).  Returns ``(out, lse, k_cache
+    after, v_cache after)``."""
+    sl = _np(cache_seqlens).astype(np.int32, copy=False)
+    bt = _np(block_table).astype(np.int32, copy=False)
+    bs = k_cache.shape[1]
+    slots = np.array([slot_of(bt[b], int(sl[b]), bs) for b in range(len(sl))], dtype=np.int32)
+    kc, vc = reshape_and_cache(k_new, v_new, k_cache, v_cache, torch.from_numpy(slots))
+    out, lse = paged_decode(q, kc, vc, block_table, torch.from_numpy(sl + 1), sink, sm_scale,
+                            window_left=window_left, units=units, nthreads=nthreads)
+    return out, lse, kc, vc
+

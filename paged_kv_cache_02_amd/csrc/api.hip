@@ -273,6 +273,58 @@ pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_
     return launch_merge(m, s);
 }
 
+pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const void *k_new,
+                                   const void *v_new, void *k_cache, void *v_cache,
+                                   const int32_t *block_table, const int32_t *cache_seqlens,
+                                   const float *sink, int32_t B, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t num_blocks, int32_t max_blocks_per_seq,
+                                   int32_t max_seqlen_k, float sm_scale, int32_t window_left,
+                                   void *workspace, size_t workspace_bytes, pkv_dtype dtype,
+                                   void *stream)
+{
+    if (B < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_seqlen_k < 0)
+        return PKV_ERR_SHAPE;
+    pkv_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
+    if (st != PKV_OK) return st;
+    if ((st = check_block_size(block_size)) != PKV_OK) return st;
+    if (!dtype_ok(dtype)) return PKV_ERR_UNSUPPORTED;
+    if (window_left < -1) return PKV_ERR_SHAPE;
+    // the new token goes to position cache_seqlens[b] <= max_seqlen_k
+    if ((long long)max_seqlen_k + 1 > (long long)max_blocks_per_seq * block_size)
+        return PKV_ERR_SHAPE;
+    if (dtype == PKV_BF16 && B > kStreamMaxB) return PKV_ERR_SHAPE;
+    if (B == 0) return PKV_OK;
+    if (num_blocks == 0) return PKV_ERR_SHAPE;
+    if (!out || !q || !k_new || !v_new || !k_cache || !v_cache || !block_table || !cache_seqlens)
+        return PKV_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+        !aligned16(v_cache))
+        return PKV_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == PKV_BF16) {
+        const StreamLayout lay = stream_layout(B, num_q_heads, num_kv_heads, head_dim);
+        if (!workspace || workspace_bytes < lay.total || ((uintptr_t)workspace & 255u))
+            return PKV_ERR_WORKSPACE;
+        StreamArgs a = stream_args(q, k_cache, v_cache, block_table, cache_seqlens, B,
+                                   num_q_heads, num_kv_heads, head_dim, block_size,
+                                   max_blocks_per_seq, sm_scale, window_left, workspace);
+        a.counters = (int32_t *)((char *)workspace + lay.counters);
+        a.out = out; a.lse = lse; a.sink = sink;
+        a.k_new = k_new; a.v_new = v_new; a.append = 1;
+        return launch_decode_stream_bf16(a, s);
+    }
+    RowArgs a{};
+    a.mode = 0; a.out = out; a.lse = lse; a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
+    a.block_table = block_table; a.seqlens = cache_seqlens; a.k_new = k_new; a.v_new = v_new;
+    a.append = 1; a.sink = sink; a.B = B; a.Hq = num_q_heads; a.Hkv = num_kv_heads;
+    a.G = num_q_heads / num_kv_heads; a.D = head_dim; a.bs_log2 = ilog2(block_size);
+    a.mbps = max_blocks_per_seq; a.window_left = window_left;
+    a.part_size = max_seqlen_k + 1; a.nparts = 1; a.split = 0;
+    a.scale_log2 = sm_scale * kLog2e;
+    return launch_rows(a, false, s);
+}
+
 pkv_status pkv_paged_decode_stage(const void *q, const void *k_cache, const void *v_cache,
                                   const int32_t *block_table, const int32_t *cache_seqlens,
                                   int32_t B, int32_t num_q_heads, int32_t num_kv_heads,

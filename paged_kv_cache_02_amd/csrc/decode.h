@@ -44,6 +44,11 @@ struct StreamArgs {
     const void *v_cache;
     const int32_t *block_table;
     const int32_t *seqlens;
+    // Append (fused merge only): each sequence's new token k_new/v_new [B, Hkv,
+    // D] is stored at position seqlens[b] and attended as key seqlens[b].
+    const void *k_new;
+    const void *v_new;
+    int32_t append;              // 0 or 1
     int32_t B, Hq, Hkv, G, D;
     int32_t bs_log2, mbps, window_left;
     int32_t W;                   // workgroups (of 4 waves) per head group
@@ -63,8 +68,9 @@ __device__ __forceinline__ int stream_chunk(int T, int nwaves) {
     return max(1, (T + nwaves - 1) / nwaves);
 }
 // Block-wide (256 threads): s_cum[b] = tiles of sequences 0..b-1, b <= B.
-// The lengths themselves are kept in s_len[b] (read from global memory once).
-__device__ __forceinline__ void stream_prefix_tiles(const int32_t *seqlens, int B,
+// The key counts seqlens[b] + add are kept in s_len[b] (the lengths are read
+// from global memory once; add = 1 counts an appended token).
+__device__ __forceinline__ void stream_prefix_tiles(const int32_t *seqlens, int add, int B,
                                                     int window_left, int *s_cum, int *s_part,
                                                     int *s_len) {
     const int tid = threadIdx.x;
@@ -72,7 +78,7 @@ __device__ __forceinline__ void stream_prefix_tiles(const int32_t *seqlens, int 
     const int b0 = tid * per;
     int sum = 0;
     for (int b = b0; b < min(b0 + per, B); ++b) {
-        const int L = seqlens[b];
+        const int L = seqlens[b] + add;
         s_len[b] = L;
         sum += stream_tiles(L, window_left);
     }
@@ -134,6 +140,11 @@ struct RowArgs {
     const void *v_cache;
     const int32_t *block_table;
     const int32_t *seqlens;      // decode: [B]
+    // decode with append: the new token k_new/v_new [B, Hkv, D] is key
+    // seqlens[b] (read from k_new/v_new) and is stored into the cache there
+    const void *k_new;
+    const void *v_new;
+    int32_t append;
     const int32_t *cu_q;         // prefill: [B+1]
     const int32_t *cu_k;
     const float *sink;

@@ -453,7 +453,7 @@ __device__ void stream_merge_wave(const StreamArgs &a, int b, int h0, int s0, in
     if (a.lse && d == 0) a.lse[(size_t)b * a.Hq + h] = lse_v;
 }
 
-template <int D, int HU, bool FUSED>
+template <int D, int HU, bool FUSED, bool APPEND>
 __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
 {
     __shared__ int s_cum[kStreamMaxB + 1];   // tiles of the sequences before b
@@ -469,7 +469,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
     const int h0 = hg * HU;
     const int g = h0 / a.G;
 
-    stream_prefix_tiles(a.seqlens, a.B, a.window_left, s_cum, s_part, s_len);
+    static_assert(FUSED || !APPEND, "the append runs with the fused merge");
+    stream_prefix_tiles(a.seqlens, APPEND ? 1 : 0, a.B, a.window_left, s_cum, s_part, s_len);
     const int T = s_cum[a.B];
     const int nw = W * kWaves;
     const int chunk = stream_chunk(T, nw);
@@ -655,6 +656,34 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
         }
     };
 
+    if constexpr (APPEND) {
+        // Each sequence's new token is key L = s_len[b] - 1, in its last
+        // tile.  The wave that loads that tile is the only reader of the
+        // position in this head group, so it copies the row from k_new /
+        // v_new into the cache slot itself and waits for its stores before
+        // its first tile load.  (Head groups that share a kv head each copy
+        // the same bytes.)  Sequences b_ld .. b_end-1 end inside the range.
+        int b_end = b_ld;
+        while (b_end < a.B && s_cum[b_end + 1] <= x_end) ++b_end;
+        constexpr int LPR = D / 8;                // lanes per row, 16 bytes each
+        constexpr int SPP = 64 / (2 * LPR);       // sequences per pass (K and V rows)
+        for (int bb = b_ld; bb < b_end; bb += SPP) {
+            const int b = bb + lane / (2 * LPR);
+            const int part = lane % (2 * LPR);
+            if (b < b_end) {
+                const int L = s_len[b] - 1;
+                const int blk = a.block_table[(size_t)b * a.mbps + (L >> a.bs_log2)];
+                const bool is_v = part >= LPR;
+                const size_t col = (size_t)g * D + 8 * (part % LPR);
+                const char *src = (const char *)(is_v ? a.v_new : a.k_new) +
+                                  ((size_t)b * a.Hkv * D + col) * 2;
+                char *dst = (char *)(is_v ? a.v_cache : a.k_cache) +
+                            row_off(blk, L) + col * 2;
+                *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(src);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
     u32x4 kbuf[kRing][DecodeWave<D, HU>::KSTEPS], vbuf[kRing][DecodeWave<D, HU>::VLD];
     int rb[kRing], rt[kRing];                     // (sequence, first token) of each ring slot
     const int n_pad = (n + kRing - 1) / kRing * kRing;
@@ -750,11 +779,14 @@ void launch_part(const DecodeArgs &a, int grid, hipStream_t stream) {
 }
 template <int D, int HU>
 void launch_stream(const StreamArgs &a, int grid, hipStream_t stream) {
-    if (a.counters)
-        hipLaunchKernelGGL((decode_stream_kernel<D, HU, true>), dim3(grid), dim3(256), 0, stream,
-                           a);
+    if (a.counters && a.append)
+        hipLaunchKernelGGL((decode_stream_kernel<D, HU, true, true>), dim3(grid), dim3(256), 0,
+                           stream, a);
+    else if (a.counters)
+        hipLaunchKernelGGL((decode_stream_kernel<D, HU, true, false>), dim3(grid), dim3(256), 0,
+                           stream, a);
     else
-        hipLaunchKernelGGL((decode_stream_kernel<D, HU, false>), dim3(grid), dim3(256), 0,
+        hipLaunchKernelGGL((decode_stream_kernel<D, HU, false, false>), dim3(grid), dim3(256), 0,
                            stream, a);
 }
 

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
         const int bh = (int)(wid / a.nparts);
         req = bh / a.Hq;
         h = bh % a.Hq;
-        Lk = a.seqlens[req];
+        Lk = a.seqlens[req] + a.append;
         Lq = 1;
         i = 0;
         qrow = (size_t)bh;
@@ -68,10 +68,32 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
     float m = kNoMax, l = 0.f;
     const int32_t *bt = a.block_table ? a.block_table + (size_t)req * a.mbps : nullptr;
     const int bs_mask = (1 << a.bs_log2) - 1;
+    if (a.mode == 0 && a.append && h % a.G == 0 && pidx == 0) {
+        // store the new token at position Lk - 1; every wave of this call reads
+        // that key from k_new / v_new, so no reader waits for this store
+        const int L = Lk - 1;
+        const size_t slot = ((size_t)bt[L >> a.bs_log2] << a.bs_log2) + (L & bs_mask);
+        const size_t src = ((size_t)req * a.Hkv + g) * D, dst = (slot * a.Hkv + g) * D;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int d = lane + 64 * e;
+            if (BF16) {
+                ((uint16_t *)a.k_cache)[dst + d] = ((const uint16_t *)a.k_new)[src + d];
+                ((uint16_t *)a.v_cache)[dst + d] = ((const uint16_t *)a.v_new)[src + d];
+            } else {
+                ((float *)a.k_cache)[dst + d] = ((const float *)a.k_new)[src + d];
+                ((float *)a.v_cache)[dst + d] = ((const float *)a.v_new)[src + d];
+            }
+        }
+    }
     for (int jj = jlo; jj < jhi; ++jj) {
         size_t row;
         const void *kb, *vb;
-        if (a.k) {
+        if (a.mode == 0 && a.append && jj == Lk - 1) {   // the new token
+            row = req;
+            kb = a.k_new;
+            vb = a.v_new;
+        } else if (a.k) {
             row = (size_t)a.cu_k[req] + jj;
             kb = a.k;
             vb = a.v;

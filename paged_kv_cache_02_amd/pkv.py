@@ -32,6 +32,9 @@ SIGNATURES = {
     "pkv_paged_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                         _I32, _I32, _I32, _I32, _F, _I32, _I32, _P, _SZ,
                                         ctypes.c_int, _P]),
+    "pkv_paged_decode_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32,
+                                               _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F,
+                                               _I32, _P, _SZ, ctypes.c_int, _P]),
     "pkv_paged_decode_stage": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                               _I32, _I32, _I32, _F, _I32, _P, _SZ, ctypes.c_int,
                                               _P]),
@@ -161,6 +164,34 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: floa
         float(sm_scale), window_left, partition_size, _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _dt(q),
         _stream()), "paged_decode")
+    return out
+
+
+def paged_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens,
+                        sm_scale: float, sink=None, window_left: int = -1,
+                        max_seqlen_k: Optional[int] = None, out=None, lse=None, workspace=None):
+    """Store k_new/v_new [B,Hkv,D] at position cache_seqlens[b] of each sequence and
+    attend q [B,Hq,D] to keys 0..cache_seqlens[b]; cache_seqlens is not changed.
+
+    The bf16 path needs a zero-filled workspace of
+    decode_workspace_bytes(..., max_seqlen_k + 1, 0, bf16) bytes (allocated for
+    this call when none is given); fp32 needs none."""
+    B, Hq, D = q.shape
+    NB, bs, Hkv, _ = k_cache.shape
+    if max_seqlen_k is None:
+        max_seqlen_k = int(cache_seqlens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_workspace_bytes(B, Hq, Hkv, D, bs, max_seqlen_k + 1, 0, q.dtype)
+    if workspace is None and need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    _check(lib.pkv_paged_decode_append(
+        _ptr(out), _ptr(_f32(lse, "lse")), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+        _ptr(v_cache), _ptr(_i32(block_table, "block_table")),
+        _ptr(_i32(cache_seqlens, "cache_seqlens")), _ptr(_f32(sink, "sink")), B, Hq, Hkv, D, bs,
+        NB, block_table.shape[1], max_seqlen_k, float(sm_scale), window_left, _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _dt(q),
+        _stream()), "paged_decode_append")
     return out
 
 

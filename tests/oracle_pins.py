@@ -470,4 +470,64 @@ def pin_reshape_and_cache():
         assert torch.equal(kc[blk, int(c.cache_seqlens[b]) % 32], new_k[b])
 
 
+def pin_decode_append():
+    """Decode with the new token appended, against an independent numpy
+    evaluation: keys 0..L-1 gathered from the original cache through the
+    block table, k_new as key L, window L - w <= j, the sink as one more
+    logit.  The returned caches differ from the inputs exactly at the new
+    tokens' slots, which hold k_new / v_new; on the page's decode example
+    those slots are 94, 32 and 198."""
+    rng = np.random.default_rng(77)
+    for trial in range(12):
+        G = [1, 2, 4][trial % 3]
+        Hkv = 1 + trial % 2
+        Hq = G * Hkv
+        B, D, bs, MB = 3, 8, 4, 6
+        NB = B * MB
+        lens = rng.integers(0, MB * bs - 1, size=B)
+        if trial % 4 == 0:
+            lens[0] = 0
+        w = [-1, 0, 1, 6][trial % 4]
+        sink = None if trial % 2 else torch.from_numpy(rng.normal(size=Hq).astype(np.float32))
+        q = torch.from_numpy(rng.normal(size=(B, Hq, D)).astype(np.float32))
+        kn = torch.from_numpy(rng.normal(size=(B, Hkv, D)).astype(np.float32))
+        vn = torch.from_numpy(rng.normal(size=(B, Hkv, D)).astype(np.float32))
+        kc0 = torch.from_numpy(rng.normal(size=(NB, bs, Hkv, D)).astype(np.float32))
+        vc0 = torch.from_numpy(rng.normal(size=(NB, bs, Hkv, D)).astype(np.float32))
+        bt = torch.from_numpy(rng.permutation(NB).reshape(B, MB).astype(np.int32))
+        sl = torch.from_numpy(lens.astype(np.int32))
+        out, lse, kc, vc = oracle.decode_append(q, kn, vn, kc0, vc0, bt, sl, sink, 0.7, w)
+        for b in range(B):
+            L = int(lens[b])
+            rows = [int(bt[b, j // bs]) * bs + j % bs for j in range(L)]
+            K = np.concatenate([kc0.view(-1, Hkv, D)[rows].numpy(), kn[b:b + 1].numpy()], 0)
+            V = np.concatenate([vc0.view(-1, Hkv, D)[rows].numpy(), vn[b:b + 1].numpy()], 0)
+            j = np.arange(L + 1)
+            vis = (j >= L - w) if w >= 0 else np.ones(L + 1, bool)
+            for h in range(Hq):
+                lg = np.where(vis, 0.7 * (K[:, h // G].astype(np.float64) @ q[b, h].double().numpy()),
+                              -np.inf)
+                full = np.append(lg, -np.inf if sink is None else float(sink[h]))
+                mx = full.max()
+                e = np.exp(full - mx)
+                ref = (e[:-1] / e.sum()) @ V[:, h // G].astype(np.float64)
+                _close(out[b, h], ref, 1e-12, 1e-10, f"append trial {trial} b {b} h {h}")
+                _close(lse[b, h], mx + np.log(e.sum()), 1e-12, 1e-10, "append lse")
+        slots = [int(bt[b, int(lens[b]) // bs]) * bs + int(lens[b]) % bs for b in range(B)]
+        fk, fv = kc.view(-1, Hkv, D), vc.view(-1, Hkv, D)
+        for b, s_ in enumerate(slots):
+            assert torch.equal(fk[s_], kn[b]) and torch.equal(fv[s_], vn[b])
+        other = np.setdiff1d(np.arange(NB * bs), slots)
+        assert torch.equal(fk[other], kc0.view(-1, Hkv, D)[other])
+        assert torch.equal(fv[other], vc0.view(-1, Hkv, D)[other])
+    g = _golden("decode_blocks.json")
+    c = synth.config1_decode()
+    kn = synth.to_dtype(synth.normal(6, (3, c.Hkv, c.D), 1), torch.float32)
+    _, _, kc, _ = oracle.decode_append(c.q, kn, kn, c.k_cache, c.v_cache, c.block_table,
+                                       c.cache_seqlens, c.sink, c.sm_scale)
+    fk = kc.view(-1, c.Hkv, c.D)
+    for b, s_ in enumerate(g["derived_append_slots"]):
+        assert torch.equal(fk[s_], kn[b])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -91,6 +91,37 @@ def test_decode_validation(over, status):
     assert decode_call(**over) == status
 
 
+def append_call(**over):
+    a = dict(out=FAKE, lse=None, q=FAKE, k_new=FAKE, v_new=FAKE, k_cache=FAKE, v_cache=FAKE,
+             block_table=FAKE, cache_seqlens=FAKE, sink=None, B=2, Hq=8, Hkv=2, D=128, bs=16,
+             NB=4, MB=4, max_seqlen_k=63, scale=0.1, window=-1, ws=None, ws_bytes=0, dt=1,
+             stream=None)
+    a.update(over)
+    return lib.pkv_paged_decode_append(*a.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(out=None), pkv.PKV_ERR_NULL),
+    (dict(k_new=None), pkv.PKV_ERR_NULL),
+    (dict(v_new=None), pkv.PKV_ERR_NULL),
+    (dict(k_cache=None), pkv.PKV_ERR_NULL),
+    (dict(cache_seqlens=None), pkv.PKV_ERR_NULL),
+    (dict(max_seqlen_k=64), pkv.PKV_ERR_SHAPE),      # the new token at 64 needs a 5th block
+    (dict(NB=0), pkv.PKV_ERR_SHAPE),                 # nowhere to store the new tokens
+    (dict(B=4097), pkv.PKV_ERR_SHAPE),               # bf16 schedule limit
+    (dict(Hq=6, Hkv=4), pkv.PKV_ERR_SHAPE),
+    (dict(D=96), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(bs=24), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(window=-2), pkv.PKV_ERR_SHAPE),
+    (dict(k_new=FAKE + 8), pkv.PKV_ERR_UNSUPPORTED),   # misaligned
+    (dict(ws=None), pkv.PKV_ERR_WORKSPACE),          # bf16 needs the balanced workspace
+    (dict(ws=FAKE, ws_bytes=10), pkv.PKV_ERR_WORKSPACE),
+    (dict(B=0), pkv.PKV_OK),                         # no-op, nothing launched
+])
+def test_decode_append_validation(over, status):
+    assert append_call(**over) == status
+
+
 def prefill_call(**over):
     a = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, k_cache=None, v_cache=None, bt=None,
              bs=0, NB=0, MB=0, cu_q=FAKE, cu_k=FAKE, B=2, maxq=16, maxk=16, Hq=8, Hkv=2, D=64,
