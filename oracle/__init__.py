@@ -69,10 +69,10 @@ def _load():
             path = build()
         lib = ctypes.CDLL(path)
         P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
-        lib.oracle_paged_decode.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, D, I, I, I,
-                                            I, P, I, I]
+        lib.oracle_paged_decode.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, D, I, I,
+                                            I, I, P, I, I]
         lib.oracle_varlen_prefill.argtypes = [P, P, P, P, P, P, P, P, I, I, P, P, I, I, I, I, D,
-                                              I, P, I, P, I, I]
+                                              I, P, P, I, P, I, I]
         lib.oracle_merge.argtypes = [P, P, P, P, P, P, I, I, I, I]
         lib.oracle_reshape_and_cache.argtypes = [P, P, P, P, P, I, I, I, I, I, I]
         lib.oracle_token_request.argtypes = [P, I, I, P]
@@ -130,8 +130,9 @@ def slot_of(block_table_row: Sequence[int], pos: int, block_size: int) -> int:
 
 def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sink, sm_scale: float,
                  window_left: int = -1, partition_size: int = 0,
-                 units: Optional[Sequence[int]] = None, nthreads: Optional[int] = None):
-    """Decode over a paged cache.
+                 units: Optional[Sequence[int]] = None, nthreads: Optional[int] = None,
+                 alibi=None):
+    """Decode over a paged cache (``alibi``: per-query-head slopes, or None).
 
     Returns ``(out [B,Hq,D], lse [B,Hq])`` for ``partition_size == 0``, else
     the per-partition results ``(out [B,Hq,P,D], lse [B,Hq,P])`` with the
@@ -142,6 +143,7 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sink, sm_scale
     bt = _np(block_table).astype(np.int32, copy=False)
     sl = _np(cache_seqlens).astype(np.int32, copy=False)
     sk = None if sink is None else _np(sink).astype(np.float32, copy=False)
+    al = None if alibi is None else _np(alibi).astype(np.float32, copy=False)
     B, Hq, D = qn.shape
     NB, bs, Hkv, D2 = kn.shape
     assert D2 == D and tuple(vn.shape) == tuple(kn.shape)
@@ -155,7 +157,7 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sink, sm_scale
         lse = np.full((B, Hq), np.nan)
     un = None if units is None else np.ascontiguousarray(units, dtype=np.int32)
     rc = _load().oracle_paged_decode(
-        _ptr(out), _ptr(lse), _ptr(qn), _ptr(kn), _ptr(vn), _ptr(bt), _ptr(sl), _ptr(sk),
+        _ptr(out), _ptr(lse), _ptr(qn), _ptr(kn), _ptr(vn), _ptr(bt), _ptr(sl), _ptr(sk), _ptr(al),
         B, Hq, Hkv, D, bs, bt.shape[1], float(sm_scale), int(window_left), int(partition_size),
         P, dt, _ptr(un), 0 if un is None else len(un), _threads(nthreads))
     assert rc == 0
@@ -165,9 +167,11 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sink, sm_scale
 def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, sink, sm_scale: float, num_kv_heads: int,
                    k=None, v=None, k_cache=None, v_cache=None, block_table=None,
                    block_size: int = 0, window_left: int = -1,
-                   units: Optional[Sequence[int]] = None, nthreads: Optional[int] = None):
+                   units: Optional[Sequence[int]] = None, nthreads: Optional[int] = None,
+                   alibi=None):
     """Causal varlen prefill; returns ``(out [sum Lq,Hq,D], lse [sum Lq,Hq])``.
-    ``units`` restricts the work to flat ids ``t*Hq + h``."""
+    ``units`` restricts the work to flat ids ``t*Hq + h``; ``alibi``: per-query-head
+    slopes, or None."""
     dt = _dtype_code(q)
     qn = _np(q)
     T, Hq, D = qn.shape
@@ -179,13 +183,14 @@ def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, sink, sm_scale: float, num_kv_
     bt = None if block_table is None else _np(block_table).astype(np.int32, copy=False)
     assert (kn is None) != (kc is None), "exactly one of contiguous or paged K/V"
     sk = None if sink is None else _np(sink).astype(np.float32, copy=False)
+    al = None if alibi is None else _np(alibi).astype(np.float32, copy=False)
     out = np.full((T, Hq, D), np.nan)
     lse = np.full((T, Hq), np.nan)
     un = None if units is None else np.ascontiguousarray(units, dtype=np.int32)
     rc = _load().oracle_varlen_prefill(
         _ptr(out), _ptr(lse), _ptr(qn), _ptr(kn), _ptr(vn), _ptr(kc), _ptr(vc), _ptr(bt),
         int(block_size), 0 if bt is None else bt.shape[1], _ptr(cq), _ptr(ck), B, Hq,
-        int(num_kv_heads), D, float(sm_scale), int(window_left), _ptr(sk), dt, _ptr(un),
+        int(num_kv_heads), D, float(sm_scale), int(window_left), _ptr(sk), _ptr(al), dt, _ptr(un),
         0 if un is None else len(un), _threads(nthreads))
     assert rc == 0
     return out, lse
@@ -223,7 +228,8 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping):
 
 def decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, sink,
                   sm_scale: float, window_left: int = -1,
-                  units: Optional[Sequence[int]] = None, nthreads: Optional[int] = None):
+                  units: Optional[Sequence[int]] = None, nthreads: Optional[int] = None,
+                  alibi=None):
     """Decode with the new token appended in the same call (Transformers
     "Paged attention" doc, decode path: the kvcache kernel writes k and v
     into the cache at index cache_seqlens[b], updating it in place, and the
@@ -238,6 +244,6 @@ def decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens,
     slots = np.array([slot_of(bt[b], int(sl[b]), bs) for b in range(len(sl))], dtype=np.int32)
     kc, vc = reshape_and_cache(k_new, v_new, k_cache, v_cache, torch.from_numpy(slots))
     out, lse = paged_decode(q, kc, vc, block_table, torch.from_numpy(sl + 1), sink, sm_scale,
-                            window_left=window_left, units=units, nthreads=nthreads)
+                            window_left=window_left, units=units, nthreads=nthreads, alibi=alibi)
     return out, lse, kc, vc
 

@@ -17,6 +17,11 @@
  *   p = Lk - Lq + i                               (queries are the last Lq positions)
  *   visible j: 0 <= j < Lk, j <= p, and (w < 0 or j >= p - w)
  *   s_j   = sm_scale * sum_d q[d] * K(j)[d]       (fp64)
+ *           + slope[h] * (j - p)                   (ALiBi, when slopes are given:
+ *             vLLM page "attention.py", PagedAttentionWithALiBi.set_attn_bias --
+ *             the per-head slope times key position minus query position,
+ *             added to the scaled logits under the causal mask; computed from
+ *             the exact integer distance)
  *   sigma = sink[h], a logit in scaled units, never multiplied by sm_scale;
  *           -inf when no sink is given
  *   M = max({s_j} U {sigma}),  Z = sum_j exp(s_j - M) + exp(sigma - M)
@@ -70,8 +75,9 @@ void oracle_token_request(const int32_t *cu, int B, int T, int32_t *out)
  * krow[n] is the element offset of key row n (the same offset addresses V).
  * Writes o[0..D) and *lse. */
 static void attend_row(double *o, double *lse, const void *qbase, size_t qoff,
-                       const void *kbase, const void *vbase, const size_t *krow, int nvis,
-                       int D, int dtype, double sm_scale, double sigma, double *s)
+                       const void *kbase, const void *vbase, const size_t *krow,
+                       const int *js, int nvis, int p, double slope, int D, int dtype,
+                       double sm_scale, double sigma, double *s)
 {
     /* pass 1: logits and their maximum, sink included */
     double M = sigma;
@@ -79,7 +85,7 @@ static void attend_row(double *o, double *lse, const void *qbase, size_t qoff,
         double acc = 0.0;
         for (int d = 0; d < D; ++d)
             acc += load_elem(qbase, qoff + d, dtype) * load_elem(kbase, krow[n] + d, dtype);
-        s[n] = sm_scale * acc;
+        s[n] = sm_scale * acc + slope * (double)(js[n] - p);
         if (s[n] > M) M = s[n];
     }
     if (M == -INFINITY) {          /* nothing visible and no sink */
@@ -161,7 +167,7 @@ typedef struct {
     double *out, *lse;
     const void *q, *kc, *vc;
     const int32_t *bt, *seqlens;
-    const float *sink;
+    const float *sink, *alibi;
     int B, Hq, Hkv, D, bs, mbps, window, dtype, part, nparts;
     double scale;
     const int32_t *units;
@@ -184,8 +190,9 @@ static void decode_unit(void *vctx, int u, double *s, size_t *krow, int *js)
         krow[t] = ((size_t)row * c->Hkv + g) * c->D;
     }
     double sigma = (c->part > 0 || !c->sink) ? -INFINITY : (double)c->sink[h];
+    double slope = c->alibi ? (double)c->alibi[h] : 0.0;
     attend_row(c->out + (size_t)id * c->D, c->lse + id, c->q, (size_t)bh * c->D,
-               c->kc, c->vc, krow, n, c->D, c->dtype, c->scale, sigma, s);
+               c->kc, c->vc, krow, js, n, Lk - 1, slope, c->D, c->dtype, c->scale, sigma, s);
 }
 
 /* out [B,Hq,D] / lse [B,Hq] (partition_size == 0) or
@@ -193,14 +200,14 @@ static void decode_unit(void *vctx, int u, double *s, size_t *krow, int *js)
  * units: NULL for all, else a list of flat unit ids to compute. */
 int oracle_paged_decode(double *out, double *lse, const void *q, const void *k_cache,
                         const void *v_cache, const int32_t *block_table,
-                        const int32_t *cache_seqlens, const float *sink, int B, int Hq, int Hkv,
-                        int D, int block_size, int max_blocks_per_seq, double sm_scale,
-                        int window_left, int partition_size, int nparts, int dtype,
-                        const int32_t *units, int nunits, int nthreads)
+                        const int32_t *cache_seqlens, const float *sink, const float *alibi,
+                        int B, int Hq, int Hkv, int D, int block_size, int max_blocks_per_seq,
+                        double sm_scale, int window_left, int partition_size, int nparts,
+                        int dtype, const int32_t *units, int nunits, int nthreads)
 {
     if (Hkv <= 0 || Hq % Hkv || block_size <= 0 || D <= 0) return 1;
     if (partition_size <= 0) nparts = 1;
-    decode_ctx c = {out, lse, q, k_cache, v_cache, block_table, cache_seqlens, sink,
+    decode_ctx c = {out, lse, q, k_cache, v_cache, block_table, cache_seqlens, sink, alibi,
                     B, Hq, Hkv, D, block_size, max_blocks_per_seq, window_left, dtype,
                     partition_size > 0 ? partition_size : 0, nparts, sm_scale, units};
     int maxk = 1;
@@ -219,7 +226,7 @@ typedef struct {
     double *out, *lse;
     const void *q, *k, *v, *kc, *vc;
     const int32_t *bt, *cu_q, *cu_k, *tok_req;
-    const float *sink;
+    const float *sink, *alibi;
     int B, Hq, Hkv, D, bs, mbps, window, dtype;
     double scale;
     const int32_t *units;
@@ -243,8 +250,9 @@ static void prefill_unit(void *vctx, int u, double *s, size_t *krow, int *js)
         krow[m] = ((size_t)row * c->Hkv + g) * c->D;
     }
     double sigma = c->sink ? (double)c->sink[h] : -INFINITY;
+    double slope = c->alibi ? (double)c->alibi[h] : 0.0;
     attend_row(c->out + (size_t)id * c->D, c->lse + id, c->q, (size_t)id * c->D, kb, vb,
-               krow, n, c->D, c->dtype, c->scale, sigma, s);
+               krow, js, n, p, slope, c->D, c->dtype, c->scale, sigma, s);
 }
 
 /* out [sumLq,Hq,D], lse [sumLq,Hq]; causal only (the kernels' contract). */
@@ -252,8 +260,8 @@ int oracle_varlen_prefill(double *out, double *lse, const void *q, const void *k
                           const void *k_cache, const void *v_cache, const int32_t *block_table,
                           int block_size, int max_blocks_per_seq, const int32_t *cu_q,
                           const int32_t *cu_k, int B, int Hq, int Hkv, int D, double sm_scale,
-                          int window_left, const float *sink, int dtype, const int32_t *units,
-                          int nunits, int nthreads)
+                          int window_left, const float *sink, const float *alibi, int dtype,
+                          const int32_t *units, int nunits, int nthreads)
 {
     if (Hkv <= 0 || Hq % Hkv || D <= 0 || B < 0) return 1;
     int T = cu_q[B] - cu_q[0];
@@ -262,6 +270,7 @@ int oracle_varlen_prefill(double *out, double *lse, const void *q, const void *k
     int maxk = 1;
     for (int r = 0; r < B; ++r) if (cu_k[r + 1] - cu_k[r] > maxk) maxk = cu_k[r + 1] - cu_k[r];
     prefill_ctx c = {out, lse, q, k, v, k_cache, v_cache, block_table, cu_q, cu_k, tok_req, sink,
+                     alibi,
                      B, Hq, Hkv, D, block_size, max_blocks_per_seq, window_left, dtype, sm_scale,
                      units};
     run_units(prefill_unit, &c, units ? nunits : T * Hq, nthreads, maxk);

@@ -379,7 +379,7 @@ def pin_merge_associative():
 # extra column of the logits, softmax, sink column dropped).
 # ---------------------------------------------------------------------------
 
-def _numpy_reference(q, k, v, cu_q, cu_k, sink, sm_scale, Hkv, window):
+def _numpy_reference(q, k, v, cu_q, cu_k, sink, sm_scale, Hkv, window, alibi=None):
     q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
     Hq = q.shape[1]
     G = Hq // Hkv
@@ -394,7 +394,8 @@ def _numpy_reference(q, k, v, cu_q, cu_k, sink, sm_scale, Hkv, window):
             mask &= cols >= rows - window
         for h in range(Hq):
             kk, vv = k[ks, h // G], v[ks, h // G]
-            logits = np.where(mask, sm_scale * q[qs, h] @ kk.T, -np.inf)
+            bias = 0.0 if alibi is None else float(alibi[h]) * (cols - rows)
+            logits = np.where(mask, sm_scale * q[qs, h] @ kk.T + bias, -np.inf)
             col = np.full((Lq, 1), -np.inf if sink is None else float(sink[h]))
             full = np.concatenate([logits, col], axis=1)
             mx = full.max(axis=1, keepdims=True)
@@ -418,13 +419,52 @@ def pin_brute_force():
             k_lens[0] = 0
         w = [-1, 0, 1, 5, 100][trial % 5]
         with_sink = trial % 2 == 0
+        # every third trial adds ALiBi slopes (vLLM page, PagedAttentionWithALiBi)
+        al = (torch.from_numpy(rng.uniform(0.01, 1.0, size=G * Hkv).astype(np.float32))
+              if trial % 3 == 1 else None)
         c = synth.prefill_case(500 + trial, q_lens, k_lens, G * Hkv, Hkv, 8, torch.float32,
                                with_sink, window_left=w, sm_scale=0.6)
         o, _ = oracle.varlen_prefill(c.q, c.cu_seqlens_q, c.cu_seqlens_k, c.sink, 0.6, Hkv,
-                                     k=c.k, v=c.v, window_left=w)
+                                     k=c.k, v=c.v, window_left=w, alibi=al)
         ref = _numpy_reference(c.q, c.k, c.v, c.cu_seqlens_q.tolist(), c.cu_seqlens_k.tolist(),
-                               None if c.sink is None else c.sink.numpy(), 0.6, Hkv, w)
+                               None if c.sink is None else c.sink.numpy(), 0.6, Hkv, w,
+                               None if al is None else al.numpy())
         _close(o, ref, 1e-12, 1e-10, f"brute force trial {trial}")
+
+
+def pin_alibi_closed_form():
+    """ALiBi (vLLM page "attention.py", PagedAttentionWithALiBi.set_attn_bias:
+    bias[i][j] = slope_h * (j - i), key position minus query position, added
+    to the scaled logits).  With every key equal, the logits differ only by
+    the bias, so the weights of the query at position p are the geometric
+    sequence r^(j - p), r = e^slope, normalised (with the sink e^sigma in the
+    denominator); one-hot value rows read each weight out.  The decode of the
+    same rows (query at the last position) gives the last row of the prefill."""
+    Lk, D, slopes = 6, 8, [0.5, 0.125]
+    q = torch.zeros((Lk, 2, D))
+    k = torch.ones((Lk, 1, D))
+    v = torch.zeros((Lk, 1, D))
+    for j in range(Lk):
+        v[j, 0, j] = 1.0
+    al = torch.tensor(slopes)
+    sink = torch.tensor([0.25, -1.0])
+    cu = torch.tensor([0, Lk], dtype=torch.int32)
+    o, lse = oracle.varlen_prefill(q, cu, cu, sink, 1.0, 1, k=k, v=v, alibi=al)
+    for h, m in enumerate(slopes):
+        for p in range(Lk):
+            w = np.array([np.exp(m * (j - p)) for j in range(p + 1)])
+            z = w.sum() + np.exp(float(sink[h]))
+            want = np.zeros(D)
+            want[:p + 1] = w / z
+            _close(o[p, h], want, 1e-14, 1e-12, f"alibi closed form h {h} p {p}")
+            _close(lse[p, h], np.log(z), 1e-14, 1e-12, "alibi lse")
+    bt = torch.tensor([[0, 1]], dtype=torch.int32)
+    kc, vc = torch.zeros((2, 4, 1, D)), torch.zeros((2, 4, 1, D))
+    kc.view(-1, 1, D)[:Lk] = k
+    vc.view(-1, 1, D)[:Lk] = v
+    od, _ = oracle.paged_decode(q[:1], kc, vc, bt, torch.tensor([Lk], dtype=torch.int32), sink,
+                                1.0, alibi=al)
+    _close(od[0], o[Lk - 1], 1e-14, 1e-12, "alibi decode == last prefill row")
 
 
 def pin_bf16_inputs_read_exactly():
