@@ -211,8 +211,13 @@ def replicate_pool(c, reps):
     return kc, vc, tables
 
 
+def alibi_slopes(Hq):
+    """The usual geometric ALiBi slopes 2^(-8 (h + 1) / Hq)."""
+    return torch.tensor([2.0 ** (-8.0 * (h + 1) / Hq) for h in range(Hq)], dtype=torch.float32)
+
+
 def bench_decode(c, name, steps, warmup, partition_size, reps, traffic_key=None,
-                 two_stage=False):
+                 two_stage=False, alibi=None):
     """partition_size 0: the automatic (balanced) schedule, one launch with the
     merge fused in (two_stage: its stage and merge launches, timed apart);
     > 0: fixed partitions + merge."""
@@ -220,6 +225,7 @@ def bench_decode(c, name, steps, warmup, partition_size, reps, traffic_key=None,
     kc, vc, tables = replicate_pool(c, reps)
     q = c.q.cuda()
     sl = c.cache_seqlens.cuda()
+    al = None if alibi is None else alibi.cuda()
     sink = None if c.sink is None else c.sink.cuda()
     out = torch.empty_like(q)
     msk = c.max_seqlen_k
@@ -247,7 +253,7 @@ def bench_decode(c, name, steps, warmup, partition_size, reps, traffic_key=None,
             kt.time("decode", lambda: pkv.paged_decode(q, kc, vc, bt, sl, c.sm_scale, sink=sink,
                                                        window_left=c.window_left,
                                                        partition_size=P, max_seqlen_k=msk,
-                                                       out=out, workspace=ws))
+                                                       out=out, workspace=ws, alibi_slopes=al))
 
     ms, kt = timed_steps(step, steps, warmup)
     kv, qb, table = decode_bytes(c)
@@ -342,10 +348,12 @@ def visible_pairs(q_lens, k_lens, window):
     return n
 
 
-def bench_prefill(c, name, steps, warmup, reps, with_cache_write=False, traffic_key=None):
+def bench_prefill(c, name, steps, warmup, reps, with_cache_write=False, traffic_key=None,
+                  alibi=None):
     T = c.q.shape[0]
     qs = [c.q.cuda() for _ in range(reps)]
     cq, ck = c.cu_seqlens_q.cuda(), c.cu_seqlens_k.cuda()
+    al = None if alibi is None else alibi.cuda()
     sink = None if c.sink is None else c.sink.cuda()
     out = torch.empty_like(qs[0])
     if c.paged:
@@ -376,11 +384,11 @@ def bench_prefill(c, name, steps, warmup, reps, with_cache_write=False, traffic_
             kt.time("prefill", lambda: pkv.varlen_prefill(
                 qs[r], cq, ck, c.max_seqlen_q, c.max_seqlen_k, c.sm_scale, c.Hkv,
                 k_cache=kc, v_cache=vc, block_table=tables[r], sink=sink,
-                window_left=c.window_left, out=out))
+                window_left=c.window_left, out=out, alibi_slopes=al))
         else:
             kt.time("prefill", lambda: pkv.varlen_prefill(
                 qs[r], cq, ck, c.max_seqlen_q, c.max_seqlen_k, c.sm_scale, c.Hkv, k=ks[r],
-                v=vs[r], sink=sink, window_left=c.window_left, out=out))
+                v=vs[r], sink=sink, window_left=c.window_left, out=out, alibi_slopes=al))
 
     ms, kt = timed_steps(step, steps, warmup)
     pairs = visible_pairs(c.q_lens, c.k_lens, c.window_left)
@@ -469,6 +477,10 @@ def main():
                                   reps=2, two_stage=True)
             workloads["decode_two_launches"] = r2s
             log(f"decode as stage + merge launches: {r2s['value']} GB/s step")
+            rl, _ = bench_decode(c2, "decode_64x_U512-4096_alibi", steps, warmup, 0, reps=2,
+                                 alibi=alibi_slopes(c2.Hq))
+            workloads["decode_alibi"] = rl
+            log(f"decode with ALiBi slopes: {rl['value']} GB/s step")
             ra = bench_decode_append(c2, "decode_append_64x_U512-4096", steps, warmup, reps=2)
             workloads["decode_append"] = ra
             log(f"decode with the new token appended: {ra['value']} GB/s step, "
@@ -481,6 +493,10 @@ def main():
                               with_cache_write=True, traffic_key="prefill_c3")
         workloads["varlen_prefill"] = r3
         log(f"prefill: {r3['value']} TFLOP/s")
+        r3a, _ = bench_prefill(c3, "varlen_prefill_8x_U256-4096_alibi", steps, warmup, reps=2,
+                               alibi=alibi_slopes(c3.Hq))
+        workloads["varlen_prefill_alibi"] = r3a
+        log(f"prefill with ALiBi slopes: {r3a['value']} TFLOP/s")
     if ARGS.only in ("all", "chunked"):
         log("chunked prefill workload (4 x 512 q on 8704 paged keys, window 128, 64/8, D 64)")
         c4 = synth.config4_chunked(poison=False, spare_blocks=0)

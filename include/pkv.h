@@ -36,6 +36,12 @@
  * lse, when requested, is the natural-log log-sum-exp of the row's logits
  * including the sink.
  *
+ * ALiBi (vLLM page "attention.py", PagedAttentionWithALiBi: a per-head slope
+ * times key position minus query position, added to the scaled logits):
+ * every call that computes logits takes alibi_slopes, float32 [num_q_heads]
+ * or NULL for none; with slopes, the logit of key j for a query at position
+ * p is sm_scale * q.k_j + alibi_slopes[h] * (j - p).  The sink is not biased.
+ *
  * Conventions for every entry point:
  *   - Array arguments are DEVICE pointers owned by the caller; the library
  *     allocates nothing, keeps no state between calls and never prints.
@@ -178,8 +184,8 @@ pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_
                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                             int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                             int32_t max_seqlen_k, float sm_scale, int32_t window_left,
-                            int32_t partition_size, void *workspace, size_t workspace_bytes,
-                            pkv_dtype dtype, void *stream);
+                            const float *alibi_slopes, int32_t partition_size, void *workspace,
+                            size_t workspace_bytes, pkv_dtype dtype, void *stream);
 
 /*
  * pkv_paged_decode_append -- decode with the new token appended in the same
@@ -221,8 +227,8 @@ pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const v
                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                    int32_t num_blocks, int32_t max_blocks_per_seq,
                                    int32_t max_seqlen_k, float sm_scale, int32_t window_left,
-                                   void *workspace, size_t workspace_bytes, pkv_dtype dtype,
-                                   void *stream);
+                                   const float *alibi_slopes, void *workspace,
+                                   size_t workspace_bytes, pkv_dtype dtype, void *stream);
 
 /*
  * The two stages of pkv_paged_decode with partition_size == 0 in bf16 (the
@@ -244,8 +250,8 @@ pkv_status pkv_paged_decode_stage(const void *q, const void *k_cache, const void
                                   const int32_t *block_table, const int32_t *cache_seqlens,
                                   int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                                  int32_t max_blocks_per_seq, int32_t max_seqlen_k,
-                                  float sm_scale, int32_t window_left, void *workspace,
+                                  int32_t max_blocks_per_seq, int32_t max_seqlen_k, float sm_scale,
+                                  int32_t window_left, const float *alibi_slopes, void *workspace,
                                   size_t workspace_bytes, pkv_dtype dtype, void *stream);
 pkv_status pkv_paged_decode_finish(void *out, float *lse, const float *sink, int32_t B,
                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -276,8 +282,8 @@ pkv_status pkv_paged_decode_partitions(float *part_out, float *part_lse, const v
                                        int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                        int32_t max_blocks_per_seq, int32_t max_seqlen_k,
                                        float sm_scale, int32_t window_left,
-                                       int32_t partition_size, int32_t max_partitions,
-                                       pkv_dtype dtype, void *stream);
+                                       const float *alibi_slopes, int32_t partition_size,
+                                       int32_t max_partitions, pkv_dtype dtype, void *stream);
 
 /*
  * pkv_merge_partitions -- combine split-KV partition results (vLLM page, the
@@ -330,14 +336,13 @@ pkv_status pkv_merge_partitions(void *out, float *lse, const float *part_out,
  * request's K rows) reaches 4 GiB; use the paged form for such requests.
  */
 pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *k, const void *v,
-                              const void *k_cache, const void *v_cache,
-                              const int32_t *block_table, int32_t block_size, int32_t num_blocks,
-                              int32_t max_blocks_per_seq, const int32_t *cu_seqlens_q,
-                              const int32_t *cu_seqlens_k, int32_t B, int32_t max_seqlen_q,
-                              int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads,
-                              int32_t head_dim, float sm_scale, int32_t causal,
-                              int32_t window_left, const float *sink, pkv_dtype dtype,
-                              void *stream);
+                              const void *k_cache, const void *v_cache, const int32_t *block_table,
+                              int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                              const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t B,
+                              int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                              int32_t causal, int32_t window_left, const float *alibi_slopes,
+                              const float *sink, pkv_dtype dtype, void *stream);
 
 #ifdef __cplusplus
 }

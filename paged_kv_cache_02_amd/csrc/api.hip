@@ -81,7 +81,8 @@ StreamLayout stream_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t D) {
 StreamArgs stream_args(const void *q, const void *k_cache, const void *v_cache,
                        const int32_t *block_table, const int32_t *cache_seqlens, int32_t B,
                        int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size, int32_t mbps,
-                       float sm_scale, int32_t window_left, void *workspace) {
+                       float sm_scale, int32_t window_left, const float *alibi,
+                       void *workspace) {
     const StreamLayout lay = stream_layout(B, Hq, Hkv, D);
     StreamArgs a{};
     a.part_out = (float *)((char *)workspace + lay.part_out);
@@ -90,7 +91,7 @@ StreamArgs stream_args(const void *q, const void *k_cache, const void *v_cache,
     a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.block_table = block_table;
     a.seqlens = cache_seqlens; a.B = B; a.Hq = Hq; a.Hkv = Hkv;
     a.G = Hq / Hkv; a.D = D; a.bs_log2 = ilog2(block_size);
-    a.mbps = mbps; a.window_left = window_left;
+    a.mbps = mbps; a.window_left = window_left; a.alibi = alibi;
     a.W = stream_wgs_per_head_group(Hq, Hkv);
     a.scale_log2 = sm_scale * kLog2e;
     return a;
@@ -127,7 +128,8 @@ pkv_status launch_decode_stage(void *out, float *lse, float *part_out, float *pa
                                const int32_t *block_table, const int32_t *cache_seqlens,
                                const float *sink, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                int32_t block_size, int32_t mbps, float sm_scale,
-                               int32_t window_left, const SplitPlan &plan, pkv_dtype dtype,
+                               int32_t window_left, const float *alibi, const SplitPlan &plan,
+                               pkv_dtype dtype,
                                hipStream_t s)
 {
     if (dtype == PKV_BF16) {
@@ -137,6 +139,7 @@ pkv_status launch_decode_stage(void *out, float *lse, float *part_out, float *pa
         a.block_table = block_table; a.seqlens = cache_seqlens; a.sink = sink;
         a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D;
         a.bs_log2 = ilog2(block_size); a.mbps = mbps; a.window_left = window_left;
+        a.alibi = alibi;
         a.part_size = plan.part_size; a.nparts = plan.nparts; a.split = plan.split ? 1 : 0;
         a.scale_log2 = sm_scale * kLog2e;
         return launch_decode_bf16(a, s);
@@ -146,7 +149,7 @@ pkv_status launch_decode_stage(void *out, float *lse, float *part_out, float *pa
     a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.block_table = block_table;
     a.seqlens = cache_seqlens; a.sink = sink; a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
     a.D = D; a.bs_log2 = ilog2(block_size); a.mbps = mbps; a.window_left = window_left;
-    a.part_size = plan.part_size; a.nparts = plan.nparts; a.split = plan.split ? 1 : 0;
+    a.alibi = alibi; a.part_size = plan.part_size; a.nparts = plan.nparts; a.split = plan.split ? 1 : 0;
     a.scale_log2 = sm_scale * kLog2e;
     return launch_rows(a, false, s);
 }
@@ -219,7 +222,7 @@ pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_
                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                             int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                             int32_t max_seqlen_k, float sm_scale, int32_t window_left,
-                            int32_t partition_size, void *workspace, size_t workspace_bytes,
+                            const float *alibi_slopes, int32_t partition_size, void *workspace, size_t workspace_bytes,
                             pkv_dtype dtype, void *stream)
 {
     if (B < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_seqlen_k < 0)
@@ -248,7 +251,8 @@ pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_
         // one launch: the balanced stream with the merge fused into it
         StreamArgs a = stream_args(q, k_cache, v_cache, block_table, cache_seqlens, B,
                                    num_q_heads, num_kv_heads, head_dim, block_size,
-                                   max_blocks_per_seq, sm_scale, window_left, workspace);
+                                   max_blocks_per_seq, sm_scale, window_left, alibi_slopes,
+                                   workspace);
         const StreamLayout lay = stream_layout(B, num_q_heads, num_kv_heads, head_dim);
         a.counters = (int32_t *)((char *)workspace + lay.counters);
         a.out = out; a.lse = lse; a.sink = sink;
@@ -263,8 +267,8 @@ pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_
                    : nullptr;
     st = launch_decode_stage(out, lse, part_out, part_lse, q, k_cache, v_cache, block_table,
                              cache_seqlens, sink, B, num_q_heads, num_kv_heads, head_dim,
-                             block_size, max_blocks_per_seq, sm_scale, window_left, plan, dtype,
-                             s);
+                             block_size, max_blocks_per_seq, sm_scale, window_left,
+                             alibi_slopes, plan, dtype, s);
     if (st != PKV_OK || !plan.split) return st;
     MergeArgs m{};
     m.out = out; m.lse = lse; m.part_out = part_out; m.part_lse = part_lse;
@@ -280,7 +284,7 @@ pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const v
                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                    int32_t num_blocks, int32_t max_blocks_per_seq,
                                    int32_t max_seqlen_k, float sm_scale, int32_t window_left,
-                                   void *workspace, size_t workspace_bytes, pkv_dtype dtype,
+                                   const float *alibi_slopes, void *workspace, size_t workspace_bytes, pkv_dtype dtype,
                                    void *stream)
 {
     if (B < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_seqlen_k < 0)
@@ -308,7 +312,8 @@ pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const v
             return PKV_ERR_WORKSPACE;
         StreamArgs a = stream_args(q, k_cache, v_cache, block_table, cache_seqlens, B,
                                    num_q_heads, num_kv_heads, head_dim, block_size,
-                                   max_blocks_per_seq, sm_scale, window_left, workspace);
+                                   max_blocks_per_seq, sm_scale, window_left, alibi_slopes,
+                                   workspace);
         a.counters = (int32_t *)((char *)workspace + lay.counters);
         a.out = out; a.lse = lse; a.sink = sink;
         a.k_new = k_new; a.v_new = v_new; a.append = 1;
@@ -317,7 +322,8 @@ pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const v
     RowArgs a{};
     a.mode = 0; a.out = out; a.lse = lse; a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
     a.block_table = block_table; a.seqlens = cache_seqlens; a.k_new = k_new; a.v_new = v_new;
-    a.append = 1; a.sink = sink; a.B = B; a.Hq = num_q_heads; a.Hkv = num_kv_heads;
+    a.append = 1; a.sink = sink; a.alibi = alibi_slopes; a.B = B; a.Hq = num_q_heads;
+    a.Hkv = num_kv_heads;
     a.G = num_q_heads / num_kv_heads; a.D = head_dim; a.bs_log2 = ilog2(block_size);
     a.mbps = max_blocks_per_seq; a.window_left = window_left;
     a.part_size = max_seqlen_k + 1; a.nparts = 1; a.split = 0;
@@ -330,7 +336,8 @@ pkv_status pkv_paged_decode_stage(const void *q, const void *k_cache, const void
                                   int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                   int32_t max_blocks_per_seq, int32_t max_seqlen_k,
-                                  float sm_scale, int32_t window_left, void *workspace,
+                                  float sm_scale, int32_t window_left,
+                                  const float *alibi_slopes, void *workspace,
                                   size_t workspace_bytes, pkv_dtype dtype, void *stream)
 {
     if (B < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_seqlen_k < 0)
@@ -349,7 +356,8 @@ pkv_status pkv_paged_decode_stage(const void *q, const void *k_cache, const void
         return PKV_ERR_WORKSPACE;
     const StreamArgs a = stream_args(q, k_cache, v_cache, block_table, cache_seqlens, B,
                                      num_q_heads, num_kv_heads, head_dim, block_size,
-                                     max_blocks_per_seq, sm_scale, window_left, workspace);
+                                     max_blocks_per_seq, sm_scale, window_left, alibi_slopes,
+                                   workspace);
     return launch_decode_stream_bf16(a, (hipStream_t)stream);
 }
 
@@ -384,7 +392,7 @@ pkv_status pkv_paged_decode_partitions(float *part_out, float *part_lse, const v
                                        int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                        int32_t max_blocks_per_seq, int32_t max_seqlen_k,
                                        float sm_scale, int32_t window_left,
-                                       int32_t partition_size, int32_t max_partitions,
+                                       const float *alibi_slopes, int32_t partition_size, int32_t max_partitions,
                                        pkv_dtype dtype, void *stream)
 {
     if (B < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_seqlen_k < 0)
@@ -406,7 +414,7 @@ pkv_status pkv_paged_decode_partitions(float *part_out, float *part_lse, const v
     return launch_decode_stage(nullptr, nullptr, part_out, part_lse, q, k_cache, v_cache,
                                block_table, cache_seqlens, nullptr, B, num_q_heads, num_kv_heads,
                                head_dim, block_size, max_blocks_per_seq, sm_scale, window_left,
-                               plan, dtype, (hipStream_t)stream);
+                               alibi_slopes, plan, dtype, (hipStream_t)stream);
 }
 
 pkv_status pkv_merge_partitions(void *out, float *lse, const float *part_out,
@@ -435,7 +443,8 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
                               const int32_t *cu_seqlens_k, int32_t B, int32_t max_seqlen_q,
                               int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, float sm_scale, int32_t causal,
-                              int32_t window_left, const float *sink, pkv_dtype dtype,
+                              int32_t window_left, const float *alibi_slopes,
+                              const float *sink, pkv_dtype dtype,
                               void *stream)
 {
     if (B < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return PKV_ERR_SHAPE;
@@ -470,7 +479,8 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
         PrefillArgs a{};
         a.out = out; a.lse = lse; a.q = q; a.k = k; a.v = v; a.k_cache = k_cache;
         a.v_cache = v_cache; a.block_table = block_table; a.cu_q = cu_seqlens_q;
-        a.cu_k = cu_seqlens_k; a.sink = sink; a.B = B; a.Hq = num_q_heads; a.Hkv = num_kv_heads;
+        a.cu_k = cu_seqlens_k; a.sink = sink; a.alibi = alibi_slopes; a.B = B;
+        a.Hq = num_q_heads; a.Hkv = num_kv_heads;
         a.G = num_q_heads / num_kv_heads; a.D = head_dim; a.bs_log2 = bs_log2;
         a.mbps = max_blocks_per_seq; a.window_left = window_left;
         a.hpw = prefill_heads_per_wg(a.G);
@@ -482,7 +492,7 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
     RowArgs a{};
     a.mode = 1; a.out = out; a.lse = lse; a.q = q; a.k = k; a.v = v; a.k_cache = k_cache;
     a.v_cache = v_cache; a.block_table = block_table; a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
-    a.sink = sink; a.B = B; a.Hq = num_q_heads; a.Hkv = num_kv_heads;
+    a.sink = sink; a.alibi = alibi_slopes; a.B = B; a.Hq = num_q_heads; a.Hkv = num_kv_heads;
     a.G = num_q_heads / num_kv_heads; a.D = head_dim; a.bs_log2 = bs_log2;
     a.mbps = max_blocks_per_seq; a.window_left = window_left; a.scale_log2 = sm_scale * kLog2e;
     a.T = max_seqlen_q;

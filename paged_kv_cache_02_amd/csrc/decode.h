@@ -16,6 +16,7 @@ struct DecodeArgs {
     const int32_t *block_table;  // [B, mbps]
     const int32_t *seqlens;      // [B]
     const float *sink;           // [Hq] or null
+    const float *alibi;          // [Hq] ALiBi slopes or null
     int32_t B, Hq, Hkv, G, D;
     int32_t bs_log2, mbps, window_left;
     int32_t part_size, nparts, split;
@@ -39,6 +40,7 @@ struct StreamArgs {
     void *out;                   // [B, Hq, D] bf16
     float *lse;                  // [B, Hq] or null
     const float *sink;           // [Hq] or null
+    const float *alibi;          // [Hq] ALiBi slopes or null
     const void *q;
     const void *k_cache;
     const void *v_cache;
@@ -148,6 +150,7 @@ struct RowArgs {
     const int32_t *cu_q;         // prefill: [B+1]
     const int32_t *cu_k;
     const float *sink;
+    const float *alibi;          // [Hq] ALiBi slopes or null
     int32_t B, T, Hq, Hkv, G, D;   // prefill: T = max_seqlen_q
     int32_t bs_log2, mbps, window_left;
     int32_t part_size, nparts, split;
@@ -166,6 +169,7 @@ struct PrefillArgs {
     const int32_t *cu_q;
     const int32_t *cu_k;
     const float *sink;
+    const float *alibi;          // [Hq] ALiBi slopes or null
     int32_t B, Hq, Hkv, G, D;
     int32_t bs_log2, mbps, window_left;
     int32_t hpw;                 // query heads per workgroup: prefill_heads_per_wg(G)

@@ -74,7 +74,7 @@ __device__ __forceinline__ float bcast_head(float x, int hh) {
     }
 }
 
-template <int D, int HU>
+template <int D, int HU, bool ALIBI = false>
 struct DecodeWave {
     static constexpr int KSTEPS = D / 32;          // MFMA k-steps over head_dim
     static constexpr int VLD = D == 128 ? 4 : 2;   // V rows loaded per lane per tile
@@ -87,13 +87,20 @@ struct DecodeWave {
     float acc[HU][8];
     float m_lane, l_lane;
     float scale_log2;
+    // ALiBi: the slope of this lane's head (column r % HU) times log2(e), 0
+    // without; the logit of key pos gets slope * (pos - qpos) added, qpos
+    // being the query's position
+    float slope_log2;
+    int qpos;
 
-    __device__ void setup(int g, int Hkv, float sl2) {
+    __device__ void setup(int g, int Hkv, float sl2, const float *alibi, int h0) {
         lane = threadIdx.x & 63;
         j = lane >> 4;
         r = lane & 15;
         tok_bytes = Hkv * D * 2;
         scale_log2 = sl2;
+        slope_log2 = alibi ? alibi[h0 + r % HU] * kLog2e : 0.f;
+        qpos = 0;
         koff = (uint32_t)(r * tok_bytes + (g * D + 8 * j) * 2);
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
@@ -153,7 +160,9 @@ struct DecodeWave {
         for (int i = 0; i < 4; ++i) {
             const int pos = t + 4 * j + i;
             valid[i] = !partial || (live && pos >= lo && pos < hi);
-            sv[i] = valid[i] ? s[i] * scale_log2 : -INFINITY;
+            const float x = ALIBI ? fmaf(s[i], scale_log2, slope_log2 * (float)(pos - qpos))
+                                  : s[i] * scale_log2;
+            sv[i] = valid[i] ? x : -INFINITY;
         }
         const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
         if (__any(mx > m_lane + kTau)) {
@@ -227,7 +236,7 @@ struct DecodeWave {
 // ---------------------------------------------------------------------------
 // Fixed partitions: one workgroup per (sequence, head group, partition).
 // ---------------------------------------------------------------------------
-template <int D, int HU>
+template <int D, int HU, bool ALIBI>
 __global__ __launch_bounds__(256) void decode_part_kernel(DecodeArgs a)
 {
     __shared__ float sm_m[kWaves][HU];
@@ -250,8 +259,9 @@ __global__ __launch_bounds__(256) void decode_part_kernel(DecodeArgs a)
     const int end = min(start + a.part_size, L);
     if (a.window_left >= 0) start = max(start, L - 1 - a.window_left);
 
-    DecodeWave<D, HU> w;
-    w.setup(g, a.Hkv, a.scale_log2);
+    DecodeWave<D, HU, ALIBI> w;
+    w.setup(g, a.Hkv, a.scale_log2, a.alibi, h0);
+    w.qpos = L - 1;
     w.load_q(a.q, (size_t)b * a.Hq + h0);
     w.reset();
 
@@ -453,7 +463,7 @@ __device__ void stream_merge_wave(const StreamArgs &a, int b, int h0, int s0, in
     if (a.lse && d == 0) a.lse[(size_t)b * a.Hq + h] = lse_v;
 }
 
-template <int D, int HU, bool FUSED, bool APPEND>
+template <int D, int HU, bool FUSED, bool APPEND, bool ALIBI>
 __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
 {
     __shared__ int s_cum[kStreamMaxB + 1];   // tiles of the sequences before b
@@ -496,8 +506,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
     const int n = min(T, x0 + chunk) - x0;        // tiles of this wave
     if (n <= 0) return;
 
-    DecodeWave<D, HU> w;
-    w.setup(g, a.Hkv, a.scale_log2);
+    DecodeWave<D, HU, ALIBI> w;
+    w.setup(g, a.Hkv, a.scale_log2, a.alibi, h0);
     const int bs_mask = (1 << a.bs_log2) - 1;
 
     // the sequence that holds flattened tile x0: s_cum[b] <= x0 < s_cum[b+1]
@@ -723,6 +733,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
                     const int L = s_len[seg_b];
                     seg_lo = stream_lo(L, a.window_left);
                     seg_hi = L;
+                    w.qpos = L - 1;
                     if (seg_b != q_held) {
                         if (seg_b == q_nb) {
 #pragma unroll
@@ -775,19 +786,29 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
 
 template <int D, int HU>
 void launch_part(const DecodeArgs &a, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_part_kernel<D, HU>), dim3(grid), dim3(256), 0, stream, a);
+    if (a.alibi)
+        hipLaunchKernelGGL((decode_part_kernel<D, HU, true>), dim3(grid), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_part_kernel<D, HU, false>), dim3(grid), dim3(256), 0, stream, a);
+}
+// ALiBi is a separate instantiation, so that calls without slopes run the
+// plain product for the scaled logit.
+template <int D, int HU, bool ALIBI>
+void launch_stream_al(const StreamArgs &a, int grid, hipStream_t stream) {
+    if (a.counters && a.append)
+        hipLaunchKernelGGL((decode_stream_kernel<D, HU, true, true, ALIBI>), dim3(grid), dim3(256),
+                           0, stream, a);
+    else if (a.counters)
+        hipLaunchKernelGGL((decode_stream_kernel<D, HU, true, false, ALIBI>), dim3(grid),
+                           dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_stream_kernel<D, HU, false, false, ALIBI>), dim3(grid),
+                           dim3(256), 0, stream, a);
 }
 template <int D, int HU>
 void launch_stream(const StreamArgs &a, int grid, hipStream_t stream) {
-    if (a.counters && a.append)
-        hipLaunchKernelGGL((decode_stream_kernel<D, HU, true, true>), dim3(grid), dim3(256), 0,
-                           stream, a);
-    else if (a.counters)
-        hipLaunchKernelGGL((decode_stream_kernel<D, HU, true, false>), dim3(grid), dim3(256), 0,
-                           stream, a);
-    else
-        hipLaunchKernelGGL((decode_stream_kernel<D, HU, false, false>), dim3(grid), dim3(256), 0,
-                           stream, a);
+    if (a.alibi) launch_stream_al<D, HU, true>(a, grid, stream);
+    else launch_stream_al<D, HU, false>(a, grid, stream);
 }
 
 }  // namespace

@@ -38,7 +38,11 @@
 //     by more than 2^8 (one ballot per tile); the logit scale and log2(e) are
 //     folded into one FMA per exp2;
 //   * masks only on tiles that straddle the causal diagonal, the window edge
-//     or the end of the keys; tiles outside a wave's visible range are skipped.
+//     or the end of the keys; tiles outside a wave's visible range are skipped;
+//   * ALiBi (vLLM "attention.py" page, PagedAttentionWithALiBi: slope_h times
+//     key position minus query position, added to the scaled logits) is a
+//     separate instantiation: each 32-key chunk is first turned into biased
+//     log2-unit logits with one more FMA per score.
 
 #include "common.h"
 #include "decode.h"
@@ -118,7 +122,7 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const void *base, uint32_t bytes) {
     return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kBufferWord3};
 }
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool ALIBI>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
 {
     using TL = Tile<D>;
@@ -164,6 +168,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
     const int ck0 = a.cu_k[r], Lk = a.cu_k[r + 1] - ck0;
     // the sink logit is needed only at the end: fetch it now, off the tail
     const float sig = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+    const float slope_log2 = ALIBI ? a.alibi[h] * kLog2e : 0.f;
     const int row0 = qt * 128 + blk * bm;           // first row of the workgroup (within request)
     const int nrows = min(bm, Lq - row0);
     const int pos0 = Lk - Lq + row0;                // position of the tile's first row
@@ -288,6 +293,15 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
     float l1 = 0.f;                    // second running sum (two add chains)
     auto finish = [&](f32x16 &sx, int c0) {
         const int pos = wpos0 + lr;
+        if constexpr (ALIBI) {
+            // biased logits in log2 units: s * scale + slope * (key - pos)
+            const float base = slope_log2 * (float)(c0 - pos);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float kx = (float)(8 * (i >> 2) + 4 * lh + (i & 3));
+                sx[i] = fmaf(sx[i], a.scale_log2, fmaf(slope_log2, kx, base));
+            }
+        }
         const bool full = (c0 + 31 <= wpos0) && (c0 + 32 <= Lk) &&
                           (a.window_left < 0 || c0 >= wpos1 - a.window_left);
         if (!full) {
@@ -309,8 +323,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
         // the other lane half holds the row's other keys
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mw), __float_as_uint(mw),
                                                          false, false);
-        const float mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) *
-                         a.scale_log2;
+        const float mx = ALIBI ? __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]))
+                               : __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) *
+                                     a.scale_log2;
         if (__any(mx > m + kTau)) {
             const float nm = fmaxf(m, mx);
             const float alpha = fast_exp2(m - nm);
@@ -330,8 +345,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
         u32x4 w;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-            const float p0 = fast_exp2(fmaf(sx[8 * sp + 2 * e2], a.scale_log2, -m));
-            const float p1 = fast_exp2(fmaf(sx[8 * sp + 2 * e2 + 1], a.scale_log2, -m));
+            const float p0 = ALIBI ? fast_exp2(sx[8 * sp + 2 * e2] - m)
+                                   : fast_exp2(fmaf(sx[8 * sp + 2 * e2], a.scale_log2, -m));
+            const float p1 = ALIBI ? fast_exp2(sx[8 * sp + 2 * e2 + 1] - m)
+                                   : fast_exp2(fmaf(sx[8 * sp + 2 * e2 + 1], a.scale_log2, -m));
             w[e2] = pack_bf16x2(p0, p1);
         }
         l = add_bf16_pair(w[0], l);
@@ -465,21 +482,38 @@ pkv_status launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream)
                 hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
             if (first == hipSuccess) first = e;
         };
-        set((const void *)prefill_bf16_kernel<128, false>, 2 * Tile<128>::BUF);
-        set((const void *)prefill_bf16_kernel<128, true>, 2 * Tile<128>::BUF);
-        set((const void *)prefill_bf16_kernel<64, false>, 2 * Tile<64>::BUF);
-        set((const void *)prefill_bf16_kernel<64, true>, 2 * Tile<64>::BUF);
+        set((const void *)prefill_bf16_kernel<128, false, false>, 2 * Tile<128>::BUF);
+        set((const void *)prefill_bf16_kernel<128, true, false>, 2 * Tile<128>::BUF);
+        set((const void *)prefill_bf16_kernel<64, false, false>, 2 * Tile<64>::BUF);
+        set((const void *)prefill_bf16_kernel<64, true, false>, 2 * Tile<64>::BUF);
+        set((const void *)prefill_bf16_kernel<128, false, true>, 2 * Tile<128>::BUF);
+        set((const void *)prefill_bf16_kernel<128, true, true>, 2 * Tile<128>::BUF);
+        set((const void *)prefill_bf16_kernel<64, false, true>, 2 * Tile<64>::BUF);
+        set((const void *)prefill_bf16_kernel<64, true, true>, 2 * Tile<64>::BUF);
         return first;
     }();
     if (raised != hipSuccess) return PKV_ERR_HIP;
     const bool paged = a.block_table != nullptr;
     const dim3 g((unsigned)grid), b(256);
+    auto go = [&](auto kernel, int lds) { hipLaunchKernelGGL(kernel, g, b, lds, stream, a); };
     if (a.D == 128) {
-        if (paged) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), g, b, 2 * Tile<128>::BUF, stream, a);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), g, b, 2 * Tile<128>::BUF, stream, a);
+        const int lds = 2 * Tile<128>::BUF;
+        if (a.alibi) {
+            if (paged) go(prefill_bf16_kernel<128, true, true>, lds);
+            else go(prefill_bf16_kernel<128, false, true>, lds);
+        } else {
+            if (paged) go(prefill_bf16_kernel<128, true, false>, lds);
+            else go(prefill_bf16_kernel<128, false, false>, lds);
+        }
     } else {
-        if (paged) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), g, b, 2 * Tile<64>::BUF, stream, a);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), g, b, 2 * Tile<64>::BUF, stream, a);
+        const int lds = 2 * Tile<64>::BUF;
+        if (a.alibi) {
+            if (paged) go(prefill_bf16_kernel<64, true, true>, lds);
+            else go(prefill_bf16_kernel<64, false, true>, lds);
+        } else {
+            if (paged) go(prefill_bf16_kernel<64, true, false>, lds);
+            else go(prefill_bf16_kernel<64, false, false>, lds);
+        }
     }
     return launch_status();
 }

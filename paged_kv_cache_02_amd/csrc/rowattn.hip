@@ -66,6 +66,8 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
         acc[e] = 0.f;
     }
     float m = kNoMax, l = 0.f;
+    // ALiBi: slope * (key position - query position), in log2 units like qv
+    const float slope_log2 = a.alibi ? a.alibi[h] * kLog2e : 0.f;
     const int32_t *bt = a.block_table ? a.block_table + (size_t)req * a.mbps : nullptr;
     const int bs_mask = (1 << a.bs_log2) - 1;
     if (a.mode == 0 && a.append && h % a.G == 0 && pidx == 0) {
@@ -108,6 +110,7 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
         for (int e = 0; e < E; ++e) s = fmaf(qv[e], ld_elem<BF16>(kb, off + lane + 64 * e), s);
 #pragma unroll
         for (int msk = 1; msk < 64; msk <<= 1) s += shfl_xor(s, msk);
+        s = fmaf(slope_log2, (float)(jj - pos), s);
         const float nm = fmaxf(m, s);
         const float c = fast_exp2(m - nm);
         const float p = fast_exp2(s - nm);

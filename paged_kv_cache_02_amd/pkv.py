@@ -30,24 +30,24 @@ SIGNATURES = {
                                              _I32, _I32, ctypes.c_int, _P]),
     "pkv_paged_decode_workspace_bytes": (ctypes.c_size_t, [_I32] * 7 + [ctypes.c_int]),
     "pkv_paged_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
-                                        _I32, _I32, _I32, _I32, _F, _I32, _I32, _P, _SZ,
+                                        _I32, _I32, _I32, _I32, _F, _I32, _P, _I32, _P, _SZ,
                                         ctypes.c_int, _P]),
     "pkv_paged_decode_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32,
                                                _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F,
-                                               _I32, _P, _SZ, ctypes.c_int, _P]),
+                                               _I32, _P, _P, _SZ, ctypes.c_int, _P]),
     "pkv_paged_decode_stage": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
-                                              _I32, _I32, _I32, _F, _I32, _P, _SZ, ctypes.c_int,
-                                              _P]),
+                                              _I32, _I32, _I32, _F, _I32, _P, _P, _SZ,
+                                              ctypes.c_int, _P]),
     "pkv_paged_decode_finish": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _SZ,
                                                ctypes.c_int, _P]),
     "pkv_paged_decode_partitions": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
-                                                   _I32, _I32, _I32, _I32, _I32, _F, _I32, _I32,
-                                                   _I32, ctypes.c_int, _P]),
+                                                   _I32, _I32, _I32, _I32, _I32, _F, _I32, _P,
+                                                   _I32, _I32, ctypes.c_int, _P]),
     "pkv_merge_partitions": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32,
                                             _I32, ctypes.c_int, _P]),
     "pkv_varlen_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P,
                                           _P, _I32, _I32, _I32, _I32, _I32, _I32, _F, _I32,
-                                          _I32, _P, ctypes.c_int, _P]),
+                                          _I32, _P, _P, ctypes.c_int, _P]),
 }
 
 
@@ -142,7 +142,8 @@ def decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_dim, block_size, m
 
 def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: float, sink=None,
                  window_left: int = -1, partition_size: int = 0,
-                 max_seqlen_k: Optional[int] = None, out=None, lse=None, workspace=None):
+                 max_seqlen_k: Optional[int] = None, out=None, lse=None, workspace=None,
+                 alibi_slopes=None):
     """out [B,Hq,D] for q [B,Hq,D] over k/v_cache [NB,bs,Hkv,D].
 
     A caller-provided `workspace` must have been zero-filled once (the library
@@ -161,7 +162,8 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: floa
         _ptr(out), _ptr(_f32(lse, "lse")), _ptr(q), _ptr(k_cache), _ptr(v_cache),
         _ptr(_i32(block_table, "block_table")), _ptr(_i32(cache_seqlens, "cache_seqlens")),
         _ptr(_f32(sink, "sink")), B, Hq, Hkv, D, bs, NB, block_table.shape[1], max_seqlen_k,
-        float(sm_scale), window_left, partition_size, _ptr(workspace),
+        float(sm_scale), window_left, _ptr(_f32(alibi_slopes, "alibi_slopes")), partition_size,
+        _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _dt(q),
         _stream()), "paged_decode")
     return out
@@ -169,7 +171,8 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: floa
 
 def paged_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens,
                         sm_scale: float, sink=None, window_left: int = -1,
-                        max_seqlen_k: Optional[int] = None, out=None, lse=None, workspace=None):
+                        max_seqlen_k: Optional[int] = None, out=None, lse=None, workspace=None,
+                        alibi_slopes=None):
     """Store k_new/v_new [B,Hkv,D] at position cache_seqlens[b] of each sequence and
     attend q [B,Hq,D] to keys 0..cache_seqlens[b]; cache_seqlens is not changed.
 
@@ -189,21 +192,23 @@ def paged_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_se
         _ptr(out), _ptr(_f32(lse, "lse")), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
         _ptr(v_cache), _ptr(_i32(block_table, "block_table")),
         _ptr(_i32(cache_seqlens, "cache_seqlens")), _ptr(_f32(sink, "sink")), B, Hq, Hkv, D, bs,
-        NB, block_table.shape[1], max_seqlen_k, float(sm_scale), window_left, _ptr(workspace),
+        NB, block_table.shape[1], max_seqlen_k, float(sm_scale), window_left,
+        _ptr(_f32(alibi_slopes, "alibi_slopes")), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _dt(q),
         _stream()), "paged_decode_append")
     return out
 
 
 def paged_decode_stage(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: float,
-                       max_seqlen_k: int, workspace, window_left: int = -1):
+                       max_seqlen_k: int, workspace, window_left: int = -1, alibi_slopes=None):
     """First stage of automatic bf16 decode: balanced partial results into workspace."""
     B, Hq, D = q.shape
     NB, bs, Hkv, _ = k_cache.shape
     _check(lib.pkv_paged_decode_stage(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(_i32(block_table, "block_table")),
         _ptr(_i32(cache_seqlens, "cache_seqlens")), B, Hq, Hkv, D, bs, NB, block_table.shape[1],
-        max_seqlen_k, float(sm_scale), window_left, _ptr(workspace),
+        max_seqlen_k, float(sm_scale), window_left, _ptr(_f32(alibi_slopes, "alibi_slopes")),
+        _ptr(workspace),
         workspace.numel() * workspace.element_size(), _dt(q), _stream()), "paged_decode_stage")
 
 
@@ -219,7 +224,7 @@ def paged_decode_finish(out, workspace, num_kv_heads: int, sink=None, lse=None):
 
 def paged_decode_partitions(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: float,
                             partition_size: int, max_seqlen_k: int, window_left: int = -1,
-                            part_out=None, part_lse=None):
+                            part_out=None, part_lse=None, alibi_slopes=None):
     """Per-partition results (sink excluded): part_out [B,Hq,P,D], part_lse [B,Hq,P]."""
     B, Hq, D = q.shape
     NB, bs, Hkv, _ = k_cache.shape
@@ -232,7 +237,8 @@ def paged_decode_partitions(q, k_cache, v_cache, block_table, cache_seqlens, sm_
         _ptr(_f32(part_out, "part_out")), _ptr(_f32(part_lse, "part_lse")), _ptr(q),
         _ptr(k_cache), _ptr(v_cache), _ptr(_i32(block_table, "block_table")),
         _ptr(_i32(cache_seqlens, "cache_seqlens")), B, Hq, Hkv, D, bs, NB, block_table.shape[1],
-        max_seqlen_k, float(sm_scale), window_left, partition_size, part_out.shape[2], _dt(q),
+        max_seqlen_k, float(sm_scale), window_left, _ptr(_f32(alibi_slopes, "alibi_slopes")),
+        partition_size, part_out.shape[2], _dt(q),
         _stream()), "paged_decode_partitions")
     return part_out, part_lse
 
@@ -254,7 +260,7 @@ def merge_partitions(part_out, part_lse, cache_seqlens, partition_size: int, sin
 def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                    sm_scale: float, num_kv_heads: Optional[int] = None, k=None, v=None,
                    k_cache=None, v_cache=None, block_table=None, sink=None,
-                   window_left: int = -1, out=None, lse=None):
+                   window_left: int = -1, out=None, lse=None, alibi_slopes=None):
     """Causal varlen prefill: out [sum Lq, Hq, D]."""
     T, Hq, D = q.shape
     B = cu_seqlens_q.shape[0] - 1
@@ -273,6 +279,7 @@ def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_
         _ptr(v_cache), _ptr(None if block_table is None else _i32(block_table, "block_table")),
         bs, NB, MB, _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")),
         _ptr(_i32(cu_seqlens_k, "cu_seqlens_k")), B, int(max_seqlen_q), int(max_seqlen_k), Hq,
-        Hkv, D, float(sm_scale), 1, window_left, _ptr(_f32(sink, "sink")), _dt(q), _stream()),
+        Hkv, D, float(sm_scale), 1, window_left, _ptr(_f32(alibi_slopes, "alibi_slopes")),
+        _ptr(_f32(sink, "sink")), _dt(q), _stream()),
         "varlen_prefill")
     return out

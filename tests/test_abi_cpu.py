@@ -61,7 +61,7 @@ def test_workspace_sizes():
 def decode_call(**over):
     a = dict(out=FAKE, lse=None, q=FAKE, k_cache=FAKE, v_cache=FAKE, block_table=FAKE,
              cache_seqlens=FAKE, sink=None, B=2, Hq=8, Hkv=2, D=128, bs=16, NB=4, MB=4,
-             max_seqlen_k=64, scale=0.1, window=-1, part=0, ws=None, ws_bytes=0, dt=1,
+             max_seqlen_k=64, scale=0.1, window=-1, alibi=None, part=0, ws=None, ws_bytes=0, dt=1,
              stream=None)
     a.update(over)
     return lib.pkv_paged_decode(*a.values())
@@ -94,7 +94,8 @@ def test_decode_validation(over, status):
 def append_call(**over):
     a = dict(out=FAKE, lse=None, q=FAKE, k_new=FAKE, v_new=FAKE, k_cache=FAKE, v_cache=FAKE,
              block_table=FAKE, cache_seqlens=FAKE, sink=None, B=2, Hq=8, Hkv=2, D=128, bs=16,
-             NB=4, MB=4, max_seqlen_k=63, scale=0.1, window=-1, ws=None, ws_bytes=0, dt=1,
+             NB=4, MB=4, max_seqlen_k=63, scale=0.1, window=-1, alibi=None, ws=None, ws_bytes=0,
+             dt=1,
              stream=None)
     a.update(over)
     return lib.pkv_paged_decode_append(*a.values())
@@ -125,7 +126,7 @@ def test_decode_append_validation(over, status):
 def prefill_call(**over):
     a = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, k_cache=None, v_cache=None, bt=None,
              bs=0, NB=0, MB=0, cu_q=FAKE, cu_k=FAKE, B=2, maxq=16, maxk=16, Hq=8, Hkv=2, D=64,
-             scale=0.1, causal=1, window=-1, sink=None, dt=1, stream=None)
+             scale=0.1, causal=1, window=-1, alibi=None, sink=None, dt=1, stream=None)
     a.update(over)
     return lib.pkv_varlen_prefill(*a.values())
 
