@@ -247,3 +247,74 @@ def decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens,
                             window_left=window_left, units=units, nthreads=nthreads, alibi=alibi)
     return out, lse, kc, vc
 
+
+
+# ---------------------------------------------------------------------------
+# Rotary position embedding.  The vLLM "attention.py" page (PagedAttentionWithRoPE)
+# applies a rotary embedding to query and key before attention, parameterised
+# by head size, rotary_dim, max_position, base, is_neox_style and an optional
+# rope_scaling {"type": "linear" | "dynamic", "factor"}; the rotation itself is
+# not printed on the pages.  These functions take the standard rotary
+# embedding as the reading: frequency i < rotary_dim / 2 turns at
+# base^(-2i / rotary_dim) per position; neox style pairs dimension d with
+# d + rotary_dim / 2, the other style pairs 2i with 2i + 1; dimensions from
+# rotary_dim on are left alone.  Linear scaling divides the position by the
+# factor; dynamic (NTK-aware) scaling raises the base for a table longer than
+# max_position.  All in float64 numpy.
+# ---------------------------------------------------------------------------
+
+ROPE_NONE, ROPE_LINEAR, ROPE_DYNAMIC = 0, 1, 2
+
+
+def rope_cos_sin(num_positions: int, rotary_dim: int, base: float, scaling: int = ROPE_NONE,
+                 factor: float = 1.0, max_position: int = 0) -> np.ndarray:
+    """Table [num_positions, rotary_dim]: cos of the angles, then sin."""
+    half = rotary_dim // 2
+    b = float(base)
+    if scaling == ROPE_DYNAMIC and num_positions > max_position:
+        b = b * ((factor * num_positions / max_position) - (factor - 1.0)) ** (
+            rotary_dim / (rotary_dim - 2))
+    inv_freq = b ** (-(2.0 * np.arange(half)) / rotary_dim)
+    t = np.arange(num_positions, dtype=np.float64)
+    if scaling == ROPE_LINEAR:
+        t = t / factor
+    ang = np.outer(t, inv_freq)
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1)
+
+
+def _values64(t) -> np.ndarray:
+    """Values (not storage bits) of a tensor or array as float64."""
+    if isinstance(t, torch.Tensor):
+        return t.detach().cpu().double().numpy()
+    return np.asarray(t, dtype=np.float64)
+
+
+def rope_apply(x, positions, cos_sin, rotary_dim: int, neox: bool) -> np.ndarray:
+    """Rows x [T, H, D] rotated by their positions [T]; float64 copy."""
+    y = _values64(x).copy()
+    pos = np.asarray(_np(positions)).astype(np.int64)
+    tab = _values64(cos_sin)
+    assert pos.size == 0 or (pos.min() >= 0 and pos.max() < tab.shape[0]), "position outside the table"
+    half = rotary_dim // 2
+    c = tab[pos, :half][:, None, :]           # [T, 1, half]
+    s = tab[pos, half:rotary_dim][:, None, :]
+    if neox:
+        a, b = y[..., :half].copy(), y[..., half:rotary_dim].copy()
+        y[..., :half] = a * c - b * s
+        y[..., half:rotary_dim] = b * c + a * s
+    else:
+        a, b = y[..., 0:rotary_dim:2].copy(), y[..., 1:rotary_dim:2].copy()
+        y[..., 0:rotary_dim:2] = a * c - b * s
+        y[..., 1:rotary_dim:2] = b * c + a * s
+    return y
+
+
+def query_positions(cu_seqlens_q, cu_seqlens_k) -> np.ndarray:
+    """Position of every packed query row: Lk - Lq + i within its request."""
+    cq = _np(cu_seqlens_q).astype(np.int64)
+    ck = _np(cu_seqlens_k).astype(np.int64)
+    out = []
+    for r in range(len(cq) - 1):
+        Lq, Lk = cq[r + 1] - cq[r], ck[r + 1] - ck[r]
+        out.append(Lk - Lq + np.arange(Lq))
+    return np.concatenate(out) if out else np.zeros(0, np.int64)

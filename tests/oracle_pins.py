@@ -467,6 +467,61 @@ def pin_alibi_closed_form():
     _close(od[0], o[Lk - 1], 1e-14, 1e-12, "alibi decode == last prefill row")
 
 
+def pin_rope():
+    """Rotary embedding (the reading of the vLLM page's PagedAttentionWithRoPE,
+    whose rotation is not printed): position 0 is the identity; each rotated
+    pair keeps its norm; dimensions past rotary_dim are untouched; the dot
+    product of a rotated query and key depends only on their distance (both
+    pairings); the neox pairing equals the interleaved one under the
+    dimension permutation; linear scaling is the unscaled table at pos /
+    factor; and hand-computed angles for the plain and dynamic tables."""
+    rng = np.random.default_rng(31)
+    rd, D, base = 8, 12, 10000.0
+    tab = oracle.rope_cos_sin(64, rd, base)
+    # hand values: rotary_dim 2 turns at 1 rad per position
+    t2 = oracle.rope_cos_sin(5, 2, base)
+    _close(t2[3], np.array([np.cos(3.0), np.sin(3.0)]), 1e-15, 1e-15, "rope rd 2")
+    _close(tab[5, 1], np.cos(5 * base ** -0.25), 1e-15, 1e-15, "rope freq 1")
+    for neox in (True, False):
+        x = rng.normal(size=(4, 3, D))
+        y0 = oracle.rope_apply(x, np.zeros(4, int), tab, rd, neox)
+        _close(y0, x, 0, 0, "rope pos 0")
+        pos = np.array([1, 7, 20, 63])
+        y = oracle.rope_apply(x, pos, tab, rd, neox)
+        _close(y[..., rd:], x[..., rd:], 0, 0, "rope pass-through dims")
+        if neox:
+            pairs = [(i, i + rd // 2) for i in range(rd // 2)]
+        else:
+            pairs = [(2 * i, 2 * i + 1) for i in range(rd // 2)]
+        for a, b in pairs:
+            _close(np.hypot(y[..., a], y[..., b]), np.hypot(x[..., a], x[..., b]), 1e-12, 1e-12,
+                   "rope pair norm")
+        q, k = rng.normal(size=(1, 1, D)), rng.normal(size=(1, 1, D))
+        dots = []
+        for m, n in [(10, 3), (17, 10), (40, 33)]:
+            qm = oracle.rope_apply(q, np.array([m]), tab, rd, neox)[0, 0]
+            kn = oracle.rope_apply(k, np.array([n]), tab, rd, neox)[0, 0]
+            dots.append(qm @ kn)
+        _close(np.array(dots[1:]), np.array([dots[0]] * 2), 1e-12, 1e-12, "rope relative")
+    # neox pairing == interleaved pairing under the permutation (i, i+rd/2) -> (2i, 2i+1)
+    perm = np.concatenate([np.array([[i, i + rd // 2] for i in range(rd // 2)]).ravel(),
+                           np.arange(rd, D)])
+    x = rng.normal(size=(2, 1, D))
+    pos = np.array([3, 50])
+    yn = oracle.rope_apply(x, pos, tab, rd, True)
+    yg = oracle.rope_apply(x[..., perm], pos, tab, rd, False)
+    _close(yg, yn[..., perm], 1e-13, 1e-13, "rope neox vs interleaved")
+    # linear scaling: row f*p of the linear table is row p of the plain one
+    lin = oracle.rope_cos_sin(64, rd, base, oracle.ROPE_LINEAR, 4.0, 16)
+    _close(lin[0:64:4], tab[0:16], 1e-15, 1e-15, "rope linear")
+    # dynamic: no change within max_position; beyond it base' = base * (f L / M - (f - 1))^(rd/(rd-2))
+    dyn_short = oracle.rope_cos_sin(8, 4, base, oracle.ROPE_DYNAMIC, 2.0, 8)
+    _close(dyn_short, oracle.rope_cos_sin(8, 4, base), 0, 0, "rope dynamic short")
+    dyn = oracle.rope_cos_sin(32, 4, base, oracle.ROPE_DYNAMIC, 2.0, 8)
+    # base' = 10000 * (2*32/8 - 1)^2 = 490000, frequency 1 = 490000^-0.5 = 1/700
+    _close(dyn[7, [1, 3]], np.array([np.cos(0.01), np.sin(0.01)]), 1e-15, 1e-13, "rope dynamic")
+
+
 def pin_bf16_inputs_read_exactly():
     """bf16 storage is read as its exact value: the oracle on bf16 tensors
     equals the oracle on the same values widened to fp32."""
