@@ -153,6 +153,7 @@ KERNEL_SOURCES = {
     "prefill_c3": ("prefill.hip", "decode.h", "common.h"),
     "prefill_c4": ("prefill.hip", "decode.h", "common.h"),
     "reshape_c3": ("cache.hip", "common.h"),
+    "reshape_rope_c3": ("rope.hip", "decode.h", "common.h"),
 }
 
 
@@ -348,9 +349,26 @@ def visible_pairs(q_lens, k_lens, window):
     return n
 
 
+def rope_setup(c, rotary_dim=128, neox=True):
+    """Rotary table over the longest request, and the positions of the
+    packed queries (Lk - Lq + i) and keys (0 .. Lk - 1)."""
+    tab = pkv.rope_cos_sin(max(c.k_lens), rotary_dim)
+    qpos = np.concatenate([np.arange(Lk - Lq, Lk) for Lq, Lk in zip(c.q_lens, c.k_lens)])
+    kpos = np.concatenate([np.arange(Lk) for Lk in c.k_lens])
+    return {"tab": tab, "rd": rotary_dim, "neox": neox,
+            "qpos": torch.from_numpy(qpos.astype(np.int32)).cuda(),
+            "kpos": torch.from_numpy(kpos.astype(np.int32)).cuda()}
+
+
 def bench_prefill(c, name, steps, warmup, reps, with_cache_write=False, traffic_key=None,
-                  alibi=None):
+                  alibi=None, rope=None, rope_unfused=False):
+    """rope: from rope_setup; q is then rotated inside the prefill (and K by
+    reshape_and_cache_rope when with_cache_write), or, with rope_unfused, by a
+    separate rope_apply launch before a plain prefill."""
     T = c.q.shape[0]
+    fused = rope is not None and not rope_unfused
+    rkw = dict(rope_cos_sin=rope["tab"], rotary_dim=rope["rd"], rope_neox=rope["neox"]) \
+        if fused else {}
     qs = [c.q.cuda() for _ in range(reps)]
     cq, ck = c.cu_seqlens_q.cuda(), c.cu_seqlens_k.cuda()
     al = None if alibi is None else alibi.cuda()
@@ -377,18 +395,25 @@ def bench_prefill(c, name, steps, warmup, reps, with_cache_write=False, traffic_
 
     def step(i, kt):
         r = i % reps
-        if with_cache_write:
+        if with_cache_write and fused:
+            kt.time("reshape_and_cache", lambda: pkv.reshape_and_cache_rope(
+                ks[r], vs[r], kcache, vcache, slots, rope["kpos"], rope["tab"], rope["rd"],
+                rope["neox"]))
+        elif with_cache_write:
             kt.time("reshape_and_cache",
                     lambda: pkv.reshape_and_cache(ks[r], vs[r], kcache, vcache, slots))
+        if rope_unfused:
+            kt.time("rope_apply", lambda: pkv.rope_apply(qs[r], rope["qpos"], rope["tab"],
+                                                         rope["rd"], rope["neox"]))
         if c.paged:
             kt.time("prefill", lambda: pkv.varlen_prefill(
                 qs[r], cq, ck, c.max_seqlen_q, c.max_seqlen_k, c.sm_scale, c.Hkv,
                 k_cache=kc, v_cache=vc, block_table=tables[r], sink=sink,
-                window_left=c.window_left, out=out, alibi_slopes=al))
+                window_left=c.window_left, out=out, alibi_slopes=al, **rkw))
         else:
             kt.time("prefill", lambda: pkv.varlen_prefill(
                 qs[r], cq, ck, c.max_seqlen_q, c.max_seqlen_k, c.sm_scale, c.Hkv, k=ks[r],
-                v=vs[r], sink=sink, window_left=c.window_left, out=out, alibi_slopes=al))
+                v=vs[r], sink=sink, window_left=c.window_left, out=out, alibi_slopes=al, **rkw))
 
     ms, kt = timed_steps(step, steps, warmup)
     pairs = visible_pairs(c.q_lens, c.k_lens, c.window_left)
@@ -411,14 +436,22 @@ def bench_prefill(c, name, steps, warmup, reps, with_cache_write=False, traffic_
         ridge = min(MFMA_BF16_PEAK_TFS * 1e12, flops / byts * HBM_PEAK_GBS * 1e9)
         res["min_roofline_tflops"] = round(ridge / 1e12, 2)
         res["frac_of_min_roofline"] = round(flops / (pre_ms * 1e-3) / ridge, 4)
+    if rope_unfused:
+        ra_ms = kt.mean_ms("rope_apply")
+        res["kernels_ms"]["rope_apply"] = round(ra_ms, 4)
+        res["prefill_plus_rope_apply_ms"] = round(pre_ms + ra_ms, 4)
     if with_cache_write:
         rc_ms = kt.mean_ms("reshape_and_cache")
+        # K and V rows read and written; the rotated form also reads one
+        # table row (rotary_dim float32) per token
         rbytes = 2 * sum(c.k_lens) * c.Hkv * c.D * 2 * 2
-        res["reshape_and_cache"] = {
+        if fused:
+            rbytes += sum(c.k_lens) * rope["rd"] * 4
+        res["reshape_and_cache_rope" if fused else "reshape_and_cache"] = {
             "value": round(rbytes / (rc_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
             "kernel_ms": round(rc_ms, 4), "algorithmic_bytes": rbytes,
             "roofline": roofline("hbm", rbytes / (rc_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
-                                 pmc_traffic("reshape_c3"))}
+                                 pmc_traffic("reshape_rope_c3" if fused else "reshape_c3"))}
     torch.cuda.empty_cache()
     return res, out
 
@@ -497,6 +530,18 @@ def main():
                                alibi=alibi_slopes(c3.Hq))
         workloads["varlen_prefill_alibi"] = r3a
         log(f"prefill with ALiBi slopes: {r3a['value']} TFLOP/s")
+        rp = rope_setup(c3)
+        r3r, _ = bench_prefill(c3, "varlen_prefill_8x_U256-4096_rope", steps, warmup, reps=2,
+                               with_cache_write=True, rope=rp)
+        r3u, _ = bench_prefill(c3, "varlen_prefill_8x_U256-4096_rope_unfused", steps, warmup,
+                               reps=2, rope=rp, rope_unfused=True)
+        r3r["unfused_prefill_plus_rope_apply_ms"] = r3u["prefill_plus_rope_apply_ms"]
+        r3r["speedup_vs_unfused"] = round(r3u["prefill_plus_rope_apply_ms"] /
+                                          r3r["kernels_ms"]["prefill"], 3)
+        workloads["varlen_prefill_rope"] = r3r
+        log(f"prefill with q rotated in the kernel: {r3r['value']} TFLOP/s, "
+            f"{r3r['speedup_vs_unfused']}x rope_apply + prefill; reshape_and_cache_rope "
+            f"{r3r['reshape_and_cache_rope']['value']} GB/s")
     if ARGS.only in ("all", "chunked"):
         log("chunked prefill workload (4 x 512 q on 8704 paged keys, window 128, 64/8, D 64)")
         c4 = synth.config4_chunked(poison=False, spare_blocks=0)

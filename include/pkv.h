@@ -8,6 +8,10 @@
  *                           (vLLM "attention.py" page, PagedAttention.forward:
  *                           the cache_ops.reshape_and_cache call and its
  *                           slot_mapping argument)
+ *   pkv_rope_cos_sin,       rotary position embedding: the cos/sin table,
+ *   pkv_rope_apply,         in-place rotation of rows by their positions, and
+ *   pkv_reshape_and_cache_rope  the cache store with the key rotated as it
+ *                           is written (vLLM page, PagedAttentionWithRoPE)
  *   pkv_paged_decode        one query token per sequence over a paged cache
  *                           (Transformers "Paged attention" doc, decode path:
  *                           block_table and cache_seqlens; vLLM page,
@@ -119,6 +123,49 @@ pkv_status pkv_reshape_and_cache(const void *key, const void *value, void *k_cac
                                  int64_t key_stride, int64_t value_stride, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                  pkv_dtype dtype, void *stream);
+
+/*
+ * Rotary position embedding (vLLM "attention.py" page, PagedAttentionWithRoPE:
+ * query and key are rotated by their positions before attention, with
+ * rotary_dim, base, is_neox_style and an optional rope_scaling of type
+ * "linear" or "dynamic" with a factor).  The pages name the rotation but do
+ * not print it; it is the standard rotary embedding: frequency i <
+ * rotary_dim / 2 turns by base^(-2i / rotary_dim) per position; neox style
+ * (neox != 0) rotates dimension d with d + rotary_dim / 2, the other style
+ * 2i with 2i + 1:  x'_a = x_a cos - x_b sin,  x'_b = x_b cos + x_a sin.
+ * Dimensions from rotary_dim on are unchanged.
+ *
+ * pkv_rope_cos_sin -- the table cos_sin [num_positions, rotary_dim] float32:
+ * columns [0, rotary_dim/2) hold cos(angle(p, i)), the rest sin(angle(p, i)),
+ * computed in double.  scaling 0: angle = p * f_i; 1 (linear): (p / factor) *
+ * f_i; 2 (dynamic, NTK-aware): the base becomes base * (factor *
+ * num_positions / max_position - (factor - 1))^(rotary_dim / (rotary_dim -
+ * 2)) when num_positions > max_position.  rotary_dim even >= 2.
+ *
+ * pkv_rope_apply -- rotate x [T, num_heads, head_dim] in place, row t by
+ * positions[t] (int32, contract: < the table's num_positions); row_stride
+ * elements between tokens (0: dense; a multiple of 8).  rotary_dim a
+ * multiple of 16 in [16, head_dim]; head_dim 64 or 128.
+ *
+ * pkv_reshape_and_cache_rope -- pkv_reshape_and_cache with each key row
+ * rotated by positions[t] as it is stored (values stored unchanged); the
+ * same arguments as pkv_reshape_and_cache plus positions, cos_sin, rotary_dim
+ * (as for pkv_rope_apply) and neox.  Rotation runs in float32; bf16 results
+ * are rounded to nearest even.
+ */
+pkv_status pkv_rope_cos_sin(float *cos_sin, int32_t num_positions, int32_t rotary_dim,
+                           float base, int32_t scaling, float factor, int32_t max_position,
+                           void *stream);
+pkv_status pkv_rope_apply(void *x, const int32_t *positions, const float *cos_sin, int32_t T,
+                          int32_t num_heads, int32_t head_dim, int64_t row_stride,
+                          int32_t rotary_dim, int32_t neox, pkv_dtype dtype, void *stream);
+pkv_status pkv_reshape_and_cache_rope(const void *key, const void *value, void *k_cache,
+                                      void *v_cache, const int32_t *slot_mapping,
+                                      const int32_t *positions, const float *cos_sin, int32_t T,
+                                      int64_t key_stride, int64_t value_stride,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                      int32_t num_blocks, int32_t rotary_dim, int32_t neox,
+                                      pkv_dtype dtype, void *stream);
 
 /*
  * Bytes of workspace pkv_paged_decode needs for these sizes, this
@@ -330,6 +377,12 @@ pkv_status pkv_merge_partitions(void *out, float *lse, const float *part_out,
  *                   launch); paged: Lk <= max_blocks_per_seq * block_size.
  *   causal          must be 1 (bottom-right aligned: queries are the last Lq
  *                   positions of the request's keys)
+ *   rope_cos_sin    NULL, or a pkv_rope_cos_sin table of rope_positions rows
+ *                   (>= max_seqlen_k): q is then rotated by its position p =
+ *                   Lk - Lq + i as it is loaded, with rotary_dim (a multiple
+ *                   of 32 in [32, head_dim]) and rope_neox as for
+ *                   pkv_rope_apply; the keys must already be rotated (for
+ *                   example stored with pkv_reshape_and_cache_rope)
  *
  * Errors besides the common ones: PKV_ERR_UNSUPPORTED for bfloat16 with
  * contiguous K/V when max_seqlen_k * num_kv_heads * head_dim * 2 bytes (one
@@ -342,7 +395,9 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
                               int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads,
                               int32_t num_kv_heads, int32_t head_dim, float sm_scale,
                               int32_t causal, int32_t window_left, const float *alibi_slopes,
-                              const float *sink, pkv_dtype dtype, void *stream);
+                              const float *rope_cos_sin, int32_t rope_positions,
+                              int32_t rotary_dim, int32_t rope_neox, const float *sink,
+                              pkv_dtype dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -197,6 +197,75 @@ pkv_status pkv_reshape_and_cache(const void *key, const void *value, void *k_cac
                                     (hipStream_t)stream);
 }
 
+pkv_status pkv_rope_cos_sin(float *cos_sin, int32_t num_positions, int32_t rotary_dim,
+                           float base, int32_t scaling, float factor, int32_t max_position,
+                           void *stream)
+{
+    if (num_positions < 0 || rotary_dim < 2 || rotary_dim % 2 || !(base > 0.f))
+        return PKV_ERR_SHAPE;
+    if (scaling < 0 || scaling > 2) return PKV_ERR_UNSUPPORTED;
+    if (scaling != 0 && !(factor > 0.f)) return PKV_ERR_SHAPE;
+    if (scaling == 2 && (max_position <= 0 || rotary_dim < 4)) return PKV_ERR_SHAPE;
+    if (num_positions == 0) return PKV_OK;
+    if (!cos_sin) return PKV_ERR_NULL;
+    return launch_rope_table(cos_sin, num_positions, rotary_dim, base, scaling, factor,
+                             max_position, (hipStream_t)stream);
+}
+
+// rotary_dim: a multiple of 16 within the head (the kernels rotate whole
+// 16-byte chunks and pair chunk u with chunk u + rotary_dim / 2 / chunk)
+static pkv_status check_rope(int32_t rotary_dim, int32_t head_dim) {
+    if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (rotary_dim < 16 || rotary_dim > head_dim || rotary_dim % 16) return PKV_ERR_UNSUPPORTED;
+    return PKV_OK;
+}
+
+pkv_status pkv_rope_apply(void *x, const int32_t *positions, const float *cos_sin, int32_t T,
+                          int32_t num_heads, int32_t head_dim, int64_t row_stride,
+                          int32_t rotary_dim, int32_t neox, pkv_dtype dtype, void *stream)
+{
+    if (T < 0 || num_heads <= 0) return PKV_ERR_SHAPE;
+    if (!dtype_ok(dtype)) return PKV_ERR_UNSUPPORTED;
+    pkv_status st = check_rope(rotary_dim, head_dim);
+    if (st != PKV_OK) return st;
+    if (T == 0) return PKV_OK;
+    if (!x || !positions || !cos_sin) return PKV_ERR_NULL;
+    const int64_t row = (int64_t)num_heads * head_dim;
+    if (row_stride == 0) row_stride = row;
+    if (row_stride < row) return PKV_ERR_SHAPE;
+    if (row_stride % 8 || !aligned16(x)) return PKV_ERR_UNSUPPORTED;
+    return launch_rope_apply(x, positions, cos_sin, T, num_heads, head_dim, row_stride,
+                             rotary_dim, neox, dtype == PKV_BF16, (hipStream_t)stream);
+}
+
+pkv_status pkv_reshape_and_cache_rope(const void *key, const void *value, void *k_cache,
+                                      void *v_cache, const int32_t *slot_mapping,
+                                      const int32_t *positions, const float *cos_sin, int32_t T,
+                                      int64_t key_stride, int64_t value_stride,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                      int32_t num_blocks, int32_t rotary_dim, int32_t neox,
+                                      pkv_dtype dtype, void *stream)
+{
+    if (T < 0 || num_kv_heads <= 0 || num_blocks < 0) return PKV_ERR_SHAPE;
+    if (!dtype_ok(dtype)) return PKV_ERR_UNSUPPORTED;
+    pkv_status st = check_rope(rotary_dim, head_dim);
+    if (st != PKV_OK) return st;
+    if ((st = check_block_size(block_size)) != PKV_OK) return st;
+    if (T == 0) return PKV_OK;
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping || !positions || !cos_sin)
+        return PKV_ERR_NULL;
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    if (key_stride == 0) key_stride = row;
+    if (value_stride == 0) value_stride = row;
+    if (key_stride < row || value_stride < row) return PKV_ERR_SHAPE;
+    if (key_stride % 8 || value_stride % 8) return PKV_ERR_UNSUPPORTED;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PKV_ERR_UNSUPPORTED;
+    return launch_rope_cache(key, value, k_cache, v_cache, slot_mapping, positions, cos_sin, T,
+                             key_stride, value_stride, num_kv_heads, head_dim, rotary_dim, neox,
+                             dtype == PKV_BF16, (hipStream_t)stream);
+}
+
 size_t pkv_paged_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t block_size,
                                         int32_t max_seqlen_k, int32_t partition_size,
@@ -444,7 +513,9 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
                               int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, float sm_scale, int32_t causal,
                               int32_t window_left, const float *alibi_slopes,
-                              const float *sink, pkv_dtype dtype,
+                              const float *rope_cos_sin, int32_t rope_positions,
+                              int32_t rotary_dim, int32_t rope_neox, const float *sink,
+                              pkv_dtype dtype,
                               void *stream)
 {
     if (B < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return PKV_ERR_SHAPE;
@@ -452,6 +523,13 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
     if (st != PKV_OK) return st;
     if (!dtype_ok(dtype) || causal != 1) return PKV_ERR_UNSUPPORTED;
     if (window_left < -1) return PKV_ERR_SHAPE;
+    if (rope_cos_sin) {
+        // q rotated in registers: rotary_dim a multiple of 32 within the head,
+        // and a table row for every query position (< max_seqlen_k)
+        if (rotary_dim < 32 || rotary_dim > head_dim || rotary_dim % 32)
+            return PKV_ERR_UNSUPPORTED;
+        if (rope_positions < max_seqlen_k) return PKV_ERR_SHAPE;
+    }
     const bool contiguous = k != nullptr || v != nullptr;
     const bool paged = k_cache != nullptr || v_cache != nullptr || block_table != nullptr;
     if (contiguous && paged) return PKV_ERR_SHAPE;
@@ -479,6 +557,7 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
         PrefillArgs a{};
         a.out = out; a.lse = lse; a.q = q; a.k = k; a.v = v; a.k_cache = k_cache;
         a.v_cache = v_cache; a.block_table = block_table; a.cu_q = cu_seqlens_q;
+        a.rope = rope_cos_sin; a.rope_dim = rotary_dim; a.rope_neox = rope_neox;
         a.cu_k = cu_seqlens_k; a.sink = sink; a.alibi = alibi_slopes; a.B = B;
         a.Hq = num_q_heads; a.Hkv = num_kv_heads;
         a.G = num_q_heads / num_kv_heads; a.D = head_dim; a.bs_log2 = bs_log2;
@@ -492,6 +571,7 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
     RowArgs a{};
     a.mode = 1; a.out = out; a.lse = lse; a.q = q; a.k = k; a.v = v; a.k_cache = k_cache;
     a.v_cache = v_cache; a.block_table = block_table; a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+    a.rope = rope_cos_sin; a.rope_dim = rotary_dim; a.rope_neox = rope_neox;
     a.sink = sink; a.alibi = alibi_slopes; a.B = B; a.Hq = num_q_heads; a.Hkv = num_kv_heads;
     a.G = num_q_heads / num_kv_heads; a.D = head_dim; a.bs_log2 = bs_log2;
     a.mbps = max_blocks_per_seq; a.window_left = window_left; a.scale_log2 = sm_scale * kLog2e;

@@ -151,6 +151,8 @@ struct RowArgs {
     const int32_t *cu_k;
     const float *sink;
     const float *alibi;          // [Hq] ALiBi slopes or null
+    const float *rope;           // prefill: q rotary table or null (as PrefillArgs)
+    int32_t rope_dim, rope_neox;
     int32_t B, T, Hq, Hkv, G, D;   // prefill: T = max_seqlen_q
     int32_t bs_log2, mbps, window_left;
     int32_t part_size, nparts, split;
@@ -170,6 +172,10 @@ struct PrefillArgs {
     const int32_t *cu_k;
     const float *sink;
     const float *alibi;          // [Hq] ALiBi slopes or null
+    // rotary embedding of q by its position (table [positions, rope_dim]:
+    // cos then sin) or null
+    const float *rope;
+    int32_t rope_dim, rope_neox;
     int32_t B, Hq, Hkv, G, D;
     int32_t bs_log2, mbps, window_left;
     int32_t hpw;                 // query heads per workgroup: prefill_heads_per_wg(G)
@@ -185,6 +191,16 @@ pkv_status launch_rows(const RowArgs &a, bool bf16, hipStream_t stream);
 pkv_status launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream);
 int prefill_heads_per_wg(int G);
 int prefill_block_m();
+pkv_status launch_rope_table(float *cos_sin, int n_pos, int rd, double base, int scaling,
+                             double factor, int max_position, hipStream_t stream);
+pkv_status launch_rope_apply(void *x, const int32_t *positions, const float *cos_sin, int T,
+                             int H, int D, long long row_stride, int rd, int neox, bool bf16,
+                             hipStream_t stream);
+pkv_status launch_rope_cache(const void *key, const void *value, void *k_cache, void *v_cache,
+                             const int32_t *slot_mapping, const int32_t *positions,
+                             const float *cos_sin, int T, long long key_stride,
+                             long long value_stride, int Hkv, int D, int rd, int neox, bool bf16,
+                             hipStream_t stream);
 pkv_status launch_reshape_and_cache(const void *key, const void *value, void *k_cache,
                                     void *v_cache, const int32_t *slot_mapping, int32_t T,
                                     int64_t key_stride, int64_t value_stride, int32_t Hkv,

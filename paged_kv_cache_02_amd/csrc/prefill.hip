@@ -122,6 +122,49 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const void *base, uint32_t bytes) {
     return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kBufferWord3};
 }
 
+// Rotary embedding of a lane's Q registers (lane half lh holds dims
+// 16c + 8lh .. +8 of register c).  tab: the row's table, cos then sin.
+// neox, rope_dim = 32 OFF: register c < OFF pairs with register c + OFF.
+template <int OFF, int QK>
+__device__ __forceinline__ void rope_neox(bf16x8 (&qf)[QK], const float *tab, int lh) {
+    static_assert(2 * OFF <= QK, "rotary dims within the head");
+    constexpr int half = 16 * OFF;
+#pragma unroll
+    for (int c = 0; c < OFF; ++c) {
+        const int d0 = 16 * c + 8 * lh;
+        bf16x8 x = qf[c], y = qf[c + OFF];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float co = tab[d0 + e], si = tab[half + d0 + e];
+            const float x0 = (float)qf[c][e], x1 = (float)qf[c + OFF][e];
+            x[e] = (__bf16)(x0 * co - x1 * si);
+            y[e] = (__bf16)(x1 * co + x0 * si);
+        }
+        qf[c] = x;
+        qf[c + OFF] = y;
+    }
+}
+// interleaved pairs (2i, 2i + 1) sit next to each other in a register
+template <int QK>
+__device__ __forceinline__ void rope_pairs(bf16x8 (&qf)[QK], const float *tab, int lh, int rd) {
+    const int half = rd / 2;
+#pragma unroll
+    for (int c = 0; c < QK; ++c) {
+        const int d0 = 16 * c + 8 * lh;
+        if (d0 >= rd) continue;
+        bf16x8 x = qf[c];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const int i = (d0 + e) / 2;
+            const float co = tab[i], si = tab[half + i];
+            const float x0 = (float)qf[c][e], x1 = (float)qf[c][e + 1];
+            x[e] = (__bf16)(x0 * co - x1 * si);
+            x[e + 1] = (__bf16)(x1 * co + x0 * si);
+        }
+        qf[c] = x;
+    }
+}
+
 template <int D, bool PAGED, bool ALIBI>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
 {
@@ -201,6 +244,28 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
             u32x4 x = u32x4{0u, 0u, 0u, 0u};
             if (ok) x = *reinterpret_cast<const u32x4 *>(qp + 16 * c);
             qf[c] = __builtin_bit_cast(bf16x8, x);
+        }
+        if (a.rope) {
+            // rotary embedding of the row at its position (rope_dim a multiple
+            // of 32): the neox partner of dims 16c + 8lh + e is register
+            // c + rope_dim / 32 of this lane; interleaved pairs are adjacent.
+            // Register indices stay compile-time constants (a runtime index
+            // would move qf to scratch memory).  Rows past the request (zero
+            // q) and rows at a negative position (Lq > Lk: no visible key)
+            // read table row 0, so every read stays inside the table.
+            const int tpos = wpos0 + lr;
+            const float *tab = a.rope + (size_t)(ok && tpos >= 0 ? tpos : 0) * a.rope_dim;
+            if (a.rope_neox) {
+                switch (a.rope_dim / 32) {
+                    case 1: rope_neox<1>(qf, tab, lh); break;
+                    case 2: rope_neox<2>(qf, tab, lh); break;
+                    case 3: if constexpr (QK_STEPS >= 6) rope_neox<3>(qf, tab, lh); break;
+                    case 4: if constexpr (QK_STEPS >= 8) rope_neox<4>(qf, tab, lh); break;
+                    default: break;
+                }
+            } else {
+                rope_pairs(qf, tab, lh, a.rope_dim);
+            }
         }
     }
 

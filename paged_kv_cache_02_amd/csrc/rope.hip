@@ -1,0 +1,216 @@
+// Rotary position embedding: the cos/sin table, in-place rotation of rows,
+// and reshape_and_cache with the key rotated as it is stored.
+//
+// vLLM "attention.py" page, PagedAttentionWithRoPE: query and key are rotated
+// by their positions before attention, with rotary_dim, base, is_neox_style
+// and an optional linear or dynamic rope_scaling; the rotation is the
+// standard rotary embedding (the page names it, it does not print it):
+// frequency i < rotary_dim / 2 turns by base^(-2i / rotary_dim) per
+// position; the neox pairing rotates dimension d with d + rotary_dim / 2,
+// the other pairing 2i with 2i + 1; dimensions from rotary_dim on pass
+// through.  Linear scaling divides positions by the factor; dynamic scaling
+// raises the base when the table is longer than max_position.
+//
+// The table [positions, rotary_dim] holds cos of the angles, then sin, in
+// float32 (computed in double).  Rows are rotated in float32 and rounded to
+// the storage type.  HBM-bound: one read and one write of each rotated row.
+
+#include <algorithm>
+
+#include "common.h"
+#include "decode.h"
+
+namespace pkv {
+
+namespace {
+
+__global__ __launch_bounds__(256) void rope_table_kernel(float *cos_sin, int n_pos, int rd,
+                                                         double base, int linear, double factor)
+{
+    const int half = rd / 2;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)n_pos * half) return;
+    const int pos = (int)(idx / half), i = (int)(idx % half);
+    const double inv_freq = pow(base, -2.0 * i / rd);
+    const double t = linear ? pos / factor : (double)pos;
+    double s, c;
+    sincos(t * inv_freq, &s, &c);
+    cos_sin[(size_t)pos * rd + i] = (float)c;
+    cos_sin[(size_t)pos * rd + half + i] = (float)s;
+}
+
+// 16-byte chunk of a row as floats (8 bf16 or 4 float32), and back.
+template <bool BF16> struct Chunk {
+    static constexpr int N = BF16 ? 8 : 4;
+    float x[N];
+    __device__ void load(const char *p) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            if (BF16) {
+                x[2 * w] = bf16_lo(v[w]);
+                x[2 * w + 1] = bf16_hi(v[w]);
+            } else {
+                x[w] = __uint_as_float(v[w]);
+            }
+        }
+    }
+    __device__ void store(char *p) const {
+        u32x4 v;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            v[w] = BF16 ? pack_bf16x2(x[2 * w], x[2 * w + 1]) : __float_as_uint(x[w]);
+        *reinterpret_cast<u32x4 *>(p) = v;
+    }
+};
+
+// Rotate (and move) one head row of D elements whose chunk u this thread
+// owns.  src/dst point at the row; tab at the position's table row.
+//   neox: chunk u < rd/2 / N rotates with chunk u + rd/2 / N (both written
+//         here); chunks of the second half are written by their partner;
+//   interleaved: chunk u < rd / N rotates its own pairs;
+//   chunks from rd / N on are copied when src != dst.
+template <bool BF16>
+__device__ __forceinline__ void rope_chunk(const char *src, char *dst, const float *tab, int rd,
+                                           bool neox, int u)
+{
+    using C = Chunk<BF16>;
+    constexpr int N = C::N;
+    const int half = rd / 2;
+    if (u * N >= rd) {
+        if (src != dst) *reinterpret_cast<u32x4 *>(dst + 16 * u) =
+            *reinterpret_cast<const u32x4 *>(src + 16 * u);
+        return;
+    }
+    if (neox) {
+        if (u * N >= half) return;                 // written with its partner
+        const int v = u + half / N;
+        C a, b;
+        a.load(src + 16 * u);
+        b.load(src + 16 * v);
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+            const float c = tab[u * N + e], s = tab[half + u * N + e];
+            const float x0 = a.x[e], x1 = b.x[e];
+            a.x[e] = x0 * c - x1 * s;
+            b.x[e] = x1 * c + x0 * s;
+        }
+        a.store(dst + 16 * u);
+        b.store(dst + 16 * v);
+    } else {
+        C a;
+        a.load(src + 16 * u);
+#pragma unroll
+        for (int e = 0; e < N; e += 2) {
+            const int i = (u * N + e) / 2;
+            const float c = tab[i], s = tab[half + i];
+            const float x0 = a.x[e], x1 = a.x[e + 1];
+            a.x[e] = x0 * c - x1 * s;
+            a.x[e + 1] = x1 * c + x0 * s;
+        }
+        a.store(dst + 16 * u);
+    }
+}
+
+// In place: x [T, H, D] with rows row_stride elements apart; one thread per
+// 16-byte chunk of one (token, head) row.
+template <bool BF16>
+__global__ __launch_bounds__(256) void rope_apply_kernel(char *x, const int32_t *positions,
+                                                         const float *cos_sin, int T, int H,
+                                                         int D, long long row_stride_bytes,
+                                                         int rd, int neox)
+{
+    constexpr int N = Chunk<BF16>::N;
+    const int cpr = D / N;                         // chunks per head row
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)T * H * cpr) return;
+    const int u = (int)(idx % cpr);
+    const long long th = idx / cpr;
+    const int h = (int)(th % H), t = (int)(th / H);
+    char *row = x + t * row_stride_bytes + (size_t)h * D * (BF16 ? 2 : 4);
+    rope_chunk<BF16>(row, row, cos_sin + (size_t)positions[t] * rd, rd, neox != 0, u);
+}
+
+// reshape_and_cache with the key rotated: one thread per 16-byte chunk of a
+// token's K row (all kv heads) and of its V row.
+template <bool BF16>
+__global__ __launch_bounds__(256) void rope_cache_kernel(
+    const char *key, const char *value, char *k_cache, char *v_cache,
+    const int32_t *slot_mapping, const int32_t *positions, const float *cos_sin, int T,
+    long long key_stride_bytes, long long value_stride_bytes, int Hkv, int D, int rd, int neox)
+{
+    constexpr int N = Chunk<BF16>::N;
+    const int cpr = D / N;
+    const int row_chunks = Hkv * cpr;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)T * row_chunks) return;
+    const int t = (int)(idx / row_chunks), c = (int)(idx % row_chunks);
+    const int s = slot_mapping[t];
+    if (s < 0) return;                             // padding token
+    const size_t row_bytes = (size_t)Hkv * D * (BF16 ? 2 : 4);
+    const size_t head_bytes = (size_t)D * (BF16 ? 2 : 4);
+    const int g = c / cpr, u = c % cpr;
+    const char *kr = key + t * key_stride_bytes + g * head_bytes;
+    char *kc = k_cache + (size_t)s * row_bytes + g * head_bytes;
+    rope_chunk<BF16>(kr, kc, cos_sin + (size_t)positions[t] * rd, rd, neox != 0, u);
+    *reinterpret_cast<u32x4 *>(v_cache + (size_t)s * row_bytes + 16 * (size_t)c) =
+        *reinterpret_cast<const u32x4 *>(value + t * value_stride_bytes + 16 * (size_t)c);
+}
+
+}  // namespace
+
+pkv_status launch_rope_table(float *cos_sin, int n_pos, int rd, double base, int scaling,
+                             double factor, int max_position, hipStream_t stream)
+{
+    double b = base;
+    if (scaling == 2 && n_pos > max_position)      // dynamic (NTK-aware) base
+        b = base * std::pow(factor * n_pos / max_position - (factor - 1.0),
+                            (double)rd / (rd - 2));
+    const long long n = (long long)n_pos * (rd / 2);
+    if (n == 0) return PKV_OK;
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       cos_sin, n_pos, rd, b, scaling == 1 ? 1 : 0, factor);
+    return launch_status();
+}
+
+pkv_status launch_rope_apply(void *x, const int32_t *positions, const float *cos_sin, int T,
+                             int H, int D, long long row_stride, int rd, int neox, bool bf16,
+                             hipStream_t stream)
+{
+    const long long n = (long long)T * H * (D / (bf16 ? 8 : 4));
+    if (n == 0) return PKV_OK;
+    const unsigned grid = (unsigned)((n + 255) / 256);
+    const long long stride_bytes = row_stride * (bf16 ? 2 : 4);
+    if (bf16)
+        hipLaunchKernelGGL(rope_apply_kernel<true>, dim3(grid), dim3(256), 0, stream, (char *)x,
+                           positions, cos_sin, T, H, D, stride_bytes, rd, neox);
+    else
+        hipLaunchKernelGGL(rope_apply_kernel<false>, dim3(grid), dim3(256), 0, stream, (char *)x,
+                           positions, cos_sin, T, H, D, stride_bytes, rd, neox);
+    return launch_status();
+}
+
+pkv_status launch_rope_cache(const void *key, const void *value, void *k_cache, void *v_cache,
+                             const int32_t *slot_mapping, const int32_t *positions,
+                             const float *cos_sin, int T, long long key_stride,
+                             long long value_stride, int Hkv, int D, int rd, int neox, bool bf16,
+                             hipStream_t stream)
+{
+    const long long n = (long long)T * Hkv * (D / (bf16 ? 8 : 4));
+    if (n == 0) return PKV_OK;
+    const unsigned grid = (unsigned)((n + 255) / 256);
+    const int eb = bf16 ? 2 : 4;
+    if (bf16)
+        hipLaunchKernelGGL(rope_cache_kernel<true>, dim3(grid), dim3(256), 0, stream,
+                           (const char *)key, (const char *)value, (char *)k_cache,
+                           (char *)v_cache, slot_mapping, positions, cos_sin, T, key_stride * eb,
+                           value_stride * eb, Hkv, D, rd, neox);
+    else
+        hipLaunchKernelGGL(rope_cache_kernel<false>, dim3(grid), dim3(256), 0, stream,
+                           (const char *)key, (const char *)value, (char *)k_cache,
+                           (char *)v_cache, slot_mapping, positions, cos_sin, T, key_stride * eb,
+                           value_stride * eb, Hkv, D, rd, neox);
+    return launch_status();
+}
+
+}  // namespace pkv

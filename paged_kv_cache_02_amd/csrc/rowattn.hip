@@ -62,9 +62,29 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
     float qv[E], acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        qv[e] = ld_elem<BF16>(a.q, qrow * D + lane + 64 * e) * a.scale_log2;
+        qv[e] = ld_elem<BF16>(a.q, qrow * D + lane + 64 * e);
         acc[e] = 0.f;
     }
+    if (a.mode == 1 && a.rope && pos >= 0) {
+        // rotary embedding of q at its position: the partner element is read
+        // from memory (neox: d +- rope_dim / 2; interleaved: d ^ 1).  A row
+        // at a negative position (Lq > Lk) sees no key and is not rotated.
+        const int rd = a.rope_dim, half = rd / 2;
+        const float *tab = a.rope + (size_t)pos * rd;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int d = lane + 64 * e;
+            if (d >= rd) continue;
+            const bool hi = a.rope_neox ? d >= half : (d & 1);
+            const int pd = a.rope_neox ? (hi ? d - half : d + half) : (d ^ 1);
+            const int i = a.rope_neox ? (hi ? d - half : d) : d / 2;
+            const float xp = ld_elem<BF16>(a.q, qrow * D + pd);
+            const float co = tab[i], si = tab[half + i];
+            qv[e] = hi ? fmaf(qv[e], co, xp * si) : fmaf(qv[e], co, -xp * si);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) qv[e] *= a.scale_log2;
     float m = kNoMax, l = 0.f;
     // ALiBi: slope * (key position - query position), in log2 units like qv
     const float slope_log2 = a.alibi ? a.alibi[h] * kLog2e : 0.f;

@@ -28,6 +28,12 @@ SIGNATURES = {
     "pkv_version": (ctypes.c_int, []),
     "pkv_reshape_and_cache": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I32, _I32,
                                              _I32, _I32, ctypes.c_int, _P]),
+    "pkv_rope_cos_sin": (ctypes.c_int, [_P, _I32, _I32, _F, _I32, _F, _I32, _P]),
+    "pkv_rope_apply": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32,
+                                      ctypes.c_int, _P]),
+    "pkv_reshape_and_cache_rope": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I64,
+                                                  _I32, _I32, _I32, _I32, _I32, _I32,
+                                                  ctypes.c_int, _P]),
     "pkv_paged_decode_workspace_bytes": (ctypes.c_size_t, [_I32] * 7 + [ctypes.c_int]),
     "pkv_paged_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                         _I32, _I32, _I32, _I32, _F, _I32, _P, _I32, _P, _SZ,
@@ -47,7 +53,7 @@ SIGNATURES = {
                                             _I32, ctypes.c_int, _P]),
     "pkv_varlen_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P,
                                           _P, _I32, _I32, _I32, _I32, _I32, _I32, _F, _I32,
-                                          _I32, _P, _P, ctypes.c_int, _P]),
+                                          _I32, _P, _P, _I32, _I32, _I32, _P, ctypes.c_int, _P]),
 }
 
 
@@ -76,7 +82,12 @@ def _check(status: int, what: str):
         raise PkvError(status, what)
 
 
-def _dt(t: torch.Tensor) -> int:
+def _dt(t: torch.Tensor, *same: Optional[torch.Tensor]) -> int:
+    """The library's dtype code for t; every tensor in same (None skipped)
+    must have t's dtype, since the kernels read them all as that type."""
+    for u in same:
+        if u is not None and u.dtype != t.dtype:
+            raise ValueError(f"dtype mismatch: {u.dtype} where {t.dtype} is expected")
     if t.dtype == torch.bfloat16:
         return PKV_BF16
     if t.dtype == torch.float32:
@@ -106,6 +117,16 @@ def _f32(t: Optional[torch.Tensor], name: str) -> Optional[torch.Tensor]:
     return t
 
 
+def _row_stride(t: torch.Tensor, name: str) -> int:
+    """Elements between tokens of t [T, H, D], whose per-token [H, D] blocks
+    must be contiguous (the tokens themselves may be strided)."""
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if t.dim() != 3 or (t.shape[0] > 0 and not t[0].is_contiguous()):
+        raise ValueError(f"{name}: each token's [heads, head_dim] block must be contiguous")
+    return t.stride(0)
+
+
 def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
@@ -118,16 +139,46 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping):
     """Store rows key/value [T, Hkv, D] into the caches at slot_mapping [T]."""
     T, Hkv, D = key.shape
     NB, bs = k_cache.shape[0], k_cache.shape[1]
-    if not (key.is_cuda and value.is_cuda):
-        raise ValueError("tensors must be on the GPU")
-    ks = key.stride(0) if key.dim() == 3 and key[0].is_contiguous() else None
-    vs = value.stride(0) if value.dim() == 3 and value[0].is_contiguous() else None
-    if ks is None or vs is None:
-        raise ValueError("key/value rows must be contiguous [Hkv, D] blocks")
+    ks, vs = _row_stride(key, "key"), _row_stride(value, "value")
     _check(lib.pkv_reshape_and_cache(
         key.data_ptr(), value.data_ptr(), _ptr(k_cache), _ptr(v_cache),
-        _ptr(_i32(slot_mapping, "slot_mapping")), T, ks, vs, Hkv, D, bs, NB, _dt(key), _stream()),
-        "reshape_and_cache")
+        _ptr(_i32(slot_mapping, "slot_mapping")), T, ks, vs, Hkv, D, bs, NB,
+        _dt(key, value, k_cache, v_cache), _stream()), "reshape_and_cache")
+
+
+def rope_cos_sin(num_positions: int, rotary_dim: int, base: float = 10000.0, scaling: int = 0,
+                 factor: float = 1.0, max_position: int = 0, device="cuda"):
+    """Rotary table [num_positions, rotary_dim] float32 (cos, then sin) built on the GPU;
+    scaling 0 none, 1 linear, 2 dynamic (see pkv_rope_cos_sin)."""
+    t = torch.empty((num_positions, rotary_dim), dtype=torch.float32, device=device)
+    _check(lib.pkv_rope_cos_sin(_ptr(t), num_positions, rotary_dim, float(base), scaling,
+                                float(factor), max_position, _stream()), "rope_cos_sin")
+    return t
+
+
+def rope_apply(x, positions, cos_sin, rotary_dim: int, neox: bool = True):
+    """Rotate x [T, H, D] (rows may be strided, e.g. q or k of a fused QKV
+    buffer) in place by positions [T]."""
+    T, H, D = x.shape
+    xs = _row_stride(x, "x")
+    _check(lib.pkv_rope_apply(x.data_ptr(), _ptr(_i32(positions, "positions")),
+                              _ptr(_f32(cos_sin, "cos_sin")), T, H, D, xs, rotary_dim,
+                              int(bool(neox)), _dt(x), _stream()), "rope_apply")
+    return x
+
+
+def reshape_and_cache_rope(key, value, k_cache, v_cache, slot_mapping, positions, cos_sin,
+                           rotary_dim: int, neox: bool = True):
+    """reshape_and_cache with each key row rotated by positions [T] as it is stored."""
+    T, Hkv, D = key.shape
+    NB, bs = k_cache.shape[0], k_cache.shape[1]
+    ks, vs = _row_stride(key, "key"), _row_stride(value, "value")
+    _check(lib.pkv_reshape_and_cache_rope(
+        key.data_ptr(), value.data_ptr(), _ptr(k_cache), _ptr(v_cache),
+        _ptr(_i32(slot_mapping, "slot_mapping")), _ptr(_i32(positions, "positions")),
+        _ptr(_f32(cos_sin, "cos_sin")), T, ks, vs, Hkv, D, bs, NB,
+        rotary_dim, int(bool(neox)), _dt(key, value, k_cache, v_cache), _stream()),
+        "reshape_and_cache_rope")
 
 
 def decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_dim, block_size, max_seqlen_k,
@@ -164,7 +215,8 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: floa
         _ptr(_f32(sink, "sink")), B, Hq, Hkv, D, bs, NB, block_table.shape[1], max_seqlen_k,
         float(sm_scale), window_left, _ptr(_f32(alibi_slopes, "alibi_slopes")), partition_size,
         _ptr(workspace),
-        0 if workspace is None else workspace.numel() * workspace.element_size(), _dt(q),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _dt(q, k_cache, v_cache, out),
         _stream()), "paged_decode")
     return out
 
@@ -194,7 +246,8 @@ def paged_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_se
         _ptr(_i32(cache_seqlens, "cache_seqlens")), _ptr(_f32(sink, "sink")), B, Hq, Hkv, D, bs,
         NB, block_table.shape[1], max_seqlen_k, float(sm_scale), window_left,
         _ptr(_f32(alibi_slopes, "alibi_slopes")), _ptr(workspace),
-        0 if workspace is None else workspace.numel() * workspace.element_size(), _dt(q),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _dt(q, k_new, v_new, k_cache, v_cache, out),
         _stream()), "paged_decode_append")
     return out
 
@@ -209,7 +262,8 @@ def paged_decode_stage(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale
         _ptr(_i32(cache_seqlens, "cache_seqlens")), B, Hq, Hkv, D, bs, NB, block_table.shape[1],
         max_seqlen_k, float(sm_scale), window_left, _ptr(_f32(alibi_slopes, "alibi_slopes")),
         _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _dt(q), _stream()), "paged_decode_stage")
+        workspace.numel() * workspace.element_size(), _dt(q, k_cache, v_cache), _stream()),
+        "paged_decode_stage")
 
 
 def paged_decode_finish(out, workspace, num_kv_heads: int, sink=None, lse=None):
@@ -238,7 +292,7 @@ def paged_decode_partitions(q, k_cache, v_cache, block_table, cache_seqlens, sm_
         _ptr(k_cache), _ptr(v_cache), _ptr(_i32(block_table, "block_table")),
         _ptr(_i32(cache_seqlens, "cache_seqlens")), B, Hq, Hkv, D, bs, NB, block_table.shape[1],
         max_seqlen_k, float(sm_scale), window_left, _ptr(_f32(alibi_slopes, "alibi_slopes")),
-        partition_size, part_out.shape[2], _dt(q),
+        partition_size, part_out.shape[2], _dt(q, k_cache, v_cache),
         _stream()), "paged_decode_partitions")
     return part_out, part_lse
 
@@ -260,7 +314,8 @@ def merge_partitions(part_out, part_lse, cache_seqlens, partition_size: int, sin
 def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                    sm_scale: float, num_kv_heads: Optional[int] = None, k=None, v=None,
                    k_cache=None, v_cache=None, block_table=None, sink=None,
-                   window_left: int = -1, out=None, lse=None, alibi_slopes=None):
+                   window_left: int = -1, out=None, lse=None, alibi_slopes=None,
+                   rope_cos_sin=None, rotary_dim: int = 0, rope_neox: bool = True):
     """Causal varlen prefill: out [sum Lq, Hq, D]."""
     T, Hq, D = q.shape
     B = cu_seqlens_q.shape[0] - 1
@@ -280,6 +335,8 @@ def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_
         bs, NB, MB, _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")),
         _ptr(_i32(cu_seqlens_k, "cu_seqlens_k")), B, int(max_seqlen_q), int(max_seqlen_k), Hq,
         Hkv, D, float(sm_scale), 1, window_left, _ptr(_f32(alibi_slopes, "alibi_slopes")),
-        _ptr(_f32(sink, "sink")), _dt(q), _stream()),
+        _ptr(_f32(rope_cos_sin, "rope_cos_sin")),
+        0 if rope_cos_sin is None else rope_cos_sin.shape[0], rotary_dim, int(bool(rope_neox)),
+        _ptr(_f32(sink, "sink")), _dt(q, k, v, k_cache, v_cache, out), _stream()),
         "varlen_prefill")
     return out

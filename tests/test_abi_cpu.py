@@ -126,7 +126,8 @@ def test_decode_append_validation(over, status):
 def prefill_call(**over):
     a = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, k_cache=None, v_cache=None, bt=None,
              bs=0, NB=0, MB=0, cu_q=FAKE, cu_k=FAKE, B=2, maxq=16, maxk=16, Hq=8, Hkv=2, D=64,
-             scale=0.1, causal=1, window=-1, alibi=None, sink=None, dt=1, stream=None)
+             scale=0.1, causal=1, window=-1, alibi=None, rope=None, rope_pos=0, rope_dim=0,
+             rope_neox=1, sink=None, dt=1, stream=None)
     a.update(over)
     return lib.pkv_varlen_prefill(*a.values())
 
@@ -177,3 +178,42 @@ def test_reshape_validation(args, status):
 ])
 def test_merge_validation(args, status):
     assert lib.pkv_merge_partitions(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(), pkv.PKV_OK),                                       # nothing launched for T = 0
+    (dict(T=4, x=None), pkv.PKV_ERR_NULL),
+    (dict(T=4, rd=24), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(T=4, rd=256), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(T=4, D=96), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(T=4, stride=100), pkv.PKV_ERR_SHAPE),
+    (dict(T=4, stride=1028), pkv.PKV_ERR_UNSUPPORTED),
+])
+def test_rope_apply_validation(args, status):
+    a = dict(x=FAKE, pos=FAKE, tab=FAKE, T=0, H=8, D=128, stride=0, rd=64, neox=1, dt=1,
+             stream=None)
+    a.update(args)
+    assert lib.pkv_rope_apply(*a.values()) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(n=16, rd=7), pkv.PKV_ERR_SHAPE),
+    (dict(n=16, base=0.0), pkv.PKV_ERR_SHAPE),
+    (dict(n=16, scaling=3), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(n=16, scaling=2, maxp=0), pkv.PKV_ERR_SHAPE),
+    (dict(n=16, out=None), pkv.PKV_ERR_NULL),
+    (dict(n=0), pkv.PKV_OK),
+])
+def test_rope_table_validation(args, status):
+    a = dict(out=FAKE, n=0, rd=64, base=10000.0, scaling=0, factor=1.0, maxp=0, stream=None)
+    a.update(args)
+    assert lib.pkv_rope_cos_sin(*a.values()) == status
+
+
+def test_rope_cache_validation():
+    a = dict(key=FAKE, value=FAKE, kc=FAKE, vc=FAKE, slots=FAKE, pos=FAKE, tab=FAKE, T=3, ks=0,
+             vs=0, Hkv=2, D=128, bs=16, NB=4, rd=64, neox=1, dt=1, stream=None)
+    assert lib.pkv_reshape_and_cache_rope(*dict(a, pos=None).values()) == pkv.PKV_ERR_NULL
+    assert lib.pkv_reshape_and_cache_rope(*dict(a, rd=8).values()) == pkv.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_reshape_and_cache_rope(*dict(a, bs=24).values()) == pkv.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_reshape_and_cache_rope(*dict(a, T=0).values()) == pkv.PKV_OK
