@@ -245,29 +245,31 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
             if (ok) x = *reinterpret_cast<const u32x4 *>(qp + 16 * c);
             qf[c] = __builtin_bit_cast(bf16x8, x);
         }
-        if (a.rope) {
-            // rotary embedding of the row at its position (rope_dim a multiple
-            // of 32): the neox partner of dims 16c + 8lh + e is register
-            // c + rope_dim / 32 of this lane; interleaved pairs are adjacent.
-            // Register indices stay compile-time constants (a runtime index
-            // would move qf to scratch memory).  Rows past the request (zero
-            // q) and rows at a negative position (Lq > Lk: no visible key)
-            // read table row 0, so every read stays inside the table.
-            const int tpos = wpos0 + lr;
-            const float *tab = a.rope + (size_t)(ok && tpos >= 0 ? tpos : 0) * a.rope_dim;
-            if (a.rope_neox) {
-                switch (a.rope_dim / 32) {
-                    case 1: rope_neox<1>(qf, tab, lh); break;
-                    case 2: rope_neox<2>(qf, tab, lh); break;
-                    case 3: if constexpr (QK_STEPS >= 6) rope_neox<3>(qf, tab, lh); break;
-                    case 4: if constexpr (QK_STEPS >= 8) rope_neox<4>(qf, tab, lh); break;
-                    default: break;
-                }
-            } else {
-                rope_pairs(qf, tab, lh, a.rope_dim);
-            }
-        }
     }
+
+    // Rotary embedding of the Q rows at their positions (rope_dim a multiple
+    // of 32): the neox partner of dims 16c + 8lh + e is register
+    // c + rope_dim / 32 of this lane; interleaved pairs are adjacent.
+    // Register indices stay compile-time constants (a runtime index would
+    // move qf to scratch memory).  Rows past the request (zero q) and rows at
+    // a negative position (Lq > Lk: no visible key) read table row 0, so
+    // every read stays inside the table.  Called once the first K/V tile is
+    // in flight, so the table loads overlap that tile's.
+    auto rotate_q = [&]() {
+        const int tpos = wpos0 + lr;
+        const float *tab = a.rope + (size_t)(lr < wrows && tpos >= 0 ? tpos : 0) * a.rope_dim;
+        if (a.rope_neox) {
+            switch (a.rope_dim / 32) {
+                case 1: rope_neox<1>(qf, tab, lh); break;
+                case 2: rope_neox<2>(qf, tab, lh); break;
+                case 3: if constexpr (QK_STEPS >= 6) rope_neox<3>(qf, tab, lh); break;
+                case 4: if constexpr (QK_STEPS >= 8) rope_neox<4>(qf, tab, lh); break;
+                default: break;
+            }
+        } else {
+            rope_pairs(qf, tab, lh, a.rope_dim);
+        }
+    };
 
     f32x16 o[DT];
 #pragma unroll
@@ -481,6 +483,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
 
     if (ntiles > 0) {
         issue(t_begin, 0);
+        if (a.rope) rotate_q();
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         for (int it = 0; it < ntiles; ++it) {
