@@ -231,7 +231,7 @@ def bench_decode(c, name, steps, warmup, partition_size, reps, traffic_key=None,
     out = torch.empty_like(q)
     msk = c.max_seqlen_k
     P = partition_size
-    ws_bytes = pkv.decode_workspace_bytes(B, Hq, c.Hkv, D, c.block_size, msk, P, q.dtype)
+    ws_bytes = pkv.decode_workspace_bytes(B, Hq, D, msk, P)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     split = P > 0 and P < msk
     nparts = (msk + P - 1) // P if split else 1
@@ -295,7 +295,7 @@ def bench_decode_append(c, name, steps, warmup, reps):
     sink = None if c.sink is None else c.sink.cuda()
     out = torch.empty_like(q)
     msk = c.max_seqlen_k
-    ws = torch.zeros(max(pkv.decode_workspace_bytes(B, Hq, c.Hkv, D, bs, msk, 0, q.dtype), 256),
+    ws = torch.zeros(max(pkv.decode_workspace_bytes(B, Hq, D, msk), 256),
                      dtype=torch.uint8, device="cuda")
     ar = torch.arange(B, device="cuda")
     slots = [(t[ar, (L // bs).long()] * bs + L % bs).to(torch.int32) for t in tables]

@@ -48,7 +48,9 @@
  *
  * Conventions for every entry point:
  *   - Array arguments are DEVICE pointers owned by the caller; the library
- *     allocates nothing, keeps no state between calls and never prints.
+ *     allocates nothing and never prints.  Its only host state is a cached
+ *     compute-unit count per device, a once-per-process kernel attribute and
+ *     a per-process call counter that tags the fused merge's counters.
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the legacy
  *     default stream) and the call returns without waiting; results are
  *     valid in stream order.
@@ -57,7 +59,8 @@
  *   - Output dtype is the input dtype; bf16 results are rounded to nearest
  *     even from float32 accumulators.
  *   - Arguments are checked on the host before anything is launched; a bad
- *     argument returns an error status and launches nothing.  Device-resident
+ *     argument returns an error status and launches nothing.  sm_scale must
+ *     be positive and finite (PKV_ERR_SHAPE otherwise).  Device-resident
  *     index data (block_table entries, cache_seqlens, cu_seqlens, slots) is
  *     NOT checked, since that would need a device-to-host copy: it is a
  *     caller contract (see each function), and violating it is undefined.
@@ -168,23 +171,30 @@ pkv_status pkv_reshape_and_cache_rope(const void *key, const void *value, void *
                                       pkv_dtype dtype, void *stream);
 
 /*
- * Bytes of workspace pkv_paged_decode needs for these sizes, this
- * partition_size and dtype; 0 when the call needs none.  Returns (size_t)-1
- * for invalid sizes.  The result does not depend on the sequence lengths
- * (device data), only on the arguments here and on the current device:
- *   - partition_size > 0 and max_seqlen_k > partition_size: float32 part_out
- *     [B, Hq, P, head_dim] and part_lse [B, Hq, P], P = ceil(max_seqlen_k /
- *     partition_size), each 256-byte aligned;
- *   - partition_size == 0, bf16: 4096 * Hq int32 arrival counters, then
- *     the balanced schedule's partial results, (4 * W + B) * Hq *
- *     (head_dim + 1) floats, plus B + 2 ints (W grows with the device's
- *     compute-unit count), for any B up to 4096;
- *   - otherwise 0.
+ * pkv_paged_decode_workspace_bytes -- bytes of device workspace a decode call
+ * may need, so that the caller can allocate it (vLLM "attention.py" page,
+ * single_query_cached_kv_attention: the caller allocates the split-KV
+ * buffers tmp_output [num_seqs, num_heads, max_num_partitions, head_size],
+ * exp_sums and max_logits before the partitioned kernel runs).  The
+ * arguments are those of that allocation: batch, query heads, head_dim, the
+ * longest sequence and the partition size (0 = automatic).  The result
+ * covers every kv-head count that divides num_q_heads, both dtypes and
+ * every block size, and does not depend on the sequence lengths (device
+ * data).  It is 0 for B == 0 and (size_t)-1 for invalid sizes.  Layout
+ * (private to the library; stated so that reuse is safe):
+ *   - the first kStreamMaxB * num_q_heads * 8 bytes (256-byte aligned) hold
+ *     the balanced schedule's arrival counters; no other mode writes them;
+ *   - partition_size == 0 (bf16, B <= 4096): the balanced schedule's
+ *     partial results after them, (4 * W + B) * Hq * (head_dim + 1) floats
+ *     plus B + 2 ints, W = ceil(compute units / head groups);
+ *   - partition_size > 0 and max_seqlen_k > partition_size: float32
+ *     part_out [B, Hq, P, head_dim] and part_lse [B, Hq, P],
+ *     P = ceil(max_seqlen_k / partition_size), after them.
+ * pkv_paged_decode_append needs pkv_paged_decode_workspace_bytes(B,
+ * num_q_heads, head_dim, max_seqlen_k + 1, 0).
  */
-size_t pkv_paged_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
-                                        int32_t head_dim, int32_t block_size,
-                                        int32_t max_seqlen_k, int32_t partition_size,
-                                        pkv_dtype dtype);
+size_t pkv_paged_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_dim,
+                                        int32_t max_seqlen_k, int32_t partition_size);
 
 /*
  * pkv_paged_decode -- one query token per sequence attending to its
@@ -216,14 +226,16 @@ size_t pkv_paged_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t 
  *                   reproducible for fixed arguments on a given device.
  *   workspace       device buffer of at least
  *                   pkv_paged_decode_workspace_bytes(...) bytes (may be NULL
- *                   when that is 0), 256-byte aligned.  For the balanced
- *                   schedule its leading 4096 * num_q_heads int32 counters
- *                   must be zero when the call starts; every call leaves
- *                   them zero.  Zero-fill a workspace once after allocating
- *                   it (and again after using it for anything else, such as
- *                   the partition modes, which write it from byte 0), then
- *                   reuse it for calls with the same num_q_heads and any B.
- *                   Calls that share a workspace must not overlap in time.
+ *                   when that is 0), 256-byte aligned, reused across calls.
+ *                   The balanced schedule counts the pieces of each
+ *                   (sequence, head group) in 64-bit counters at its start,
+ *                   tagged with a per-call epoch: a counter left by an
+ *                   interrupted call or holding bytes from another use reads
+ *                   as zero, and every completed call leaves its counters
+ *                   zero.  Zero-fill a new workspace once (so that it holds
+ *                   no stale epoch by chance); the fixed-partition modes
+ *                   never write the counters.  Calls that share a workspace
+ *                   must not overlap in time.
  */
 pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_cache,
                             const void *v_cache, const int32_t *block_table,
@@ -258,10 +270,9 @@ pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_
  *   max_seqlen_k    host upper bound on cache_seqlens; max_seqlen_k + 1 <=
  *                   max_blocks_per_seq * block_size
  *   workspace       bf16: at least pkv_paged_decode_workspace_bytes(B,
- *                   num_q_heads, num_kv_heads, head_dim, block_size,
- *                   max_seqlen_k + 1, 0, PKV_BF16) bytes, zeroed and reused
- *                   under the same rules as pkv_paged_decode's balanced
- *                   schedule (B <= 4096); fp32: none (may be NULL).
+ *                   num_q_heads, head_dim, max_seqlen_k + 1, 0) bytes,
+ *                   reused under the same rules as pkv_paged_decode's
+ *                   balanced schedule (B <= 4096); fp32: none (may be NULL).
  * Other arguments as for pkv_paged_decode.  bf16 runs the balanced schedule
  * with the merge fused (the wave that reads a sequence's last tile stores its
  * new row first); fp32 runs one wave per (sequence, head).  Returns
@@ -288,7 +299,7 @@ pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const v
  *                            into out / lse (same formula as
  *                            pkv_merge_partitions).
  * Arguments mean what they mean for pkv_paged_decode; `workspace` must hold
- * pkv_paged_decode_workspace_bytes(..., partition_size = 0, PKV_BF16) bytes,
+ * pkv_paged_decode_workspace_bytes(B, num_q_heads, head_dim, max_seqlen_k, 0) bytes,
  * and finish must run after stage (stream order) with the same B,
  * num_q_heads, num_kv_heads, head_dim and workspace.  The workspace layout is
  * private to the library.  dtype must be PKV_BF16 and B <= 4096.

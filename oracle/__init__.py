@@ -12,7 +12,14 @@ arrays.  See ``oracle.c`` for the definition it follows and the passages it
 cites.
 
 Parity pins (what holds this oracle to something other than itself) live in
-``tests/test_oracle_pins.py``; no function here is "parity unpinned".
+``tests/oracle_pins.py`` (run by ``tests/test_oracle_pins.py``), and
+``tests/test_oracle_mutations.py`` shows that each plausible mistake in this
+package fails one of them.
+
+Parity unpinned: the dynamic (NTK-aware) branch of ``rope_cos_sin``.  The
+vLLM page names a "dynamic" rope_scaling type but prints no formula; the
+base-raising rule used here is the common reading, and its only check
+restates that rule.  Every other function here is pinned.
 """
 
 from __future__ import annotations
@@ -110,7 +117,13 @@ def _ptr(a) -> Optional[int]:
 
 
 def _threads(n: Optional[int]) -> int:
-    return n if n else (os.cpu_count() or 1)
+    """Worker threads: n, else OMP_NUM_THREADS, else the host's cores (at most 16)."""
+    if n:
+        return n
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    return max(1, min(16, os.cpu_count() or 1))
 
 
 def token_request(cu: Sequence[int], T: Optional[int] = None) -> np.ndarray:
@@ -268,7 +281,8 @@ ROPE_NONE, ROPE_LINEAR, ROPE_DYNAMIC = 0, 1, 2
 
 def rope_cos_sin(num_positions: int, rotary_dim: int, base: float, scaling: int = ROPE_NONE,
                  factor: float = 1.0, max_position: int = 0) -> np.ndarray:
-    """Table [num_positions, rotary_dim]: cos of the angles, then sin."""
+    """Table [num_positions, rotary_dim]: cos of the angles, then sin.
+    The dynamic branch is parity unpinned (see the module docstring)."""
     half = rotary_dim // 2
     b = float(base)
     if scaling == ROPE_DYNAMIC and num_positions > max_position:
@@ -310,7 +324,9 @@ def rope_apply(x, positions, cos_sin, rotary_dim: int, neox: bool) -> np.ndarray
 
 
 def query_positions(cu_seqlens_q, cu_seqlens_k) -> np.ndarray:
-    """Position of every packed query row: Lk - Lq + i within its request."""
+    """Position of every packed query row: Lk - Lq + i within its request
+    (FlashInfer page, sink_attention_unified, varlen branch: the queries are
+    the last qo_len positions of the request's keys)."""
     cq = _np(cu_seqlens_q).astype(np.int64)
     ck = _np(cu_seqlens_k).astype(np.int64)
     out = []

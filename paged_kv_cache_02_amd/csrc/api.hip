@@ -6,6 +6,10 @@
 #include "decode.h"
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <cmath>
+#include <unistd.h>
 
 using namespace pkv;
 
@@ -32,6 +36,22 @@ pkv_status check_block_size(int32_t bs) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Logit scale: a positive finite number (the kernels take the row maximum of
+// q.k before or after scaling, which is the same only for a positive scale).
+bool scale_ok(float s) { return s > 0.f && std::isfinite(s); }
+
+// Epoch of one fused-merge launch: a per-process call counter (never 0),
+// started from the clock and the process id so that a workspace a previous
+// process left dirty is unlikely to hold a matching epoch either.
+uint32_t next_epoch() {
+    static std::atomic<uint32_t> counter{
+        (uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u ^
+        ((uint32_t)getpid() << 16)};
+    uint32_t v;
+    do { v = counter.fetch_add(1, std::memory_order_relaxed); } while (v == 0);
+    return v;
+}
 
 // Compute units of the current device (cached per device; 256 if unknown).
 int device_cus() {
@@ -60,22 +80,40 @@ int stream_wgs_per_head_group(int Hq, int Hkv) {
     return std::max(1, (device_cus() + NHG - 1) / NHG);
 }
 
-// Balanced-schedule workspace: the fused merge's arrival counters (one per
-// sequence and head group; kStreamMaxB * Hq ints whatever B is, so that one
-// zeroed workspace serves calls with any batch size), then the partial
-// results and the tile prefix sums.
+// Decode workspace.  Its first counter_bytes(Hq) bytes hold the fused
+// merge's 64-bit arrival counters (one per sequence and head group;
+// kStreamMaxB * Hq of them whatever B is, so that one workspace serves calls
+// with any batch size).  Every other use of the workspace starts after them:
+// the balanced schedule's partial results and tile prefix sums, or the fixed
+// partitions' part_out / part_lse.  A workspace used for both never has its
+// counters overwritten.
+size_t counter_bytes(int32_t Hq) { return align256((size_t)kStreamMaxB * Hq * sizeof(uint64_t)); }
+
 struct StreamLayout {
     size_t counters, part_out, part_lse, cum, total;
 };
-StreamLayout stream_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t D) {
-    const size_t slots = (size_t)stream_wgs_per_head_group(Hq, Hkv) * 4 + B;
+StreamLayout stream_layout_hu(int32_t B, int32_t Hq, int HU, int32_t D) {
+    const int NHG = Hq / HU;
+    const size_t W = (size_t)std::max(1, (device_cus() + NHG - 1) / NHG);
+    const size_t slots = W * 4 + B;
     StreamLayout l;
     l.counters = 0;
-    l.part_out = align256((size_t)kStreamMaxB * Hq * sizeof(int32_t));
+    l.part_out = counter_bytes(Hq);
     l.part_lse = l.part_out + align256(slots * Hq * D * sizeof(float));
     l.cum = l.part_lse + align256(slots * Hq * sizeof(float));
     l.total = l.cum + align256((size_t)(B + 2) * sizeof(int32_t));
     return l;
+}
+StreamLayout stream_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t D) {
+    return stream_layout_hu(B, Hq, decode_heads_per_unit(Hq / Hkv), D);
+}
+// fixed partitions: part_out [B, Hq, P, D] then part_lse [B, Hq, P], after the counters
+size_t split_part_lse_offset(int32_t B, int32_t Hq, int32_t D, int32_t nparts) {
+    return counter_bytes(Hq) + align256((size_t)B * Hq * nparts * D * sizeof(float));
+}
+size_t split_bytes(int32_t B, int32_t Hq, int32_t D, int32_t nparts) {
+    return split_part_lse_offset(B, Hq, D, nparts) +
+           align256((size_t)B * Hq * nparts * sizeof(float));
 }
 // Arguments of the balanced stream kernel without the fused merge.
 StreamArgs stream_args(const void *q, const void *k_cache, const void *v_cache,
@@ -94,6 +132,7 @@ StreamArgs stream_args(const void *q, const void *k_cache, const void *v_cache,
     a.mbps = mbps; a.window_left = window_left; a.alibi = alibi;
     a.W = stream_wgs_per_head_group(Hq, Hkv);
     a.scale_log2 = sm_scale * kLog2e;
+    a.epoch = next_epoch();
     return a;
 }
 bool use_stream(pkv_dtype dtype, int32_t B, int32_t partition_size, int32_t max_seqlen_k) {
@@ -119,6 +158,15 @@ SplitPlan plan_split(int32_t max_seqlen_k, int32_t partition_size) {
         p.split = p.nparts > 1;
     }
     return p;
+}
+
+// Workspace bytes a decode call with these arguments uses (0: none).
+size_t decode_need(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_seqlen_k,
+                   int32_t partition_size, pkv_dtype dtype) {
+    if (B == 0) return 0;
+    if (use_stream(dtype, B, partition_size, max_seqlen_k)) return stream_layout(B, Hq, Hkv, D).total;
+    const SplitPlan p = plan_split(max_seqlen_k, partition_size);
+    return p.split ? split_bytes(B, Hq, D, p.nparts) : 0;
 }
 
 // Launch the decode kernel for one plan: the final output (no split) or
@@ -151,7 +199,7 @@ pkv_status launch_decode_stage(void *out, float *lse, float *part_out, float *pa
     a.D = D; a.bs_log2 = ilog2(block_size); a.mbps = mbps; a.window_left = window_left;
     a.alibi = alibi; a.part_size = plan.part_size; a.nparts = plan.nparts; a.split = plan.split ? 1 : 0;
     a.scale_log2 = sm_scale * kLog2e;
-    return launch_rows(a, false, s);
+    return launch_rows(a, s);
 }
 
 }  // namespace
@@ -266,23 +314,22 @@ pkv_status pkv_reshape_and_cache_rope(const void *key, const void *value, void *
                              dtype == PKV_BF16, (hipStream_t)stream);
 }
 
-size_t pkv_paged_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
-                                        int32_t head_dim, int32_t block_size,
-                                        int32_t max_seqlen_k, int32_t partition_size,
-                                        pkv_dtype dtype)
+size_t pkv_paged_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_dim,
+                                        int32_t max_seqlen_k, int32_t partition_size)
 {
-    if (B < 0 || max_seqlen_k < 0 || partition_size < 0) return (size_t)-1;
-    if (check_heads(num_q_heads, num_kv_heads, head_dim) != PKV_OK) return (size_t)-1;
-    if (check_block_size(block_size) != PKV_OK) return (size_t)-1;
-    if (!dtype_ok(dtype)) return (size_t)-1;
-    if (partition_size > 0 && partition_size % block_size) return (size_t)-1;
+    if (B < 0 || num_q_heads <= 0 || max_seqlen_k < 0 || partition_size < 0) return (size_t)-1;
+    if (head_dim != 64 && head_dim != 128) return (size_t)-1;
     if (B == 0) return 0;
-    if (use_stream(dtype, B, partition_size, max_seqlen_k))
-        return stream_layout(B, num_q_heads, num_kv_heads, head_dim).total;
+    size_t need = 0;
+    if (B <= kStreamMaxB && max_seqlen_k > 0 && partition_size == 0) {
+        // the balanced bf16 schedule, for whichever GQA grouping the call has
+        for (int hu = 1; hu <= 4; hu *= 2)
+            if (num_q_heads % hu == 0)
+                need = std::max(need, stream_layout_hu(B, num_q_heads, hu, head_dim).total);
+    }
     const SplitPlan p = plan_split(max_seqlen_k, partition_size);
-    if (!p.split) return 0;
-    const size_t rows = (size_t)B * num_q_heads * p.nparts;
-    return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
+    if (p.split) need = std::max(need, split_bytes(B, num_q_heads, head_dim, p.nparts));
+    return need;
 }
 
 pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_cache,
@@ -300,7 +347,7 @@ pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_
     if (st != PKV_OK) return st;
     if ((st = check_block_size(block_size)) != PKV_OK) return st;
     if (!dtype_ok(dtype)) return PKV_ERR_UNSUPPORTED;
-    if (window_left < -1 || partition_size < 0) return PKV_ERR_SHAPE;
+    if (window_left < -1 || partition_size < 0 || !scale_ok(sm_scale)) return PKV_ERR_SHAPE;
     if (partition_size > 0 && partition_size % block_size) return PKV_ERR_SHAPE;
     if ((long long)max_seqlen_k > (long long)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
     if (B == 0) return PKV_OK;
@@ -310,9 +357,8 @@ pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
 
     hipStream_t s = (hipStream_t)stream;
-    const size_t need = pkv_paged_decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_dim,
-                                                         block_size, max_seqlen_k,
-                                                         partition_size, dtype);
+    const size_t need = decode_need(B, num_q_heads, num_kv_heads, head_dim, max_seqlen_k,
+                                    partition_size, dtype);
     if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
     if (need > 0 && ((uintptr_t)workspace & 255u)) return PKV_ERR_WORKSPACE;
 
@@ -323,16 +369,17 @@ pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_
                                    max_blocks_per_seq, sm_scale, window_left, alibi_slopes,
                                    workspace);
         const StreamLayout lay = stream_layout(B, num_q_heads, num_kv_heads, head_dim);
-        a.counters = (int32_t *)((char *)workspace + lay.counters);
+        a.counters = (uint64_t *)((char *)workspace + lay.counters);
         a.out = out; a.lse = lse; a.sink = sink;
         return launch_decode_stream_bf16(a, s);
     }
 
     const SplitPlan plan = plan_split(max_seqlen_k, partition_size);
-    const size_t rows = (size_t)B * num_q_heads * plan.nparts;
-    float *part_out = plan.split ? (float *)workspace : nullptr;
+    float *part_out =
+        plan.split ? (float *)((char *)workspace + counter_bytes(num_q_heads)) : nullptr;
     float *part_lse =
-        plan.split ? (float *)((char *)workspace + align256(rows * head_dim * sizeof(float)))
+        plan.split ? (float *)((char *)workspace +
+                               split_part_lse_offset(B, num_q_heads, head_dim, plan.nparts))
                    : nullptr;
     st = launch_decode_stage(out, lse, part_out, part_lse, q, k_cache, v_cache, block_table,
                              cache_seqlens, sink, B, num_q_heads, num_kv_heads, head_dim,
@@ -362,7 +409,7 @@ pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const v
     if (st != PKV_OK) return st;
     if ((st = check_block_size(block_size)) != PKV_OK) return st;
     if (!dtype_ok(dtype)) return PKV_ERR_UNSUPPORTED;
-    if (window_left < -1) return PKV_ERR_SHAPE;
+    if (window_left < -1 || !scale_ok(sm_scale)) return PKV_ERR_SHAPE;
     // the new token goes to position cache_seqlens[b] <= max_seqlen_k
     if ((long long)max_seqlen_k + 1 > (long long)max_blocks_per_seq * block_size)
         return PKV_ERR_SHAPE;
@@ -383,7 +430,7 @@ pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const v
                                    num_q_heads, num_kv_heads, head_dim, block_size,
                                    max_blocks_per_seq, sm_scale, window_left, alibi_slopes,
                                    workspace);
-        a.counters = (int32_t *)((char *)workspace + lay.counters);
+        a.counters = (uint64_t *)((char *)workspace + lay.counters);
         a.out = out; a.lse = lse; a.sink = sink;
         a.k_new = k_new; a.v_new = v_new; a.append = 1;
         return launch_decode_stream_bf16(a, s);
@@ -397,7 +444,7 @@ pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const v
     a.mbps = max_blocks_per_seq; a.window_left = window_left;
     a.part_size = max_seqlen_k + 1; a.nparts = 1; a.split = 0;
     a.scale_log2 = sm_scale * kLog2e;
-    return launch_rows(a, false, s);
+    return launch_rows(a, s);
 }
 
 pkv_status pkv_paged_decode_stage(const void *q, const void *k_cache, const void *v_cache,
@@ -415,7 +462,7 @@ pkv_status pkv_paged_decode_stage(const void *q, const void *k_cache, const void
     if (st != PKV_OK) return st;
     if ((st = check_block_size(block_size)) != PKV_OK) return st;
     if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
-    if (window_left < -1 || B > kStreamMaxB) return PKV_ERR_SHAPE;
+    if (window_left < -1 || B > kStreamMaxB || !scale_ok(sm_scale)) return PKV_ERR_SHAPE;
     if ((long long)max_seqlen_k > (long long)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
     if (B == 0) return PKV_OK;
     if (!q || !block_table || !cache_seqlens || !k_cache || !v_cache) return PKV_ERR_NULL;
@@ -470,7 +517,8 @@ pkv_status pkv_paged_decode_partitions(float *part_out, float *part_lse, const v
     if (st != PKV_OK) return st;
     if ((st = check_block_size(block_size)) != PKV_OK) return st;
     if (!dtype_ok(dtype)) return PKV_ERR_UNSUPPORTED;
-    if (window_left < -1 || partition_size <= 0 || partition_size % block_size)
+    if (window_left < -1 || partition_size <= 0 || partition_size % block_size ||
+        !scale_ok(sm_scale))
         return PKV_ERR_SHAPE;
     if ((long long)max_seqlen_k > (long long)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
     const long long need_parts = ((long long)max_seqlen_k + partition_size - 1) / partition_size;
@@ -522,7 +570,7 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
     pkv_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
     if (st != PKV_OK) return st;
     if (!dtype_ok(dtype) || causal != 1) return PKV_ERR_UNSUPPORTED;
-    if (window_left < -1) return PKV_ERR_SHAPE;
+    if (window_left < -1 || !scale_ok(sm_scale)) return PKV_ERR_SHAPE;
     if (rope_cos_sin) {
         // q rotated in registers: rotary_dim a multiple of 32 within the head,
         // and a table row for every query position (< max_seqlen_k)
@@ -576,7 +624,7 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
     a.G = num_q_heads / num_kv_heads; a.D = head_dim; a.bs_log2 = bs_log2;
     a.mbps = max_blocks_per_seq; a.window_left = window_left; a.scale_log2 = sm_scale * kLog2e;
     a.T = max_seqlen_q;
-    return launch_rows(a, false, s);
+    return launch_rows(a, s);
 }
 
 }  // extern "C"

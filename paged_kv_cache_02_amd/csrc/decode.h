@@ -34,9 +34,13 @@ struct StreamArgs {
     float *part_lse;             // [slots, Hq]
     int32_t *cum_out;            // [B + 2]: tile prefix sums, then the per-wave chunk
     // Fused merge (counters != null): the last wave to finish a (sequence,
-    // head group) merges its pieces into out/lse.  counters [B, Hq / HU] must
-    // be zero at launch; the kernel leaves them zero.
-    int32_t *counters;
+    // head group) merges its pieces into out/lse.  counters [B, Hq / HU],
+    // 64 bits each: the call's epoch in the high half, the pieces counted so
+    // far in the low half.  A counter whose epoch is not this call's is stale
+    // (left by an interrupted call, or never used) and counts as zero; the
+    // wave that completes a count sets the counter back to zero.
+    uint64_t *counters;
+    uint32_t epoch;              // nonzero, different from the previous calls'
     void *out;                   // [B, Hq, D] bf16
     float *lse;                  // [B, Hq] or null
     const float *sink;           // [Hq] or null
@@ -127,8 +131,8 @@ struct MergeArgs {
     int32_t dtype;
 };
 
-// One query row per wave, plain VALU arithmetic: the fp32 path of decode and
-// prefill.  mode 0 = paged decode, 1 = varlen prefill.
+// One query row per wave, plain fp32 VALU arithmetic: the fp32 path of decode
+// and prefill.  mode 0 = paged decode, 1 = varlen prefill.
 struct RowArgs {
     int32_t mode;
     void *out;
@@ -187,7 +191,7 @@ int decode_heads_per_unit(int G);
 pkv_status launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);
 pkv_status launch_decode_stream_bf16(const StreamArgs &a, hipStream_t stream);
 pkv_status launch_merge(const MergeArgs &a, hipStream_t stream);
-pkv_status launch_rows(const RowArgs &a, bool bf16, hipStream_t stream);
+pkv_status launch_rows(const RowArgs &a, hipStream_t stream);
 pkv_status launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream);
 int prefill_heads_per_wg(int G);
 int prefill_block_m();

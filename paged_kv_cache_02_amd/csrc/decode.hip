@@ -760,26 +760,39 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
         // count.  The wave that brings a count to pieces(b) merges b and
         // leaves its counter zero for the next call.
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        // A counter holds (epoch << 32) | count.  One compare-and-swap per
+        // arrival: a counter left by another call (another epoch) restarts
+        // from zero, so a workspace that an interrupted call or another mode
+        // left dirty cannot make a merge run early or never.
         auto arrive = [&](int b) {
-            int old = 0;
-            if (lane == 0)
-                old = __hip_atomic_fetch_add(a.counters + (size_t)b * NHG + hg, 1,
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            return __builtin_amdgcn_readlane(old, 0) == pieces(b) - 1;
+            int arrived = 0;
+            if (lane == 0) {
+                uint64_t *ctr = a.counters + (size_t)b * NHG + hg;
+                uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                uint64_t nv;
+                do {
+                    const uint32_t cnt = (uint32_t)(old >> 32) == a.epoch ? (uint32_t)old : 0u;
+                    nv = ((uint64_t)a.epoch << 32) | (cnt + 1u);
+                } while (!__hip_atomic_compare_exchange_strong(ctr, &old, nv, __ATOMIC_RELAXED,
+                                                               __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_AGENT));
+                arrived = (int)(uint32_t)nv;
+            }
+            return __builtin_amdgcn_readlane(arrived, 0) == pieces(b);
         };
         const bool last_a = arrive(shared_a);
         const bool last_b = shared_b >= 0 && arrive(shared_b);
         if (last_a) {
             stream_merge_wave<D, HU>(a, shared_a, h0, first_slot(shared_a), pieces(shared_a));
             if (lane == 0)
-                __hip_atomic_store(a.counters + (size_t)shared_a * NHG + hg, 0, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(a.counters + (size_t)shared_a * NHG + hg, (uint64_t)0,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if (last_b) {
             stream_merge_wave<D, HU>(a, shared_b, h0, first_slot(shared_b), pieces(shared_b));
             if (lane == 0)
-                __hip_atomic_store(a.counters + (size_t)shared_b * NHG + hg, 0, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(a.counters + (size_t)shared_b * NHG + hg, (uint64_t)0,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

@@ -1,5 +1,5 @@
 // Attention with one wave per (query row, head): the float32 path of paged
-// decode and varlen prefill (and a plain bf16 variant used as a cross-check).
+// decode and varlen prefill.
 //
 // Same definition as the bf16 kernels (FlashInfer sink-attention page:
 // logits sm_scale*q.k, bottom-right causal position p = Lk - Lq + i, window
@@ -15,12 +15,11 @@
 
 namespace pkv {
 
-template <bool BF16>
 __device__ __forceinline__ float ld_elem(const void *p, size_t i) {
-    return BF16 ? bf16_to_f32(((const uint16_t *)p)[i]) : ((const float *)p)[i];
+    return ((const float *)p)[i];
 }
 
-template <int D, bool BF16>
+template <int D>
 __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
 {
     constexpr int E = D / 64;
@@ -62,7 +61,7 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
     float qv[E], acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        qv[e] = ld_elem<BF16>(a.q, qrow * D + lane + 64 * e);
+        qv[e] = ld_elem(a.q, qrow * D + lane + 64 * e);
         acc[e] = 0.f;
     }
     if (a.mode == 1 && a.rope && pos >= 0) {
@@ -78,7 +77,7 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
             const bool hi = a.rope_neox ? d >= half : (d & 1);
             const int pd = a.rope_neox ? (hi ? d - half : d + half) : (d ^ 1);
             const int i = a.rope_neox ? (hi ? d - half : d) : d / 2;
-            const float xp = ld_elem<BF16>(a.q, qrow * D + pd);
+            const float xp = ld_elem(a.q, qrow * D + pd);
             const float co = tab[i], si = tab[half + i];
             qv[e] = hi ? fmaf(qv[e], co, xp * si) : fmaf(qv[e], co, -xp * si);
         }
@@ -99,13 +98,8 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const int d = lane + 64 * e;
-            if (BF16) {
-                ((uint16_t *)a.k_cache)[dst + d] = ((const uint16_t *)a.k_new)[src + d];
-                ((uint16_t *)a.v_cache)[dst + d] = ((const uint16_t *)a.v_new)[src + d];
-            } else {
-                ((float *)a.k_cache)[dst + d] = ((const float *)a.k_new)[src + d];
-                ((float *)a.v_cache)[dst + d] = ((const float *)a.v_new)[src + d];
-            }
+            ((float *)a.k_cache)[dst + d] = ((const float *)a.k_new)[src + d];
+            ((float *)a.v_cache)[dst + d] = ((const float *)a.v_new)[src + d];
         }
     }
     for (int jj = jlo; jj < jhi; ++jj) {
@@ -127,7 +121,7 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
         const size_t off = (row * a.Hkv + g) * D;
         float s = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) s = fmaf(qv[e], ld_elem<BF16>(kb, off + lane + 64 * e), s);
+        for (int e = 0; e < E; ++e) s = fmaf(qv[e], ld_elem(kb, off + lane + 64 * e), s);
 #pragma unroll
         for (int msk = 1; msk < 64; msk <<= 1) s += shfl_xor(s, msk);
         s = fmaf(slope_log2, (float)(jj - pos), s);
@@ -136,7 +130,7 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
         const float p = fast_exp2(s - nm);
         l = fmaf(l, c, p);
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = fmaf(acc[e], c, p * ld_elem<BF16>(vb, off + lane + 64 * e));
+        for (int e = 0; e < E; ++e) acc[e] = fmaf(acc[e], c, p * ld_elem(vb, off + lane + 64 * e));
         m = nm;
     }
 
@@ -154,27 +148,20 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const float res = Lt > 0.f ? acc[e] * sc / Lt : 0.f;
-        const size_t oi = qrow * D + lane + 64 * e;
-        if (BF16) ((uint16_t *)a.out)[oi] = f32_to_bf16(res);
-        else ((float *)a.out)[oi] = res;
+        ((float *)a.out)[qrow * D + lane + 64 * e] = res;
     }
     if (a.lse && lane == 0) a.lse[qrow] = Lt > 0.f ? Mt * kLn2 + logf(Lt) : -INFINITY;
 }
 
-pkv_status launch_rows(const RowArgs &a, bool bf16, hipStream_t stream)
+pkv_status launch_rows(const RowArgs &a, hipStream_t stream)
 {
     const long long waves =
         a.mode == 0 ? (long long)a.B * a.Hq * a.nparts : (long long)a.B * a.T * a.Hq;
     if (waves == 0) return PKV_OK;
     if ((waves + 3) / 4 > 0x7fffffffLL) return PKV_ERR_SHAPE;
     const int grid = (int)((waves + 3) / 4);
-    if (a.D == 128) {
-        if (bf16) hipLaunchKernelGGL((rows_kernel<128, true>), dim3(grid), dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((rows_kernel<128, false>), dim3(grid), dim3(256), 0, stream, a);
-    } else {
-        if (bf16) hipLaunchKernelGGL((rows_kernel<64, true>), dim3(grid), dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((rows_kernel<64, false>), dim3(grid), dim3(256), 0, stream, a);
-    }
+    if (a.D == 128) hipLaunchKernelGGL((rows_kernel<128>), dim3(grid), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((rows_kernel<64>), dim3(grid), dim3(256), 0, stream, a);
     return launch_status();
 }
 

@@ -34,7 +34,7 @@ SIGNATURES = {
     "pkv_reshape_and_cache_rope": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I64,
                                                   _I32, _I32, _I32, _I32, _I32, _I32,
                                                   ctypes.c_int, _P]),
-    "pkv_paged_decode_workspace_bytes": (ctypes.c_size_t, [_I32] * 7 + [ctypes.c_int]),
+    "pkv_paged_decode_workspace_bytes": (ctypes.c_size_t, [_I32] * 5),
     "pkv_paged_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                         _I32, _I32, _I32, _I32, _F, _I32, _P, _I32, _P, _SZ,
                                         ctypes.c_int, _P]),
@@ -117,6 +117,20 @@ def _f32(t: Optional[torch.Tensor], name: str) -> Optional[torch.Tensor]:
     return t
 
 
+def _rope_table(cos_sin: torch.Tensor, rotary_dim: int) -> torch.Tensor:
+    """The kernels step through the table rotary_dim floats per row and the C
+    ABI does not take its width: it must be a contiguous float32
+    [positions, rotary_dim] tensor, or a row would be read from the wrong
+    place (or past the end of the table)."""
+    if cos_sin.dtype != torch.float32 or cos_sin.dim() != 2:
+        raise ValueError("cos_sin must be a float32 [positions, rotary_dim] table")
+    if cos_sin.shape[1] != rotary_dim:
+        raise ValueError(f"cos_sin has {cos_sin.shape[1]} columns, rotary_dim is {rotary_dim}")
+    if not cos_sin.is_contiguous():
+        raise ValueError("cos_sin must be contiguous")
+    return cos_sin
+
+
 def _row_stride(t: torch.Tensor, name: str) -> int:
     """Elements between tokens of t [T, H, D], whose per-token [H, D] blocks
     must be contiguous (the tokens themselves may be strided)."""
@@ -159,10 +173,11 @@ def rope_cos_sin(num_positions: int, rotary_dim: int, base: float = 10000.0, sca
 def rope_apply(x, positions, cos_sin, rotary_dim: int, neox: bool = True):
     """Rotate x [T, H, D] (rows may be strided, e.g. q or k of a fused QKV
     buffer) in place by positions [T]."""
+    _rope_table(cos_sin, rotary_dim)
     T, H, D = x.shape
     xs = _row_stride(x, "x")
     _check(lib.pkv_rope_apply(x.data_ptr(), _ptr(_i32(positions, "positions")),
-                              _ptr(_f32(cos_sin, "cos_sin")), T, H, D, xs, rotary_dim,
+                              _ptr(cos_sin), T, H, D, xs, rotary_dim,
                               int(bool(neox)), _dt(x), _stream()), "rope_apply")
     return x
 
@@ -170,22 +185,23 @@ def rope_apply(x, positions, cos_sin, rotary_dim: int, neox: bool = True):
 def reshape_and_cache_rope(key, value, k_cache, v_cache, slot_mapping, positions, cos_sin,
                            rotary_dim: int, neox: bool = True):
     """reshape_and_cache with each key row rotated by positions [T] as it is stored."""
+    _rope_table(cos_sin, rotary_dim)
     T, Hkv, D = key.shape
     NB, bs = k_cache.shape[0], k_cache.shape[1]
     ks, vs = _row_stride(key, "key"), _row_stride(value, "value")
     _check(lib.pkv_reshape_and_cache_rope(
         key.data_ptr(), value.data_ptr(), _ptr(k_cache), _ptr(v_cache),
         _ptr(_i32(slot_mapping, "slot_mapping")), _ptr(_i32(positions, "positions")),
-        _ptr(_f32(cos_sin, "cos_sin")), T, ks, vs, Hkv, D, bs, NB,
+        _ptr(cos_sin), T, ks, vs, Hkv, D, bs, NB,
         rotary_dim, int(bool(neox)), _dt(key, value, k_cache, v_cache), _stream()),
         "reshape_and_cache_rope")
 
 
-def decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_dim, block_size, max_seqlen_k,
-                           partition_size=0, dtype=torch.bfloat16) -> int:
-    dt = PKV_BF16 if dtype == torch.bfloat16 else PKV_F32
-    n = lib.pkv_paged_decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_dim, block_size,
-                                             max_seqlen_k, partition_size, dt)
+def decode_workspace_bytes(B, num_q_heads, head_dim, max_seqlen_k, partition_size=0) -> int:
+    """Workspace bytes for a decode of these sizes (any kv-head count, dtype
+    and block size; see pkv_paged_decode_workspace_bytes)."""
+    n = lib.pkv_paged_decode_workspace_bytes(B, num_q_heads, head_dim, max_seqlen_k,
+                                             partition_size)
     if n == ctypes.c_size_t(-1).value:
         raise PkvError(PKV_ERR_SHAPE, "paged_decode_workspace_bytes")
     return n
@@ -206,7 +222,7 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: floa
         max_seqlen_k = int(cache_seqlens.max().item()) if B else 0
     if out is None:
         out = torch.empty_like(q)
-    need = decode_workspace_bytes(B, Hq, Hkv, D, bs, max_seqlen_k, partition_size, q.dtype)
+    need = decode_workspace_bytes(B, Hq, D, max_seqlen_k, partition_size)
     if workspace is None and need:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     _check(lib.pkv_paged_decode(
@@ -229,7 +245,7 @@ def paged_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_se
     attend q [B,Hq,D] to keys 0..cache_seqlens[b]; cache_seqlens is not changed.
 
     The bf16 path needs a zero-filled workspace of
-    decode_workspace_bytes(..., max_seqlen_k + 1, 0, bf16) bytes (allocated for
+    decode_workspace_bytes(B, Hq, D, max_seqlen_k + 1) bytes (allocated for
     this call when none is given); fp32 needs none."""
     B, Hq, D = q.shape
     NB, bs, Hkv, _ = k_cache.shape
@@ -237,7 +253,7 @@ def paged_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_se
         max_seqlen_k = int(cache_seqlens.max().item()) if B else 0
     if out is None:
         out = torch.empty_like(q)
-    need = decode_workspace_bytes(B, Hq, Hkv, D, bs, max_seqlen_k + 1, 0, q.dtype)
+    need = decode_workspace_bytes(B, Hq, D, max_seqlen_k + 1)
     if workspace is None and need:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     _check(lib.pkv_paged_decode_append(
@@ -317,6 +333,8 @@ def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_
                    window_left: int = -1, out=None, lse=None, alibi_slopes=None,
                    rope_cos_sin=None, rotary_dim: int = 0, rope_neox: bool = True):
     """Causal varlen prefill: out [sum Lq, Hq, D]."""
+    if rope_cos_sin is not None:
+        _rope_table(rope_cos_sin, rotary_dim)
     T, Hq, D = q.shape
     B = cu_seqlens_q.shape[0] - 1
     if k is not None:
@@ -335,7 +353,7 @@ def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_
         bs, NB, MB, _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")),
         _ptr(_i32(cu_seqlens_k, "cu_seqlens_k")), B, int(max_seqlen_q), int(max_seqlen_k), Hq,
         Hkv, D, float(sm_scale), 1, window_left, _ptr(_f32(alibi_slopes, "alibi_slopes")),
-        _ptr(_f32(rope_cos_sin, "rope_cos_sin")),
+        _ptr(rope_cos_sin),
         0 if rope_cos_sin is None else rope_cos_sin.shape[0], rotary_dim, int(bool(rope_neox)),
         _ptr(_f32(sink, "sink")), _dt(q, k, v, k_cache, v_cache, out), _stream()),
         "varlen_prefill")

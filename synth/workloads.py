@@ -45,6 +45,7 @@ __all__ = [
     "config1_decode",
     "config1_prefill",
     "config2_decode",
+    "config3_lengths",
     "config3_prefill",
     "config4_chunked",
     "config5_split_decode",

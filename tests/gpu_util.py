@@ -34,16 +34,36 @@ def assert_close(got, want, dtype, what="", lse=False):
     else:
         atol, rtol = tol(dtype)
     both_inf = np.isinf(want) & (got == want)
-    err = np.abs(got - want)
-    ok = (err <= atol + rtol * np.abs(want)) | both_inf
+    # matching infinities compare equal; subtract only the other elements
+    err = np.abs(np.where(both_inf, 0.0, got) - np.where(both_inf, 0.0, want))
+    ok = (err <= atol + rtol * np.abs(np.where(both_inf, 0.0, want))) | both_inf
     if not ok.all():
         idx = np.argwhere(~ok)[:5]
         raise AssertionError(f"{what}: {int((~ok).sum())} of {ok.size} outside tolerance; "
                              f"first {idx.tolist()} got {got[tuple(idx.T)]} want {want[tuple(idx.T)]}")
 
 
+def check_decode_case(c, append=False):
+    """Host validation of a decode case's index data before any launch."""
+    from paged_kv_cache_02_amd import validate
+    validate.check_decode(c.block_table, c.cache_seqlens, c.num_blocks, c.block_size,
+                          c.max_seqlen_k, append=append)
+
+
+def check_prefill_case(c):
+    """Host validation of a prefill case's index data before any launch."""
+    from paged_kv_cache_02_amd import validate
+    if c.paged:
+        validate.check_varlen(c.cu_seqlens_q, c.cu_seqlens_k, c.max_seqlen_q, c.max_seqlen_k,
+                              c.block_table, c.k_cache.shape[0], c.block_size)
+    else:
+        validate.check_varlen(c.cu_seqlens_q, c.cu_seqlens_k, c.max_seqlen_q, c.max_seqlen_k,
+                              num_k_rows=c.k.shape[0])
+
+
 def run_decode(c, partition_size=0, with_lse=True):
     from paged_kv_cache_02_amd import pkv
+    check_decode_case(c)
     q, kc, vc = dev(c.q), dev(c.k_cache), dev(c.v_cache)
     lse = torch.empty(c.B, c.Hq, dtype=torch.float32, device="cuda") if with_lse else None
     out = pkv.paged_decode(q, kc, vc, dev(c.block_table), dev(c.cache_seqlens), c.sm_scale,
@@ -60,6 +80,7 @@ def oracle_decode(c, units=None):
 
 def run_prefill(c, with_lse=True):
     from paged_kv_cache_02_amd import pkv
+    check_prefill_case(c)
     T = c.q.shape[0]
     lse = torch.empty(T, c.Hq, dtype=torch.float32, device="cuda") if with_lse else None
     out = pkv.varlen_prefill(dev(c.q), dev(c.cu_seqlens_q), dev(c.cu_seqlens_k), c.max_seqlen_q,

@@ -53,6 +53,32 @@ def pin_varlen_map():
     assert oracle.token_request(ck).tolist() == g["k_request_index"]
 
 
+def pin_query_positions():
+    """Query positions on the Transformers doc's varlen example (lengths
+    [10,3,1] over [0,1,7]) under the FlashInfer varlen branch's alignment
+    (queries are the last qo_len positions), from a hand-written fixture; and
+    the prefill oracle's mask agrees with them: with q = 0 every visible key
+    gets the same weight, and with V(j) = j in dimension 0 each row's output
+    is the mean of 0..p, i.e. p / 2 (0 for a row that sees no key)."""
+    g = _golden("varlen_positions.json")
+    cq = synth.cu_from_lengths(g["q_lens"])
+    ck = synth.cu_from_lengths(g["k_lens"])
+    assert oracle.query_positions(cq, ck).tolist() == g["query_positions"]
+    D = 4
+    q = torch.zeros((int(cq[-1]), 2, D))
+    kv = torch.zeros((int(ck[-1]), 1, D))
+    v = torch.zeros((int(ck[-1]), 1, D))
+    for r, Lk in enumerate(g["k_lens"]):
+        v[int(ck[r]):int(ck[r]) + Lk, 0, 0] = torch.arange(Lk, dtype=torch.float32)
+        v[int(ck[r]):int(ck[r]) + Lk, 0, 1] = 1.0
+    o, _ = oracle.varlen_prefill(q, cq, ck, None, 1.0, 1, k=kv, v=v)
+    pos = np.array(g["query_positions"])
+    seen = np.array(g["visible_keys_causal"])
+    for h in range(2):
+        _close(o[:, h, 1], (seen > 0).astype(float), 0, 1e-15, "rows that see a key")
+        _close(o[:, h, 0], np.where(seen > 0, pos / 2.0, 0.0), 0, 1e-14, "mean key index")
+
+
 def pin_decode_block_example():
     """Transformers 'Paged attention' doc, Decode path example."""
     g = _golden("decode_blocks.json")

@@ -39,23 +39,27 @@ def test_status_strings_and_version():
 
 
 def test_workspace_sizes():
-    import torch
-    f32, bf = torch.float32, torch.bfloat16
-    # long-context split: B=16, Hq=32, D=128, 131072 keys, partitions of 512
-    n = pkv.decode_workspace_bytes(16, 32, 8, 128, 64, 131072, 512, bf)
+    counters = 4096 * 32 * 8          # the balanced schedule's 64-bit counters lead
+    # long-context split: B=16, Hq=32, D=128, 131072 keys, partitions of 512:
+    # part_out and part_lse come after the counter region, never over it
+    n = pkv.decode_workspace_bytes(16, 32, 128, 131072, 512)
     rows = 16 * 32 * 256
-    assert n == rows * 128 * 4 + rows * 4
-    assert pkv.decode_workspace_bytes(4, 8, 8, 64, 16, 100, 0, f32) == 0    # fp32 auto: no split
-    assert pkv.decode_workspace_bytes(4, 8, 8, 64, 16, 512, 512, bf) == 0   # one partition
-    # bf16 auto: balanced schedule, size independent of the sequence lengths
-    a = pkv.decode_workspace_bytes(64, 32, 8, 128, 16, 4096, 0, bf)
-    b = pkv.decode_workspace_bytes(64, 32, 8, 128, 16, 100, 0, bf)
-    assert a == b and a > 0 and a % 256 == 0
-    assert pkv.decode_workspace_bytes(0, 32, 8, 128, 16, 100, 0, bf) == 0
+    assert n == counters + rows * 128 * 4 + rows * 4
+    assert pkv.decode_workspace_bytes(4, 8, 64, 512, 512) == 0       # one partition: no split
+    # automatic: the balanced schedule, size independent of the sequence lengths
+    a = pkv.decode_workspace_bytes(64, 32, 128, 4096)
+    b = pkv.decode_workspace_bytes(64, 32, 128, 100)
+    assert a == b and a > counters and a % 256 == 0
+    # the size covers every kv-head count: grouping 4 heads per unit needs the most slots
+    assert pkv.decode_workspace_bytes(64, 30, 128, 100) > 0
+    assert pkv.decode_workspace_bytes(0, 32, 128, 100) == 0
+    assert pkv.decode_workspace_bytes(4097, 32, 128, 100) == 0        # no balanced schedule
     with pytest.raises(pkv.PkvError):
-        pkv.decode_workspace_bytes(4, 8, 3, 64, 16, 100, 0, bf)              # Hq % Hkv
+        pkv.decode_workspace_bytes(4, 8, 96, 100)                     # head_dim
     with pytest.raises(pkv.PkvError):
-        pkv.decode_workspace_bytes(4, 8, 8, 64, 16, 1000, 24, bf)            # P % bs
+        pkv.decode_workspace_bytes(4, 0, 64, 100)                     # no heads
+    with pytest.raises(pkv.PkvError):
+        pkv.decode_workspace_bytes(-1, 8, 64, 100)
 
 
 def decode_call(**over):
@@ -81,6 +85,10 @@ def decode_call(**over):
     (dict(part=24), pkv.PKV_ERR_SHAPE),
     (dict(max_seqlen_k=65, MB=4), pkv.PKV_ERR_SHAPE),
     (dict(B=-1), pkv.PKV_ERR_SHAPE),
+    (dict(scale=0.0), pkv.PKV_ERR_SHAPE),            # sm_scale must be positive and finite
+    (dict(scale=-0.1), pkv.PKV_ERR_SHAPE),
+    (dict(scale=float("nan")), pkv.PKV_ERR_SHAPE),
+    (dict(scale=float("inf")), pkv.PKV_ERR_SHAPE),
     (dict(part=16), pkv.PKV_ERR_WORKSPACE),          # split without workspace
     (dict(part=0), pkv.PKV_ERR_WORKSPACE),           # bf16 balanced schedule needs one
     (dict(part=16, ws=FAKE, ws_bytes=10), pkv.PKV_ERR_WORKSPACE),
@@ -114,6 +122,7 @@ def append_call(**over):
     (dict(D=96), pkv.PKV_ERR_UNSUPPORTED),
     (dict(bs=24), pkv.PKV_ERR_UNSUPPORTED),
     (dict(window=-2), pkv.PKV_ERR_SHAPE),
+    (dict(scale=-1.0), pkv.PKV_ERR_SHAPE),
     (dict(k_new=FAKE + 8), pkv.PKV_ERR_UNSUPPORTED),   # misaligned
     (dict(ws=None), pkv.PKV_ERR_WORKSPACE),          # bf16 needs the balanced workspace
     (dict(ws=FAKE, ws_bytes=10), pkv.PKV_ERR_WORKSPACE),
@@ -146,6 +155,8 @@ def prefill_call(**over):
     (dict(Hkv=3), pkv.PKV_ERR_SHAPE),
     (dict(D=80), pkv.PKV_ERR_UNSUPPORTED),
     (dict(window=-5), pkv.PKV_ERR_SHAPE),
+    (dict(scale=0.0), pkv.PKV_ERR_SHAPE),
+    (dict(scale=float("-inf")), pkv.PKV_ERR_SHAPE),
     (dict(dt=2), pkv.PKV_ERR_UNSUPPORTED),
     (dict(maxk=1 << 24, Hkv=8, Hq=8, D=128), pkv.PKV_ERR_UNSUPPORTED),   # 4 GiB of K per request
     (dict(B=0), pkv.PKV_OK),
@@ -217,3 +228,44 @@ def test_rope_cache_validation():
     assert lib.pkv_reshape_and_cache_rope(*dict(a, rd=8).values()) == pkv.PKV_ERR_UNSUPPORTED
     assert lib.pkv_reshape_and_cache_rope(*dict(a, bs=24).values()) == pkv.PKV_ERR_UNSUPPORTED
     assert lib.pkv_reshape_and_cache_rope(*dict(a, T=0).values()) == pkv.PKV_OK
+
+
+def test_stage_and_partitions_validation():
+    # pkv_paged_decode_stage: a positive finite sm_scale, bf16 only, B <= 4096
+    st = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, B=2, Hq=8, Hkv=2, D=128, bs=16, NB=4,
+              MB=4, msk=64, scale=0.1, window=-1, alibi=None, ws=None, ws_bytes=0, dt=1,
+              stream=None)
+    assert lib.pkv_paged_decode_stage(*dict(st, scale=-0.1).values()) == pkv.PKV_ERR_SHAPE
+    assert lib.pkv_paged_decode_stage(*dict(st, dt=0).values()) == pkv.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_paged_decode_stage(*dict(st, B=4097).values()) == pkv.PKV_ERR_SHAPE
+    assert lib.pkv_paged_decode_stage(*st.values()) == pkv.PKV_ERR_WORKSPACE
+    # pkv_paged_decode_partitions
+    pa = dict(po=FAKE, pl=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, B=2, Hq=8, Hkv=2,
+              D=128, bs=16, NB=4, MB=4, msk=64, scale=0.1, window=-1, alibi=None, P=32, maxp=2,
+              dt=1, stream=None)
+    assert lib.pkv_paged_decode_partitions(*dict(pa, scale=float("nan")).values()) == \
+        pkv.PKV_ERR_SHAPE
+    assert lib.pkv_paged_decode_partitions(*dict(pa, maxp=1).values()) == pkv.PKV_ERR_SHAPE
+    assert lib.pkv_paged_decode_partitions(*dict(pa, P=24).values()) == pkv.PKV_ERR_SHAPE
+    assert lib.pkv_paged_decode_partitions(*dict(pa, po=None).values()) == pkv.PKV_ERR_NULL
+    assert lib.pkv_paged_decode_partitions(*dict(pa, B=0).values()) == pkv.PKV_OK
+
+
+def test_rope_table_width_checked_before_launch():
+    """The C ABI does not take the cos/sin table's width, and the kernels step
+    through it rotary_dim floats per row: the binding refuses a table of any
+    other width (or dtype) before it touches the library or the device."""
+    import torch
+    x = torch.zeros(4, 8, 128, dtype=torch.bfloat16)
+    pos = torch.zeros(4, dtype=torch.int32)
+    for bad in (torch.zeros(16, 64), torch.zeros(16, 128, dtype=torch.float64),
+                torch.zeros(16 * 128)):
+        with pytest.raises(ValueError):
+            pkv.rope_apply(x, pos, bad, 128)
+        with pytest.raises(ValueError):
+            pkv.reshape_and_cache_rope(x, x, x, x, pos, pos, bad, 128)
+        with pytest.raises(ValueError):
+            pkv.varlen_prefill(x, pos, pos, 4, 4, 0.1, 8, k=x, v=x, rope_cos_sin=bad,
+                               rotary_dim=128)
+    with pytest.raises(ValueError):
+        pkv.rope_apply(x, pos, torch.zeros(128, 16).t(), 128)     # not contiguous

@@ -39,7 +39,7 @@ def test_decode_alibi(case, mode):
     msk = int(c.cache_seqlens.max())
     lse = torch.empty(c.B, Hq, dtype=torch.float32, device="cuda")
     if mode == "two_launch":
-        nb = pkv.decode_workspace_bytes(c.B, Hq, Hkv, D, bs, msk, 0, dtype)
+        nb = pkv.decode_workspace_bytes(c.B, Hq, D, msk)
         ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
         pkv.paged_decode_stage(q, kc, vc, bt, sl, c.sm_scale, msk, ws, window, alibi_slopes=dev(al))
         out = torch.empty_like(q)

@@ -8,6 +8,7 @@ import torch
 import oracle
 import synth
 from gpu_util import assert_close, banner, dev
+from paged_kv_cache_02_amd import validate
 
 pytestmark = pytest.mark.gpu
 
@@ -30,11 +31,15 @@ def make_case(seed, lens, Hq, Hkv, D, bs, dtype, sink, window=-1):
 
 def run_append(c, L, kn, vn, workspace=None):
     from paged_kv_cache_02_amd import pkv
+    validate.check_decode(c.block_table, L, c.num_blocks, c.block_size, int(L.max()), append=True)
     kc, vc = dev(c.k_cache), dev(c.v_cache)
-    lse = torch.empty(c.q.shape[0], c.q.shape[1], dtype=torch.float32, device="cuda")
-    out = pkv.paged_decode_append(dev(c.q), dev(kn), dev(vn), kc, vc, dev(c.block_table), dev(L),
-                                  c.sm_scale, sink=dev(c.sink), window_left=c.window_left,
-                                  max_seqlen_k=int(L.max()), lse=lse, workspace=workspace)
+    # outputs poisoned with NaN: a row the call does not write shows up
+    lse = torch.full((c.q.shape[0], c.q.shape[1]), float("nan"), dtype=torch.float32,
+                     device="cuda")
+    out = torch.full_like(dev(c.q), float("nan"))
+    pkv.paged_decode_append(dev(c.q), dev(kn), dev(vn), kc, vc, dev(c.block_table), dev(L),
+                            c.sm_scale, sink=dev(c.sink), window_left=c.window_left,
+                            max_seqlen_k=int(L.max()), lse=lse, workspace=workspace, out=out)
     torch.cuda.synchronize()
     return out, lse, kc, vc
 
@@ -110,7 +115,7 @@ def test_append_workspace_reuse():
     from paged_kv_cache_02_amd import pkv
     banner("append workspace reuse")
     c, L, kn, vn = make_case(311, [100, 333, 2000, 1], 32, 8, 128, 16, torch.bfloat16, True)
-    nb = pkv.decode_workspace_bytes(4, 32, 8, 128, 16, int(L.max()) + 1, 0, torch.bfloat16)
+    nb = pkv.decode_workspace_bytes(4, 32, 128, int(L.max()) + 1)
     ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
     out1, lse1, kc, vc = run_append(c, L, kn, vn, workspace=ws)
     out2, lse2, _, _ = run_append(c, L, kn, vn, workspace=ws)
@@ -124,10 +129,10 @@ def test_append_workspace_reuse():
                                             c.sink, c.sm_scale)[0], torch.bfloat16, "decode after")
 
 
-def test_append_config2_full_size_sampled():
+def test_append_config2_full_size():
     """The headline decode shape (64 sequences of 512..4096 cached tokens,
     32/8 heads, D 128, block size 16, sink) with the new token appended;
-    256 sampled (sequence, head) rows against the oracle, and the caches
+    every output element and lse against the oracle, and the caches
     compared in full on the GPU."""
     banner("append config2 full size")
     c2 = synth.config2_decode()
@@ -135,13 +140,10 @@ def test_append_config2_full_size_sampled():
     c, L, kn, vn = make_case(312, lens, c2.Hq, c2.Hkv, c2.D, c2.block_size, torch.bfloat16, True)
     kc0, vc0 = dev(c.k_cache).clone(), dev(c.v_cache).clone()
     out, lse, kc, vc = run_append(c, L, kn, vn)
-    units = np.sort(np.random.default_rng(5).choice(c.q.shape[0] * c.q.shape[1], 256,
-                                                    replace=False))
     o, l, _, _ = oracle.decode_append(c.q, kn, vn, c.k_cache, c.v_cache, c.block_table, L,
-                                      c.sink, c.sm_scale, units=units)
-    b, h = units // c.q.shape[1], units % c.q.shape[1]
-    assert_close(out.float().cpu()[b, h], o[b, h], torch.bfloat16, "config2 append sampled")
-    assert_close(lse.cpu()[b, h], l[b, h], torch.bfloat16, "config2 append lse", lse=True)
+                                      c.sink, c.sm_scale)
+    assert_close(out, o, torch.bfloat16, "config2 append out")
+    assert_close(lse, l, torch.bfloat16, "config2 append lse", lse=True)
     bs = c.block_size
     slots = torch.tensor([int(c.block_table[i, Lb // bs]) * bs + Lb % bs
                           for i, Lb in enumerate(lens)], device="cuda")

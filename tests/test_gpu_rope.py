@@ -56,7 +56,8 @@ def test_rope_apply(case, dtype):
     tab = pkv.rope_cos_sin(512, rd, 10000.0)
     pkv.rope_apply(x, pos.cuda(), tab, rd, neox)
     torch.cuda.synchronize()
-    want = oracle.rope_apply(before[:, H:2 * H].cpu(), pos, tab.cpu(), rd, neox)
+    want = oracle.rope_apply(before[:, H:2 * H].cpu(), pos, oracle.rope_cos_sin(512, rd, 10000.0),
+                             rd, neox)
     assert_close(x, want, dtype, "rope apply")
     bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
     assert torch.equal(buf[:, :H].view(bits), before[:, :H].view(bits))
@@ -85,7 +86,7 @@ def test_reshape_and_cache_rope(neox, dtype):
     pkv.reshape_and_cache_rope(key.cuda(), val.cuda(), gk, gv, torch.from_numpy(slots).cuda(),
                                torch.from_numpy(pos).cuda(), tab, rd, neox)
     torch.cuda.synchronize()
-    krot = oracle.rope_apply(key, pos, tab.cpu(), rd, neox)
+    krot = oracle.rope_apply(key, pos, oracle.rope_cos_sin(1000, rd, 10000.0), rd, neox)
     fk, fv = gk.cpu().view(-1, Hkv, D), gv.cpu().view(-1, Hkv, D)
     live = slots >= 0
     assert_close(fk[slots[live]], krot[live], dtype, "rotated keys")
@@ -117,8 +118,9 @@ def test_prefill_rope(case, dtype):
     c = synth.prefill_case(510 + len(q_lens), q_lens, k_lens, Hq, Hkv, D, dtype, True)
     n_pos = max(k_lens)
     tab = pkv.rope_cos_sin(n_pos, rd, 10000.0)
+    otab = oracle.rope_cos_sin(n_pos, rd, 10000.0)      # the oracle's own table
     kpos = np.concatenate([np.arange(L) for L in k_lens]).astype(np.int32)
-    krot = synth.to_dtype(oracle.rope_apply(c.k, kpos, tab.cpu(), rd, neox).astype(np.float32),
+    krot = synth.to_dtype(oracle.rope_apply(c.k, kpos, otab, rd, neox).astype(np.float32),
                           dtype)
     kw = dict(k=dev(krot), v=dev(c.v))
     if bs:
@@ -139,7 +141,7 @@ def test_prefill_rope(case, dtype):
                              rope_cos_sin=tab, rotary_dim=rd, rope_neox=neox, **kw)
     torch.cuda.synchronize()
     qpos = oracle.query_positions(c.cu_seqlens_q, c.cu_seqlens_k)
-    qrot = torch.from_numpy(oracle.rope_apply(c.q, qpos, tab.cpu(), rd, neox)).float()
+    qrot = torch.from_numpy(oracle.rope_apply(c.q, qpos, otab, rd, neox)).float()
     o, l = oracle.varlen_prefill(qrot, c.cu_seqlens_q, c.cu_seqlens_k, c.sink, c.sm_scale, Hkv,
                                  k=krot.float(), v=c.v.float())
     assert_close(out, o, dtype, "prefill rope out")
@@ -192,9 +194,10 @@ def test_decode_with_rope(dtype):
     lse = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
     out = pkv.paged_decode(qg, kc, vc, bt.cuda(), sl.cuda(), sm, sink=sink.cuda(), lse=lse)
     torch.cuda.synchronize()
-    krot = synth.to_dtype(oracle.rope_apply(key, kpos, tab.cpu(), rd, True).astype(np.float32),
+    otab = oracle.rope_cos_sin(max(lens), rd, 10000.0)    # the oracle's own table
+    krot = synth.to_dtype(oracle.rope_apply(key, kpos, otab, rd, True).astype(np.float32),
                           dtype).float()
-    qrot = synth.to_dtype(oracle.rope_apply(q, qpos, tab.cpu(), rd, True).astype(np.float32),
+    qrot = synth.to_dtype(oracle.rope_apply(q, qpos, otab, rd, True).astype(np.float32),
                           dtype).float()
     pk = torch.zeros((nb * bs, Hkv, D), dtype=torch.float32)
     pv = torch.zeros_like(pk)
@@ -216,8 +219,9 @@ def test_prefill_rope_window_alibi(dtype):
     c = synth.prefill_case(540, q_lens, k_lens, Hq, Hkv, D, dtype, True, window_left=window)
     al = torch.tensor([2.0 ** (-8.0 * (h + 1) / Hq) for h in range(Hq)], dtype=torch.float32)
     tab = pkv.rope_cos_sin(max(k_lens), rd)
+    otab = oracle.rope_cos_sin(max(k_lens), rd, 10000.0)  # the oracle's own table
     kpos = np.concatenate([np.arange(L) for L in k_lens]).astype(np.int32)
-    krot = synth.to_dtype(oracle.rope_apply(c.k, kpos, tab.cpu(), rd, True).astype(np.float32),
+    krot = synth.to_dtype(oracle.rope_apply(c.k, kpos, otab, rd, True).astype(np.float32),
                           dtype)
     lse = torch.empty(c.q.shape[0], Hq, dtype=torch.float32, device="cuda")
     out = pkv.varlen_prefill(dev(c.q), dev(c.cu_seqlens_q), dev(c.cu_seqlens_k), c.max_seqlen_q,
@@ -226,18 +230,18 @@ def test_prefill_rope_window_alibi(dtype):
                              rope_cos_sin=tab, rotary_dim=rd)
     torch.cuda.synchronize()
     qpos = oracle.query_positions(c.cu_seqlens_q, c.cu_seqlens_k)
-    qrot = torch.from_numpy(oracle.rope_apply(c.q, qpos, tab.cpu(), rd, True)).float()
+    qrot = torch.from_numpy(oracle.rope_apply(c.q, qpos, otab, rd, True)).float()
     o, l = oracle.varlen_prefill(qrot, c.cu_seqlens_q, c.cu_seqlens_k, c.sink, c.sm_scale, Hkv,
                                  k=krot.float(), v=c.v.float(), window_left=window, alibi=al)
     assert_close(out, o, dtype, "prefill rope window alibi out")
     assert_close(lse, l, dtype, "prefill rope window alibi lse", lse=True)
 
 
-def test_config3_rope_full_size_sampled():
+def test_config3_rope_full_size():
     """The 8-request prefill workload (256..4096 tokens, 32/8 heads, D 128,
     sink) as the benchmark times it with RoPE (rotary_dim 128, neox): q
-    rotated inside the prefill over contiguous keys that the oracle rotated,
-    256 sampled (token, head) rows plus each request's first and last row;
+    rotated inside the prefill over contiguous keys that the oracle rotated
+    with its own table, every output element and lse against the oracle;
     and every key stored by reshape_and_cache_rope into a block-16 pool,
     compared in full with the oracle's rotation (values bitwise)."""
     from paged_kv_cache_02_amd import pkv
@@ -245,15 +249,16 @@ def test_config3_rope_full_size_sampled():
     c = synth.config3_prefill()
     rd = 128
     tab = pkv.rope_cos_sin(max(c.k_lens), rd)
-    tab_cpu = tab.cpu()
+    tab_cpu = oracle.rope_cos_sin(max(c.k_lens), rd, 10000.0)   # the oracle's own table
     kpos = np.concatenate([np.arange(L) for L in c.k_lens]).astype(np.int32)
     krot = synth.to_dtype(oracle.rope_apply(c.k, kpos, tab_cpu, rd, True).astype(np.float32),
                           torch.bfloat16)
     T = c.q.shape[0]
-    lse = torch.empty(T, c.Hq, dtype=torch.float32, device="cuda")
-    out = pkv.varlen_prefill(dev(c.q), dev(c.cu_seqlens_q), dev(c.cu_seqlens_k), c.max_seqlen_q,
-                             c.max_seqlen_k, c.sm_scale, c.Hkv, k=dev(krot), v=dev(c.v),
-                             sink=dev(c.sink), lse=lse, rope_cos_sin=tab, rotary_dim=rd)
+    lse = torch.full((T, c.Hq), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full((T, c.Hq, c.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    pkv.varlen_prefill(dev(c.q), dev(c.cu_seqlens_q), dev(c.cu_seqlens_k), c.max_seqlen_q,
+                       c.max_seqlen_k, c.sm_scale, c.Hkv, k=dev(krot), v=dev(c.v),
+                       sink=dev(c.sink), lse=lse, out=out, rope_cos_sin=tab, rotary_dim=rd)
     bt, nb = synth.pool_from_lengths(np.random.default_rng(7), c.k_lens, 16)
     slots = torch.cat([synth.slots_for_tokens(bt[r:r + 1].expand(L, -1).contiguous(),
                                               list(range(L)), 16)
@@ -263,19 +268,12 @@ def test_config3_rope_full_size_sampled():
     pkv.reshape_and_cache_rope(dev(c.k), dev(c.v), kc, vc, slots, torch.from_numpy(kpos).cuda(),
                                tab, rd)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(12)
-    units = np.sort(rng.choice(T * c.Hq, 256, replace=False))
-    cu = c.cu_seqlens_q.tolist()
-    extra = [cu[r] * c.Hq for r in range(c.B)] + [(cu[r + 1] - 1) * c.Hq + c.Hq - 1
-                                                  for r in range(c.B)]
-    units = np.unique(np.concatenate([units, extra]))
     qpos = oracle.query_positions(c.cu_seqlens_q, c.cu_seqlens_k)
     qrot = torch.from_numpy(oracle.rope_apply(c.q, qpos, tab_cpu, rd, True).astype(np.float32))
     o, l = oracle.varlen_prefill(qrot, c.cu_seqlens_q, c.cu_seqlens_k, c.sink, c.sm_scale, c.Hkv,
-                                 k=krot.float(), v=c.v.float(), units=units)
-    t, h = units // c.Hq, units % c.Hq
-    assert_close(out.float().cpu()[t, h], o[t, h], torch.bfloat16, "config3 rope sampled")
-    assert_close(lse.cpu()[t, h], l[t, h], torch.bfloat16, "config3 rope lse", lse=True)
+                                 k=krot.float(), v=c.v.float())
+    assert_close(out, o, torch.bfloat16, "config3 rope out")
+    assert_close(lse, l, torch.bfloat16, "config3 rope lse", lse=True)
     s = slots.long()
     assert_close(kc.view(-1, c.Hkv, c.D)[s], krot.float().numpy(), torch.bfloat16,
                  "config3 rotated keys")

@@ -1,0 +1,291 @@
+"""CPU models of the kernels' work-to-address mappings, checked for bounds.
+
+Each model restates, in numpy, how a kernel turns its launch coordinates
+(workgroup, wave, lane) and the device index data (cu_seqlens, cache_seqlens,
+block tables) into the rows it reads and writes.  The assertions are facts
+the kernels rely on and nothing else checks on the GPU: every query row,
+rotary-table row, key/value row, block-table entry, partial-result slot and
+output row lies inside its buffer, and every output row is written exactly
+once.  The models run over every test shape of the GPU suite, the five
+workloads and the edge cases (Lq > Lk, Lk = 0, empty requests), so a change
+to a kernel's indexing that breaks a bound fails here, on the CPU, before it
+can fault a GPU.  A model must change together with the kernel it models.
+"""
+
+import importlib
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+CUS = 256          # compute units the decode schedule is sized for
+BN = 64            # prefill keys per tile
+BM = 128           # prefill positions per workgroup tile
+
+
+def heads_per_unit(G):
+    return 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
+
+
+# ---------------------------------------------------------------------------
+# prefill_bf16_kernel (csrc/prefill.hip)
+# ---------------------------------------------------------------------------
+
+def model_prefill(q_lens, k_lens, Hq, Hkv, D, window=-1, paged_bs=0, rope_rows=None):
+    """Every access of one prefill launch; returns the number of workgroups
+    that did work.  rope_rows: rows of the rotary table (>= max Lk), or None."""
+    B = len(q_lens)
+    cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64)
+    cu_k = np.concatenate([[0], np.cumsum(k_lens)]).astype(np.int64)
+    G = Hq // Hkv
+    hpw = heads_per_unit(G)
+    bm = BM // hpw
+    ng = G // hpw
+    max_q_tiles = (max(q_lens, default=0) + BM - 1) // BM
+    grid = B * max_q_tiles * Hq
+    if grid == 0:
+        return 0
+    bid = np.arange(grid, dtype=np.int64)
+    p = bid % Hq
+    slot = bid // Hq
+    g = p % Hkv
+    hs = (p // Hkv) % ng
+    blk = (hpw - 1 - (p // Hkv) // ng + slot) % hpw
+    r = slot % B
+    qt = max_q_tiles - 1 - slot // B
+    assert (qt >= 0).all()
+    cq0, Lq = cu_q[r], cu_q[r + 1] - cu_q[r]
+    live = qt * BM + blk * bm < Lq
+    bid, g, hs, blk, r, qt, cq0, Lq = (x[live] for x in (bid, g, hs, blk, r, qt, cq0, Lq))
+    ck0, Lk = cu_k[r], cu_k[r + 1] - cu_k[r]
+    row0 = qt * BM + blk * bm
+    nrows = np.minimum(bm, Lq - row0)
+    pos0 = Lk - Lq + row0
+    pos_last = pos0 + nrows - 1
+    kv_lo = np.maximum(0, pos0 - window) if window >= 0 else np.zeros_like(pos0)
+    kv_hi = np.minimum(Lk, pos_last + 1)
+    t_begin = kv_lo & ~(BN - 1)
+    ntiles = np.where(kv_hi > kv_lo, (kv_hi - t_begin + BN - 1) // BN, 0)
+    # K/V tiles: the first and the last tile issued lie inside the request's keys
+    has = ntiles > 0
+    assert (t_begin[has] >= 0).all()
+    t_last = t_begin + (ntiles - 1) * BN
+    assert (t_last[has] < Lk[has]).all(), "a K/V tile starts past the request's last key"
+    rowbytes = Hkv * D * 2
+    if not paged_bs:
+        # one buffer per tile whose range (Lk - t0) rows must be positive and fit 32 bits
+        assert ((Lk[has] - t_begin[has]) * rowbytes < 2 ** 32).all()
+        assert (ck0[has] + t_last[has] < cu_k[-1]).all()
+    else:
+        bs = paged_bs
+        U = D // 8
+        RPI = 64 // U                      # key rows per load instruction
+        assert bs >= RPI
+        nblk = (Lk + bs - 1) // bs         # valid block-table entries of the request
+        for k in range(int(ntiles.max(initial=0))):
+            sel = k < ntiles
+            t0 = t_begin[sel] + k * BN
+            lk, nb = Lk[sel], nblk[sel]
+            tail = t0 + BN > lk
+            for i in range(U):             # load instructions of all four waves
+                key0 = np.where(tail, np.minimum(t0 + RPI * i, lk - 1), t0 + RPI * i)
+                assert (key0 >= 0).all() and (key0 < lk).all()
+                assert ((key0 // bs) < nb).all(), "block-table entry past the request's blocks"
+                for lrow in range(RPI):
+                    row = np.where(tail, key0 + np.minimum(lrow, lk - 1 - key0), key0 + lrow)
+                    assert (row < lk).all(), "a K/V row past the request's keys"
+                    assert (row // bs == key0 // bs).all(), "a load instruction crosses a block"
+    # waves: query rows, rotary-table rows and output rows
+    written = np.zeros((int(cu_q[-1]), Hq), dtype=np.int64)
+    for wave in range(4):
+        h = g * G + hs * hpw + wave % hpw
+        assert (h < Hq).all()
+        wrow0 = row0 + 32 * (wave // hpw)
+        wrows = np.maximum(0, np.minimum(32, Lq - wrow0))
+        wpos0 = Lk - Lq + wrow0
+        for lr in range(32):
+            ok = lr < wrows
+            qrow = cq0 + wrow0 + lr
+            assert (qrow[ok] < cq0[ok] + Lq[ok]).all()
+            if rope_rows is not None:
+                tpos = wpos0 + lr
+                trow = np.where(ok & (tpos >= 0), tpos, 0)
+                assert (trow >= 0).all() and (trow < rope_rows).all(), "rotary row outside the table"
+            np.add.at(written, (qrow[ok], h[ok]), 1)
+    assert (written == 1).all(), "an output row written twice or not at all"
+    return int(live.sum())
+
+
+# ---------------------------------------------------------------------------
+# decode_stream_kernel (balanced schedule) and decode_part_kernel (csrc/decode.hip)
+# ---------------------------------------------------------------------------
+
+def stream_lo(L, w):
+    return np.maximum(0, L - 1 - w) if w >= 0 else np.zeros_like(L)
+
+
+def stream_tiles(L, w):
+    return np.where(L <= 0, 0, (L - (stream_lo(L, w) & ~15) + 15) >> 4)
+
+
+def model_decode_stream(lens, Hq, Hkv, bs, mbps, window=-1, append=False):
+    """Every tile of the balanced schedule: its block-table entry, the rows it
+    reads, the wave that owns it and the partial-result slot it writes."""
+    L = np.asarray(lens, dtype=np.int64) + (1 if append else 0)
+    B = L.size
+    assert bs >= 16 and bs % 16 == 0, "a 16-token tile must lie inside one block"
+    HU = heads_per_unit(Hq // Hkv)
+    NHG = Hq // HU
+    W = max(1, (CUS + NHG - 1) // NHG)
+    nw = 4 * W
+    tiles = stream_tiles(L, window)
+    cum = np.concatenate([[0], np.cumsum(tiles)])
+    T = int(cum[-1])
+    chunk = max(1, (T + nw - 1) // nw)
+    x = np.arange(T, dtype=np.int64)
+    b = np.searchsorted(cum, x, side="right") - 1
+    assert (b >= 0).all() and (b < B).all()
+    t = (stream_lo(L[b], window) & ~15) + 16 * (x - cum[b])
+    assert (t >= 0).all() and (t < L[b]).all(), "a tile starts outside its sequence"
+    assert ((t >> int(math.log2(bs))) < (L[b] + bs - 1) // bs).all(), "block entry past the sequence"
+    assert ((t >> int(math.log2(bs))) < mbps).all()
+    assert (t % bs + 16 <= bs).all()
+    gw = x // chunk
+    assert (gw < nw).all(), "a tile past the last wave"
+    slots = 4 * W + B
+    assert (gw + b < slots).all(), "partial-result slot past the workspace"
+    # the merge reads pieces(b) consecutive slots from first_slot(b)
+    has = tiles > 0
+    bb = np.arange(B)[has]
+    pieces = (cum[bb + 1] - 1) // chunk - cum[bb] // chunk + 1
+    first = cum[bb] // chunk + bb
+    assert (pieces >= 1).all() and (first + pieces <= slots).all()
+    # pieces(b) is exactly the number of waves whose range meets b
+    owners = {}
+    for xx, bx in zip(gw.tolist(), b.tolist()):
+        owners.setdefault(bx, set()).add(xx)
+    for k, bx in enumerate(bb.tolist()):
+        assert len(owners[bx]) == pieces[k] and min(owners[bx]) + bx == first[k]
+    if append:
+        # the owner of each sequence's last tile stores row L - 1 (the new token)
+        pos = L - 1
+        assert ((pos >> int(math.log2(bs))) < mbps).all()
+    return T
+
+
+def model_decode_part(lens, Hq, Hkv, bs, part_size, window=-1):
+    """Fixed partitions: every (sequence, head group, partition) unit's tiles."""
+    L = np.asarray(lens, dtype=np.int64)
+    msk = int(L.max(initial=0))
+    nparts = max(1, (max(msk, 1) + part_size - 1) // part_size)
+    HU = heads_per_unit(Hq // Hkv)
+    NHG = Hq // HU
+    for pidx in range(nparts):
+        start = np.full_like(L, pidx * part_size)
+        end = np.minimum(start + part_size, L)
+        if window >= 0:
+            start = np.maximum(start, L - 1 - window)
+        tile0 = start & ~15
+        ntiles = np.where(start < end, (end - tile0 + 15) >> 4, 0)
+        has = ntiles > 0
+        last = tile0 + 16 * (ntiles - 1)
+        assert (tile0[has] >= 0).all() and (last[has] < L[has]).all()
+        assert ((last[has] // bs) < (L[has] + bs - 1) // bs).all()
+    return nparts * NHG * L.size
+
+
+# ---------------------------------------------------------------------------
+# shapes: the GPU suite's cases, the five workloads and edge cases
+# ---------------------------------------------------------------------------
+
+def _gpu_module(name):
+    return importlib.import_module(name)
+
+
+def prefill_shapes():
+    P = _gpu_module("test_gpu_prefill")
+    R = _gpu_module("test_gpu_rope")
+    shapes = []
+    for q_lens, k_lens, Hq, Hkv, D, sink, window in P.CASES:
+        shapes.append((q_lens, k_lens or q_lens, Hq, Hkv, D, window, 0))
+    for q_lens, k_lens, Hq, Hkv, D, bs, sink, window in P.PAGED:
+        shapes.append((q_lens, k_lens, Hq, Hkv, D, window, bs))
+    for case in R.PREFILL:
+        q_lens, k_lens, Hq, Hkv, D, rd, neox, bs = case
+        shapes.append((q_lens, k_lens or q_lens, Hq, Hkv, D, -1, bs))
+    import synth
+    L3 = synth.config3_lengths()
+    shapes += [
+        ([10, 3, 1], [10, 3, 1], 4, 2, 64, -1, 0),                 # workload 1 (prefill)
+        ([10, 3, 1], [0, 1, 7], 4, 2, 64, -1, 0),                  # the varlen example, Lq > Lk
+        ([10, 3, 1], [0, 1, 7], 4, 2, 64, -1, 16),
+        (L3, L3, 32, 8, 128, -1, 0),                               # workload 3
+        ([512] * 4, [8704] * 4, 64, 8, 64, 128, 16),               # workload 4
+        ([0, 5, 300], [0, 5, 300], 8, 8, 128, 3, 16),              # empty request, window
+        ([129, 1], [0, 0], 12, 4, 128, -1, 0),                     # no keys at all
+        ([1000], [70], 16, 2, 64, 17, 32),                         # Lq > Lk with a window
+        ([64, 65, 127, 128, 129], [64, 65, 127, 128, 129], 6, 2, 128, 0, 16),
+    ]
+    return shapes
+
+
+@pytest.mark.parametrize("window_override", [None, 0, 50])
+def test_prefill_mapping_in_bounds(window_override):
+    n = 0
+    for q_lens, k_lens, Hq, Hkv, D, window, bs in prefill_shapes():
+        w = window if window_override is None else window_override
+        for paged in sorted({0, bs}):
+            n += model_prefill(q_lens, k_lens, Hq, Hkv, D, w, paged,
+                               rope_rows=max(max(k_lens, default=0), 1))
+    assert n > 0
+
+
+def decode_shapes():
+    Dm = _gpu_module("test_gpu_decode")
+    shapes = []
+    for lengths, Hq, Hkv, D, bs, sink, window in Dm.CASES:
+        shapes.append((lengths, Hq, Hkv, bs, window))
+    import synth
+    rng = np.random.default_rng([1, 11])
+    L2 = rng.integers(512, 4096, size=64, endpoint=True).tolist()
+    shapes += [
+        ([30, 32, 70], 4, 2, 32, -1),                              # workload 1 (the page example)
+        (L2, 32, 8, 16, -1),                                       # workload 2
+        ([131072] * 16, 32, 8, 64, -1),                            # workload 5
+        ([0, 0, 0], 32, 8, 16, -1),
+        (np.random.default_rng(61).integers(1, 40, size=1200).tolist(), 16, 2, 16, 9),
+        ([1] * 4096, 32, 8, 16, -1),                               # the largest batch
+    ]
+    return shapes
+
+
+def test_decode_stream_mapping_in_bounds():
+    for lengths, Hq, Hkv, bs, window in decode_shapes():
+        mbps = (max(max(lengths), 1) + 1 + bs - 1) // bs
+        model_decode_stream(lengths, Hq, Hkv, bs, mbps, window)
+        model_decode_stream(lengths, Hq, Hkv, bs, mbps, window, append=True)
+
+
+def test_decode_partition_mapping_in_bounds():
+    for lengths, Hq, Hkv, bs, window in decode_shapes():
+        if len(lengths) > 512:
+            continue
+        for P in sorted({bs, 2 * bs, 512 if 512 % bs == 0 else bs}):
+            model_decode_part(lengths, Hq, Hkv, bs, P, window)
+
+
+def test_models_catch_a_planted_mistake():
+    """The models are not vacuous: a prefill whose last tile would start at the
+    request's end (ntiles one too many), or a decode table entry one block too
+    far, fails their bounds."""
+    with pytest.raises(AssertionError):
+        # a rotary table one row short of the longest request
+        model_prefill([100, 7], [300, 7], 8, 2, 64, -1, 0, rope_rows=299)
+    with pytest.raises(AssertionError):
+        # a block table one block short for the appended token
+        model_decode_stream([16, 31], 8, 2, 16, mbps=1, append=True)

@@ -3,8 +3,12 @@ that at least one pin catches each of them.  This is what shows the pins
 constrain every part of the oracle: a dropped sink term, a scaled sink, a
 wrong GQA grouping, top-left instead of bottom-right causal alignment, a
 window off by one, a paged-address mistake, a wrong lse, a wrong merge
-weight, K used in place of V, the sink left out of the max, and a decode
-query at the wrong position."""
+weight, K used in place of V, the sink left out of the max, a decode query
+at the wrong position, an ALiBi bias of the wrong sign, a partition one key
+too long, top-left query positions, and four rotary-embedding mistakes (the
+frequency exponent, the sign of the sine, the pairing, linear scaling
+inverted).  A mutation names the file of the oracle package it changes; each
+mutant package is a copy of ``oracle/`` imported in its own subprocess."""
 
 import json
 import os
@@ -17,30 +21,44 @@ import pytest
 
 import oracle
 
-SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+PKG = os.path.dirname(oracle.__file__)
+
+C, PY = "oracle.c", "__init__.py"
 
 MUTATIONS = {
-    "sink_dropped_from_Z": ("double Z = exp(sigma - M);\n    for (int d = 0;",
+    "sink_dropped_from_Z": (C, "double Z = exp(sigma - M);\n    for (int d = 0;",
                             "double Z = 0.0 * exp(sigma - M);\n    for (int d = 0;"),
-    "sink_scaled": ("double sigma = c->sink ? (double)c->sink[h] : -INFINITY;",
+    "sink_scaled": (C, "double sigma = c->sink ? (double)c->sink[h] : -INFINITY;",
                     "double sigma = c->sink ? c->scale * (double)c->sink[h] : -INFINITY;"),
-    "gqa_modulo": ("int G = c->Hq / c->Hkv, g = h / G;\n    int Lq",
+    "gqa_modulo": (C, "int G = c->Hq / c->Hkv, g = h / G;\n    int Lq",
                    "int G = c->Hq / c->Hkv, g = h % c->Hkv;\n    int Lq"),
-    "causal_top_left": ("int p = Lk - Lq + i;", "int p = i;"),
-    "window_off_by_one": ("if (window_left >= 0 && j < p - window_left) continue;",
+    "causal_top_left": (C, "int p = Lk - Lq + i;", "int p = i;"),
+    "window_off_by_one": (C, "if (window_left >= 0 && j < p - window_left) continue;",
                           "if (window_left >= 0 && j <= p - window_left) continue;"),
-    "paged_addr_swapped": ("return (long long)block_table_row[pos / block_size] * block_size + pos % block_size;",
+    "paged_addr_swapped": (C, "return (long long)block_table_row[pos / block_size] * block_size + pos % block_size;",
                            "return (long long)block_table_row[pos % block_size] * block_size + pos / block_size;"),
-    "paged_offset_shifted": ("return (long long)block_table_row[pos / block_size] * block_size + pos % block_size;",
+    "paged_offset_shifted": (C, "return (long long)block_table_row[pos / block_size] * block_size + pos % block_size;",
                              "return (long long)block_table_row[pos / block_size] * block_size + (pos + 1) % block_size;"),
-    "lse_without_max": ("*lse = M + log(Z);", "*lse = log(Z);"),
-    "merge_weight_wrong": ("double wgt = exp(pl[p] - L);", "double wgt = exp(pl[p] - M);"),
-    "pv_uses_k": ("o[d] += e * load_elem(vbase, krow[n] + d, dtype);",
+    "lse_without_max": (C, "*lse = M + log(Z);", "*lse = log(Z);"),
+    "merge_weight_wrong": (C, "double wgt = exp(pl[p] - L);", "double wgt = exp(pl[p] - M);"),
+    "pv_uses_k": (C, "o[d] += e * load_elem(vbase, krow[n] + d, dtype);",
                   "o[d] += e * load_elem(kbase, krow[n] + d, dtype);"),
-    "max_ignores_sink": ("    double M = sigma;\n    for (int n = 0;", "    double M = -INFINITY;\n    for (int n = 0;"),
-    "decode_query_position": ("visible_keys(Lk, Lk - 1, c->window, lo, hi, js)",
+    "max_ignores_sink": (C, "    double M = sigma;\n    for (int n = 0;", "    double M = -INFINITY;\n    for (int n = 0;"),
+    "decode_query_position": (C, "visible_keys(Lk, Lk - 1, c->window, lo, hi, js)",
                               "visible_keys(Lk, Lk - 2, c->window, lo, hi, js)"),
-    "merge_sink_dropped": ("double Z = exp(sigma - M);\n            for (int p = 0; p < np; ++p) Z",
+    "alibi_sign": (C, "s[n] = sm_scale * acc + slope * (double)(js[n] - p);",
+                   "s[n] = sm_scale * acc + slope * (double)(p - js[n]);"),
+    "partition_one_key_long": (C, "if (c->part > 0) { lo = p * c->part; hi = lo + c->part; }",
+                               "if (c->part > 0) { lo = p * c->part; hi = lo + c->part + 1; }"),
+    "query_positions_top_left": (PY, "out.append(Lk - Lq + np.arange(Lq))",
+                                 "out.append(np.arange(Lq))"),
+    "rope_frequency_exponent": (PY, "inv_freq = b ** (-(2.0 * np.arange(half)) / rotary_dim)",
+                                "inv_freq = b ** (-(np.arange(half)) / rotary_dim)"),
+    "rope_sine_sign": (PY, "y[..., :half] = a * c - b * s", "y[..., :half] = a * c + b * s"),
+    "rope_pairing_swapped": (PY, "    if neox:\n        a, b = y[..., :half]",
+                             "    if not neox:\n        a, b = y[..., :half]"),
+    "rope_linear_inverted": (PY, "t = t / factor", "t = t * factor"),
+    "merge_sink_dropped": (C, "double Z = exp(sigma - M);\n            for (int p = 0; p < np; ++p) Z",
                            "double Z = 0.0;\n            for (int p = 0; p < np; ++p) Z"),
 }
 
@@ -54,21 +72,27 @@ def workdir():
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_mutation_is_caught(name, workdir):
-    before, after = MUTATIONS[name]
-    src = open(SRC).read()
-    assert src.count(before) == 1, f"mutation anchor for {name} not unique in oracle.c"
-    path = os.path.join(workdir, f"{name}.c")
+    fname, before, after = MUTATIONS[name]
+    pkg = os.path.join(workdir, name, "oracle")
+    os.makedirs(pkg)
+    for f in (C, PY):
+        shutil.copy(os.path.join(PKG, f), os.path.join(pkg, f))
+    path = os.path.join(pkg, fname)
+    src = open(path).read()
+    assert src.count(before) == 1, f"mutation anchor for {name} not unique in {fname}"
     with open(path, "w") as f:
         f.write(src.replace(before, after))
-    lib = oracle.compile_source(path, os.path.join(workdir, f"lib{name}.so"))
-    # each mutant runs in a child process: a mutant that reads out of bounds
-    # and crashes has been caught too
+    # each mutant runs in a child process that imports the mutated copy of the
+    # package (it builds its own liboracle.so): a mutant that reads out of
+    # bounds and crashes has been caught too
     here = os.path.dirname(os.path.abspath(__file__))
     code = (
         "import json, sys\n"
-        f"sys.path[:0] = [{here!r}, {os.path.dirname(here)!r}]\n"
+        f"sys.path[:0] = [{os.path.dirname(pkg)!r}, {here!r}, {os.path.dirname(here)!r}]\n"
         "import oracle, oracle_pins as P\n"
-        f"oracle.use_library({lib!r})\n"
+        f"assert oracle.__file__.startswith({pkg!r}), oracle.__file__\n"
+        "oracle.build()\n"
+        "print('READY', flush=True)\n"
         "caught = []\n"
         "for pin in P.ALL_PINS:\n"
         "    try:\n"
@@ -78,6 +102,8 @@ def test_mutation_is_caught(name, workdir):
         "print(json.dumps(caught))\n")
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=600)
     if r.returncode != 0:
+        # a crash counts as caught only once the mutant package has loaded
+        assert "READY" in r.stdout, f"mutant package did not load:\n{r.stderr[-2000:]}"
         caught = [f"crash (exit {r.returncode})"]
     else:
         caught = json.loads(r.stdout.strip().splitlines()[-1])
