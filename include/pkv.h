@@ -92,7 +92,9 @@ typedef enum pkv_status {
     PKV_ERR_SHAPE = 2,       /* sizes inconsistent or out of range            */
     PKV_ERR_UNSUPPORTED = 3, /* valid request this library does not implement */
     PKV_ERR_WORKSPACE = 4,   /* workspace missing or too small                */
-    PKV_ERR_HIP = 5          /* a HIP launch failed (hipGetLastError)         */
+    PKV_ERR_HIP = 5,         /* a HIP launch failed (hipGetLastError)         */
+    PKV_ERR_SCRATCH = 6      /* the call needs more than the static scratch of
+                                pkv_paged_decode_noalloc                      */
 } pkv_status;
 
 typedef enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
@@ -245,6 +247,36 @@ pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_
                             int32_t max_seqlen_k, float sm_scale, int32_t window_left,
                             const float *alibi_slopes, int32_t partition_size, void *workspace,
                             size_t workspace_bytes, pkv_dtype dtype, void *stream);
+
+/*
+ * pkv_paged_decode_noalloc -- pkv_paged_decode for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The arguments and the result are those of
+ * pkv_paged_decode without workspace / workspace_bytes: the workspace is a
+ * static device array of PKV_NOALLOC_SCRATCH_BYTES (32 MiB) inside the
+ * library, which each device it runs on holds until the process ends.  The
+ * call allocates nothing (no hipMalloc, hipFree or allocating library call);
+ * the caller still owns every input and output.
+ *   - PKV_ERR_SCRATCH (nothing launched) when the call would need more than
+ *     PKV_NOALLOC_SCRATCH_BYTES, i.e. when
+ *     pkv_paged_decode_workspace_bytes for its arguments exceeds it (for
+ *     example very large batches, or a split into many fixed partitions).
+ *   - The first call on a device looks up the array's address there and
+ *     clears it with a fill kernel on `stream`, ahead of its own work.
+ *   - Every call on one device shares that device's array and leaves it as the
+ *     last call left it (the merge counters at zero): calls that overlap in
+ *     time on one device race and must be serialised, e.g. on one stream.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+pkv_status pkv_paged_decode_noalloc(void *out, float *lse, const void *q, const void *k_cache,
+                                    const void *v_cache, const int32_t *block_table,
+                                    const int32_t *cache_seqlens, const float *sink, int32_t B,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t num_blocks,
+                                    int32_t max_blocks_per_seq, int32_t max_seqlen_k,
+                                    float sm_scale, int32_t window_left,
+                                    const float *alibi_slopes, int32_t partition_size,
+                                    pkv_dtype dtype, void *stream);
 
 /*
  * pkv_paged_decode_append -- decode with the new token appended in the same

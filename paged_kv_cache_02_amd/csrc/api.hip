@@ -204,6 +204,63 @@ pkv_status launch_decode_stage(void *out, float *lse, float *part_out, float *pa
 
 }  // namespace
 
+namespace pkv {
+
+pkv_status decode_check(const DecodeCall &c) {
+    if (c.B < 0 || c.num_blocks < 0 || c.mbps < 0 || c.max_seqlen_k < 0) return PKV_ERR_SHAPE;
+    pkv_status st = check_heads(c.Hq, c.Hkv, c.D);
+    if (st != PKV_OK) return st;
+    if ((st = check_block_size(c.block_size)) != PKV_OK) return st;
+    if (!dtype_ok(c.dtype)) return PKV_ERR_UNSUPPORTED;
+    if (c.window_left < -1 || c.partition_size < 0 || !scale_ok(c.sm_scale)) return PKV_ERR_SHAPE;
+    if (c.partition_size > 0 && c.partition_size % c.block_size) return PKV_ERR_SHAPE;
+    if ((long long)c.max_seqlen_k > (long long)c.mbps * c.block_size) return PKV_ERR_SHAPE;
+    if (c.B == 0) return PKV_OK;
+    if (!c.out || !c.q || !c.block_table || !c.cache_seqlens) return PKV_ERR_NULL;
+    if (c.max_seqlen_k > 0 && (!c.k_cache || !c.v_cache)) return PKV_ERR_NULL;
+    if (c.max_seqlen_k > 0 && c.num_blocks == 0) return PKV_ERR_SHAPE;
+    if (!aligned16(c.q) || !aligned16(c.k_cache) || !aligned16(c.v_cache))
+        return PKV_ERR_UNSUPPORTED;
+    return PKV_OK;
+}
+
+size_t decode_workspace_need(const DecodeCall &c) {
+    return decode_need(c.B, c.Hq, c.Hkv, c.D, c.max_seqlen_k, c.partition_size, c.dtype);
+}
+
+pkv_status decode_launch(const DecodeCall &c, void *workspace) {
+    hipStream_t s = (hipStream_t)c.stream;
+    if (use_stream(c.dtype, c.B, c.partition_size, c.max_seqlen_k)) {
+        // one launch: the balanced stream with the merge fused into it
+        StreamArgs a = stream_args(c.q, c.k_cache, c.v_cache, c.block_table, c.cache_seqlens,
+                                   c.B, c.Hq, c.Hkv, c.D, c.block_size, c.mbps, c.sm_scale,
+                                   c.window_left, c.alibi, workspace);
+        const StreamLayout lay = stream_layout(c.B, c.Hq, c.Hkv, c.D);
+        a.counters = (uint64_t *)((char *)workspace + lay.counters);
+        a.out = c.out; a.lse = c.lse; a.sink = c.sink;
+        return launch_decode_stream_bf16(a, s);
+    }
+    const SplitPlan plan = plan_split(c.max_seqlen_k, c.partition_size);
+    float *part_out = plan.split ? (float *)((char *)workspace + counter_bytes(c.Hq)) : nullptr;
+    float *part_lse =
+        plan.split ? (float *)((char *)workspace + split_part_lse_offset(c.B, c.Hq, c.D, plan.nparts))
+                   : nullptr;
+    pkv_status st = launch_decode_stage(c.out, c.lse, part_out, part_lse, c.q, c.k_cache,
+                                        c.v_cache, c.block_table, c.cache_seqlens, c.sink, c.B,
+                                        c.Hq, c.Hkv, c.D, c.block_size, c.mbps, c.sm_scale,
+                                        c.window_left, c.alibi, plan, c.dtype, s);
+    if (st != PKV_OK || !plan.split) return st;
+    MergeArgs m{};
+    m.out = c.out; m.lse = c.lse; m.part_out = part_out; m.part_lse = part_lse;
+    m.seqlens = c.cache_seqlens; m.sink = c.sink; m.B = c.B; m.Hq = c.Hq; m.D = c.D;
+    m.part_size = plan.part_size; m.nparts = plan.nparts; m.dtype = c.dtype;
+    return launch_merge(m, s);
+}
+
+size_t decode_counter_bytes(int32_t Hq) { return counter_bytes(Hq); }
+
+}  // namespace pkv
+
 extern "C" {
 
 const char *pkv_status_string(pkv_status s) {
@@ -214,6 +271,7 @@ const char *pkv_status_string(pkv_status s) {
         case PKV_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, dtype or mode";
         case PKV_ERR_WORKSPACE: return "workspace missing or too small";
         case PKV_ERR_HIP: return "HIP launch failed";
+        case PKV_ERR_SCRATCH: return "needs more than the static scratch of the allocation-free entry point";
     }
     return "unknown status";
 }
@@ -338,59 +396,19 @@ pkv_status pkv_paged_decode(void *out, float *lse, const void *q, const void *k_
                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                             int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                             int32_t max_seqlen_k, float sm_scale, int32_t window_left,
-                            const float *alibi_slopes, int32_t partition_size, void *workspace, size_t workspace_bytes,
-                            pkv_dtype dtype, void *stream)
+                            const float *alibi_slopes, int32_t partition_size, void *workspace,
+                            size_t workspace_bytes, pkv_dtype dtype, void *stream)
 {
-    if (B < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_seqlen_k < 0)
-        return PKV_ERR_SHAPE;
-    pkv_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
-    if (st != PKV_OK) return st;
-    if ((st = check_block_size(block_size)) != PKV_OK) return st;
-    if (!dtype_ok(dtype)) return PKV_ERR_UNSUPPORTED;
-    if (window_left < -1 || partition_size < 0 || !scale_ok(sm_scale)) return PKV_ERR_SHAPE;
-    if (partition_size > 0 && partition_size % block_size) return PKV_ERR_SHAPE;
-    if ((long long)max_seqlen_k > (long long)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
-    if (B == 0) return PKV_OK;
-    if (!out || !q || !block_table || !cache_seqlens) return PKV_ERR_NULL;
-    if (max_seqlen_k > 0 && (!k_cache || !v_cache)) return PKV_ERR_NULL;
-    if (max_seqlen_k > 0 && num_blocks == 0) return PKV_ERR_SHAPE;
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
-
-    hipStream_t s = (hipStream_t)stream;
-    const size_t need = decode_need(B, num_q_heads, num_kv_heads, head_dim, max_seqlen_k,
-                                    partition_size, dtype);
+    const DecodeCall c{out, lse, q, k_cache, v_cache, block_table, cache_seqlens, sink,
+                       B, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, max_seqlen_k, sm_scale, window_left, alibi_slopes,
+                       partition_size, dtype, stream};
+    pkv_status st = decode_check(c);
+    if (st != PKV_OK || B == 0) return st;
+    const size_t need = decode_workspace_need(c);
     if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
     if (need > 0 && ((uintptr_t)workspace & 255u)) return PKV_ERR_WORKSPACE;
-
-    if (use_stream(dtype, B, partition_size, max_seqlen_k)) {
-        // one launch: the balanced stream with the merge fused into it
-        StreamArgs a = stream_args(q, k_cache, v_cache, block_table, cache_seqlens, B,
-                                   num_q_heads, num_kv_heads, head_dim, block_size,
-                                   max_blocks_per_seq, sm_scale, window_left, alibi_slopes,
-                                   workspace);
-        const StreamLayout lay = stream_layout(B, num_q_heads, num_kv_heads, head_dim);
-        a.counters = (uint64_t *)((char *)workspace + lay.counters);
-        a.out = out; a.lse = lse; a.sink = sink;
-        return launch_decode_stream_bf16(a, s);
-    }
-
-    const SplitPlan plan = plan_split(max_seqlen_k, partition_size);
-    float *part_out =
-        plan.split ? (float *)((char *)workspace + counter_bytes(num_q_heads)) : nullptr;
-    float *part_lse =
-        plan.split ? (float *)((char *)workspace +
-                               split_part_lse_offset(B, num_q_heads, head_dim, plan.nparts))
-                   : nullptr;
-    st = launch_decode_stage(out, lse, part_out, part_lse, q, k_cache, v_cache, block_table,
-                             cache_seqlens, sink, B, num_q_heads, num_kv_heads, head_dim,
-                             block_size, max_blocks_per_seq, sm_scale, window_left,
-                             alibi_slopes, plan, dtype, s);
-    if (st != PKV_OK || !plan.split) return st;
-    MergeArgs m{};
-    m.out = out; m.lse = lse; m.part_out = part_out; m.part_lse = part_lse;
-    m.seqlens = cache_seqlens; m.sink = sink; m.B = B; m.Hq = num_q_heads; m.D = head_dim;
-    m.part_size = plan.part_size; m.nparts = plan.nparts; m.dtype = dtype;
-    return launch_merge(m, s);
+    return decode_launch(c, workspace);
 }
 
 pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const void *k_new,

@@ -187,6 +187,30 @@ struct PrefillArgs {
     float scale_log2;
 };
 
+// The arguments of pkv_paged_decode without its workspace.
+struct DecodeCall {
+    void *out;
+    float *lse;
+    const void *q, *k_cache, *v_cache;
+    const int32_t *block_table, *cache_seqlens;
+    const float *sink;
+    int32_t B, Hq, Hkv, D, block_size, num_blocks, mbps, max_seqlen_k;
+    float sm_scale;
+    int32_t window_left;
+    const float *alibi;
+    int32_t partition_size;
+    pkv_dtype dtype;
+    void *stream;
+};
+// pkv_paged_decode in three steps: the host checks (PKV_OK for a valid call),
+// the workspace bytes the call uses, and the launches with a workspace of at
+// least that size (256-byte aligned).
+pkv_status decode_check(const DecodeCall &c);
+size_t decode_workspace_need(const DecodeCall &c);
+pkv_status decode_launch(const DecodeCall &c, void *workspace);
+// bytes of the fused merge's counters at the start of a decode workspace
+size_t decode_counter_bytes(int32_t Hq);
+
 int decode_heads_per_unit(int G);
 pkv_status launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);
 pkv_status launch_decode_stream_bf16(const StreamArgs &a, hipStream_t stream);

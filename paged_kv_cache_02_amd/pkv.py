@@ -17,7 +17,9 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
-PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = range(6)
+(PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP,
+ PKV_ERR_SCRATCH) = range(7)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 PKV_F32, PKV_BF16 = 0, 1
 
 # name -> (restype, argtypes), in the order of include/pkv.h
@@ -38,6 +40,9 @@ SIGNATURES = {
     "pkv_paged_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                         _I32, _I32, _I32, _I32, _F, _I32, _P, _I32, _P, _SZ,
                                         ctypes.c_int, _P]),
+    "pkv_paged_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                                _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _I32,
+                                                ctypes.c_int, _P]),
     "pkv_paged_decode_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32,
                                                _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F,
                                                _I32, _P, _P, _SZ, ctypes.c_int, _P]),
@@ -234,6 +239,29 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: floa
         0 if workspace is None else workspace.numel() * workspace.element_size(),
         _dt(q, k_cache, v_cache, out),
         _stream()), "paged_decode")
+    return out
+
+
+def paged_decode_noalloc(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: float,
+                         sink=None, window_left: int = -1, partition_size: int = 0,
+                         max_seqlen_k: Optional[int] = None, out=None, lse=None,
+                         alibi_slopes=None):
+    """paged_decode with the library's static device scratch as its workspace
+    (pkv_paged_decode_noalloc): allocates nothing beyond `out` when the
+    caller passes it.  Raises PkvError (PKV_ERR_SCRATCH) for calls that need
+    more than NOALLOC_SCRATCH_BYTES."""
+    B, Hq, D = q.shape
+    NB, bs, Hkv, _ = k_cache.shape
+    if max_seqlen_k is None:
+        max_seqlen_k = int(cache_seqlens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.pkv_paged_decode_noalloc(
+        _ptr(out), _ptr(_f32(lse, "lse")), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        _ptr(_i32(block_table, "block_table")), _ptr(_i32(cache_seqlens, "cache_seqlens")),
+        _ptr(_f32(sink, "sink")), B, Hq, Hkv, D, bs, NB, block_table.shape[1], max_seqlen_k,
+        float(sm_scale), window_left, _ptr(_f32(alibi_slopes, "alibi_slopes")), partition_size,
+        _dt(q, k_cache, v_cache, out), _stream()), "paged_decode_noalloc")
     return out
 
 

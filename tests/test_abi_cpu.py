@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    for s in range(6):
+    for s in range(7):
         assert lib.pkv_status_string(s)
     assert lib.pkv_status_string(99) == b"unknown status"
     assert lib.pkv_version() >= 10000
@@ -269,3 +269,24 @@ def test_rope_table_width_checked_before_launch():
                                rotary_dim=128)
     with pytest.raises(ValueError):
         pkv.rope_apply(x, pos, torch.zeros(128, 16).t(), 128)     # not contiguous
+
+
+def test_noalloc_validation():
+    """The allocation-free decode checks its arguments like pkv_paged_decode
+    and refuses, before touching the device, a call whose workspace would not
+    fit its static scratch."""
+    a = dict(out=FAKE, lse=None, q=FAKE, k_cache=FAKE, v_cache=FAKE, block_table=FAKE,
+             cache_seqlens=FAKE, sink=None, B=2, Hq=8, Hkv=2, D=128, bs=16, NB=4, MB=4,
+             max_seqlen_k=64, scale=0.1, window=-1, alibi=None, part=0, dt=1, stream=None)
+    f = lib.pkv_paged_decode_noalloc
+    assert f(*dict(a, out=None).values()) == pkv.PKV_ERR_NULL
+    assert f(*dict(a, scale=-1.0).values()) == pkv.PKV_ERR_SHAPE
+    assert f(*dict(a, bs=24).values()) == pkv.PKV_ERR_UNSUPPORTED
+    assert f(*dict(a, B=0).values()) == pkv.PKV_OK
+    # 4000 sequences x 64 heads in the balanced schedule: ~135 MB of partials
+    big = dict(a, B=4000, Hq=64, Hkv=8, MB=4096, max_seqlen_k=65536)
+    assert pkv.decode_workspace_bytes(4000, 64, 128, 65536) > pkv.NOALLOC_SCRATCH_BYTES
+    assert f(*big.values()) == pkv.PKV_ERR_SCRATCH
+    # a split into 512-token partitions over 131072 keys for 16 x 32 heads: 68 MB
+    assert f(*dict(a, B=16, Hq=32, Hkv=8, bs=64, MB=2048, max_seqlen_k=131072,
+                   part=512).values()) == pkv.PKV_ERR_SCRATCH
