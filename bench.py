@@ -16,7 +16,8 @@ that no step finds its keys in the 256 MB last-level cache.
 The other workloads (varlen prefill with reshape_and_cache, chunked paged
 prefill with a window, long-context split decode) are timed the same way and
 reported in the same JSON line under "workloads".  The fp64 CPU oracle is
-timed on the host cores for the headline workload ("cpu_baseline").
+timed on the host cores, at all threads and at one thread, for every workload
+("cpu_baseline", bounded samples of the larger ones).
 
 Peaks: HBM3E 8.0 TB/s, dense bf16 MFMA 2.5 PFLOP/s (MI355X public figures).
 """
@@ -467,16 +468,75 @@ def host_threads():
     return min(16, os.cpu_count() or 1)
 
 
-def cpu_baseline_decode(c, algo_bytes):
+def _sample(n_units, k, seed):
+    """k distinct unit ids out of n_units (all of them when k >= n_units), sorted."""
+    if k >= n_units:
+        return None
+    return np.sort(np.random.default_rng(seed).choice(n_units, k, replace=False))
+
+
+def oracle_decode_rate(c, units, threads):
+    """Time the oracle on the (sequence, head) units of a decode workload (None:
+    all); return (seconds, GB/s of the algorithmic bytes those units stand for:
+    each query head's share, 1 / Hq of its sequence's K/V, q and out rows)."""
     import oracle  # the CPU-baseline leg is the only bench code that runs the oracle
-    n = host_threads()
     t0 = time.perf_counter()
     o, _ = oracle.paged_decode(c.q, c.k_cache, c.v_cache, c.block_table, c.cache_seqlens,
-                               c.sink, c.sm_scale, c.window_left, nthreads=n)
+                               c.sink, c.sm_scale, c.window_left, units=units,
+                               nthreads=threads)
     dt = time.perf_counter() - t0
-    return {"value": round(algo_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": n,
-            "kind": "oracle", "seconds": round(dt, 3),
-            "sample": "the full headline workload (64 sequences x 32 heads), fp64 two-pass"}, o
+    L = c.cache_seqlens.numpy().astype(np.int64)
+    u = np.arange(c.B * c.Hq) if units is None else np.asarray(units)
+    b = u // c.Hq
+    byts = float(np.sum(L[b] * c.Hkv * c.D * 2 * 2 / c.Hq + 2 * c.D * 2))
+    return dt, byts / dt / 1e9, o
+
+
+def oracle_prefill_rate(c, units, threads):
+    """Time the oracle on (token, head) units of a prefill workload (None: all);
+    return (seconds, GFLOP/s of 4 D flops per visible (row, key) pair)."""
+    import oracle
+    t0 = time.perf_counter()
+    oracle.varlen_prefill(c.q, c.cu_seqlens_q, c.cu_seqlens_k, c.sink, c.sm_scale, c.Hkv,
+                          k=c.k, v=c.v, k_cache=c.k_cache, v_cache=c.v_cache,
+                          block_table=c.block_table, block_size=c.block_size,
+                          window_left=c.window_left, units=units, nthreads=threads)
+    dt = time.perf_counter() - t0
+    vis = []
+    for Lq, Lk in zip(c.q_lens, c.k_lens):
+        pos = np.arange(Lk - Lq, Lk, dtype=np.int64)
+        hi = np.minimum(pos, Lk - 1)
+        lo = np.zeros_like(pos) if c.window_left < 0 else np.maximum(0, pos - c.window_left)
+        vis.append(np.maximum(0, hi - lo + 1))
+    vis = np.concatenate(vis)
+    u = np.arange(len(vis) * c.Hq) if units is None else np.asarray(units)
+    flops = float(np.sum(vis[u // c.Hq])) * 4 * c.D
+    return dt, flops / dt / 1e9
+
+
+def cpu_baseline(kind, c, n_all, n_one, seed, what):
+    """The oracle as it stands, timed at all host threads and at one thread on
+    bounded samples of the workload: kind 'decode' (GB/s) or 'prefill'
+    (GFLOP/s).  n_all / n_one: units timed at each thread count (None: all)."""
+    n = host_threads()
+    units_total = c.B * c.Hq if kind == "decode" else c.q.shape[0] * c.Hq
+    res = {"kind": "oracle", "unit": "GB/s" if kind == "decode" else "GFLOP/s", "cores": n}
+    out = None
+    for label, threads, k, sd in (("all_cores", n, n_all, seed), ("one_thread", 1, n_one, seed + 1)):
+        units = None if k is None else _sample(units_total, k, sd)
+        if kind == "decode":
+            dt, rate, o = oracle_decode_rate(c, units, threads)
+            if units is None and label == "all_cores":
+                out = o
+        else:
+            dt, rate = oracle_prefill_rate(c, units, threads)
+        res[label] = {"threads": threads, "seconds": round(dt, 3), "value": round(rate, 4),
+                      "units": units_total if units is None else int(len(units))}
+    res["value"] = res["all_cores"]["value"]
+    res["sample"] = (f"{what}: {res['all_cores']['units']} of {units_total} "
+                     f"({'sequence' if kind == 'decode' else 'token'}, head) units at {n} threads, "
+                     f"{res['one_thread']['units']} at one thread (seeded); fp64 two-pass oracle")
+    return res, out
 
 
 def spot_check(out, want, units, Hq, what):
@@ -526,6 +586,9 @@ def main():
                               with_cache_write=True, traffic_key="prefill_c3")
         workloads["varlen_prefill"] = r3
         log(f"prefill: {r3['value']} TFLOP/s")
+        if not ARGS.no_cpu_baseline:
+            r3["cpu_baseline"], _ = cpu_baseline("prefill", c3, 32768, 4096, 30,
+                                                 "the 8-request prefill workload")
         r3a, _ = bench_prefill(c3, "varlen_prefill_8x_U256-4096_alibi", steps, warmup, reps=2,
                                alibi=alibi_slopes(c3.Hq))
         workloads["varlen_prefill_alibi"] = r3a
@@ -545,9 +608,15 @@ def main():
     if ARGS.only in ("all", "chunked"):
         log("chunked prefill workload (4 x 512 q on 8704 paged keys, window 128, 64/8, D 64)")
         c4 = synth.config4_chunked(poison=False, spare_blocks=0)
-        r4, _ = bench_prefill(c4, "chunked_prefill_4x512_on_8704_w128", steps, warmup, reps=8,
+        # 48 replicas of q and the pool: ~1 GiB of touched bytes, so no step finds
+        # its inputs in the 256 MB last-level cache
+        r4, _ = bench_prefill(c4, "chunked_prefill_4x512_on_8704_w128", steps, warmup, reps=48,
                               traffic_key="prefill_c4")
+        r4["replicas"] = 48
         workloads["chunked_prefill"] = r4
+        if not ARGS.no_cpu_baseline:
+            r4["cpu_baseline"], _ = cpu_baseline("prefill", c4, None, 16384, 40,
+                                                 "the chunked-prefill workload")
         log(f"chunked: {r4['value']} TFLOP/s, {r4['hbm_gbs']} GB/s")
     if ARGS.only in ("all", "longctx") and not ARGS.skip_long:
         log("long-context decode workload (16 x 131072, bs 64, partitions of 512, sink)")
@@ -559,6 +628,9 @@ def main():
         r5b, _ = bench_decode(c5, "split_decode_16x131072_auto", max(3, steps // 4), 2, 0,
                               reps=1)
         workloads["split_decode_long_auto"] = r5b
+        if not ARGS.no_cpu_baseline:
+            r5["cpu_baseline"], _ = cpu_baseline("decode", c5, 256, 16, 50,
+                                                 "the long-context decode workload")
         log(f"long decode: {r5['value']} GB/s (P=512), {r5b['value']} GB/s (auto)")
         del c5
     if ARGS.copy_calibration_mb:
@@ -587,7 +659,7 @@ def main():
                      "frac_of_hbm_peak_step": head["frac_of_hbm_peak_step"]})
         if not ARGS.no_cpu_baseline:
             log("timing the fp64 oracle on the host cores")
-            cb, o2 = cpu_baseline_decode(c2, head["algorithmic_bytes"])
+            cb, o2 = cpu_baseline("decode", c2, None, None, 20, "the full headline workload")
             line["cpu_baseline"] = cb
             rng = np.random.default_rng(0)
             units = rng.choice(c2.B * c2.Hq, 64, replace=False)

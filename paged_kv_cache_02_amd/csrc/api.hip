@@ -68,16 +68,15 @@ int device_cus() {
     return cached[dev];
 }
 
-// Balanced schedule: one 4-wave workgroup (one wave per SIMD) per compute
-// unit, spread over the head groups.  With two per unit the one dispatched
-// second gets its memory requests served only after the first has finished
-// (a timeline probe showed its first tile arriving ~50 us into a ~120 us
-// launch), so the two ran one after the other and the second one's spread
-// of end times set the launch time; one per unit measured 5 % faster on the
-// 64-sequence workload.
-int stream_wgs_per_head_group(int Hq, int Hkv) {
-    const int NHG = Hq / decode_heads_per_unit(Hq / Hkv);
-    return std::max(1, (device_cus() + NHG - 1) / NHG);
+// Balanced schedule: one workgroup of kStreamWaves waves (two per SIMD) per
+// compute unit, the waves of a workgroup on the head groups of one token
+// range; K ranges per head group.
+int stream_ranges_hu(int Hq, int HU) {
+    const int NHG = Hq / HU;
+    return std::max(1, (device_cus() * kStreamWaves + NHG - 1) / NHG);
+}
+int stream_ranges_per_head_group(int Hq, int Hkv) {
+    return stream_ranges_hu(Hq, decode_heads_per_unit(Hq / Hkv));
 }
 
 // Decode workspace.  Its first counter_bytes(Hq) bytes hold the fused
@@ -93,9 +92,7 @@ struct StreamLayout {
     size_t counters, part_out, part_lse, cum, total;
 };
 StreamLayout stream_layout_hu(int32_t B, int32_t Hq, int HU, int32_t D) {
-    const int NHG = Hq / HU;
-    const size_t W = (size_t)std::max(1, (device_cus() + NHG - 1) / NHG);
-    const size_t slots = W * 4 + B;
+    const size_t slots = (size_t)stream_ranges_hu(Hq, HU) + B;
     StreamLayout l;
     l.counters = 0;
     l.part_out = counter_bytes(Hq);
@@ -130,7 +127,7 @@ StreamArgs stream_args(const void *q, const void *k_cache, const void *v_cache,
     a.seqlens = cache_seqlens; a.B = B; a.Hq = Hq; a.Hkv = Hkv;
     a.G = Hq / Hkv; a.D = D; a.bs_log2 = ilog2(block_size);
     a.mbps = mbps; a.window_left = window_left; a.alibi = alibi;
-    a.W = stream_wgs_per_head_group(Hq, Hkv);
+    a.K = stream_ranges_per_head_group(Hq, Hkv);
     a.scale_log2 = sm_scale * kLog2e;
     a.epoch = next_epoch();
     return a;
@@ -180,6 +177,15 @@ pkv_status launch_decode_stage(void *out, float *lse, float *part_out, float *pa
                                pkv_dtype dtype,
                                hipStream_t s)
 {
+    if (dtype == PKV_BF16 && plan.split && B <= kStreamMaxB) {
+        // fixed partitions through the balanced stream: whole partitions per
+        // wave, each written straight to part_out / part_lse
+        StreamArgs a = stream_args(q, k_cache, v_cache, block_table, cache_seqlens, B, Hq, Hkv, D,
+                                   block_size, mbps, sm_scale, window_left, alibi, nullptr);
+        a.part_out = part_out; a.part_lse = part_lse; a.cum_out = nullptr;
+        a.mode = kStreamParts; a.part_size = plan.part_size; a.max_parts = plan.nparts;
+        return launch_decode_stream_bf16(a, s);
+    }
     if (dtype == PKV_BF16) {
         DecodeArgs a{};
         a.out = out; a.lse = lse; a.part_out = part_out; a.part_lse = part_lse;
@@ -238,6 +244,7 @@ pkv_status decode_launch(const DecodeCall &c, void *workspace) {
         const StreamLayout lay = stream_layout(c.B, c.Hq, c.Hkv, c.D);
         a.counters = (uint64_t *)((char *)workspace + lay.counters);
         a.out = c.out; a.lse = c.lse; a.sink = c.sink;
+        a.mode = kStreamFused;
         return launch_decode_stream_bf16(a, s);
     }
     const SplitPlan plan = plan_split(c.max_seqlen_k, c.partition_size);
@@ -451,6 +458,7 @@ pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const v
         a.counters = (uint64_t *)((char *)workspace + lay.counters);
         a.out = out; a.lse = lse; a.sink = sink;
         a.k_new = k_new; a.v_new = v_new; a.append = 1;
+        a.mode = kStreamAppend;
         return launch_decode_stream_bf16(a, s);
     }
     RowArgs a{};

@@ -24,13 +24,23 @@ struct DecodeArgs {
 };
 
 // Balanced decode schedule (decode_stream_kernel): the 16-token tiles of all
-// sequences of a head group laid end to end and cut into equal contiguous
-// ranges, one per wave.  Wave gw's partial result for sequence b goes to slot
-// gw + b (unique: a wave's range moves forward through the sequences).
+// sequences laid end to end (the same list for every head group) and cut into
+// K equal contiguous ranges per head group, one per wave.  A workgroup of
+// kStreamWaves waves takes consecutive (head group, range) pairs, head group
+// fastest, so its waves read the columns of the same token rows together.
+// Range k's partial result for sequence b goes to slot k + b (unique: a
+// range moves forward through the sequences).
+constexpr int kStreamWaves = 4;
+// What a stream launch computes: per-range pieces for the merge kernel
+// (stage), final outputs with the merge fused in (fused), the same with each
+// sequence's new token appended first (append), or fixed partitions of
+// part_size tokens written to part_out / part_lse, each partition wholly in
+// one wave's range (parts).
+enum { kStreamStage = 0, kStreamFused = 1, kStreamAppend = 2, kStreamParts = 3 };
 constexpr int kStreamMaxB = 4096;
 
 struct StreamArgs {
-    float *part_out;             // [slots, Hq, D], slots = W*4 + B
+    float *part_out;             // [slots, Hq, D], slots = K + B (parts mode: see below)
     float *part_lse;             // [slots, Hq]
     int32_t *cum_out;            // [B + 2]: tile prefix sums, then the per-wave chunk
     // Fused merge (counters != null): the last wave to finish a (sequence,
@@ -55,9 +65,12 @@ struct StreamArgs {
     const void *k_new;
     const void *v_new;
     int32_t append;              // 0 or 1
+    int32_t mode;                // kStream*
+    // parts mode: part_out [B, Hq, max_parts, D] / part_lse [B, Hq, max_parts]
+    int32_t part_size, max_parts;
     int32_t B, Hq, Hkv, G, D;
     int32_t bs_log2, mbps, window_left;
-    int32_t W;                   // workgroups (of 4 waves) per head group
+    int32_t K;                   // ranges (waves) per head group
     float scale_log2;
 };
 
@@ -73,14 +86,17 @@ __device__ __forceinline__ int stream_tiles(int L, int window_left) {
 __device__ __forceinline__ int stream_chunk(int T, int nwaves) {
     return max(1, (T + nwaves - 1) / nwaves);
 }
-// Block-wide (256 threads): s_cum[b] = tiles of sequences 0..b-1, b <= B.
+// Block-wide (NT threads): s_cum[b] = tiles of sequences 0..b-1, b <= B.
 // The key counts seqlens[b] + add are kept in s_len[b] (the lengths are read
 // from global memory once; add = 1 counts an appended token).
+template <int NT>
 __device__ __forceinline__ void stream_prefix_tiles(const int32_t *seqlens, int add, int B,
                                                     int window_left, int *s_cum, int *s_part,
                                                     int *s_len) {
+    static_assert(NT % 64 == 0 && NT <= 1024, "whole waves");
+    constexpr int PL = NT / 64;       // strip sums per lane of the scanning wave
     const int tid = threadIdx.x;
-    const int per = (B + 255) / 256;
+    const int per = (B + NT - 1) / NT;
     const int b0 = tid * per;
     int sum = 0;
     for (int b = b0; b < min(b0 + per, B); ++b) {
@@ -90,11 +106,14 @@ __device__ __forceinline__ void stream_prefix_tiles(const int32_t *seqlens, int 
     }
     s_part[tid] = sum;
     __syncthreads();
-    if (tid < 64) {   // exclusive scan of the 256 strip sums by one wave
-        int x[4];
+    if (tid < 64) {   // exclusive scan of the NT strip sums by one wave
+        int x[PL];
+        int mine = 0;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) x[u] = s_part[4 * tid + u];
-        const int mine = x[0] + x[1] + x[2] + x[3];
+        for (int u = 0; u < PL; ++u) {
+            x[u] = s_part[PL * tid + u];
+            mine += x[u];
+        }
         int incl = mine;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -103,8 +122,8 @@ __device__ __forceinline__ void stream_prefix_tiles(const int32_t *seqlens, int 
         }
         int run = incl - mine;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            s_part[4 * tid + u] = run;
+        for (int u = 0; u < PL; ++u) {
+            s_part[PL * tid + u] = run;
             run += x[u];
         }
     }
@@ -114,7 +133,7 @@ __device__ __forceinline__ void stream_prefix_tiles(const int32_t *seqlens, int 
         s_cum[b] = run;
         run += stream_tiles(s_len[b], window_left);
     }
-    if (tid == 255) s_cum[B] = run;   // strip 255 ends at B (B <= 256 * per)
+    if (tid == NT - 1) s_cum[B] = run;   // the last strip ends at B (B <= NT * per)
     __syncthreads();
 }
 

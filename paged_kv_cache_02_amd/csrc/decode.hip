@@ -214,18 +214,35 @@ struct DecodeWave {
     // Sum the state over the lanes that hold the same (head, dims): afterwards
     // lanes with j == 0 (and r < 8 for D = 64) hold acc for dims d0()..d0()+7,
     // and the returned sum of p is complete in lanes r < HU (for head r).
+    // x + x^16 and x + x^32 (lane index xor 16 / 32) with the VALU lane swaps
+    // of gfx950: permlane16_swap(x, x) returns the even and the odd 16-lane
+    // rows of each pair side by side, permlane32_swap(x, x) the two halves
+    // of the wave, so the two results summed give the pairwise sum in every
+    // lane (no LDS permute)
+    static __device__ __forceinline__ float sum_xor16(float x) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                         false, false);
+        return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    static __device__ __forceinline__ float sum_xor32(float x) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                         false, false);
+        return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    // x + x^8 within each 16-lane row (DPP row rotate by 8)
+    static __device__ __forceinline__ float sum_xor8(float x) {
+        return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf,
+                                                              0xf, false));
+    }
     __device__ float reduce() {
-        float lsum = l_lane + shfl_xor(l_lane, 16);
-        lsum += shfl_xor(lsum, 32);
+        const float lsum = sum_xor32(sum_xor16(l_lane));
 #pragma unroll
         for (int hh = 0; hh < HU; ++hh)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float x = acc[hh][e];
-                if (D == 64) x += shfl_xor(x, 8);
-                x += shfl_xor(x, 16);
-                x += shfl_xor(x, 32);
-                acc[hh][e] = x;
+                if (D == 64) x = sum_xor8(x);
+                acc[hh][e] = sum_xor32(sum_xor16(x));
             }
         return lsum;
     }
@@ -463,31 +480,80 @@ __device__ void stream_merge_wave(const StreamArgs &a, int b, int h0, int s0, in
     if (a.lse && d == 0) a.lse[(size_t)b * a.Hq + h] = lse_v;
 }
 
-template <int D, int HU, bool FUSED, bool APPEND, bool ALIBI>
-__global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
+template <int D, int HU, int MODE, bool ALIBI>
+__global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(StreamArgs a)
 {
+    constexpr bool FUSED = MODE == kStreamFused || MODE == kStreamAppend;
+    constexpr bool APPEND = MODE == kStreamAppend;
+    constexpr bool PARTS = MODE == kStreamParts;
+    constexpr int NT = 64 * kStreamWaves;
     __shared__ int s_cum[kStreamMaxB + 1];   // tiles of the sequences before b
     __shared__ int s_len[kStreamMaxB];       // cache_seqlens
-    __shared__ int s_part[256];
+    __shared__ int s_part[NT];
+    // partitions mode: each wave stages up to kStage partition results and
+    // writes them in one burst (rows of consecutive partitions of a head are
+    // contiguous), so the few writes do not trickle through the read stream
+    constexpr int kStage = 8;
+    __shared__ __attribute__((aligned(16))) float s_stage[PARTS ? kStreamWaves : 1]
+                                                         [PARTS ? kStage * HU * D : 1];
+    __shared__ float s_stage_lse[PARTS ? kStreamWaves : 1][PARTS ? kStage * HU : 1];
 
     const int tid = threadIdx.x;
     const int wave = readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     const int NHG = a.Hq / HU;
-    const int hg = blockIdx.x % NHG;
-    const int wg = blockIdx.x / NHG;
-    const int W = gridDim.x / NHG;                 // workgroups per head group
+    // (head group, range) of this wave: head group fastest, so the waves of a
+    // workgroup stream the columns of the same token rows at the same time
+    // (one compute unit reads whole token rows, whatever speed each column's
+    // addresses get from the memory system)
+    const int gwid = readfirstlane((int)blockIdx.x * kStreamWaves + wave);
+    const int hg = gwid % NHG;
+    const int k = gwid / NHG;                     // this wave's range
     const int h0 = hg * HU;
     const int g = h0 / a.G;
 
-    static_assert(FUSED || !APPEND, "the append runs with the fused merge");
-    stream_prefix_tiles(a.seqlens, APPEND ? 1 : 0, a.B, a.window_left, s_cum, s_part, s_len);
+    stream_prefix_tiles<NT>(a.seqlens, APPEND ? 1 : 0, a.B, a.window_left, s_cum, s_part, s_len);
     const int T = s_cum[a.B];
-    const int nw = W * kWaves;
-    const int chunk = stream_chunk(T, nw);
-    if (FUSED) {
-        // sequences without tiles: zero output, lse = sink (or -inf)
-        if (wg == 0) {
-            for (int idx = tid; idx < a.B * HU; idx += 256) {
+    const int chunk = stream_chunk(T, a.K);
+    if (k >= a.K) return;                         // a padding wave of the last workgroup
+    // the sequence that holds flattened tile x < T: s_cum[b] <= x < s_cum[b+1]
+    auto seq_of = [&](int x) {
+        int lo = 0, hi = a.B;                     // s_cum[lo] <= x < s_cum[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_cum[mid] <= x) lo = mid; else hi = mid;
+        }
+        return lo;
+    };
+    const int P = a.part_size;                    // partitions mode: tokens per partition
+    if (PARTS) {
+        // Partitions with no tile in the list (left of the window, past the
+        // sequence, or of an empty sequence): output 0 and lse -inf, written
+        // by the range-0 wave of each head group.
+        if (k == 0) {
+            for (int b = lane; b < a.B; b += 64) {
+                const int L = s_len[b];
+                // partitions [pf, pl] of b have tiles; the others are empty
+                const int pf = L > 0 ? stream_lo(L, a.window_left) / P : a.max_parts;
+                const int pl = L > 0 ? (L - 1) / P : a.max_parts - 1;
+                for (int pp = 0; pp < a.max_parts; ++pp) {
+                    if (pp == pf) pp = pl + 1;
+                    if (pp >= a.max_parts) break;
+                    for (int hh = 0; hh < HU; ++hh) {
+                        const size_t row = ((size_t)b * a.Hq + h0 + hh) * a.max_parts + pp;
+                        for (int d = 0; d < D; d += 4)
+                            *reinterpret_cast<f32x4 *>(a.part_out + row * D + d) =
+                                f32x4{0.f, 0.f, 0.f, 0.f};
+                        a.part_lse[row] = -INFINITY;
+                    }
+                }
+            }
+        }
+    } else if (FUSED) {
+        // sequences without tiles: zero output, lse = sink (or -inf); the
+        // range-0 wave of each head group writes them
+        if (k == 0) {
+            for (int idx = lane; idx < a.B * HU; idx += 64) {
                 const int b = idx / HU, h = h0 + idx % HU;
                 if (s_cum[b + 1] != s_cum[b]) continue;
                 uint16_t *po = (uint16_t *)a.out + ((size_t)b * a.Hq + h) * D;
@@ -496,33 +562,45 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
                 if (a.lse) a.lse[(size_t)b * a.Hq + h] = a.sink ? a.sink[h] : -INFINITY;
             }
         }
-    } else if (blockIdx.x == 0) {
-        for (int b = tid; b <= a.B; b += 256) a.cum_out[b] = s_cum[b];
-        if (tid == 0) a.cum_out[a.B + 1] = chunk;
+    } else if (gwid == 0) {
+        for (int b = lane; b <= a.B; b += 64) a.cum_out[b] = s_cum[b];
+        if (lane == 0) a.cum_out[a.B + 1] = chunk;
     }
 
-    const int gw = wg * kWaves + wave;            // wave index within the head group
-    const int x0 = min(T, gw * chunk);
-    const int n = min(T, x0 + chunk) - x0;        // tiles of this wave
+    const int gw = k;                             // slot base of this range
+    int x0 = min(T, gw * chunk);
+    int n = min(T, x0 + chunk) - x0;              // tiles of this wave
+    if (PARTS) {
+        // whole partitions per wave: both ends of the range move up to the
+        // next partition start (a sequence start, or a token multiple of P)
+        auto snap = [&](int x) {
+            if (x >= T) return T;
+            const int b = seq_of(x);
+            if (x == s_cum[b]) return x;
+            const int lo_al = stream_lo(s_len[b], a.window_left) & ~15;
+            const int t = lo_al + 16 * (x - s_cum[b]);
+            if (t % P == 0) return x;
+            return min(s_cum[b] + ((t / P + 1) * P - lo_al) / 16, s_cum[b + 1]);
+        };
+        const int x1 = snap(min(T, (gw + 1) * chunk));
+        x0 = snap(x0);
+        n = x1 - x0;
+    }
     if (n <= 0) return;
 
     DecodeWave<D, HU, ALIBI> w;
     w.setup(g, a.Hkv, a.scale_log2, a.alibi, h0);
     const int bs_mask = (1 << a.bs_log2) - 1;
 
-    // the sequence that holds flattened tile x0: s_cum[b] <= x0 < s_cum[b+1]
-    int b_ld;
-    {
-        int lo = 0, hi = a.B;                     // s_cum[lo] <= x0 < s_cum[hi]
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (s_cum[mid] <= x0) lo = mid; else hi = mid;
-        }
-        b_ld = readfirstlane(lo);
-    }
+    // the sequence that holds flattened tile x0
+    int b_ld = readfirstlane(seq_of(x0));
     int L_ld = readfirstlane(s_len[b_ld]);
     int t_ld = readfirstlane((stream_lo(L_ld, a.window_left) & ~15) + 16 * (x0 - s_cum[b_ld]));
     int x_ld = x0;                                // flattened index of the cursor's tile
+    // partitions mode: the cursor tile's partition and the token where the
+    // next one starts, kept up to date without a division per tile
+    int p_ld = PARTS ? t_ld / P : 0;
+    int pb_ld = PARTS ? (p_ld + 1) * P : 0;
     // advance the load cursor by one tile, skipping sequences with no tiles
     auto advance = [&]() {
         t_ld += 16;
@@ -533,7 +611,14 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
             if (b_ld < a.B) {
                 L_ld = readfirstlane(s_len[b_ld]);
                 t_ld = stream_lo(L_ld, a.window_left) & ~15;
+                if (PARTS) {
+                    p_ld = readfirstlane(t_ld / P);
+                    pb_ld = (p_ld + 1) * P;
+                }
             }
+        } else if (PARTS && t_ld >= pb_ld) {
+            ++p_ld;
+            pb_ld += P;
         }
     };
     // Block ids of this wave's tiles, 64 at a time: lane i of a batch holds
@@ -541,7 +626,6 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
     // dependent memory load per tile queued behind the K/V stream (that
     // dependency, not bandwidth, limited short-context decode).  The first
     // batch is read before any tile load; later ones 64 tiles ahead.
-    const int lane = tid & 63;
     const int x_end = x0 + n;
     auto gather = [&](int xs) {
         const int x = xs + lane;
@@ -597,12 +681,79 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
     auto pieces = [&](int b) { return (s_cum[b + 1] - 1) / chunk - s_cum[b] / chunk + 1; };
     auto first_slot = [&](int b) { return s_cum[b] / chunk + b; };
 
-    int seg_b = -1, seg_lo = 0, seg_hi = 0;
+    int seg_b = -1, seg_p = 0, seg_lo = 0, seg_hi = 0;
+    // partitions mode: results staged in s_stage[wave], lane i of staged_row
+    // holding b * max_parts + p of slot i
+    int n_staged = 0, staged_row = 0;
+    auto write_staged = [&]() {
+        if (!PARTS || n_staged == 0) return;
+        // the stage was written by other lanes of this wave: make those LDS
+        // writes complete and visible before reading them back
+        __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        constexpr int C4 = D / 4;                 // 16-byte chunks per row
+        // rows (slot i, head hh) in order hh-major: consecutive partitions of
+        // one head sit next to each other in part_out.  Every lane runs every
+        // iteration (the shuffles read lanes 0 .. n_staged-1); only the
+        // stores are guarded.
+        const int total = HU * n_staged * C4;
+        for (int base = 0; base < total; base += 64) {
+            const int e = min(base + lane, total - 1);
+            const int c = e % C4, i = (e / C4) % n_staged, hh = e / (C4 * n_staged);
+            const int bp = __shfl(staged_row, i, 64);
+            if (base + lane < total) {
+                const int b = bp / a.max_parts, pp = bp % a.max_parts;
+                const size_t row = ((size_t)b * a.Hq + h0 + hh) * a.max_parts + pp;
+                *reinterpret_cast<f32x4 *>(a.part_out + row * D + 4 * c) =
+                    *reinterpret_cast<const f32x4 *>(s_stage[wave] + (i * HU + hh) * D + 4 * c);
+            }
+        }
+        {
+            const int li = min(lane, HU * n_staged - 1);
+            const int bp = __shfl(staged_row, li / HU, 64);
+            if (lane < HU * n_staged) {
+                const int b = bp / a.max_parts, pp = bp % a.max_parts;
+                a.part_lse[((size_t)b * a.Hq + h0 + li % HU) * a.max_parts + pp] =
+                    s_stage_lse[wave][li];
+            }
+        }
+        // the next stage writes must not overtake these reads
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        n_staged = 0;
+    };
     // sequences whose pieces this wave wrote but has not counted yet: only the
     // first and the last sequence of a range can be shared with other waves
     int shared_a = -1, shared_b = -1;
     auto flush = [&]() {
         const float lsum = w.reduce();
+        if (PARTS) {
+            // partition (seg_b, seg_p) is this wave's alone: its normalised
+            // output and lse (sink left out), staged for the next burst
+            float *st = s_stage[wave] + n_staged * HU * D;
+#pragma unroll
+            for (int hh = 0; hh < HU; ++hh) {
+                const float lh = __shfl(lsum, hh, 64);
+                const float inv = lh > 0.f ? 1.f / lh : 0.f;
+                if (w.holds_acc()) {
+                    float *ps = st + hh * D + w.d0();
+                    *reinterpret_cast<f32x4 *>(ps) = f32x4{w.acc[hh][0] * inv, w.acc[hh][1] * inv,
+                                                           w.acc[hh][2] * inv, w.acc[hh][3] * inv};
+                    *reinterpret_cast<f32x4 *>(ps + 4) = f32x4{w.acc[hh][4] * inv,
+                                                               w.acc[hh][5] * inv,
+                                                               w.acc[hh][6] * inv,
+                                                               w.acc[hh][7] * inv};
+                }
+            }
+            if (w.j == 0 && w.r < HU)
+                s_stage_lse[wave][n_staged * HU + w.r] =
+                    lsum > 0.f ? w.m_lane * kLn2 + logf(lsum) : -INFINITY;
+            // (b, p) of the staged slot, kept in lane n_staged of a VGPR
+            if (lane == n_staged) staged_row = seg_b * a.max_parts + seg_p;
+            if (++n_staged == kStage) write_staged();
+            return;
+        }
         if (FUSED && pieces(seg_b) == 1) {
             // the whole sequence was this wave's: final result with the sink
 #pragma unroll
@@ -696,12 +847,14 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
     }
     u32x4 kbuf[kRing][DecodeWave<D, HU>::KSTEPS], vbuf[kRing][DecodeWave<D, HU>::VLD];
     int rb[kRing], rt[kRing];                     // (sequence, first token) of each ring slot
+    int rp[kRing];                                // partitions mode: partition of each slot
     const int n_pad = (n + kRing - 1) / kRing * kRing;
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) {
         const bool live = k < n;
         rb[k] = b_ld;
         rt[k] = t_ld;
+        if (PARTS) rp[k] = p_ld;
         w.load(a.k_cache, a.v_cache, live ? row_off(block_at(), t_ld) : 0, live, kbuf[k],
                vbuf[k]);
         if (k + 1 < n) advance();
@@ -719,6 +872,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
             const bool live_n = nxt < n;
             rb[slot] = b_ld;
             rt[slot] = t_ld;
+            if (PARTS) rp[slot] = p_ld;
             w.load(a.k_cache, a.v_cache, live_n ? row_off(blk_next, t_ld) : 0, live_n,
                    kbuf[slot], vbuf[slot]);
             if (nxt + 1 < n) {
@@ -727,12 +881,18 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
             }
             __builtin_amdgcn_sched_barrier(0);
             if (cur < n) {
-                if (rb[k] != seg_b) {                 // entering a new sequence
+                const int pk = PARTS ? rp[k] : 0;
+                if (rb[k] != seg_b || (PARTS && pk != seg_p)) {   // a new sequence (or partition)
                     if (seg_b >= 0) flush();
                     seg_b = rb[k];
+                    seg_p = pk;
                     const int L = s_len[seg_b];
                     seg_lo = stream_lo(L, a.window_left);
                     seg_hi = L;
+                    if (PARTS) {
+                        seg_lo = max(seg_lo, pk * P);
+                        seg_hi = min(L, (pk + 1) * P);
+                    }
                     w.qpos = L - 1;
                     if (seg_b != q_held) {
                         if (seg_b == q_nb) {
@@ -754,6 +914,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs a)
         }
     }
     if (seg_b >= 0) flush();
+    write_staged();
     if (FUSED && shared_a >= 0) {
         // Count this wave's shared pieces once its stream is over (the
         // pieces are complete first), so the stream itself never waits on a
@@ -808,15 +969,20 @@ void launch_part(const DecodeArgs &a, int grid, hipStream_t stream) {
 // plain product for the scaled logit.
 template <int D, int HU, bool ALIBI>
 void launch_stream_al(const StreamArgs &a, int grid, hipStream_t stream) {
-    if (a.counters && a.append)
-        hipLaunchKernelGGL((decode_stream_kernel<D, HU, true, true, ALIBI>), dim3(grid), dim3(256),
-                           0, stream, a);
-    else if (a.counters)
-        hipLaunchKernelGGL((decode_stream_kernel<D, HU, true, false, ALIBI>), dim3(grid),
-                           dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL((decode_stream_kernel<D, HU, false, false, ALIBI>), dim3(grid),
-                           dim3(256), 0, stream, a);
+    const dim3 g(grid), b(64 * kStreamWaves);
+    switch (a.mode) {
+        case kStreamAppend:
+            hipLaunchKernelGGL((decode_stream_kernel<D, HU, kStreamAppend, ALIBI>), g, b, 0, stream, a);
+            break;
+        case kStreamFused:
+            hipLaunchKernelGGL((decode_stream_kernel<D, HU, kStreamFused, ALIBI>), g, b, 0, stream, a);
+            break;
+        case kStreamParts:
+            hipLaunchKernelGGL((decode_stream_kernel<D, HU, kStreamParts, ALIBI>), g, b, 0, stream, a);
+            break;
+        default:
+            hipLaunchKernelGGL((decode_stream_kernel<D, HU, kStreamStage, ALIBI>), g, b, 0, stream, a);
+    }
 }
 template <int D, int HU>
 void launch_stream(const StreamArgs &a, int grid, hipStream_t stream) {
@@ -849,7 +1015,7 @@ pkv_status launch_decode_bf16(const DecodeArgs &a, hipStream_t stream)
 pkv_status launch_decode_stream_bf16(const StreamArgs &a, hipStream_t stream)
 {
     const int HU = decode_heads_per_unit(a.G);
-    const long long grid = (long long)a.W * (a.Hq / HU);
+    const long long grid = ((long long)a.K * (a.Hq / HU) + kStreamWaves - 1) / kStreamWaves;
     if (a.B == 0 || grid <= 0) return PKV_OK;
     if (a.B > kStreamMaxB || grid > 0x7fffffffLL) return PKV_ERR_SHAPE;
     if (a.D == 128) {

@@ -24,6 +24,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 CUS = 256          # compute units the decode schedule is sized for
+STREAM_WAVES = 4   # waves per workgroup of the balanced decode schedule
 BN = 64            # prefill keys per tile
 BM = 128           # prefill positions per workgroup tile
 
@@ -141,8 +142,13 @@ def model_decode_stream(lens, Hq, Hkv, bs, mbps, window=-1, append=False):
     assert bs >= 16 and bs % 16 == 0, "a 16-token tile must lie inside one block"
     HU = heads_per_unit(Hq // Hkv)
     NHG = Hq // HU
-    W = max(1, (CUS + NHG - 1) // NHG)
-    nw = 4 * W
+    K = max(1, (CUS * STREAM_WAVES + NHG - 1) // NHG)   # ranges (waves) per head group
+    nw = K
+    # the grid: ceil(NHG * K / 8) workgroups of 8 waves, head group fastest
+    grid = (NHG * K + STREAM_WAVES - 1) // STREAM_WAVES
+    gwid = np.arange(grid * STREAM_WAVES)
+    assert set(zip((gwid % NHG)[gwid // NHG < K].tolist(), (gwid // NHG)[gwid // NHG < K].tolist())) \
+        == {(h, k) for h in range(NHG) for k in range(K)}, "every (head group, range) has one wave"
     tiles = stream_tiles(L, window)
     cum = np.concatenate([[0], np.cumsum(tiles)])
     T = int(cum[-1])
@@ -157,7 +163,7 @@ def model_decode_stream(lens, Hq, Hkv, bs, mbps, window=-1, append=False):
     assert (t % bs + 16 <= bs).all()
     gw = x // chunk
     assert (gw < nw).all(), "a tile past the last wave"
-    slots = 4 * W + B
+    slots = K + B
     assert (gw + b < slots).all(), "partial-result slot past the workspace"
     # the merge reads pieces(b) consecutive slots from first_slot(b)
     has = tiles > 0
@@ -175,6 +181,53 @@ def model_decode_stream(lens, Hq, Hkv, bs, mbps, window=-1, append=False):
         # the owner of each sequence's last tile stores row L - 1 (the new token)
         pos = L - 1
         assert ((pos >> int(math.log2(bs))) < mbps).all()
+    return T
+
+
+def model_decode_stream_parts(lens, Hq, Hkv, bs, P, max_parts, window=-1):
+    """The balanced schedule in partition mode: each wave's range snapped up to
+    partition starts.  Every tile belongs to exactly one range, every partition
+    with tiles lies wholly in one range, and every part_out row written is
+    inside [B, Hq, max_parts]."""
+    L = np.asarray(lens, dtype=np.int64)
+    B = L.size
+    assert P % 16 == 0 and P % bs == 0
+    HU = heads_per_unit(Hq // Hkv)
+    NHG = Hq // HU
+    K = max(1, (CUS * STREAM_WAVES + NHG - 1) // NHG)
+    tiles = stream_tiles(L, window)
+    cum = np.concatenate([[0], np.cumsum(tiles)])
+    T = int(cum[-1])
+    chunk = max(1, (T + K - 1) // K)
+    lo_al = stream_lo(L, window) & ~15
+
+    def snap(x):
+        if x >= T:
+            return T
+        b = int(np.searchsorted(cum, x, side="right") - 1)
+        if x == cum[b]:
+            return x
+        t = int(lo_al[b]) + 16 * (x - int(cum[b]))
+        if t % P == 0:
+            return x
+        return min(int(cum[b]) + ((t // P + 1) * P - int(lo_al[b])) // 16, int(cum[b + 1]))
+
+    owner = np.full(T, -1)
+    for k in range(K):
+        x0, x1 = snap(min(T, k * chunk)), snap(min(T, (k + 1) * chunk))
+        assert x0 <= x1
+        assert (owner[x0:x1] == -1).all(), "two ranges share a tile"
+        owner[x0:x1] = k
+    assert (owner >= 0).all(), "a tile in no range"
+    x = np.arange(T)
+    b = np.searchsorted(cum, x, side="right") - 1
+    t = lo_al[b] + 16 * (x - cum[b])
+    part = t // P
+    assert (part < max_parts).all(), "part_out row past max_partitions"
+    assert (t < L[b]).all()
+    key = b * max_parts + part
+    for kk in np.unique(key):
+        assert np.unique(owner[key == kk]).size == 1, "a partition split between waves"
     return T
 
 
@@ -277,6 +330,8 @@ def test_decode_partition_mapping_in_bounds():
             continue
         for P in sorted({bs, 2 * bs, 512 if 512 % bs == 0 else bs}):
             model_decode_part(lengths, Hq, Hkv, bs, P, window)
+            maxp = max(1, (max(max(lengths), 1) + P - 1) // P)
+            model_decode_stream_parts(lengths, Hq, Hkv, bs, P, maxp, window)
 
 
 def test_models_catch_a_planted_mistake():
