@@ -639,6 +639,18 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
         a.hpw = prefill_heads_per_wg(a.G);
         a.max_q_tiles = (max_seqlen_q + prefill_block_m() - 1) / prefill_block_m();
         a.scale_log2 = sm_scale * kLog2e;
+        if (window_left >= 0) {
+            // sliding window: workgroups walk runs of position blocks (each
+            // step's keys overlap the last step's), sized for about two
+            // resident workgroups per compute unit
+            const int bm = prefill_block_m() / a.hpw;
+            const long long per_req = (max_seqlen_q + bm - 1) / bm;
+            const long long blocks = (long long)B * per_req * (a.G / a.hpw) * num_kv_heads;
+            const long long steps = std::min<long long>(
+                16, std::max<long long>(1, blocks / (2LL * device_cus())));
+            a.run_steps = (int)steps;
+            a.runs = (int)((per_req + steps - 1) / steps);
+        }
         return launch_prefill_bf16(a, s);
     }
     // fp32: one wave per (request, row < max_seqlen_q, head)

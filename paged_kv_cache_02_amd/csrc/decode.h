@@ -203,6 +203,10 @@ struct PrefillArgs {
     int32_t bs_log2, mbps, window_left;
     int32_t hpw;                 // query heads per workgroup: prefill_heads_per_wg(G)
     int32_t max_q_tiles;         // ceil(max_seqlen_q / prefill_block_m())
+    // runs (sliding windows): each workgroup walks run_steps consecutive
+    // blocks of 128 / hpw positions; runs = ceil(blocks per request /
+    // run_steps).  run_steps == 0: one block per workgroup.
+    int32_t runs, run_steps;
     float scale_log2;
 };
 

@@ -47,6 +47,8 @@
 #include "common.h"
 #include "decode.h"
 
+#include <type_traits>
+
 namespace pkv {
 
 namespace {
@@ -165,8 +167,8 @@ __device__ __forceinline__ void rope_pairs(bf16x8 (&qf)[QK], const float *tab, i
     }
 }
 
-template <int D, bool PAGED, bool ALIBI>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
+template <int D, bool PAGED, bool ALIBI, bool RUN>
+__global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_kernel(PrefillArgs a)
 {
     using TL = Tile<D>;
     constexpr int U = TL::U;
@@ -198,54 +200,86 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
     const int hpw = a.hpw;
     const int bm = 128 / hpw;                       // positions per workgroup
     const int ng = a.G / hpw;                       // head subgroups per kv head
-    const int p = blockIdx.x % a.Hq;
-    const int slot = blockIdx.x / a.Hq;
-    const int g = p % a.Hkv;
-    const int hs = (p / a.Hkv) % ng;
-    const int blk = (hpw - 1 - (p / a.Hkv) / ng + slot) % hpw;   // position block
+    int g, hs, r, blk0, nsteps;                     // blk0: first block of bm positions
+    if constexpr (RUN) {
+        // Runs (sliding-window prefill): workgroup (request, run u, head
+        // subgroup, kv head), kv head fastest so that the subgroups of a kv
+        // head share an XCD's L2; it walks the run_steps consecutive position
+        // blocks of run u, each step's key window overlapping the last one's
+        int id = blockIdx.x;
+        g = id % a.Hkv;
+        id /= a.Hkv;
+        hs = id % ng;
+        id /= ng;
+        const int u = id % a.runs;
+        r = id / a.runs;
+        blk0 = u * a.run_steps;
+        nsteps = a.run_steps;
+    } else {
+        const int p = blockIdx.x % a.Hq;
+        const int slot = blockIdx.x / a.Hq;
+        g = p % a.Hkv;
+        hs = (p / a.Hkv) % ng;
+        const int blk = (hpw - 1 - (p / a.Hkv) / ng + slot) % hpw;   // position block
+        r = slot % a.B;
+        const int qt = a.max_q_tiles - 1 - slot / a.B;
+        blk0 = qt * hpw + blk;
+        nsteps = 1;
+    }
     const int h = g * a.G + hs * hpw + wave % hpw;
-    const int r = slot % a.B;
-    const int qt = a.max_q_tiles - 1 - slot / a.B;
     const int cq0 = a.cu_q[r], Lq = a.cu_q[r + 1] - cq0;
-    if (qt * 128 + blk * bm >= Lq) return;
+    if (blk0 * bm >= Lq) return;
     const int ck0 = a.cu_k[r], Lk = a.cu_k[r + 1] - ck0;
     // the sink logit is needed only at the end: fetch it now, off the tail
     const float sig = a.sink ? a.sink[h] * kLog2e : -INFINITY;
     const float slope_log2 = ALIBI ? a.alibi[h] * kLog2e : 0.f;
-    const int row0 = qt * 128 + blk * bm;           // first row of the workgroup (within request)
-    const int nrows = min(bm, Lq - row0);
-    const int pos0 = Lk - Lq + row0;                // position of the tile's first row
-    const int pos_last = pos0 + nrows - 1;
-    int kv_lo = 0;
-    if (a.window_left >= 0) kv_lo = max(0, pos0 - a.window_left);
-    const int kv_hi = min(Lk, pos_last + 1);        // exclusive
-    const int t_begin = kv_lo & ~(BN - 1);
-    const int ntiles = kv_hi > kv_lo ? (kv_hi - t_begin + BN - 1) / BN : 0;
 
-    // this wave's rows and visible key range
-    const int wrow0 = row0 + 32 * (wave / hpw);
-    const int wrows = max(0, min(32, Lq - wrow0));
-    const int wpos0 = Lk - Lq + wrow0;
-    const int wpos1 = wpos0 + wrows - 1;
-    const int w_lo = a.window_left >= 0 ? max(0, wpos0 - a.window_left) : 0;
-    const int w_hi = min(Lk, wpos1 + 1);
+    // Rows, positions and key range of the workgroup and of this wave at
+    // position block blk0 + s (one step).
+    int row0, nrows, pos0, pos_last, kv_lo, kv_hi, t_begin, ntiles;
+    int wrow0, wrows, wpos0, wpos1, w_lo, w_hi;
+    auto block_keys = [&](int row0_, int &lo_, int &tb_, int &nt_) {
+        const int nr = min(bm, Lq - row0_);
+        const int p0 = Lk - Lq + row0_;
+        lo_ = a.window_left >= 0 ? max(0, p0 - a.window_left) : 0;
+        const int hi_ = min(Lk, p0 + nr);
+        tb_ = lo_ & ~(BN - 1);
+        nt_ = hi_ > lo_ ? (hi_ - tb_ + BN - 1) / BN : 0;
+    };
+    auto set_step = [&](int s) {
+        row0 = (blk0 + s) * bm;                     // first row of the workgroup (within request)
+        nrows = min(bm, Lq - row0);
+        pos0 = Lk - Lq + row0;                      // position of the first row
+        pos_last = pos0 + nrows - 1;
+        block_keys(row0, kv_lo, t_begin, ntiles);
+        kv_hi = min(Lk, pos_last + 1);              // exclusive
+        // this wave's rows and visible key range
+        wrow0 = row0 + 32 * (wave / hpw);
+        wrows = max(0, min(32, Lq - wrow0));
+        wpos0 = Lk - Lq + wrow0;
+        wpos1 = wpos0 + wrows - 1;
+        w_lo = a.window_left >= 0 ? max(0, wpos0 - a.window_left) : 0;
+        w_hi = min(Lk, wpos1 + 1);
+    };
+    set_step(0);
 
     const size_t qstride = (size_t)a.Hq * D;     // elements between tokens of q/out
     const size_t kvstride = (size_t)a.Hkv * D;   // elements between tokens of k/v
 
     // ---- Q^T operand: lane holds row lr, dims 16c + 8lh .. +8 ----
-    bf16x8 qf[QK_STEPS];
-    {
-        const bool ok = lr < wrows;
-        const uint16_t *qp = (const uint16_t *)a.q + (size_t)(cq0 + wrow0 + (ok ? lr : 0)) * qstride +
+    auto load_q = [&](bf16x8 (&dst)[QK_STEPS], int wrow0_, int wrows_) {
+        const bool ok = lr < wrows_;
+        const uint16_t *qp = (const uint16_t *)a.q + (size_t)(cq0 + wrow0_ + (ok ? lr : 0)) * qstride +
                              (size_t)h * D + 8 * lh;
 #pragma unroll
         for (int c = 0; c < QK_STEPS; ++c) {
             u32x4 x = u32x4{0u, 0u, 0u, 0u};
             if (ok) x = *reinterpret_cast<const u32x4 *>(qp + 16 * c);
-            qf[c] = __builtin_bit_cast(bf16x8, x);
+            dst[c] = __builtin_bit_cast(bf16x8, x);
         }
-    }
+    };
+    bf16x8 qf[QK_STEPS];
+    load_q(qf, wrow0, wrows);
 
     // Rotary embedding of the Q rows at their positions (rope_dim a multiple
     // of 32): the neox partner of dims 16c + 8lh + e is register
@@ -481,68 +515,132 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
         }
     };
 
-    if (ntiles > 0) {
-        issue(t_begin, 0);
-        if (a.rope) rotate_q();
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        __syncthreads();
-        for (int it = 0; it < ntiles; ++it) {
-            const int t0 = t_begin + it * BN;
-            if (it + 1 < ntiles) issue(t0 + BN, (it + 1) & 1);
-            if (wrows > 0 && t0 < w_hi && t0 + BN > w_lo) compute(it & 1, t0);
+    // Steps: with RUN, the next step's first K/V tile goes into the free
+    // buffer and its Q into qn during this step's last tile, so a step starts
+    // with both in place and the workgroup pays the load latency once.
+    constexpr int kRowPad = D * 2 + 16;
+    [[maybe_unused]] bf16x8 qn[RUN ? QK_STEPS : 1];
+    int buf = 0;
+    bool prefetched = false;
+    for (int s = 0; s < nsteps; ++s) {
+        if (s > 0) {
+            set_step(s);
+            if (row0 >= Lq) break;
+            if constexpr (RUN) {
+#pragma unroll
+                for (int c = 0; c < QK_STEPS; ++c) qf[c] = qn[c];
+            }
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
+            m = kNoMax;
+            l = 0.f;
+            l1 = 0.f;
+        }
+        // the next step, if this workgroup has one with keys
+        int nx_lo = 0, nx_tb = 0, nx_nt = 0;
+        const int nx_row0 = row0 + bm;
+        const bool has_next = RUN && s + 1 < nsteps && nx_row0 < Lq;
+        if (has_next) block_keys(nx_row0, nx_lo, nx_tb, nx_nt);
+        if (ntiles > 0) {
+            if (!prefetched) issue(t_begin, buf);
+            if (a.rope) rotate_q();
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             __syncthreads();
         }
-    }
-
+        prefetched = false;
+        for (int it = 0; it < ntiles; ++it) {
+            const int t0 = t_begin + it * BN;
+            if (it + 1 < ntiles) {
+                issue(t0 + BN, buf ^ 1);
+            } else if constexpr (RUN) {
+                if (has_next) {
+                    const int nw0 = nx_row0 + 32 * (wave / hpw);
+                    load_q(qn, nw0, max(0, min(32, Lq - nw0)));
+                    if (nx_nt > 0) {
+                        issue(nx_tb, buf ^ 1);
+                        prefetched = true;
+                    }
+                }
+            }
+            if (wrows > 0 && t0 < w_hi && t0 + BN > w_lo) compute(buf, t0);
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __syncthreads();
+            buf ^= 1;
+        }
+        if constexpr (RUN) {
+            // no tile in this step: the next step's Q still has to arrive
+            if (ntiles == 0 && has_next) {
+                const int nw0 = nx_row0 + 32 * (wave / hpw);
+                load_q(qn, nw0, max(0, min(32, Lq - nw0)));
+            }
+        }
     // ---- epilogue: normalise with the sink, write the wave's rows ----
     // The accumulators hold 4 dims of a row per lane, so a direct store would
     // write 32 separate 16-byte pieces per instruction.  Instead each wave
     // stages its 32 rows in LDS (the K/V buffers are free after the last
-    // barrier) and writes whole rows, 16 bytes per lane.  Staged rows are
-    // padded by 16 bytes so that consecutive rows start on different banks.
-    l += l1;
-    l += shfl_xor(l, 32);
-    const float Mt = fmaxf(l > 0.f ? m : kNoMax, sig);
-    const float sc = fast_exp2(m - Mt);
-    const float Lt = l * sc + fast_exp2(sig - Mt);
-    const float f = Lt > 0.f ? sc / Lt : 0.f;
-    constexpr int kRowPad = D * 2 + 16;
-    static_assert(4 * 32 * kRowPad <= 2 * TL::BUF, "staging fits in the K/V buffers");
-    char *stage = lds + wave * 32 * kRowPad;
+    // barrier; with RUN a region of its own, since the next step's first
+    // tile is already in a K/V buffer) and writes whole rows, 16 bytes per
+    // lane.  Staged rows are padded by 16 bytes so that consecutive rows start
+    // on different banks.
+    {
+        float lt = l + l1;
+        lt += shfl_xor(lt, 32);
+        const float Mt = fmaxf(lt > 0.f ? m : kNoMax, sig);
+        const float sc = fast_exp2(m - Mt);
+        const float Lt = lt * sc + fast_exp2(sig - Mt);
+        const float f = Lt > 0.f ? sc / Lt : 0.f;
+        static_assert(4 * 32 * kRowPad <= 2 * TL::BUF, "staging fits in the K/V buffers");
+        char *stage = lds + (RUN ? 2 * TL::BUF : 0) + wave * 32 * kRowPad;
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+        for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int d = 32 * t + 8 * q4 + 4 * lh;
-            const u32x2 w = {pack_bf16x2(o[t][4 * q4] * f, o[t][4 * q4 + 1] * f),
-                             pack_bf16x2(o[t][4 * q4 + 2] * f, o[t][4 * q4 + 3] * f)};
-            *reinterpret_cast<u32x2 *>(stage + lr * kRowPad + d * 2) = w;
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d = 32 * t + 8 * q4 + 4 * lh;
+                const u32x2 w = {pack_bf16x2(o[t][4 * q4] * f, o[t][4 * q4 + 1] * f),
+                                 pack_bf16x2(o[t][4 * q4 + 2] * f, o[t][4 * q4 + 3] * f)};
+                *reinterpret_cast<u32x2 *>(stage + lr * kRowPad + d * 2) = w;
+            }
+        constexpr int LPR = D / 8;      // lanes per row, 16 bytes each
+        constexpr int RPS = 64 / LPR;   // rows per store instruction
+        const int srow = lane / LPR, sunit = lane % LPR;
+        uint16_t *ob = (uint16_t *)a.out + (size_t)(cq0 + wrow0) * qstride + (size_t)h * D;
+#pragma unroll
+        for (int k = 0; k < 32 / RPS; ++k) {
+            const int row = srow + RPS * k;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * kRowPad + sunit * 16);
+            if (row < wrows) *reinterpret_cast<u32x4 *>(ob + (size_t)row * qstride + sunit * 8) = v;
         }
-    constexpr int LPR = D / 8;      // lanes per row, 16 bytes each
-    constexpr int RPS = 64 / LPR;   // rows per store instruction
-    const int srow = lane / LPR, sunit = lane % LPR;
-    uint16_t *ob = (uint16_t *)a.out + (size_t)(cq0 + wrow0) * qstride + (size_t)h * D;
-#pragma unroll
-    for (int k = 0; k < 32 / RPS; ++k) {
-        const int row = srow + RPS * k;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * kRowPad + sunit * 16);
-        if (row < wrows) *reinterpret_cast<u32x4 *>(ob + (size_t)row * qstride + sunit * 8) = v;
+        if (a.lse && lh == 0 && lr < wrows)
+            a.lse[(size_t)(cq0 + wrow0 + lr) * a.Hq + h] = Lt > 0.f ? Mt * kLn2 + logf(Lt) : -INFINITY;
     }
-    if (a.lse && lh == 0 && lr < wrows)
-        a.lse[(size_t)(cq0 + wrow0 + lr) * a.Hq + h] = Lt > 0.f ? Mt * kLn2 + logf(Lt) : -INFINITY;
+    }   // steps
 }
 
 }  // namespace
 
+template <int D>
+constexpr int prefill_lds_bytes(bool run) {
+    return 2 * Tile<D>::BUF + (run ? 4 * 32 * (D * 2 + 16) : 0);
+}
+
 pkv_status launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream)
 {
     if (a.hpw != prefill_heads_per_wg(a.G) || a.Hq % a.hpw) return PKV_ERR_SHAPE;
-    const long long grid = (long long)a.B * a.max_q_tiles * a.Hq;
+    const bool run = a.run_steps > 0;
+    long long grid;
+    if (run) {
+        if (a.runs <= 0) return PKV_ERR_SHAPE;
+        grid = (long long)a.B * a.runs * (a.G / a.hpw) * a.Hkv;
+    } else {
+        grid = (long long)a.B * a.max_q_tiles * a.Hq;
+    }
     if (grid == 0) return PKV_OK;
     if (grid > 0x7fffffffLL) return PKV_ERR_SHAPE;
-    // 64 KiB of dynamic LDS at D 128: raise the per-kernel limit once; a
-    // failure there is reported by every call rather than by a faulting launch
+    // more dynamic LDS than the default limit: raise the per-kernel limit
+    // once; a failure there is reported by every call rather than by a
+    // faulting launch
     static const hipError_t raised = [] {
         hipError_t first = hipSuccess;
         auto set = [&](const void *fn, int bytes) {
@@ -550,39 +648,46 @@ pkv_status launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream)
                 hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
             if (first == hipSuccess) first = e;
         };
-        set((const void *)prefill_bf16_kernel<128, false, false>, 2 * Tile<128>::BUF);
-        set((const void *)prefill_bf16_kernel<128, true, false>, 2 * Tile<128>::BUF);
-        set((const void *)prefill_bf16_kernel<64, false, false>, 2 * Tile<64>::BUF);
-        set((const void *)prefill_bf16_kernel<64, true, false>, 2 * Tile<64>::BUF);
-        set((const void *)prefill_bf16_kernel<128, false, true>, 2 * Tile<128>::BUF);
-        set((const void *)prefill_bf16_kernel<128, true, true>, 2 * Tile<128>::BUF);
-        set((const void *)prefill_bf16_kernel<64, false, true>, 2 * Tile<64>::BUF);
-        set((const void *)prefill_bf16_kernel<64, true, true>, 2 * Tile<64>::BUF);
+#define PKV_SET(DD, PG, AL, RN) \
+        set((const void *)prefill_bf16_kernel<DD, PG, AL, RN>, prefill_lds_bytes<DD>(RN))
+        PKV_SET(128, false, false, false); PKV_SET(128, true, false, false);
+        PKV_SET(64, false, false, false); PKV_SET(64, true, false, false);
+        PKV_SET(128, false, true, false); PKV_SET(128, true, true, false);
+        PKV_SET(64, false, true, false); PKV_SET(64, true, true, false);
+        PKV_SET(128, false, false, true); PKV_SET(128, true, false, true);
+        PKV_SET(64, false, false, true); PKV_SET(64, true, false, true);
+        PKV_SET(128, false, true, true); PKV_SET(128, true, true, true);
+        PKV_SET(64, false, true, true); PKV_SET(64, true, true, true);
+#undef PKV_SET
         return first;
     }();
     if (raised != hipSuccess) return PKV_ERR_HIP;
     const bool paged = a.block_table != nullptr;
     const dim3 g((unsigned)grid), b(256);
     auto go = [&](auto kernel, int lds) { hipLaunchKernelGGL(kernel, g, b, lds, stream, a); };
-    if (a.D == 128) {
-        const int lds = 2 * Tile<128>::BUF;
+    auto pick = [&](auto dtag) {
+        constexpr int DD = decltype(dtag)::value;
+        const int lds = prefill_lds_bytes<DD>(run);
         if (a.alibi) {
-            if (paged) go(prefill_bf16_kernel<128, true, true>, lds);
-            else go(prefill_bf16_kernel<128, false, true>, lds);
+            if (run) {
+                if (paged) go(prefill_bf16_kernel<DD, true, true, true>, lds);
+                else go(prefill_bf16_kernel<DD, false, true, true>, lds);
+            } else {
+                if (paged) go(prefill_bf16_kernel<DD, true, true, false>, lds);
+                else go(prefill_bf16_kernel<DD, false, true, false>, lds);
+            }
         } else {
-            if (paged) go(prefill_bf16_kernel<128, true, false>, lds);
-            else go(prefill_bf16_kernel<128, false, false>, lds);
+            if (run) {
+                if (paged) go(prefill_bf16_kernel<DD, true, false, true>, lds);
+                else go(prefill_bf16_kernel<DD, false, false, true>, lds);
+            } else {
+                if (paged) go(prefill_bf16_kernel<DD, true, false, false>, lds);
+                else go(prefill_bf16_kernel<DD, false, false, false>, lds);
+            }
         }
-    } else {
-        const int lds = 2 * Tile<64>::BUF;
-        if (a.alibi) {
-            if (paged) go(prefill_bf16_kernel<64, true, true>, lds);
-            else go(prefill_bf16_kernel<64, false, true>, lds);
-        } else {
-            if (paged) go(prefill_bf16_kernel<64, true, false>, lds);
-            else go(prefill_bf16_kernel<64, false, false>, lds);
-        }
-    }
+    };
+    if (a.D == 128) pick(std::integral_constant<int, 128>{});
+    else pick(std::integral_constant<int, 64>{});
     return launch_status();
 }
 

@@ -38,8 +38,10 @@ def heads_per_unit(G):
 # ---------------------------------------------------------------------------
 
 def model_prefill(q_lens, k_lens, Hq, Hkv, D, window=-1, paged_bs=0, rope_rows=None):
-    """Every access of one prefill launch; returns the number of workgroups
-    that did work.  rope_rows: rows of the rotary table (>= max Lk), or None."""
+    """Every access of one prefill launch; returns the number of (workgroup,
+    step) blocks that did work.  rope_rows: rows of the rotary table (>= max
+    Lk), or None.  With a window the launch walks runs of position blocks
+    (run_steps blocks per workgroup), otherwise one block per workgroup."""
     B = len(q_lens)
     cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64)
     cu_k = np.concatenate([[0], np.cumsum(k_lens)]).astype(np.int64)
@@ -47,24 +49,46 @@ def model_prefill(q_lens, k_lens, Hq, Hkv, D, window=-1, paged_bs=0, rope_rows=N
     hpw = heads_per_unit(G)
     bm = BM // hpw
     ng = G // hpw
-    max_q_tiles = (max(q_lens, default=0) + BM - 1) // BM
-    grid = B * max_q_tiles * Hq
-    if grid == 0:
-        return 0
-    bid = np.arange(grid, dtype=np.int64)
-    p = bid % Hq
-    slot = bid // Hq
-    g = p % Hkv
-    hs = (p // Hkv) % ng
-    blk = (hpw - 1 - (p // Hkv) // ng + slot) % hpw
-    r = slot % B
-    qt = max_q_tiles - 1 - slot // B
-    assert (qt >= 0).all()
+    max_q = max(q_lens, default=0)
+    if window >= 0:
+        per_req = (max_q + bm - 1) // bm
+        blocks = B * per_req * ng * Hkv
+        steps = min(16, max(1, blocks // (2 * CUS)))
+        runs = (per_req + steps - 1) // steps
+        grid = B * runs * ng * Hkv
+        if grid == 0:
+            return 0
+        bid = np.arange(grid, dtype=np.int64)
+        g = bid % Hkv
+        rest = bid // Hkv
+        hs = rest % ng
+        rest = rest // ng
+        u = rest % runs
+        r = rest // runs
+        # one entry per (workgroup, step)
+        step = np.tile(np.arange(steps), grid)
+        g, hs, u, r = (np.repeat(x, steps) for x in (g, hs, u, r))
+        blk_index = u * steps + step
+    else:
+        max_q_tiles = (max_q + BM - 1) // BM
+        grid = B * max_q_tiles * Hq
+        if grid == 0:
+            return 0
+        bid = np.arange(grid, dtype=np.int64)
+        p = bid % Hq
+        slot = bid // Hq
+        g = p % Hkv
+        hs = (p // Hkv) % ng
+        blk = (hpw - 1 - (p // Hkv) // ng + slot) % hpw
+        r = slot % B
+        qt = max_q_tiles - 1 - slot // B
+        assert (qt >= 0).all()
+        blk_index = qt * hpw + blk
     cq0, Lq = cu_q[r], cu_q[r + 1] - cu_q[r]
-    live = qt * BM + blk * bm < Lq
-    bid, g, hs, blk, r, qt, cq0, Lq = (x[live] for x in (bid, g, hs, blk, r, qt, cq0, Lq))
+    live = blk_index * bm < Lq
+    g, hs, r, blk_index, cq0, Lq = (x[live] for x in (g, hs, r, blk_index, cq0, Lq))
     ck0, Lk = cu_k[r], cu_k[r + 1] - cu_k[r]
-    row0 = qt * BM + blk * bm
+    row0 = blk_index * bm
     nrows = np.minimum(bm, Lq - row0)
     pos0 = Lk - Lq + row0
     pos_last = pos0 + nrows - 1
