@@ -79,7 +79,7 @@ def _load():
         lib.oracle_paged_decode.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, D, I, I,
                                             I, I, P, I, I]
         lib.oracle_varlen_prefill.argtypes = [P, P, P, P, P, P, P, P, I, I, P, P, I, I, I, I, D,
-                                              I, P, P, I, P, I, I]
+                                              I, I, P, P, I, P, I, I]
         lib.oracle_merge.argtypes = [P, P, P, P, P, P, I, I, I, I]
         lib.oracle_reshape_and_cache.argtypes = [P, P, P, P, P, I, I, I, I, I, I]
         lib.oracle_token_request.argtypes = [P, I, I, P]
@@ -181,10 +181,11 @@ def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, sink, sm_scale: float, num_kv_
                    k=None, v=None, k_cache=None, v_cache=None, block_table=None,
                    block_size: int = 0, window_left: int = -1,
                    units: Optional[Sequence[int]] = None, nthreads: Optional[int] = None,
-                   alibi=None):
-    """Causal varlen prefill; returns ``(out [sum Lq,Hq,D], lse [sum Lq,Hq])``.
+                   alibi=None, causal: bool = True):
+    """Varlen prefill; returns ``(out [sum Lq,Hq,D], lse [sum Lq,Hq])``.
     ``units`` restricts the work to flat ids ``t*Hq + h``; ``alibi``: per-query-head
-    slopes, or None."""
+    slopes, or None; ``causal=False`` drops the upper bound on the visible keys
+    (a window then bounds only the left side)."""
     dt = _dtype_code(q)
     qn = _np(q)
     T, Hq, D = qn.shape
@@ -203,7 +204,8 @@ def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, sink, sm_scale: float, num_kv_
     rc = _load().oracle_varlen_prefill(
         _ptr(out), _ptr(lse), _ptr(qn), _ptr(kn), _ptr(vn), _ptr(kc), _ptr(vc), _ptr(bt),
         int(block_size), 0 if bt is None else bt.shape[1], _ptr(cq), _ptr(ck), B, Hq,
-        int(num_kv_heads), D, float(sm_scale), int(window_left), _ptr(sk), _ptr(al), dt, _ptr(un),
+        int(num_kv_heads), D, float(sm_scale), int(bool(causal)), int(window_left), _ptr(sk),
+        _ptr(al), dt, _ptr(un),
         0 if un is None else len(un), _threads(nthreads))
     assert rc == 0
     return out, lse

@@ -15,7 +15,8 @@
  *
  *   G = Hq / Hkv, kv head g = h / G               (repeat_interleave grouping)
  *   p = Lk - Lq + i                               (queries are the last Lq positions)
- *   visible j: 0 <= j < Lk, j <= p, and (w < 0 or j >= p - w)
+ *   visible j: 0 <= j < Lk, j <= p (causal; no upper bound otherwise),
+ *              and (w < 0 or j >= p - w)
  *   s_j   = sm_scale * sum_d q[d] * K(j)[d]       (fp64)
  *           + slope[h] * (j - p)                   (ALiBi, when slopes are given:
  *             vLLM page "attention.py", PagedAttentionWithALiBi.set_attn_bias --
@@ -106,12 +107,15 @@ static void attend_row(double *o, double *lse, const void *qbase, size_t qoff,
     *lse = M + log(Z);
 }
 
-/* Visible logical keys of a query at absolute position p among Lk keys. */
-static int visible_keys(int Lk, int p, int window_left, int lo, int hi, int *js)
+/* Visible logical keys of a query at absolute position p among Lk keys.
+ * causal: keys after the query are hidden (j <= p).  Non-causal (FlashInfer
+ * page, sink_attention_unified, the non-causal branches): every key is a
+ * candidate and a window only bounds the left side, p - window_left <= j. */
+static int visible_keys(int Lk, int p, int causal, int window_left, int lo, int hi, int *js)
 {
     int n = 0;
     for (int j = 0; j < Lk; ++j) {
-        if (j > p) continue;
+        if (causal && j > p) continue;
         if (window_left >= 0 && j < p - window_left) continue;
         if (j < lo || j >= hi) continue;      /* partition restriction */
         js[n++] = j;
@@ -184,7 +188,7 @@ static void decode_unit(void *vctx, int u, double *s, size_t *krow, int *js)
     int Lk = c->seqlens[b];
     int lo = 0, hi = Lk;
     if (c->part > 0) { lo = p * c->part; hi = lo + c->part; }
-    int n = visible_keys(Lk, Lk - 1, c->window, lo, hi, js);
+    int n = visible_keys(Lk, Lk - 1, 1, c->window, lo, hi, js);
     for (int t = 0; t < n; ++t) {
         long long row = oracle_slot_of(c->bt + (size_t)b * c->mbps, js[t], c->bs);
         krow[t] = ((size_t)row * c->Hkv + g) * c->D;
@@ -227,7 +231,7 @@ typedef struct {
     const void *q, *k, *v, *kc, *vc;
     const int32_t *bt, *cu_q, *cu_k, *tok_req;
     const float *sink, *alibi;
-    int B, Hq, Hkv, D, bs, mbps, window, dtype;
+    int B, Hq, Hkv, D, bs, mbps, window, causal, dtype;
     double scale;
     const int32_t *units;
 } prefill_ctx;
@@ -242,7 +246,7 @@ static void prefill_unit(void *vctx, int u, double *s, size_t *krow, int *js)
     int Lq = c->cu_q[r + 1] - c->cu_q[r], Lk = c->cu_k[r + 1] - c->cu_k[r];
     int i = t - c->cu_q[r];
     int p = Lk - Lq + i;
-    int n = visible_keys(Lk, p, c->window, 0, Lk, js);
+    int n = visible_keys(Lk, p, c->causal, c->window, 0, Lk, js);
     const void *kb = c->k ? c->k : c->kc, *vb = c->k ? c->v : c->vc;
     for (int m = 0; m < n; ++m) {
         long long row = c->k ? (long long)c->cu_k[r] + js[m]
@@ -255,13 +259,14 @@ static void prefill_unit(void *vctx, int u, double *s, size_t *krow, int *js)
                krow, js, n, p, slope, c->D, c->dtype, c->scale, sigma, s);
 }
 
-/* out [sumLq,Hq,D], lse [sumLq,Hq]; causal only (the kernels' contract). */
+/* out [sumLq,Hq,D], lse [sumLq,Hq]; causal 1 or 0 (no upper bound on the
+ * visible keys). */
 int oracle_varlen_prefill(double *out, double *lse, const void *q, const void *k, const void *v,
                           const void *k_cache, const void *v_cache, const int32_t *block_table,
                           int block_size, int max_blocks_per_seq, const int32_t *cu_q,
                           const int32_t *cu_k, int B, int Hq, int Hkv, int D, double sm_scale,
-                          int window_left, const float *sink, const float *alibi, int dtype,
-                          const int32_t *units, int nunits, int nthreads)
+                          int causal, int window_left, const float *sink, const float *alibi,
+                          int dtype, const int32_t *units, int nunits, int nthreads)
 {
     if (Hkv <= 0 || Hq % Hkv || D <= 0 || B < 0) return 1;
     int T = cu_q[B] - cu_q[0];
@@ -271,8 +276,8 @@ int oracle_varlen_prefill(double *out, double *lse, const void *q, const void *k
     for (int r = 0; r < B; ++r) if (cu_k[r + 1] - cu_k[r] > maxk) maxk = cu_k[r + 1] - cu_k[r];
     prefill_ctx c = {out, lse, q, k, v, k_cache, v_cache, block_table, cu_q, cu_k, tok_req, sink,
                      alibi,
-                     B, Hq, Hkv, D, block_size, max_blocks_per_seq, window_left, dtype, sm_scale,
-                     units};
+                     B, Hq, Hkv, D, block_size, max_blocks_per_seq, window_left, causal ? 1 : 0,
+                     dtype, sm_scale, units};
     run_units(prefill_unit, &c, units ? nunits : T * Hq, nthreads, maxk);
     free(tok_req);
     return 0;

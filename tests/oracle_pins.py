@@ -405,7 +405,7 @@ def pin_merge_associative():
 # extra column of the logits, softmax, sink column dropped).
 # ---------------------------------------------------------------------------
 
-def _numpy_reference(q, k, v, cu_q, cu_k, sink, sm_scale, Hkv, window, alibi=None):
+def _numpy_reference(q, k, v, cu_q, cu_k, sink, sm_scale, Hkv, window, alibi=None, causal=True):
     q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
     Hq = q.shape[1]
     G = Hq // Hkv
@@ -415,7 +415,7 @@ def _numpy_reference(q, k, v, cu_q, cu_k, sink, sm_scale, Hkv, window, alibi=Non
         Lq, Lk = cu_q[r + 1] - cu_q[r], cu_k[r + 1] - cu_k[r]
         rows = (Lk - Lq + np.arange(Lq))[:, None]
         cols = np.arange(Lk)[None, :]
-        mask = cols <= rows
+        mask = cols <= rows if causal else np.ones((Lq, Lk), bool)
         if window >= 0:
             mask &= cols >= rows - window
         for h in range(Hq):
@@ -456,6 +456,66 @@ def pin_brute_force():
                                None if c.sink is None else c.sink.numpy(), 0.6, Hkv, w,
                                None if al is None else al.numpy())
         _close(o, ref, 1e-12, 1e-10, f"brute force trial {trial}")
+
+
+def pin_noncausal_brute_force():
+    """Non-causal prefill (FlashInfer page, sink_attention_unified, the
+    non-causal branches: every key is a candidate; a window only bounds the
+    left side, query_position - window_left <= key) against the mask-matrix
+    reference, queries shorter and longer than the keys, with sinks and ALiBi."""
+    rng = np.random.default_rng(4321)
+    for trial in range(18):
+        G = [1, 2, 4][trial % 3]
+        Hkv = 1 + trial % 2
+        B = 1 + trial % 3
+        q_lens = rng.integers(0, 9, size=B).tolist()
+        k_lens = [max(0, ql + int(rng.integers(-3, 6))) for ql in q_lens]
+        w = [-1, 0, 2, 5, 100, 3][trial % 6]
+        with_sink = trial % 2 == 1
+        al = (torch.from_numpy(rng.uniform(0.01, 1.0, size=G * Hkv).astype(np.float32))
+              if trial % 4 == 3 else None)
+        c = synth.prefill_case(700 + trial, q_lens, k_lens, G * Hkv, Hkv, 8, torch.float32,
+                               with_sink, window_left=w, sm_scale=0.7)
+        o, _ = oracle.varlen_prefill(c.q, c.cu_seqlens_q, c.cu_seqlens_k, c.sink, 0.7, Hkv,
+                                     k=c.k, v=c.v, window_left=w, alibi=al, causal=False)
+        ref = _numpy_reference(c.q, c.k, c.v, c.cu_seqlens_q.tolist(), c.cu_seqlens_k.tolist(),
+                               None if c.sink is None else c.sink.numpy(), 0.7, Hkv, w,
+                               None if al is None else al.numpy(), causal=False)
+        _close(o, ref, 1e-12, 1e-10, f"non-causal brute force trial {trial}")
+
+
+def pin_noncausal_sdpa():
+    """Non-causal prefill without a window or sink is textbook attention over
+    all of the request's keys: torch's float64 SDPA with no mask (GQA by
+    repeated kv heads), for queries fewer and more than the keys; with one
+    query it equals decode over the same keys (a causal query at the last
+    position sees them all)."""
+    for seed, (q_lens, k_lens, Hq, Hkv, D) in enumerate([([5, 9, 1], [7, 3, 4], 4, 2, 8),
+                                                         ([12], [20], 6, 3, 16)]):
+        c = synth.prefill_case(800 + seed, q_lens, k_lens, Hq, Hkv, D, torch.float32, False,
+                               sm_scale=0.25 + 0.1 * seed)
+        o, l = oracle.varlen_prefill(c.q, c.cu_seqlens_q, c.cu_seqlens_k, None, c.sm_scale,
+                                     Hkv, k=c.k, v=c.v, causal=False)
+        cq, ck = c.cu_seqlens_q.tolist(), c.cu_seqlens_k.tolist()
+        for r in range(len(q_lens)):
+            qr = c.q[cq[r]:cq[r + 1]].double().transpose(0, 1)[None]
+            kr = c.k[ck[r]:ck[r + 1]].double().transpose(0, 1)[None]
+            vr = c.v[ck[r]:ck[r + 1]].double().transpose(0, 1)[None]
+            ref = F.scaled_dot_product_attention(qr, kr, vr, scale=c.sm_scale,
+                                                 enable_gqa=True)[0].transpose(0, 1)
+            _close(o[cq[r]:cq[r + 1]], ref.numpy(), 1e-12, 1e-10, f"non-causal sdpa request {r}")
+    # one query per request, non-causal == decode over the request's keys
+    dc = synth.decode_case(810, [1, 9, 30], 8, 2, 16, 4, torch.float32, with_sink=True,
+                           sm_scale=0.4, shuffle=True)
+    od, ld = oracle.paged_decode(dc.q, dc.k_cache, dc.v_cache, dc.block_table, dc.cache_seqlens,
+                                 dc.sink, 0.4)
+    cu_q = torch.arange(dc.B + 1, dtype=torch.int32)
+    cu_k = synth.cu_from_lengths(dc.cache_seqlens.tolist())
+    op, lp = oracle.varlen_prefill(dc.q, cu_q, cu_k, dc.sink, 0.4, dc.Hkv, k_cache=dc.k_cache,
+                                   v_cache=dc.v_cache, block_table=dc.block_table, block_size=4,
+                                   causal=False)
+    _close(op, od, 1e-13, 1e-12, "non-causal Lq = 1 vs decode")
+    _close(lp, ld, 1e-13, 1e-12, "non-causal Lq = 1 vs decode lse")
 
 
 def pin_alibi_closed_form():

@@ -5,7 +5,8 @@ wrong GQA grouping, top-left instead of bottom-right causal alignment, a
 window off by one, a paged-address mistake, a wrong lse, a wrong merge
 weight, K used in place of V, the sink left out of the max, a decode query
 at the wrong position, an ALiBi bias of the wrong sign, a partition one key
-too long, top-left query positions, and four rotary-embedding mistakes (the
+too long, a non-causal prefill that keeps the causal bound or bounds the
+window on both sides, top-left query positions, and four rotary-embedding mistakes (the
 frequency exponent, the sign of the sine, the pairing, linear scaling
 inverted).  A mutation names the file of the oracle package it changes; each
 mutant package is a copy of ``oracle/`` imported in its own subprocess."""
@@ -44,8 +45,11 @@ MUTATIONS = {
     "pv_uses_k": (C, "o[d] += e * load_elem(vbase, krow[n] + d, dtype);",
                   "o[d] += e * load_elem(kbase, krow[n] + d, dtype);"),
     "max_ignores_sink": (C, "    double M = sigma;\n    for (int n = 0;", "    double M = -INFINITY;\n    for (int n = 0;"),
-    "decode_query_position": (C, "visible_keys(Lk, Lk - 1, c->window, lo, hi, js)",
-                              "visible_keys(Lk, Lk - 2, c->window, lo, hi, js)"),
+    "decode_query_position": (C, "visible_keys(Lk, Lk - 1, 1, c->window, lo, hi, js)",
+                              "visible_keys(Lk, Lk - 2, 1, c->window, lo, hi, js)"),
+    "noncausal_keeps_upper_bound": (C, "if (causal && j > p) continue;", "if (j > p) continue;"),
+    "noncausal_window_both_sides": (C, "if (window_left >= 0 && j < p - window_left) continue;",
+                                    "if (window_left >= 0 && (j < p - window_left || j > p + window_left)) continue;"),
     "alibi_sign": (C, "s[n] = sm_scale * acc + slope * (double)(js[n] - p);",
                    "s[n] = sm_scale * acc + slope * (double)(p - js[n]);"),
     "partition_one_key_long": (C, "if (c->part > 0) { lo = p * c->part; hi = lo + c->part; }",
