@@ -24,7 +24,7 @@
  *                           (vLLM page, single_query_cached_kv_attention: the
  *                           partitioned "v2" path with exp_sums / max_logits /
  *                           tmp_output)
- *   pkv_varlen_prefill      causal attention for packed variable-length
+ *   pkv_varlen_prefill      causal or non-causal attention for packed variable-length
  *                           requests (Transformers doc, varlen path:
  *                           cu_seq_lens_q/k and max_length_q/k), over
  *                           contiguous K/V or over the paged cache
@@ -32,7 +32,9 @@
  * What every attention call computes (FlashInfer "sink_attention_reference.py"
  * page, sink_softmax and sink_attention_unified): for request r with Lq
  * queries and Lk keys, query row i sits at absolute position p = Lk - Lq + i
- * and sees key j iff 0 <= j <= p and (window_left < 0 or j >= p - window_left).
+ * and sees key j iff 0 <= j <= p and (window_left < 0 or j >= p - window_left);
+ * a non-causal prefill (same page, the non-causal branches) drops j <= p, so
+ * row i sees every key j < Lk with (window_left < 0 or j >= p - window_left).
  * Query head h reads kv head h / (Hq / Hkv).  Logits are sm_scale * q.k;
  * the optional per-query-head sink is one more logit, NOT multiplied by
  * sm_scale, that joins the softmax denominator and has no value row.  A row
@@ -400,7 +402,7 @@ pkv_status pkv_merge_partitions(void *out, float *lse, const float *part_out,
                                 pkv_dtype dtype, void *stream);
 
 /*
- * pkv_varlen_prefill -- causal attention over packed variable-length requests
+ * pkv_varlen_prefill -- attention over packed variable-length requests
  * (Transformers doc, varlen path; FlashInfer page, varlen branch).
  *
  *   out             [sum Lq, num_q_heads, head_dim]
@@ -418,14 +420,18 @@ pkv_status pkv_merge_partitions(void *out, float *lse, const float *part_out,
  *                   Contract: nondecreasing; every Lq <= max_seqlen_q and
  *                   Lk <= max_seqlen_k (host upper bounds that size the
  *                   launch); paged: Lk <= max_blocks_per_seq * block_size.
- *   causal          must be 1 (bottom-right aligned: queries are the last Lq
- *                   positions of the request's keys)
+ *   causal          1: row i at position p = Lk - Lq + i (queries are the
+ *                   last Lq positions of the request's keys) sees keys j <= p;
+ *                   0: it sees every key of the request.  A window (window_left
+ *                   >= 0) bounds the left side in both, j >= p - window_left.
+ *                   Other values: PKV_ERR_SHAPE.
  *   rope_cos_sin    NULL, or a pkv_rope_cos_sin table of rope_positions rows
  *                   (>= max_seqlen_k): q is then rotated by its position p =
  *                   Lk - Lq + i as it is loaded, with rotary_dim (a multiple
  *                   of 32 in [32, head_dim]) and rope_neox as for
  *                   pkv_rope_apply; the keys must already be rotated (for
- *                   example stored with pkv_reshape_and_cache_rope)
+ *                   example stored with pkv_reshape_and_cache_rope).  Rows at
+ *                   a negative position (Lq > Lk) are not rotated.
  *
  * Errors besides the common ones: PKV_ERR_UNSUPPORTED for bfloat16 with
  * contiguous K/V when max_seqlen_k * num_kv_heads * head_dim * 2 bytes (one

@@ -595,7 +595,8 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
     if (B < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return PKV_ERR_SHAPE;
     pkv_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
     if (st != PKV_OK) return st;
-    if (!dtype_ok(dtype) || causal != 1) return PKV_ERR_UNSUPPORTED;
+    if (!dtype_ok(dtype)) return PKV_ERR_UNSUPPORTED;
+    if (causal != 0 && causal != 1) return PKV_ERR_SHAPE;
     if (window_left < -1 || !scale_ok(sm_scale)) return PKV_ERR_SHAPE;
     if (rope_cos_sin) {
         // q rotated in registers: rotary_dim a multiple of 32 within the head,
@@ -635,13 +636,13 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
         a.cu_k = cu_seqlens_k; a.sink = sink; a.alibi = alibi_slopes; a.B = B;
         a.Hq = num_q_heads; a.Hkv = num_kv_heads;
         a.G = num_q_heads / num_kv_heads; a.D = head_dim; a.bs_log2 = bs_log2;
-        a.mbps = max_blocks_per_seq; a.window_left = window_left;
+        a.mbps = max_blocks_per_seq; a.window_left = window_left; a.causal = causal;
         a.hpw = prefill_heads_per_wg(a.G);
         a.max_q_tiles = (max_seqlen_q + prefill_block_m() - 1) / prefill_block_m();
         a.scale_log2 = sm_scale * kLog2e;
-        if (window_left >= 0) {
-            // sliding window: workgroups walk runs of position blocks (each
-            // step's keys overlap the last step's), sized for about two
+        if (window_left >= 0 && causal) {
+            // causal sliding window: workgroups walk runs of position blocks
+            // (each step's keys overlap the last step's), sized for about two
             // resident workgroups per compute unit
             const int bm = prefill_block_m() / a.hpw;
             const long long per_req = (max_seqlen_q + bm - 1) / bm;
@@ -661,7 +662,7 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
     a.sink = sink; a.alibi = alibi_slopes; a.B = B; a.Hq = num_q_heads; a.Hkv = num_kv_heads;
     a.G = num_q_heads / num_kv_heads; a.D = head_dim; a.bs_log2 = bs_log2;
     a.mbps = max_blocks_per_seq; a.window_left = window_left; a.scale_log2 = sm_scale * kLog2e;
-    a.T = max_seqlen_q;
+    a.T = max_seqlen_q; a.causal = causal;
     return launch_rows(a, s);
 }
 

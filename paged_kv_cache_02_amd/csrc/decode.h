@@ -178,6 +178,9 @@ struct RowArgs {
     int32_t rope_dim, rope_neox;
     int32_t B, T, Hq, Hkv, G, D;   // prefill: T = max_seqlen_q
     int32_t bs_log2, mbps, window_left;
+    // prefill: 1 = key j visible to position p only when j <= p; 0 = every
+    // key of the request (a window still bounds the left side)
+    int32_t causal;
     int32_t part_size, nparts, split;
     float scale_log2;
 };
@@ -201,6 +204,7 @@ struct PrefillArgs {
     int32_t rope_dim, rope_neox;
     int32_t B, Hq, Hkv, G, D;
     int32_t bs_log2, mbps, window_left;
+    int32_t causal;              // as RowArgs::causal
     int32_t hpw;                 // query heads per workgroup: prefill_heads_per_wg(G)
     int32_t max_q_tiles;         // ceil(max_seqlen_q / prefill_block_m())
     // runs (sliding windows): each workgroup walks run_steps consecutive

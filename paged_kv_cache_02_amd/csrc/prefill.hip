@@ -1,11 +1,13 @@
-// Varlen causal prefill over contiguous or paged K/V, bf16 with fp32 accumulation.
+// Varlen prefill over contiguous or paged K/V, bf16 with fp32 accumulation.
 //
 // Transformers "Paged attention" doc, varlen path: packed requests indexed by
 // cu_seq_lens_q/k, launch sized by max_length_q/k; FlashInfer
 // "sink_attention_reference.py" page, varlen branch: request r's query row i
 // sits at position p = Lk - Lq + i (queries are the last Lq positions), sees
 // keys j <= p with p - window_left <= j when a window is set, GQA h -> h / G,
-// and the per-head sink joins the denominator; vLLM "attention.py" page,
+// and the per-head sink joins the denominator (its non-causal branch: every
+// key of the request, a window bounding only the left side, p - window_left
+// <= j); vLLM "attention.py" page,
 // multi_query_kv_attention: block-diagonal causal attention over packed
 // prompts.  Paged mode reads K/V through the request's block_table row, so a
 // query chunk can attend to keys already in the cache.
@@ -125,10 +127,11 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const void *base, uint32_t bytes) {
 }
 
 // Rotary embedding of a lane's Q registers (lane half lh holds dims
-// 16c + 8lh .. +8 of register c).  tab: the row's table, cos then sin.
+// 16c + 8lh .. +8 of register c).  tab: the row's table, cos then sin;
+// lanes with rot false keep their values.
 // neox, rope_dim = 32 OFF: register c < OFF pairs with register c + OFF.
 template <int OFF, int QK>
-__device__ __forceinline__ void rope_neox(bf16x8 (&qf)[QK], const float *tab, int lh) {
+__device__ __forceinline__ void rope_neox(bf16x8 (&qf)[QK], const float *tab, int lh, bool rot) {
     static_assert(2 * OFF <= QK, "rotary dims within the head");
     constexpr int half = 16 * OFF;
 #pragma unroll
@@ -139,8 +142,8 @@ __device__ __forceinline__ void rope_neox(bf16x8 (&qf)[QK], const float *tab, in
         for (int e = 0; e < 8; ++e) {
             const float co = tab[d0 + e], si = tab[half + d0 + e];
             const float x0 = (float)qf[c][e], x1 = (float)qf[c + OFF][e];
-            x[e] = (__bf16)(x0 * co - x1 * si);
-            y[e] = (__bf16)(x1 * co + x0 * si);
+            x[e] = rot ? (__bf16)(x0 * co - x1 * si) : qf[c][e];
+            y[e] = rot ? (__bf16)(x1 * co + x0 * si) : qf[c + OFF][e];
         }
         qf[c] = x;
         qf[c + OFF] = y;
@@ -148,7 +151,8 @@ __device__ __forceinline__ void rope_neox(bf16x8 (&qf)[QK], const float *tab, in
 }
 // interleaved pairs (2i, 2i + 1) sit next to each other in a register
 template <int QK>
-__device__ __forceinline__ void rope_pairs(bf16x8 (&qf)[QK], const float *tab, int lh, int rd) {
+__device__ __forceinline__ void rope_pairs(bf16x8 (&qf)[QK], const float *tab, int lh, int rd,
+                                           bool rot) {
     const int half = rd / 2;
 #pragma unroll
     for (int c = 0; c < QK; ++c) {
@@ -160,8 +164,8 @@ __device__ __forceinline__ void rope_pairs(bf16x8 (&qf)[QK], const float *tab, i
             const int i = (d0 + e) / 2;
             const float co = tab[i], si = tab[half + i];
             const float x0 = (float)qf[c][e], x1 = (float)qf[c][e + 1];
-            x[e] = (__bf16)(x0 * co - x1 * si);
-            x[e + 1] = (__bf16)(x1 * co + x0 * si);
+            x[e] = rot ? (__bf16)(x0 * co - x1 * si) : qf[c][e];
+            x[e + 1] = rot ? (__bf16)(x1 * co + x0 * si) : qf[c][e + 1];
         }
         qf[c] = x;
     }
@@ -242,7 +246,7 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
         const int nr = min(bm, Lq - row0_);
         const int p0 = Lk - Lq + row0_;
         lo_ = a.window_left >= 0 ? max(0, p0 - a.window_left) : 0;
-        const int hi_ = min(Lk, p0 + nr);
+        const int hi_ = a.causal ? min(Lk, p0 + nr) : Lk;
         tb_ = lo_ & ~(BN - 1);
         nt_ = hi_ > lo_ ? (hi_ - tb_ + BN - 1) / BN : 0;
     };
@@ -252,14 +256,14 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
         pos0 = Lk - Lq + row0;                      // position of the first row
         pos_last = pos0 + nrows - 1;
         block_keys(row0, kv_lo, t_begin, ntiles);
-        kv_hi = min(Lk, pos_last + 1);              // exclusive
+        kv_hi = a.causal ? min(Lk, pos_last + 1) : Lk;   // exclusive
         // this wave's rows and visible key range
         wrow0 = row0 + 32 * (wave / hpw);
         wrows = max(0, min(32, Lq - wrow0));
         wpos0 = Lk - Lq + wrow0;
         wpos1 = wpos0 + wrows - 1;
         w_lo = a.window_left >= 0 ? max(0, wpos0 - a.window_left) : 0;
-        w_hi = min(Lk, wpos1 + 1);
+        w_hi = a.causal ? min(Lk, wpos1 + 1) : Lk;
     };
     set_step(0);
 
@@ -286,22 +290,25 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
     // c + rope_dim / 32 of this lane; interleaved pairs are adjacent.
     // Register indices stay compile-time constants (a runtime index would
     // move qf to scratch memory).  Rows past the request (zero q) and rows at
-    // a negative position (Lq > Lk: no visible key) read table row 0, so
-    // every read stays inside the table.  Called once the first K/V tile is
-    // in flight, so the table loads overlap that tile's.
+    // a negative position (Lq > Lk) read table row 0, so every read stays
+    // inside the table, and keep q as it is: a negative position has no table
+    // row (causal rows there see no key; non-causal rows see them all).
+    // Called once the first K/V tile is in flight, so the table loads overlap
+    // that tile's.
     auto rotate_q = [&]() {
         const int tpos = wpos0 + lr;
-        const float *tab = a.rope + (size_t)(lr < wrows && tpos >= 0 ? tpos : 0) * a.rope_dim;
+        const bool rot = lr < wrows && tpos >= 0;
+        const float *tab = a.rope + (size_t)(rot ? tpos : 0) * a.rope_dim;
         if (a.rope_neox) {
             switch (a.rope_dim / 32) {
-                case 1: rope_neox<1>(qf, tab, lh); break;
-                case 2: rope_neox<2>(qf, tab, lh); break;
-                case 3: if constexpr (QK_STEPS >= 6) rope_neox<3>(qf, tab, lh); break;
-                case 4: if constexpr (QK_STEPS >= 8) rope_neox<4>(qf, tab, lh); break;
+                case 1: rope_neox<1>(qf, tab, lh, rot); break;
+                case 2: rope_neox<2>(qf, tab, lh, rot); break;
+                case 3: if constexpr (QK_STEPS >= 6) rope_neox<3>(qf, tab, lh, rot); break;
+                case 4: if constexpr (QK_STEPS >= 8) rope_neox<4>(qf, tab, lh, rot); break;
                 default: break;
             }
         } else {
-            rope_pairs(qf, tab, lh, a.rope_dim);
+            rope_pairs(qf, tab, lh, a.rope_dim, rot);
         }
     };
 
@@ -403,10 +410,10 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
                 sx[i] = fmaf(sx[i], a.scale_log2, fmaf(slope_log2, kx, base));
             }
         }
-        const bool full = (c0 + 31 <= wpos0) && (c0 + 32 <= Lk) &&
+        const bool full = (!a.causal || c0 + 31 <= wpos0) && (c0 + 32 <= Lk) &&
                           (a.window_left < 0 || c0 >= wpos1 - a.window_left);
         if (!full) {
-            const int hi = min(pos, Lk - 1) - c0;                         // keys <= hi visible
+            const int hi = (a.causal ? min(pos, Lk - 1) : Lk - 1) - c0;   // keys <= hi visible
             const int lo = a.window_left >= 0 ? pos - a.window_left - c0 : -1 << 30;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {

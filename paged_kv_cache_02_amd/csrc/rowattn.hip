@@ -4,6 +4,7 @@
 // Same definition as the bf16 kernels (FlashInfer sink-attention page:
 // logits sm_scale*q.k, bottom-right causal position p = Lk - Lq + i, window
 // p - window_left <= j <= p, GQA h -> h / G, sink in the denominator only;
+// its non-causal branch drops j <= p and keeps the window's left bound;
 // Transformers paged-attention doc: keys through block_table / cu_seqlens),
 // computed with plain fp32 FMAs: the 64 lanes split head_dim, each key's dot
 // product is a wave reduction, and the softmax is updated online one key at
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
     }
     const int g = h / a.G;
     const int pos = Lk - Lq + i;
-    int jlo = 0, jhi = min(Lk, pos + 1);
+    int jlo = 0, jhi = (a.mode == 1 && !a.causal) ? Lk : min(Lk, pos + 1);
     if (a.window_left >= 0) jlo = max(jlo, pos - a.window_left);
     if (a.split) {
         jlo = max(jlo, pidx * a.part_size);
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
     if (a.mode == 1 && a.rope && pos >= 0) {
         // rotary embedding of q at its position: the partner element is read
         // from memory (neox: d +- rope_dim / 2; interleaved: d ^ 1).  A row
-        // at a negative position (Lq > Lk) sees no key and is not rotated.
+        // at a negative position (Lq > Lk) has no table row and is not rotated.
         const int rd = a.rope_dim, half = rd / 2;
         const float *tab = a.rope + (size_t)pos * rd;
 #pragma unroll

@@ -359,8 +359,10 @@ def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_
                    sm_scale: float, num_kv_heads: Optional[int] = None, k=None, v=None,
                    k_cache=None, v_cache=None, block_table=None, sink=None,
                    window_left: int = -1, out=None, lse=None, alibi_slopes=None,
-                   rope_cos_sin=None, rotary_dim: int = 0, rope_neox: bool = True):
-    """Causal varlen prefill: out [sum Lq, Hq, D]."""
+                   rope_cos_sin=None, rotary_dim: int = 0, rope_neox: bool = True,
+                   causal: bool = True):
+    """Varlen prefill: out [sum Lq, Hq, D].  causal=False lets every query
+    row see every key of its request (a window still bounds the left side)."""
     if rope_cos_sin is not None:
         _rope_table(rope_cos_sin, rotary_dim)
     T, Hq, D = q.shape
@@ -380,7 +382,7 @@ def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_
         _ptr(v_cache), _ptr(None if block_table is None else _i32(block_table, "block_table")),
         bs, NB, MB, _ptr(_i32(cu_seqlens_q, "cu_seqlens_q")),
         _ptr(_i32(cu_seqlens_k, "cu_seqlens_k")), B, int(max_seqlen_q), int(max_seqlen_k), Hq,
-        Hkv, D, float(sm_scale), 1, window_left, _ptr(_f32(alibi_slopes, "alibi_slopes")),
+        Hkv, D, float(sm_scale), int(bool(causal)), window_left, _ptr(_f32(alibi_slopes, "alibi_slopes")),
         _ptr(rope_cos_sin),
         0 if rope_cos_sin is None else rope_cos_sin.shape[0], rotary_dim, int(bool(rope_neox)),
         _ptr(_f32(sink, "sink")), _dt(q, k, v, k_cache, v_cache, out), _stream()),

@@ -78,7 +78,7 @@ def oracle_decode(c, units=None):
                                c.sm_scale, c.window_left, units=units)
 
 
-def run_prefill(c, with_lse=True):
+def run_prefill(c, with_lse=True, causal=True):
     from paged_kv_cache_02_amd import pkv
     check_prefill_case(c)
     T = c.q.shape[0]
@@ -87,16 +87,16 @@ def run_prefill(c, with_lse=True):
                              c.max_seqlen_k, c.sm_scale, c.Hkv, k=dev(c.k), v=dev(c.v),
                              k_cache=dev(c.k_cache), v_cache=dev(c.v_cache),
                              block_table=dev(c.block_table), sink=dev(c.sink),
-                             window_left=c.window_left, lse=lse)
+                             window_left=c.window_left, lse=lse, causal=causal)
     torch.cuda.synchronize()
     return out, lse
 
 
-def oracle_prefill(c, units=None):
+def oracle_prefill(c, units=None, causal=True):
     return oracle.varlen_prefill(c.q, c.cu_seqlens_q, c.cu_seqlens_k, c.sink, c.sm_scale, c.Hkv,
                                  k=c.k, v=c.v, k_cache=c.k_cache, v_cache=c.v_cache,
                                  block_table=c.block_table, block_size=c.block_size,
-                                 window_left=c.window_left, units=units)
+                                 window_left=c.window_left, units=units, causal=causal)
 
 
 def banner(msg: str):

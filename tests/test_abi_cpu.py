@@ -151,7 +151,9 @@ def prefill_call(**over):
      pkv.PKV_ERR_UNSUPPORTED),
     (dict(k=None, v=None, k_cache=FAKE, v_cache=FAKE, bt=FAKE, bs=16, NB=4, MB=1, maxk=17),
      pkv.PKV_ERR_SHAPE),
-    (dict(causal=0), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(causal=2), pkv.PKV_ERR_SHAPE),
+    (dict(causal=-1), pkv.PKV_ERR_SHAPE),
+    (dict(causal=0, B=0), pkv.PKV_OK),                          # non-causal accepted
     (dict(Hkv=3), pkv.PKV_ERR_SHAPE),
     (dict(D=80), pkv.PKV_ERR_UNSUPPORTED),
     (dict(window=-5), pkv.PKV_ERR_SHAPE),

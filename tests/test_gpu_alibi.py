@@ -117,6 +117,38 @@ def test_prefill_alibi(case, dtype):
     assert_close(lse, l, dtype, "prefill alibi lse", lse=True)
 
 
+@pytest.mark.parametrize("case", [PREFILL[1], PREFILL[3]], ids=["window", "paged"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_prefill_alibi_noncausal(case, dtype):
+    """ALiBi with causal=False: keys after the query position get a positive
+    bias (slope times key minus query position)."""
+    from paged_kv_cache_02_amd import pkv
+    q_lens, k_lens, Hq, Hkv, D, sink, window, bs = case
+    banner(f"prefill alibi non-causal {dtype} {case}")
+    k_lens = k_lens or q_lens
+    if bs:
+        c = synth.paged_prefill_case(440 + len(q_lens), q_lens, k_lens, Hq, Hkv, D, bs, dtype, sink,
+                                     window_left=window)
+    else:
+        c = synth.prefill_case(440 + len(q_lens), q_lens, k_lens, Hq, Hkv, D, dtype, sink,
+                               window_left=window)
+    al = slopes(Hq)
+    T = c.q.shape[0]
+    lse = torch.empty(T, Hq, dtype=torch.float32, device="cuda")
+    out = pkv.varlen_prefill(dev(c.q), dev(c.cu_seqlens_q), dev(c.cu_seqlens_k), c.max_seqlen_q,
+                             c.max_seqlen_k, c.sm_scale, c.Hkv, k=dev(c.k), v=dev(c.v),
+                             k_cache=dev(c.k_cache), v_cache=dev(c.v_cache),
+                             block_table=dev(c.block_table), sink=dev(c.sink),
+                             window_left=window, lse=lse, alibi_slopes=dev(al), causal=False)
+    torch.cuda.synchronize()
+    o, l = oracle.varlen_prefill(c.q, c.cu_seqlens_q, c.cu_seqlens_k, c.sink, c.sm_scale, c.Hkv,
+                                 k=c.k, v=c.v, k_cache=c.k_cache, v_cache=c.v_cache,
+                                 block_table=c.block_table, block_size=c.block_size,
+                                 window_left=window, alibi=al, causal=False)
+    assert_close(out, o, dtype, "prefill alibi non-causal out")
+    assert_close(lse, l, dtype, "prefill alibi non-causal lse", lse=True)
+
+
 def test_alibi_zero_slopes_equal_plain():
     """Slopes of zero give exactly the results of a call without slopes
     (bf16 prefill: the ALiBi instantiation reorders no arithmetic that

@@ -1,4 +1,5 @@
-"""Varlen causal prefill (contiguous and paged K/V) on the GPU against the fp64 oracle."""
+"""Varlen prefill, causal and non-causal (contiguous and paged K/V), on the GPU
+against the fp64 oracle."""
 
 import numpy as np
 import pytest
@@ -99,6 +100,53 @@ def test_prefill_paged_vs_oracle(case, dtype):
     o, l = oracle_prefill(c)
     assert_close(out, o, dtype, "out")
     assert_close(lse, l, dtype, "lse", lse=True)
+
+
+NONCAUSAL = [
+    # q_lens, k_lens, Hq, Hkv, D, sink, window, paged block size (0: contiguous)
+    ([1, 5, 128, 129, 300], None, 8, 2, 128, True, -1, 0),
+    ([130, 20], [500, 20], 8, 4, 128, True, -1, 0),          # queries fewer than keys
+    ([10, 3, 1], [0, 1, 7], 4, 2, 64, True, -1, 0),           # more queries than keys, Lk = 0
+    ([200, 77, 400], None, 8, 1, 64, True, 31, 0),            # left-only window
+    ([300], None, 4, 4, 128, False, 0, 0),                    # window 0: from p on
+    ([129, 40, 260], None, 12, 2, 64, True, 3, 0),            # G 6, small window
+    ([64, 100], [364, 100], 16, 8, 64, True, 128, 16),
+    ([129, 1], [129, 2000], 8, 8, 128, False, 17, 64),
+    ([1000], [70], 16, 2, 64, True, 17, 32),                  # Lq > Lk with a window
+    ([40, 1, 200], [190, 70, 264], 8, 2, 64, False, -1, 16),
+]
+
+
+@pytest.mark.parametrize("case", NONCAUSAL, ids=[str(i) for i in range(len(NONCAUSAL))])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_prefill_noncausal_vs_oracle(case, dtype):
+    """causal=False (the FlashInfer page's non-causal branches): every key of
+    the request, a window bounding only the left side."""
+    q_lens, k_lens, Hq, Hkv, D, sink, window, bs = case
+    banner(f"prefill non-causal {dtype} {case}")
+    k_lens = k_lens or q_lens
+    if bs:
+        c = synth.paged_prefill_case(90 + len(q_lens), q_lens, k_lens, Hq, Hkv, D, bs, dtype,
+                                     sink, window_left=window, poison=True)
+    else:
+        c = synth.prefill_case(90 + len(q_lens), q_lens, k_lens, Hq, Hkv, D, dtype, sink,
+                               window_left=window)
+    out, lse = run_prefill(c, causal=False)
+    o, l = oracle_prefill(c, causal=False)
+    assert_close(out, o, dtype, "out")
+    assert_close(lse, l, dtype, "lse", lse=True)
+
+
+def test_prefill_noncausal_differs_from_causal():
+    """The flag reaches the kernel: a non-causal call equals the oracle's
+    non-causal result and not its causal one."""
+    banner("prefill non-causal vs causal")
+    c = synth.prefill_case(99, [200, 70], [200, 70], 8, 2, 128, torch.bfloat16, True)
+    out, _ = run_prefill(c, causal=False)
+    o_nc, _ = oracle_prefill(c, causal=False)
+    o_c, _ = oracle_prefill(c, causal=True)
+    assert_close(out, o_nc, torch.bfloat16, "non-causal")
+    assert (out.float().cpu() - torch.as_tensor(o_c).float()).abs().max() > 0.1
 
 
 @pytest.mark.parametrize("heads", [(4, 4), (8, 4), (12, 4), (8, 2), (12, 2), (16, 2), (16, 1)],

@@ -148,6 +148,43 @@ def test_prefill_rope(case, dtype):
     assert_close(lse, l, dtype, "prefill rope lse", lse=True)
 
 
+@pytest.mark.parametrize("case", [
+    ([33, 200], [500, 200], 12, 4, 128, 64, True),
+    ([100, 5], [40, 5], 8, 2, 64, 64, False),         # rows 0..59 of request 0 at p < 0
+], ids=["chunk", "lq_gt_lk"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_prefill_rope_noncausal(case, dtype):
+    """q rotated inside a non-causal prefill.  Rows at a negative position
+    (more queries than keys) have no table row: they are not rotated, and
+    (non-causal) still see every key."""
+    from paged_kv_cache_02_amd import pkv
+    q_lens, k_lens, Hq, Hkv, D, rd, neox = case
+    banner(f"prefill rope non-causal {dtype} {case}")
+    c = synth.prefill_case(540 + len(q_lens), q_lens, k_lens, Hq, Hkv, D, dtype, True)
+    n_pos = max(k_lens)
+    tab = pkv.rope_cos_sin(n_pos, rd, 10000.0)
+    otab = oracle.rope_cos_sin(n_pos, rd, 10000.0)
+    kpos = np.concatenate([np.arange(L) for L in k_lens]).astype(np.int32)
+    krot = synth.to_dtype(oracle.rope_apply(c.k, kpos, otab, rd, neox).astype(np.float32),
+                          dtype)
+    T = c.q.shape[0]
+    lse = torch.empty(T, Hq, dtype=torch.float32, device="cuda")
+    out = pkv.varlen_prefill(dev(c.q), dev(c.cu_seqlens_q), dev(c.cu_seqlens_k), c.max_seqlen_q,
+                             c.max_seqlen_k, c.sm_scale, Hkv, k=dev(krot), v=dev(c.v),
+                             sink=dev(c.sink), lse=lse, rope_cos_sin=tab, rotary_dim=rd,
+                             rope_neox=neox, causal=False)
+    torch.cuda.synchronize()
+    qpos = oracle.query_positions(c.cu_seqlens_q, c.cu_seqlens_k)
+    at = qpos >= 0
+    qrot = c.q.double().numpy().copy()
+    qrot[at] = oracle.rope_apply(c.q[torch.from_numpy(at)], qpos[at], otab, rd, neox)
+    o, l = oracle.varlen_prefill(torch.from_numpy(qrot).float(), c.cu_seqlens_q, c.cu_seqlens_k,
+                                 c.sink, c.sm_scale, Hkv, k=krot.float(), v=c.v.float(),
+                                 causal=False)
+    assert_close(out, o, dtype, "prefill rope non-causal out")
+    assert_close(lse, l, dtype, "prefill rope non-causal lse", lse=True)
+
+
 def test_prefill_rejects_mixed_dtypes():
     """K or V of another dtype than q is refused before any launch (the
     kernels would read its bytes as q's type)."""

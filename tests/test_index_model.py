@@ -37,11 +37,13 @@ def heads_per_unit(G):
 # prefill_bf16_kernel (csrc/prefill.hip)
 # ---------------------------------------------------------------------------
 
-def model_prefill(q_lens, k_lens, Hq, Hkv, D, window=-1, paged_bs=0, rope_rows=None):
+def model_prefill(q_lens, k_lens, Hq, Hkv, D, window=-1, paged_bs=0, rope_rows=None,
+                  causal=True):
     """Every access of one prefill launch; returns the number of (workgroup,
     step) blocks that did work.  rope_rows: rows of the rotary table (>= max
-    Lk), or None.  With a window the launch walks runs of position blocks
-    (run_steps blocks per workgroup), otherwise one block per workgroup."""
+    Lk), or None.  With a causal window the launch walks runs of position
+    blocks (run_steps blocks per workgroup), otherwise one block per
+    workgroup.  Non-causal blocks read keys up to the request's last."""
     B = len(q_lens)
     cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64)
     cu_k = np.concatenate([[0], np.cumsum(k_lens)]).astype(np.int64)
@@ -50,7 +52,7 @@ def model_prefill(q_lens, k_lens, Hq, Hkv, D, window=-1, paged_bs=0, rope_rows=N
     bm = BM // hpw
     ng = G // hpw
     max_q = max(q_lens, default=0)
-    if window >= 0:
+    if window >= 0 and causal:
         per_req = (max_q + bm - 1) // bm
         blocks = B * per_req * ng * Hkv
         steps = min(16, max(1, blocks // (2 * CUS)))
@@ -93,7 +95,7 @@ def model_prefill(q_lens, k_lens, Hq, Hkv, D, window=-1, paged_bs=0, rope_rows=N
     pos0 = Lk - Lq + row0
     pos_last = pos0 + nrows - 1
     kv_lo = np.maximum(0, pos0 - window) if window >= 0 else np.zeros_like(pos0)
-    kv_hi = np.minimum(Lk, pos_last + 1)
+    kv_hi = np.minimum(Lk, pos_last + 1) if causal else Lk
     t_begin = kv_lo & ~(BN - 1)
     ntiles = np.where(kv_hi > kv_lo, (kv_hi - t_begin + BN - 1) // BN, 0)
     # K/V tiles: the first and the last tile issued lie inside the request's keys
@@ -292,6 +294,8 @@ def prefill_shapes():
         shapes.append((q_lens, k_lens or q_lens, Hq, Hkv, D, window, 0))
     for q_lens, k_lens, Hq, Hkv, D, bs, sink, window in P.PAGED:
         shapes.append((q_lens, k_lens, Hq, Hkv, D, window, bs))
+    for q_lens, k_lens, Hq, Hkv, D, sink, window, bs in P.NONCAUSAL:
+        shapes.append((q_lens, k_lens or q_lens, Hq, Hkv, D, window, bs))
     for case in R.PREFILL:
         q_lens, k_lens, Hq, Hkv, D, rd, neox, bs = case
         shapes.append((q_lens, k_lens or q_lens, Hq, Hkv, D, -1, bs))
@@ -311,14 +315,15 @@ def prefill_shapes():
     return shapes
 
 
+@pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("window_override", [None, 0, 50])
-def test_prefill_mapping_in_bounds(window_override):
+def test_prefill_mapping_in_bounds(window_override, causal):
     n = 0
     for q_lens, k_lens, Hq, Hkv, D, window, bs in prefill_shapes():
         w = window if window_override is None else window_override
         for paged in sorted({0, bs}):
             n += model_prefill(q_lens, k_lens, Hq, Hkv, D, w, paged,
-                               rope_rows=max(max(k_lens, default=0), 1))
+                               rope_rows=max(max(k_lens, default=0), 1), causal=causal)
     assert n > 0
 
 
