@@ -190,7 +190,8 @@ pkv_status pkv_reshape_and_cache_rope(const void *key, const void *value, void *
  *     the balanced schedule's arrival counters; no other mode writes them;
  *   - partition_size == 0 (bf16, B <= 4096): the balanced schedule's
  *     partial results after them, (4 * W + B) * Hq * (head_dim + 1) floats
- *     plus B + 2 ints, W = ceil(compute units / head groups);
+ *     plus B + 2 ints, W = ceil(compute units / head groups), then room for
+ *     q rotated by pkv_paged_decode_append (B * Hq * head_dim bf16);
  *   - partition_size > 0 and max_seqlen_k > partition_size: float32
  *     part_out [B, Hq, P, head_dim] and part_lse [B, Hq, P],
  *     P = ceil(max_seqlen_k / partition_size), after them.
@@ -303,6 +304,17 @@ pkv_status pkv_paged_decode_noalloc(void *out, float *lse, const void *q, const 
  *                   of the call reads the slot of position cache_seqlens[b].
  *   max_seqlen_k    host upper bound on cache_seqlens; max_seqlen_k + 1 <=
  *                   max_blocks_per_seq * block_size
+ *   rope_cos_sin    NULL, or a pkv_rope_cos_sin table of rope_positions rows
+ *                   (>= max_seqlen_k + 1) with rotary_dim (a multiple of 32
+ *                   in [32, head_dim]) and rope_neox as for pkv_rope_apply:
+ *                   q and k_new are then rotated by the new token's position
+ *                   cache_seqlens[b] inside the call (vLLM page,
+ *                   PagedAttentionWithRoPE.forward: query and key rotated
+ *                   before attention), the rotated key is what the cache
+ *                   receives, and q itself is not modified.  The cached keys
+ *                   must already be rotated (pkv_reshape_and_cache_rope).
+ *                   Equal to pkv_rope_apply on q and k_new followed by this
+ *                   call without a table.
  *   workspace       bf16: at least pkv_paged_decode_workspace_bytes(B,
  *                   num_q_heads, head_dim, max_seqlen_k + 1, 0) bytes,
  *                   reused under the same rules as pkv_paged_decode's
@@ -319,8 +331,10 @@ pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const v
                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                    int32_t num_blocks, int32_t max_blocks_per_seq,
                                    int32_t max_seqlen_k, float sm_scale, int32_t window_left,
-                                   const float *alibi_slopes, void *workspace,
-                                   size_t workspace_bytes, pkv_dtype dtype, void *stream);
+                                   const float *alibi_slopes, const float *rope_cos_sin,
+                                   int32_t rope_positions, int32_t rotary_dim, int32_t rope_neox,
+                                   void *workspace, size_t workspace_bytes, pkv_dtype dtype,
+                                   void *stream);
 
 /*
  * The two stages of pkv_paged_decode with partition_size == 0 in bf16 (the

@@ -89,7 +89,7 @@ int stream_ranges_per_head_group(int Hq, int Hkv) {
 size_t counter_bytes(int32_t Hq) { return align256((size_t)kStreamMaxB * Hq * sizeof(uint64_t)); }
 
 struct StreamLayout {
-    size_t counters, part_out, part_lse, cum, total;
+    size_t counters, part_out, part_lse, cum, q_rot, total;
 };
 StreamLayout stream_layout_hu(int32_t B, int32_t Hq, int HU, int32_t D) {
     const size_t slots = (size_t)stream_ranges_hu(Hq, HU) + B;
@@ -98,7 +98,9 @@ StreamLayout stream_layout_hu(int32_t B, int32_t Hq, int HU, int32_t D) {
     l.part_out = counter_bytes(Hq);
     l.part_lse = l.part_out + align256(slots * Hq * D * sizeof(float));
     l.cum = l.part_lse + align256(slots * Hq * sizeof(float));
-    l.total = l.cum + align256((size_t)(B + 2) * sizeof(int32_t));
+    l.q_rot = l.cum + align256((size_t)(B + 2) * sizeof(int32_t));
+    // q rotated by the append-with-rope call, bf16 [B, Hq, D]
+    l.total = l.q_rot + align256((size_t)B * Hq * D * 2);
     return l;
 }
 StreamLayout stream_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t D) {
@@ -425,7 +427,9 @@ pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const v
                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                    int32_t num_blocks, int32_t max_blocks_per_seq,
                                    int32_t max_seqlen_k, float sm_scale, int32_t window_left,
-                                   const float *alibi_slopes, void *workspace, size_t workspace_bytes, pkv_dtype dtype,
+                                   const float *alibi_slopes, const float *rope_cos_sin,
+                                   int32_t rope_positions, int32_t rotary_dim, int32_t rope_neox,
+                                   void *workspace, size_t workspace_bytes, pkv_dtype dtype,
                                    void *stream)
 {
     if (B < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_seqlen_k < 0)
@@ -438,6 +442,13 @@ pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const v
     // the new token goes to position cache_seqlens[b] <= max_seqlen_k
     if ((long long)max_seqlen_k + 1 > (long long)max_blocks_per_seq * block_size)
         return PKV_ERR_SHAPE;
+    if (rope_cos_sin) {
+        // q and k_new rotated by position cache_seqlens[b]: rotary_dim a
+        // multiple of 32 within the head, a table row for every such position
+        if (rotary_dim < 32 || rotary_dim > head_dim || rotary_dim % 32)
+            return PKV_ERR_UNSUPPORTED;
+        if ((long long)rope_positions < (long long)max_seqlen_k + 1) return PKV_ERR_SHAPE;
+    }
     if (dtype == PKV_BF16 && B > kStreamMaxB) return PKV_ERR_SHAPE;
     if (B == 0) return PKV_OK;
     if (num_blocks == 0) return PKV_ERR_SHAPE;
@@ -458,6 +469,8 @@ pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const v
         a.counters = (uint64_t *)((char *)workspace + lay.counters);
         a.out = out; a.lse = lse; a.sink = sink;
         a.k_new = k_new; a.v_new = v_new; a.append = 1;
+        a.rope = rope_cos_sin; a.rope_dim = rotary_dim; a.rope_neox = rope_neox != 0;
+        a.q_rot = (char *)workspace + lay.q_rot;
         a.mode = kStreamAppend;
         return launch_decode_stream_bf16(a, s);
     }
@@ -470,6 +483,7 @@ pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const v
     a.mbps = max_blocks_per_seq; a.window_left = window_left;
     a.part_size = max_seqlen_k + 1; a.nparts = 1; a.split = 0;
     a.scale_log2 = sm_scale * kLog2e;
+    a.rope = rope_cos_sin; a.rope_dim = rotary_dim; a.rope_neox = rope_neox != 0;
     return launch_rows(a, s);
 }
 

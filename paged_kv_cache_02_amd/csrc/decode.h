@@ -65,6 +65,13 @@ struct StreamArgs {
     const void *k_new;
     const void *v_new;
     int32_t append;              // 0 or 1
+    // Append with rotary embedding (rope != null): the [positions, rope_dim]
+    // table, cos then sin.  k_new is rotated by its position as it is stored,
+    // and q by the same position into q_rot [B, Hq, D] (workspace), which the
+    // waves then read in place of q.
+    const float *rope;
+    int32_t rope_dim, rope_neox;
+    void *q_rot;
     int32_t mode;                // kStream*
     // parts mode: part_out [B, Hq, max_parts, D] / part_lse [B, Hq, max_parts]
     int32_t part_size, max_parts;

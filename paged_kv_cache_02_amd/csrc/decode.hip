@@ -48,6 +48,7 @@
 
 #include "common.h"
 #include "decode.h"
+#include "rope.h"
 
 namespace pkv {
 
@@ -641,6 +642,31 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(Stream
         }
         return v;
     };
+    // Append with rotary embedding: this wave's q rows (its head group, every
+    // sequence its range meets) rotated by the new token's position into
+    // q_rot, read back below in place of q.  Waves that share a sequence
+    // write the same bytes; each reads only rows it has written itself.
+    const void *qsrc = a.q;
+    if constexpr (APPEND) {
+        if (a.rope) {
+            constexpr int LPR = D / 8;            // 16-byte chunks per head row
+            const int b_last = seq_of(x_end - 1);
+            const int total = (b_last - b_ld + 1) * HU * LPR;
+            for (int base = 0; base < total; base += 64) {
+                const int e = base + lane;
+                if (e < total) {
+                    const int b = b_ld + e / (HU * LPR);
+                    const int hh = (e / LPR) % HU;
+                    const size_t row = ((size_t)b * a.Hq + h0 + hh) * D * 2;
+                    rope_chunk<true>((const char *)a.q + row, (char *)a.q_rot + row,
+                                     a.rope + (size_t)(s_len[b] - 1) * a.rope_dim, a.rope_dim,
+                                     a.rope_neox != 0, e % LPR);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            qsrc = a.q_rot;
+        }
+    }
     int xb = x0, blk_batch = gather(x0), blk_ahead = 0;
     if (x0 + 64 < x_end) blk_ahead = gather(x0 + 64);
 
@@ -661,8 +687,8 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(Stream
         }
         q_nb = readfirstlane(lo);
     }
-    w.load_q(a.q, (size_t)q_held * a.Hq + h0);
-    if (q_nb >= 0) w.load_q_to(q_next, a.q, (size_t)q_nb * a.Hq + h0);
+    w.load_q(qsrc, (size_t)q_held * a.Hq + h0);
+    if (q_nb >= 0) w.load_q_to(q_next, qsrc, (size_t)q_nb * a.Hq + h0);
     __builtin_amdgcn_sched_barrier(0);
     auto block_at = [&]() {
         if (x_ld - xb >= 64) {                    // next batch (read 64 tiles ago)
@@ -824,6 +850,8 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(Stream
         // v_new into the cache slot itself and waits for its stores before
         // its first tile load.  (Head groups that share a kv head each copy
         // the same bytes.)  Sequences b_ld .. b_end-1 end inside the range.
+        // With a rotary table the key row is rotated by position L as it is
+        // copied.
         int b_end = b_ld;
         while (b_end < a.B && s_cum[b_end + 1] <= x_end) ++b_end;
         constexpr int LPR = D / 8;                // lanes per row, 16 bytes each
@@ -835,12 +863,17 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(Stream
                 const int L = s_len[b] - 1;
                 const int blk = a.block_table[(size_t)b * a.mbps + (L >> a.bs_log2)];
                 const bool is_v = part >= LPR;
-                const size_t col = (size_t)g * D + 8 * (part % LPR);
+                const int u = part % LPR;
                 const char *src = (const char *)(is_v ? a.v_new : a.k_new) +
-                                  ((size_t)b * a.Hkv * D + col) * 2;
-                char *dst = (char *)(is_v ? a.v_cache : a.k_cache) +
-                            row_off(blk, L) + col * 2;
-                *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(src);
+                                  ((size_t)b * a.Hkv + g) * D * 2;
+                char *dst = (char *)(is_v ? a.v_cache : a.k_cache) + row_off(blk, L) +
+                            (size_t)g * D * 2;
+                if (!is_v && a.rope)
+                    rope_chunk<true>(src, dst, a.rope + (size_t)L * a.rope_dim, a.rope_dim,
+                                     a.rope_neox != 0, u);
+                else
+                    *reinterpret_cast<u32x4 *>(dst + 16 * u) =
+                        *reinterpret_cast<const u32x4 *>(src + 16 * u);
             }
         }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -899,7 +932,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(Stream
 #pragma unroll
                             for (int c = 0; c < DW::KSTEPS; ++c) w.qf[c] = q_next[c];
                         } else {
-                            w.load_q(a.q, (size_t)seg_b * a.Hq + h0);
+                            w.load_q(qsrc, (size_t)seg_b * a.Hq + h0);
                             // Wait for Q here, inside the rare branch: otherwise the
                             // wait lands after the join and drains the ring every trip.
                             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);

@@ -65,12 +65,12 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
         qv[e] = ld_elem(a.q, qrow * D + lane + 64 * e);
         acc[e] = 0.f;
     }
-    if (a.mode == 1 && a.rope && pos >= 0) {
-        // rotary embedding of q at its position: the partner element is read
-        // from memory (neox: d +- rope_dim / 2; interleaved: d ^ 1).  A row
-        // at a negative position (Lq > Lk) has no table row and is not rotated.
+    // Rotary embedding of row x (elements row0 .. row0 + D) at position p,
+    // this lane's elements xv: the partner element is read from memory
+    // (neox: d +- rope_dim / 2; interleaved: d ^ 1).
+    auto rotate = [&](float (&xv)[E], const void *x, size_t row0, int p) {
         const int rd = a.rope_dim, half = rd / 2;
-        const float *tab = a.rope + (size_t)pos * rd;
+        const float *tab = a.rope + (size_t)p * rd;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const int d = lane + 64 * e;
@@ -78,11 +78,15 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
             const bool hi = a.rope_neox ? d >= half : (d & 1);
             const int pd = a.rope_neox ? (hi ? d - half : d + half) : (d ^ 1);
             const int i = a.rope_neox ? (hi ? d - half : d) : d / 2;
-            const float xp = ld_elem(a.q, qrow * D + pd);
+            const float xp = ld_elem(x, row0 + pd);
             const float co = tab[i], si = tab[half + i];
-            qv[e] = hi ? fmaf(qv[e], co, xp * si) : fmaf(qv[e], co, -xp * si);
+            xv[e] = hi ? fmaf(xv[e], co, xp * si) : fmaf(xv[e], co, -xp * si);
         }
-    }
+    };
+    // q at its position (prefill: Lk - Lq + i; decode with append: the new
+    // token's).  A prefill row at a negative position (Lq > Lk) has no table
+    // row and is not rotated.
+    if ((a.mode == 1 || a.append) && a.rope && pos >= 0) rotate(qv, a.q, qrow * D, pos);
 #pragma unroll
     for (int e = 0; e < E; ++e) qv[e] *= a.scale_log2;
     float m = kNoMax, l = 0.f;
@@ -90,16 +94,25 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
     const float slope_log2 = a.alibi ? a.alibi[h] * kLog2e : 0.f;
     const int32_t *bt = a.block_table ? a.block_table + (size_t)req * a.mbps : nullptr;
     const int bs_mask = (1 << a.bs_log2) - 1;
+    // decode with append: the new token's key (rotated by its position with
+    // a rotary table), which every wave of this call reads from here
+    float kn[E] = {};
+    if (a.mode == 0 && a.append) {
+        const size_t src = ((size_t)req * a.Hkv + g) * D;
+#pragma unroll
+        for (int e = 0; e < E; ++e) kn[e] = ld_elem(a.k_new, src + lane + 64 * e);
+        if (a.rope) rotate(kn, a.k_new, src, Lk - 1);
+    }
     if (a.mode == 0 && a.append && h % a.G == 0 && pidx == 0) {
         // store the new token at position Lk - 1; every wave of this call reads
-        // that key from k_new / v_new, so no reader waits for this store
+        // that key from kn / v_new, so no reader waits for this store
         const int L = Lk - 1;
         const size_t slot = ((size_t)bt[L >> a.bs_log2] << a.bs_log2) + (L & bs_mask);
         const size_t src = ((size_t)req * a.Hkv + g) * D, dst = (slot * a.Hkv + g) * D;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const int d = lane + 64 * e;
-            ((float *)a.k_cache)[dst + d] = ((const float *)a.k_new)[src + d];
+            ((float *)a.k_cache)[dst + d] = kn[e];
             ((float *)a.v_cache)[dst + d] = ((const float *)a.v_new)[src + d];
         }
     }
@@ -120,9 +133,11 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
             vb = a.v_cache;
         }
         const size_t off = (row * a.Hkv + g) * D;
+        const bool is_new = a.mode == 0 && a.append && jj == Lk - 1;
         float s = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) s = fmaf(qv[e], ld_elem(kb, off + lane + 64 * e), s);
+        for (int e = 0; e < E; ++e)
+            s = fmaf(qv[e], is_new ? kn[e] : ld_elem(kb, off + lane + 64 * e), s);
 #pragma unroll
         for (int msk = 1; msk < 64; msk <<= 1) s += shfl_xor(s, msk);
         s = fmaf(slope_log2, (float)(jj - pos), s);

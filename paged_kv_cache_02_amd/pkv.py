@@ -45,7 +45,8 @@ SIGNATURES = {
                                                 ctypes.c_int, _P]),
     "pkv_paged_decode_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32,
                                                _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F,
-                                               _I32, _P, _P, _SZ, ctypes.c_int, _P]),
+                                               _I32, _P, _P, _I32, _I32, _I32, _P, _SZ,
+                                               ctypes.c_int, _P]),
     "pkv_paged_decode_stage": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                               _I32, _I32, _I32, _F, _I32, _P, _P, _SZ,
                                               ctypes.c_int, _P]),
@@ -268,17 +269,21 @@ def paged_decode_noalloc(q, k_cache, v_cache, block_table, cache_seqlens, sm_sca
 def paged_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens,
                         sm_scale: float, sink=None, window_left: int = -1,
                         max_seqlen_k: Optional[int] = None, out=None, lse=None, workspace=None,
-                        alibi_slopes=None):
+                        alibi_slopes=None, rope_cos_sin=None, rotary_dim: int = 0,
+                        rope_neox: bool = True):
     """Store k_new/v_new [B,Hkv,D] at position cache_seqlens[b] of each sequence and
     attend q [B,Hq,D] to keys 0..cache_seqlens[b]; cache_seqlens is not changed.
+    With rope_cos_sin, q and k_new are rotated by that position in the call.
 
-    The bf16 path needs a zero-filled workspace of
-    decode_workspace_bytes(B, Hq, D, max_seqlen_k + 1) bytes (allocated for
-    this call when none is given); fp32 needs none."""
+    The bf16 path needs a workspace of decode_workspace_bytes(B, Hq, D,
+    max_seqlen_k + 1) bytes (allocated for this call when none is given);
+    fp32 needs none."""
     B, Hq, D = q.shape
     NB, bs, Hkv, _ = k_cache.shape
     if max_seqlen_k is None:
         max_seqlen_k = int(cache_seqlens.max().item()) if B else 0
+    if rope_cos_sin is not None:
+        _rope_table(rope_cos_sin, rotary_dim)
     if out is None:
         out = torch.empty_like(q)
     need = decode_workspace_bytes(B, Hq, D, max_seqlen_k + 1)
@@ -289,8 +294,9 @@ def paged_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_se
         _ptr(v_cache), _ptr(_i32(block_table, "block_table")),
         _ptr(_i32(cache_seqlens, "cache_seqlens")), _ptr(_f32(sink, "sink")), B, Hq, Hkv, D, bs,
         NB, block_table.shape[1], max_seqlen_k, float(sm_scale), window_left,
-        _ptr(_f32(alibi_slopes, "alibi_slopes")), _ptr(workspace),
-        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _ptr(_f32(alibi_slopes, "alibi_slopes")), _ptr(rope_cos_sin),
+        0 if rope_cos_sin is None else rope_cos_sin.shape[0], rotary_dim, int(bool(rope_neox)),
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
         _dt(q, k_new, v_new, k_cache, v_cache, out),
         _stream()), "paged_decode_append")
     return out

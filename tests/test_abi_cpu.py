@@ -102,9 +102,8 @@ def test_decode_validation(over, status):
 def append_call(**over):
     a = dict(out=FAKE, lse=None, q=FAKE, k_new=FAKE, v_new=FAKE, k_cache=FAKE, v_cache=FAKE,
              block_table=FAKE, cache_seqlens=FAKE, sink=None, B=2, Hq=8, Hkv=2, D=128, bs=16,
-             NB=4, MB=4, max_seqlen_k=63, scale=0.1, window=-1, alibi=None, ws=None, ws_bytes=0,
-             dt=1,
-             stream=None)
+             NB=4, MB=4, max_seqlen_k=63, scale=0.1, window=-1, alibi=None, rope=None,
+             rope_pos=0, rope_dim=0, rope_neox=1, ws=None, ws_bytes=0, dt=1, stream=None)
     a.update(over)
     return lib.pkv_paged_decode_append(*a.values())
 
@@ -126,6 +125,10 @@ def append_call(**over):
     (dict(k_new=FAKE + 8), pkv.PKV_ERR_UNSUPPORTED),   # misaligned
     (dict(ws=None), pkv.PKV_ERR_WORKSPACE),          # bf16 needs the balanced workspace
     (dict(ws=FAKE, ws_bytes=10), pkv.PKV_ERR_WORKSPACE),
+    (dict(rope=FAKE, rope_pos=64, rope_dim=48), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(rope=FAKE, rope_pos=64, rope_dim=256), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(rope=FAKE, rope_pos=63, rope_dim=64), pkv.PKV_ERR_SHAPE),   # no row for position 63
+    (dict(rope=FAKE, rope_pos=64, rope_dim=64, B=0), pkv.PKV_OK),
     (dict(B=0), pkv.PKV_OK),                         # no-op, nothing launched
 ])
 def test_decode_append_validation(over, status):

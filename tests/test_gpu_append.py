@@ -151,3 +151,59 @@ def test_append_config2_full_size():
         want = before.view(-1, c.Hkv, c.D).clone()
         want[slots] = dev(new)
         assert torch.equal(got.view(-1, c.Hkv, c.D).view(torch.int16), want.view(torch.int16))
+
+
+ROPE = [
+    # lengths already cached, Hq, Hkv, D, block size, window, rotary_dim, neox
+    ([0, 1, 15, 16, 17, 31, 32, 33, 100, 257], 8, 2, 128, 16, -1, 128, True),
+    ([5, 64, 300, 1000], 32, 8, 128, 16, 127, 64, False),
+    ([40, 0, 63, 64], 16, 16, 64, 32, -1, 32, True),
+    ([77, 200, 15], 12, 4, 128, 64, 20, 96, True),      # G 3, a quarter of the dims pass through
+]
+
+
+@pytest.mark.parametrize("case", ROPE, ids=[str(i) for i in range(len(ROPE))])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_append_rope(case, dtype):
+    """q and k_new rotated by the new token's position inside the append
+    call (vLLM page, PagedAttentionWithRoPE.forward: rotate, then attend).
+    The oracle rotates with its own table, rounds to the storage type as
+    the kernel does, and runs its decode_append; q itself is unchanged, the
+    cache receives the rotated key, and every other cache byte is unchanged."""
+    from paged_kv_cache_02_amd import pkv
+    lens, Hq, Hkv, D, bs, window, rd, neox = case
+    banner(f"append rope {dtype} {case}")
+    c, L, kn, vn = make_case(330 + len(lens), lens, Hq, Hkv, D, bs, dtype, True, window)
+    n_pos = int(L.max()) + 1
+    tab = pkv.rope_cos_sin(n_pos, rd, 10000.0)
+    otab = oracle.rope_cos_sin(n_pos, rd, 10000.0)      # the oracle's own table
+    validate.check_decode(c.block_table, L, c.num_blocks, c.block_size, int(L.max()), append=True)
+    q, kc, vc = dev(c.q), dev(c.k_cache), dev(c.v_cache)
+    q0 = q.clone()
+    lse = torch.empty((c.q.shape[0], Hq), dtype=torch.float32, device="cuda")
+    out = pkv.paged_decode_append(q, dev(kn), dev(vn), kc, vc, dev(c.block_table), dev(L),
+                                  c.sm_scale, sink=dev(c.sink), window_left=window,
+                                  max_seqlen_k=int(L.max()), lse=lse, rope_cos_sin=tab,
+                                  rotary_dim=rd, rope_neox=neox)
+    torch.cuda.synchronize()
+    bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(q.view(bits), q0.view(bits)), "q modified"
+    pos = L.numpy().astype(np.int32)
+    qr = synth.to_dtype(oracle.rope_apply(c.q, pos, otab, rd, neox).astype(np.float32), dtype)
+    kr = synth.to_dtype(oracle.rope_apply(kn, pos, otab, rd, neox).astype(np.float32), dtype)
+    o, l, okc, ovc = oracle.decode_append(qr, kr, vn, c.k_cache, c.v_cache, c.block_table, L,
+                                          c.sink, c.sm_scale, window)
+    assert_close(out, o, dtype, "append rope out")
+    assert_close(lse, l, dtype, "append rope lse", lse=True)
+    assert torch.equal(vc.cpu().view(bits), ovc.view(bits)), "v_cache"
+    # the rotated keys at the new slots (the kernel rotates in float32, the
+    # oracle in float64: one unit in the last place apart at most), every
+    # other slot bit for bit
+    slots = [int(c.block_table[b, Lb // bs]) * bs + Lb % bs for b, Lb in enumerate(lens)]
+    got = kc.cpu().view(-1, Hkv, D)
+    want = okc.view(-1, Hkv, D)
+    rest = np.setdiff1d(np.arange(got.shape[0]), slots)
+    assert torch.equal(got[rest].view(bits), want[rest].view(bits)), "k_cache outside the new slots"
+    g, w = got[slots].double(), want[slots].double()
+    rtol = 2.0 ** -7 if dtype == torch.bfloat16 else 1e-6
+    assert ((g - w).abs() <= 1e-6 + rtol * w.abs()).all(), float((g - w).abs().max())

@@ -207,6 +207,16 @@ def model_decode_stream(lens, Hq, Hkv, bs, mbps, window=-1, append=False):
         # the owner of each sequence's last tile stores row L - 1 (the new token)
         pos = L - 1
         assert ((pos >> int(math.log2(bs))) < mbps).all()
+        # with a rotary table each wave rotates the q rows of the sequences
+        # its range meets, b_first .. b_last, into q_rot [B, Hq, D], reading
+        # table row L - 1 (the table has max(lens) + 1 rows)
+        rope_rows = int(L.max()) if B else 0
+        for w in np.unique(gw).tolist():
+            xs = x[gw == w]
+            b_first, b_last = int(b[xs[0]]), int(b[xs[-1]])
+            assert 0 <= b_first <= b_last < B
+            assert ((L[b_first:b_last + 1] - 1) < rope_rows).all(), "rotary row outside the table"
+            assert ((L[b_first:b_last + 1] - 1) >= 0).all()
     return T
 
 
