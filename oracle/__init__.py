@@ -85,6 +85,9 @@ def _load():
         lib.oracle_token_request.argtypes = [P, I, I, P]
         lib.oracle_slot_of.argtypes = [P, I, I]
         lib.oracle_slot_of.restype = ctypes.c_longlong
+        lib.oracle_vertical_slash_blocks.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I]
+        lib.oracle_masked_prefill.argtypes = [P, P, P, P, P, P, I, I, I, I, D, P, I, P, I, P, I,
+                                              I]
         _lib = lib
     return _lib
 
@@ -209,6 +212,112 @@ def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, sink, sm_scale: float, num_kv_
         0 if un is None else len(un), _threads(nthreads))
     assert rc == 0
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Vertical + slash sparse prefill (nano-vllm "minference.py" page,
+# MInferencePolicy.estimate_pattern / sparse_prefill_attention, 64 x 64
+# blocks).  The block form is the reading stated in oracle.c: key block n is a
+# slash block of row block m when a diagonal of the head meets it within m's
+# rows; vertical columns outside those blocks are listed one by one.
+# ---------------------------------------------------------------------------
+
+SPARSE_BLOCK = 64
+
+
+def vertical_slash_blocks(vertical, slash, cu_seqlens, max_seqlen: int):
+    """Block lists of every (request, head, 64-row block).  vertical [B,H,NV]
+    key positions (ascending), slash [B,H,NS] diagonal offsets i - j.  Returns
+    ``(block_count [B,H,NM], block_offset [B,H,NM,NM], column_count [B,H,NM],
+    column_index [B,H,NM,NV])``, NM = ceil(max_seqlen / 64); entries past a
+    count are -1."""
+    V = np.ascontiguousarray(vertical, dtype=np.int32)
+    S = np.ascontiguousarray(slash, dtype=np.int32)
+    cu = np.ascontiguousarray(_np(cu_seqlens), dtype=np.int32)
+    B, H, NV = V.shape
+    NS = S.shape[2]
+    assert S.shape[:2] == (B, H) and len(cu) == B + 1
+    NM = (int(max_seqlen) + SPARSE_BLOCK - 1) // SPARSE_BLOCK
+    bc = np.zeros((B, H, NM), dtype=np.int32)
+    bo = np.full((B, H, NM, NM), -1, dtype=np.int32)
+    cc = np.zeros((B, H, NM), dtype=np.int32)
+    ci = np.full((B, H, NM, NV), -1, dtype=np.int32)
+    rc = _load().oracle_vertical_slash_blocks(_ptr(bc), _ptr(bo), _ptr(cc), _ptr(ci), _ptr(V),
+                                              _ptr(S), _ptr(cu), B, H, NV, NS, NM)
+    assert rc == 0
+    return bc, bo, cc, ci
+
+
+def block_sparse_mask(block_count, block_offset, column_count, column_index, cu_seqlens,
+                      num_heads: int, units: Optional[Sequence[int]] = None) -> np.ndarray:
+    """The explicit key mask the block lists describe: row i of request r
+    (64-row block m = i // 64) of head h sees key j iff j <= i and j lies in
+    one of m's 64-key blocks or is one of m's columns.  One row of W =
+    ceil(max L / 64) uint64 words per unit (t * Hq + h), bit j % 64 of word
+    j // 64; all units, or those listed."""
+    cu = np.asarray(_np(cu_seqlens), dtype=np.int64)
+    B = len(cu) - 1
+    T = int(cu[-1])
+    Lmax = int((cu[1:] - cu[:-1]).max()) if B else 0
+    W = max(1, (Lmax + 63) // 64)
+    ids = np.arange(T * num_heads) if units is None else np.asarray(units, dtype=np.int64)
+    req = token_request(cu.astype(np.int32), T)
+    out = np.zeros((len(ids), W), dtype=np.uint64)
+    cache = {}
+    for n, uid in enumerate(ids.tolist()):
+        t, h = divmod(uid, num_heads)
+        r = int(req[t])
+        i = t - int(cu[r])
+        m = i // SPARSE_BLOCK
+        key = (r, h, m)
+        if key not in cache:
+            vis = np.zeros(W * 64, dtype=bool)
+            for k in range(int(block_count[r, h, m])):
+                off = int(block_offset[r, h, m, k])
+                vis[off:off + SPARSE_BLOCK] = True
+            for k in range(int(column_count[r, h, m])):
+                vis[int(column_index[r, h, m, k])] = True
+            cache = {key: vis}
+        row = cache[key].copy()
+        row[i + 1:] = False
+        out[n] = np.packbits(row, bitorder="little").view(np.uint64)[:W]
+    return out
+
+
+def masked_prefill(q, k, v, cu_seqlens, mask, sink, sm_scale: float, num_kv_heads: int,
+                   units: Optional[Sequence[int]] = None, nthreads: Optional[int] = None):
+    """Self-attention prefill (Lq = Lk per request) under an explicit mask:
+    unit n (``t * Hq + h``, all or ``units``) sees exactly the keys whose bit
+    is set in ``mask[n]`` (uint64 words, as block_sparse_mask).  Returns
+    ``(out [T,Hq,D], lse [T,Hq])`` with NaN for units not computed."""
+    dt = _dtype_code(q)
+    qn, kn, vn = _np(q), _np(k), _np(v)
+    T, Hq, D = qn.shape
+    cu = np.ascontiguousarray(_np(cu_seqlens), dtype=np.int32)
+    mk = np.ascontiguousarray(mask, dtype=np.uint64)
+    un = None if units is None else np.ascontiguousarray(units, dtype=np.int32)
+    assert mk.shape[0] == (T * Hq if un is None else len(un))
+    sk = None if sink is None else _np(sink).astype(np.float32, copy=False)
+    out = np.full((T, Hq, D), np.nan)
+    lse = np.full((T, Hq), np.nan)
+    rc = _load().oracle_masked_prefill(
+        _ptr(out), _ptr(lse), _ptr(qn), _ptr(kn), _ptr(vn), _ptr(cu), len(cu) - 1, Hq,
+        int(num_kv_heads), D, float(sm_scale), _ptr(mk), mk.shape[1], _ptr(sk), dt, _ptr(un),
+        0 if un is None else len(un), _threads(nthreads))
+    assert rc == 0
+    return out, lse
+
+
+def sparse_prefill(q, k, v, cu_seqlens, vertical, slash, sink, sm_scale: float,
+                   num_kv_heads: int, units: Optional[Sequence[int]] = None,
+                   nthreads: Optional[int] = None):
+    """Vertical + slash sparse prefill: block lists, their mask, attention."""
+    cu = np.asarray(_np(cu_seqlens), dtype=np.int64)
+    Lmax = int((cu[1:] - cu[:-1]).max()) if len(cu) > 1 else 0
+    lists = vertical_slash_blocks(vertical, slash, cu_seqlens, Lmax)
+    mask = block_sparse_mask(*lists, cu_seqlens, _np(q).shape[1], units)
+    return masked_prefill(q, k, v, cu_seqlens, mask, sink, sm_scale, num_kv_heads, units,
+                          nthreads)
 
 
 def merge(part_out, part_lse, nparts_per_seq, sink):

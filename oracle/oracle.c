@@ -339,3 +339,126 @@ int oracle_reshape_and_cache(const void *key, const void *value, void *k_cache, 
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Vertical + slash sparse prefill (nano-vllm "minference.py" page,          */
+/* MInferencePolicy: estimate_pattern returns per head a set of key          */
+/* positions, vertical_indices, and a set of diagonal offsets,               */
+/* slash_indices, where a query at position i and a key at position j lie    */
+/* on diagonal i - j; sparse_prefill_attention converts them into a block    */
+/* form with block_size_M = block_size_N = 64 before attending).  The page   */
+/* does not print the conversion.  Reading taken here: row block m holds     */
+/* rows [64m, min(64m + 64, L)); key block n holds keys [64n, 64n + 64).     */
+/* Key block n is a slash block of row block m when some diagonal s of the   */
+/* head meets it within m's rows: i - s lies in block n for a row i of m,    */
+/* with 0 <= i - s.  A vertical column v (v < L, v <= m's last row) is       */
+/* listed for m when its key block is not a slash block of m.  Attention     */
+/* for row i of m then covers the keys j <= i of m's slash blocks and the    */
+/* listed columns j <= i.                                                    */
+/*                                                                           */
+/* Per request b (L = cu[b+1] - cu[b]), head h, row block m < NM:            */
+/*   block_count[b,h,m], block_offset[b,h,m, 0..count) = 64n ascending;     */
+/*   column_count[b,h,m], column_index[b,h,m, 0..count) in the order the     */
+/*   vertical indices are given.  Row blocks at or past L have no entries.  */
+/* vertical [B,H,NV], slash [B,H,NS]; entries outside [0, L) are ignored.   */
+int oracle_vertical_slash_blocks(int32_t *block_count, int32_t *block_offset,
+                                 int32_t *column_count, int32_t *column_index,
+                                 const int32_t *vertical, const int32_t *slash,
+                                 const int32_t *cu, int B, int H, int NV, int NS, int NM)
+{
+    char *sel = (char *)malloc(NM > 0 ? (size_t)NM : 1);
+    for (int b = 0; b < B; ++b) {
+        int L = cu[b + 1] - cu[b];
+        for (int h = 0; h < H; ++h) {
+            const int32_t *S = slash + ((size_t)b * H + h) * NS;
+            const int32_t *V = vertical + ((size_t)b * H + h) * NV;
+            for (int m = 0; m < NM; ++m) {
+                size_t bhm = ((size_t)b * H + h) * NM + m;
+                int r0 = 64 * m, r1 = 64 * m + 64 < L ? 64 * m + 64 : L;   /* rows [r0, r1) */
+                memset(sel, 0, (size_t)NM);
+                int nb = 0, nc = 0;
+                if (r0 < L) {
+                    for (int t = 0; t < NS; ++t) {
+                        int s = S[t];
+                        if (s < 0 || s >= L) continue;
+                        int lo = r0 - s, hi = r1 - 1 - s;     /* keys of diagonal s */
+                        if (hi < 0) continue;
+                        if (lo < 0) lo = 0;
+                        for (int n = lo / 64; n <= hi / 64; ++n) sel[n] = 1;
+                    }
+                    for (int n = 0; n < NM; ++n)
+                        if (sel[n]) block_offset[bhm * NM + nb++] = 64 * n;
+                    for (int t = 0; t < NV; ++t) {
+                        int v = V[t];
+                        if (v < 0 || v >= L || v > r1 - 1) continue;
+                        if (sel[v / 64]) continue;
+                        column_index[bhm * NV + nc++] = v;
+                    }
+                }
+                block_count[bhm] = nb;
+                column_count[bhm] = nc;
+            }
+        }
+    }
+    free(sel);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention under an explicit mask (self-attention prefill, Lq = Lk = L    */
+/* per request, packed by cu): query row t (request r, row i = t - cu[r])   */
+/* of head h sees exactly the keys j < L whose bit is set in its mask row,  */
+/* mask[(u * W) + j / 64] bit j % 64, u = the unit's index in `units` (or   */
+/* t * Hq + h without units).  Logits, sink and normalisation as above;      */
+/* nothing is implied by position (no causal bound of its own).             */
+
+typedef struct {
+    double *out, *lse;
+    const void *q, *k, *v;
+    const int32_t *cu, *tok_req;
+    const uint64_t *mask;
+    const float *sink;
+    int Hq, Hkv, D, W, dtype;
+    double scale;
+    const int32_t *units;
+} masked_ctx;
+
+static void masked_unit(void *vctx, int u, double *s, size_t *krow, int *js)
+{
+    masked_ctx *c = (masked_ctx *)vctx;
+    int id = c->units ? c->units[u] : u;          /* t*Hq + h */
+    int t = id / c->Hq, h = id % c->Hq;
+    int r = c->tok_req[t];
+    int G = c->Hq / c->Hkv, g = h / G;
+    int L = c->cu[r + 1] - c->cu[r];
+    const uint64_t *row = c->mask + (size_t)u * c->W;
+    int n = 0;
+    for (int j = 0; j < L && j < 64 * c->W; ++j) {
+        if (!((row[j / 64] >> (j % 64)) & 1u)) continue;
+        js[n] = j;
+        krow[n] = ((size_t)(c->cu[r] + j) * c->Hkv + g) * c->D;
+        ++n;
+    }
+    double sigma = c->sink ? (double)c->sink[h] : -INFINITY;
+    attend_row(c->out + (size_t)id * c->D, c->lse + id, c->q, (size_t)id * c->D, c->k, c->v,
+               krow, js, n, t - c->cu[r], 0.0, c->D, c->dtype, c->scale, sigma, s);
+}
+
+/* out [T,Hq,D], lse [T,Hq] for the rows computed (all, or `units`). */
+int oracle_masked_prefill(double *out, double *lse, const void *q, const void *k, const void *v,
+                          const int32_t *cu, int B, int Hq, int Hkv, int D, double sm_scale,
+                          const uint64_t *mask, int W, const float *sink, int dtype,
+                          const int32_t *units, int nunits, int nthreads)
+{
+    if (Hkv <= 0 || Hq % Hkv || D <= 0 || B < 0 || W < 0) return 1;
+    int T = cu[B] - cu[0];
+    int32_t *tok_req = (int32_t *)malloc(sizeof(int32_t) * (T > 0 ? T : 1));
+    oracle_token_request(cu, B, T, tok_req);
+    int maxk = 1;
+    for (int r = 0; r < B; ++r) if (cu[r + 1] - cu[r] > maxk) maxk = cu[r + 1] - cu[r];
+    masked_ctx c = {out, lse, q, k, v, cu, tok_req, mask, sink, Hq, Hkv, D, W, dtype, sm_scale,
+                    units};
+    run_units(masked_unit, &c, units ? nunits : T * Hq, nthreads, maxk);
+    free(tok_req);
+    return 0;
+}

@@ -711,4 +711,180 @@ def pin_decode_append():
         assert torch.equal(fk[s_], kn[b])
 
 
+# ---------------------------------------------------------------------------
+# Vertical + slash sparse prefill (nano-vllm "minference.py" page: vertical
+# key positions and slash diagonal offsets i - j per head, 64 x 64 blocks)
+# ---------------------------------------------------------------------------
+
+def _vs_brute(V, S, L):
+    """Block lists of one head by enumeration: for every row i of block m and
+    diagonal s, the key i - s (when >= 0) marks its 64-key block; vertical
+    columns inside the block's rows and outside those blocks are kept."""
+    NM = (L + 63) // 64
+    out = []
+    for m in range(NM):
+        rows = range(64 * m, min(64 * m + 64, L))
+        sel = set()
+        for i in rows:
+            for s_ in S:
+                if 0 <= s_ < L and i - s_ >= 0:
+                    sel.add((i - s_) // 64)
+        cols = [v for v in V if 0 <= v < L and v <= rows[-1] and v // 64 not in sel]
+        out.append(([64 * n for n in sorted(sel)], cols))
+    return out
+
+
+def _vs_lists(bc, bo, cc, ci, b, h, m):
+    return (bo[b, h, m, :bc[b, h, m]].tolist(), ci[b, h, m, :cc[b, h, m]].tolist())
+
+
+def pin_vertical_slash_brute_force():
+    """The oracle's conversion against enumeration over every (row, diagonal)
+    pair, on small requests of several row blocks; indices outside [0, L),
+    repeated diagonals and unsorted diagonals included."""
+    rng = np.random.default_rng(2594)
+    for trial in range(30):
+        B, H = 1 + trial % 2, 1 + trial % 3
+        lens = rng.integers(1, 330, size=B).tolist()
+        NV, NS = int(rng.integers(0, 12)), int(rng.integers(0, 12))
+        Lmax = max(lens)
+        V = np.sort(rng.choice(Lmax + 40, size=(B, H, NV)), axis=-1).astype(np.int32)
+        S = rng.integers(-3, Lmax + 20, size=(B, H, NS)).astype(np.int32)
+        if NS > 1:
+            S[..., 1] = S[..., 0]                            # a repeated diagonal
+        cu = synth.cu_from_lengths(lens)
+        bc, bo, cc, ci = oracle.vertical_slash_blocks(V, S, cu, Lmax)
+        NM = (Lmax + 63) // 64
+        for b in range(B):
+            for h in range(H):
+                want = _vs_brute(V[b, h].tolist(), S[b, h].tolist(), lens[b])
+                for m in range(NM):
+                    got = _vs_lists(bc, bo, cc, ci, b, h, m)
+                    exp = want[m] if m < len(want) else ([], [])
+                    assert got == exp, (trial, b, h, m, got, exp)
+
+
+def pin_vertical_slash_closed_forms():
+    """Closed forms of the conversion: every diagonal selects the causal
+    triangle of blocks 0..m; diagonal 0 alone selects block m; diagonal 64k
+    selects block m - k exactly (the rows of m shifted by a whole block);
+    diagonal 1 selects blocks m - 1 and m; no diagonal and every column lists
+    keys 0 .. m's last row."""
+    L = 300
+    cu = [0, L]
+    NM = 5
+    def lists(V, S):
+        V = np.asarray(V, dtype=np.int32).reshape(1, 1, -1)
+        S = np.asarray(S, dtype=np.int32).reshape(1, 1, -1)
+        r = oracle.vertical_slash_blocks(V, S, cu, L)
+        return [_vs_lists(*r, 0, 0, m) for m in range(NM)]
+    assert lists([], list(range(L))) == [([64 * n for n in range(m + 1)], []) for m in range(NM)]
+    assert lists([], [0]) == [([64 * m], []) for m in range(NM)]
+    for k in (1, 2):
+        assert lists([], [64 * k]) == [([64 * (m - k)] if m >= k else [], []) for m in range(NM)]
+    assert lists([], [1]) == [([0], [])] + [([64 * (m - 1), 64 * m], []) for m in range(1, NM)]
+    assert lists(list(range(L)), []) == [([], list(range(min(64 * m + 64, L)))) for m in range(NM)]
+
+
+def _masked_reference(q, k, v, mask_bool, sink, sm_scale, Hkv):
+    """numpy mask-matrix attention for one request: mask_bool [H, L, L]."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    L, Hq, _ = q.shape
+    G = Hq // Hkv
+    out = np.zeros(q.shape)
+    for h in range(Hq):
+        logits = np.where(mask_bool[h], sm_scale * q[:, h] @ k[:, h // G].T, -np.inf)
+        col = np.full((L, 1), -np.inf if sink is None else float(sink[h]))
+        full = np.concatenate([logits, col], axis=1)
+        mx = full.max(axis=1, keepdims=True)
+        mx[np.isneginf(mx)] = 0.0
+        e = np.exp(full - mx)
+        den = e.sum(axis=1, keepdims=True)
+        p = np.divide(e, den, out=np.zeros_like(e), where=den > 0)[:, :-1]
+        out[:, h] = p @ v[:, h // G]
+    return out
+
+
+def _bits(mask_bool):
+    """[units, L] bool -> [units, W] uint64 rows (bit j % 64 of word j // 64)."""
+    U, L = mask_bool.shape
+    W = max(1, (L + 63) // 64)
+    padded = np.zeros((U, W * 64), dtype=bool)
+    padded[:, :L] = mask_bool
+    return np.packbits(padded, axis=1, bitorder="little").view(np.uint64)
+
+
+def pin_masked_prefill():
+    """Attention under an explicit mask: against torch's float64 SDPA with a
+    boolean mask (no sink; every row keeps its diagonal key), against the
+    mask-matrix reference with a sink and with fully masked rows, and on a
+    subset of units."""
+    rng = np.random.default_rng(77)
+    for trial, (L, Hq, Hkv, D) in enumerate([(37, 4, 2, 8), (70, 2, 2, 16), (9, 6, 3, 8)]):
+        c = synth.prefill_case(900 + trial, [L], [L], Hq, Hkv, D, torch.float32, True,
+                               sm_scale=0.3)
+        mb = rng.random((Hq, L, L)) < 0.4
+        mb[:, np.arange(L), np.arange(L)] = True
+        units_mask = mb.transpose(1, 0, 2).reshape(L * Hq, L)    # unit t * Hq + h
+        o, _ = oracle.masked_prefill(c.q, c.k, c.v, c.cu_seqlens_q, _bits(units_mask), None,
+                                     0.3, Hkv)
+        ref = F.scaled_dot_product_attention(
+            c.q.double().transpose(0, 1)[None], c.k.double().transpose(0, 1)[None],
+            c.v.double().transpose(0, 1)[None], attn_mask=torch.from_numpy(mb)[None],
+            scale=0.3, enable_gqa=True)[0].transpose(0, 1)
+        _close(o, ref.numpy(), 1e-12, 1e-10, f"masked vs sdpa {trial}")
+        mb[:, 1, :] = False                                      # a row with no key
+        units_mask = mb.transpose(1, 0, 2).reshape(L * Hq, L)
+        o, l = oracle.masked_prefill(c.q, c.k, c.v, c.cu_seqlens_q, _bits(units_mask), c.sink,
+                                     0.3, Hkv)
+        _close(o, _masked_reference(c.q, c.k, c.v, mb, c.sink.numpy(), 0.3, Hkv), 1e-12, 1e-10,
+               f"masked vs reference {trial}")
+        _close(l[1], c.sink.numpy(), 1e-6, 1e-6, "masked row lse = sink")
+        units = [3, L * Hq - 1, Hq + 1]
+        ou, _ = oracle.masked_prefill(c.q, c.k, c.v, c.cu_seqlens_q, _bits(units_mask[units]),
+                                      c.sink, 0.3, Hkv, units=units)
+        for u in units:
+            _close(ou[u // Hq, u % Hq], o[u // Hq, u % Hq], 0, 0, "masked units")
+
+
+def pin_block_sparse_mask():
+    """The mask of the block lists is the definition written out: row i of
+    block m sees key j <= i when j's block is a slash block of m or j is a
+    vertical index; and two limits reduce to plain attention: every diagonal,
+    or every column, gives causal prefill; no index gives rows that see
+    nothing (output 0, lse = the sink)."""
+    rng = np.random.default_rng(31)
+    lens = [150, 64, 1]
+    cu = synth.cu_from_lengths(lens)
+    Hq, Hkv, D = 4, 2, 8
+    V = np.stack([np.stack([np.sort(rng.choice(160, 6, replace=False)) for _ in range(Hq)])
+                  for _ in lens]).astype(np.int32)
+    S = rng.integers(0, 160, size=(3, Hq, 4)).astype(np.int32)
+    lists = oracle.vertical_slash_blocks(V, S, cu, max(lens))
+    T = int(cu[-1])
+    got = oracle.block_sparse_mask(*lists, cu, Hq)
+    want = np.zeros((T * Hq, max(lens)), dtype=bool)
+    for r, L in enumerate(lens):
+        for h in range(Hq):
+            bl = _vs_brute(V[r, h].tolist(), S[r, h].tolist(), L)
+            for i in range(L):
+                blocks, _ = bl[i // 64]
+                for j in range(i + 1):
+                    if 64 * (j // 64) in blocks or j in V[r, h].tolist():
+                        want[(int(cu[r]) + i) * Hq + h, j] = True
+    assert (got == _bits(want)).all(), "block-sparse mask differs from the definition"
+    c = synth.prefill_case(950, lens, lens, Hq, Hkv, D, torch.float32, True, sm_scale=0.5)
+    causal, _ = oracle.varlen_prefill(c.q, c.cu_seqlens_q, c.cu_seqlens_k, c.sink, 0.5, Hkv,
+                                      k=c.k, v=c.v)
+    all_diag = np.broadcast_to(np.arange(max(lens), dtype=np.int32), (3, Hq, max(lens)))
+    none = np.zeros((3, Hq, 0), dtype=np.int32)
+    o1, _ = oracle.sparse_prefill(c.q, c.k, c.v, cu, none, all_diag, c.sink, 0.5, Hkv)
+    o2, _ = oracle.sparse_prefill(c.q, c.k, c.v, cu, all_diag, none, c.sink, 0.5, Hkv)
+    _close(o1, causal, 1e-13, 1e-12, "every diagonal = causal")
+    _close(o2, causal, 1e-13, 1e-12, "every column = causal")
+    o3, l3 = oracle.sparse_prefill(c.q, c.k, c.v, cu, none, none, c.sink, 0.5, Hkv)
+    assert (o3 == 0).all()
+    _close(l3, np.broadcast_to(c.sink.numpy(), l3.shape), 1e-6, 1e-6, "no index: lse = sink")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

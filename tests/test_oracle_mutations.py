@@ -6,9 +6,11 @@ window off by one, a paged-address mistake, a wrong lse, a wrong merge
 weight, K used in place of V, the sink left out of the max, a decode query
 at the wrong position, an ALiBi bias of the wrong sign, a partition one key
 too long, a non-causal prefill that keeps the causal bound or bounds the
-window on both sides, top-left query positions, and four rotary-embedding mistakes (the
+window on both sides, top-left query positions, four rotary-embedding mistakes (the
 frequency exponent, the sign of the sine, the pairing, linear scaling
-inverted).  A mutation names the file of the oracle package it changes; each
+inverted), and five in the vertical + slash sparse prefill (a diagonal's key
+range one key long, a vertical column kept inside a slash block or past the
+row block, a row that does not see its own key, a mask bit ignored).  A mutation names the file of the oracle package it changes; each
 mutant package is a copy of ``oracle/`` imported in its own subprocess."""
 
 import json
@@ -62,6 +64,14 @@ MUTATIONS = {
     "rope_pairing_swapped": (PY, "    if neox:\n        a, b = y[..., :half]",
                              "    if not neox:\n        a, b = y[..., :half]"),
     "rope_linear_inverted": (PY, "t = t / factor", "t = t * factor"),
+    "slash_range_one_key_long": (C, "int lo = r0 - s, hi = r1 - 1 - s;",
+                                 "int lo = r0 - s, hi = r1 - s;"),
+    "vertical_kept_in_slash_block": (C, "if (sel[v / 64]) continue;", "if (sel[v / 64] > 1) continue;"),
+    "vertical_past_last_row": (C, "if (v < 0 || v >= L || v > r1 - 1) continue;",
+                               "if (v < 0 || v >= L || v > r1) continue;"),
+    "masked_row_sees_itself_not": (PY, "row[i + 1:] = False", "row[i:] = False"),
+    "masked_ignores_bit": (C, "if (!((row[j / 64] >> (j % 64)) & 1u)) continue;",
+                           "if (!((row[j / 64] >> (j % 64)) & 1u) && j != 0) continue;"),
     "merge_sink_dropped": (C, "double Z = exp(sigma - M);\n            for (int p = 0; p < np; ++p) Z",
                            "double Z = 0.0;\n            for (int p = 0; p < np; ++p) Z"),
 }
