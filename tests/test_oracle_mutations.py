@@ -31,8 +31,8 @@ C, PY = "oracle.c", "__init__.py"
 MUTATIONS = {
     "sink_dropped_from_Z": (C, "double Z = exp(sigma - M);\n    for (int d = 0;",
                             "double Z = 0.0 * exp(sigma - M);\n    for (int d = 0;"),
-    "sink_scaled": (C, "double sigma = c->sink ? (double)c->sink[h] : -INFINITY;",
-                    "double sigma = c->sink ? c->scale * (double)c->sink[h] : -INFINITY;"),
+    "sink_scaled": (C, "double sigma = c->sink ? (double)c->sink[h] : -INFINITY;\n    double slope",
+                    "double sigma = c->sink ? c->scale * (double)c->sink[h] : -INFINITY;\n    double slope"),
     "gqa_modulo": (C, "int G = c->Hq / c->Hkv, g = h / G;\n    int Lq",
                    "int G = c->Hq / c->Hkv, g = h % c->Hkv;\n    int Lq"),
     "causal_top_left": (C, "int p = Lk - Lq + i;", "int p = i;"),
