@@ -42,7 +42,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--only", default="all",
-                   choices=["all", "decode", "prefill", "chunked", "longctx", "none"])
+                   choices=["all", "decode", "prefill", "chunked", "longctx", "sparse", "none"])
     p.add_argument("--skip-long", action="store_true", help="skip the 131072-token workload")
     p.add_argument("--spinup", type=float, default=0.3,
                    help="seconds of untimed steps before the warmup steps of each workload")
@@ -457,6 +457,91 @@ def bench_prefill(c, name, steps, warmup, reps, with_cache_write=False, traffic_
     return res, out
 
 
+def sparse_pairs(lists, L):
+    """Visible (row, key) pairs of every head under the block lists: the keys
+    j <= i of each row block's 64-key blocks and columns."""
+    bc, bo, cc, ci = lists
+    H, NM = bc.shape[1], bc.shape[2]
+    per_unit_rows = []
+    total = 0
+    for h in range(H):
+        for m in range(NM):
+            r0, r1 = 64 * m, min(L, 64 * m + 64)
+            if r0 >= r1:
+                continue
+            rows = np.arange(r0, r1, dtype=np.int64)
+            offs = bo[0, h, m, :bc[0, h, m]].astype(np.int64)      # ascending
+            cols = np.sort(ci[0, h, m, :cc[0, h, m]].astype(np.int64))
+            # whole blocks before the row's own, the row's own block up to
+            # the row, and the columns at or before it
+            full = np.searchsorted(offs, rows - 64, side="right")
+            own = np.isin(rows & ~63, offs)
+            n = 64 * full + own * ((rows & 63) + 1) + np.searchsorted(cols, rows, side="right")
+            total += int(n.sum())
+            per_unit_rows.append((h, r0, n))
+    return total, per_unit_rows
+
+
+def bench_sparse(steps, warmup):
+    """Vertical + slash sparse prefill: the block lists, then the attention,
+    on one request of 32768 tokens; the dense causal prefill of the same input
+    timed beside it."""
+    c, V, S = synth.sparse_prefill_workload()
+    L, Hq, D = c.q.shape
+    q, k, v = c.q.cuda(), c.k.cuda(), c.v.cuda()
+    cu = c.cu_seqlens_q.cuda()
+    Vd, Sd = V.cuda(), S.cuda()
+    lists = pkv.vertical_slash_blocks(Vd, Sd, cu, L)
+    out = torch.empty_like(q)
+
+    def step(i, kt):
+        kt.time("lists", lambda: pkv.vertical_slash_blocks(Vd, Sd, cu, L))
+        kt.time("sparse", lambda: pkv.sparse_prefill(q, k, v, cu, L, lists, c.sm_scale,
+                                                     out=out))
+
+    def dense(i, kt):
+        kt.time("dense", lambda: pkv.varlen_prefill(q, cu, cu, L, L, c.sm_scale, c.Hkv, k=k,
+                                                    v=v, out=out))
+
+    ms, kt = timed_steps(step, steps, warmup)
+    _, ktd = timed_steps(dense, steps, warmup, launches_per_step=1)
+    host = [t.cpu().numpy() for t in lists]
+    pairs, _ = sparse_pairs(host, L)
+    flops = 4 * D * pairs
+    sp_ms, li_ms, de_ms = kt.mean_ms("sparse"), kt.mean_ms("lists"), ktd.mean_ms("dense")
+    dense_flops = 4 * D * Hq * visible_pairs([L], [L], -1)
+    achieved = flops / (sp_ms * 1e-3) / 1e12
+    res = {"name": "sparse_prefill_1x32768_vs", "value": round(achieved, 2), "unit": "TFLOP/s",
+           "ms_per_step": round(ms, 4), "algorithmic_flops": flops,
+           "density_vs_causal": round(flops / dense_flops, 4),
+           "kernels_ms": {"vertical_slash_blocks": round(li_ms, 4), "sparse_prefill": round(sp_ms, 4)},
+           "dense_causal_prefill_ms": round(de_ms, 4),
+           "speedup_vs_dense": round(de_ms / (sp_ms + li_ms), 3),
+           "roofline": roofline("mfma", achieved, MFMA_BF16_PEAK_TFS, "TFLOP/s")}
+    if not ARGS.no_cpu_baseline:
+        import oracle  # the CPU-baseline leg is the only bench code that runs the oracle
+        n = host_threads()
+        units = _sample(L * Hq, 2048, 60)
+        t0 = time.perf_counter()
+        oracle.sparse_prefill(c.q, c.k, c.v, c.cu_seqlens_q, V.numpy(), S.numpy(), None,
+                              c.sm_scale, c.Hkv, units=units.tolist(), nthreads=n)
+        dt = time.perf_counter() - t0
+        # flops of the sampled units: their rows' visible keys
+        _, rows = sparse_pairs(host, L)
+        vis = np.zeros((Hq, L), dtype=np.int64)
+        for h, r0, nn in rows:
+            vis[h, r0:r0 + len(nn)] = nn
+        ufl = float(vis[units % Hq, units // Hq].sum()) * 4 * D
+        res["cpu_baseline"] = {"kind": "oracle", "unit": "GFLOP/s", "cores": n,
+                               "value": round(ufl / dt / 1e9, 4), "seconds": round(dt, 3),
+                               "sample": f"{len(units)} of {L * Hq} (token, head) units of the "
+                                         f"sparse workload (seeded), block lists, mask and "
+                                         f"fp64 masked attention, {n} threads"}
+    del q, k, v, out, lists
+    torch.cuda.empty_cache()
+    return res
+
+
 # ----------------------------------------------------------------------------
 # oracle parity spot check and CPU baseline
 # ----------------------------------------------------------------------------
@@ -633,6 +718,14 @@ def main():
                                                  "the long-context decode workload")
         log(f"long decode: {r5['value']} GB/s (P=512), {r5b['value']} GB/s (auto)")
         del c5
+    if ARGS.only in ("all", "sparse"):
+        log("sparse prefill workload (1 x 32768, 32/8 heads, D 128, vertical + slash, "
+            "budget 0.3)")
+        rs = bench_sparse(steps, warmup)
+        workloads["sparse_prefill"] = rs
+        log(f"sparse prefill: {rs['value']} TFLOP/s on {rs['density_vs_causal']} of the causal "
+            f"pairs, lists {rs['kernels_ms']['vertical_slash_blocks']} ms, "
+            f"{rs['speedup_vs_dense']}x the dense causal prefill")
     if ARGS.copy_calibration_mb:
         n = ARGS.copy_calibration_mb * (1 << 20) // 4
         src = torch.ones(n, device="cuda")

@@ -24,6 +24,9 @@
  *                           (vLLM page, single_query_cached_kv_attention: the
  *                           partitioned "v2" path with exp_sums / max_logits /
  *                           tmp_output)
+ *   pkv_vertical_slash_blocks / pkv_sparse_prefill
+ *                           vertical + slash block-sparse prefill (nano-vllm
+ *                           minference.py page, MInferencePolicy)
  *   pkv_varlen_prefill      causal or non-causal attention for packed variable-length
  *                           requests (Transformers doc, varlen path:
  *                           cu_seq_lens_q/k and max_length_q/k), over
@@ -460,6 +463,65 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
                               int32_t causal, int32_t window_left, const float *alibi_slopes,
                               const float *rope_cos_sin, int32_t rope_positions,
                               int32_t rotary_dim, int32_t rope_neox, const float *sink,
+                              pkv_dtype dtype, void *stream);
+
+/*
+ * Vertical + slash sparse prefill (nano-vllm "minference.py" page,
+ * MInferencePolicy: estimate_pattern returns, per head, vertical_indices --
+ * key positions to keep -- and slash_indices -- diagonal offsets i - j of a
+ * query at position i and a key at j -- and sparse_prefill_attention turns
+ * them into a block form with block_size_M = block_size_N = 64 before
+ * attending).  The page does not print that conversion; this library's block
+ * form: row block m of a request holds rows [64m, 64m + 64), key block n
+ * keys [64n, 64n + 64).  Key block n is a SLASH BLOCK of m when some diagonal
+ * s of the head meets it within m's rows (a key i - s >= 0 in block n for a
+ * row i of m); m's COLUMNS are its vertical indices v < L, v <= m's last row,
+ * whose key block is not a slash block of m.  Row i of m attends keys j <= i
+ * of m's slash blocks and columns (self-attention prefill: Lq = Lk = L per
+ * request, queries at positions 0 .. L - 1), with the optional sink in the
+ * denominator.  Estimating the pattern is not part of the library.
+ *
+ * pkv_vertical_slash_blocks -- the block form of every (request, head, row
+ * block):
+ *   vertical_indices [B, num_heads, num_vertical] int32; the entries of a
+ *                    row that lie in [0, L) must be distinct (the page's are
+ *                    sorted top-k indices); entries outside [0, L) are
+ *                    ignored (padding)
+ *   slash_indices    [B, num_heads, num_slash] int32, any order, repeats
+ *                    allowed; entries outside [0, L) are ignored
+ *   cu_seqlens       [B + 1] int32 prefix sums of the request lengths L,
+ *                    each L <= max_seqlen
+ *   block_count      [B, num_heads, NM] out, NM = ceil(max_seqlen / 64)
+ *   block_offset     [B, num_heads, NM, NM] out: the first key (64n) of each
+ *                    slash block, ascending, block_count entries per row
+ *   column_count     [B, num_heads, NM] out
+ *   column_index     [B, num_heads, NM, num_vertical] out: the columns in the
+ *                    order given, column_count entries per row
+ * Entries past a count are not written.  Row blocks at or past a request's
+ * end get counts 0.  Device pointers, caller-owned; all integers exact.
+ *
+ * pkv_sparse_prefill -- attention over that block form, bf16 only:
+ *   q [sum L, num_q_heads, head_dim], k / v [sum L, num_kv_heads, head_dim]
+ *   packed by cu_seqlens; out like q; lse [sum L, num_q_heads] float32 or
+ *   NULL; the block form as written by pkv_vertical_slash_blocks for
+ *   num_heads = num_q_heads (query head h reads kv head h / (Hq / Hkv)) and
+ *   the same max_seqlen / num_vertical.
+ * Errors besides the common ones: PKV_ERR_UNSUPPORTED for float32, and when
+ * max_seqlen * num_kv_heads * head_dim * 2 bytes (one request's K rows)
+ * reaches 4 GiB.
+ */
+pkv_status pkv_vertical_slash_blocks(int32_t *block_count, int32_t *block_offset,
+                                     int32_t *column_count, int32_t *column_index,
+                                     const int32_t *vertical_indices,
+                                     const int32_t *slash_indices, const int32_t *cu_seqlens,
+                                     int32_t B, int32_t num_heads, int32_t num_vertical,
+                                     int32_t num_slash, int32_t max_seqlen, void *stream);
+pkv_status pkv_sparse_prefill(void *out, float *lse, const void *q, const void *k, const void *v,
+                              const int32_t *cu_seqlens, const int32_t *block_count,
+                              const int32_t *block_offset, const int32_t *column_count,
+                              const int32_t *column_index, int32_t B, int32_t max_seqlen,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t num_vertical, float sm_scale, const float *sink,
                               pkv_dtype dtype, void *stream);
 
 #ifdef __cplusplus

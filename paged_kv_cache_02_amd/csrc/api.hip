@@ -680,4 +680,58 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
     return launch_rows(a, s);
 }
 
+pkv_status pkv_vertical_slash_blocks(int32_t *block_count, int32_t *block_offset,
+                                     int32_t *column_count, int32_t *column_index,
+                                     const int32_t *vertical_indices,
+                                     const int32_t *slash_indices, const int32_t *cu_seqlens,
+                                     int32_t B, int32_t num_heads, int32_t num_vertical,
+                                     int32_t num_slash, int32_t max_seqlen, void *stream)
+{
+    if (B < 0 || num_heads <= 0 || num_vertical < 0 || num_slash < 0 || max_seqlen < 0)
+        return PKV_ERR_SHAPE;
+    const int NM = (max_seqlen + 63) / 64;
+    if (B == 0 || NM == 0) return PKV_OK;
+    if (!block_count || !block_offset || !column_count || !cu_seqlens) return PKV_ERR_NULL;
+    if ((num_vertical > 0 && (!vertical_indices || !column_index)) ||
+        (num_slash > 0 && !slash_indices))
+        return PKV_ERR_NULL;
+    VerticalSlashArgs a{};
+    a.block_count = block_count; a.block_offset = block_offset; a.column_count = column_count;
+    a.column_index = column_index; a.vertical = vertical_indices; a.slash = slash_indices;
+    a.cu = cu_seqlens; a.B = B; a.H = num_heads; a.NV = num_vertical; a.NS = num_slash; a.NM = NM;
+    return launch_vertical_slash(a, (hipStream_t)stream);
+}
+
+pkv_status pkv_sparse_prefill(void *out, float *lse, const void *q, const void *k, const void *v,
+                              const int32_t *cu_seqlens, const int32_t *block_count,
+                              const int32_t *block_offset, const int32_t *column_count,
+                              const int32_t *column_index, int32_t B, int32_t max_seqlen,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t num_vertical, float sm_scale, const float *sink,
+                              pkv_dtype dtype, void *stream)
+{
+    if (B < 0 || max_seqlen < 0 || num_vertical < 0) return PKV_ERR_SHAPE;
+    pkv_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
+    if (st != PKV_OK) return st;
+    if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+    if (!scale_ok(sm_scale)) return PKV_ERR_SHAPE;
+    // K/V rows of one request are addressed with 32-bit byte offsets
+    if ((unsigned long long)max_seqlen * num_kv_heads * head_dim * 2 >= (1ull << 32))
+        return PKV_ERR_UNSUPPORTED;
+    const int NM = (max_seqlen + 63) / 64;
+    if (B == 0 || NM == 0) return PKV_OK;
+    if (!out || !q || !k || !v || !cu_seqlens || !block_count || !block_offset || !column_count)
+        return PKV_ERR_NULL;
+    if (num_vertical > 0 && !column_index) return PKV_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(k) || !aligned16(v))
+        return PKV_ERR_UNSUPPORTED;
+    SparseArgs a{};
+    a.out = out; a.lse = lse; a.q = q; a.k = k; a.v = v; a.cu = cu_seqlens;
+    a.block_count = block_count; a.block_offset = block_offset; a.column_count = column_count;
+    a.column_index = column_index; a.sink = sink; a.B = B; a.Hq = num_q_heads;
+    a.Hkv = num_kv_heads; a.G = num_q_heads / num_kv_heads; a.D = head_dim; a.NM = NM;
+    a.NV = num_vertical; a.scale_log2 = sm_scale * kLog2e;
+    return launch_sparse_prefill(a, (hipStream_t)stream);
+}
+
 }  // extern "C"

@@ -249,8 +249,34 @@ int decode_heads_per_unit(int G);
 pkv_status launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);
 pkv_status launch_decode_stream_bf16(const StreamArgs &a, hipStream_t stream);
 pkv_status launch_merge(const MergeArgs &a, hipStream_t stream);
+// Vertical + slash block lists (pkv_vertical_slash_blocks).
+struct VerticalSlashArgs {
+    int32_t *block_count;        // [B, H, NM]
+    int32_t *block_offset;       // [B, H, NM, NM]
+    int32_t *column_count;       // [B, H, NM]
+    int32_t *column_index;       // [B, H, NM, NV]
+    const int32_t *vertical;     // [B, H, NV]
+    const int32_t *slash;        // [B, H, NS]
+    const int32_t *cu;           // [B + 1]
+    int32_t B, H, NV, NS, NM;    // NM = ceil(max_seqlen / 64)
+};
+
+// Block-sparse prefill over those lists (pkv_sparse_prefill), bf16.
+struct SparseArgs {
+    void *out;                   // [sum L, Hq, D]
+    float *lse;                  // [sum L, Hq] or null
+    const void *q, *k, *v;       // q [sum L, Hq, D], k / v [sum L, Hkv, D]
+    const int32_t *cu;           // [B + 1]
+    const int32_t *block_count, *block_offset, *column_count, *column_index;
+    const float *sink;
+    int32_t B, Hq, Hkv, G, D, NM, NV;
+    float scale_log2;
+};
+
 pkv_status launch_rows(const RowArgs &a, hipStream_t stream);
 pkv_status launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream);
+pkv_status launch_vertical_slash(const VerticalSlashArgs &a, hipStream_t stream);
+pkv_status launch_sparse_prefill(const SparseArgs &a, hipStream_t stream);
 int prefill_heads_per_wg(int G);
 int prefill_block_m();
 pkv_status launch_rope_table(float *cos_sin, int n_pos, int rd, double base, int scaling,

@@ -57,6 +57,10 @@ SIGNATURES = {
                                                    _I32, _I32, ctypes.c_int, _P]),
     "pkv_merge_partitions": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32,
                                             _I32, ctypes.c_int, _P]),
+    "pkv_vertical_slash_blocks": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                                 _I32, _I32, _P]),
+    "pkv_sparse_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32,
+                                          _I32, _I32, _I32, _I32, _F, _P, ctypes.c_int, _P]),
     "pkv_varlen_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P,
                                           _P, _I32, _I32, _I32, _I32, _I32, _I32, _F, _I32,
                                           _I32, _P, _P, _I32, _I32, _I32, _P, ctypes.c_int, _P]),
@@ -393,4 +397,53 @@ def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_
         0 if rope_cos_sin is None else rope_cos_sin.shape[0], rotary_dim, int(bool(rope_neox)),
         _ptr(_f32(sink, "sink")), _dt(q, k, v, k_cache, v_cache, out), _stream()),
         "varlen_prefill")
+    return out
+
+
+SPARSE_BLOCK = 64
+
+
+def vertical_slash_blocks(vertical_indices, slash_indices, cu_seqlens, max_seqlen: int):
+    """Block form of vertical [B,H,NV] / slash [B,H,NS] indices per 64-row block:
+    ``(block_count [B,H,NM], block_offset [B,H,NM,NM], column_count [B,H,NM],
+    column_index [B,H,NM,NV])``, NM = ceil(max_seqlen / 64); entries past a
+    count are left as -1."""
+    B, H, NV = vertical_indices.shape
+    NS = slash_indices.shape[2]
+    if slash_indices.shape[:2] != (B, H) or cu_seqlens.shape[0] != B + 1:
+        raise ValueError("vertical / slash / cu_seqlens shapes disagree")
+    NM = (int(max_seqlen) + SPARSE_BLOCK - 1) // SPARSE_BLOCK
+    dev = vertical_indices.device
+    bc = torch.zeros((B, H, NM), dtype=torch.int32, device=dev)
+    bo = torch.full((B, H, NM, NM), -1, dtype=torch.int32, device=dev)
+    cc = torch.zeros((B, H, NM), dtype=torch.int32, device=dev)
+    ci = torch.full((B, H, NM, NV), -1, dtype=torch.int32, device=dev)
+    _check(lib.pkv_vertical_slash_blocks(
+        _ptr(bc), _ptr(bo), _ptr(cc), _ptr(ci), _ptr(_i32(vertical_indices, "vertical_indices")),
+        _ptr(_i32(slash_indices, "slash_indices")), _ptr(_i32(cu_seqlens, "cu_seqlens")), B, H,
+        NV, NS, int(max_seqlen), _stream()), "vertical_slash_blocks")
+    return bc, bo, cc, ci
+
+
+def sparse_prefill(q, k, v, cu_seqlens, max_seqlen: int, blocks, sm_scale: float, sink=None,
+                   out=None, lse=None):
+    """Block-sparse prefill (bf16) over ``blocks`` from vertical_slash_blocks:
+    q [sum L, Hq, D], k / v [sum L, Hkv, D]; returns out like q."""
+    bc, bo, cc, ci = blocks
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    B = cu_seqlens.shape[0] - 1
+    NM = (int(max_seqlen) + SPARSE_BLOCK - 1) // SPARSE_BLOCK
+    if tuple(bc.shape) != (B, Hq, NM) or tuple(bo.shape) != (B, Hq, NM, NM) \
+            or tuple(cc.shape) != (B, Hq, NM) or ci.shape[:3] != (B, Hq, NM):
+        raise ValueError("block lists do not match the request shape")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.pkv_sparse_prefill(
+        _ptr(out), _ptr(_f32(lse, "lse")), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(_i32(cu_seqlens, "cu_seqlens")), _ptr(_i32(bc, "block_count")),
+        _ptr(_i32(bo, "block_offset")), _ptr(_i32(cc, "column_count")),
+        _ptr(_i32(ci, "column_index")), B, int(max_seqlen), Hq, Hkv, D, ci.shape[3],
+        float(sm_scale), _ptr(_f32(sink, "sink")), _dt(q, k, v, out), _stream()),
+        "sparse_prefill")
     return out

@@ -50,6 +50,8 @@ __all__ = [
     "config4_chunked",
     "config5_split_decode",
     "random_partials",
+    "vertical_slash_pattern",
+    "sparse_prefill_workload",
 ]
 
 CHUNK = 1 << 22  # values per independent child stream for large draws
@@ -359,3 +361,47 @@ def random_partials(seed: int, B: int, Hq: int, P: int, D: int, nparts) -> tuple
         po[b, :, n:, :] = np.nan
         pl[b, :, n:] = np.nan
     return torch.from_numpy(po), torch.from_numpy(pl)
+
+
+def vertical_slash_pattern(seed: int, lengths, H: int, budget: float = 0.3,
+                           num_sink: int = 30, num_recent: int = 100, band: int = 64):
+    """Synthetic vertical + slash index sets shaped like the nano-vllm
+    minference.py page's estimate_pattern output (which needs a trained
+    model's attention to mean anything): per request and head, with the
+    page's adaptive budget (vertical = max(num_sink + 1, 0.2 budget L), slash
+    = max(num_recent + 1, 0.8 budget L)), vertical = the first num_sink keys
+    plus distinct random keys, ascending; slash = diagonals 0 .. num_recent-1
+    plus runs of `band` consecutive diagonals at random offsets.  Returns
+    int32 ``vertical [B,H,NV]`` and ``slash [B,H,NS]`` padded with -1 (ignored
+    entries) to the longest request's sizes."""
+    rng = np.random.default_rng([seed, 2594])
+    Lmax = max(lengths)
+    def sizes(L):
+        b = int(L * budget)
+        return (min(L, max(num_sink + 1, int(b * 0.2))), min(L, max(num_recent + 1, int(b * 0.8))))
+    NV, NS = sizes(Lmax)
+    V = np.full((len(lengths), H, NV), -1, dtype=np.int32)
+    S = np.full((len(lengths), H, NS), -1, dtype=np.int32)
+    for r, L in enumerate(lengths):
+        nv, ns = sizes(L)
+        for h in range(H):
+            sink = np.arange(min(num_sink, L))
+            rest = rng.choice(np.arange(len(sink), L), size=max(0, nv - len(sink)), replace=False)
+            V[r, h, :nv] = np.sort(np.concatenate([sink, rest]))[:nv]
+            diags = set(range(min(num_recent, L)))
+            while len(diags) < ns:
+                start = int(rng.integers(0, L))
+                diags.update(range(start, min(L, start + band)))
+            S[r, h, :ns] = np.array(sorted(diags)[:ns], dtype=np.int32)[rng.permutation(ns)]
+    return torch.from_numpy(V), torch.from_numpy(S)
+
+
+def sparse_prefill_workload(seed: int = 6, L: int = 32768, Hq: int = 32, Hkv: int = 8,
+                            D: int = 128):
+    """A long-context vertical + slash sparse prefill: one request of 32768
+    tokens, 32/8 heads, head_dim 128, bf16, no sink (the minference.py page
+    attends without one), with the page's default pattern knobs (budget 0.3,
+    30 sink columns, 100 recent diagonals)."""
+    c = prefill_case(seed, [L], [L], Hq, Hkv, D, torch.bfloat16, False)
+    V, S = vertical_slash_pattern(seed, [L], Hq)
+    return c, V, S

@@ -295,3 +295,50 @@ def test_noalloc_validation():
     # a split into 512-token partitions over 131072 keys for 16 x 32 heads: 68 MB
     assert f(*dict(a, B=16, Hq=32, Hkv=8, bs=64, MB=2048, max_seqlen_k=131072,
                    part=512).values()) == pkv.PKV_ERR_SCRATCH
+
+
+def vs_call(**over):
+    a = dict(bc=FAKE, bo=FAKE, cc=FAKE, ci=FAKE, V=FAKE, S=FAKE, cu=FAKE, B=2, H=8, NV=16, NS=32,
+             max_seqlen=1000, stream=None)
+    a.update(over)
+    return lib.pkv_vertical_slash_blocks(*a.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(bc=None), pkv.PKV_ERR_NULL),
+    (dict(cu=None), pkv.PKV_ERR_NULL),
+    (dict(V=None), pkv.PKV_ERR_NULL),
+    (dict(S=None), pkv.PKV_ERR_NULL),
+    (dict(H=0), pkv.PKV_ERR_SHAPE),
+    (dict(NV=-1), pkv.PKV_ERR_SHAPE),
+    (dict(max_seqlen=-5), pkv.PKV_ERR_SHAPE),
+    (dict(B=0), pkv.PKV_OK),
+    (dict(max_seqlen=0), pkv.PKV_OK),
+])
+def test_vertical_slash_validation(over, status):
+    assert vs_call(**over) == status
+
+
+def sparse_call(**over):
+    a = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, cu=FAKE, bc=FAKE, bo=FAKE, cc=FAKE,
+             ci=FAKE, B=2, max_seqlen=1000, Hq=8, Hkv=2, D=128, NV=16, scale=0.1, sink=None,
+             dt=1, stream=None)
+    a.update(over)
+    return lib.pkv_sparse_prefill(*a.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(out=None), pkv.PKV_ERR_NULL),
+    (dict(bo=None), pkv.PKV_ERR_NULL),
+    (dict(ci=None), pkv.PKV_ERR_NULL),
+    (dict(dt=0), pkv.PKV_ERR_UNSUPPORTED),                       # float32: not implemented
+    (dict(Hkv=3), pkv.PKV_ERR_SHAPE),
+    (dict(D=96), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(scale=0.0), pkv.PKV_ERR_SHAPE),
+    (dict(q=FAKE + 8), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(max_seqlen=1 << 24, Hkv=8, Hq=8), pkv.PKV_ERR_UNSUPPORTED),   # 4 GiB of K per request
+    (dict(B=0), pkv.PKV_OK),
+    (dict(ci=None, NV=0, B=0), pkv.PKV_OK),
+])
+def test_sparse_prefill_validation(over, status):
+    assert sparse_call(**over) == status

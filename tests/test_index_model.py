@@ -383,3 +383,73 @@ def test_models_catch_a_planted_mistake():
     with pytest.raises(AssertionError):
         # a block table one block short for the appended token
         model_decode_stream([16, 31], 8, 2, 16, mbps=1, append=True)
+
+
+# ---------------------------------------------------------------------------
+# vertical_slash_kernel and sparse_prefill_kernel (csrc/sparse.hip)
+# ---------------------------------------------------------------------------
+
+def model_sparse(lens, H, Hkv, D, V, S):
+    """The block lists (the oracle's conversion, equal to the kernel's by the
+    GPU tests) and every access of the conversion and of the sparse prefill:
+    bit-set words, list slots, K/V rows, gathered positions, output rows."""
+    import oracle
+    import synth
+    cu = synth.cu_from_lengths(lens).numpy().astype(np.int64)
+    Lmax = max(lens)
+    NM = (Lmax + 63) // 64
+    NMW = (NM + 31) // 32
+    NV, NS = V.shape[2], S.shape[2]
+    bc, bo, cc, ci = oracle.vertical_slash_blocks(V, S, cu, Lmax)
+    rowbytes = Hkv * D * 2
+    U = D // 8
+    RPI = 64 // U
+    for b, L in enumerate(lens):
+        for h in range(H):
+            for m in range(NM):
+                r0 = 64 * m
+                if r0 >= L:
+                    assert bc[b, h, m] == 0 and cc[b, h, m] == 0
+                    continue
+                r1 = min(L, r0 + 64)
+                # conversion: the bit-set words a diagonal or a column touches
+                s = S[b, h]
+                s = s[(s >= 0) & (s < L) & (r1 - 1 - s >= 0)]
+                hi = (r1 - 1 - s) >> 6
+                lo = np.maximum(0, r0 - s) >> 6
+                assert (hi >> 5 < NMW).all() and (lo >> 5 < NMW).all()
+                v = V[b, h]
+                v = v[(v >= 0) & (v < r1)]
+                assert (v >> 11 < NMW).all()
+                assert bc[b, h, m] <= NM and cc[b, h, m] <= NV
+                # prefill: 64-key blocks inside the request, descriptor range
+                # positive and within 32 bits; gathered rows inside it
+                t0 = bo[b, h, m, :bc[b, h, m]]
+                assert (t0 % 64 == 0).all() and (t0 >= 0).all() and (t0 < L).all()
+                assert ((L - t0) * rowbytes < 2 ** 32).all()
+                cols = ci[b, h, m, :cc[b, h, m]]
+                assert (cols >= 0).all() and (cols < L).all()
+                for c0 in range(0, int(cc[b, h, m]), 64):
+                    for i in range(U):            # load instructions of both waves
+                        for lrow in range(RPI):
+                            e = c0 + RPI * i + lrow
+                            col = cols[e] if e < cc[b, h, m] else cols[c0]
+                            assert 0 <= col < L and col * rowbytes + rowbytes <= 2 ** 32
+                # output rows of both waves
+                for w in range(2):
+                    wrow0 = r0 + 32 * w
+                    wrows = max(0, min(32, L - wrow0))
+                    assert wrows == 0 or wrow0 + wrows <= L
+    return int(bc.sum() + cc.sum())
+
+
+def test_sparse_mapping_in_bounds():
+    import synth
+    G = _gpu_module("test_gpu_sparse")
+    n = 0
+    for lens, Hq, Hkv, D, sink, kind in G.SPARSE:
+        V, S = G._indices(70 + len(lens), lens, Hq, kind)
+        n += model_sparse(lens, Hq, Hkv, D, V.numpy(), S.numpy())
+    V, S = synth.vertical_slash_pattern(6, [4096, 100], 4)
+    n += model_sparse([4096, 100], 4, 2, 128, V.numpy(), S.numpy())
+    assert n > 0
