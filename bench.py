@@ -362,14 +362,16 @@ def rope_setup(c, rotary_dim=128, neox=True):
 
 
 def bench_prefill(c, name, steps, warmup, reps, with_cache_write=False, traffic_key=None,
-                  alibi=None, rope=None, rope_unfused=False):
+                  alibi=None, rope=None, rope_unfused=False, rope_k=False):
     """rope: from rope_setup; q is then rotated inside the prefill (and K by
     reshape_and_cache_rope when with_cache_write), or, with rope_unfused, by a
-    separate rope_apply launch before a plain prefill."""
+    separate rope_apply launch before a plain prefill.  rope_k: the
+    contiguous keys are rotated too, inside the prefill (or, unfused, by a
+    rope_apply launch of their own)."""
     T = c.q.shape[0]
     fused = rope is not None and not rope_unfused
-    rkw = dict(rope_cos_sin=rope["tab"], rotary_dim=rope["rd"], rope_neox=rope["neox"]) \
-        if fused else {}
+    rkw = dict(rope_cos_sin=rope["tab"], rotary_dim=rope["rd"], rope_neox=rope["neox"],
+               rope_k=rope_k) if fused else {}
     qs = [c.q.cuda() for _ in range(reps)]
     cq, ck = c.cu_seqlens_q.cuda(), c.cu_seqlens_k.cuda()
     al = None if alibi is None else alibi.cuda()
@@ -406,6 +408,9 @@ def bench_prefill(c, name, steps, warmup, reps, with_cache_write=False, traffic_
         if rope_unfused:
             kt.time("rope_apply", lambda: pkv.rope_apply(qs[r], rope["qpos"], rope["tab"],
                                                          rope["rd"], rope["neox"]))
+            if rope_k:
+                kt.time("rope_apply_k", lambda: pkv.rope_apply(ks[r], rope["kpos"], rope["tab"],
+                                                               rope["rd"], rope["neox"]))
         if c.paged:
             kt.time("prefill", lambda: pkv.varlen_prefill(
                 qs[r], cq, ck, c.max_seqlen_q, c.max_seqlen_k, c.sm_scale, c.Hkv,
@@ -440,6 +445,10 @@ def bench_prefill(c, name, steps, warmup, reps, with_cache_write=False, traffic_
     if rope_unfused:
         ra_ms = kt.mean_ms("rope_apply")
         res["kernels_ms"]["rope_apply"] = round(ra_ms, 4)
+        if rope_k:
+            rk_ms = kt.mean_ms("rope_apply_k")
+            res["kernels_ms"]["rope_apply_k"] = round(rk_ms, 4)
+            ra_ms += rk_ms
         res["prefill_plus_rope_apply_ms"] = round(pre_ms + ra_ms, 4)
     if with_cache_write:
         rc_ms = kt.mean_ms("reshape_and_cache")
@@ -690,6 +699,16 @@ def main():
         log(f"prefill with q rotated in the kernel: {r3r['value']} TFLOP/s, "
             f"{r3r['speedup_vs_unfused']}x rope_apply + prefill; reshape_and_cache_rope "
             f"{r3r['reshape_and_cache_rope']['value']} GB/s")
+        r3k, _ = bench_prefill(c3, "varlen_prefill_8x_U256-4096_rope_qk", steps, warmup, reps=2,
+                               rope=rp, rope_k=True)
+        r3ku, _ = bench_prefill(c3, "varlen_prefill_8x_U256-4096_rope_qk_unfused", steps, warmup,
+                                reps=2, rope=rp, rope_unfused=True, rope_k=True)
+        r3k["unfused_prefill_plus_rope_apply_ms"] = r3ku["prefill_plus_rope_apply_ms"]
+        r3k["speedup_vs_unfused"] = round(r3ku["prefill_plus_rope_apply_ms"] /
+                                          r3k["kernels_ms"]["prefill"], 3)
+        workloads["varlen_prefill_rope_qk"] = r3k
+        log(f"prefill with q and k rotated in the kernel: {r3k['value']} TFLOP/s, "
+            f"{r3k['speedup_vs_unfused']}x rope_apply (q, k) + prefill")
     if ARGS.only in ("all", "chunked"):
         log("chunked prefill workload (4 x 512 q on 8704 paged keys, window 128, 64/8, D 64)")
         c4 = synth.config4_chunked(poison=False, spare_blocks=0)

@@ -446,9 +446,18 @@ pkv_status pkv_merge_partitions(void *out, float *lse, const float *part_out,
  *                   (>= max_seqlen_k): q is then rotated by its position p =
  *                   Lk - Lq + i as it is loaded, with rotary_dim (a multiple
  *                   of 32 in [32, head_dim]) and rope_neox as for
- *                   pkv_rope_apply; the keys must already be rotated (for
- *                   example stored with pkv_reshape_and_cache_rope).  Rows at
- *                   a negative position (Lq > Lk) are not rotated.
+ *                   pkv_rope_apply.  Rows at a negative position (Lq > Lk)
+ *                   are not rotated.
+ *   rope_k          0: the keys are already rotated (for example stored with
+ *                   pkv_reshape_and_cache_rope; always so for paged keys).
+ *                   1 (contiguous K and a table only): key j is rotated by
+ *                   its position j as it is loaded (vLLM page,
+ *                   PagedAttentionWithRoPE.forward rotates query and key
+ *                   before attention); k itself is not modified.  The
+ *                   rotated keys are rounded to bf16 as pkv_rope_apply
+ *                   would store them.  Other values: PKV_ERR_SHAPE; 1 with
+ *                   paged keys, without a table or with ALiBi slopes (two
+ *                   position encodings at once): PKV_ERR_UNSUPPORTED.
  *
  * Errors besides the common ones: PKV_ERR_UNSUPPORTED for bfloat16 with
  * contiguous K/V when max_seqlen_k * num_kv_heads * head_dim * 2 bytes (one
@@ -462,8 +471,8 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
                               int32_t num_kv_heads, int32_t head_dim, float sm_scale,
                               int32_t causal, int32_t window_left, const float *alibi_slopes,
                               const float *rope_cos_sin, int32_t rope_positions,
-                              int32_t rotary_dim, int32_t rope_neox, const float *sink,
-                              pkv_dtype dtype, void *stream);
+                              int32_t rotary_dim, int32_t rope_neox, int32_t rope_k,
+                              const float *sink, pkv_dtype dtype, void *stream);
 
 /*
  * Vertical + slash sparse prefill (nano-vllm "minference.py" page,

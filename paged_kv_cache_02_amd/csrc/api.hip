@@ -602,9 +602,8 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
                               int32_t head_dim, float sm_scale, int32_t causal,
                               int32_t window_left, const float *alibi_slopes,
                               const float *rope_cos_sin, int32_t rope_positions,
-                              int32_t rotary_dim, int32_t rope_neox, const float *sink,
-                              pkv_dtype dtype,
-                              void *stream)
+                              int32_t rotary_dim, int32_t rope_neox, int32_t rope_k,
+                              const float *sink, pkv_dtype dtype, void *stream)
 {
     if (B < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return PKV_ERR_SHAPE;
     pkv_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
@@ -622,6 +621,10 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
     const bool contiguous = k != nullptr || v != nullptr;
     const bool paged = k_cache != nullptr || v_cache != nullptr || block_table != nullptr;
     if (contiguous && paged) return PKV_ERR_SHAPE;
+    // rotating K as it is loaded: a table, and contiguous keys (cached keys
+    // are rotated when they are stored)
+    if (rope_k != 0 && rope_k != 1) return PKV_ERR_SHAPE;
+    if (rope_k && (!rope_cos_sin || paged || alibi_slopes)) return PKV_ERR_UNSUPPORTED;
     if (paged) {
         if ((st = check_block_size(block_size)) != PKV_OK) return st;
         if (num_blocks < 0 || max_blocks_per_seq < 0) return PKV_ERR_SHAPE;
@@ -647,6 +650,7 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
         a.out = out; a.lse = lse; a.q = q; a.k = k; a.v = v; a.k_cache = k_cache;
         a.v_cache = v_cache; a.block_table = block_table; a.cu_q = cu_seqlens_q;
         a.rope = rope_cos_sin; a.rope_dim = rotary_dim; a.rope_neox = rope_neox;
+        a.rope_k = rope_k;
         a.cu_k = cu_seqlens_k; a.sink = sink; a.alibi = alibi_slopes; a.B = B;
         a.Hq = num_q_heads; a.Hkv = num_kv_heads;
         a.G = num_q_heads / num_kv_heads; a.D = head_dim; a.bs_log2 = bs_log2;
@@ -672,7 +676,7 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
     RowArgs a{};
     a.mode = 1; a.out = out; a.lse = lse; a.q = q; a.k = k; a.v = v; a.k_cache = k_cache;
     a.v_cache = v_cache; a.block_table = block_table; a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
-    a.rope = rope_cos_sin; a.rope_dim = rotary_dim; a.rope_neox = rope_neox;
+    a.rope = rope_cos_sin; a.rope_dim = rotary_dim; a.rope_neox = rope_neox; a.rope_k = rope_k;
     a.sink = sink; a.alibi = alibi_slopes; a.B = B; a.Hq = num_q_heads; a.Hkv = num_kv_heads;
     a.G = num_q_heads / num_kv_heads; a.D = head_dim; a.bs_log2 = bs_log2;
     a.mbps = max_blocks_per_seq; a.window_left = window_left; a.scale_log2 = sm_scale * kLog2e;

@@ -183,6 +183,7 @@ struct RowArgs {
     const float *alibi;          // [Hq] ALiBi slopes or null
     const float *rope;           // prefill: q rotary table or null (as PrefillArgs)
     int32_t rope_dim, rope_neox;
+    int32_t rope_k;              // prefill: contiguous K rotated too (as PrefillArgs)
     int32_t B, T, Hq, Hkv, G, D;   // prefill: T = max_seqlen_q
     int32_t bs_log2, mbps, window_left;
     // prefill: 1 = key j visible to position p only when j <= p; 0 = every
@@ -209,6 +210,9 @@ struct PrefillArgs {
     // cos then sin) or null
     const float *rope;
     int32_t rope_dim, rope_neox;
+    // 1: contiguous K is rotated by key position as it is loaded (the
+    // table above; paged keys are rotated when they are cached)
+    int32_t rope_k;
     int32_t B, Hq, Hkv, G, D;
     int32_t bs_log2, mbps, window_left;
     int32_t causal;              // as RowArgs::causal

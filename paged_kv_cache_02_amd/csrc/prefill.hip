@@ -108,7 +108,7 @@ __device__ __forceinline__ void rope_pairs(bf16x8 (&qf)[QK], const float *tab, i
     }
 }
 
-template <int D, bool PAGED, bool ALIBI, bool RUN>
+template <int D, bool PAGED, bool ALIBI, bool RUN, bool ROPEK = false>
 __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_kernel(PrefillArgs a)
 {
     using TL = Tile<D>;
@@ -246,6 +246,110 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
             }
         } else {
             rope_pairs(qf, tab, lh, a.rope_dim, rot);
+        }
+    };
+
+    // ---- ROPEK: contiguous K rotated by key position in LDS ----
+    // Once a K tile has landed, each wave rotates 16 of its rows in place
+    // (row 16 wave + lane / 4; lane % 4 takes every fourth chunk pair (neox)
+    // or chunk (interleaved) of the row) before any wave reads the tile.
+    // Rows past the request's keys stay as they are (zeros, masked).  The
+    // table rows of a tile are loaded after the tile before it has been
+    // computed, in flight with that tile's last copies.
+    static_assert(!(ROPEK && (PAGED || ALIBI)),
+                  "paged keys are rotated when they are cached; rotary and ALiBi positions "
+                  "are alternatives");
+    constexpr int KR = ROPEK ? (D == 128 ? 32 : 16) : 1;    // table floats per lane
+    [[maybe_unused]] float ktab[KR];
+    const int kr_row = 16 * wave + (lane >> 2), kr_part = lane & 3;
+    [[maybe_unused]] auto load_ktab = [&](int t0) {
+        if constexpr (ROPEK) {
+            const int half = a.rope_dim / 2;
+            const float *tab = a.rope + (size_t)max(0, min(t0 + kr_row, Lk - 1)) * a.rope_dim;
+            if (a.rope_neox) {
+#pragma unroll
+                for (int k = 0; k < KR / 16; ++k) {          // chunk pair p: dims 8p and half + 8p
+                    const int p = kr_part + 4 * k;
+                    if (8 * p < half) {
+#pragma unroll
+                        for (int e = 0; e < 8; e += 4) {
+                            *reinterpret_cast<f32x4 *>(ktab + 16 * k + e) =
+                                *reinterpret_cast<const f32x4 *>(tab + 8 * p + e);
+                            *reinterpret_cast<f32x4 *>(ktab + 16 * k + 8 + e) =
+                                *reinterpret_cast<const f32x4 *>(tab + half + 8 * p + e);
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < KR / 8; ++k) {           // chunk c: pairs 4c .. 4c + 3
+                    const int c = kr_part + 4 * k;
+                    if (8 * c < a.rope_dim) {
+                        *reinterpret_cast<f32x4 *>(ktab + 8 * k) =
+                            *reinterpret_cast<const f32x4 *>(tab + 4 * c);
+                        *reinterpret_cast<f32x4 *>(ktab + 8 * k + 4) =
+                            *reinterpret_cast<const f32x4 *>(tab + half + 4 * c);
+                    }
+                }
+            }
+        }
+    };
+    [[maybe_unused]] auto rotate_k = [&](int buf, int t0) {
+        if constexpr (ROPEK) {
+            if (t0 + kr_row >= Lk) return;
+            char *kr = lds + buf * TL::BUF + kr_row * U * 16;
+            const int sw = TL::swz_k(kr_row);
+            const int half = a.rope_dim / 2;
+            auto unpack = [](u32x4 w, float (&x)[8]) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    x[2 * j] = bf16_lo(w[j]);
+                    x[2 * j + 1] = bf16_hi(w[j]);
+                }
+            };
+            if (a.rope_neox) {
+#pragma unroll
+                for (int k = 0; k < KR / 16; ++k) {
+                    const int p = kr_part + 4 * k;
+                    if (8 * p < half) {
+                        u32x4 *pu = reinterpret_cast<u32x4 *>(kr + ((p ^ sw) * 16));
+                        u32x4 *pv = reinterpret_cast<u32x4 *>(kr + (((p + half / 8) ^ sw) * 16));
+                        float x[8], y[8];
+                        unpack(*pu, x);
+                        unpack(*pv, y);
+                        u32x4 wx, wy;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float c0 = ktab[16 * k + 2 * j], c1 = ktab[16 * k + 2 * j + 1];
+                            const float s0 = ktab[16 * k + 8 + 2 * j], s1 = ktab[16 * k + 9 + 2 * j];
+                            wx[j] = pack_bf16x2(x[2 * j] * c0 - y[2 * j] * s0,
+                                                x[2 * j + 1] * c1 - y[2 * j + 1] * s1);
+                            wy[j] = pack_bf16x2(y[2 * j] * c0 + x[2 * j] * s0,
+                                                y[2 * j + 1] * c1 + x[2 * j + 1] * s1);
+                        }
+                        *pu = wx;
+                        *pv = wy;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < KR / 8; ++k) {
+                    const int c = kr_part + 4 * k;
+                    if (8 * c < a.rope_dim) {
+                        u32x4 *pc = reinterpret_cast<u32x4 *>(kr + ((c ^ sw) * 16));
+                        float x[8];
+                        unpack(*pc, x);
+                        u32x4 w;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float co = ktab[8 * k + j], si = ktab[8 * k + 4 + j];
+                            w[j] = pack_bf16x2(x[2 * j] * co - x[2 * j + 1] * si,
+                                               x[2 * j + 1] * co + x[2 * j] * si);
+                        }
+                        *pc = w;
+                    }
+                }
+            }
         }
     };
 
@@ -490,12 +594,20 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
         if (ntiles > 0) {
             if (!prefetched) issue(t_begin, buf);
             if (a.rope) rotate_q();
+            if constexpr (ROPEK) load_ktab(t_begin);
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             __syncthreads();
         }
         prefetched = false;
         for (int it = 0; it < ntiles; ++it) {
             const int t0 = t_begin + it * BN;
+            if constexpr (ROPEK) {
+                // the landed tile rotated before any wave reads it, and before
+                // the next tile's copies are issued (nothing is in flight at
+                // this barrier)
+                rotate_k(buf, t0);
+                __syncthreads();
+            }
             if (it + 1 < ntiles) {
                 issue(t0 + BN, buf ^ 1);
             } else if constexpr (RUN) {
@@ -509,6 +621,11 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
                 }
             }
             if (wrows > 0 && t0 < w_hi && t0 + BN > w_lo) compute(buf, t0);
+            // the next tile's table rows, in flight with its copies (loaded
+            // after the tile's compute, so that they take no registers there)
+            if constexpr (ROPEK) {
+                if (it + 1 < ntiles) load_ktab(t0 + BN);
+            }
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             __syncthreads();
             buf ^= 1;
@@ -594,6 +711,8 @@ pkv_status launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream)
         };
 #define PKV_SET(DD, PG, AL, RN) \
         set((const void *)prefill_bf16_kernel<DD, PG, AL, RN>, prefill_lds_bytes<DD>(RN))
+#define PKV_SET_RK(DD, AL, RN) \
+        set((const void *)prefill_bf16_kernel<DD, false, AL, RN, true>, prefill_lds_bytes<DD>(RN))
         PKV_SET(128, false, false, false); PKV_SET(128, true, false, false);
         PKV_SET(64, false, false, false); PKV_SET(64, true, false, false);
         PKV_SET(128, false, true, false); PKV_SET(128, true, true, false);
@@ -602,16 +721,25 @@ pkv_status launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream)
         PKV_SET(64, false, false, true); PKV_SET(64, true, false, true);
         PKV_SET(128, false, true, true); PKV_SET(128, true, true, true);
         PKV_SET(64, false, true, true); PKV_SET(64, true, true, true);
+        PKV_SET_RK(128, false, false); PKV_SET_RK(64, false, false);
+        PKV_SET_RK(128, false, true); PKV_SET_RK(64, false, true);
+#undef PKV_SET_RK
 #undef PKV_SET
         return first;
     }();
     if (raised != hipSuccess) return PKV_ERR_HIP;
     const bool paged = a.block_table != nullptr;
+    if (a.rope_k && (paged || !a.rope || a.alibi)) return PKV_ERR_UNSUPPORTED;
     const dim3 g((unsigned)grid), b(256);
     auto go = [&](auto kernel, int lds) { hipLaunchKernelGGL(kernel, g, b, lds, stream, a); };
     auto pick = [&](auto dtag) {
         constexpr int DD = decltype(dtag)::value;
         const int lds = prefill_lds_bytes<DD>(run);
+        if (a.rope_k) {
+            if (run) go(prefill_bf16_kernel<DD, false, false, true, true>, lds);
+            else go(prefill_bf16_kernel<DD, false, false, false, true>, lds);
+            return;
+        }
         if (a.alibi) {
             if (run) {
                 if (paged) go(prefill_bf16_kernel<DD, true, true, true>, lds);

@@ -134,10 +134,14 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a)
         }
         const size_t off = (row * a.Hkv + g) * D;
         const bool is_new = a.mode == 0 && a.append && jj == Lk - 1;
+        float kv[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) kv[e] = is_new ? kn[e] : ld_elem(kb, off + lane + 64 * e);
+        // prefill over contiguous K with rope_k: the key rotated by its position
+        if (a.mode == 1 && a.rope_k && a.k) rotate(kv, kb, off, jj);
         float s = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-            s = fmaf(qv[e], is_new ? kn[e] : ld_elem(kb, off + lane + 64 * e), s);
+        for (int e = 0; e < E; ++e) s = fmaf(qv[e], kv[e], s);
 #pragma unroll
         for (int msk = 1; msk < 64; msk <<= 1) s += shfl_xor(s, msk);
         s = fmaf(slope_log2, (float)(jj - pos), s);

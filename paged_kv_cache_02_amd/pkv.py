@@ -63,7 +63,8 @@ SIGNATURES = {
                                           _I32, _I32, _I32, _I32, _F, _P, ctypes.c_int, _P]),
     "pkv_varlen_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P,
                                           _P, _I32, _I32, _I32, _I32, _I32, _I32, _F, _I32,
-                                          _I32, _P, _P, _I32, _I32, _I32, _P, ctypes.c_int, _P]),
+                                          _I32, _P, _P, _I32, _I32, _I32, _I32, _P, ctypes.c_int,
+                                          _P]),
 }
 
 
@@ -370,9 +371,11 @@ def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_
                    k_cache=None, v_cache=None, block_table=None, sink=None,
                    window_left: int = -1, out=None, lse=None, alibi_slopes=None,
                    rope_cos_sin=None, rotary_dim: int = 0, rope_neox: bool = True,
-                   causal: bool = True):
+                   causal: bool = True, rope_k: bool = False):
     """Varlen prefill: out [sum Lq, Hq, D].  causal=False lets every query
-    row see every key of its request (a window still bounds the left side)."""
+    row see every key of its request (a window still bounds the left side).
+    With rope_cos_sin, q is rotated by its position; rope_k=True rotates the
+    contiguous keys by theirs too (k is not modified)."""
     if rope_cos_sin is not None:
         _rope_table(rope_cos_sin, rotary_dim)
     T, Hq, D = q.shape
@@ -395,8 +398,8 @@ def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_
         Hkv, D, float(sm_scale), int(bool(causal)), window_left, _ptr(_f32(alibi_slopes, "alibi_slopes")),
         _ptr(rope_cos_sin),
         0 if rope_cos_sin is None else rope_cos_sin.shape[0], rotary_dim, int(bool(rope_neox)),
-        _ptr(_f32(sink, "sink")), _dt(q, k, v, k_cache, v_cache, out), _stream()),
-        "varlen_prefill")
+        int(bool(rope_k)), _ptr(_f32(sink, "sink")), _dt(q, k, v, k_cache, v_cache, out),
+        _stream()), "varlen_prefill")
     return out
 
 

@@ -139,7 +139,7 @@ def prefill_call(**over):
     a = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, k_cache=None, v_cache=None, bt=None,
              bs=0, NB=0, MB=0, cu_q=FAKE, cu_k=FAKE, B=2, maxq=16, maxk=16, Hq=8, Hkv=2, D=64,
              scale=0.1, causal=1, window=-1, alibi=None, rope=None, rope_pos=0, rope_dim=0,
-             rope_neox=1, sink=None, dt=1, stream=None)
+             rope_neox=1, rope_k=0, sink=None, dt=1, stream=None)
     a.update(over)
     return lib.pkv_varlen_prefill(*a.values())
 
@@ -157,6 +157,12 @@ def prefill_call(**over):
     (dict(causal=2), pkv.PKV_ERR_SHAPE),
     (dict(causal=-1), pkv.PKV_ERR_SHAPE),
     (dict(causal=0, B=0), pkv.PKV_OK),                          # non-causal accepted
+    (dict(rope_k=1), pkv.PKV_ERR_UNSUPPORTED),                  # K rotation needs a table
+    (dict(rope_k=2, rope=FAKE, rope_pos=16, rope_dim=64), pkv.PKV_ERR_SHAPE),
+    (dict(rope_k=1, rope=FAKE, rope_pos=16, rope_dim=64, k=None, v=None, k_cache=FAKE,
+          v_cache=FAKE, bt=FAKE, bs=16, NB=4, MB=4), pkv.PKV_ERR_UNSUPPORTED),  # paged keys
+    (dict(rope_k=1, rope=FAKE, rope_pos=16, rope_dim=64, B=0), pkv.PKV_OK),
+    (dict(rope_k=1, rope=FAKE, rope_pos=16, rope_dim=64, alibi=FAKE), pkv.PKV_ERR_UNSUPPORTED),
     (dict(Hkv=3), pkv.PKV_ERR_SHAPE),
     (dict(D=80), pkv.PKV_ERR_UNSUPPORTED),
     (dict(window=-5), pkv.PKV_ERR_SHAPE),

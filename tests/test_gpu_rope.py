@@ -185,6 +185,56 @@ def test_prefill_rope_noncausal(case, dtype):
     assert_close(lse, l, dtype, "prefill rope non-causal lse", lse=True)
 
 
+ROPE_K = [
+    # q_lens, k_lens, Hq, Hkv, D, rotary_dim, neox, window, causal
+    ([1, 100, 300], None, 32, 8, 128, 128, True, -1, True),
+    ([64, 257], None, 8, 2, 64, 32, False, -1, True),
+    ([33, 200], [500, 200], 12, 4, 128, 64, True, -1, True),     # chunks after cached keys
+    ([300, 77, 513], None, 8, 2, 128, 128, True, 50, True),       # window: runs of blocks
+    ([90, 7], [300, 64], 16, 4, 64, 64, True, -1, False),         # non-causal
+    ([129, 1000], [129, 1000], 16, 2, 128, 96, False, -1, True),
+]
+
+
+@pytest.mark.parametrize("case", ROPE_K, ids=[str(i) for i in range(len(ROPE_K))])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_prefill_rope_k(case, dtype):
+    """rope_k: contiguous keys rotated by their positions as the prefill loads
+    them, q by its own; against the oracle fed q and k rotated with its own
+    table (k rounded to the storage type, as the kernel rounds it)."""
+    from paged_kv_cache_02_amd import pkv
+    q_lens, k_lens, Hq, Hkv, D, rd, neox, window, causal = case
+    banner(f"prefill rope_k {dtype} {case}")
+    k_lens = k_lens or q_lens
+    c = synth.prefill_case(560 + len(q_lens), q_lens, k_lens, Hq, Hkv, D, dtype, True,
+                           window_left=window)
+    n_pos = max(k_lens)
+    tab = pkv.rope_cos_sin(n_pos, rd, 10000.0)
+    otab = oracle.rope_cos_sin(n_pos, rd, 10000.0)
+    k0 = dev(c.k)
+    k_before = k0.clone()
+    T = c.q.shape[0]
+    lse = torch.empty(T, Hq, dtype=torch.float32, device="cuda")
+    out = pkv.varlen_prefill(dev(c.q), dev(c.cu_seqlens_q), dev(c.cu_seqlens_k), c.max_seqlen_q,
+                             c.max_seqlen_k, c.sm_scale, Hkv, k=k0, v=dev(c.v), sink=dev(c.sink),
+                             lse=lse, window_left=window, causal=causal, rope_cos_sin=tab,
+                             rotary_dim=rd, rope_neox=neox, rope_k=True)
+    torch.cuda.synchronize()
+    bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(k0.view(bits), k_before.view(bits)), "k modified"
+    kpos = np.concatenate([np.arange(L) for L in k_lens]).astype(np.int32)
+    krot = synth.to_dtype(oracle.rope_apply(c.k, kpos, otab, rd, neox).astype(np.float32), dtype)
+    qpos = oracle.query_positions(c.cu_seqlens_q, c.cu_seqlens_k)
+    at = qpos >= 0
+    qrot = c.q.double().numpy().copy()
+    qrot[at] = oracle.rope_apply(c.q[torch.from_numpy(at)], qpos[at], otab, rd, neox)
+    o, l = oracle.varlen_prefill(torch.from_numpy(qrot).float(), c.cu_seqlens_q, c.cu_seqlens_k,
+                                 c.sink, c.sm_scale, Hkv, k=krot.float(), v=c.v.float(),
+                                 window_left=window, causal=causal)
+    assert_close(out, o, dtype, "prefill rope_k out")
+    assert_close(lse, l, dtype, "prefill rope_k lse", lse=True)
+
+
 def test_prefill_rejects_mixed_dtypes():
     """K or V of another dtype than q is refused before any launch (the
     kernels would read its bytes as q's type)."""
@@ -279,6 +329,7 @@ def test_config3_rope_full_size():
     sink) as the benchmark times it with RoPE (rotary_dim 128, neox): q
     rotated inside the prefill over contiguous keys that the oracle rotated
     with its own table, every output element and lse against the oracle;
+    the same with the unrotated keys rotated inside the same launch;
     and every key stored by reshape_and_cache_rope into a block-16 pool,
     compared in full with the oracle's rotation (values bitwise)."""
     from paged_kv_cache_02_amd import pkv
@@ -311,6 +362,16 @@ def test_config3_rope_full_size():
                                  k=krot.float(), v=c.v.float())
     assert_close(out, o, torch.bfloat16, "config3 rope out")
     assert_close(lse, l, torch.bfloat16, "config3 rope lse", lse=True)
+    # one launch: the unrotated keys rotated as the prefill loads them
+    out.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    pkv.varlen_prefill(dev(c.q), dev(c.cu_seqlens_q), dev(c.cu_seqlens_k), c.max_seqlen_q,
+                       c.max_seqlen_k, c.sm_scale, c.Hkv, k=dev(c.k), v=dev(c.v),
+                       sink=dev(c.sink), lse=lse, out=out, rope_cos_sin=tab, rotary_dim=rd,
+                       rope_k=True)
+    torch.cuda.synchronize()
+    assert_close(out, o, torch.bfloat16, "config3 rope_k out")
+    assert_close(lse, l, torch.bfloat16, "config3 rope_k lse", lse=True)
     s = slots.long()
     assert_close(kc.view(-1, c.Hkv, c.D)[s], krot.float().numpy(), torch.bfloat16,
                  "config3 rotated keys")
