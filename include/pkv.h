@@ -78,8 +78,11 @@
  * j % block_size.  Entries of block_table past the ones a sequence needs are
  * never read (they may hold -1).
  *
- * Supported: head_dim in {64, 128}; block_size a power of two in [16, 512];
- * num_q_heads a multiple of num_kv_heads; dtype PKV_F32 or PKV_BF16.
+ * Supported: head_dim in {64, 128}; block_size a power of two in [8, 512];
+ * num_q_heads a multiple of num_kv_heads; dtype PKV_F32 or PKV_BF16.  The
+ * bf16 decode kernels read keys in tiles of 16 tokens: with block_size 8 a
+ * tile spans two blocks (read through per-lane addresses instead of one
+ * range-checked descriptor), and bf16 partitions must be multiples of 16.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -224,7 +227,8 @@ size_t pkv_paged_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t 
  *   max_seqlen_k    host upper bound on cache_seqlens (sizes the launch)
  *   window_left     -1 for none, else >= 0
  *   partition_size  > 0: split the keys into [p*P, (p+1)*P) partitions (a
- *                   multiple of block_size), each reduced on its own, then
+ *                   multiple of block_size, and of 16 in bf16; otherwise
+ *                   PKV_ERR_SHAPE), each reduced on its own, then
  *                   merged by log-sum-exp.  0: automatic -- bf16 uses a balanced
  *                   schedule that gives every wave of the device an equal share
  *                   of all sequences' key tiles and merges the pieces the same

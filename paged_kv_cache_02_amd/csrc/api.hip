@@ -31,7 +31,7 @@ pkv_status check_heads(int32_t Hq, int32_t Hkv, int32_t D) {
 
 pkv_status check_block_size(int32_t bs) {
     if (bs <= 0) return PKV_ERR_SHAPE;
-    if (!is_pow2(bs) || bs < 16 || bs > 512) return PKV_ERR_UNSUPPORTED;
+    if (!is_pow2(bs) || bs < 8 || bs > 512) return PKV_ERR_UNSUPPORTED;
     return PKV_OK;
 }
 
@@ -222,6 +222,8 @@ pkv_status decode_check(const DecodeCall &c) {
     if (!dtype_ok(c.dtype)) return PKV_ERR_UNSUPPORTED;
     if (c.window_left < -1 || c.partition_size < 0 || !scale_ok(c.sm_scale)) return PKV_ERR_SHAPE;
     if (c.partition_size > 0 && c.partition_size % c.block_size) return PKV_ERR_SHAPE;
+    // bf16 partitions hold whole 16-token tiles
+    if (c.dtype == PKV_BF16 && c.partition_size % 16) return PKV_ERR_SHAPE;
     if ((long long)c.max_seqlen_k > (long long)c.mbps * c.block_size) return PKV_ERR_SHAPE;
     if (c.B == 0) return PKV_OK;
     if (!c.out || !c.q || !c.block_table || !c.cache_seqlens) return PKV_ERR_NULL;
@@ -558,7 +560,7 @@ pkv_status pkv_paged_decode_partitions(float *part_out, float *part_lse, const v
     if ((st = check_block_size(block_size)) != PKV_OK) return st;
     if (!dtype_ok(dtype)) return PKV_ERR_UNSUPPORTED;
     if (window_left < -1 || partition_size <= 0 || partition_size % block_size ||
-        !scale_ok(sm_scale))
+        (dtype == PKV_BF16 && partition_size % 16) || !scale_ok(sm_scale))
         return PKV_ERR_SHAPE;
     if ((long long)max_seqlen_k > (long long)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
     const long long need_parts = ((long long)max_seqlen_k + partition_size - 1) / partition_size;

@@ -278,6 +278,9 @@ struct SparseArgs {
 };
 
 pkv_status launch_rows(const RowArgs &a, hipStream_t stream);
+// block size 8 (decode_bs8.hip)
+pkv_status launch_decode_bf16_bs8(const DecodeArgs &a, hipStream_t stream);
+pkv_status launch_decode_stream_bf16_bs8(const StreamArgs &a, hipStream_t stream);
 pkv_status launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream);
 pkv_status launch_vertical_slash(const VerticalSlashArgs &a, hipStream_t stream);
 pkv_status launch_sparse_prefill(const SparseArgs &a, hipStream_t stream);

@@ -79,7 +79,10 @@ def decode_call(**over):
     (dict(Hq=6, Hkv=4), pkv.PKV_ERR_SHAPE),
     (dict(D=96), pkv.PKV_ERR_UNSUPPORTED),
     (dict(bs=24), pkv.PKV_ERR_UNSUPPORTED),
-    (dict(bs=8), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(bs=4), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(bs=8, MB=8), pkv.PKV_ERR_WORKSPACE),        # block size 8 accepted (bf16 needs one)
+    (dict(bs=8, MB=8, part=8), pkv.PKV_ERR_SHAPE),    # bf16 partitions are whole 16-token tiles
+    (dict(bs=8, MB=8, part=8, dt=0), pkv.PKV_ERR_WORKSPACE),   # fp32: any multiple of 8
     (dict(dt=7), pkv.PKV_ERR_UNSUPPORTED),
     (dict(window=-2), pkv.PKV_ERR_SHAPE),
     (dict(part=24), pkv.PKV_ERR_SHAPE),

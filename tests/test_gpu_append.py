@@ -69,6 +69,7 @@ CASES = [
     ([77, 200, 15], 16, 2, 128, 64, True, 0),          # window 0: only the new token
     ([1000, 3, 48], 64, 8, 128, 16, True, -1),          # G 8: two head groups per kv head
     ([129, 7], 12, 4, 64, 16, True, 20),                # G 3
+    ([0, 7, 8, 15, 16, 100], 8, 2, 128, 8, True, -1),   # block size 8: tiles over two blocks
 ]
 
 

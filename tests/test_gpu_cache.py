@@ -25,7 +25,8 @@ def _scatter_case(seed, T, Hkv, D, bs, NB, dtype, n_pad=3):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("T,Hkv,D,bs,NB", [(1, 1, 64, 16, 1), (37, 2, 64, 32, 4),
-                                            (300, 8, 128, 16, 40), (50, 32, 128, 64, 2)])
+                                            (300, 8, 128, 16, 40), (50, 32, 128, 64, 2),
+                                            (41, 4, 128, 8, 12)])
 def test_reshape_and_cache_bitwise(dtype, T, Hkv, D, bs, NB):
     banner(f"reshape_and_cache {dtype} T={T} Hkv={Hkv} D={D}")
     from paged_kv_cache_02_amd import pkv

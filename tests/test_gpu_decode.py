@@ -88,6 +88,9 @@ CASES = [
     ([1, 2, 200, 600], 16, 2, 64, 16, True, 0),
     ([300, 301, 2048], 4, 1, 128, 128, True, 700),
     ([47, 1500], 16, 4, 64, 16, False, 3),
+    # block size 8: every 16-token tile spans two blocks
+    ([0, 1, 7, 8, 9, 15, 16, 17, 100, 333], 8, 2, 128, 8, True, -1),
+    ([40, 1500, 63], 16, 4, 64, 8, False, 20),
 ]
 
 
@@ -99,7 +102,7 @@ def test_decode_vs_oracle(case, dtype):
     c = synth.decode_case(11 + len(lengths), lengths, Hq, Hkv, D, bs, dtype, with_sink=sink,
                           window_left=window, poison=True)
     o, l = oracle_decode(c)
-    for P in (0, bs, 2 * bs, 256 if 256 % bs == 0 else bs, 512):
+    for P in (0, max(16, bs), 2 * max(16, bs), 256 if 256 % bs == 0 else bs, 512):
         out, lse = run_decode(c, partition_size=P)
         assert_close(out, o, dtype, f"out P={P}")
         assert_close(lse, l, dtype, f"lse P={P}", lse=True)
@@ -333,8 +336,10 @@ def test_two_launch_decode_vs_oracle(case):
     assert_close(lse, l, torch.bfloat16, "two-launch lse", lse=True)
 
 
-@pytest.mark.parametrize("D,Hq,Hkv,window,B", [(128, 32, 8, -1, 300), (64, 16, 2, 9, 1200)])
-def test_decode_many_short_sequences(D, Hq, Hkv, window, B):
+@pytest.mark.parametrize("D,Hq,Hkv,window,B,bs", [(128, 32, 8, -1, 300, 16),
+                                                   (64, 16, 2, 9, 1200, 16),
+                                                   (128, 8, 2, -1, 500, 8)])
+def test_decode_many_short_sequences(D, Hq, Hkv, window, B, bs):
     """Hundreds of 1..40-key sequences: each wave's range of the balanced
     schedule crosses several sequences, so the Q of the second sequence
     (preloaded) and of later ones (loaded at the change) are both used;
@@ -343,7 +348,7 @@ def test_decode_many_short_sequences(D, Hq, Hkv, window, B):
     from paged_kv_cache_02_amd import pkv
     rng = np.random.default_rng(61)
     lengths = rng.integers(1, 40, size=B, endpoint=True).tolist()
-    c = synth.decode_case(62, lengths, Hq, Hkv, D, 16, torch.bfloat16, with_sink=True,
+    c = synth.decode_case(62, lengths, Hq, Hkv, D, bs, torch.bfloat16, with_sink=True,
                           window_left=window, poison=True)
     o, l = oracle_decode(c)
     out, lse = run_decode(c)
@@ -358,3 +363,20 @@ def test_decode_many_short_sequences(D, Hq, Hkv, window, B):
     torch.cuda.synchronize()
     assert_close(out2, o, torch.bfloat16, "two launches out")
     assert_close(lse2, l, torch.bfloat16, "two launches lse", lse=True)
+
+
+@pytest.mark.parametrize("bs", [16, 8])
+def test_decode_large_batch(bs):
+    """More sequences than the balanced schedule takes (B > 4096): bf16 decode
+    runs one workgroup per (sequence, head group, partition), unsplit and
+    with 64-token partitions merged afterwards."""
+    banner(f"large batch bs={bs}")
+    rng = np.random.default_rng(63)
+    lengths = rng.integers(0, 80, size=4100, endpoint=True).tolist()
+    c = synth.decode_case(64, lengths, 8, 2, 128, bs, torch.bfloat16, with_sink=True,
+                          poison=True)
+    o, l = oracle_decode(c)
+    for P in (0, 64):
+        out, lse = run_decode(c, partition_size=P)
+        assert_close(out, o, torch.bfloat16, f"out P={P}")
+        assert_close(lse, l, torch.bfloat16, f"lse P={P}", lse=True)

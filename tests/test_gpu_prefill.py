@@ -86,6 +86,8 @@ PAGED = [
     ([129, 1], [129, 2000], 8, 8, 128, 64, False, 17),
     ([40, 1, 200], [40 + 150, 70, 200 + 64], 8, 2, 64, 16, False, -1),   # D 64 ring, no window
     ([90, 200], [300, 200], 16, 2, 128, 16, True, -1),                   # G 8: two head subgroups
+    ([64, 100], [364, 100], 16, 8, 64, 8, True, 128),                    # block size 8
+    ([90, 200], [300, 200], 8, 2, 128, 8, True, -1),
 ]
 
 
