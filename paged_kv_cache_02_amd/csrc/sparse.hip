@@ -18,10 +18,13 @@
 //     blocks), then writes the offsets in ascending order (a wave prefix sum
 //     over the set's words) and the surviving columns in the order given
 //     (ballot and bit count);
-//   * sparse_prefill_kernel: one workgroup of two waves per (request, head,
-//     row block), 32 query rows per wave with Q in registers, row blocks
-//     issued longest first.  It walks its slash blocks, then its columns 64
-//     at a time, with the dense prefill's tile layout: K and V rows go
+//   * sparse_prefill_kernel: one workgroup of four waves per (request, head,
+//     row block), row blocks issued longest first; wave w takes query rows
+//     32 (w % 2) .. +32 (Q in registers) against keys 32 (w / 2) .. +32 of
+//     every tile, so that a 64-row block still keeps eight waves on a compute
+//     unit, and the two key halves of a row are merged through LDS at the
+//     end.  It walks its slash blocks, then its columns 64 at a time, with
+//     the dense prefill's tile layout: K and V rows go
 //     straight from global memory into a swizzled LDS tile (a 64-key block
 //     through a range-checked buffer descriptor, 64 columns as gathered
 //     rows), double buffered; S^T = K . Q^T and O^T += V^T . P^T on
@@ -38,7 +41,7 @@ namespace pkv {
 
 namespace {
 
-constexpr int kSparseWaves = 2;
+constexpr int kSparseWaves = 4;
 constexpr int kNoKey = 0x7fffffff;       // position of a padding row: never visible
 
 __global__ __launch_bounds__(64) void vertical_slash_kernel(VerticalSlashArgs a)
@@ -121,7 +124,7 @@ template <int D>
 constexpr int sparse_lds_bytes() { return 2 * Tile<D>::BUF + 2 * BN * (int)sizeof(int); }
 
 template <int D>
-__global__ __launch_bounds__(64 * kSparseWaves) void sparse_prefill_kernel(SparseArgs a)
+__global__ __launch_bounds__(64 * kSparseWaves, 2) void sparse_prefill_kernel(SparseArgs a)
 {
     using TL = Tile<D>;
     constexpr int U = TL::U;
@@ -158,7 +161,8 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_prefill_kernel(Spars
     const int32_t *cidx = a.column_index + bhm * a.NV;
     const float sig = a.sink ? a.sink[h] * kLog2e : -INFINITY;
 
-    const int wrow0 = r0 + 32 * wave;            // this wave's first row
+    const int kh = wave >> 1;                    // this wave's 32 keys of each tile
+    const int wrow0 = r0 + 32 * (wave & 1);      // this wave's first row
     const int wrows = max(0, min(32, L - wrow0));
     const int qpos = wrow0 + lr;                 // this lane's query position
 
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_prefill_kernel(Spars
         }
     }
 
-    // ---- direct loads: instruction i = wave + 2n of a tile fills LDS bytes
+    // ---- direct loads: instruction i = wave + 4n of a tile fills LDS bytes
     // [1024i, 1024i + 1024), lane L writing row RPI*i + L/U at swizzled unit
     // position (L % U) ^ swz(row) ----
     const uint32_t rowbytes = (uint32_t)kvstride * 2;
@@ -252,68 +256,88 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_prefill_kernel(Spars
         for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
     float m_run = kNoMax, l = 0.f, l1 = 0.f;
 
-    // One tile: S^T of both 32-key chunks, the mask by position, one online
-    // softmax update for the tile, then P.V by 16-key steps.  Accumulator i
-    // of chunk c holds key 32c + 8(i/4) + 4lh + i%4 of query row lr.
+    // One tile, this wave's 32 keys: S^T, the mask by position, one online
+    // softmax update, then P.V by 16-key steps.  Accumulator i holds key
+    // 32kh + 8(i/4) + 4lh + i%4 of query row lr.  LDS operand reads run
+    // ahead of the MFMAs that use them (K reads KA ahead; the V^T reads of
+    // P.V are issued before the softmax work and consumed VA behind), and
+    // the reference max is raised only when a logit exceeds it by more than
+    // 2^kTau (a wave-uniform branch), as in the dense prefill.
+    constexpr int KA = 4;
+    constexpr int NPV = 2 * DT;                  // P.V MFMAs per tile
+    constexpr int VA = NPV < 5 ? NPV : 5;
+    constexpr float kTau = 8.0f;
     auto compute = [&](int buf, int it) {
         const char *kl = lds + buf * TL::BUF;
         const char *vl = kl + TL::BYTES;
         const bool gathered = it >= nb;
         const int t0 = gathered ? 0 : readfirstlane(boff[it]);
-        f32x16 s[2];
+        auto kread = [&](int c) {
+            return *reinterpret_cast<const bf16x8 *>(kl + k_lane + 32 * kh * U * 16 + k_unit[c]);
+        };
+        // V^T operand of P.V MFMA n: 16-key step 2kh + n / DT, dims tile n % DT
+        auto vread = [&](int n) {
+            const char *p0 = vl + v_lane + 16 * (2 * kh + n / DT) * U * 16 + v_unit[n % DT];
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p0);
+            const bf16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p0 + 8 * U * 16));
+            return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        };
+        f32x16 sx;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[0][i] = s[1][i] = 0.f;
+        for (int i = 0; i < 16; ++i) sx[i] = 0.f;
+        bf16x8 kk[KA + 1];
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
+        for (int n = 0; n < KA; ++n) kk[n] = kread(n);
 #pragma unroll
-            for (int c = 0; c < QK_STEPS; ++c) {
-                const bf16x8 kk = *reinterpret_cast<const bf16x8 *>(kl + k_lane + 32 * kc * U * 16 +
-                                                                    k_unit[c]);
-                s[kc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qf[c], s[kc], 0, 0, 0);
-            }
+        for (int n = 0; n < QK_STEPS; ++n) {
+            if (n + KA < QK_STEPS) kk[(n + KA) % (KA + 1)] = kread(n + KA);
+            __builtin_amdgcn_sched_barrier(0);
+            sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[n % (KA + 1)], qf[n], sx, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        bf16x8 vv[VA + 1];
+#pragma unroll
+        for (int n = 0; n < VA; ++n) vv[n] = vread(n);
         float mx = -INFINITY;
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int k0 = 32 * kh + 8 * q4 + 4 * lh;
+            int pos[4];
+            if (gathered) {
+                const u32x4 p4 = *reinterpret_cast<const u32x4 *>(s_pos + buf * BN + k0);
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int k0 = 32 * kc + 8 * q4 + 4 * lh;
-                int pos[4];
-                if (gathered) {
-                    const u32x4 p4 = *reinterpret_cast<const u32x4 *>(s_pos + buf * BN + k0);
+                for (int e = 0; e < 4; ++e) pos[e] = (int)p4[e];
+            } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) pos[e] = (int)p4[e];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) pos[e] = t0 + k0 + e;
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool vis = pos[e] <= qpos && pos[e] < L;
-                    const float x = vis ? s[kc][4 * q4 + e] * a.scale_log2 : -INFINITY;
-                    s[kc][4 * q4 + e] = x;
-                    mx = __builtin_fmaxf(mx, x);
-                }
+                for (int e = 0; e < 4; ++e) pos[e] = t0 + k0 + e;
             }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool vis = pos[e] <= qpos && pos[e] < L;
+                const float x = vis ? sx[4 * q4 + e] * a.scale_log2 : -INFINITY;
+                sx[4 * q4 + e] = x;
+                mx = __builtin_fmaxf(mx, x);
+            }
+        }
         // the other lane half holds the row's other keys
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                          false, false);
         mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        if (mx > m_run) {
-            const float alpha = fast_exp2(m_run - mx);
+        if (__any(mx > m_run + kTau)) {
+            const float nm = fmaxf(m_run, mx);
+            const float alpha = fast_exp2(m_run - nm);
             l *= alpha;
             l1 *= alpha;
 #pragma unroll
             for (int t = 0; t < DT; ++t)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-            m_run = mx;
+            m_run = nm;
         }
-        // O^T += V^T . P^T, 16-key step ks from chunk ks / 2: P slot (lh, e)
-        // is key 16(ks % 2) + 8(e/4) + 4lh + e%4 of the chunk
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const f32x16 &sx = s[ks >> 1];
-            const int sp = ks & 1;
+        // O^T += V^T . P^T: P slot (lh, e) of 16-key step sp is key
+        // 16sp + 8(e/4) + 4lh + e%4 of this wave's 32
+        auto make_p = [&](int sp) {
             u32x4 w;
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2)
@@ -323,16 +347,17 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_prefill_kernel(Spars
             l1 = add_bf16_pair(w[1], l1);
             l = add_bf16_pair(w[2], l);
             l1 = add_bf16_pair(w[3], l1);
-            const bf16x8 pf = __builtin_bit_cast(bf16x8, w);
+            return __builtin_bit_cast(bf16x8, w);
+        };
+        bf16x8 pf = make_p(0);
 #pragma unroll
-            for (int t = 0; t < DT; ++t) {
-                const char *p0 = vl + v_lane + 16 * ks * U * 16 + v_unit[t];
-                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p0);
-                const bf16x4 hi =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p0 + 8 * U * 16));
-                const bf16x8 vv = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pf, o[t], 0, 0, 0);
-            }
+        for (int n = 0; n < NPV; ++n) {
+            if (n + VA < NPV) vv[(n + VA) % (VA + 1)] = vread(n + VA);
+            __builtin_amdgcn_sched_barrier(0);
+            o[n % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[n % (VA + 1)], pf, o[n % DT], 0,
+                                                               0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (n == DT - 1) pf = make_p(1);
         }
     };
 
@@ -348,10 +373,46 @@ __global__ __launch_bounds__(64 * kSparseWaves) void sparse_prefill_kernel(Spars
         if (wrows > 0) compute(buf, it);
     }
 
+    // ---- the two key halves of each row: the kh = 1 waves leave their
+    // running max, sums and accumulators in LDS (the tile buffers are free
+    // once every wave is past its last tile); the kh = 0 waves rescale both
+    // to the larger max and add ----
+    float lsum = l + l1;
+    __syncthreads();
+    constexpr int OW = DT * 16;                  // accumulator floats per lane
+    float *xch = reinterpret_cast<float *>(lds) + (wave & 1) * 64 * (OW + 2);
+    static_assert(2 * 64 * (OW + 2) * 4 <= 2 * TL::BUF, "the exchange fits in the tile buffers");
+    if (kh == 1) {
+        xch[lane] = m_run;
+        xch[64 + lane] = lsum;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; i += 4)
+                *reinterpret_cast<f32x4 *>(xch + 128 + lane * OW + 16 * t + i) =
+                    f32x4{o[t][i], o[t][i + 1], o[t][i + 2], o[t][i + 3]};
+    }
+    __syncthreads();
+    if (kh == 1 || wrows == 0) return;
+    {
+        const float m1 = xch[lane], l1s = xch[64 + lane];
+        const float M = fmaxf(m_run, m1);
+        const float a0 = fast_exp2(m_run - M), a1 = fast_exp2(m1 - M);
+        lsum = lsum * a0 + l1s * a1;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; i += 4) {
+                const f32x4 y = *reinterpret_cast<const f32x4 *>(xch + 128 + lane * OW + 16 * t + i);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[t][i + e] = o[t][i + e] * a0 + y[e] * a1;
+            }
+        m_run = M;
+    }
+
     // ---- epilogue: the sink joins the denominator; each lane stores 4 dims
     // of its row per accumulator quad ----
-    if (wrows == 0) return;
-    float lt = l + l1;
+    float lt = lsum;
     lt += shfl_xor(lt, 32);
     const float Mt = fmaxf(lt > 0.f ? m_run : kNoMax, sig);
     const float sc = fast_exp2(m_run - Mt);
