@@ -150,11 +150,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 # source files of each kernel whose PMC traffic is recorded in the summary
 KERNEL_SOURCES = {
-    "decode_c2": ("decode.hip", "decode.h", "common.h"),
-    "prefill_c3": ("prefill.hip", "decode.h", "common.h"),
-    "prefill_c4": ("prefill.hip", "decode.h", "common.h"),
+    "decode_c2": ("decode_impl.h", "decode.hip", "decode.h", "common.h", "rope.h"),
+    "prefill_c3": ("prefill.hip", "tile.h", "decode.h", "common.h"),
+    "prefill_c4": ("prefill.hip", "tile.h", "decode.h", "common.h"),
     "reshape_c3": ("cache.hip", "common.h"),
-    "reshape_rope_c3": ("rope.hip", "decode.h", "common.h"),
+    "reshape_rope_c3": ("rope.hip", "rope.h", "decode.h", "common.h"),
+    "sparse_32k": ("sparse.hip", "tile.h", "decode.h", "common.h"),
 }
 
 
@@ -526,7 +527,8 @@ def bench_sparse(steps, warmup):
            "kernels_ms": {"vertical_slash_blocks": round(li_ms, 4), "sparse_prefill": round(sp_ms, 4)},
            "dense_causal_prefill_ms": round(de_ms, 4),
            "speedup_vs_dense": round(de_ms / (sp_ms + li_ms), 3),
-           "roofline": roofline("mfma", achieved, MFMA_BF16_PEAK_TFS, "TFLOP/s")}
+           "roofline": roofline("mfma", achieved, MFMA_BF16_PEAK_TFS, "TFLOP/s",
+                                pmc_traffic("sparse_32k"))}
     if not ARGS.no_cpu_baseline:
         import oracle  # the CPU-baseline leg is the only bench code that runs the oracle
         n = host_threads()
