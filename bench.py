@@ -72,48 +72,52 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-class KernelTimer:
-    """HIP events on torch's current stream at launch boundaries.
-
-    Events are preallocated and shared between neighbouring launches (the
-    event that ends one launch starts the next), so a two-kernel step costs
-    two event records, not four."""
-
-    def __init__(self, n=0):
-        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        self.marks = []      # (name, start index, end index)
-        self.k = 0
-
-    def _next(self):
-        if self.k == len(self.events):
-            self.events.append(torch.cuda.Event(enable_timing=True))
-        e = self.events[self.k]
-        self.k += 1
-        e.record()
-        return self.k - 1
-
-    def time(self, name, fn):
-        if self.k == 0 or not self.marks or self.marks[-1][2] != self.k - 1:
-            self._next()
-        start = self.k - 1
-        r = fn()
-        end = self._next()
-        self.marks.append((name, start, end))
-        return r
-
-    def mean_ms(self, name):
-        return float(np.mean([self.events[a].elapsed_time(self.events[b])
-                              for n, a, b in self.marks if n == name]))
-
-    def names(self):
-        return {n for n, _, _ in self.marks}
-
-
 class NoTimer:
-    """Stands in for KernelTimer outside the timed region: launches only."""
+    """Passed to a step outside the kernel timing: launches only."""
 
     def time(self, name, fn):
         return fn()
+
+
+class Preparer:
+    """Passed to a step to collect its launches: each named launch becomes a
+    prepared launcher (pkv.prepare: arguments marshalled once, no Python
+    checks when it runs), so that a timing loop is not limited by the
+    host's call overhead."""
+
+    def __init__(self):
+        self.launchers = {}
+
+    def time(self, name, fn):
+        self.launchers.setdefault(name, []).append(pkv.prepare(fn))
+
+
+class KernelTimes:
+    def __init__(self, ms):
+        self.ms = ms
+
+    def mean_ms(self, name):
+        return self.ms[name]
+
+    def names(self):
+        return set(self.ms)
+
+
+def kernel_ms(launchers, steps, warmup):
+    """Mean duration of one launch: HIP events on the launch stream around
+    `steps` back-to-back launches (cycling through the replicas' launchers),
+    after `warmup` untimed ones."""
+    for i in range(warmup):
+        launchers[i % len(launchers)]()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(steps):
+        launchers[i % len(launchers)]()
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def spin_up(step, seconds):
@@ -130,20 +134,25 @@ def spin_up(step, seconds):
         torch.cuda.synchronize()
 
 
-def timed_steps(step, steps, warmup, launches_per_step=2):
-    """Spin-up, warmup steps, then timed steps; returns (ms per step,
-    KernelTimer of the timed steps)."""
+def timed_steps(step, steps, warmup, reps=1):
+    """Spin-up, warmup steps, then timed steps (wall clock between two
+    synchronizations: ms per step); then each kernel of the step timed on
+    its own with HIP events over back-to-back prepared launches of the
+    `reps` input replicas.  Returns (ms per step, KernelTimes)."""
     spin_up(step, ARGS.spinup)
     for i in range(warmup):
         step(i, NoTimer())
-    kt = KernelTimer(steps * launches_per_step + 1)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i, kt)
+        step(i, NoTimer())
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
-    return ms, kt
+    pr = Preparer()
+    for i in range(reps):
+        step(i, pr)
+    kms = {name: kernel_ms(ls, steps, warmup) for name, ls in pr.launchers.items()}
+    return ms, KernelTimes(kms)
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -258,7 +267,7 @@ def bench_decode(c, name, steps, warmup, partition_size, reps, traffic_key=None,
                                                        partition_size=P, max_seqlen_k=msk,
                                                        out=out, workspace=ws, alibi_slopes=al))
 
-    ms, kt = timed_steps(step, steps, warmup)
+    ms, kt = timed_steps(step, steps, warmup, reps)
     kv, qb, table = decode_bytes(c)
     step_bytes = kv + 2 * qb + table
     dec_ms = kt.mean_ms("decode")
@@ -316,8 +325,8 @@ def bench_decode_append(c, name, steps, warmup, reps):
                                                    window_left=c.window_left, max_seqlen_k=msk,
                                                    out=out, workspace=ws))
 
-    ms, kt = timed_steps(fused, steps, warmup, launches_per_step=1)
-    ms_u, kt_u = timed_steps(unfused, steps, warmup)
+    ms, kt = timed_steps(fused, steps, warmup, reps)
+    ms_u, kt_u = timed_steps(unfused, steps, warmup, reps)
     kv, qb, table = decode_bytes(c)          # K/V of the L + 1 attended keys, q, table
     new_rows = B * c.Hkv * D * 2 * 2         # the new K/V rows, written into the cache
     step_bytes = kv + 2 * qb + table + new_rows
@@ -422,7 +431,7 @@ def bench_prefill(c, name, steps, warmup, reps, with_cache_write=False, traffic_
                 qs[r], cq, ck, c.max_seqlen_q, c.max_seqlen_k, c.sm_scale, c.Hkv, k=ks[r],
                 v=vs[r], sink=sink, window_left=c.window_left, out=out, alibi_slopes=al, **rkw))
 
-    ms, kt = timed_steps(step, steps, warmup)
+    ms, kt = timed_steps(step, steps, warmup, reps)
     pairs = visible_pairs(c.q_lens, c.k_lens, c.window_left)
     flops = 4 * c.D * c.Hq * pairs
     pre_ms = kt.mean_ms("prefill")
@@ -514,7 +523,7 @@ def bench_sparse(steps, warmup):
                                                     v=v, out=out))
 
     ms, kt = timed_steps(step, steps, warmup)
-    _, ktd = timed_steps(dense, steps, warmup, launches_per_step=1)
+    _, ktd = timed_steps(dense, steps, warmup)
     host = [t.cpu().numpy() for t in lists]
     pairs, _ = sparse_pairs(host, L)
     flops = 4 * D * pairs

@@ -141,8 +141,15 @@ __global__ __launch_bounds__(64 * kSparseWaves, 2) void sparse_prefill_kernel(Sp
     const int lr = lane & 31;                    // row within the wave / column of the MFMA
     const int lh = lane >> 5;                    // lane half
 
+    // Consecutive workgroups go to the eight XCDs in turn.  Position p among
+    // the Hq workgroups of one (request, row block) takes kv head p % Hkv
+    // and its query head p / Hkv within the group, so the query heads of a
+    // kv head, and its successive row blocks, land on the same XCD and share
+    // that XCD's L2 (whenever Hkv divides 8 or 8 divides Hkv, and Hq is a
+    // multiple of 8).
     int id = blockIdx.x;
-    const int h = id % a.Hq;
+    const int p = id % a.Hq;
+    const int h = (p % a.Hkv) * a.G + p / a.Hkv;
     id /= a.Hq;
     const int m = a.NM - 1 - id % a.NM;          // the longest row blocks first
     const int b = id / a.NM;

@@ -79,7 +79,41 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
-lib = load_library()
+# Entry points that enqueue GPU work (prepare() records these instead of
+# running them).
+_LAUNCHES = {
+    "pkv_reshape_and_cache", "pkv_reshape_and_cache_rope", "pkv_rope_apply", "pkv_rope_cos_sin",
+    "pkv_paged_decode", "pkv_paged_decode_noalloc", "pkv_paged_decode_append",
+    "pkv_paged_decode_stage", "pkv_paged_decode_finish", "pkv_paged_decode_partitions",
+    "pkv_merge_partitions", "pkv_varlen_prefill", "pkv_vertical_slash_blocks",
+    "pkv_sparse_prefill",
+}
+_recording = None          # while prepare() runs: [(function, args, name)], and the tensors kept
+_keep = None
+
+
+class _Library:
+    """The loaded library.  Attribute access gives its functions; while
+    prepare() records a call, the launching ones are noted with their
+    marshalled arguments instead of being run."""
+
+    def __init__(self, cdll):
+        self._cdll = cdll
+
+    def __getattr__(self, name):
+        fn = getattr(self._cdll, name)
+        if name in _LAUNCHES:
+            def call(*args, _fn=fn, _name=name):
+                if _recording is not None:
+                    _recording.append((_fn, args, _name))
+                    return PKV_OK
+                return _fn(*args)
+            fn = call
+        setattr(self, name, fn)
+        return fn
+
+
+lib = _Library(load_library())
 
 
 class PkvError(RuntimeError):
@@ -109,6 +143,8 @@ def _dt(t: torch.Tensor, *same: Optional[torch.Tensor]) -> int:
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     if t is None:
         return None
+    if _keep is not None:
+        _keep.append(t)
     if not t.is_cuda:
         raise ValueError("tensors must be on the GPU")
     if not t.is_contiguous():
@@ -152,6 +188,15 @@ def _row_stride(t: torch.Tensor, name: str) -> int:
     return t.stride(0)
 
 
+def _raw_ptr(t: torch.Tensor) -> int:
+    """Address of a GPU tensor whose rows may be strided (checked by the caller)."""
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if _keep is not None:
+        _keep.append(t)
+    return t.data_ptr()
+
+
 def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
@@ -160,13 +205,37 @@ def version() -> int:
     return lib.pkv_version()
 
 
+def prepare(fn, *args, **kwargs):
+    """Run the binding call fn(*args, **kwargs) up to its library launches,
+    which are recorded rather than run, and return a callable that issues
+    those launches with the same marshalled arguments, skipping the Python
+    checks (for timing loops and tight serving loops).  Every tensor the
+    call passed to the library, including buffers it allocated, is kept
+    alive by the callable; the launches go to the stream that was current
+    when the call was prepared."""
+    global _recording, _keep
+    rec, keep = [], []
+    _recording, _keep = rec, keep
+    try:
+        result = fn(*args, **kwargs)
+    finally:
+        _recording, _keep = None, None
+
+    def run(_rec=rec, _keep_alive=(keep, result)):
+        for f, a, name in _rec:
+            status = f(*a)
+            if status != PKV_OK:
+                raise PkvError(status, name)
+    return run
+
+
 def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping):
     """Store rows key/value [T, Hkv, D] into the caches at slot_mapping [T]."""
     T, Hkv, D = key.shape
     NB, bs = k_cache.shape[0], k_cache.shape[1]
     ks, vs = _row_stride(key, "key"), _row_stride(value, "value")
     _check(lib.pkv_reshape_and_cache(
-        key.data_ptr(), value.data_ptr(), _ptr(k_cache), _ptr(v_cache),
+        _raw_ptr(key), _raw_ptr(value), _ptr(k_cache), _ptr(v_cache),
         _ptr(_i32(slot_mapping, "slot_mapping")), T, ks, vs, Hkv, D, bs, NB,
         _dt(key, value, k_cache, v_cache), _stream()), "reshape_and_cache")
 
@@ -187,7 +256,7 @@ def rope_apply(x, positions, cos_sin, rotary_dim: int, neox: bool = True):
     _rope_table(cos_sin, rotary_dim)
     T, H, D = x.shape
     xs = _row_stride(x, "x")
-    _check(lib.pkv_rope_apply(x.data_ptr(), _ptr(_i32(positions, "positions")),
+    _check(lib.pkv_rope_apply(_raw_ptr(x), _ptr(_i32(positions, "positions")),
                               _ptr(cos_sin), T, H, D, xs, rotary_dim,
                               int(bool(neox)), _dt(x), _stream()), "rope_apply")
     return x
@@ -201,7 +270,7 @@ def reshape_and_cache_rope(key, value, k_cache, v_cache, slot_mapping, positions
     NB, bs = k_cache.shape[0], k_cache.shape[1]
     ks, vs = _row_stride(key, "key"), _row_stride(value, "value")
     _check(lib.pkv_reshape_and_cache_rope(
-        key.data_ptr(), value.data_ptr(), _ptr(k_cache), _ptr(v_cache),
+        _raw_ptr(key), _raw_ptr(value), _ptr(k_cache), _ptr(v_cache),
         _ptr(_i32(slot_mapping, "slot_mapping")), _ptr(_i32(positions, "positions")),
         _ptr(cos_sin), T, ks, vs, Hkv, D, bs, NB,
         rotary_dim, int(bool(neox)), _dt(key, value, k_cache, v_cache), _stream()),
@@ -224,9 +293,9 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: floa
                  alibi_slopes=None):
     """out [B,Hq,D] for q [B,Hq,D] over k/v_cache [NB,bs,Hkv,D].
 
-    A caller-provided `workspace` must have been zero-filled once (the library
-    leaves it zero after every call; see pkv_paged_decode); without one, a
-    zeroed buffer is allocated for this call."""
+    `workspace`: at least decode_workspace_bytes(...) bytes, reusable across
+    calls (see pkv_paged_decode); without one, a buffer is allocated for this
+    call."""
     B, Hq, D = q.shape
     NB, bs, Hkv, _ = k_cache.shape
     if max_seqlen_k is None:

@@ -380,3 +380,37 @@ def test_decode_large_batch(bs):
         out, lse = run_decode(c, partition_size=P)
         assert_close(out, o, torch.bfloat16, f"out P={P}")
         assert_close(lse, l, torch.bfloat16, f"lse P={P}", lse=True)
+
+
+def test_prepared_launches_match_direct_calls():
+    """pkv.prepare records a binding call's launches with their marshalled
+    arguments; running the prepared launcher (twice) gives bit for bit what
+    the direct call gives (decode through the balanced schedule, and a
+    varlen prefill)."""
+    from paged_kv_cache_02_amd import pkv
+    banner("prepared launches")
+    c = synth.decode_case(65, [5, 300, 1000, 2048], 32, 8, 128, 16, torch.bfloat16, True)
+    q, kc, vc, bt, sl = dev(c.q), dev(c.k_cache), dev(c.v_cache), dev(c.block_table), \
+        dev(c.cache_seqlens)
+    ws = torch.empty(pkv.decode_workspace_bytes(c.B, c.Hq, c.D, c.max_seqlen_k), dtype=torch.uint8,
+                     device="cuda")
+    want = pkv.paged_decode(q, kc, vc, bt, sl, c.sm_scale, sink=dev(c.sink), workspace=ws,
+                            max_seqlen_k=c.max_seqlen_k)
+    out = torch.full_like(want, float("nan"))
+    run = pkv.prepare(pkv.paged_decode, q, kc, vc, bt, sl, c.sm_scale, sink=dev(c.sink),
+                      workspace=ws, max_seqlen_k=c.max_seqlen_k, out=out)
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all(), "prepare must not launch"
+    for _ in range(2):
+        run()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16))
+    p = synth.prefill_case(66, [100, 333], [100, 333], 8, 2, 64, torch.bfloat16, True)
+    args = (dev(p.q), dev(p.cu_seqlens_q), dev(p.cu_seqlens_k), p.max_seqlen_q, p.max_seqlen_k,
+            p.sm_scale, p.Hkv)
+    kw = dict(k=dev(p.k), v=dev(p.v), sink=dev(p.sink))
+    want = pkv.varlen_prefill(*args, **kw)
+    out = torch.empty_like(want)
+    pkv.prepare(pkv.varlen_prefill, *args, out=out, **kw)()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), want.view(torch.int16))
