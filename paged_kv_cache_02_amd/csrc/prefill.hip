@@ -57,6 +57,8 @@ namespace pkv {
 namespace {
 
 constexpr float kTau = 8.0f;
+// tile buffers of the ring that runs of position blocks keep in LDS
+constexpr int kRunSlots = 4;
 // LDS operand reads are issued this many MFMAs ahead of their use (K for S,
 // V^T for P.V), to cover LDS latency with eight waves per CU reading (2 and 3
 // ahead left 15 % of the C3 time on the table; 6 and 7 gain nothing more)
@@ -563,42 +565,66 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
         }
     };
 
-    // Steps: with RUN, the next step's first K/V tile goes into the free
-    // buffer and its Q into qn during this step's last tile, so a step starts
-    // with both in place and the workgroup pays the load latency once.
+    // ---- epilogue: normalise with the sink, write the wave's rows ----
+    // The accumulators hold 4 dims of a row per lane, so a direct store would
+    // write 32 separate 16-byte pieces per instruction.  Instead each wave
+    // stages its rows in LDS and writes whole rows, 16 bytes per lane: all 32
+    // at once in the K/V buffers, which are free after the last barrier, or,
+    // with RUN, 16 at a time in a region of their own (the ring still holds
+    // tiles of the next step).  Staged rows are padded by 16 bytes so that
+    // consecutive rows start on different banks.
     constexpr int kRowPad = D * 2 + 16;
-    [[maybe_unused]] bf16x8 qn[RUN ? QK_STEPS : 1];
-    int buf = 0;
-    bool prefetched = false;
-    for (int s = 0; s < nsteps; ++s) {
-        if (s > 0) {
-            set_step(s);
-            if (row0 >= Lq) break;
-            if constexpr (RUN) {
+    constexpr int SR = RUN ? 16 : 32;               // rows staged per pass
+    auto epilogue = [&]() {
+        float lt = l + l1;
+        lt += shfl_xor(lt, 32);
+        const float Mt = fmaxf(lt > 0.f ? m : kNoMax, sig);
+        const float sc = fast_exp2(m - Mt);
+        const float Lt = lt * sc + fast_exp2(sig - Mt);
+        const float f = Lt > 0.f ? sc / Lt : 0.f;
+        static_assert(4 * 32 * kRowPad <= 2 * TL::BUF, "staging fits in the K/V buffers");
+        char *stage = lds + (RUN ? kRunSlots * TL::BUF : 0) + wave * SR * kRowPad;
+        constexpr int LPR = D / 8;      // lanes per row, 16 bytes each
+        constexpr int RPS = 64 / LPR;   // rows per store instruction
+        const int srow = lane / LPR, sunit = lane % LPR;
+        uint16_t *ob = (uint16_t *)a.out + (size_t)(cq0 + wrow0) * qstride + (size_t)h * D;
 #pragma unroll
-                for (int c = 0; c < QK_STEPS; ++c) qf[c] = qn[c];
+        for (int ps = 0; ps < 32 / SR; ++ps) {
+            // a wave's LDS accesses run in order: the reads of one pass are
+            // done before the next pass writes the same rows
+            if (lr >= SR * ps && lr < SR * (ps + 1)) {
+#pragma unroll
+                for (int t = 0; t < DT; ++t)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int d = 32 * t + 8 * q4 + 4 * lh;
+                        const u32x2 w = {pack_bf16x2(o[t][4 * q4] * f, o[t][4 * q4 + 1] * f),
+                                         pack_bf16x2(o[t][4 * q4 + 2] * f, o[t][4 * q4 + 3] * f)};
+                        *reinterpret_cast<u32x2 *>(stage + (lr - SR * ps) * kRowPad + d * 2) = w;
+                    }
             }
 #pragma unroll
-            for (int t = 0; t < DT; ++t)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
-            m = kNoMax;
-            l = 0.f;
-            l1 = 0.f;
+            for (int k = 0; k < SR / RPS; ++k) {
+                const int row = srow + RPS * k;
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * kRowPad + sunit * 16);
+                if (SR * ps + row < wrows)
+                    *reinterpret_cast<u32x4 *>(ob + (size_t)(SR * ps + row) * qstride + sunit * 8) = v;
+            }
         }
-        // the next step, if this workgroup has one with keys
-        int nx_lo = 0, nx_tb = 0, nx_nt = 0;
-        const int nx_row0 = row0 + bm;
-        const bool has_next = RUN && s + 1 < nsteps && nx_row0 < Lq;
-        if (has_next) block_keys(nx_row0, nx_lo, nx_tb, nx_nt);
+        if (a.lse && lh == 0 && lr < wrows)
+            a.lse[(size_t)(cq0 + wrow0 + lr) * a.Hq + h] = Lt > 0.f ? Mt * kLn2 + logf(Lt) : -INFINITY;
+    };
+
+    if constexpr (!RUN) {
+        // one block of positions: its tiles streamed through two buffers
+        int buf = 0;
         if (ntiles > 0) {
-            if (!prefetched) issue(t_begin, buf);
+            issue(t_begin, buf);
             if (a.rope) rotate_q();
             if constexpr (ROPEK) load_ktab(t_begin);
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             __syncthreads();
         }
-        prefetched = false;
         for (int it = 0; it < ntiles; ++it) {
             const int t0 = t_begin + it * BN;
             if constexpr (ROPEK) {
@@ -608,18 +634,7 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
                 rotate_k(buf, t0);
                 __syncthreads();
             }
-            if (it + 1 < ntiles) {
-                issue(t0 + BN, buf ^ 1);
-            } else if constexpr (RUN) {
-                if (has_next) {
-                    const int nw0 = nx_row0 + 32 * (wave / hpw);
-                    load_q(qn, nw0, max(0, min(32, Lq - nw0)));
-                    if (nx_nt > 0) {
-                        issue(nx_tb, buf ^ 1);
-                        prefetched = true;
-                    }
-                }
-            }
+            if (it + 1 < ntiles) issue(t0 + BN, buf ^ 1);
             if (wrows > 0 && t0 < w_hi && t0 + BN > w_lo) compute(buf, t0);
             // the next tile's table rows, in flight with its copies (loaded
             // after the tile's compute, so that they take no registers there)
@@ -630,60 +645,103 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
             __syncthreads();
             buf ^= 1;
         }
-        if constexpr (RUN) {
+        epilogue();
+    } else {
+        // Runs: the tiles live in a ring of kRunSlots buffers, tile n (keys
+        // [BN n, BN n + BN)) in slot n % kRunSlots.  The key ranges of
+        // consecutive steps overlap, so a tile that is still resident is not
+        // loaded again.  A step's tiles are taken in chunks of at most
+        // kRunSlots: the chunk's missing tiles are issued together (one wait
+        // for all of them), and while it is computed the next chunk's tiles
+        // (the rest of the step, or the next step's first ones) are copied
+        // into the slots it does not use, with the next step's Q.  Tiles
+        // [res_lo, res_hi) are resident (or in flight); they only move
+        // forward, so a tile is evicted only once no later chunk needs it.
+        bf16x8 qn[QK_STEPS];
+        int res_lo = 0, res_hi = 0;
+        [[maybe_unused]] int rot_hi = 0;        // ROPEK: resident tiles below it are rotated
+        auto load_tile = [&](int tn) { issue(tn * BN, tn % kRunSlots); };
+        for (int s = 0; s < nsteps; ++s) {
+            if (s > 0) {
+                set_step(s);
+                if (row0 >= Lq) break;
+#pragma unroll
+                for (int c = 0; c < QK_STEPS; ++c) qf[c] = qn[c];
+#pragma unroll
+                for (int t = 0; t < DT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
+                m = kNoMax;
+                l = 0.f;
+                l1 = 0.f;
+            }
+            // the next step, if this workgroup has one
+            int nx_lo = 0, nx_tb = 0, nx_nt = 0;
+            const int nx_row0 = row0 + bm;
+            const bool has_next = s + 1 < nsteps && nx_row0 < Lq;
+            if (has_next) block_keys(nx_row0, nx_lo, nx_tb, nx_nt);
+            const int nx_w0 = nx_row0 + 32 * (wave / hpw);
+            const int tb0 = t_begin / BN, tb1 = tb0 + ntiles;
+            for (int c0 = tb0; c0 < tb1; c0 += kRunSlots) {
+                const int c1 = min(tb1, c0 + kRunSlots);
+                // the chunk's missing tiles (the barrier that ended the last
+                // chunk has passed: no wave still reads a slot refilled here)
+                if (c0 < res_lo || c0 > res_hi) {
+                    res_lo = res_hi = c0;
+                    if constexpr (ROPEK) rot_hi = c0;
+                }
+                while (res_hi < c1) load_tile(res_hi++);
+                res_lo = max(res_lo, res_hi - kRunSlots);
+                if (c0 == tb0 && a.rope) rotate_q();
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                __syncthreads();
+                if constexpr (ROPEK) {
+                    // landed tiles rotated once, before any wave reads them
+                    if (rot_hi < c1) {
+                        for (int tn = max(rot_hi, c0); tn < c1; ++tn) {
+                            load_ktab(tn * BN);
+                            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                            rotate_k(tn % kRunSlots, tn * BN);
+                        }
+                        rot_hi = c1;
+                        __syncthreads();
+                    }
+                }
+                // the next chunk: the rest of this step, or the next step's first
+                int n0 = 0, n1 = 0;
+                if (c1 < tb1) {
+                    n0 = c1;
+                    n1 = min(tb1, c1 + kRunSlots);
+                } else if (has_next && nx_nt > 0) {
+                    n0 = nx_tb / BN;
+                    n1 = n0 + min(nx_nt, kRunSlots);
+                }
+                // its tiles that continue the resident range, into slots this
+                // chunk does not read (tile n evicts tile n - kRunSlots < c0)
+                if (n1 > n0 && n0 <= res_hi && n0 >= res_lo) {
+                    while (res_hi < n1 && res_hi < c0 + kRunSlots) load_tile(res_hi++);
+                    res_lo = max(res_lo, res_hi - kRunSlots);
+                }
+                if (c1 == tb1 && has_next) load_q(qn, nx_w0, max(0, min(32, Lq - nx_w0)));
+                for (int tn = c0; tn < c1; ++tn) {
+                    const int t0 = tn * BN;
+                    if (wrows > 0 && t0 < w_hi && t0 + BN > w_lo) compute(tn % kRunSlots, t0);
+                }
+                __syncthreads();
+            }
             // no tile in this step: the next step's Q still has to arrive
-            if (ntiles == 0 && has_next) {
-                const int nw0 = nx_row0 + 32 * (wave / hpw);
-                load_q(qn, nw0, max(0, min(32, Lq - nw0)));
-            }
+            if (ntiles == 0 && has_next) load_q(qn, nx_w0, max(0, min(32, Lq - nx_w0)));
+            epilogue();
         }
-    // ---- epilogue: normalise with the sink, write the wave's rows ----
-    // The accumulators hold 4 dims of a row per lane, so a direct store would
-    // write 32 separate 16-byte pieces per instruction.  Instead each wave
-    // stages its 32 rows in LDS (the K/V buffers are free after the last
-    // barrier; with RUN a region of its own, since the next step's first
-    // tile is already in a K/V buffer) and writes whole rows, 16 bytes per
-    // lane.  Staged rows are padded by 16 bytes so that consecutive rows start
-    // on different banks.
-    {
-        float lt = l + l1;
-        lt += shfl_xor(lt, 32);
-        const float Mt = fmaxf(lt > 0.f ? m : kNoMax, sig);
-        const float sc = fast_exp2(m - Mt);
-        const float Lt = lt * sc + fast_exp2(sig - Mt);
-        const float f = Lt > 0.f ? sc / Lt : 0.f;
-        static_assert(4 * 32 * kRowPad <= 2 * TL::BUF, "staging fits in the K/V buffers");
-        char *stage = lds + (RUN ? 2 * TL::BUF : 0) + wave * 32 * kRowPad;
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = 32 * t + 8 * q4 + 4 * lh;
-                const u32x2 w = {pack_bf16x2(o[t][4 * q4] * f, o[t][4 * q4 + 1] * f),
-                                 pack_bf16x2(o[t][4 * q4 + 2] * f, o[t][4 * q4 + 3] * f)};
-                *reinterpret_cast<u32x2 *>(stage + lr * kRowPad + d * 2) = w;
-            }
-        constexpr int LPR = D / 8;      // lanes per row, 16 bytes each
-        constexpr int RPS = 64 / LPR;   // rows per store instruction
-        const int srow = lane / LPR, sunit = lane % LPR;
-        uint16_t *ob = (uint16_t *)a.out + (size_t)(cq0 + wrow0) * qstride + (size_t)h * D;
-#pragma unroll
-        for (int k = 0; k < 32 / RPS; ++k) {
-            const int row = srow + RPS * k;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * kRowPad + sunit * 16);
-            if (row < wrows) *reinterpret_cast<u32x4 *>(ob + (size_t)row * qstride + sunit * 8) = v;
-        }
-        if (a.lse && lh == 0 && lr < wrows)
-            a.lse[(size_t)(cq0 + wrow0 + lr) * a.Hq + h] = Lt > 0.f ? Mt * kLn2 + logf(Lt) : -INFINITY;
     }
-    }   // steps
 }
 
 }  // namespace
 
 template <int D>
 constexpr int prefill_lds_bytes(bool run) {
-    return 2 * Tile<D>::BUF + (run ? 4 * 32 * (D * 2 + 16) : 0);
+    // runs: the tile ring and 16 staged rows per wave
+    return run ? kRunSlots * Tile<D>::BUF + 4 * 16 * (D * 2 + 16) : 2 * Tile<D>::BUF;
 }
 
 pkv_status launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream)
