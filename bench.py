@@ -372,16 +372,22 @@ def rope_setup(c, rotary_dim=128, neox=True):
 
 
 def bench_prefill(c, name, steps, warmup, reps, with_cache_write=False, traffic_key=None,
-                  alibi=None, rope=None, rope_unfused=False, rope_k=False):
+                  alibi=None, rope=None, rope_unfused=False, rope_k=False, keys_in_kernel=False):
     """rope: from rope_setup; q is then rotated inside the prefill (and K by
     reshape_and_cache_rope when with_cache_write), or, with rope_unfused, by a
     separate rope_apply launch before a plain prefill.  rope_k: the
-    contiguous keys are rotated too, inside the prefill (or, unfused, by a
-    rope_apply launch of their own)."""
+    contiguous keys are rotated too in the same call, once into a workspace
+    (or, keys_in_kernel, inside the attention kernel as it loads them; or,
+    unfused, by a rope_apply launch of their own)."""
     T = c.q.shape[0]
     fused = rope is not None and not rope_unfused
     rkw = dict(rope_cos_sin=rope["tab"], rotary_dim=rope["rd"], rope_neox=rope["neox"],
                rope_k=rope_k) if fused else {}
+    if fused and rope_k:
+        need = pkv.varlen_prefill_workspace_bytes(len(c.q_lens), c.max_seqlen_k, c.Hkv, c.D,
+                                                  True, c.q.dtype)
+        rkw["workspace"] = False if keys_in_kernel else \
+            torch.empty(need, dtype=torch.uint8, device="cuda")
     qs = [c.q.cuda() for _ in range(reps)]
     cq, ck = c.cu_seqlens_q.cuda(), c.cu_seqlens_k.cuda()
     al = None if alibi is None else alibi.cuda()
@@ -714,12 +720,18 @@ def main():
                                rope=rp, rope_k=True)
         r3ku, _ = bench_prefill(c3, "varlen_prefill_8x_U256-4096_rope_qk_unfused", steps, warmup,
                                 reps=2, rope=rp, rope_unfused=True, rope_k=True)
-        r3k["unfused_prefill_plus_rope_apply_ms"] = r3ku["prefill_plus_rope_apply_ms"]
-        r3k["speedup_vs_unfused"] = round(r3ku["prefill_plus_rope_apply_ms"] /
-                                          r3k["kernels_ms"]["prefill"], 3)
+        r3kk, _ = bench_prefill(c3, "varlen_prefill_8x_U256-4096_rope_qk_keys_in_kernel", steps,
+                                warmup, reps=2, rope=rp, rope_k=True, keys_in_kernel=True)
+        for r in (r3k, r3kk):
+            r["unfused_prefill_plus_rope_apply_ms"] = r3ku["prefill_plus_rope_apply_ms"]
+            r["speedup_vs_unfused"] = round(r3ku["prefill_plus_rope_apply_ms"] /
+                                            r["kernels_ms"]["prefill"], 3)
         workloads["varlen_prefill_rope_qk"] = r3k
-        log(f"prefill with q and k rotated in the kernel: {r3k['value']} TFLOP/s, "
-            f"{r3k['speedup_vs_unfused']}x rope_apply (q, k) + prefill")
+        workloads["varlen_prefill_rope_qk_keys_in_kernel"] = r3kk
+        log(f"prefill with q and k rotated in the call (keys once into a workspace): "
+            f"{r3k['value']} TFLOP/s, {r3k['speedup_vs_unfused']}x rope_apply (q, k) + prefill; "
+            f"keys rotated inside the attention kernel: {r3kk['value']} TFLOP/s, "
+            f"{r3kk['speedup_vs_unfused']}x")
     if ARGS.only in ("all", "chunked"):
         log("chunked prefill workload (4 x 512 q on 8704 paged keys, window 128, 64/8, D 64)")
         c4 = synth.config4_chunked(poison=False, spare_blocks=0)

@@ -455,13 +455,27 @@ pkv_status pkv_merge_partitions(void *out, float *lse, const float *part_out,
  *   rope_k          0: the keys are already rotated (for example stored with
  *                   pkv_reshape_and_cache_rope; always so for paged keys).
  *                   1 (contiguous K and a table only): key j is rotated by
- *                   its position j as it is loaded (vLLM page,
+ *                   its position j before attention (vLLM page,
  *                   PagedAttentionWithRoPE.forward rotates query and key
  *                   before attention); k itself is not modified.  The
  *                   rotated keys are rounded to bf16 as pkv_rope_apply
- *                   would store them.  Other values: PKV_ERR_SHAPE; 1 with
- *                   paged keys, without a table or with ALiBi slopes (two
- *                   position encodings at once): PKV_ERR_UNSUPPORTED.
+ *                   would store them.  bfloat16 with a workspace: the keys
+ *                   are rotated once into it by a first launch and attended
+ *                   from there; without one, each workgroup of the attention
+ *                   kernel rotates the key tiles it loads, in LDS (no
+ *                   workspace, but every tile is rotated once per workgroup
+ *                   that reads it, which costs more on long requests).
+ *                   Other values: PKV_ERR_SHAPE; 1 with paged keys or
+ *                   without a table: PKV_ERR_UNSUPPORTED; 1 with ALiBi
+ *                   slopes is supported only through the workspace (else
+ *                   PKV_ERR_UNSUPPORTED).
+ *   workspace,      NULL / 0, or device memory (16-byte aligned) of at least
+ *   workspace_bytes pkv_varlen_prefill_workspace_bytes(B, max_seqlen_k,
+ *                   num_kv_heads, head_dim, rope_k, dtype) bytes, owned by
+ *                   the caller, used only for bfloat16 with rope_k = 1 (the
+ *                   rotated keys, [sum Lk, num_kv_heads, head_dim]); its
+ *                   contents need no initialisation and are scratch after
+ *                   the call.  Too small: PKV_ERR_WORKSPACE.
  *
  * Errors besides the common ones: PKV_ERR_UNSUPPORTED for bfloat16 with
  * contiguous K/V when max_seqlen_k * num_kv_heads * head_dim * 2 bytes (one
@@ -476,7 +490,17 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
                               int32_t causal, int32_t window_left, const float *alibi_slopes,
                               const float *rope_cos_sin, int32_t rope_positions,
                               int32_t rotary_dim, int32_t rope_neox, int32_t rope_k,
-                              const float *sink, pkv_dtype dtype, void *stream);
+                              const float *sink, void *workspace, size_t workspace_bytes,
+                              pkv_dtype dtype, void *stream);
+
+/*
+ * pkv_varlen_prefill_workspace_bytes -- the workspace pkv_varlen_prefill
+ * needs to rotate contiguous keys once (bfloat16, rope_k = 1): room for
+ * B * max_seqlen_k key rows, rounded up to 256 bytes; 0 for any other call.
+ * (size_t)-1 for a negative B or max_seqlen_k, or no heads.
+ */
+size_t pkv_varlen_prefill_workspace_bytes(int32_t B, int32_t max_seqlen_k, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t rope_k, pkv_dtype dtype);
 
 /*
  * Vertical + slash sparse prefill (nano-vllm "minference.py" page,

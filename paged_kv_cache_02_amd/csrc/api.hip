@@ -595,6 +595,14 @@ pkv_status pkv_merge_partitions(void *out, float *lse, const float *part_out,
     return launch_merge(m, (hipStream_t)stream);
 }
 
+size_t pkv_varlen_prefill_workspace_bytes(int32_t B, int32_t max_seqlen_k, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t rope_k, pkv_dtype dtype)
+{
+    if (B < 0 || max_seqlen_k < 0 || num_kv_heads <= 0 || head_dim <= 0) return (size_t)-1;
+    if (!rope_k || dtype != PKV_BF16) return 0;
+    return align256((size_t)B * max_seqlen_k * num_kv_heads * head_dim * 2);
+}
+
 pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *k, const void *v,
                               const void *k_cache, const void *v_cache,
                               const int32_t *block_table, int32_t block_size, int32_t num_blocks,
@@ -605,7 +613,8 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
                               int32_t window_left, const float *alibi_slopes,
                               const float *rope_cos_sin, int32_t rope_positions,
                               int32_t rotary_dim, int32_t rope_neox, int32_t rope_k,
-                              const float *sink, pkv_dtype dtype, void *stream)
+                              const float *sink, void *workspace, size_t workspace_bytes,
+                              pkv_dtype dtype, void *stream)
 {
     if (B < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return PKV_ERR_SHAPE;
     pkv_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
@@ -626,7 +635,17 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
     // rotating K as it is loaded: a table, and contiguous keys (cached keys
     // are rotated when they are stored)
     if (rope_k != 0 && rope_k != 1) return PKV_ERR_SHAPE;
-    if (rope_k && (!rope_cos_sin || paged || alibi_slopes)) return PKV_ERR_UNSUPPORTED;
+    if (rope_k && (!rope_cos_sin || paged)) return PKV_ERR_UNSUPPORTED;
+    // bf16 keys rotated once into the workspace, or else inside the attention
+    // kernels (which have no variant with ALiBi slopes as well)
+    const bool keys_copied = rope_k && dtype == PKV_BF16 && workspace != nullptr;
+    if (rope_k && !keys_copied && alibi_slopes) return PKV_ERR_UNSUPPORTED;
+    if (keys_copied) {
+        const size_t need = pkv_varlen_prefill_workspace_bytes(B, max_seqlen_k, num_kv_heads,
+                                                               head_dim, rope_k, dtype);
+        if (workspace_bytes < need) return PKV_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return PKV_ERR_UNSUPPORTED;
+    }
     if (paged) {
         if ((st = check_block_size(block_size)) != PKV_OK) return st;
         if (num_blocks < 0 || max_blocks_per_seq < 0) return PKV_ERR_SHAPE;
@@ -648,6 +667,15 @@ pkv_status pkv_varlen_prefill(void *out, float *lse, const void *q, const void *
         // contiguous K/V are read through one 32-bit-ranged buffer per request
         if (contiguous && (unsigned long long)max_seqlen_k * num_kv_heads * head_dim * 2 >= (1ull << 32))
             return PKV_ERR_UNSUPPORTED;
+        if (keys_copied) {
+            // the keys rotated by their positions into the workspace (same
+            // rows), then attended from there as keys already rotated
+            if ((st = launch_rope_keys(k, workspace, cu_seqlens_k, rope_cos_sin, B, max_seqlen_k,
+                                       num_kv_heads, head_dim, rotary_dim, rope_neox, s)) != PKV_OK)
+                return st;
+            k = workspace;
+            rope_k = 0;
+        }
         PrefillArgs a{};
         a.out = out; a.lse = lse; a.q = q; a.k = k; a.v = v; a.k_cache = k_cache;
         a.v_cache = v_cache; a.block_table = block_table; a.cu_q = cu_seqlens_q;

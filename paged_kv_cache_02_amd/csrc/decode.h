@@ -291,6 +291,10 @@ pkv_status launch_rope_table(float *cos_sin, int n_pos, int rd, double base, int
 pkv_status launch_rope_apply(void *x, const int32_t *positions, const float *cos_sin, int T,
                              int H, int D, long long row_stride, int rd, int neox, bool bf16,
                              hipStream_t stream);
+// bf16 keys of varlen requests rotated into dst (same rows), positions 0..L-1
+pkv_status launch_rope_keys(const void *k, void *dst, const int32_t *cu_k,
+                            const float *cos_sin, int B, int max_len, int H, int D, int rd,
+                            int neox, hipStream_t stream);
 pkv_status launch_rope_cache(const void *key, const void *value, void *k_cache, void *v_cache,
                              const int32_t *slot_mapping, const int32_t *positions,
                              const float *cos_sin, int T, long long key_stride,

@@ -59,6 +59,30 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(char *x, const int32_t 
     rope_chunk<BF16>(row, row, cos_sin + (size_t)positions[t] * rd, rd, neox != 0, u);
 }
 
+// The contiguous keys of varlen requests rotated by their positions into a
+// copy: row cu_k[r] + j of k (position j of request r) goes to the same row
+// of dst.  One thread per 16-byte chunk of one (request, position, kv head)
+// row, positions up to max_len; rows past a request's keys do nothing.
+__global__ __launch_bounds__(256) void rope_keys_kernel(const char *k, char *dst,
+                                                        const int32_t *cu_k,
+                                                        const float *cos_sin, int B, int max_len,
+                                                        int H, int D, int rd, int neox)
+{
+    const int cpr = D / 8;                         // chunks per head row
+    long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    const int u = (int)(idx % cpr);
+    idx /= cpr;
+    const int h = (int)(idx % H);
+    idx /= H;
+    const int j = (int)(idx % max_len);
+    const long long r = idx / max_len;
+    if (r >= B) return;
+    const int c0 = cu_k[r];
+    if (j >= cu_k[r + 1] - c0) return;
+    const size_t row = ((size_t)(c0 + j) * H + h) * D * 2;
+    rope_chunk<true>(k + row, dst + row, cos_sin + (size_t)j * rd, rd, neox != 0, u);
+}
+
 // reshape_and_cache with the key rotated: one thread per 16-byte chunk of a
 // token's K row (all kv heads) and of its V row.
 template <bool BF16>
@@ -115,6 +139,19 @@ pkv_status launch_rope_apply(void *x, const int32_t *positions, const float *cos
     else
         hipLaunchKernelGGL(rope_apply_kernel<false>, dim3(grid), dim3(256), 0, stream, (char *)x,
                            positions, cos_sin, T, H, D, stride_bytes, rd, neox);
+    return launch_status();
+}
+
+pkv_status launch_rope_keys(const void *k, void *dst, const int32_t *cu_k,
+                            const float *cos_sin, int B, int max_len, int H, int D, int rd,
+                            int neox, hipStream_t stream)
+{
+    const long long n = (long long)B * max_len * H * (D / 8);
+    if (n == 0) return PKV_OK;
+    const long long grid = (n + 255) / 256;
+    if (grid > 0x7fffffffLL) return PKV_ERR_SHAPE;
+    hipLaunchKernelGGL(rope_keys_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const char *)k, (char *)dst, cu_k, cos_sin, B, max_len, H, D, rd, neox);
     return launch_status();
 }
 

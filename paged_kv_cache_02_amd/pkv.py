@@ -63,8 +63,10 @@ SIGNATURES = {
                                           _I32, _I32, _I32, _I32, _F, _P, ctypes.c_int, _P]),
     "pkv_varlen_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P,
                                           _P, _I32, _I32, _I32, _I32, _I32, _I32, _F, _I32,
-                                          _I32, _P, _P, _I32, _I32, _I32, _I32, _P, ctypes.c_int,
-                                          _P]),
+                                          _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ,
+                                          ctypes.c_int, _P]),
+    "pkv_varlen_prefill_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32,
+                                                             ctypes.c_int]),
 }
 
 
@@ -440,11 +442,14 @@ def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_
                    k_cache=None, v_cache=None, block_table=None, sink=None,
                    window_left: int = -1, out=None, lse=None, alibi_slopes=None,
                    rope_cos_sin=None, rotary_dim: int = 0, rope_neox: bool = True,
-                   causal: bool = True, rope_k: bool = False):
+                   causal: bool = True, rope_k: bool = False, workspace=None):
     """Varlen prefill: out [sum Lq, Hq, D].  causal=False lets every query
     row see every key of its request (a window still bounds the left side).
     With rope_cos_sin, q is rotated by its position; rope_k=True rotates the
-    contiguous keys by theirs too (k is not modified)."""
+    contiguous keys by theirs too (k is not modified).  bfloat16 rope_k
+    rotates the keys once into `workspace` (at least
+    varlen_prefill_workspace_bytes(...) bytes; allocated when None), or,
+    with workspace=False, inside the attention kernel."""
     if rope_cos_sin is not None:
         _rope_table(rope_cos_sin, rotary_dim)
     T, Hq, D = q.shape
@@ -459,6 +464,13 @@ def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_
         raise ValueError("num_kv_heads does not match the K/V tensors")
     if out is None:
         out = torch.empty_like(q)
+    dt = _dt(q, k, v, k_cache, v_cache, out)
+    if workspace is False:
+        workspace = None
+    elif workspace is None and rope_k:
+        need = varlen_prefill_workspace_bytes(B, max_seqlen_k, Hkv, D, rope_k, q.dtype)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     _check(lib.pkv_varlen_prefill(
         _ptr(out), _ptr(_f32(lse, "lse")), _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache),
         _ptr(v_cache), _ptr(None if block_table is None else _i32(block_table, "block_table")),
@@ -467,9 +479,22 @@ def varlen_prefill(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_
         Hkv, D, float(sm_scale), int(bool(causal)), window_left, _ptr(_f32(alibi_slopes, "alibi_slopes")),
         _ptr(rope_cos_sin),
         0 if rope_cos_sin is None else rope_cos_sin.shape[0], rotary_dim, int(bool(rope_neox)),
-        int(bool(rope_k)), _ptr(_f32(sink, "sink")), _dt(q, k, v, k_cache, v_cache, out),
+        int(bool(rope_k)), _ptr(_f32(sink, "sink")), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), dt,
         _stream()), "varlen_prefill")
     return out
+
+
+def varlen_prefill_workspace_bytes(B: int, max_seqlen_k: int, num_kv_heads: int, head_dim: int,
+                                   rope_k: bool, dtype: torch.dtype) -> int:
+    """Workspace bytes varlen_prefill needs to rotate the keys once (see
+    pkv_varlen_prefill_workspace_bytes); 0 when it needs none."""
+    code = PKV_BF16 if dtype == torch.bfloat16 else PKV_F32
+    n = lib.pkv_varlen_prefill_workspace_bytes(int(B), int(max_seqlen_k), int(num_kv_heads),
+                                               int(head_dim), int(bool(rope_k)), code)
+    if n == ctypes.c_size_t(-1).value:
+        raise PkvError(PKV_ERR_SHAPE, "varlen_prefill_workspace_bytes")
+    return int(n)
 
 
 SPARSE_BLOCK = 64

@@ -142,7 +142,7 @@ def prefill_call(**over):
     a = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, k_cache=None, v_cache=None, bt=None,
              bs=0, NB=0, MB=0, cu_q=FAKE, cu_k=FAKE, B=2, maxq=16, maxk=16, Hq=8, Hkv=2, D=64,
              scale=0.1, causal=1, window=-1, alibi=None, rope=None, rope_pos=0, rope_dim=0,
-             rope_neox=1, rope_k=0, sink=None, dt=1, stream=None)
+             rope_neox=1, rope_k=0, sink=None, ws=None, ws_bytes=0, dt=1, stream=None)
     a.update(over)
     return lib.pkv_varlen_prefill(*a.values())
 
@@ -166,6 +166,13 @@ def prefill_call(**over):
           v_cache=FAKE, bt=FAKE, bs=16, NB=4, MB=4), pkv.PKV_ERR_UNSUPPORTED),  # paged keys
     (dict(rope_k=1, rope=FAKE, rope_pos=16, rope_dim=64, B=0), pkv.PKV_OK),
     (dict(rope_k=1, rope=FAKE, rope_pos=16, rope_dim=64, alibi=FAKE), pkv.PKV_ERR_UNSUPPORTED),
+    # keys rotated once into a workspace: too small, misaligned; ALiBi allowed there
+    (dict(rope_k=1, rope=FAKE, rope_pos=16, rope_dim=64, ws=FAKE, ws_bytes=8191),
+     pkv.PKV_ERR_WORKSPACE),
+    (dict(rope_k=1, rope=FAKE, rope_pos=16, rope_dim=64, ws=FAKE + 8, ws_bytes=1 << 20),
+     pkv.PKV_ERR_UNSUPPORTED),
+    (dict(rope_k=1, rope=FAKE, rope_pos=16, rope_dim=64, alibi=FAKE, ws=FAKE, ws_bytes=1 << 20,
+          B=0), pkv.PKV_OK),
     (dict(Hkv=3), pkv.PKV_ERR_SHAPE),
     (dict(D=80), pkv.PKV_ERR_UNSUPPORTED),
     (dict(window=-5), pkv.PKV_ERR_SHAPE),
@@ -178,6 +185,19 @@ def prefill_call(**over):
 ])
 def test_prefill_validation(over, status):
     assert prefill_call(**over) == status
+
+
+def test_prefill_workspace_bytes():
+    f = lib.pkv_varlen_prefill_workspace_bytes
+    # B * max_seqlen_k key rows of num_kv_heads * head_dim bf16, to 256 bytes
+    assert f(2, 16, 2, 64, 1, pkv.PKV_BF16) == 2 * 16 * 2 * 64 * 2
+    assert f(3, 5, 1, 64, 1, pkv.PKV_BF16) == 2048          # 1920 rounded up
+    assert f(2, 16, 2, 64, 0, pkv.PKV_BF16) == 0            # keys not rotated
+    assert f(2, 16, 2, 64, 1, pkv.PKV_F32) == 0             # fp32 rotates in registers
+    assert f(0, 16, 2, 64, 1, pkv.PKV_BF16) == 0
+    assert f(-1, 16, 2, 64, 1, pkv.PKV_BF16) == ctypes.c_size_t(-1).value
+    assert pkv.varlen_prefill_workspace_bytes(8, 4096, 8, 128, True, pkv.torch.bfloat16) == \
+        8 * 4096 * 8 * 128 * 2
 
 
 @pytest.mark.parametrize("args,status", [

@@ -197,14 +197,19 @@ ROPE_K = [
 
 
 @pytest.mark.parametrize("case", ROPE_K, ids=[str(i) for i in range(len(ROPE_K))])
+@pytest.mark.parametrize("keys", ["workspace", "in_kernel"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_prefill_rope_k(case, dtype):
-    """rope_k: contiguous keys rotated by their positions as the prefill loads
-    them, q by its own; against the oracle fed q and k rotated with its own
-    table (k rounded to the storage type, as the kernel rounds it)."""
+def test_prefill_rope_k(case, keys, dtype):
+    """rope_k: contiguous keys rotated by their positions, q by its own;
+    bf16 rotates the keys once into a workspace (NaN-filled beforehand) or,
+    without one, inside the attention kernel as it loads them; against the
+    oracle fed q and k rotated with its own table (k rounded to the storage
+    type, as the kernels round it)."""
     from paged_kv_cache_02_amd import pkv
     q_lens, k_lens, Hq, Hkv, D, rd, neox, window, causal = case
-    banner(f"prefill rope_k {dtype} {case}")
+    if dtype == torch.float32 and keys == "in_kernel":
+        pytest.skip("float32 rotates the keys in registers, with or without a workspace")
+    banner(f"prefill rope_k {dtype} {keys} {case}")
     k_lens = k_lens or q_lens
     c = synth.prefill_case(560 + len(q_lens), q_lens, k_lens, Hq, Hkv, D, dtype, True,
                            window_left=window)
@@ -215,10 +220,15 @@ def test_prefill_rope_k(case, dtype):
     k_before = k0.clone()
     T = c.q.shape[0]
     lse = torch.empty(T, Hq, dtype=torch.float32, device="cuda")
+    ws = False
+    if keys == "workspace":
+        need = pkv.varlen_prefill_workspace_bytes(len(q_lens), c.max_seqlen_k, Hkv, D, True, dtype)
+        ws = torch.full((max(need, 1) // 2,), float("nan"), dtype=torch.bfloat16,
+                        device="cuda").view(torch.uint8) if need else None
     out = pkv.varlen_prefill(dev(c.q), dev(c.cu_seqlens_q), dev(c.cu_seqlens_k), c.max_seqlen_q,
                              c.max_seqlen_k, c.sm_scale, Hkv, k=k0, v=dev(c.v), sink=dev(c.sink),
                              lse=lse, window_left=window, causal=causal, rope_cos_sin=tab,
-                             rotary_dim=rd, rope_neox=neox, rope_k=True)
+                             rotary_dim=rd, rope_neox=neox, rope_k=True, workspace=ws)
     torch.cuda.synchronize()
     bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
     assert torch.equal(k0.view(bits), k_before.view(bits)), "k modified"
@@ -324,6 +334,37 @@ def test_prefill_rope_window_alibi(dtype):
     assert_close(lse, l, dtype, "prefill rope window alibi lse", lse=True)
 
 
+def test_prefill_rope_k_alibi_workspace():
+    """rope_k with ALiBi slopes and a window (bf16): the keys rotated once
+    into the workspace, then the ALiBi kernel; without a workspace the call
+    is refused (no in-kernel rotation variant carries ALiBi)."""
+    from paged_kv_cache_02_amd import pkv
+    banner("prefill rope_k + alibi + window, workspace")
+    dtype = torch.bfloat16
+    q_lens, k_lens, Hq, Hkv, D, rd, window = [70, 200], [400, 200], 16, 4, 128, 64, 50
+    c = synth.prefill_case(541, q_lens, k_lens, Hq, Hkv, D, dtype, True, window_left=window)
+    al = torch.tensor([2.0 ** (-8.0 * (h + 1) / Hq) for h in range(Hq)], dtype=torch.float32)
+    tab = pkv.rope_cos_sin(max(k_lens), rd)
+    otab = oracle.rope_cos_sin(max(k_lens), rd, 10000.0)
+    kpos = np.concatenate([np.arange(L) for L in k_lens]).astype(np.int32)
+    krot = synth.to_dtype(oracle.rope_apply(c.k, kpos, otab, rd, True).astype(np.float32), dtype)
+    lse = torch.empty(c.q.shape[0], Hq, dtype=torch.float32, device="cuda")
+    args = (dev(c.q), dev(c.cu_seqlens_q), dev(c.cu_seqlens_k), c.max_seqlen_q, c.max_seqlen_k,
+            c.sm_scale, Hkv)
+    kw = dict(k=dev(c.k), v=dev(c.v), sink=dev(c.sink), window_left=window, lse=lse,
+              alibi_slopes=dev(al), rope_cos_sin=tab, rotary_dim=rd, rope_k=True)
+    out = pkv.varlen_prefill(*args, **kw)
+    torch.cuda.synchronize()
+    qpos = oracle.query_positions(c.cu_seqlens_q, c.cu_seqlens_k)
+    qrot = torch.from_numpy(oracle.rope_apply(c.q, qpos, otab, rd, True)).float()
+    o, l = oracle.varlen_prefill(qrot, c.cu_seqlens_q, c.cu_seqlens_k, c.sink, c.sm_scale, Hkv,
+                                 k=krot.float(), v=c.v.float(), window_left=window, alibi=al)
+    assert_close(out, o, dtype, "prefill rope_k alibi out")
+    assert_close(lse, l, dtype, "prefill rope_k alibi lse", lse=True)
+    with pytest.raises(pkv.PkvError):
+        pkv.varlen_prefill(*args, **kw, workspace=False)
+
+
 def test_config3_rope_full_size():
     """The 8-request prefill workload (256..4096 tokens, 32/8 heads, D 128,
     sink) as the benchmark times it with RoPE (rotary_dim 128, neox): q
@@ -362,16 +403,18 @@ def test_config3_rope_full_size():
                                  k=krot.float(), v=c.v.float())
     assert_close(out, o, torch.bfloat16, "config3 rope out")
     assert_close(lse, l, torch.bfloat16, "config3 rope lse", lse=True)
-    # one launch: the unrotated keys rotated as the prefill loads them
-    out.fill_(float("nan"))
-    lse.fill_(float("nan"))
-    pkv.varlen_prefill(dev(c.q), dev(c.cu_seqlens_q), dev(c.cu_seqlens_k), c.max_seqlen_q,
-                       c.max_seqlen_k, c.sm_scale, c.Hkv, k=dev(c.k), v=dev(c.v),
-                       sink=dev(c.sink), lse=lse, out=out, rope_cos_sin=tab, rotary_dim=rd,
-                       rope_k=True)
-    torch.cuda.synchronize()
-    assert_close(out, o, torch.bfloat16, "config3 rope_k out")
-    assert_close(lse, l, torch.bfloat16, "config3 rope_k lse", lse=True)
+    # the unrotated keys rotated in the same call: once into a workspace, or
+    # inside the attention kernel as it loads them
+    for ws in (None, False):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        pkv.varlen_prefill(dev(c.q), dev(c.cu_seqlens_q), dev(c.cu_seqlens_k), c.max_seqlen_q,
+                           c.max_seqlen_k, c.sm_scale, c.Hkv, k=dev(c.k), v=dev(c.v),
+                           sink=dev(c.sink), lse=lse, out=out, rope_cos_sin=tab, rotary_dim=rd,
+                           rope_k=True, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(out, o, torch.bfloat16, f"config3 rope_k out (workspace {ws})")
+        assert_close(lse, l, torch.bfloat16, f"config3 rope_k lse (workspace {ws})", lse=True)
     s = slots.long()
     assert_close(kc.view(-1, c.Hkv, c.D)[s], krot.float().numpy(), torch.bfloat16,
                  "config3 rotated keys")

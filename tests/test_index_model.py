@@ -346,6 +346,51 @@ def test_prefill_mapping_in_bounds(window_override, causal):
     assert n > 0
 
 
+def model_rope_keys(k_lens, Hkv, D, max_len, rope_rows, ws_rows):
+    """rope_keys_kernel (csrc/rope.hip): thread -> (request r, position j,
+    kv head h, 16-byte chunk u) over B * max_len * Hkv * D/8 threads; a thread
+    with j < L_r reads key row cu[r] + j and table row j and writes the same
+    row of the workspace.  Every key row is covered once, and every row read
+    or written lies inside k, the table and the workspace."""
+    L = np.asarray(k_lens, dtype=np.int64)
+    B = L.size
+    cu = np.concatenate([[0], np.cumsum(L)])
+    cpr = D // 8
+    n = B * max_len * Hkv * cpr
+    grid = (n + 255) // 256
+    idx = np.arange(grid * 256, dtype=np.int64)
+    u = idx % cpr
+    rest = idx // cpr
+    h = rest % Hkv
+    rest //= Hkv
+    j = rest % max_len
+    r = rest // max_len
+    live = r < B
+    r, j, h, u = r[live], j[live], h[live], u[live]
+    act = j < L[r]
+    row = cu[r][act] + j[act]
+    assert (row < cu[-1]).all() and (row >= 0).all(), "key row outside k"
+    assert (row < ws_rows).all(), "row outside the workspace"
+    assert (j[act] < rope_rows).all(), "table row outside the table"
+    # each (row, head, chunk) exactly once
+    key = (row * Hkv + h[act]) * cpr + u[act]
+    assert np.unique(key).size == key.size == cu[-1] * Hkv * cpr
+    return int(act.sum())
+
+
+def test_rope_keys_mapping_in_bounds():
+    n = 0
+    for q_lens, k_lens, Hq, Hkv, D, window, bs in prefill_shapes():
+        if not k_lens:
+            continue
+        mx = max(k_lens)
+        # the workspace holds B * max_seqlen_k rows; the table max_seqlen_k rows
+        n += model_rope_keys(k_lens, Hkv, D, mx, rope_rows=mx, ws_rows=len(k_lens) * mx)
+    assert n > 0
+    with pytest.raises(AssertionError):     # a table one row short
+        model_rope_keys([5, 9], 2, 64, 9, rope_rows=8, ws_rows=18)
+
+
 def decode_shapes():
     Dm = _gpu_module("test_gpu_decode")
     shapes = []
