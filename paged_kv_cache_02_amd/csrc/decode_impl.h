@@ -779,8 +779,11 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(Stream
             if (base + lane < total) {
                 const int b = bp / a.max_parts, pp = bp % a.max_parts;
                 const size_t row = ((size_t)b * a.Hq + h0 + hh) * a.max_parts + pp;
-                *reinterpret_cast<f32x4 *>(a.part_out + row * D + 4 * c) =
-                    *reinterpret_cast<const f32x4 *>(s_stage[wave] + (i * HU + hh) * D + 4 * c);
+                // nontemporal: the rows are read once, by the merge kernel,
+                // and need not displace anything on their way out
+                __builtin_nontemporal_store(
+                    *reinterpret_cast<const f32x4 *>(s_stage[wave] + (i * HU + hh) * D + 4 * c),
+                    reinterpret_cast<f32x4 *>(a.part_out + row * D + 4 * c));
             }
         }
         {
