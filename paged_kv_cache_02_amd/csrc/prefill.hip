@@ -57,8 +57,12 @@ namespace pkv {
 namespace {
 
 constexpr float kTau = 8.0f;
-// tile buffers of the ring that runs of position blocks keep in LDS
-constexpr int kRunSlots = 4;
+// Runs of position blocks keep their key tiles in a ring of 4 LDS slots and
+// stage the output rows in passes of 16 (head_dim 64: 73 KB, two workgroups
+// per compute unit) or 8 rows per wave (head_dim 128: 137 KB, one workgroup,
+// whose registers also hold the next step's Q).
+template <int D> constexpr int run_slots() { return 4; }
+template <int D> constexpr int run_stage_rows() { return D == 128 ? 8 : 16; }
 // LDS operand reads are issued this many MFMAs ahead of their use (K for S,
 // V^T for P.V), to cover LDS latency with eight waves per CU reading (2 and 3
 // ahead left 15 % of the C3 time on the table; 6 and 7 gain nothing more)
@@ -145,17 +149,18 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
     const int ng = a.G / hpw;                       // head subgroups per kv head
     int g, hs, r, blk0, nsteps;                     // blk0: first block of bm positions
     if constexpr (RUN) {
-        // Runs (sliding-window prefill): workgroup (request, run u, head
-        // subgroup, kv head), kv head fastest so that the subgroups of a kv
-        // head share an XCD's L2; it walks the run_steps consecutive position
-        // blocks of run u, each step's key window overlapping the last one's
+        // Runs: workgroup (run u, request, head subgroup, kv head), kv head
+        // fastest so that the subgroups of a kv head share an XCD's L2, and
+        // the last runs of the requests first (the heaviest, when causal); it
+        // walks the run_steps consecutive position blocks of run u, each
+        // step's keys overlapping the last one's
         int id = blockIdx.x;
         g = id % a.Hkv;
         id /= a.Hkv;
         hs = id % ng;
         id /= ng;
-        const int u = id % a.runs;
-        r = id / a.runs;
+        r = id % a.B;
+        const int u = a.runs - 1 - id / a.B;
         blk0 = u * a.run_steps;
         nsteps = a.run_steps;
     } else {
@@ -574,7 +579,7 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
     // tiles of the next step).  Staged rows are padded by 16 bytes so that
     // consecutive rows start on different banks.
     constexpr int kRowPad = D * 2 + 16;
-    constexpr int SR = RUN ? 16 : 32;               // rows staged per pass
+    constexpr int SR = RUN ? run_stage_rows<D>() : 32;   // rows staged per pass
     auto epilogue = [&]() {
         float lt = l + l1;
         lt += shfl_xor(lt, 32);
@@ -583,7 +588,7 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
         const float Lt = lt * sc + fast_exp2(sig - Mt);
         const float f = Lt > 0.f ? sc / Lt : 0.f;
         static_assert(4 * 32 * kRowPad <= 2 * TL::BUF, "staging fits in the K/V buffers");
-        char *stage = lds + (RUN ? kRunSlots * TL::BUF : 0) + wave * SR * kRowPad;
+        char *stage = lds + (RUN ? run_slots<D>() * TL::BUF : 0) + wave * SR * kRowPad;
         constexpr int LPR = D / 8;      // lanes per row, 16 bytes each
         constexpr int RPS = 64 / LPR;   // rows per store instruction
         const int srow = lane / LPR, sunit = lane % LPR;
@@ -647,20 +652,23 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
         }
         epilogue();
     } else {
-        // Runs: the tiles live in a ring of kRunSlots buffers, tile n (keys
-        // [BN n, BN n + BN)) in slot n % kRunSlots.  The key ranges of
-        // consecutive steps overlap, so a tile that is still resident is not
-        // loaded again.  A step's tiles are taken in chunks of at most
-        // kRunSlots: the chunk's missing tiles are issued together (one wait
-        // for all of them), and while it is computed the next chunk's tiles
-        // (the rest of the step, or the next step's first ones) are copied
-        // into the slots it does not use, with the next step's Q.  Tiles
-        // [res_lo, res_hi) are resident (or in flight); they only move
-        // forward, so a tile is evicted only once no later chunk needs it.
+        // Runs: the tiles live in a ring of R slots, tile n (keys [BN n,
+        // BN n + BN)) in slot n % R.  The key ranges of consecutive steps
+        // overlap, so a tile that is still resident is not loaded again.  A
+        // step's tiles are taken in chunks: all of them at once when they fit
+        // in the ring, else R / 2 at a time.  A chunk's missing tiles are
+        // issued together (one wait for all of them), and while it is
+        // computed the next chunk's tiles (the rest of the step, or the next
+        // step's first ones) are copied into the slots it does not read, with
+        // the next step's Q.  Tiles [res_lo, res_hi) are resident (or in
+        // flight); they only move forward, so a tile is evicted only once no
+        // later chunk needs it.
+        constexpr int R = run_slots<D>();
+        auto chunk_of = [&](int nt) { return nt <= R ? R : max(1, R / 2); };
         bf16x8 qn[QK_STEPS];
         int res_lo = 0, res_hi = 0;
         [[maybe_unused]] int rot_hi = 0;        // ROPEK: resident tiles below it are rotated
-        auto load_tile = [&](int tn) { issue(tn * BN, tn % kRunSlots); };
+        auto load_tile = [&](int tn) { issue(tn * BN, tn % R); };
         for (int s = 0; s < nsteps; ++s) {
             if (s > 0) {
                 set_step(s);
@@ -682,16 +690,20 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
             if (has_next) block_keys(nx_row0, nx_lo, nx_tb, nx_nt);
             const int nx_w0 = nx_row0 + 32 * (wave / hpw);
             const int tb0 = t_begin / BN, tb1 = tb0 + ntiles;
-            for (int c0 = tb0; c0 < tb1; c0 += kRunSlots) {
-                const int c1 = min(tb1, c0 + kRunSlots);
-                // the chunk's missing tiles (the barrier that ended the last
-                // chunk has passed: no wave still reads a slot refilled here)
+            const int ch = chunk_of(ntiles);
+            for (int c0 = tb0; c0 < tb1; c0 += ch) {
+                const int c1 = min(tb1, c0 + ch);
+                // the chunk's missing tiles; the slots they refill may still
+                // be read by slower waves, so all waves meet first
                 if (c0 < res_lo || c0 > res_hi) {
                     res_lo = res_hi = c0;
                     if constexpr (ROPEK) rot_hi = c0;
                 }
-                while (res_hi < c1) load_tile(res_hi++);
-                res_lo = max(res_lo, res_hi - kRunSlots);
+                if (res_hi < c1) {
+                    __syncthreads();
+                    while (res_hi < c1) load_tile(res_hi++);
+                    res_lo = max(res_lo, res_hi - R);
+                }
                 if (c0 == tb0 && a.rope) rotate_q();
                 __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
                 __syncthreads();
@@ -701,7 +713,7 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
                         for (int tn = max(rot_hi, c0); tn < c1; ++tn) {
                             load_ktab(tn * BN);
                             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-                            rotate_k(tn % kRunSlots, tn * BN);
+                            rotate_k(tn % R, tn * BN);
                         }
                         rot_hi = c1;
                         __syncthreads();
@@ -711,23 +723,24 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
                 int n0 = 0, n1 = 0;
                 if (c1 < tb1) {
                     n0 = c1;
-                    n1 = min(tb1, c1 + kRunSlots);
+                    n1 = min(tb1, c1 + ch);
                 } else if (has_next && nx_nt > 0) {
                     n0 = nx_tb / BN;
-                    n1 = n0 + min(nx_nt, kRunSlots);
+                    n1 = n0 + min(nx_nt, chunk_of(nx_nt));
                 }
                 // its tiles that continue the resident range, into slots this
-                // chunk does not read (tile n evicts tile n - kRunSlots < c0)
+                // chunk does not read (tile n evicts tile n - R < c0); every
+                // wave has passed the barrier above, so no wave still reads
+                // an earlier chunk
                 if (n1 > n0 && n0 <= res_hi && n0 >= res_lo) {
-                    while (res_hi < n1 && res_hi < c0 + kRunSlots) load_tile(res_hi++);
-                    res_lo = max(res_lo, res_hi - kRunSlots);
+                    while (res_hi < n1 && res_hi < c0 + R) load_tile(res_hi++);
+                    res_lo = max(res_lo, res_hi - R);
                 }
                 if (c1 == tb1 && has_next) load_q(qn, nx_w0, max(0, min(32, Lq - nx_w0)));
                 for (int tn = c0; tn < c1; ++tn) {
                     const int t0 = tn * BN;
-                    if (wrows > 0 && t0 < w_hi && t0 + BN > w_lo) compute(tn % kRunSlots, t0);
+                    if (wrows > 0 && t0 < w_hi && t0 + BN > w_lo) compute(tn % R, t0);
                 }
-                __syncthreads();
             }
             // no tile in this step: the next step's Q still has to arrive
             if (ntiles == 0 && has_next) load_q(qn, nx_w0, max(0, min(32, Lq - nx_w0)));
@@ -740,8 +753,9 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
 
 template <int D>
 constexpr int prefill_lds_bytes(bool run) {
-    // runs: the tile ring and 16 staged rows per wave
-    return run ? kRunSlots * Tile<D>::BUF + 4 * 16 * (D * 2 + 16) : 2 * Tile<D>::BUF;
+    // runs: the tile ring and the staged rows of the four waves
+    return run ? run_slots<D>() * Tile<D>::BUF + 4 * run_stage_rows<D>() * (D * 2 + 16)
+               : 2 * Tile<D>::BUF;
 }
 
 pkv_status launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream)
