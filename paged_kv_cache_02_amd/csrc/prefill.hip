@@ -521,6 +521,15 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
     auto compute = [&](int buf, int t0) {
         const char *kl = lds + buf * TL::BUF;
         const char *vl = kl + TL::BYTES;
+        // A 32-key chunk that no row of the wave sees (left of the window of
+        // its first row, or right of the diagonal of its last) skips the
+        // softmax: its logits would all be masked, its P all zero.  The
+        // MFMAs still run, which keeps the instruction schedule one shape.
+        const bool dead0 = t0 + 32 <= w_lo || t0 >= w_hi;
+        const bool dead1 = t0 + BN <= w_lo || t0 + 32 >= w_hi;
+        auto p_of = [&](const f32x16 &sx, int sp, bool dead) {
+            return dead ? bf16x8{} : make_p(sx, sp);
+        };
         auto kread = [&](int n) {      // K operand of S MFMA n: chunk n / QK, k-step n % QK
             return *reinterpret_cast<const bf16x8 *>(kl + k_lane + 32 * (n / QK_STEPS) * U * 16 +
                                                      k_unit[n % QK_STEPS]);
@@ -539,7 +548,7 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
             if (n < QK_STEPS) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[n % (KA + 1)], qf[n], s0, 0, 0, 0);
             else s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[n % (KA + 1)], qf[n - QK_STEPS], s1, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
-            if (n == QK_STEPS + 1) finish(s0, t0);
+            if (n == QK_STEPS + 1 && !dead0) finish(s0, t0);
         }
         // O^T += V^T . P^T, one 16-key step at a time (ks 0, 1 from chunk 0,
         // ks 2, 3 from chunk 1); V^T operands (transpose reads) VA ahead
@@ -554,7 +563,7 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
         bf16x8 vv[VA + 1];
 #pragma unroll
         for (int n = 0; n < VA; ++n) vv[n] = vread(n / DT, n % DT);
-        bf16x8 pf = make_p(s0, 0);
+        bf16x8 pf = p_of(s0, 0, dead0);
 #pragma unroll
         for (int n = 0; n < NPV; ++n) {
             const int ks = n / DT, t = n % DT;
@@ -564,8 +573,9 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
             __builtin_amdgcn_sched_barrier(0);
             if (t == DT - 1) {
                 // a rescale may only fall between whole k-steps of P.V
-                if (ks == 0) finish(s1, t0 + 32);
-                if (ks + 1 < 4) pf = make_p(ks + 1 < 2 ? s0 : s1, (ks + 1) & 1);
+                if (ks == 0 && !dead1) finish(s1, t0 + 32);
+                if (ks + 1 < 4)
+                    pf = ks + 1 < 2 ? p_of(s0, (ks + 1) & 1, dead0) : p_of(s1, (ks + 1) & 1, dead1);
             }
         }
     };
