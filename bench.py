@@ -103,19 +103,43 @@ class KernelTimes:
         return set(self.ms)
 
 
-def kernel_ms(launchers, steps, warmup):
+GRAPH_FALLBACKS = []       # kernels whose launches could not be captured in a graph
+
+
+def kernel_ms(launchers, steps, warmup, stream, name):
     """Mean duration of one launch: HIP events on the launch stream around
     `steps` back-to-back launches (cycling through the replicas' launchers),
-    after `warmup` untimed ones."""
-    for i in range(warmup):
-        launchers[i % len(launchers)]()
+    after `warmup` untimed ones.  The launches are captured once in a HIP
+    graph and replayed, so that the host's call overhead (tens of µs per
+    Python call) does not space out kernels shorter than it; if the capture
+    fails they are issued one by one instead (noted in GRAPH_FALLBACKS)."""
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            launchers[i % len(launchers)]()
+    torch.cuda.synchronize()
+    graph = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(steps):
+                launchers[i % len(launchers)]()
+        with torch.cuda.stream(stream):  # a graph replays on the current stream
+            g.replay()                  # once untimed
+        torch.cuda.synchronize()
+        graph = g
+    except Exception as exc:            # noqa: BLE001 - any capture failure: eager timing
+        GRAPH_FALLBACKS.append(f"{name}: {type(exc).__name__}")
+        torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(steps):
-        launchers[i % len(launchers)]()
-    e1.record()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(steps):
+                launchers[i % len(launchers)]()
+        e1.record(stream)
     e1.synchronize()
     return e0.elapsed_time(e1) / steps
 
@@ -148,10 +172,14 @@ def timed_steps(step, steps, warmup, reps=1):
         step(i, NoTimer())
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
+    # the launchers are prepared on a side stream (default priority), which
+    # they then launch on and which the graph capture uses
+    side = torch.cuda.Stream()
     pr = Preparer()
-    for i in range(reps):
-        step(i, pr)
-    kms = {name: kernel_ms(ls, steps, warmup) for name, ls in pr.launchers.items()}
+    with torch.cuda.stream(side):
+        for i in range(reps):
+            step(i, pr)
+    kms = {name: kernel_ms(ls, steps, warmup, side, name) for name, ls in pr.launchers.items()}
     return ms, KernelTimes(kms)
 
 
@@ -800,6 +828,10 @@ def main():
             units = rng.choice(c2.B * c2.Hq, 64, replace=False)
             line["parity_spot_check"] = spot_check(out2, o2, units, c2.Hq, "decode vs oracle")
     line["workloads"] = workloads
+    line["kernel_timing"] = {
+        "method": "HIP events around one replay of a HIP graph of back-to-back prepared "
+                  "launches (steps per kernel), on the stream the launches use",
+        "eager_fallbacks": GRAPH_FALLBACKS}
     print(json.dumps(line), flush=True)
 
 
