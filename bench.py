@@ -103,45 +103,58 @@ class KernelTimes:
         return set(self.ms)
 
 
-GRAPH_FALLBACKS = []       # kernels whose launches could not be captured in a graph
+# how each kernel's launch time was taken, in the order the kernels were
+# timed: "eager" (back-to-back launches from the host) or "graph" (one replay
+# of a HIP graph of the same launches)
+KERNEL_TIMING = []
+GRAPH_BELOW_MS = 0.06      # kernels shorter than this are also timed through a graph
 
 
 def kernel_ms(launchers, steps, warmup, stream, name):
     """Mean duration of one launch: HIP events on the launch stream around
     `steps` back-to-back launches (cycling through the replicas' launchers),
-    after `warmup` untimed ones.  The launches are captured once in a HIP
-    graph and replayed, so that the host's call overhead (tens of µs per
-    Python call) does not space out kernels shorter than it; if the capture
-    fails they are issued one by one instead (noted in GRAPH_FALLBACKS)."""
+    after `warmup` untimed ones.  A kernel shorter than GRAPH_BELOW_MS is
+    issued by the host faster than it runs only barely, if at all (a Python
+    call costs tens of µs), so its launches are also captured once in a HIP
+    graph and replayed, and the faster of the two timings is kept; the
+    method is noted in KERNEL_TIMING.  Longer kernels keep the eager timing
+    (graph replays ran them no faster)."""
     with torch.cuda.stream(stream):
         for i in range(warmup):
             launchers[i % len(launchers)]()
     torch.cuda.synchronize()
-    graph = None
-    try:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(steps):
-                launchers[i % len(launchers)]()
-        with torch.cuda.stream(stream):  # a graph replays on the current stream
-            g.replay()                  # once untimed
-        torch.cuda.synchronize()
-        graph = g
-    except Exception as exc:            # noqa: BLE001 - any capture failure: eager timing
-        GRAPH_FALLBACKS.append(f"{name}: {type(exc).__name__}")
-        torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        if graph is not None:
-            graph.replay()
-        else:
-            for i in range(steps):
-                launchers[i % len(launchers)]()
-        e1.record(stream)
-    e1.synchronize()
-    return e0.elapsed_time(e1) / steps
+
+    def timed(body):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            body()
+            e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def eager():
+        for i in range(steps):
+            launchers[i % len(launchers)]()
+    ms = timed(eager)
+    method = "eager"
+    if ms < GRAPH_BELOW_MS:
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                eager()
+            with torch.cuda.stream(stream):   # a graph replays on the current stream
+                g.replay()                    # once untimed
+            torch.cuda.synchronize()
+            gms = timed(g.replay)
+            if gms < ms:
+                ms, method = gms, "graph"
+        except Exception as exc:              # noqa: BLE001 - capture failed: eager timing
+            method = f"eager (graph capture failed: {type(exc).__name__})"
+            torch.cuda.synchronize()
+    KERNEL_TIMING.append({"kernel": name, "method": method, "ms": round(ms, 4)})
+    return ms
 
 
 def spin_up(step, seconds):
@@ -829,9 +842,10 @@ def main():
             line["parity_spot_check"] = spot_check(out2, o2, units, c2.Hq, "decode vs oracle")
     line["workloads"] = workloads
     line["kernel_timing"] = {
-        "method": "HIP events around one replay of a HIP graph of back-to-back prepared "
-                  "launches (steps per kernel), on the stream the launches use",
-        "eager_fallbacks": GRAPH_FALLBACKS}
+        "method": "HIP events on the launch stream around back-to-back prepared launches "
+                  "(steps per kernel); kernels under 60 us also through one replay of a HIP "
+                  "graph of the same launches, the faster kept",
+        "in_order": KERNEL_TIMING}
     print(json.dumps(line), flush=True)
 
 
