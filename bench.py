@@ -108,6 +108,22 @@ class KernelTimes:
 # of a HIP graph of the same launches)
 KERNEL_TIMING = []
 GRAPH_BELOW_MS = 0.06      # kernels shorter than this are also timed through a graph
+WORKLOAD = ""              # the workload being timed (names the marker ranges)
+
+
+def _range(label):
+    """Push a named range (roctx under ROCm: rocprofv3 --marker-trace records
+    it), so that a kernel trace can pick out each timed block of launches."""
+    try:
+        torch.cuda.nvtx.range_push(label)
+        return True
+    except Exception:           # noqa: BLE001 - no marker library: nothing to mark
+        return False
+
+
+def _range_end(pushed):
+    if pushed:
+        torch.cuda.nvtx.range_pop()
 
 
 def kernel_ms(launchers, steps, warmup, stream, name):
@@ -124,20 +140,22 @@ def kernel_ms(launchers, steps, warmup, stream, name):
             launchers[i % len(launchers)]()
     torch.cuda.synchronize()
 
-    def timed(body):
+    def timed(body, kind):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        pushed = _range(f"timed|{WORKLOAD}|{name}|{kind}")
         with torch.cuda.stream(stream):
             e0.record(stream)
             body()
             e1.record(stream)
         e1.synchronize()
+        _range_end(pushed)
         return e0.elapsed_time(e1) / steps
 
     def eager():
         for i in range(steps):
             launchers[i % len(launchers)]()
-    ms = timed(eager)
+    ms = timed(eager, "eager")
     method = "eager"
     if ms < GRAPH_BELOW_MS:
         try:
@@ -147,13 +165,14 @@ def kernel_ms(launchers, steps, warmup, stream, name):
             with torch.cuda.stream(stream):   # a graph replays on the current stream
                 g.replay()                    # once untimed
             torch.cuda.synchronize()
-            gms = timed(g.replay)
+            gms = timed(g.replay, "graph")
             if gms < ms:
                 ms, method = gms, "graph"
         except Exception as exc:              # noqa: BLE001 - capture failed: eager timing
             method = f"eager (graph capture failed: {type(exc).__name__})"
             torch.cuda.synchronize()
-    KERNEL_TIMING.append({"kernel": name, "method": method, "ms": round(ms, 4)})
+    KERNEL_TIMING.append({"workload": WORKLOAD, "kernel": name, "method": method,
+                          "ms": round(ms, 4)})
     return ms
 
 
@@ -274,6 +293,8 @@ def bench_decode(c, name, steps, warmup, partition_size, reps, traffic_key=None,
     """partition_size 0: the automatic (balanced) schedule, one launch with the
     merge fused in (two_stage: its stage and merge launches, timed apart);
     > 0: fixed partitions + merge."""
+    global WORKLOAD
+    WORKLOAD = name
     B, Hq, D = c.B, c.Hq, c.D
     kc, vc, tables = replicate_pool(c, reps)
     q = c.q.cuda()
@@ -337,6 +358,8 @@ def bench_decode_append(c, name, steps, warmup, reps):
     tokens already cached), so the attended keys are those of the plain
     decode.  Timed as one pkv_paged_decode_append launch, and beside it the
     unfused equivalent: reshape_and_cache of the B new rows, then decode."""
+    global WORKLOAD
+    WORKLOAD = name
     B, Hq, D, bs = c.B, c.Hq, c.D, c.block_size
     kc, vc, tables = replicate_pool(c, reps)
     q = c.q.cuda()
@@ -420,6 +443,8 @@ def bench_prefill(c, name, steps, warmup, reps, with_cache_write=False, traffic_
     contiguous keys are rotated too in the same call, once into a workspace
     (or, keys_in_kernel, inside the attention kernel as it loads them; or,
     unfused, by a rope_apply launch of their own)."""
+    global WORKLOAD
+    WORKLOAD = name
     T = c.q.shape[0]
     fused = rope is not None and not rope_unfused
     rkw = dict(rope_cos_sin=rope["tab"], rotary_dim=rope["rd"], rope_neox=rope["neox"],
@@ -552,6 +577,8 @@ def bench_sparse(steps, warmup):
     """Vertical + slash sparse prefill: the block lists, then the attention,
     on one request of 32768 tokens; the dense causal prefill of the same input
     timed beside it."""
+    global WORKLOAD
+    WORKLOAD = "sparse_prefill_1x32768_vs"
     c, V, S = synth.sparse_prefill_workload()
     L, Hq, D = c.q.shape
     q, k, v = c.q.cuda(), c.k.cuda(), c.v.cuda()
@@ -570,6 +597,7 @@ def bench_sparse(steps, warmup):
                                                     v=v, out=out))
 
     ms, kt = timed_steps(step, steps, warmup)
+    WORKLOAD = "sparse_prefill_1x32768_vs/dense"
     _, ktd = timed_steps(dense, steps, warmup)
     host = [t.cpu().numpy() for t in lists]
     pairs, _ = sparse_pairs(host, L)
