@@ -196,9 +196,13 @@ ROPE_K = [
 ]
 
 
+# float32 rotates the keys in registers, with or without a workspace: one case
+ROPE_K_PATHS = [("workspace", torch.bfloat16), ("in_kernel", torch.bfloat16),
+                ("registers", torch.float32)]
+
+
 @pytest.mark.parametrize("case", ROPE_K, ids=[str(i) for i in range(len(ROPE_K))])
-@pytest.mark.parametrize("keys", ["workspace", "in_kernel"])
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("keys,dtype", ROPE_K_PATHS, ids=[k for k, _ in ROPE_K_PATHS])
 def test_prefill_rope_k(case, keys, dtype):
     """rope_k: contiguous keys rotated by their positions, q by its own;
     bf16 rotates the keys once into a workspace (NaN-filled beforehand) or,
@@ -207,8 +211,6 @@ def test_prefill_rope_k(case, keys, dtype):
     type, as the kernels round it)."""
     from paged_kv_cache_02_amd import pkv
     q_lens, k_lens, Hq, Hkv, D, rd, neox, window, causal = case
-    if dtype == torch.float32 and keys == "in_kernel":
-        pytest.skip("float32 rotates the keys in registers, with or without a workspace")
     banner(f"prefill rope_k {dtype} {keys} {case}")
     k_lens = k_lens or q_lens
     c = synth.prefill_case(560 + len(q_lens), q_lens, k_lens, Hq, Hkv, D, dtype, True,
@@ -221,7 +223,7 @@ def test_prefill_rope_k(case, keys, dtype):
     T = c.q.shape[0]
     lse = torch.empty(T, Hq, dtype=torch.float32, device="cuda")
     ws = False
-    if keys == "workspace":
+    if keys != "in_kernel":
         need = pkv.varlen_prefill_workspace_bytes(len(q_lens), c.max_seqlen_k, Hkv, D, True, dtype)
         ws = torch.full((max(need, 1) // 2,), float("nan"), dtype=torch.bfloat16,
                         device="cuda").view(torch.uint8) if need else None
