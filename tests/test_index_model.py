@@ -65,8 +65,9 @@ def model_prefill(q_lens, k_lens, Hq, Hkv, D, window=-1, paged_bs=0, rope_rows=N
         rest = bid // Hkv
         hs = rest % ng
         rest = rest // ng
-        u = rest % runs
-        r = rest // runs
+        r = rest % B                       # the last runs of the requests first
+        u = runs - 1 - rest // B
+        assert (u >= 0).all()
         # one entry per (workgroup, step)
         step = np.tile(np.arange(steps), grid)
         g, hs, u, r = (np.repeat(x, steps) for x in (g, hs, u, r))
@@ -389,6 +390,105 @@ def test_rope_keys_mapping_in_bounds():
     assert n > 0
     with pytest.raises(AssertionError):     # a table one row short
         model_rope_keys([5, 9], 2, 64, 9, rope_rows=8, ws_rows=18)
+
+
+RUN_SLOTS = 4      # tile slots of the LDS ring of a run
+
+
+def model_run_ring(q_lens, k_lens, Hq, Hkv, window, causal=True, slots=RUN_SLOTS):
+    """The tile ring of a run of position blocks (prefill_bf16_kernel, RUN):
+    per step, its tile range [tb0, tb1) is taken in chunks (all of it when it
+    fits in the ring, else half the ring at a time); a chunk's missing tiles
+    are loaded (tile n into slot n % slots), then the next chunk's tiles that
+    continue the resident range are prefetched into slots the chunk does not
+    read.  Checks, for every run of every request, that each computed tile is
+    in its slot when the chunk computes it and that no prefetch refills a slot
+    the chunk reads.  Returns the number of tile loads."""
+    G = Hq // Hkv
+    hpw = heads_per_unit(G)
+    bm = BM // hpw
+    B = len(q_lens)
+    max_q = max(q_lens, default=0)
+    per_req = (max_q + bm - 1) // bm
+    blocks = B * per_req * (G // hpw) * Hkv
+    steps = min(16, max(1, blocks // (2 * CUS)))
+    runs = (per_req + steps - 1) // steps
+
+    def keys(row0, Lq, Lk):
+        nr = min(bm, Lq - row0)
+        p0 = Lk - Lq + row0
+        lo = max(0, p0 - window) if window >= 0 else 0
+        hi = min(Lk, p0 + nr) if causal else Lk
+        tb = lo & ~(BN - 1)
+        return tb // BN, ((hi - tb + BN - 1) // BN if hi > lo else 0)
+
+    def chunk_of(nt):
+        return slots if nt <= slots else max(1, slots // 2)
+
+    loads = 0
+    for Lq, Lk in zip(q_lens, k_lens):
+        for u in range(runs):
+            slot = [None] * slots
+            res_lo = res_hi = 0
+            for s in range(steps):
+                row0 = (u * steps + s) * bm
+                if row0 >= Lq:
+                    break
+                tb0, nt = keys(row0, Lq, Lk)
+                tb1 = tb0 + nt
+                has_next = s + 1 < steps and row0 + bm < Lq
+                nx_tb, nx_nt = keys(row0 + bm, Lq, Lk) if has_next else (0, 0)
+                ch = chunk_of(nt)
+                for c0 in range(tb0, tb1, ch):
+                    c1 = min(tb1, c0 + ch)
+                    if c0 < res_lo or c0 > res_hi:
+                        res_lo = res_hi = c0
+                    while res_hi < c1:
+                        slot[res_hi % slots] = res_hi
+                        res_hi += 1
+                        loads += 1
+                    res_lo = max(res_lo, res_hi - slots)
+                    if c1 < tb1:
+                        n0, n1 = c1, min(tb1, c1 + ch)
+                    elif has_next and nx_nt > 0:
+                        n0, n1 = nx_tb, nx_tb + min(nx_nt, chunk_of(nx_nt))
+                    else:
+                        n0 = n1 = 0
+                    pre = []
+                    if n1 > n0 and res_lo <= n0 <= res_hi:
+                        while res_hi < n1 and res_hi < c0 + slots:
+                            assert res_hi % slots not in {t % slots for t in range(c0, c1)}, \
+                                "a prefetch refills a slot the chunk reads"
+                            pre.append(res_hi)
+                            res_hi += 1
+                            loads += 1
+                        res_lo = max(res_lo, res_hi - slots)
+                    for tn in range(c0, c1):
+                        assert slot[tn % slots] == tn, "a computed tile is not in its slot"
+                    for t in pre:
+                        slot[t % slots] = t
+    return loads
+
+
+def test_run_ring_residency():
+    import random
+    n = 0
+    for q_lens, k_lens, Hq, Hkv, D, window, bs in prefill_shapes():
+        for w in sorted({window, 0, 50, 128, 300}):
+            if w >= 0:
+                n += model_run_ring(q_lens, k_lens or q_lens, Hq, Hkv, w)
+    rnd = random.Random(5)
+    for _ in range(300):               # windows, lengths and GQA shapes the suite does not hold
+        Lk = rnd.randint(1, 3000)
+        Lq = rnd.randint(1, Lk + 50)
+        Hkv = rnd.choice([1, 2, 8])
+        Hq = Hkv * rnd.choice([1, 2, 4, 8])
+        w = rnd.choice([0, 1, 63, 64, 127, 129, 255, 1000])
+        n += model_run_ring([Lq], [Lk], Hq, Hkv, w)
+        n += model_run_ring([Lq], [Lk], Hq, Hkv, w, causal=False)
+    assert n > 0
+    # the chunked workload: 2 steps of 32 positions per run read the same 3 tiles
+    assert model_run_ring([512] * 4, [8704] * 4, 64, 8, 128) == 4 * 8 * 3
 
 
 def decode_shapes():
