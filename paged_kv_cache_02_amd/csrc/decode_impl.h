@@ -19,9 +19,12 @@
 //     straight from 16-byte loads (lane r%16 = token, 8 dims per lane), the
 //     HU heads (replicated to 16 columns) are the B operand in registers;
 //     lane (j, r) receives the logits of tokens 4j..4j+3 for head r % HU;
-//   * P.V on the VALU: lane (j, r) loads V rows of the same 4 tokens (16
-//     lanes cover a 256-byte row) and takes the other heads' probabilities
-//     from its quad with DPP broadcasts;
+//   * O^T += V^T . P on v_mfma_f32_16x16x16_bf16, one MFMA per 16 dims: lane
+//     (j, r) loads V rows of the same 4 tokens (16 lanes cover a 256-byte
+//     row) and leaves them in the wave's LDS buffer, token-major; the V^T
+//     operand comes back by the LDS transpose read, P (the logits' lanes,
+//     rounded to bf16) is the B operand as it stands, and lane (j, r) then
+//     holds head r % HU at dims 16 db + 4 j .. +3 of every 16-dim block db;
 //   * online softmax with a reference maximum per head that is raised only
 //     when a logit exceeds it by more than 2^8 (one ballot per tile);
 //   * a ring of 4 register buffers keeps 3 tiles in flight per wave; loads go
@@ -81,11 +84,23 @@ __device__ __forceinline__ float bcast_head(float x, int hh) {
     }
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+
+// The per-wave LDS buffer of the P.V step: 16 token rows of V (head_dim bf16
+// plus 16 bytes of padding, so that the lanes' 16-byte row writes spread over
+// all banks); reduce() reuses it for the accumulators.
+template <int D> constexpr int vt_row_bytes() { return D * 2 + 16; }
+template <int D> constexpr int vt_bytes() { return 16 * vt_row_bytes<D>(); }
+
 template <int D, int HU, bool ALIBI = false, bool BS8 = false>
 struct DecodeWave {
     static constexpr int KSTEPS = D / 32;          // MFMA k-steps over head_dim
     static constexpr int VLD = D == 128 ? 4 : 2;   // V rows loaded per lane per tile
+    static constexpr int DB = D / 16;              // 16-dim blocks of the output
+    static constexpr int VROW = vt_row_bytes<D>();
     static_assert(HU == 1 || HU == 2 || HU == 4, "heads per unit");
+    static_assert(HU * D * 4 <= vt_bytes<D>(), "reduce() fits in the buffer");
 
     int lane, j, r;
     int tok_bytes;          // one token row, all kv heads
@@ -94,7 +109,9 @@ struct DecodeWave {
     // 8-token block of a tile
     bool khi, vhi[VLD];
     bf16x8 qf[KSTEPS];
-    float acc[HU][8];
+    f32x4 oacc[DB];         // O^T: head r % HU, dims 16 db + 4 j + i
+    float acc[HU][8];       // after reduce(): see there
+    char *vt;               // this wave's LDS buffer
     float m_lane, l_lane;
     float scale_log2;
     // ALiBi: the slope of this lane's head (column r % HU) times log2(e), 0
@@ -103,7 +120,8 @@ struct DecodeWave {
     float slope_log2;
     int qpos;
 
-    __device__ void setup(int g, int Hkv, float sl2, const float *alibi, int h0) {
+    __device__ void setup(int g, int Hkv, float sl2, const float *alibi, int h0, char *vt_buf) {
+        vt = vt_buf;
         lane = threadIdx.x & 63;
         j = lane >> 4;
         r = lane & 15;
@@ -132,9 +150,7 @@ struct DecodeWave {
 
     __device__ void reset() {
 #pragma unroll
-        for (int hh = 0; hh < HU; ++hh)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+        for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
         m_lane = kNoMax;
         l_lane = 0.f;
     }
@@ -201,18 +217,19 @@ struct DecodeWave {
             const float alpha = fast_exp2(m_lane - nm);
             l_lane *= alpha;
             m_lane = nm;
+            // lane (j, r) holds head r % HU only: its own alpha
 #pragma unroll
-            for (int hh = 0; hh < HU; ++hh) {
-                const float ah = bcast_head<HU>(alpha, hh);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[hh][e] *= ah;
-            }
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
         }
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - m_lane);
-        l_lane += (p[0] + p[1]) + (p[2] + p[3]);
+        // P rounded to bf16 for the MFMA; the row sum takes the rounded values
+        const uint32_t p01 = pack_bf16x2(p[0], p[1]), p23 = pack_bf16x2(p[2], p[3]);
+        l_lane += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
 
+        // V rows at masked positions are zeroed: whatever those cache slots
+        // hold (never written, NaN) must not reach the MFMA, even times 0
         if (partial) {
 #pragma unroll
             for (int i = 0; i < VLD; ++i) {
@@ -220,27 +237,32 @@ struct DecodeWave {
                 if (!vv) vb[i] = u32x4{0u, 0u, 0u, 0u};
             }
         }
+        // V token-major into the wave's buffer (lane (j, r) has rows tv of
+        // dims dv .. dv + 7), then O^T += V^T . P per 16-dim block: lane
+        // (j, r) reads by the transpose read the 4 dims 16 db + 4 (r % 4) of
+        // token row 4 j + r / 4, and receives dim 16 db + r of tokens 4 j ..
+        // 4 j + 3, the A operand; P of those tokens for head column r is the
+        // B operand.  A wave's LDS accesses run in order, so the reads see
+        // this tile's writes and the next tile's writes come after them.
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
-            const float pi = D == 128 ? p[i] : ((r >> 3) ? p[2 + i] : p[i]);
-            float v[8];
+            const int tv = D == 128 ? 4 * j + i : 4 * j + 2 * (r >> 3) + i;
+            const int dv = D == 128 ? 8 * r : 8 * (r & 7);
+            *reinterpret_cast<u32x4 *>(vt + tv * VROW + dv * 2) = vb[i];
+        }
+        const s16x4 pb = __builtin_bit_cast(s16x4, u32x2{p01, p23});
+        const char *vr = vt + (4 * j + (r >> 2)) * VROW + 8 * (r & 3);
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                v[2 * w] = bf16_lo(vb[i][w]);
-                v[2 * w + 1] = bf16_hi(vb[i][w]);
-            }
-#pragma unroll
-            for (int hh = 0; hh < HU; ++hh) {
-                const float ph = bcast_head<HU>(pi, hh);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(ph, v[e], acc[hh][e]);
-            }
+        for (int db = 0; db < DB; ++db) {
+            const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(vr + 32 * db));
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, va), pb,
+                                                                 oacc[db], 0, 0, 0);
         }
     }
 
-    // Sum the state over the lanes that hold the same (head, dims): afterwards
-    // lanes with j == 0 (and r < 8 for D = 64) hold acc for dims d0()..d0()+7,
-    // and the returned sum of p is complete in lanes r < HU (for head r).
+    // Gather the state: afterwards lanes with j == 0 (and r < 8 for D = 64)
+    // hold acc[hh] for dims d0()..d0()+7 of every head hh, and the returned
+    // sum of p is complete in lanes r < HU (for head r).
     // x + x^16 and x + x^32 (lane index xor 16 / 32) with the VALU lane swaps
     // of gfx950: permlane16_swap(x, x) returns the even and the odd 16-lane
     // rows of each pair side by side, permlane32_swap(x, x) the two halves
@@ -263,14 +285,28 @@ struct DecodeWave {
     }
     __device__ float reduce() {
         const float lsum = sum_xor32(sum_xor16(l_lane));
+        // the MFMA summed over the tokens already; the lanes of head column
+        // r < HU leave their dims in the buffer as [head][dim] floats, and
+        // the holding lanes read their 8 dims of every head back (in order
+        // within the wave, like the P.V step)
+        float *sa = reinterpret_cast<float *>(vt);
+        if (r < HU) {
 #pragma unroll
-        for (int hh = 0; hh < HU; ++hh)
+            for (int db = 0; db < DB; ++db)
+                *reinterpret_cast<f32x4 *>(sa + r * D + 16 * db + 4 * j) = oacc[db];
+        }
+        if (holds_acc()) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float x = acc[hh][e];
-                if (D == 64) x = sum_xor8(x);
-                acc[hh][e] = sum_xor32(sum_xor16(x));
+            for (int hh = 0; hh < HU; ++hh) {
+                const f32x4 lo4 = *reinterpret_cast<const f32x4 *>(sa + hh * D + d0());
+                const f32x4 hi4 = *reinterpret_cast<const f32x4 *>(sa + hh * D + d0() + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[hh][e] = lo4[e];
+                    acc[hh][4 + e] = hi4[e];
+                }
             }
+        }
         return lsum;
     }
     __device__ bool holds_acc() const { return j == 0 && (D == 128 || r < 8); }
@@ -286,6 +322,7 @@ __global__ __launch_bounds__(256) void decode_part_kernel(DecodeArgs a)
     __shared__ float sm_m[kWaves][HU];
     __shared__ float sm_l[kWaves][HU];
     __shared__ float sm_acc[kWaves][HU][D];
+    __shared__ __attribute__((aligned(16))) char s_vt[kWaves][vt_bytes<D>()];
 
     const int wave = readfirstlane(threadIdx.x >> 6);
     const int NHG = a.Hq / HU;
@@ -304,7 +341,7 @@ __global__ __launch_bounds__(256) void decode_part_kernel(DecodeArgs a)
     if (a.window_left >= 0) start = max(start, L - 1 - a.window_left);
 
     DecodeWave<D, HU, ALIBI, BS8> w;
-    w.setup(g, a.Hkv, a.scale_log2, a.alibi, h0);
+    w.setup(g, a.Hkv, a.scale_log2, a.alibi, h0, s_vt[wave]);
     w.qpos = L - 1;
     w.load_q(a.q, (size_t)b * a.Hq + h0);
     w.reset();
@@ -531,6 +568,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(Stream
     __shared__ __attribute__((aligned(16))) float s_stage[PARTS ? kStreamWaves : 1]
                                                          [PARTS ? kStage * HU * D : 1];
     __shared__ float s_stage_lse[PARTS ? kStreamWaves : 1][PARTS ? kStage * HU : 1];
+    __shared__ __attribute__((aligned(16))) char s_vt[kStreamWaves][vt_bytes<D>()];
 
     const int tid = threadIdx.x;
     const int wave = readfirstlane(tid >> 6);
@@ -623,7 +661,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(Stream
     if (n <= 0) return;
 
     DecodeWave<D, HU, ALIBI, BS8> w;
-    w.setup(g, a.Hkv, a.scale_log2, a.alibi, h0);
+    w.setup(g, a.Hkv, a.scale_log2, a.alibi, h0, s_vt[wave]);
     const int bs_mask = (1 << a.bs_log2) - 1;
 
     // the sequence that holds flattened tile x0
