@@ -1045,23 +1045,33 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(Stream
         // count.  The wave that brings a count to pieces(b) merges b and
         // leaves its counter zero for the next call.
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        // A counter holds (epoch << 32) | count.  One compare-and-swap per
-        // arrival: a counter left by another call (another epoch) restarts
-        // from zero, so a workspace that an interrupted call or another mode
-        // left dirty cannot make a merge run early or never.
+        // A counter holds (epoch << 32) | count, and zero at rest.  The first
+        // arrival of a call claims the counter with one compare-and-swap
+        // (whatever epoch it held: a counter left by an interrupted call, or
+        // never used, restarts from zero); every later arrival, seeing this
+        // call's epoch, adds one.  A counter that holds this call's epoch
+        // keeps it until its last arrival, so the add never lands on a stale
+        // count, and no wave retries more than once (a compare-and-swap loop
+        // per arrival serialised the many waves that end together on one
+        // sequence when a batch is small).
         auto arrive = [&](int b) {
             int arrived = 0;
             if (lane == 0) {
                 uint64_t *ctr = a.counters + (size_t)b * NHG + hg;
-                uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                uint64_t nv;
-                do {
-                    const uint32_t cnt = (uint32_t)(old >> 32) == a.epoch ? (uint32_t)old : 0u;
-                    nv = ((uint64_t)a.epoch << 32) | (cnt + 1u);
-                } while (!__hip_atomic_compare_exchange_strong(ctr, &old, nv, __ATOMIC_RELAXED,
-                                                               __ATOMIC_RELAXED,
-                                                               __HIP_MEMORY_SCOPE_AGENT));
-                arrived = (int)(uint32_t)nv;
+                const uint64_t mine = (uint64_t)a.epoch << 32;
+                uint64_t v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if ((v >> 32) != a.epoch &&
+                    __hip_atomic_compare_exchange_strong(ctr, &v, mine | 1u, __ATOMIC_RELAXED,
+                                                         __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT)) {
+                    arrived = 1;
+                } else {
+                    // v holds this call's epoch: read so, or left by the
+                    // compare-and-swap that another arrival won
+                    v = __hip_atomic_fetch_add(ctr, (uint64_t)1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                    arrived = (int)(uint32_t)v + 1;
+                }
             }
             return __builtin_amdgcn_readlane(arrived, 0) == pieces(b);
         };
