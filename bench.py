@@ -290,9 +290,11 @@ def alibi_slopes(Hq):
 
 def bench_decode(c, name, steps, warmup, partition_size, reps, traffic_key=None,
                  two_stage=False, alibi=None):
-    """partition_size 0: the automatic (balanced) schedule, one launch with the
-    merge fused in (two_stage: its stage and merge launches, timed apart);
-    > 0: fixed partitions + merge."""
+    """partition_size 0: the automatic (balanced) schedule, whose stage and
+    merge launches pkv_paged_decode issues one after the other (two_stage:
+    the same two launches through their own calls, timed apart); -1: the
+    balanced schedule in one launch with the merge fused in; > 0: fixed
+    partitions + merge."""
     global WORKLOAD
     WORKLOAD = name
     B, Hq, D = c.B, c.Hq, c.D
@@ -338,8 +340,9 @@ def bench_decode(c, name, steps, warmup, partition_size, reps, traffic_key=None,
     res = {
         "name": name, "value": round(step_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
         "ms_per_step": round(ms, 4), "algorithmic_bytes": step_bytes,
-        "schedule": ("balanced, two launches" if two_stage else "balanced, merge fused")
-        if P == 0 else (f"partitions of {P}" if split else "unsplit"),
+        "schedule": "balanced, stage + merge launches" if P == 0
+        else "balanced, one launch (merge fused)" if P == -1
+        else (f"partitions of {P}" if split else "unsplit"),
         "kernels_ms": {"decode": round(dec_ms, 4)},
         "roofline": roofline("hbm", dec_bytes / (dec_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
                              pmc_traffic(traffic_key) if traffic_key else None),
@@ -743,13 +746,14 @@ def main():
     if ARGS.only in ("all", "decode"):
         head, out2 = bench_decode(c2, "decode_64x_U512-4096", steps, warmup,
                                   ARGS.partition_size, reps=2,
-                                  traffic_key="decode_c2" if ARGS.partition_size == 0 else None)
+                                  traffic_key="decode_c2" if ARGS.partition_size == 0 else None,
+                                  two_stage=ARGS.partition_size == 0)
         log(f"decode: {head['value']} GB/s step, kernel {head['roofline']['achieved']} GB/s")
         if ARGS.partition_size == 0:
-            r2s, _ = bench_decode(c2, "decode_64x_U512-4096_two_launches", steps, warmup, 0,
-                                  reps=2, two_stage=True)
-            workloads["decode_two_launches"] = r2s
-            log(f"decode as stage + merge launches: {r2s['value']} GB/s step")
+            r1, _ = bench_decode(c2, "decode_64x_U512-4096_one_launch", steps, warmup, -1,
+                                 reps=2)
+            workloads["decode_one_launch"] = r1
+            log(f"decode in one launch (merge fused): {r1['value']} GB/s step")
             rl, _ = bench_decode(c2, "decode_64x_U512-4096_alibi", steps, warmup, 0, reps=2,
                                  alibi=alibi_slopes(c2.Hq))
             workloads["decode_alibi"] = rl
@@ -822,7 +826,7 @@ def main():
                                 reps=1)
         workloads["split_decode_long"] = r5
         r5b, _ = bench_decode(c5, "split_decode_16x131072_auto", max(3, steps // 4), 2, 0,
-                              reps=1)
+                              reps=1, two_stage=True)
         workloads["split_decode_long_auto"] = r5b
         if not ARGS.no_cpu_baseline:
             r5["cpu_baseline"], _ = cpu_baseline("decode", c5, 256, 16, 50,

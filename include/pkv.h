@@ -187,14 +187,15 @@ pkv_status pkv_reshape_and_cache_rope(const void *key, const void *value, void *
  * buffers tmp_output [num_seqs, num_heads, max_num_partitions, head_size],
  * exp_sums and max_logits before the partitioned kernel runs).  The
  * arguments are those of that allocation: batch, query heads, head_dim, the
- * longest sequence and the partition size (0 = automatic).  The result
+ * longest sequence and the partition size (0 or -1: the balanced schedule, in
+ * two launches or one).  The result
  * covers every kv-head count that divides num_q_heads, both dtypes and
  * every block size, and does not depend on the sequence lengths (device
  * data).  It is 0 for B == 0 and (size_t)-1 for invalid sizes.  Layout
  * (private to the library; stated so that reuse is safe):
  *   - the first kStreamMaxB * num_q_heads * 8 bytes (256-byte aligned) hold
  *     the balanced schedule's arrival counters; no other mode writes them;
- *   - partition_size == 0 (bf16, B <= 4096): the balanced schedule's
+ *   - partition_size 0 or -1 (bf16, B <= 4096): the balanced schedule's
  *     partial results after them, (4 * W + B) * Hq * (head_dim + 1) floats
  *     plus B + 2 ints, W = ceil(compute units / head groups), then room for
  *     q rotated by pkv_paged_decode_append (B * Hq * head_dim bf16);
@@ -232,15 +233,21 @@ size_t pkv_paged_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t 
  *                   merged by log-sum-exp.  0: automatic -- bf16 uses a balanced
  *                   schedule that gives every wave of the device an equal share
  *                   of all sequences' key tiles and merges the pieces the same
- *                   way (B <= 4096), in one launch: the last wave to finish
- *                   a (sequence, head group) merges its pieces; fp32 (and
- *                   larger B) does not split.  Results are bitwise
+ *                   way (B <= 4096), in two launches: the stage launch writes
+ *                   each wave's partial result per sequence to the workspace,
+ *                   the merge launch combines them (the two calls
+ *                   pkv_paged_decode_stage + pkv_paged_decode_finish); fp32
+ *                   (and larger B) does not split.  -1: the same schedule in
+ *                   one launch, the last wave to finish a (sequence, head
+ *                   group) merging its pieces (the same result, bit for bit;
+ *                   one launch fewer, a longer tail).  Results are bitwise
  *                   reproducible for fixed arguments on a given device.
+ *                   Below -1: PKV_ERR_SHAPE.
  *   workspace       device buffer of at least
  *                   pkv_paged_decode_workspace_bytes(...) bytes (may be NULL
  *                   when that is 0), 256-byte aligned, reused across calls.
- *                   The balanced schedule counts the pieces of each
- *                   (sequence, head group) in 64-bit counters at its start,
+ *                   The one-launch balanced schedule (-1) counts the pieces of
+ *                   each (sequence, head group) in 64-bit counters at its start,
  *                   tagged with a per-call epoch: a counter left by an
  *                   interrupted call or holding bytes from another use reads
  *                   as zero, and every completed call leaves its counters
@@ -344,8 +351,9 @@ pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const v
                                    void *stream);
 
 /*
- * The two stages of pkv_paged_decode with partition_size == 0 in bf16 (the
- * balanced schedule), for callers that want to time or overlap them:
+ * The two launches of pkv_paged_decode with partition_size == 0 in bf16 (the
+ * balanced schedule), as separate calls for callers that want to time or
+ * overlap them; pkv_paged_decode(partition_size = 0) is exactly these two:
  *   pkv_paged_decode_stage   every wave of the device takes an equal share of
  *                            all sequences' key tiles and writes one partial
  *                            result (normalised output + lse, sink left out)

@@ -134,8 +134,22 @@ StreamArgs stream_args(const void *q, const void *k_cache, const void *v_cache,
     a.epoch = next_epoch();
     return a;
 }
+// Merge launch of the two-launch balanced decode, over the pieces, lse values
+// and tile prefix sums that a stage launch left in the workspace.
+pkv_status launch_finish(void *out, float *lse, const float *sink, int32_t B, int32_t Hq,
+                         int32_t Hkv, int32_t D, const void *workspace, hipStream_t s) {
+    const StreamLayout lay = stream_layout(B, Hq, Hkv, D);
+    StreamArgs a{};
+    a.part_out = (float *)((char *)workspace + lay.part_out);
+    a.part_lse = (float *)((char *)workspace + lay.part_lse);
+    a.cum_out = (int32_t *)((char *)workspace + lay.cum);
+    a.out = out; a.lse = lse; a.sink = sink; a.B = B; a.Hq = Hq; a.D = D;
+    return launch_stream_merge(a, s);
+}
+// The balanced schedule: partition_size 0 (stage launch + merge launch) or
+// -1 (one launch, merge fused in).
 bool use_stream(pkv_dtype dtype, int32_t B, int32_t partition_size, int32_t max_seqlen_k) {
-    return dtype == PKV_BF16 && partition_size == 0 && B <= kStreamMaxB && max_seqlen_k > 0;
+    return dtype == PKV_BF16 && partition_size <= 0 && B <= kStreamMaxB && max_seqlen_k > 0;
 }
 
 struct SplitPlan {
@@ -220,10 +234,10 @@ pkv_status decode_check(const DecodeCall &c) {
     if (st != PKV_OK) return st;
     if ((st = check_block_size(c.block_size)) != PKV_OK) return st;
     if (!dtype_ok(c.dtype)) return PKV_ERR_UNSUPPORTED;
-    if (c.window_left < -1 || c.partition_size < 0 || !scale_ok(c.sm_scale)) return PKV_ERR_SHAPE;
+    if (c.window_left < -1 || c.partition_size < -1 || !scale_ok(c.sm_scale)) return PKV_ERR_SHAPE;
     if (c.partition_size > 0 && c.partition_size % c.block_size) return PKV_ERR_SHAPE;
     // bf16 partitions hold whole 16-token tiles
-    if (c.dtype == PKV_BF16 && c.partition_size % 16) return PKV_ERR_SHAPE;
+    if (c.dtype == PKV_BF16 && c.partition_size > 0 && c.partition_size % 16) return PKV_ERR_SHAPE;
     if ((long long)c.max_seqlen_k > (long long)c.mbps * c.block_size) return PKV_ERR_SHAPE;
     if (c.B == 0) return PKV_OK;
     if (!c.out || !c.q || !c.block_table || !c.cache_seqlens) return PKV_ERR_NULL;
@@ -241,10 +255,16 @@ size_t decode_workspace_need(const DecodeCall &c) {
 pkv_status decode_launch(const DecodeCall &c, void *workspace) {
     hipStream_t s = (hipStream_t)c.stream;
     if (use_stream(c.dtype, c.B, c.partition_size, c.max_seqlen_k)) {
-        // one launch: the balanced stream with the merge fused into it
         StreamArgs a = stream_args(c.q, c.k_cache, c.v_cache, c.block_table, c.cache_seqlens,
                                    c.B, c.Hq, c.Hkv, c.D, c.block_size, c.mbps, c.sm_scale,
                                    c.window_left, c.alibi, workspace);
+        if (c.partition_size == 0) {
+            // stage launch (pieces, lse, tile prefix sums), then the merge launch
+            const pkv_status st = launch_decode_stream_bf16(a, s);
+            if (st != PKV_OK) return st;
+            return launch_finish(c.out, c.lse, c.sink, c.B, c.Hq, c.Hkv, c.D, workspace, s);
+        }
+        // one launch: the merge fused in, by the last wave to finish each sequence
         const StreamLayout lay = stream_layout(c.B, c.Hq, c.Hkv, c.D);
         a.counters = (uint64_t *)((char *)workspace + lay.counters);
         a.out = c.out; a.lse = c.lse; a.sink = c.sink;
@@ -386,11 +406,11 @@ pkv_status pkv_reshape_and_cache_rope(const void *key, const void *value, void *
 size_t pkv_paged_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_dim,
                                         int32_t max_seqlen_k, int32_t partition_size)
 {
-    if (B < 0 || num_q_heads <= 0 || max_seqlen_k < 0 || partition_size < 0) return (size_t)-1;
+    if (B < 0 || num_q_heads <= 0 || max_seqlen_k < 0 || partition_size < -1) return (size_t)-1;
     if (head_dim != 64 && head_dim != 128) return (size_t)-1;
     if (B == 0) return 0;
     size_t need = 0;
-    if (B <= kStreamMaxB && max_seqlen_k > 0 && partition_size == 0) {
+    if (B <= kStreamMaxB && max_seqlen_k > 0 && partition_size <= 0) {
         // the balanced bf16 schedule, for whichever GQA grouping the call has
         for (int hu = 1; hu <= 4; hu *= 2)
             if (num_q_heads % hu == 0)
@@ -534,13 +554,8 @@ pkv_status pkv_paged_decode_finish(void *out, float *lse, const float *sink, int
     const StreamLayout lay = stream_layout(B, num_q_heads, num_kv_heads, head_dim);
     if (!workspace || workspace_bytes < lay.total || ((uintptr_t)workspace & 255u))
         return PKV_ERR_WORKSPACE;
-    MergeArgs m{};
-    m.out = out; m.lse = lse;
-    m.part_out = (const float *)((const char *)workspace + lay.part_out);
-    m.part_lse = (const float *)((const char *)workspace + lay.part_lse);
-    m.cum = (const int32_t *)((const char *)workspace + lay.cum);
-    m.sink = sink; m.B = B; m.Hq = num_q_heads; m.D = head_dim; m.stream = 1; m.dtype = dtype;
-    return launch_merge(m, (hipStream_t)stream);
+    return launch_finish(out, lse, sink, B, num_q_heads, num_kv_heads, head_dim, workspace,
+                         (hipStream_t)stream);
 }
 
 pkv_status pkv_paged_decode_partitions(float *part_out, float *part_lse, const void *q,

@@ -149,11 +149,9 @@ struct MergeArgs {
     float *lse;
     const float *part_out;
     const float *part_lse;
-    const int32_t *seqlens;      // partition mode
-    const int32_t *cum;          // stream mode: [B + 2] from decode_stream_kernel
+    const int32_t *seqlens;
     const float *sink;
     int32_t B, Hq, D, part_size, nparts;
-    int32_t stream;              // 1: slots of the balanced schedule
     int32_t dtype;
 };
 
@@ -253,6 +251,9 @@ int decode_heads_per_unit(int G);
 pkv_status launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);
 pkv_status launch_decode_stream_bf16(const StreamArgs &a, hipStream_t stream);
 pkv_status launch_merge(const MergeArgs &a, hipStream_t stream);
+// Merge of the balanced schedule's pieces written by a stage launch (mode 0):
+// reads part_out, part_lse, cum_out; writes out, lse; sink optional.
+pkv_status launch_stream_merge(const StreamArgs &a, hipStream_t stream);
 // Vertical + slash block lists (pkv_vertical_slash_blocks).
 struct VerticalSlashArgs {
     int32_t *block_count;        // [B, H, NM]

@@ -86,6 +86,7 @@ __device__ __forceinline__ float bcast_head(float x, int hh) {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // The per-wave LDS buffer of the P.V step: 16 token rows of V (head_dim bf16
 // plus 16 bytes of padding, so that the lanes' 16-byte row writes spread over
@@ -455,6 +456,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const float *bas
                                              kBufferWord3);
 }
 
+// Global -> LDS copy of one 4-byte word per lane, lane L's word landing at
+// LDS address dst + 4 L (dst wave-uniform), written as an instruction so that
+// the compiler does not track it.  The stream's block-id batches travel this
+// way: a batch kept in a VGPR whose load is still in flight made the compiler
+// wait for every outstanding load (vmcnt 0, the whole K/V ring) on the path
+// that joins the batch switch, which every tile takes.  The copy of batch
+// n + 1 is issued at the switch to batch n and read 64 tiles later; vector
+// memory operations complete in issue order, and the ring's waits on the
+// tiles in between have retired it by then.  These kernels use m0 nowhere
+// else.
+__device__ __forceinline__ void copy4_to_lds(const int32_t *src, uint32_t dst) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(src), "s"(dst) : "memory", "m0");
+}
+
+__device__ __forceinline__ float readfirstlane_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
 // bf16 image of a row of E floats.
 template <int E>
 __device__ __forceinline__ void store_row_bf16(uint16_t *p, const float (&x)[E]) {
@@ -477,9 +497,12 @@ __device__ __forceinline__ void store_row_bf16(uint16_t *p, const float (&x)[E])
 // formula is the one of merge.hip (vLLM attention.py page, the reduction
 // step of single_query_cached_kv_attention; FlashInfer sink page for the
 // sink term), folded in slot order with a running maximum, so the result
-// does not depend on which wave runs it.
-template <int D, int HU>
+// does not depend on which wave runs it.  COHERENT: the pieces were written
+// in this launch, by waves on other XCDs (device-coherent loads); otherwise
+// by an earlier launch.
+template <int D, int HU, bool COHERENT = true>
 __device__ void stream_merge_wave(const StreamArgs &a, int b, int h0, int s0, int nb) {
+    constexpr int kPolicy = COHERENT ? kSc1 : 0;
     constexpr int E = HU * D / 64;                // floats of the head rows per lane
     const int lane = threadIdx.x & 63;
     const int hh = lane * E / D, d = lane * E % D;
@@ -496,7 +519,7 @@ __device__ void stream_merge_wave(const StreamArgs &a, int b, int h0, int s0, in
             const __amdgpu_buffer_rsrc_t rl = coherent_rsrc(a.part_lse + row0, HU * 4);
             const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(a.part_out + row0 * D, HU * D * 4);
             l[u] = __builtin_bit_cast(float,
-                                      __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * hh, 0, kSc1));
+                                      __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * hh, 0, kPolicy));
             const int off = 4 * (hh * D + d);
             // (whole-vector bit casts: a bit cast of one vector element
             // reads element 0 with this compiler)
@@ -504,18 +527,18 @@ __device__ void stream_merge_wave(const StreamArgs &a, int b, int h0, int s0, in
 #pragma unroll
                 for (int c = 0; c < E / 4; ++c) {
                     const f32x4 v = __builtin_bit_cast(
-                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off + 16 * c, 0, kSc1));
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off + 16 * c, 0, kPolicy));
 #pragma unroll
                     for (int e = 0; e < 4; ++e) x[u][4 * c + e] = v[e];
                 }
             } else if constexpr (E == 2) {
                 const f32x2 v =
-                    __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(ro, off, 0, kSc1));
+                    __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(ro, off, 0, kPolicy));
                 x[u][0] = v[0];
                 x[u][1] = v[1];
             } else {
                 x[u][0] = __builtin_bit_cast(float,
-                                             __builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, kSc1));
+                                             __builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, kPolicy));
             }
         }
 #pragma unroll
@@ -569,6 +592,9 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(Stream
                                                          [PARTS ? kStage * HU * D : 1];
     __shared__ float s_stage_lse[PARTS ? kStreamWaves : 1][PARTS ? kStage * HU : 1];
     __shared__ __attribute__((aligned(16))) char s_vt[kStreamWaves][vt_bytes<D>()];
+    // block-id batches 1, 2, ... of each wave, alternating between two slots
+    // (BS8: two more for the second block of each tile)
+    __shared__ int32_t s_blk[kStreamWaves][BS8 ? 4 : 2][64];
 
     const int tid = threadIdx.x;
     const int wave = readfirstlane(tid >> 6);
@@ -584,6 +610,12 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(Stream
     const int h0 = hg * HU;
     const int g = h0 / a.G;
 
+    // the sink logits of this wave's heads (log2 units), read once here: a
+    // load at a sequence's end inside the stream waited for the whole ring
+    float sig_h[HU];
+#pragma unroll
+    for (int hh = 0; hh < HU; ++hh)
+        sig_h[hh] = FUSED && a.sink ? readfirstlane_f(a.sink[h0 + hh] * kLog2e) : -INFINITY;
     stream_prefix_tiles<NT>(a.seqlens, APPEND ? 1 : 0, a.B, a.window_left, s_cum, s_part, s_len);
     const int T = s_cum[a.B];
     const int chunk = stream_chunk(T, a.K);
@@ -697,13 +729,17 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(Stream
     // the block of tile xb + i.  A tile's block id is then a lane read, not a
     // dependent memory load per tile queued behind the K/V stream (that
     // dependency, not bandwidth, limited short-context decode).  The first
-    // batch is read before any tile load; later ones 64 tiles ahead.
+    // batch is read into a VGPR before any tile load; each later one is
+    // copied to LDS 64 tiles ahead (copy4_to_lds) and read from there.
     const int x_end = x0 + n;
-    // (second: BS8, the block of the tile's rows 8..15, which is its first
-    // block when they lie past the sequence)
-    auto gather = [&](int xs, bool second = false) {
+    // Address of the block-table entry of tile xs + lane (second: BS8, the
+    // block of the tile's rows 8..15, which is its first block when they lie
+    // past the sequence); lanes past the range get entry 0, which exists
+    // (the kernel runs only with B >= 1 and max_blocks_per_seq >= 1) and
+    // whose value is never used.
+    auto gather_ptr = [&](int xs, bool second = false) {
         const int x = xs + lane;
-        int v = 0;
+        const int32_t *p = a.block_table;
         if (x < x_end) {
             int lo = 0, hi = a.B;                 // s_cum[lo] <= x < s_cum[hi]
             while (hi - lo > 1) {
@@ -711,10 +747,16 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(Stream
                 if (s_cum[mid] <= x) lo = mid; else hi = mid;
             }
             const int t = (stream_lo(s_len[lo], a.window_left) & ~15) + 16 * (x - s_cum[lo]);
-            v = second ? a.block_table[(size_t)lo * a.mbps + (min(t + 8, s_len[lo] - 1) >> 3)]
-                       : a.block_table[(size_t)lo * a.mbps + (t >> a.bs_log2)];
+            p += (size_t)lo * a.mbps + (second ? (min(t + 8, s_len[lo] - 1) >> 3) : (t >> a.bs_log2));
         }
-        return v;
+        return p;
+    };
+    auto copy_batch = [&](int xs, int slot) {
+        copy4_to_lds(gather_ptr(xs),
+                     (uint32_t)(uintptr_t)(const lds_void_t *)&s_blk[wave][slot][0]);
+        if constexpr (BS8)
+            copy4_to_lds(gather_ptr(xs, true),
+                         (uint32_t)(uintptr_t)(const lds_void_t *)&s_blk[wave][2 + slot][0]);
     };
     // Append with rotary embedding: this wave's q rows (its head group, every
     // sequence its range meets) rotated by the new token's position into
@@ -741,13 +783,10 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(Stream
             qsrc = a.q_rot;
         }
     }
-    int xb = x0, blk_batch = gather(x0), blk_ahead = 0;
-    if (x0 + 64 < x_end) blk_ahead = gather(x0 + 64);
-    [[maybe_unused]] int blk_batch1 = 0, blk_ahead1 = 0;
-    if constexpr (BS8) {
-        blk_batch1 = gather(x0, true);
-        if (x0 + 64 < x_end) blk_ahead1 = gather(x0 + 64, true);
-    }
+    int xb = x0, nbat = 0, blk_batch = *gather_ptr(x0);
+    [[maybe_unused]] int blk_batch1 = 0;
+    if constexpr (BS8) blk_batch1 = *gather_ptr(x0, true);
+    if (x0 + 64 < x_end) copy_batch(x0 + 64, 1);
 
     // Q of the first two sequences of the range, loaded before the first
     // tiles and waited for on their own after the tiles are issued, so that
@@ -771,14 +810,15 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(Stream
     __builtin_amdgcn_sched_barrier(0);
     int blk1_at = 0;                              // BS8: block_at's second block
     auto block_at = [&]() {
-        if (x_ld - xb >= 64) {                    // next batch (read 64 tiles ago)
+        if (x_ld - xb >= 64) {                    // next batch (copied 64 tiles ago)
             xb += 64;
-            blk_batch = blk_ahead;
-            if (xb + 64 < x_end) blk_ahead = gather(xb + 64);
-            if constexpr (BS8) {
-                blk_batch1 = blk_ahead1;
-                if (xb + 64 < x_end) blk_ahead1 = gather(xb + 64, true);
-            }
+            const int sl = ++nbat & 1;
+            blk_batch = s_blk[wave][sl][lane];
+            if constexpr (BS8) blk_batch1 = s_blk[wave][2 + sl][lane];
+            // the reads complete here, in the rare branch; then the other
+            // slot (read at the previous switch) takes the batch after
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+            if (xb + 64 < x_end) copy_batch(xb + 64, sl ^ 1);
         }
         if constexpr (BS8) blk1_at = __builtin_amdgcn_readlane(blk_batch1, x_ld - xb);
         return __builtin_amdgcn_readlane(blk_batch, x_ld - xb);
@@ -876,7 +916,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(Stream
                 const int h = h0 + hh;
                 const float lh = __shfl(lsum, hh, 64);
                 const float mh = __shfl(w.m_lane, hh, 64);
-                const float sig = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+                const float sig = sig_h[hh];
                 const float Mt = fmaxf(lh > 0.f ? mh : kNoMax, sig);
                 const float sc = fast_exp2(mh - Mt);
                 const float Lt = fmaf(lh, sc, fast_exp2(sig - Mt));
@@ -1090,6 +1130,22 @@ __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(Stream
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+}
+
+// Second launch of the two-launch balanced decode: one wave per (sequence,
+// HU heads) merges that sequence's pieces, which the stage launch wrote to
+// the slots the tile prefix sums it left in cum_out ([B + 2]: the sums, then
+// the per-wave chunk) place them in.
+template <int D, int HU>
+__global__ __launch_bounds__(256) void stream_merge_kernel(StreamArgs a)
+{
+    const int w = readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
+    const int NHG = a.Hq / HU;
+    if (w >= a.B * NHG) return;
+    const int b = w / NHG, h0 = (w % NHG) * HU;
+    const int c0 = a.cum_out[b], c1 = a.cum_out[b + 1], chunk = a.cum_out[a.B + 1];
+    const int nb = c1 > c0 ? (c1 - 1) / chunk - c0 / chunk + 1 : 0;
+    stream_merge_wave<D, HU, false>(a, b, h0, c0 / chunk + b, nb);
 }
 
 template <int D, int HU, bool BS8>

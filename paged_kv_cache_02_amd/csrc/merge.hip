@@ -29,24 +29,11 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bh = blockIdx.x;
     const int b = bh / a.Hq, h = bh % a.Hq;
-    // partial results of (b, h): n entries, entry p at element p * stride
-    int n;
-    size_t pl0, pls, po0, pos;
-    if (a.stream) {
-        // slots gw + b for the waves gw whose tile range meets sequence b
-        const int c0 = a.cum[b], c1 = a.cum[b + 1], chunk = a.cum[a.B + 1];
-        const int g0 = c0 / chunk;
-        n = c1 > c0 ? (c1 - 1) / chunk - g0 + 1 : 0;
-        pl0 = ((size_t)(g0 + b)) * a.Hq + h;
-        pls = a.Hq;
-    } else {
-        const int L = a.seqlens[b];
-        n = (L + a.part_size - 1) / a.part_size;
-        pl0 = (size_t)bh * a.nparts;
-        pls = 1;
-    }
-    po0 = pl0 * D;
-    pos = pls * D;
+    // partial results of (b, h): n partitions, partition p at row bh * nparts + p
+    const int L = a.seqlens[b];
+    const int n = (L + a.part_size - 1) / a.part_size;
+    const size_t pl0 = (size_t)bh * a.nparts, pls = 1;
+    const size_t po0 = pl0 * D, pos = pls * D;
     const float *pl = a.part_lse + pl0;
     const float *po_base = a.part_out + po0;
     const float sig = a.sink ? a.sink[h] * kLog2e : -INFINITY;

@@ -295,6 +295,9 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, sm_scale: floa
                  alibi_slopes=None):
     """out [B,Hq,D] for q [B,Hq,D] over k/v_cache [NB,bs,Hkv,D].
 
+    partition_size: 0 the balanced schedule (bf16: a stage launch and a merge
+    launch), -1 the same in one launch with the merge fused in, > 0 fixed
+    partitions of that many keys (see pkv_paged_decode).
     `workspace`: at least decode_workspace_bytes(...) bytes, reusable across
     calls (see pkv_paged_decode); without one, a buffer is allocated for this
     call."""

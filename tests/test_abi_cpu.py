@@ -50,6 +50,10 @@ def test_workspace_sizes():
     a = pkv.decode_workspace_bytes(64, 32, 128, 4096)
     b = pkv.decode_workspace_bytes(64, 32, 128, 100)
     assert a == b and a > counters and a % 256 == 0
+    # its one-launch form (-1) uses the same workspace; nothing below -1
+    assert pkv.decode_workspace_bytes(64, 32, 128, 4096, -1) == a
+    with pytest.raises(pkv.PkvError):
+        pkv.decode_workspace_bytes(64, 32, 128, 4096, -2)
     # the size covers every kv-head count: grouping 4 heads per unit needs the most slots
     assert pkv.decode_workspace_bytes(64, 30, 128, 100) > 0
     assert pkv.decode_workspace_bytes(0, 32, 128, 100) == 0
@@ -86,6 +90,7 @@ def decode_call(**over):
     (dict(dt=7), pkv.PKV_ERR_UNSUPPORTED),
     (dict(window=-2), pkv.PKV_ERR_SHAPE),
     (dict(part=24), pkv.PKV_ERR_SHAPE),
+    (dict(part=-2), pkv.PKV_ERR_SHAPE),               # -1 (one launch) is the lowest
     (dict(max_seqlen_k=65, MB=4), pkv.PKV_ERR_SHAPE),
     (dict(B=-1), pkv.PKV_ERR_SHAPE),
     (dict(scale=0.0), pkv.PKV_ERR_SHAPE),            # sm_scale must be positive and finite

@@ -91,6 +91,10 @@ CASES = [
     # block size 8: every 16-token tile spans two blocks
     ([0, 1, 7, 8, 9, 15, 16, 17, 100, 333], 8, 2, 128, 8, True, -1),
     ([40, 1500, 63], 16, 4, 64, 8, False, 20),
+    # head counts that are not a multiple of what one merge wave takes (2 heads
+    # of 128 dims, 4 of 64): the merge falls back to fewer heads per wave
+    ([3, 90, 400, 2000], 3, 1, 128, 16, True, -1),
+    ([10, 200, 1300], 6, 2, 64, 16, False, -1),
 ]
 
 
@@ -102,7 +106,7 @@ def test_decode_vs_oracle(case, dtype):
     c = synth.decode_case(11 + len(lengths), lengths, Hq, Hkv, D, bs, dtype, with_sink=sink,
                           window_left=window, poison=True)
     o, l = oracle_decode(c)
-    for P in (0, max(16, bs), 2 * max(16, bs), 256 if 256 % bs == 0 else bs, 512):
+    for P in (0, -1, max(16, bs), 2 * max(16, bs), 256 if 256 % bs == 0 else bs, 512):
         out, lse = run_decode(c, partition_size=P)
         assert_close(out, o, dtype, f"out P={P}")
         assert_close(lse, l, dtype, f"lse P={P}", lse=True)
@@ -117,12 +121,17 @@ def test_decode_deterministic_and_permutation_invariant():
                           shuffle=False, poison=True)
     # same logical keys, different physical pools
     assert torch.equal(a.q, b.q)
-    for P in (0, 256):
+    for P in (0, -1, 256):
         o1, l1 = run_decode(a, P)
         o2, l2 = run_decode(a, P)
         o3, l3 = run_decode(b, P)
         assert torch.equal(o1, o2) and torch.equal(l1, l2), "run-to-run"
         assert torch.equal(o1, o3) and torch.equal(l1, l3), "block permutation"
+    # the balanced schedule folds the same pieces in the same order whether
+    # the merge is its own launch (0) or fused into the stream (-1)
+    o0, l0 = run_decode(a, 0)
+    o1, l1 = run_decode(a, -1)
+    assert torch.equal(o0, o1) and torch.equal(l0, l1), "two launches vs one"
 
 
 def _decode_poisoned(c, P):
@@ -140,21 +149,23 @@ def _decode_poisoned(c, P):
 def test_config2_full_size():
     """bf16 decode at full size (64 seqs, 512..4096 keys, 32/8 heads, D 128,
     bs 16), in the launch configuration the benchmark times (the balanced
-    schedule with the merge fused); every element against the oracle, the
-    output poisoned with NaN first."""
+    schedule, stage and merge launches), and in one launch with the merge
+    fused; every element against the oracle, the output poisoned with NaN
+    first."""
     banner("config2 full size")
     c = synth.config2_decode(poison=True, spare_blocks=4)
-    out, lse = _decode_poisoned(c, 0)
     o, l = oracle_decode(c)
-    assert_close(out, o, torch.bfloat16, "config2 out")
-    assert_close(lse, l, torch.bfloat16, "config2 lse", lse=True)
+    for P in (0, -1):
+        out, lse = _decode_poisoned(c, P)
+        assert_close(out, o, torch.bfloat16, f"config2 P={P} out")
+        assert_close(lse, l, torch.bfloat16, f"config2 P={P} lse", lse=True)
 
 
 @pytest.mark.slow
 def test_config5_long_context():
     """Long-context split decode at full size: 16 x 131072 keys, bs 64, sink;
     partitions of 512 merged by log-sum-exp (the configured split), and the
-    automatic one-launch balanced schedule; every element of out and lse
+    automatic balanced schedule (two launches); every element of out and lse
     against the oracle.  The partition stage alone is compared too: its
     part_out / part_lse against the oracle's partition mode."""
     banner("config5 full size (generating 8.6 GB of K/V)")
@@ -263,8 +274,8 @@ def test_fused_merge_workspace_reuse():
         lse = torch.empty(c.B, c.Hq, dtype=torch.float32, device="cuda")
         out = pkv.paged_decode(dev(c.q), dev(c.k_cache), dev(c.v_cache), dev(c.block_table),
                                dev(c.cache_seqlens), c.sm_scale, sink=dev(c.sink),
-                               window_left=c.window_left, max_seqlen_k=c.max_seqlen_k, lse=lse,
-                               workspace=ws)
+                               window_left=c.window_left, partition_size=-1,
+                               max_seqlen_k=c.max_seqlen_k, lse=lse, workspace=ws)
         torch.cuda.synchronize()
         counters = ws[:4096 * c.Hq * 8].view(torch.int64)
         assert int((counters != 0).sum()) == 0, f"call {rep}: counters left non-zero"
@@ -279,10 +290,11 @@ def test_fused_merge_workspace_reuse():
 
 def test_dirty_workspace_still_correct():
     """A workspace left dirty must not change the result: (1) fixed partitions,
-    then the balanced schedule, on one buffer never re-zeroed (the partition
-    results sit after the counter region); (2) counters holding stale counts
-    of another epoch (what an interrupted call leaves) and NaN everywhere
-    else.  Both balanced calls match the oracle, and leave the counters zero."""
+    then the balanced schedule in both forms, on one buffer never re-zeroed
+    (the partition results sit after the counter region); (2) counters
+    holding stale counts of another epoch (what an interrupted call leaves)
+    and NaN everywhere else, under the one-launch form that uses them.  Every
+    call matches the oracle; the one-launch calls leave the counters zero."""
     banner("dirty workspace")
     from paged_kv_cache_02_amd import pkv
     c = synth.decode_case(43, [5, 700, 1500, 2100, 16, 3000, 1], 32, 8, 128, 16, torch.bfloat16,
@@ -292,7 +304,7 @@ def test_dirty_workspace_still_correct():
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     args = (dev(c.q), dev(c.k_cache), dev(c.v_cache), dev(c.block_table), dev(c.cache_seqlens),
             c.sm_scale)
-    for P in (256, 0):
+    for P in (256, 0, -1):
         lse = torch.empty(c.B, c.Hq, dtype=torch.float32, device="cuda")
         out = pkv.paged_decode(*args, sink=dev(c.sink), partition_size=P,
                                max_seqlen_k=c.max_seqlen_k, lse=lse, workspace=ws)
@@ -304,8 +316,8 @@ def test_dirty_workspace_still_correct():
     stale = (0x5EEDF00D << 32) | 3
     ws[:nc * 8].view(torch.int64)[:] = stale
     lse = torch.empty(c.B, c.Hq, dtype=torch.float32, device="cuda")
-    out = pkv.paged_decode(*args, sink=dev(c.sink), max_seqlen_k=c.max_seqlen_k, lse=lse,
-                           workspace=ws)
+    out = pkv.paged_decode(*args, sink=dev(c.sink), partition_size=-1,
+                           max_seqlen_k=c.max_seqlen_k, lse=lse, workspace=ws)
     torch.cuda.synchronize()
     assert_close(out, o, torch.bfloat16, "stale counters: out")
     assert_close(lse, l, torch.bfloat16, "stale counters: lse", lse=True)
@@ -351,7 +363,7 @@ def test_decode_many_short_sequences(D, Hq, Hkv, window, B, bs):
     c = synth.decode_case(62, lengths, Hq, Hkv, D, bs, torch.bfloat16, with_sink=True,
                           window_left=window, poison=True)
     o, l = oracle_decode(c)
-    out, lse = run_decode(c)
+    out, lse = run_decode(c, partition_size=-1)
     assert_close(out, o, torch.bfloat16, "one launch out")
     assert_close(lse, l, torch.bfloat16, "one launch lse", lse=True)
     ws = torch.empty(pkv.decode_workspace_bytes(c.B, Hq, D, c.max_seqlen_k), dtype=torch.uint8, device="cuda")
