@@ -637,9 +637,14 @@ __global__ __launch_bounds__(256, (RUN && D == 128) ? 1 : 2) void prefill_bf16_k
             issue(t_begin, buf);
             if (a.rope) rotate_q();
             if constexpr (ROPEK) load_ktab(t_begin);
-            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-            __syncthreads();
         }
+        // Q (and the first tile) landed, on both paths: the compiler then
+        // knows Q's registers are complete inside the loop.  With the wait on
+        // one path only it waited for Q again before each tile's first
+        // MFMAs, with a count that ignores the copies it does not track, so
+        // each tile waited for the next tile's copies.
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        if (ntiles > 0) __syncthreads();
         for (int it = 0; it < ntiles; ++it) {
             const int t0 = t_begin + it * BN;
             if constexpr (ROPEK) {
