@@ -220,6 +220,8 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 # source files of each kernel whose PMC traffic is recorded in the summary
 KERNEL_SOURCES = {
     "decode_c2": ("decode_impl.h", "decode.hip", "decode.h", "common.h", "rope.h"),
+    "merge_c2": ("decode_impl.h", "decode.hip", "decode.h", "common.h", "rope.h"),
+    "decode_c2_one_launch": ("decode_impl.h", "decode.hip", "decode.h", "common.h", "rope.h"),
     "prefill_c3": ("prefill.hip", "tile.h", "decode.h", "common.h"),
     "prefill_c4": ("prefill.hip", "tile.h", "decode.h", "common.h"),
     "reshape_c3": ("cache.hip", "common.h"),
