@@ -227,6 +227,57 @@ def model_decode_stream(lens, Hq, Hkv, bs, mbps, window=-1, append=False):
     return T
 
 
+def model_block_batches(n, batch=64, plant_slot=False):
+    """A wave's block-id batches over its n tiles: batch 0 is loaded into a
+    register; batch k >= 1 is copied to LDS slot k % 2 when the wave switches
+    to batch k - 1 (batch 1: before the first tile) and read from that slot
+    when it switches to batch k.  Checks that every batch read was copied
+    into the slot it is read from, at least one batch (64 tiles) earlier,
+    and that no copy lands in a slot between the copy and the read of the
+    batch it holds.  Returns the number of copies.  plant_slot: copy each
+    batch into the slot the wave is reading (a planted mistake)."""
+    nb = (n + batch - 1) // batch
+    copies, reads = {}, {}                  # batch -> (tile index of the event, slot)
+    if n > batch:
+        copies[1] = (-1, 1)
+    for k in range(1, nb):
+        reads[k] = (batch * k, k % 2)
+        if batch * (k + 1) < n:
+            copies[k + 1] = (batch * k, (k if plant_slot else k + 1) % 2)
+    for k, (tr, sr) in reads.items():
+        assert k in copies, f"batch {k} read but never copied"
+        tc, sc = copies[k]
+        assert sc == sr, "batch read from another slot than it was copied to"
+        assert tr - tc >= batch or tc == -1, "batch read less than one batch after its copy"
+        for j, (tj, sj) in copies.items():
+            assert not (j != k and sj == sr and tc < tj <= tr), "slot overwritten before its read"
+    assert set(copies) == set(reads)
+    return len(copies)
+
+
+def model_stream_merge(B, Hq, D):
+    """The merge launch of the two-launch balanced decode: one wave per
+    (sequence, HU heads), HU = 256 / D halved until it divides Hq; every
+    (sequence, head) row merged by exactly one wave, 16 bytes (or fewer, with
+    fewer heads) of each head row per lane."""
+    HU = 256 // D
+    while Hq % HU:
+        HU //= 2
+    NHG = Hq // HU
+    waves = B * NHG
+    grid = (waves + 3) // 4
+    seen = np.zeros((B, Hq), dtype=np.int64)
+    for w in range(grid * 4):
+        if w >= waves:
+            continue
+        b, h0 = w // NHG, (w % NHG) * HU
+        assert 0 <= b < B and 0 <= h0 and h0 + HU <= Hq
+        seen[b, h0:h0 + HU] += 1
+    assert (seen == 1).all(), "a row merged twice or never"
+    E = HU * D // 64
+    assert E in (1, 2, 4) and 64 * E == HU * D
+
+
 def model_decode_stream_parts(lens, Hq, Hkv, bs, P, max_parts, window=-1):
     """The balanced schedule in partition mode: each wave's range snapped up to
     partition starts.  Every tile belongs to exactly one range, every partition
@@ -515,6 +566,16 @@ def test_decode_stream_mapping_in_bounds():
         mbps = (max(max(lengths), 1) + 1 + bs - 1) // bs
         model_decode_stream(lengths, Hq, Hkv, bs, mbps, window)
         model_decode_stream(lengths, Hq, Hkv, bs, mbps, window, append=True)
+        for D in (64, 128):
+            model_stream_merge(len(lengths), Hq, D)
+
+
+def test_block_batches():
+    """The LDS double buffer of block-id batches, for every range length up to
+    a few batches past the boundaries, and the C5-sized ranges."""
+    for n in list(range(0, 400)) + [1024, 1025, 2047, 131072 // 16 // 128 * 16]:
+        copies = model_block_batches(n)
+        assert copies == max(0, (n + 63) // 64 - 1)
 
 
 def test_decode_partition_mapping_in_bounds():
@@ -538,6 +599,9 @@ def test_models_catch_a_planted_mistake():
     with pytest.raises(AssertionError):
         # a block table one block short for the appended token
         model_decode_stream([16, 31], 8, 2, 16, mbps=1, append=True)
+    with pytest.raises(AssertionError):
+        # block ids copied into the LDS slot the wave is reading from
+        model_block_batches(200, plant_slot=True)
 
 
 # ---------------------------------------------------------------------------
