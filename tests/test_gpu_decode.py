@@ -426,3 +426,69 @@ def test_prepared_launches_match_direct_calls():
     pkv.prepare(pkv.varlen_prefill, *args, out=out, **kw)()
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), want.view(torch.int16))
+
+
+def _repage(kc, bt, lengths, bs, seed):
+    """The same logical keys in a pool of block size bs with a shuffled
+    block table (built on the GPU from a paged cache kc / table bt)."""
+    bs0 = kc.shape[1]
+    rows = []
+    for b, L in enumerate(lengths):
+        nb0 = (L + bs0 - 1) // bs0
+        rows.append(kc[bt[b, :nb0].long()].reshape(nb0 * bs0, *kc.shape[2:])[:L])
+    nbs = [(L + bs - 1) // bs for L in lengths]
+    perm = torch.from_numpy(np.random.default_rng(seed).permutation(sum(nbs))).cuda()
+    pool = torch.zeros((sum(nbs), bs) + tuple(kc.shape[2:]), dtype=kc.dtype, device="cuda")
+    table = torch.zeros((len(lengths), max(nbs)), dtype=torch.int32, device="cuda")
+    o = 0
+    for b, L in enumerate(lengths):
+        ids = perm[o:o + nbs[b]]
+        flat = torch.zeros((nbs[b] * bs,) + tuple(kc.shape[2:]), dtype=kc.dtype, device="cuda")
+        flat[:L] = rows[b]
+        pool[ids] = flat.reshape(nbs[b], bs, *kc.shape[2:])
+        table[b, :nbs[b]] = ids.int()
+        o += nbs[b]
+    return pool, table
+
+
+def test_long_ranges_block_sizes_bitwise():
+    """Ranges of more than two 64-tile batches per wave (about 136 tiles), so
+    each wave reads block ids from both LDS slots of its batch double buffer:
+    the same logical cache paged with block sizes 8, 16 and 64 gives the same
+    bits in every decode form (the schedule's tiles are 16 tokens whatever
+    the block size), and two sequences match the oracle."""
+    banner("long ranges, block sizes 8 / 16 / 64")
+    from paged_kv_cache_02_amd import pkv
+    lengths = [70001, 69000, 71234, 68500]
+    c = synth.decode_case(71, lengths, 32, 8, 128, 16, torch.bfloat16, with_sink=True,
+                          poison=False, spare_blocks=0)
+    q, kc, vc, bt, sl = dev(c.q), dev(c.k_cache), dev(c.v_cache), dev(c.block_table), \
+        dev(c.cache_seqlens)
+    sink = dev(c.sink)
+    results = {}
+    for bs in (16, 8, 64):
+        if bs == 16:
+            k2, v2, t2 = kc, vc, bt
+        else:
+            k2, t2 = _repage(kc, bt, lengths, bs, 72 + bs)
+            v2, _ = _repage(vc, bt, lengths, bs, 72 + bs)    # same seed: the same table
+        for P in (0, -1, 512):
+            lse = torch.empty(c.B, c.Hq, dtype=torch.float32, device="cuda")
+            out = pkv.paged_decode(q, k2, v2, t2, sl, c.sm_scale, sink=sink, partition_size=P,
+                                   max_seqlen_k=max(lengths), lse=lse)
+            torch.cuda.synchronize()
+            results[(bs, P)] = (out, lse)
+        del k2, v2
+    ref_out, ref_lse = results[(16, 0)]
+    for key, (out, lse) in results.items():
+        if key[1] == 512:
+            continue            # fixed partitions fold in another order
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"bs/P {key} differs"
+    for bs in (8, 64):
+        assert torch.equal(results[(bs, 512)][0], results[(16, 512)][0]), f"bs {bs} P 512 differs"
+    # two sequences against the oracle
+    sub = synth.DecodeCase(c.q[:2], c.k_cache, c.v_cache, c.block_table[:2],
+                           c.cache_seqlens[:2], c.sink, c.block_size, c.sm_scale, c.window_left)
+    o, l = oracle_decode(sub)
+    assert_close(ref_out[:2], o, torch.bfloat16, "long ranges out")
+    assert_close(ref_lse[:2], l, torch.bfloat16, "long ranges lse", lse=True)
