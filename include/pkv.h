@@ -306,7 +306,7 @@ pkv_status pkv_paged_decode_noalloc(void *out, float *lse, const void *q, const 
  * block_table[b][L / block_size] * block_size + L % block_size), and the
  * query, at position L, attends to keys 0..L (window: L - window_left <= j)
  * with the sink -- exactly pkv_reshape_and_cache of the new rows followed by
- * pkv_paged_decode over cache_seqlens[b] + 1 keys, in one launch.
+ * pkv_paged_decode over cache_seqlens[b] + 1 keys, in one call.
  *
  *   k_new, v_new    [B, num_kv_heads, head_dim], same dtype as the caches
  *   k_cache,        written at the new tokens' slots and nowhere else
@@ -334,8 +334,9 @@ pkv_status pkv_paged_decode_noalloc(void *out, float *lse, const void *q, const 
  *                   reused under the same rules as pkv_paged_decode's
  *                   balanced schedule (B <= 4096); fp32: none (may be NULL).
  * Other arguments as for pkv_paged_decode.  bf16 runs the balanced schedule
- * with the merge fused (the wave that reads a sequence's last tile stores its
- * new row first); fp32 runs one wave per (sequence, head).  Returns
+ * as two launches, like pkv_paged_decode's default: the stage launch (the
+ * wave that reads a sequence's last tile stores its new row first) and the
+ * merge launch; fp32 runs one wave per (sequence, head).  Returns
  * PKV_ERR_SHAPE for B > 4096 in bf16 or when the new token does not fit.
  */
 pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const void *k_new,

@@ -488,13 +488,14 @@ pkv_status pkv_paged_decode_append(void *out, float *lse, const void *q, const v
                                    num_q_heads, num_kv_heads, head_dim, block_size,
                                    max_blocks_per_seq, sm_scale, window_left, alibi_slopes,
                                    workspace);
-        a.counters = (uint64_t *)((char *)workspace + lay.counters);
-        a.out = out; a.lse = lse; a.sink = sink;
         a.k_new = k_new; a.v_new = v_new; a.append = 1;
         a.rope = rope_cos_sin; a.rope_dim = rotary_dim; a.rope_neox = rope_neox != 0;
         a.q_rot = (char *)workspace + lay.q_rot;
         a.mode = kStreamAppend;
-        return launch_decode_stream_bf16(a, s);
+        // the stage launch with the new tokens stored and attended, then the
+        // merge launch over its pieces (prefix sums counting the new tokens)
+        if ((st = launch_decode_stream_bf16(a, s)) != PKV_OK) return st;
+        return launch_finish(out, lse, sink, B, num_q_heads, num_kv_heads, head_dim, workspace, s);
     }
     RowArgs a{};
     a.mode = 0; a.out = out; a.lse = lse; a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;

@@ -32,10 +32,10 @@ struct DecodeArgs {
 // range moves forward through the sequences).
 constexpr int kStreamWaves = 4;
 // What a stream launch computes: per-range pieces for the merge kernel
-// (stage), final outputs with the merge fused in (fused), the same with each
-// sequence's new token appended first (append), or fixed partitions of
-// part_size tokens written to part_out / part_lse, each partition wholly in
-// one wave's range (parts).
+// (stage), final outputs with the merge fused in (fused), the stage's pieces
+// with each sequence's new token appended first (append; the merge kernel
+// follows), or fixed partitions of part_size tokens written to part_out /
+// part_lse, each partition wholly in one wave's range (parts).
 enum { kStreamStage = 0, kStreamFused = 1, kStreamAppend = 2, kStreamParts = 3 };
 constexpr int kStreamMaxB = 4096;
 

@@ -577,7 +577,7 @@ __device__ void stream_merge_wave(const StreamArgs &a, int b, int h0, int s0, in
 template <int D, int HU, int MODE, bool ALIBI, bool BS8>
 __global__ __launch_bounds__(64 * kStreamWaves) void decode_stream_kernel(StreamArgs a)
 {
-    constexpr bool FUSED = MODE == kStreamFused || MODE == kStreamAppend;
+    constexpr bool FUSED = MODE == kStreamFused;
     constexpr bool APPEND = MODE == kStreamAppend;
     constexpr bool PARTS = MODE == kStreamParts;
     constexpr int NT = 64 * kStreamWaves;
