@@ -26,7 +26,7 @@ DECODE = [
 
 
 @pytest.mark.parametrize("case", DECODE, ids=[str(i) for i in range(len(DECODE))])
-@pytest.mark.parametrize("mode", ["auto", "two_launch", "partitions", "fp32"])
+@pytest.mark.parametrize("mode", ["auto", "one_launch", "two_launch", "partitions", "fp32"])
 def test_decode_alibi(case, mode):
     from paged_kv_cache_02_amd import pkv
     lens, Hq, Hkv, D, bs, sink, window = case
@@ -46,7 +46,7 @@ def test_decode_alibi(case, mode):
         pkv.paged_decode_finish(out, ws, Hkv, sink=dev(c.sink), lse=lse)
     else:
         out = pkv.paged_decode(q, kc, vc, bt, sl, c.sm_scale, sink=dev(c.sink), window_left=window,
-                               partition_size=64 if mode == "partitions" else 0,
+                               partition_size={"partitions": 64, "one_launch": -1}.get(mode, 0),
                                max_seqlen_k=msk, lse=lse, alibi_slopes=dev(al))
     torch.cuda.synchronize()
     o, l = oracle.paged_decode(c.q, c.k_cache, c.v_cache, c.block_table, c.cache_seqlens, c.sink,
