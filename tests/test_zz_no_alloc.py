@@ -1,8 +1,9 @@
 """pkv_paged_decode_noalloc (the decode entry point that allocates nothing,
 its workspace a static device array) against pkv_paged_decode with a
 caller-allocated workspace: the same outputs on two calls in a row, the
-second with a smaller batch, in the balanced schedule and with fixed
-partitions; and both against the oracle."""
+second with a smaller batch, in the balanced schedule (two launches, and one
+launch with the merge fused, which counts pieces in the static array) and
+with fixed partitions; and both against the oracle."""
 
 import ctypes
 
@@ -40,7 +41,7 @@ def _with_workspace(c, P):
     return out, lse
 
 
-@pytest.mark.parametrize("P", [0, 256])
+@pytest.mark.parametrize("P", [0, -1, 256])
 def test_noalloc_matches_workspace_entry(P):
     from paged_kv_cache_02_amd import pkv
     big = synth.decode_case(91, np.random.default_rng(91).integers(1, 3000, 48).tolist(), 32, 8,
