@@ -492,3 +492,28 @@ def test_long_ranges_block_sizes_bitwise():
     o, l = oracle_decode(sub)
     assert_close(ref_out[:2], o, torch.bfloat16, "long ranges out")
     assert_close(ref_lse[:2], l, torch.bfloat16, "long ranges lse", lse=True)
+
+
+@pytest.mark.parametrize("P", [0, -1, 64])
+def test_all_sequences_empty(P):
+    """No sequence has a key: with a positive max_seqlen_k the balanced
+    schedule runs with an empty tile list (every wave's range is empty, the
+    merge sees no piece), and with max_seqlen_k 0 no schedule is needed.
+    out is 0 and lse the sink (or -inf), as the oracle gives."""
+    banner(f"all sequences empty P={P}")
+    from paged_kv_cache_02_amd import pkv
+    for with_sink in (True, False):
+        c = synth.decode_case(81, [0, 0, 0, 0, 0], 32, 8, 128, 16, torch.bfloat16,
+                              with_sink=with_sink, poison=True, max_blocks_per_seq=4)
+        o, l = oracle_decode(c)
+        for msk in (64, 0):
+            if msk == 0 and P == 64:
+                continue
+            out = torch.full((c.B, c.Hq, c.D), float("nan"), dtype=c.q.dtype, device="cuda")
+            lse = torch.full((c.B, c.Hq), float("nan"), dtype=torch.float32, device="cuda")
+            pkv.paged_decode(dev(c.q), dev(c.k_cache), dev(c.v_cache), dev(c.block_table),
+                             dev(c.cache_seqlens), c.sm_scale, sink=dev(c.sink),
+                             partition_size=P, max_seqlen_k=msk, out=out, lse=lse)
+            torch.cuda.synchronize()
+            assert_close(out, o, torch.bfloat16, f"empty out msk={msk} sink={with_sink}")
+            assert_close(lse, l, torch.bfloat16, f"empty lse msk={msk} sink={with_sink}", lse=True)
