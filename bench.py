@@ -660,33 +660,45 @@ def _sample(n_units, k, seed):
     return np.sort(np.random.default_rng(seed).choice(n_units, k, replace=False))
 
 
+CPU_MIN_SECONDS = 3.0      # each oracle timing repeats its pass until this much time has run
+
+
+def _repeat_timed(fn):
+    """Run fn() until CPU_MIN_SECONDS have elapsed (at least once, at most 50
+    times); return (mean seconds per pass, passes, fn's last result)."""
+    total, n, res = 0.0, 0, None
+    while n < 50 and (n == 0 or total < CPU_MIN_SECONDS):
+        t0 = time.perf_counter()
+        res = fn()
+        total += time.perf_counter() - t0
+        n += 1
+    return total / n, n, res
+
+
 def oracle_decode_rate(c, units, threads):
     """Time the oracle on the (sequence, head) units of a decode workload (None:
     all); return (seconds, GB/s of the algorithmic bytes those units stand for:
-    each query head's share, 1 / Hq of its sequence's K/V, q and out rows)."""
+    each query head's share, 1 / Hq of its sequence's K/V, q and out rows),
+    with the seconds per pass and the number of passes timed."""
     import oracle  # the CPU-baseline leg is the only bench code that runs the oracle
-    t0 = time.perf_counter()
-    o, _ = oracle.paged_decode(c.q, c.k_cache, c.v_cache, c.block_table, c.cache_seqlens,
-                               c.sink, c.sm_scale, c.window_left, units=units,
-                               nthreads=threads)
-    dt = time.perf_counter() - t0
+    dt, n, (o, _) = _repeat_timed(lambda: oracle.paged_decode(
+        c.q, c.k_cache, c.v_cache, c.block_table, c.cache_seqlens, c.sink, c.sm_scale,
+        c.window_left, units=units, nthreads=threads))
     L = c.cache_seqlens.numpy().astype(np.int64)
     u = np.arange(c.B * c.Hq) if units is None else np.asarray(units)
     b = u // c.Hq
     byts = float(np.sum(L[b] * c.Hkv * c.D * 2 * 2 / c.Hq + 2 * c.D * 2))
-    return dt, byts / dt / 1e9, o
+    return dt, n, byts / dt / 1e9, o
 
 
 def oracle_prefill_rate(c, units, threads):
     """Time the oracle on (token, head) units of a prefill workload (None: all);
-    return (seconds, GFLOP/s of 4 D flops per visible (row, key) pair)."""
+    return (seconds per pass, passes, GFLOP/s of 4 D flops per visible (row, key) pair)."""
     import oracle
-    t0 = time.perf_counter()
-    oracle.varlen_prefill(c.q, c.cu_seqlens_q, c.cu_seqlens_k, c.sink, c.sm_scale, c.Hkv,
-                          k=c.k, v=c.v, k_cache=c.k_cache, v_cache=c.v_cache,
-                          block_table=c.block_table, block_size=c.block_size,
-                          window_left=c.window_left, units=units, nthreads=threads)
-    dt = time.perf_counter() - t0
+    dt, n, _ = _repeat_timed(lambda: oracle.varlen_prefill(
+        c.q, c.cu_seqlens_q, c.cu_seqlens_k, c.sink, c.sm_scale, c.Hkv, k=c.k, v=c.v,
+        k_cache=c.k_cache, v_cache=c.v_cache, block_table=c.block_table,
+        block_size=c.block_size, window_left=c.window_left, units=units, nthreads=threads))
     vis = []
     for Lq, Lk in zip(c.q_lens, c.k_lens):
         pos = np.arange(Lk - Lq, Lk, dtype=np.int64)
@@ -696,7 +708,7 @@ def oracle_prefill_rate(c, units, threads):
     vis = np.concatenate(vis)
     u = np.arange(len(vis) * c.Hq) if units is None else np.asarray(units)
     flops = float(np.sum(vis[u // c.Hq])) * 4 * c.D
-    return dt, flops / dt / 1e9
+    return dt, n, flops / dt / 1e9
 
 
 def cpu_baseline(kind, c, n_all, n_one, seed, what):
@@ -710,17 +722,20 @@ def cpu_baseline(kind, c, n_all, n_one, seed, what):
     for label, threads, k, sd in (("all_cores", n, n_all, seed), ("one_thread", 1, n_one, seed + 1)):
         units = None if k is None else _sample(units_total, k, sd)
         if kind == "decode":
-            dt, rate, o = oracle_decode_rate(c, units, threads)
+            dt, passes, rate, o = oracle_decode_rate(c, units, threads)
             if units is None and label == "all_cores":
                 out = o
         else:
-            dt, rate = oracle_prefill_rate(c, units, threads)
-        res[label] = {"threads": threads, "seconds": round(dt, 3), "value": round(rate, 4),
+            dt, passes, rate = oracle_prefill_rate(c, units, threads)
+        res[label] = {"threads": threads, "seconds": round(dt, 5), "passes": passes,
+                      "value": round(rate, 4),
                       "units": units_total if units is None else int(len(units))}
     res["value"] = res["all_cores"]["value"]
     res["sample"] = (f"{what}: {res['all_cores']['units']} of {units_total} "
                      f"({'sequence' if kind == 'decode' else 'token'}, head) units at {n} threads, "
-                     f"{res['one_thread']['units']} at one thread (seeded); fp64 two-pass oracle")
+                     f"{res['one_thread']['units']} at one thread (seeded), each timing repeated "
+                     f"until {CPU_MIN_SECONDS:g} s have run or 50 passes (seconds = mean per pass); "
+                     f"fp64 two-pass oracle")
     return res, out
 
 
